@@ -1,0 +1,685 @@
+"""Plain, slow, obviously-correct CPU oracle of the RDKV hot path.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path imports this module;
+it exists so tests, the smoke check and the CPU-baseline leg of the benchmark
+can check the HIP library against an independent implementation.  It shares no
+code, tables or constants with the HIP sources: the blob format below is
+re-implemented here from its written specification.
+
+Everything is numpy.  Floating point is fp64 except where the method fixes a
+narrower type (fp16 storage, the fp32 unit cost, the fp32/fp16 quantizer steps),
+which are then evaluated with numpy's IEEE fp32/fp16 arithmetic (round to
+nearest even).
+
+Sources (cited by page title and section):
+
+* [RDKV] "RDKV - distortion-bit allocation for joint KV cache eviction and
+  quantization" (gist.science technical summary of paper 2605.08317):
+  section 2.1 (token and channel distortion weights, the rate-distortion
+  objective), 2.2 (bitwidth set {0,2,4,8,16}, reverse water-filling /
+  Lagrangian relaxation, stage 1 weighting after prefill, stage 2 V-token
+  allocation with 0 = eviction, stage 3 K-channel allocation over kept
+  tokens), 2.3 (TriZone: zone A packed 2/4/8-bit rows grouped by bitwidth,
+  zone B fp16 V rows of 16-bit tokens, zone C fp16 rows of new tokens; fused
+  dequantization inside attention).
+* [KVMATH] "Matematika KV Cache Compression" (aistudio.id), section
+  "Solusi 3: Kuantisasi KV Cache Tingkat Rendah": asymmetric uniform
+  quantization with a scale and zero-point per vector; section "Anatomi
+  Krisis": bytes of a KV cache = 2 * L * H_kv * D * P * N.
+
+Readings where the pages leave a step open are marked READING and are the
+same as in the design notes; they are listed again next to each function.
+
+Parity status: every function below is pinned by tests/test_oracle_*.py
+against closed forms, brute force, library routines or printed values.
+"""
+from __future__ import annotations
+
+import math
+from fractions import Fraction
+
+import numpy as np
+
+D = 128                       # head dimension supported by the format
+BITWIDTHS = (0, 2, 4, 8, 16)  # [RDKV] 2.2
+
+# Increments of the Lagrangian water-filling.  Raising a unit from bitwidth
+# b_j to b_{j+1} lowers its distortion c * 2^-b by c * (2^-b_j - 2^-b_{j+1})
+# at a cost of (b_{j+1} - b_j) bits; the per-bit gain (slope) is
+#   0->2: 3/8,  2->4: 3/32,  4->8: 15/1024,  8->16: 255/524288   (times c).
+# Every product c * slope is exact in fp64 for an fp32 c.
+_STEP_FROM = (0, 2, 4, 8)
+_STEP_TO = (2, 4, 8, 16)
+STEP_BITS = np.array([b1 - b0 for b0, b1 in zip(_STEP_FROM, _STEP_TO)], dtype=np.int64)
+STEP_SLOPE = np.array([(2.0 ** -b0 - 2.0 ** -b1) / (b1 - b0) for b0, b1 in zip(_STEP_FROM, _STEP_TO)])
+
+MAGIC = 0x564B4452            # "RDKV" little-endian
+VERSION = 1
+HEADER_BYTES = 256
+DESC_BYTES = 256
+ALIGN = 256
+
+
+# --------------------------------------------------------------------------
+# Stage 1: distortion weights  ([RDKV] 2.1, 2.2 stage 1)
+# --------------------------------------------------------------------------
+
+def token_weights(Qg: np.ndarray, Kh: np.ndarray, block: int = 512) -> np.ndarray:
+    """w_t = sum over query heads g of the group and query rows tau of a_{g,tau,t}.
+
+    [RDKV] 2.1: the distortion weight of a V token is the attention mass it
+    receives, summed over all query positions.  READING: prefill attention is
+    causal (token t is visible to rows tau >= t), every prefill position is a
+    query, and with GQA the weights of the G query heads that share the KV
+    head are summed.
+
+    Qg: [G][N][d] fp16, Kh: [N][d] fp16.  Returns [N] float64.
+    """
+    G, N, d = Qg.shape
+    K64 = Kh.astype(np.float64)
+    inv = 1.0 / math.sqrt(d)
+    w = np.zeros(N)
+    for g in range(G):
+        Q64 = Qg[g].astype(np.float64)
+        for r0 in range(0, N, block):
+            r1 = min(N, r0 + block)
+            S = (Q64[r0:r1] @ K64[:r1].T) * inv
+            S[np.arange(r1)[None, :] > np.arange(r0, r1)[:, None]] = -np.inf
+            S -= S.max(axis=1, keepdims=True)
+            P = np.exp(S)
+            P /= P.sum(axis=1, keepdims=True)
+            w[:r1] += P.sum(axis=0)
+    return w
+
+
+def channel_weights(Qg: np.ndarray, Kh: np.ndarray) -> np.ndarray:
+    """w_c = ||Q_{:,c}||_2 * ||K_{:,c}||_2 / sqrt(d)   ([RDKV] 2.1).
+
+    READING: Q_{:,c} stacks the G*N query rows of the heads in the group, and
+    K_{:,c} runs over all N prefill tokens (stage 1 uses the full cache).
+    Qg: [G][N][d], Kh: [N][d].  Returns [d] float64.
+    """
+    G, N, d = Qg.shape
+    q = np.sqrt(np.sum(Qg.astype(np.float64).reshape(G * N, d) ** 2, axis=0))
+    k = np.sqrt(np.sum(Kh.astype(np.float64) ** 2, axis=0))
+    return q * k / math.sqrt(d)
+
+
+def token_variance(Vh: np.ndarray) -> np.ndarray:
+    """sigma_t = population variance of the d values of V row t.
+
+    The objective of [RDKV] 2.1 multiplies each unit's weight by sigma_u, the
+    spread of the values quantized as that unit.  READING: the variance
+    (ddof 0) of the unit's values; for a V token the unit is its row.
+    Vh: [N][d].  Returns [N] float64.
+    """
+    return np.var(Vh.astype(np.float64), axis=1)
+
+
+# --------------------------------------------------------------------------
+# Exact fp32 rounding helpers
+# --------------------------------------------------------------------------
+
+def round_rational_to_f32(num: int, den: int) -> np.float32:
+    """Correctly rounded (nearest, ties to even) fp32 value of num/den >= 0.
+
+    Exact integer arithmetic; restricted to the normal fp32 range, which is all
+    the variance below can produce.
+    """
+    if num < 0 or den <= 0:
+        raise ValueError("num >= 0, den > 0 required")
+    if num == 0:
+        return np.float32(0.0)
+    # choose e with 2^23 <= num / den / 2^e < 2^24
+    e = num.bit_length() - den.bit_length() - 24
+    while True:
+        a, b = (num, den << e) if e >= 0 else (num << -e, den)
+        if a >= (b << 24):
+            e += 1
+        elif a < (b << 23):
+            e -= 1
+        else:
+            break
+    m, r = divmod(a, b)
+    if 2 * r > b or (2 * r == b and (m & 1)):
+        m += 1
+    if m == 1 << 24:
+        m >>= 1
+        e += 1
+    if not (-149 <= e and e + 24 <= 128):
+        raise OverflowError("value outside the fp32 range handled here")
+    if e + 23 < -126:
+        raise OverflowError("subnormal fp32 results are not produced by this method")
+    return np.float32(math.ldexp(m, e))
+
+
+def exact_population_variance(x16: np.ndarray) -> Fraction:
+    """Exact population variance of fp16 values, as a rational number.
+
+    Every fp16 value is an integer multiple of 2^-24, so with X = x * 2^24,
+    var = (n * sum X^2 - (sum X)^2) / (n^2 * 2^48) exactly.  The sums are
+    done with Python integers.  An empty input has variance 0.
+    """
+    n = int(np.size(x16))
+    if n == 0:
+        return Fraction(0)
+    X = [int(v) for v in (np.asarray(x16, np.float16).astype(np.float64) * float(1 << 24)).astype(np.int64).ravel()]
+    s1 = sum(X)
+    s2 = sum(v * v for v in X)
+    return Fraction(n * s2 - s1 * s1, n * n << 48)
+
+
+def exact_population_variance_f32(x16: np.ndarray) -> np.float32:
+    """The exact population variance rounded once (nearest-even) to fp32."""
+    v = exact_population_variance(x16)
+    return round_rational_to_f32(v.numerator, v.denominator)
+
+
+def masked_channel_variance(Kh: np.ndarray, bits_tok: np.ndarray) -> np.ndarray:
+    """sigma_c over the tokens kept by the V allocation, one value per channel.
+
+    [RDKV] 2.2 stage 3 solves the K-channel problem only over the tokens kept
+    in stage 2.  READING: sigma_c is the population variance of K[:, c] over
+    the kept tokens (b_t > 0), taken exactly and rounded once to fp32 so that
+    the fp32 unit costs are well defined.  No kept tokens gives 0.
+    Kh: [N][d] fp16, bits_tok: [N] uint8.  Returns [d] float32.
+    """
+    kept = Kh[bits_tok > 0]
+    return np.array([exact_population_variance_f32(kept[:, c]) for c in range(Kh.shape[1])],
+                    dtype=np.float32)
+
+
+# --------------------------------------------------------------------------
+# Stages 2-3: Lagrangian bit allocation  ([RDKV] 2.1 objective, 2.2)
+# --------------------------------------------------------------------------
+
+def unit_costs(w: np.ndarray, sigma: np.ndarray) -> np.ndarray:
+    """c_u = w_u * sigma_u rounded once to fp32 (both factors are fp32)."""
+    return np.asarray(w, np.float32) * np.asarray(sigma, np.float32)
+
+
+def lagrangian_allocate(c: np.ndarray, budget: int):
+    """Bitwidths in {0,2,4,8,16} from reverse water-filling on the unit costs.
+
+    The problem of [RDKV] 2.1 is  min sum_u c_u 2^-b_u  s.t.  sum_u b_u <= B,
+    solved by Lagrangian relaxation ([RDKV] 2.2).  For a multiplier lambda each
+    unit independently minimises c_u 2^-b + lambda*b over the bitwidth set.
+    Because the per-bit gains 3/8 > 3/32 > 15/1024 > 255/524288 decrease, all
+    five bitwidths lie on every unit's lower convex hull and the minimiser is
+    "take step j iff c_u * slope_j > lambda" (ties stay at the lower
+    bitwidth, READING).  The multiplier is the smallest lambda in
+    {0} U {c_u * slope_j} whose allocation meets the budget (READING: no greedy
+    use of leftover bits).  Units with c_u <= 0 (or NaN) get 0 bits.
+
+    Returns (bits uint8 [n], lambda float64).
+    """
+    c = np.asarray(c, np.float32)
+    if budget < 0:
+        raise ValueError("budget must be >= 0")
+    v = c.astype(np.float64)[:, None] * STEP_SLOPE[None, :]          # exact
+    wts = np.broadcast_to(STEP_BITS[None, :], v.shape)
+    pos = v > 0
+    if int(wts[pos].sum()) <= budget:
+        lam = 0.0
+    else:
+        vals = v[pos]
+        vw = wts[pos]
+        order = np.argsort(vals, kind="stable")
+        sv, sw = vals[order], vw[order]
+        # cost(lambda) = total bits of increments strictly above lambda
+        suffix = np.concatenate([np.cumsum(sw[::-1])[::-1], [0]])
+        cand = np.unique(sv)
+        above = suffix[np.searchsorted(sv, cand, side="right")]
+        lam = float(cand[np.argmax(above <= budget)])               # first feasible
+    bits = ((v > lam) * wts).sum(axis=1)
+    return bits.astype(np.uint8), lam
+
+
+def allocate_segment(w_tok, var_tok, w_chan, Kh, budget_v: int, budget_k: int):
+    """Stage 2 (V tokens) then stage 3 (K channels over kept tokens).
+
+    Inputs are fp32 weights/variances of one segment and its fp16 K [N][d].
+    Returns dict(bits_tok, bits_chan, var_chan, lambda_v, lambda_k).
+    """
+    bt, lv = lagrangian_allocate(unit_costs(w_tok, var_tok), budget_v)
+    vc = masked_channel_variance(Kh, bt)
+    bc, lk = lagrangian_allocate(unit_costs(w_chan, vc), budget_k)
+    return dict(bits_tok=bt, bits_chan=bc, var_chan=vc, lambda_v=lv, lambda_k=lk)
+
+
+# --------------------------------------------------------------------------
+# Quantizer  ([KVMATH] Solusi 3; fp16 scale/zero per (token, bit-segment))
+# --------------------------------------------------------------------------
+
+def quantize(x16: np.ndarray, b: int):
+    """Asymmetric uniform b-bit quantization of fp16 vectors (last axis).
+
+    scale = (max - min) / (2^b - 1), zero = min, q = round((x - zero) / scale)
+    ([KVMATH] Solusi 3), one (scale, zero) per vector.  Fixed precisions: the
+    range and the quotient are IEEE fp32 operations, the scale is stored
+    rounded to fp16, the zero is the fp16 minimum itself, codes use
+    round-half-to-even on the fp32 quotient and are clamped to [0, 2^b - 1];
+    a zero scale gives all-zero codes.
+
+    Returns (codes uint32 [..., n], scale fp16 [...], zero fp16 [...]).
+    """
+    x = np.asarray(x16, np.float16).astype(np.float32)
+    mn = x.min(axis=-1)
+    mx = x.max(axis=-1)
+    rng = (mx - mn).astype(np.float32)
+    scale = (rng / np.float32((1 << b) - 1)).astype(np.float32).astype(np.float16)
+    zero = mn.astype(np.float16)
+    s = scale.astype(np.float32)[..., None]
+    diff = (x - zero.astype(np.float32)[..., None]).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        quot = (diff / s).astype(np.float32)
+    q = np.clip(np.rint(quot), 0, (1 << b) - 1)
+    q = np.where(s == 0, 0, q)
+    return q.astype(np.uint32), scale, zero
+
+
+def dequantize(codes, scale, zero) -> np.ndarray:
+    """x_hat = code * scale + zero with a single rounding to fp32 (fused multiply-add).
+
+    code * scale + zero is a multiple of 2^-24 below 2^24, so the fp64
+    evaluation is exact and the one rounding to fp32 is that of the fused
+    multiply-add.
+    """
+    return (np.asarray(codes, np.float64) * np.float64(np.float16(scale))
+            + np.float64(np.float16(zero))).astype(np.float32)
+
+
+# --------------------------------------------------------------------------
+# Blob format (TriZone, [RDKV] 2.3) -- written from the format specification
+# --------------------------------------------------------------------------
+
+def _align(x: int, a: int = ALIGN) -> int:
+    return (x + a - 1) // a * a
+
+
+def _cdiv(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+class Layout:
+    """Sizes and fixed offsets of a packed cache.
+
+    The blob is: a 256-byte header, one 256-byte descriptor per segment
+    (segment = (sequence, layer, KV head), index (s*L + l)*Hkv + h), then one
+    fixed-size slot per segment.  A slot holds, at fixed offsets, zone C
+    (K then V, [cap][128] fp16 each), the V rows of kept tokens (groups of
+    2/4/8-bit code rows then fp16 rows, each group 256-byte aligned), the
+    per-token K records and the int32 original positions of kept tokens.
+    Region sizes are bounds that follow from the budgets alone.
+    """
+
+    def __init__(self, n_seq, n_layers, n_q_heads, n_kv_heads, head_dim, n_tokens,
+                 budget_v, budget_k, zone_c_capacity):
+        if head_dim != D:
+            raise ValueError("head_dim must be 128")
+        self.S, self.L, self.Hq, self.Hkv = n_seq, n_layers, n_q_heads, n_kv_heads
+        self.d, self.N = head_dim, n_tokens
+        self.budget_v, self.budget_k, self.cap = budget_v, budget_k, zone_c_capacity
+        self.n_seg = n_seq * n_layers * n_kv_heads
+        self.nk_max = min(n_tokens, budget_v // 2)
+        bk = min(budget_k, 16 * D)
+        self.rec_max = 4 * ((bk + 98) // 32 + 4)
+        self.off_kc = 0
+        self.off_vc = zone_c_capacity * D * 2
+        self.off_v = _align(2 * zone_c_capacity * D * 2)
+        self.v_reserve = _align(min(16 * budget_v, 2 * D * n_tokens) + 768)
+        self.off_krec = self.off_v + self.v_reserve
+        self.off_pos = self.off_krec + _align(self.nk_max * self.rec_max)
+        self.slot_bytes = self.off_pos + _align(4 * self.nk_max)
+        self.desc_offset = HEADER_BYTES
+        self.slots_offset = _align(HEADER_BYTES + DESC_BYTES * self.n_seg)
+        self.cache_bytes = self.slots_offset + self.n_seg * self.slot_bytes
+
+    def seg_index(self, s, l, h):
+        return (s * self.L + l) * self.Hkv + h
+
+    def slot_base(self, seg):
+        return self.slots_offset + seg * self.slot_bytes
+
+    def header_bytes(self) -> bytes:
+        h = np.zeros(HEADER_BYTES, np.uint8)
+        i32 = [MAGIC, VERSION, self.S, self.L, self.Hq, self.Hkv, self.d, self.cap]
+        h[0:32] = np.array(i32, np.uint32).view(np.uint8)
+        i64 = [self.N, self.budget_v, self.budget_k, self.n_seg, self.desc_offset,
+               self.slots_offset, self.slot_bytes]
+        h[32:88] = np.array(i64, np.int64).view(np.uint8)
+        return h.tobytes()
+
+
+def channel_permutation(bits_chan: np.ndarray) -> np.ndarray:
+    """Channels ordered by bitwidth 16, 8, 4, 2, 0; ties by ascending index."""
+    rank = {16: 0, 8: 1, 4: 2, 2: 3, 0: 4}
+    return np.array(sorted(range(D), key=lambda c: (rank[int(bits_chan[c])], c)), np.uint8)
+
+
+def pack_codes(codes, b) -> np.ndarray:
+    """LSB-first packing of b-bit codes (last axis) into little-endian uint32 words.
+
+    Element i lands in word i // (32/b) at bit offset (i % (32/b)) * b; a
+    partial last word is zero-filled.
+    """
+    codes = np.asarray(codes, np.uint64)
+    per = 32 // b
+    n = codes.shape[-1]
+    nw = _cdiv(n, per)
+    padded = np.zeros(codes.shape[:-1] + (nw * per,), np.uint64)
+    padded[..., :n] = codes
+    shifts = (np.arange(per, dtype=np.uint64) * np.uint64(b))
+    words = (padded.reshape(codes.shape[:-1] + (nw, per)) << shifts).sum(axis=-1)
+    return words.astype(np.uint32)
+
+
+def unpack_codes(words, b, n) -> np.ndarray:
+    """Inverse of pack_codes: the first n b-bit codes of the words (last axis)."""
+    words = np.asarray(words, np.uint32).astype(np.uint64)
+    per = 32 // b
+    shifts = (np.arange(per, dtype=np.uint64) * np.uint64(b))
+    codes = (words[..., :, None] >> shifts) & np.uint64((1 << b) - 1)
+    return codes.reshape(words.shape[:-1] + (words.shape[-1] * per,))[..., :n].astype(np.uint32)
+
+
+def half2_words(scale, zero) -> np.ndarray:
+    """uint32 words holding fp16 scale in the low half and fp16 zero in the high half."""
+    sb = np.asarray(scale, np.float16).view(np.uint16).astype(np.uint32)
+    zb = np.asarray(zero, np.float16).view(np.uint16).astype(np.uint32)
+    return sb | (zb << np.uint32(16))
+
+
+def record_words(n_chan):
+    """Word counts of a K record: (w16, w8, w4, w2, n_meta), n_chan = (n16, n8, n4, n2)."""
+    n16, n8, n4, n2 = n_chan
+    n_meta = sum(1 for n in (n8, n4, n2) if n > 0)
+    return _cdiv(n16, 2), _cdiv(n8, 4), _cdiv(n4, 8), _cdiv(n2, 16), n_meta
+
+
+def pack_segment(lay: Layout, blob: np.ndarray, seg: int, Kh, Vh, bits_tok, bits_chan):
+    """Write one segment's descriptor and slot into `blob` (uint8 array).
+
+    Kept tokens (b_t > 0) are grouped by bitwidth 2, 4, 8 (zone A) and 16
+    (zone B), ascending position inside a group ([RDKV] 2.3, rows grouped by
+    bitwidth; the group order is a format choice).  V rows: 2/4/8-bit rows hold
+    the 128 codes of the token, LSB-first in uint32 words; 16-bit rows are the
+    fp16 values.  One K record per kept token, in the same order: fp16 values
+    of the 16-bit channels, then the codes of the 8-, 4- and 2-bit channels
+    (channels in permutation order, each part padded to a whole word), then one
+    (scale, zero) fp16 pair per present integer part (order 8, 4, 2), then,
+    for a 2/4/8-bit token only, the (scale, zero) of its V row; the records of
+    16-bit tokens are one word shorter.  0-bit channels are not stored.
+    """
+    base = lay.slot_base(seg)
+    bits_tok = np.asarray(bits_tok)
+    bits_chan = np.asarray(bits_chan)
+    Kh = np.asarray(Kh, np.float16)
+    Vh = np.asarray(Vh, np.float16)
+    groups = [np.nonzero(bits_tok == b)[0] for b in (2, 4, 8, 16)]
+    kept = np.concatenate(groups).astype(np.int64)
+    nk = len(kept)
+    perm = channel_permutation(bits_chan)
+    n_chan = [int(np.sum(bits_chan == b)) for b in (16, 8, 4, 2)]
+    w16, w8, w4, w2, n_meta = record_words(n_chan)
+    rec_words = w16 + w8 + w4 + w2 + n_meta + 1
+
+    # V rows group by group, and the (scale, zero) word of each kept V row
+    off_v = []
+    vmeta = []
+    cur = base + lay.off_v
+    for b, toks in zip((2, 4, 8, 16), groups):
+        off_v.append(cur)
+        row = D * b // 8
+        if b == 16:
+            data = Vh[toks].reshape(len(toks), D).view(np.uint8)
+            vmeta.append(np.zeros(len(toks), np.uint32))
+        else:
+            q, sc, z = quantize(Vh[toks].reshape(len(toks), D), b)
+            data = pack_codes(q, b).view(np.uint8)
+            vmeta.append(half2_words(sc, z))
+        blob[cur:cur + len(toks) * row] = data.reshape(-1)
+        cur = _align(cur + len(toks) * row)
+
+    # K records
+    kp = Kh[kept][:, perm.astype(np.int64)].reshape(nk, D)
+    c = np.cumsum([0] + n_chan)
+    parts = []
+    part16 = np.zeros((nk, 2 * w16), np.float16)
+    part16[:, :n_chan[0]] = kp[:, c[0]:c[1]]
+    parts.append(part16.view(np.uint32).reshape(nk, w16))
+    metas = []
+    for j, b in zip((1, 2, 3), (8, 4, 2)):
+        if n_chan[j] == 0:
+            continue
+        q, sc, z = quantize(kp[:, c[j]:c[j + 1]], b)
+        parts.append(pack_codes(q, b).reshape(nk, -1))
+        metas.append(half2_words(sc, z).reshape(nk, 1))
+    parts += metas
+    parts.append(np.concatenate(vmeta).reshape(nk, 1))
+    words = np.concatenate(parts, axis=1).astype(np.uint32)
+    assert words.shape == (nk, rec_words)
+    # zone-A tokens take the full record; 16-bit tokens (last in kept order)
+    # drop the trailing V word, which they do not have
+    n_a = nk - len(groups[3])
+    off_rec = base + lay.off_krec
+    ra = words[:n_a].reshape(-1).view(np.uint8)
+    rb = np.ascontiguousarray(words[n_a:, :-1]).reshape(-1).view(np.uint8)
+    blob[off_rec:off_rec + ra.size] = ra
+    blob[off_rec + ra.size:off_rec + ra.size + rb.size] = rb
+
+    # positions
+    pos0 = base + lay.off_pos
+    blob[pos0: pos0 + 4 * nk] = kept.astype(np.int32).view(np.uint8)
+
+    # descriptor
+    dsc = np.zeros(DESC_BYTES, np.uint8)
+    i32 = [len(g) for g in groups] + [nk] + n_chan + [4 * rec_words, lay.cap, 0]
+    dsc[0:48] = np.array(i32, np.int32).view(np.uint8)
+    u64 = off_v + [off_rec, pos0, base + lay.off_kc, base + lay.off_vc]
+    dsc[48:112] = np.array(u64, np.uint64).view(np.uint8)
+    dsc[128:256] = perm
+    d0 = lay.desc_offset + seg * DESC_BYTES
+    blob[d0:d0 + DESC_BYTES] = dsc
+
+
+def empty_blob(lay: Layout) -> np.ndarray:
+    """A cache with every segment empty: header, descriptors with zero counts."""
+    blob = np.zeros(lay.cache_bytes, np.uint8)
+    blob[:HEADER_BYTES] = np.frombuffer(lay.header_bytes(), np.uint8)
+    for seg in range(lay.n_seg):
+        pack_segment(lay, blob, seg, np.zeros((0, D), np.float16), np.zeros((0, D), np.float16),
+                     np.zeros(0, np.uint8), np.zeros(D, np.uint8))
+    return blob
+
+
+def pack_cache(lay: Layout, K, V, bits_tok, bits_chan, layer_begin: int = 0, blob=None):
+    """Pack segments of layers [layer_begin, layer_begin + L_in) into a blob.
+
+    K, V: [S][L_in][Hkv][N][d] fp16; bits_tok [S][L_in][Hkv][N]; bits_chan
+    [S][L_in][Hkv][d].  Segments not covered keep their previous content
+    (a fresh blob starts empty).
+    """
+    if blob is None:
+        blob = empty_blob(lay)
+    S, Lin = K.shape[0], K.shape[1]
+    for s in range(S):
+        for l in range(Lin):
+            for h in range(lay.Hkv):
+                seg = lay.seg_index(s, layer_begin + l, h)
+                pack_segment(lay, blob, seg, K[s, l, h], V[s, l, h], bits_tok[s, l, h], bits_chan[s, l, h])
+    return blob
+
+
+# --------------------------------------------------------------------------
+# Blob parsing and decode  ([RDKV] 2.3, fused dequant attention over A+B+C)
+# --------------------------------------------------------------------------
+
+def _u32(blob, off, n):
+    return blob[off:off + 4 * n].view(np.uint32)
+
+
+def _half_pairs(words):
+    """(scale, zero) fp16 arrays from uint32 words (scale in the low half)."""
+    h = np.asarray(words, np.uint32).reshape(-1, 1).view(np.float16)
+    return h[:, 0], h[:, 1]
+
+
+def read_descriptor(blob, lay: Layout, seg: int) -> dict:
+    d0 = lay.desc_offset + seg * DESC_BYTES
+    i32 = blob[d0:d0 + 48].view(np.int32)
+    u64 = blob[d0 + 48:d0 + 112].view(np.uint64)
+    return dict(n_tok=[int(x) for x in i32[0:4]], n_kept=int(i32[4]),
+                n_chan=[int(x) for x in i32[5:9]], rec=int(i32[9]), cap=int(i32[10]),
+                off_v=[int(x) for x in u64[0:4]], off_krec=int(u64[4]), off_pos=int(u64[5]),
+                off_kc=int(u64[6]), off_vc=int(u64[7]),
+                perm=blob[d0 + 128:d0 + 256].copy())
+
+
+def unpack_segment(blob, lay: Layout, seg: int):
+    """Dequantized kept rows of one segment, in kept order.
+
+    Returns (K_hat [n_kept][128] float32 with 0 on 0-bit channels,
+    V_hat [n_kept][128] float32, positions [n_kept] int32, bits [n_kept]).
+    """
+    ds = read_descriptor(blob, lay, seg)
+    nk, rec = ds["n_kept"], ds["rec"]
+    n16, n8, n4, n2 = ds["n_chan"]
+    w16, w8, w4, w2, n_meta = record_words(ds["n_chan"])
+    n_a = nk - ds["n_tok"][3]
+    ra = _u32(blob, ds["off_krec"], n_a * rec // 4).reshape(n_a, rec // 4)
+    rb = _u32(blob, ds["off_krec"] + n_a * rec, (nk - n_a) * (rec // 4 - 1)).reshape(nk - n_a, rec // 4 - 1)
+    words = np.concatenate([ra, np.concatenate([rb, np.zeros((nk - n_a, 1), np.uint32)], axis=1)])
+    vs, vz = _half_pairs(words[:, -1])
+    tb = np.concatenate([np.full(n, b, np.int32) for n, b in zip(ds["n_tok"], (2, 4, 8, 16))])
+    # V rows
+    Vh = np.zeros((nk, D), np.float32)
+    i = 0
+    for gi, b in enumerate((2, 4, 8, 16)):
+        n = ds["n_tok"][gi]
+        row = D * b // 8
+        raw = blob[ds["off_v"][gi]:ds["off_v"][gi] + n * row]
+        if b == 16:
+            Vh[i:i + n] = raw.view(np.float16).reshape(n, D).astype(np.float32)
+        else:
+            codes = unpack_codes(raw.view(np.uint32).reshape(n, row // 4), b, D)
+            Vh[i:i + n] = dequantize(codes, vs[i:i + n, None], vz[i:i + n, None])
+        i += n
+    # K records
+    kp = np.zeros((nk, D), np.float32)
+    kp[:, :n16] = words[:, :w16].copy().view(np.float16)[:, :n16].astype(np.float32)
+    wo, mo, c0 = w16, w16 + w8 + w4 + w2, n16
+    for n, b, nw in ((n8, 8, w8), (n4, 4, w4), (n2, 2, w2)):
+        if n == 0:
+            continue
+        s, z = _half_pairs(words[:, mo])
+        kp[:, c0:c0 + n] = dequantize(unpack_codes(words[:, wo:wo + nw], b, n), s[:, None], z[:, None])
+        mo, wo, c0 = mo + 1, wo + nw, c0 + n
+    Kh = np.zeros((nk, D), np.float32)
+    Kh[:, ds["perm"].astype(np.int64)] = kp
+    pos = blob[ds["off_pos"]:ds["off_pos"] + 4 * nk].view(np.int32).copy()
+    return Kh, Vh, pos, tb
+
+
+def zone_c_rows(blob, lay: Layout, seg: int, n_rows: int):
+    ds = read_descriptor(blob, lay, seg)
+    kc = blob[ds["off_kc"]:ds["off_kc"] + n_rows * D * 2].view(np.float16).reshape(n_rows, D)
+    vc = blob[ds["off_vc"]:ds["off_vc"] + n_rows * D * 2].view(np.float16).reshape(n_rows, D)
+    return kc.astype(np.float32), vc.astype(np.float32)
+
+
+def append_zone_c(blob, lay: Layout, c_len: int, k_new, v_new):
+    """Write the new token's fp16 k, v at row c_len of every segment's zone C."""
+    if not (0 <= c_len < lay.cap):
+        raise ValueError("zone C is full")
+    for s in range(lay.S):
+        for l in range(lay.L):
+            for h in range(lay.Hkv):
+                ds = read_descriptor(blob, lay, lay.seg_index(s, l, h))
+                o = ds["off_kc"] + c_len * D * 2
+                blob[o:o + D * 2] = np.asarray(k_new[s, l, h], np.float16).view(np.uint8)
+                o = ds["off_vc"] + c_len * D * 2
+                blob[o:o + D * 2] = np.asarray(v_new[s, l, h], np.float16).view(np.uint8)
+
+
+def attention(q64: np.ndarray, K: np.ndarray, V: np.ndarray) -> np.ndarray:
+    """softmax(q K^T / sqrt(d)) V in fp64 for q [G][d], K, V [n][d]; empty n -> 0."""
+    if K.shape[0] == 0:
+        return np.zeros((q64.shape[0], V.shape[1]))
+    s = (q64 @ K.astype(np.float64).T) / math.sqrt(q64.shape[1])
+    s -= s.max(axis=1, keepdims=True)
+    p = np.exp(s)
+    p /= p.sum(axis=1, keepdims=True)
+    return p @ V.astype(np.float64)
+
+
+def decode_step(blob, lay: Layout, q, c_len: int, k_new=None, v_new=None):
+    """One decode step over every segment; returns out [S][L][Hq][d] float64.
+
+    If k_new/v_new are given they are first appended at zone-C row c_len and
+    the step attends over c_len + 1 zone-C rows, else over c_len rows.
+    Attention runs over the kept tokens (zones A and B, dequantized, 0-bit K
+    channels contributing 0) and the zone-C rows; evicted tokens take no part
+    in the softmax (READING of bitwidth 0 = eviction, [RDKV] 2.2).
+    The logit scale stays 1/sqrt(128).
+    """
+    n_c = c_len
+    if k_new is not None:
+        append_zone_c(blob, lay, c_len, k_new, v_new)
+        n_c = c_len + 1
+    G = lay.Hq // lay.Hkv
+    out = np.zeros((lay.S, lay.L, lay.Hq, D))
+    for s in range(lay.S):
+        for l in range(lay.L):
+            for h in range(lay.Hkv):
+                seg = lay.seg_index(s, l, h)
+                Kh, Vh, _, _ = unpack_segment(blob, lay, seg)
+                kc, vc = zone_c_rows(blob, lay, seg, n_c)
+                Ka = np.concatenate([Kh, kc])
+                Va = np.concatenate([Vh, vc])
+                qg = np.asarray(q[s, l, h * G:(h + 1) * G], np.float16).astype(np.float64)
+                out[s, l, h * G:(h + 1) * G] = attention(qg, Ka, Va)
+    return out
+
+
+# --------------------------------------------------------------------------
+# Byte accounting  ([KVMATH] Anatomi Krisis; [RDKV] 1: decode rereads the cache)
+# --------------------------------------------------------------------------
+
+def kv_bytes_fp16_per_token(n_layers: int, n_kv_heads: int, head_dim: int, bytes_per_elem: float = 2.0):
+    """Bytes of an uncompressed KV cache per token: 2 (K and V) * L * H_kv * D * P."""
+    return 2 * n_layers * n_kv_heads * head_dim * bytes_per_elem
+
+
+def segment_decode_bytes(blob, lay: Layout, seg: int, n_c: int) -> int:
+    """Bytes one decode step must read for a segment: V rows, K records, zone C.
+
+    Counted from the packed descriptor: code/fp16 payload of every kept row,
+    the (scale, zero) words, and n_c fp16 K and V rows of zone C.  Word padding
+    inside records is included (it is read); alignment gaps are not.
+    """
+    ds = read_descriptor(blob, lay, seg)
+    v = sum(n * D * b // 8 for n, b in zip(ds["n_tok"], (2, 4, 8, 16)))
+    k = ds["n_kept"] * ds["rec"] - 4 * ds["n_tok"][3]
+    return v + k + 2 * n_c * D * 2
+
+
+def segment_payload_bytes(blob, lay: Layout, seg: int) -> float:
+    """Bytes of quantized/fp16 values alone (no scale/zero words, no padding).
+
+    sum over kept tokens of (d * b_t + sum_c b_c) / 8: the rate of the
+    allocation in bytes.
+    """
+    ds = read_descriptor(blob, lay, seg)
+    vbits = sum(n * D * b for n, b in zip(ds["n_tok"], (2, 4, 8, 16)))
+    kbits = ds["n_kept"] * sum(n * b for n, b in zip(ds["n_chan"], (16, 8, 4, 2)))
+    return (vbits + kbits) / 8
+
+
+# --------------------------------------------------------------------------
+# Whole pipeline on one segment (convenience for tests and the CPU baseline)
+# --------------------------------------------------------------------------
+
+def score_segment(Qg, Kh, Vh):
+    """Stage 1 on one segment: (w_tok, var_tok, w_chan) in float64."""
+    return token_weights(Qg, Kh), token_variance(Vh), channel_weights(Qg, Kh)

@@ -1,0 +1,470 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Closed forms, brute force on tiny inputs, independent library routines
+(torch's scaled_dot_product_attention, numpy's SVD-based matrix 2-norm,
+Python's exact `statistics.pvariance` on Fractions) and hand-worked values.
+Each test is chosen so that a plausible slip in the oracle (a dropped term,
+a wrong sign or index, a transposed operand, the wrong causal side, the wrong
+rounding mode) fails it.  CPU only.
+"""
+import itertools
+import math
+import statistics
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------- stage 1
+
+def _attention_matrix_sdpa(Qg, Kh):
+    """A[g] = causal softmax(Q_g K^T / sqrt(d)) via torch SDPA with V = I (fp64, CPU)."""
+    G, N, d = Qg.shape
+    q = torch.from_numpy(Qg.astype(np.float64))[None]
+    k = torch.from_numpy(np.broadcast_to(Kh.astype(np.float64), (G, N, d)).copy())[None]
+    eye = torch.eye(N, dtype=torch.float64).expand(1, G, N, N).contiguous()
+    return torch.nn.functional.scaled_dot_product_attention(q, k, eye, is_causal=True)[0].numpy()
+
+
+@pytest.mark.parametrize("G,N", [(1, 7), (4, 33), (2, 130)])
+def test_token_weights_match_sdpa_column_sums(G, N):
+    r = _rng(1)
+    Q = r.standard_normal((G, N, 128)).astype(np.float16)
+    K = (r.standard_normal((N, 128)) * 1.5).astype(np.float16)
+    A = _attention_matrix_sdpa(Q, K)
+    ref = A.sum(axis=(0, 1))
+    w = O.token_weights(Q, K, block=16)
+    np.testing.assert_allclose(w, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_token_weights_sum_to_number_of_query_rows():
+    r = _rng(2)
+    G, N = 4, 300
+    Q = r.standard_normal((G, N, 128)).astype(np.float16)
+    K = r.standard_normal((N, 128)).astype(np.float16)
+    K[:10, 0] = 60  # strong heavy hitters
+    w = O.token_weights(Q, K, block=64)
+    assert abs(w.sum() - G * N) < 1e-9 * G * N
+    assert np.all(w > 0)
+
+
+def test_token_weights_uniform_attention_harmonic_closed_form():
+    # Q = 0: every row attends uniformly to its tau + 1 visible tokens, so
+    # w_t = G * (H_N - H_t) with H_n the n-th harmonic number (t 0-indexed).
+    G, N = 3, 257
+    Q = np.zeros((G, N, 128), np.float16)
+    K = _rng(3).standard_normal((N, 128)).astype(np.float16)
+    w = O.token_weights(Q, K, block=100)
+    H = [Fraction(0)]
+    for i in range(1, N + 1):
+        H.append(H[-1] + Fraction(1, i))
+    ref = np.array([float(G * (H[N] - H[t])) for t in range(N)])
+    np.testing.assert_allclose(w, ref, rtol=1e-13)
+    # first token sees every row, last token only its own
+    assert w[0] > w[1] > w[-1]
+
+
+def test_token_weight_is_total_variation_of_eviction():
+    # The page defines w_t as the total-variation distance of the attention
+    # distribution after evicting t.  Brute force: for every row, remove t,
+    # renormalise, measure TV; a row whose only visible token is t goes to the
+    # empty distribution (TV 1).
+    G, N = 2, 9
+    r = _rng(4)
+    Q = r.standard_normal((G, N, 128)).astype(np.float16)
+    K = r.standard_normal((N, 128)).astype(np.float16)
+    A = _attention_matrix_sdpa(Q, K)
+    w = O.token_weights(Q, K)
+    for t in range(N):
+        tv = 0.0
+        for g in range(G):
+            for tau in range(N):
+                p = A[g, tau, : tau + 1]
+                if t > tau:
+                    continue
+                rest = np.delete(np.arange(tau + 1), t)
+                if rest.size == 0:
+                    tv += 1.0
+                    continue
+                pe = np.zeros(tau + 1)
+                pe[rest] = p[rest] / p[rest].sum()
+                tv += 0.5 * np.abs(p - pe).sum()
+        assert abs(tv - w[t]) < 1e-12
+
+
+def test_channel_weight_is_spectral_norm_of_logit_deviation():
+    # Zeroing channel c changes the logits of the group by the rank-1 matrix
+    # Q_{:,c} K_{:,c}^T / sqrt(d); its spectral norm is w_c.
+    G, N = 4, 40
+    r = _rng(5)
+    Q = r.standard_normal((G, N, 128)).astype(np.float16)
+    K = (r.standard_normal((N, 128)) * np.linspace(0.1, 3, 128)).astype(np.float16)
+    w = O.channel_weights(Q, K)
+    Qs = Q.astype(np.float64).reshape(G * N, 128)
+    K64 = K.astype(np.float64)
+    for c in [0, 1, 63, 127]:
+        Qz, Kz = Qs.copy(), K64.copy()
+        Qz[:, c] = 0
+        dev = Qs @ K64.T / math.sqrt(128) - Qz @ K64.T / math.sqrt(128)
+        assert abs(np.linalg.norm(dev, 2) - w[c]) < 1e-10 * w[c]
+        Kz[:, c] = 0
+        dev2 = Qs @ K64.T / math.sqrt(128) - Qs @ Kz.T / math.sqrt(128)
+        assert abs(np.linalg.norm(dev2, 2) - w[c]) < 1e-10 * w[c]
+
+
+def test_token_variance_matches_pvariance():
+    V = _rng(6).standard_normal((5, 128)).astype(np.float16)
+    got = O.token_variance(V)
+    for t in range(5):
+        ref = statistics.pvariance([Fraction(float(x)) for x in V[t]])
+        assert abs(got[t] - float(ref)) < 1e-14
+
+
+# ---------------------------------------------------------------- exact variance and rounding
+
+def test_round_rational_to_f32_matches_numpy_away_from_ties():
+    r = _rng(7)
+    for _ in range(2000):
+        num = int(r.integers(1, 1 << 62))
+        den = int(r.integers(1, 1 << 40))
+        got = O.round_rational_to_f32(num, den)
+        assert got == np.float32(num / den) or abs(float(got) - num / den) <= abs(float(np.float32(num / den)) - num / den)
+        # the result is the nearest fp32: neither neighbour is closer
+        exact = Fraction(num, den)
+        lo = np.nextafter(got, np.float32(0))
+        hi = np.nextafter(got, np.float32(np.inf))
+        d0 = abs(Fraction(float(got)) - exact)
+        assert d0 <= abs(Fraction(float(lo)) - exact) and d0 <= abs(Fraction(float(hi)) - exact)
+
+
+def test_round_rational_to_f32_ties_to_even():
+    one = Fraction(1)
+    ulp = Fraction(1, 1 << 23)
+    # 1 + ulp/2 is a tie between 1 (even) and 1 + ulp (odd) -> 1
+    t = one + ulp / 2
+    assert O.round_rational_to_f32(t.numerator, t.denominator) == np.float32(1.0)
+    # 1 + 3ulp/2 is a tie between 1 + ulp (odd) and 1 + 2ulp (even) -> 1 + 2ulp
+    t = one + 3 * ulp / 2
+    assert O.round_rational_to_f32(t.numerator, t.denominator) == np.float32(1 + 2 * 2.0 ** -23)
+    # just above the tie rounds up
+    t = one + ulp / 2 + Fraction(1, 1 << 60)
+    assert O.round_rational_to_f32(t.numerator, t.denominator) == np.float32(1 + 2.0 ** -23)
+
+
+def test_exact_variance_matches_statistics_pvariance():
+    r = _rng(8)
+    for n in [1, 2, 5, 64, 301]:
+        x = (r.standard_normal(n) * r.choice([1e-3, 1, 300])).astype(np.float16)
+        ref = statistics.pvariance([Fraction(float(v)) for v in x])
+        assert O.exact_population_variance(x) == ref
+    assert O.exact_population_variance(np.zeros(0, np.float16)) == 0
+    assert O.exact_population_variance(np.full(7, 3.5, np.float16)) == 0
+
+
+def test_masked_channel_variance_uses_kept_tokens_only():
+    r = _rng(9)
+    K = r.standard_normal((50, 128)).astype(np.float16)
+    bits = np.zeros(50, np.uint8)
+    bits[[3, 7, 8, 20, 49]] = [2, 16, 4, 8, 2]
+    got = O.masked_channel_variance(K, bits)
+    for c in [0, 5, 127]:
+        ref = statistics.pvariance([Fraction(float(v)) for v in K[[3, 7, 8, 20, 49], c]])
+        assert got[c] == O.round_rational_to_f32(ref.numerator, ref.denominator)
+    assert np.all(O.masked_channel_variance(K, np.zeros(50, np.uint8)) == 0)
+
+
+# ---------------------------------------------------------------- allocation
+
+BITS = (0, 2, 4, 8, 16)
+
+
+def _lagrangian_value(c, b, lam):
+    return Fraction(float(c)) * Fraction(1, 1 << b) + lam * b
+
+
+def _exact_argmin_bits(c, lam):
+    """Per-unit argmin of c 2^-b + lam b over {0,2,4,8,16}, ties to the lower b (exact)."""
+    out = []
+    for cu in c:
+        vals = [_lagrangian_value(cu, b, lam) for b in BITS]
+        out.append(BITS[min(range(5), key=lambda i: (vals[i], i))])
+    return np.array(out)
+
+
+def test_step_slopes_are_the_exact_hull_slopes():
+    exact = [Fraction(3, 8), Fraction(3, 32), Fraction(15, 1024), Fraction(255, 524288)]
+    assert [Fraction(float(s)) for s in O.STEP_SLOPE] == exact
+    assert list(O.STEP_BITS) == [2, 2, 4, 8]
+
+
+@pytest.mark.parametrize("seed", range(60))
+def test_allocation_is_lagrangian_and_hull_optimal_bruteforce(seed):
+    r = _rng(100 + seed)
+    n = int(r.integers(1, 6))
+    c = np.exp(r.standard_normal(n) * 2).astype(np.float32)
+    if seed % 5 == 0:
+        c[0] = c[-1]            # equal costs
+    if seed % 7 == 0:
+        c[0] = 0                # a zero-cost unit
+    B = int(r.integers(0, 16 * n + 4))
+    bits, lam = O.lagrangian_allocate(c, B)
+    R = int(bits.sum())
+    assert R <= B
+    lamf = Fraction(lam)
+    # (1) every unit is at the exact per-unit Lagrangian argmin for lambda*
+    assert np.array_equal(bits, _exact_argmin_bits(c, lamf))
+    # (2) lambda* is minimal: any smaller candidate multiplier overshoots B
+    cands = sorted({Fraction(float(cu)) * Fraction(s) for cu in c for s in
+                    (Fraction(3, 8), Fraction(3, 32), Fraction(15, 1024), Fraction(255, 524288))} | {Fraction(0)})
+    smaller = [x for x in cands if x < lamf]
+    if smaller:
+        assert int(_exact_argmin_bits(c, smaller[-1]).sum()) > B
+    # (3) hull optimality: no assignment with rate <= R has lower distortion
+    dist = sum(Fraction(float(cu)) / (1 << int(b)) for cu, b in zip(c, bits))
+    best = min(sum(Fraction(float(cu)) / (1 << b) for cu, b in zip(c, a))
+               for a in itertools.product(BITS, repeat=n) if sum(a) <= R)
+    assert dist == best
+
+
+def test_allocation_special_cases():
+    c = np.array([1.0, 2.0, 0.5, 3.0], np.float32)
+    assert list(O.lagrangian_allocate(c, 64)[0]) == [16] * 4          # budget covers all 16
+    assert O.lagrangian_allocate(c, 64)[1] == 0.0
+    assert list(O.lagrangian_allocate(c, 1)[0]) == [0] * 4            # below one 2-bit step
+    assert list(O.lagrangian_allocate(c, 0)[0]) == [0] * 4
+    z = np.array([0.0, 1.0, -2.0, np.nan], np.float32)
+    assert list(O.lagrangian_allocate(z, 1000)[0]) == [0, 16, 0, 0]   # non-positive units evicted
+    e = np.full(6, 1.7, np.float32)
+    b, _ = O.lagrangian_allocate(e, 25)                               # equal costs, equal bits
+    assert len(set(b.tolist())) == 1
+    with pytest.raises(ValueError):
+        O.lagrangian_allocate(c, -1)
+
+
+def test_allocation_invariances():
+    r = _rng(11)
+    c = np.exp(r.standard_normal(500) * 1.5).astype(np.float32)
+    prev = None
+    for B in range(0, 4000, 97):
+        b, lam = O.lagrangian_allocate(c, B)
+        assert b.sum() <= B
+        if prev is not None:
+            assert np.all(b >= prev)                                   # monotone in the budget
+        prev = b
+        b2, lam2 = O.lagrangian_allocate(c * np.float32(8), B)         # exact power-of-two scaling
+        assert np.array_equal(b, b2) and lam2 == 8 * lam
+    b, _ = O.lagrangian_allocate(c, 1000)
+    order = np.argsort(c)
+    assert np.all(np.diff(b[order].astype(int)) >= 0)                  # monotone in the cost
+
+
+def test_allocation_mixes_eviction_and_quantization():
+    # the pages' central claim: the optimum mixes zero-bit and finite-bit units
+    w = np.exp(_rng(12).standard_normal(2000) * 2).astype(np.float32)
+    b, _ = O.lagrangian_allocate(w, 2 * 2000)
+    assert {0, 2, 4}.issubset(set(b.tolist()))
+
+
+# ---------------------------------------------------------------- quantizer
+
+def test_quantize_hand_worked_examples():
+    # scale = (2 - (-1)) / 3 = 1, zero = -1: (x - zero) = 0, 1, 1.5, 3
+    q, s, z = O.quantize(np.array([-1, 0, 0.5, 2], np.float16), 2)
+    assert list(q) == [0, 1, 2, 3] and s == 1 and z == -1        # 1.5 rounds to even 2
+    q, s, z = O.quantize(np.array([0, 0.5, 2.5, 3], np.float16), 2)
+    assert list(q) == [0, 0, 2, 3]                                  # 0.5 -> 0, 2.5 -> 2 (half-even)
+    q, s, z = O.quantize(np.array([5, 5, 5], np.float16), 4)
+    assert list(q) == [0, 0, 0] and s == 0 and z == 5               # zero range
+    # 8 bits over [0, 255]: identity codes
+    x = np.arange(256).astype(np.float16)
+    q, s, z = O.quantize(x, 8)
+    assert s == 1 and z == 0 and np.array_equal(q, np.arange(256))
+
+
+@pytest.mark.parametrize("b", [2, 4, 8])
+def test_quantize_properties(b):
+    r = _rng(20 + b)
+    X = (r.standard_normal((200, 37)) * r.choice([0.01, 1, 100], (200, 1))).astype(np.float16)
+    q, s, z = O.quantize(X, b)
+    assert q.max() <= (1 << b) - 1
+    assert np.all(q[np.arange(200), X.argmin(axis=1)] == 0)           # min maps to 0
+    assert np.all(z == X.min(axis=1))
+    xr = O.dequantize(q, s[:, None], z[:, None]).astype(np.float64)
+    err = np.abs(xr - X.astype(np.float64))
+    top = (z.astype(np.float64) + s.astype(np.float64) * ((1 << b) - 1))[:, None]
+    unclamped = X.astype(np.float64) <= top
+    bound = s.astype(np.float64)[:, None] / 2 * (1 + 1e-6) + np.abs(X.astype(np.float64)) * 2 ** -22
+    assert np.all(err[unclamped] <= bound[unclamped])
+
+
+def test_dequantize_is_single_rounding_fma():
+    r = _rng(30)
+    q = r.integers(0, 256, 3000)
+    s = (np.abs(r.standard_normal(3000)) * r.choice([1e-4, 1, 300], 3000)).astype(np.float16)
+    z = (r.standard_normal(3000) * 50).astype(np.float16)
+    got = O.dequantize(q, s, z)
+    for i in range(0, 3000, 7):
+        ex = Fraction(int(q[i])) * Fraction(float(s[i])) + Fraction(float(z[i]))
+        if ex >= 0:
+            ref = O.round_rational_to_f32(ex.numerator, ex.denominator) if ex else np.float32(0)
+        else:
+            ref = -O.round_rational_to_f32((-ex).numerator, (-ex).denominator)
+        assert got[i] == ref
+
+
+def test_pack_codes_bit_order():
+    assert O.pack_codes(np.array([1, 2, 3, 0]), 2)[0] == 1 | (2 << 2) | (3 << 4)
+    assert O.pack_codes(np.array([0xA, 0x5] + [0] * 6 + [0xF]), 4).tolist() == [0x5A, 0xF]
+    assert O.pack_codes(np.array([1, 2, 3, 4, 5]), 8).tolist() == [0x04030201, 5]
+    r = _rng(31)
+    for b in (2, 4, 8):
+        c = r.integers(0, 1 << b, (3, 77))
+        assert np.array_equal(O.unpack_codes(O.pack_codes(c, b), b, 77), c)
+
+
+# ---------------------------------------------------------------- format, decode
+
+def _layout(N, budget_v=None, budget_k=512, cap=16, S=1, L=1, Hq=4, Hkv=1):
+    return O.Layout(S, L, Hq, Hkv, 128, N, budget_v if budget_v is not None else 16 * N, budget_k, cap)
+
+
+def _sdpa(q, K, V):
+    """softmax(q K^T/sqrt(d)) V via torch SDPA in fp64 on the CPU."""
+    qt = torch.from_numpy(np.asarray(q, np.float64))[None, :, None, :]
+    kt = torch.from_numpy(np.asarray(K, np.float64))[None, None].expand(1, q.shape[0], -1, -1)
+    vt = torch.from_numpy(np.asarray(V, np.float64))[None, None].expand(1, q.shape[0], -1, -1)
+    return torch.nn.functional.scaled_dot_product_attention(qt, kt.contiguous(), vt.contiguous())[0, :, 0].numpy()
+
+
+def test_all_16_bit_cache_is_exact_attention_and_exact_bytes():
+    N = 70
+    r = _rng(40)
+    K = r.standard_normal((N, 128)).astype(np.float16)
+    V = r.standard_normal((N, 128)).astype(np.float16)
+    lay = _layout(N, budget_k=2048)
+    bt = np.full(N, 16, np.uint8)
+    bc = np.full(128, 16, np.uint8)
+    blob = O.pack_cache(lay, K[None, None, None], V[None, None, None], bt[None, None, None], bc[None, None, None])
+    Kh, Vh, pos, tb = O.unpack_segment(blob, lay, 0)
+    assert np.array_equal(pos, np.arange(N)) and np.all(tb == 16)
+    assert np.array_equal(Kh, K.astype(np.float32)) and np.array_equal(Vh, V.astype(np.float32))
+    # fp16 bytes verbatim: the V rows and the K records are the fp16 cache
+    ds = O.read_descriptor(blob, lay, 0)
+    assert blob[ds["off_v"][3]:ds["off_v"][3] + N * 256].tobytes() == V.tobytes()
+    assert blob[ds["off_krec"]:ds["off_krec"] + N * 256].tobytes() == K.tobytes()
+    assert O.segment_decode_bytes(blob, lay, 0, 0) == 2 * N * 128 * 2
+    q = r.standard_normal((1, 1, 4, 128)).astype(np.float16)
+    out = O.decode_step(blob, lay, q, 0)
+    np.testing.assert_allclose(out[0, 0], _sdpa(q[0, 0], K, V), rtol=1e-12, atol=1e-13)
+
+
+def test_eviction_only_cache_is_attention_over_kept_tokens():
+    N = 90
+    r = _rng(41)
+    K = r.standard_normal((N, 128)).astype(np.float16)
+    V = r.standard_normal((N, 128)).astype(np.float16)
+    bt = np.where(r.random(N) < 0.4, 16, 0).astype(np.uint8)
+    lay = _layout(N, budget_k=2048)
+    blob = O.pack_cache(lay, K[None, None, None], V[None, None, None], bt[None, None, None],
+                        np.full((1, 1, 1, 128), 16, np.uint8))
+    q = r.standard_normal((1, 1, 4, 128)).astype(np.float16)
+    out = O.decode_step(blob, lay, q, 0)
+    keep = np.nonzero(bt)[0]
+    np.testing.assert_allclose(out[0, 0], _sdpa(q[0, 0], K[keep], V[keep]), rtol=1e-12, atol=1e-13)
+
+
+def test_zero_bit_channels_contribute_nothing():
+    N = 40
+    r = _rng(42)
+    K = r.standard_normal((N, 128)).astype(np.float16)
+    V = r.standard_normal((N, 128)).astype(np.float16)
+    bc = np.where(np.arange(128) % 3 == 0, 0, 16).astype(np.uint8)
+    lay = _layout(N, budget_k=2048)
+    blob = O.pack_cache(lay, K[None, None, None], V[None, None, None], np.full((1, 1, 1, N), 16, np.uint8),
+                        bc[None, None, None])
+    Kh, _, _, _ = O.unpack_segment(blob, lay, 0)
+    Kz = K.astype(np.float32) * (bc > 0)
+    assert np.array_equal(Kh, Kz)
+    q = r.standard_normal((1, 1, 4, 128)).astype(np.float16)
+    np.testing.assert_allclose(O.decode_step(blob, lay, q, 0)[0, 0], _sdpa(q[0, 0], Kz, V), rtol=1e-12, atol=1e-13)
+
+
+def test_mixed_pack_roundtrip_and_group_order():
+    N = 200
+    r = _rng(43)
+    K = (r.standard_normal((N, 128)) * 3).astype(np.float16)
+    V = r.standard_normal((N, 128)).astype(np.float16)
+    bt = r.choice(np.array([0, 2, 4, 8, 16], np.uint8), N)
+    bc = r.choice(np.array([0, 2, 4, 8, 16], np.uint8), 128)
+    lay = _layout(N, budget_v=int(bt.sum()), budget_k=int(bc.sum()))
+    blob = O.pack_cache(lay, K[None, None, None], V[None, None, None], bt[None, None, None], bc[None, None, None])
+    Kh, Vh, pos, tb = O.unpack_segment(blob, lay, 0)
+    # kept order: bitwidth 2, 4, 8, 16, ascending positions inside each group
+    exp_pos = np.concatenate([np.nonzero(bt == b)[0] for b in (2, 4, 8, 16)])
+    assert np.array_equal(pos, exp_pos) and np.array_equal(tb, bt[exp_pos])
+    for i, t in enumerate(pos):
+        b = int(bt[t])
+        if b == 16:
+            assert np.array_equal(Vh[i], V[t].astype(np.float32))
+        else:
+            qv, s, z = O.quantize(V[t], b)
+            assert np.array_equal(Vh[i], O.dequantize(qv, s, z))
+        for cb in (8, 4, 2):
+            ch = np.nonzero(bc == cb)[0]
+            qk, s, z = O.quantize(K[t, ch], cb)
+            assert np.array_equal(Kh[i, ch], O.dequantize(qk, s, z))
+        assert np.array_equal(Kh[i, bc == 16], K[t, bc == 16].astype(np.float32))
+        assert np.all(Kh[i, bc == 0] == 0)
+    assert O.segment_payload_bytes(blob, lay, 0) * 8 == 128 * int(bt.sum()) + len(pos) * int(bc.sum())
+    # regions stay inside the slot and the slot inside the blob
+    ds = O.read_descriptor(blob, lay, 0)
+    assert ds["off_pos"] + 4 * len(pos) <= lay.slot_base(0) + lay.slot_bytes <= lay.cache_bytes
+
+
+def test_zone_c_append_and_zone_c_only_attention():
+    N = 30
+    r = _rng(44)
+    K = r.standard_normal((N, 128)).astype(np.float16)
+    V = r.standard_normal((N, 128)).astype(np.float16)
+    lay = _layout(N, cap=4)
+    blob = O.pack_cache(lay, K[None, None, None], V[None, None, None], np.zeros((1, 1, 1, N), np.uint8),
+                        np.zeros((1, 1, 1, 128), np.uint8))
+    q = r.standard_normal((1, 1, 4, 128)).astype(np.float16)
+    assert np.all(O.decode_step(blob, lay, q, 0) == 0)                 # nothing to attend to
+    kn = r.standard_normal((3, 1, 1, 1, 128)).astype(np.float16)
+    vn = r.standard_normal((3, 1, 1, 1, 128)).astype(np.float16)
+    for step in range(3):
+        out = O.decode_step(blob, lay, q, step, kn[step], vn[step])
+        ref = _sdpa(q[0, 0], kn[:step + 1, 0, 0, 0], vn[:step + 1, 0, 0, 0])
+        np.testing.assert_allclose(out[0, 0], ref, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(O.decode_step(blob, lay, q, 3)[0, 0], ref, rtol=1e-12, atol=1e-13)
+    with pytest.raises(ValueError):
+        O.decode_step(blob, lay, q, 4, kn[0], vn[0])
+
+
+def test_layout_bounds_hold_at_the_budget_extremes():
+    # a maximal allocation must fit its slot: all kept tokens at 2 bits, K bits
+    # spread to maximise padding
+    N = 64
+    for bk in (0, 1, 2, 3, 7, 30, 81, 100, 256, 2048, 5000):
+        lay = _layout(N, budget_v=2 * N, budget_k=bk)
+        bits_c = np.zeros(128, np.uint8)
+        left = min(bk, 2048)
+        for b in (16, 8, 4, 2):            # one channel of each width first, most padding
+            if left >= b and np.sum(bits_c == 0):
+                bits_c[np.nonzero(bits_c == 0)[0][0]] = b
+                left -= b
+        for i in np.nonzero(bits_c == 0)[0]:
+            if left >= 2:
+                bits_c[i] = 2
+                left -= 2
+        w16, w8, w4, w2, nm = O.record_words([int(np.sum(bits_c == b)) for b in (16, 8, 4, 2)])
+        assert 4 * (w16 + w8 + w4 + w2 + nm + 1) <= lay.rec_max
