@@ -1,0 +1,235 @@
+// C ABI of the RDKV library: host-side validation, layout arithmetic and
+// dispatch to the kernels.  Every entry point validates before enqueueing
+// anything; on an error nothing is enqueued and no output is touched.
+#include <algorithm>
+#include <cstring>
+
+#include "rdkv_internal.h"
+
+using namespace rdkv;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+rdkv_status check_dims(const rdkv_dims* d) {
+  if (!d) return RDKV_ERR_NULL;
+  if (d->reserved != 0) return RDKV_ERR_SHAPE;
+  if (d->n_tokens < 1 || d->n_seq < 1 || d->n_layers < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1)
+    return RDKV_ERR_SHAPE;
+  if (d->n_q_heads % d->n_kv_heads != 0) return RDKV_ERR_SHAPE;
+  if (d->head_dim != kHeadDim) return RDKV_ERR_UNSUPPORTED;
+  const int G = d->n_q_heads / d->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return RDKV_ERR_UNSUPPORTED;
+  // the exact channel variance keeps |sum X| < 2^63 and n^2 < 2^38 in integers
+  if (d->n_tokens > kMaxTokens) return RDKV_ERR_SHAPE;
+  return RDKV_OK;
+}
+
+rdkv_status check_layout(const rdkv_layout* lay) {
+  if (!lay) return RDKV_ERR_NULL;
+  rdkv_layout ref;
+  rdkv_status st = rdkv_layout_init(&lay->dims, lay->budget_v, lay->budget_k, lay->zone_c_capacity, &ref);
+  if (st != RDKV_OK) return st;
+  if (std::memcmp(&ref, lay, sizeof(ref)) != 0) return RDKV_ERR_SHAPE;  // not from rdkv_layout_init
+  return RDKV_OK;
+}
+
+rdkv_status hip_status(hipError_t e) { return e == hipSuccess ? RDKV_OK : RDKV_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t rdkv_version(void) { return (kFormatVersion << 16) | 1; }
+
+const char* rdkv_status_string(rdkv_status s) {
+  switch (s) {
+    case RDKV_OK: return "ok";
+    case RDKV_ERR_NULL: return "null pointer";
+    case RDKV_ERR_SHAPE: return "bad shape";
+    case RDKV_ERR_UNSUPPORTED: return "unsupported shape";
+    case RDKV_ERR_BUDGET: return "negative budget";
+    case RDKV_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case RDKV_ERR_WORKSPACE: return "buffer too small";
+    case RDKV_ERR_CAPACITY: return "zone C capacity exceeded";
+    case RDKV_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+rdkv_status rdkv_layout_init(const rdkv_dims* dims, int64_t budget_v, int64_t budget_k,
+                             int32_t zone_c_capacity, rdkv_layout* out) {
+  if (!out) return RDKV_ERR_NULL;
+  rdkv_status st = check_dims(dims);
+  if (st != RDKV_OK) return st;
+  if (budget_v < 0 || budget_k < 0) return RDKV_ERR_BUDGET;
+  if (zone_c_capacity < 0 || zone_c_capacity > (1 << 20)) return RDKV_ERR_SHAPE;
+  if (budget_v > (int64_t(1) << 40) || budget_k > (int64_t(1) << 40)) return RDKV_ERR_BUDGET;
+  rdkv_layout L;
+  std::memset(&L, 0, sizeof(L));
+  L.dims = *dims;
+  L.budget_v = budget_v;
+  L.budget_k = budget_k;
+  L.zone_c_capacity = zone_c_capacity;
+  const int64_t N = dims->n_tokens;
+  const int64_t cap = zone_c_capacity;
+  L.n_seg = int64_t(dims->n_seq) * dims->n_layers * dims->n_kv_heads;
+  L.nk_max = std::min<int64_t>(N, budget_v / 2);
+  const int64_t bk = std::min<int64_t>(budget_k, 16 * kHeadDim);
+  // each of the four record parts pads to a word: words <= bk/32 + 3.0625
+  L.rec_max = int32_t(4 * ((bk + 98) / 32 + 4));
+  const uint64_t zone_c = uint64_t(cap) * kHeadDim * 2;           // one of K_C, V_C
+  L.slot_off_v = align_up(2 * zone_c, kAlign);
+  const uint64_t v_res = align_up(uint64_t(std::min<int64_t>(16 * budget_v, 2 * kHeadDim * N)) + 768, kAlign);
+  L.slot_off_krec = L.slot_off_v + v_res;
+  L.slot_off_pos = L.slot_off_krec + align_up(uint64_t(L.nk_max) * L.rec_max, kAlign);
+  L.slot_bytes = L.slot_off_pos + align_up(uint64_t(4) * L.nk_max, kAlign);
+  L.slots_offset = align_up(kHeaderBytes + uint64_t(kDescBytes) * L.n_seg, kAlign);
+  L.cache_bytes = L.slots_offset + uint64_t(L.n_seg) * L.slot_bytes;
+  const int64_t tok_chunks = std::min<int64_t>(budget_v / (2 * kChunkTok2), N / 128) + 4;
+  L.max_chunks = int32_t(tok_chunks + cdiv(cap, kChunkRowsC));
+  const int G = dims->n_q_heads / dims->n_kv_heads;
+  L.decode_workspace_bytes = uint64_t(L.n_seg) * L.max_chunks * G * kPartialFloats * sizeof(float);
+  *out = L;
+  return RDKV_OK;
+}
+
+size_t rdkv_score_workspace_bytes(const rdkv_dims* dims) {
+  if (check_dims(dims) != RDKV_OK) return 0;
+  return score_workspace_bytes(dims->n_seq, dims->n_layers, dims->n_q_heads, dims->n_tokens);
+}
+
+rdkv_status rdkv_score(const rdkv_dims* dims, const void* Q, const void* K, const void* V,
+                       float* w_tok, float* var_tok, float* w_chan,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  rdkv_status st = check_dims(dims);
+  if (st != RDKV_OK) return st;
+  if (!Q || !K || !V || !w_tok || !var_tok || !w_chan || !workspace) return RDKV_ERR_NULL;
+  for (const void* p : {Q, K, V, (const void*)w_tok, (const void*)var_tok, (const void*)w_chan, (const void*)workspace})
+    if (!aligned16(p)) return RDKV_ERR_ALIGN;
+  if (workspace_bytes < rdkv_score_workspace_bytes(dims)) return RDKV_ERR_WORKSPACE;
+  ScoreParams p;
+  p.n_tokens = dims->n_tokens;
+  p.S = dims->n_seq;
+  p.L = dims->n_layers;
+  p.Hq = dims->n_q_heads;
+  p.Hkv = dims->n_kv_heads;
+  p.Q = static_cast<const __half*>(Q);
+  p.K = static_cast<const __half*>(K);
+  p.V = static_cast<const __half*>(V);
+  p.w_tok = w_tok;
+  p.var_tok = var_tok;
+  p.w_chan = w_chan;
+  p.lse = static_cast<float*>(workspace);
+  return hip_status(launch_score(p, stream));
+}
+
+rdkv_status rdkv_allocate(const rdkv_dims* dims, const float* w_tok, const float* var_tok,
+                          const float* w_chan, const void* K, int64_t budget_v, int64_t budget_k,
+                          uint8_t* bits_tok, uint8_t* bits_chan, float* var_chan, double* lambda,
+                          hipStream_t stream) {
+  rdkv_status st = check_dims(dims);
+  if (st != RDKV_OK) return st;
+  if (!w_tok || !var_tok || !w_chan || !K || !bits_tok || !bits_chan || !var_chan || !lambda)
+    return RDKV_ERR_NULL;
+  for (const void* p : {(const void*)w_tok, (const void*)var_tok, (const void*)w_chan, K, (const void*)bits_tok,
+                        (const void*)bits_chan, (const void*)var_chan, (const void*)lambda})
+    if (!aligned16(p)) return RDKV_ERR_ALIGN;
+  if (budget_v < 0 || budget_k < 0) return RDKV_ERR_BUDGET;
+  AllocParams p;
+  p.n_seg = int64_t(dims->n_seq) * dims->n_layers * dims->n_kv_heads;
+  p.n_tokens = dims->n_tokens;
+  p.w_tok = w_tok;
+  p.var_tok = var_tok;
+  p.w_chan = w_chan;
+  p.K = static_cast<const __half*>(K);
+  p.budget_v = budget_v;
+  p.budget_k = budget_k;
+  p.bits_tok = bits_tok;
+  p.bits_chan = bits_chan;
+  p.var_chan = var_chan;
+  p.lambda = lambda;
+  return hip_status(launch_allocate(p, stream));
+}
+
+rdkv_status rdkv_cache_init(const rdkv_layout* layout, void* cache, size_t cache_bytes, hipStream_t stream) {
+  rdkv_status st = check_layout(layout);
+  if (st != RDKV_OK) return st;
+  if (!cache) return RDKV_ERR_NULL;
+  if (!aligned16(cache)) return RDKV_ERR_ALIGN;
+  if (cache_bytes < layout->cache_bytes) return RDKV_ERR_WORKSPACE;
+  return hip_status(launch_cache_init(static_cast<uint8_t*>(cache), *layout, stream));
+}
+
+rdkv_status rdkv_pack(const rdkv_layout* layout, int32_t layer_begin, int32_t n_layers,
+                      const void* K, const void* V, const uint8_t* bits_tok, const uint8_t* bits_chan,
+                      void* cache, size_t cache_bytes, hipStream_t stream) {
+  rdkv_status st = check_layout(layout);
+  if (st != RDKV_OK) return st;
+  if (!K || !V || !bits_tok || !bits_chan || !cache) return RDKV_ERR_NULL;
+  for (const void* p : {K, V, (const void*)bits_tok, (const void*)bits_chan, (const void*)cache})
+    if (!aligned16(p)) return RDKV_ERR_ALIGN;
+  if (layer_begin < 0 || n_layers < 1 || int64_t(layer_begin) + n_layers > layout->dims.n_layers)
+    return RDKV_ERR_SHAPE;
+  if (cache_bytes < layout->cache_bytes) return RDKV_ERR_WORKSPACE;
+  PackParams p;
+  p.cache = static_cast<uint8_t*>(cache);
+  p.cache_bytes = cache_bytes;
+  p.lay = layout;
+  p.layer_begin = layer_begin;
+  p.n_layers_in = n_layers;
+  p.K = static_cast<const __half*>(K);
+  p.V = static_cast<const __half*>(V);
+  p.bits_tok = bits_tok;
+  p.bits_chan = bits_chan;
+  return hip_status(launch_pack(p, stream));
+}
+
+rdkv_status rdkv_decode(const rdkv_layout* layout, void* cache, size_t cache_bytes, int32_t c_len,
+                        const void* q, const void* k_new, const void* v_new, float* out,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  rdkv_status st = check_layout(layout);
+  if (st != RDKV_OK) return st;
+  if (!cache || !q || !out || !workspace) return RDKV_ERR_NULL;
+  if ((k_new == nullptr) != (v_new == nullptr)) return RDKV_ERR_NULL;
+  for (const void* p : {(const void*)cache, q, (const void*)out, (const void*)workspace})
+    if (!aligned16(p)) return RDKV_ERR_ALIGN;
+  if (k_new && (!aligned16(k_new) || !aligned16(v_new))) return RDKV_ERR_ALIGN;
+  if (cache_bytes < layout->cache_bytes || workspace_bytes < layout->decode_workspace_bytes)
+    return RDKV_ERR_WORKSPACE;
+  const int append = k_new != nullptr;
+  if (c_len < 0 || int64_t(c_len) + append > layout->zone_c_capacity) return RDKV_ERR_CAPACITY;
+  DecodeParams p;
+  p.cache = static_cast<uint8_t*>(cache);
+  p.cache_bytes = layout->cache_bytes;
+  p.n_seg = layout->n_seg;
+  p.nk_max = layout->nk_max;
+  p.max_chunks = layout->max_chunks;
+  p.rec_max = layout->rec_max;
+  p.group = layout->dims.n_q_heads / layout->dims.n_kv_heads;
+  p.c_len = c_len;
+  p.n_c = c_len + append;
+  p.append = append;
+  p.q = static_cast<const __half*>(q);
+  p.k_new = static_cast<const __half*>(k_new);
+  p.v_new = static_cast<const __half*>(v_new);
+  p.partials = static_cast<float*>(workspace);
+  p.out = out;
+  return hip_status(launch_decode(p, stream));
+}
+
+rdkv_status rdkv_unpack(const rdkv_layout* layout, const void* cache, size_t cache_bytes, int64_t seg,
+                        float* k_hat, float* v_hat, hipStream_t stream) {
+  rdkv_status st = check_layout(layout);
+  if (st != RDKV_OK) return st;
+  if (!cache || !k_hat || !v_hat) return RDKV_ERR_NULL;
+  for (const void* p : {cache, (const void*)k_hat, (const void*)v_hat})
+    if (!aligned16(p)) return RDKV_ERR_ALIGN;
+  if (seg < 0 || seg >= layout->n_seg) return RDKV_ERR_SHAPE;
+  if (cache_bytes < layout->cache_bytes) return RDKV_ERR_WORKSPACE;
+  return hip_status(launch_unpack(static_cast<const uint8_t*>(cache), layout->cache_bytes, *layout, seg,
+                                  k_hat, v_hat, stream));
+}
+
+}  // extern "C"

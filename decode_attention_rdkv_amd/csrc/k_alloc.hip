@@ -1,0 +1,236 @@
+// Lagrangian bit allocation (RDKV summary, section 2.1 objective, section 2.2
+// "reverse water-filling", stages 2 and 3).
+//
+// For one segment and one problem (V tokens, or K channels) with unit costs
+// c_u = fl32(w_u * sigma_u), unit u takes step j of the staircase
+// 0 -> 2 -> 4 -> 8 -> 16 bits iff c_u * k_j > lambda, k = (3/8, 3/32, 15/1024,
+// 255/524288); those are the exact per-bit gains of c * 2^-b, all five
+// bitwidths lie on the unit's lower convex hull, and the rule is the per-unit
+// argmin of c 2^-b + lambda b with ties at the lower bitwidth.  lambda* is the
+// smallest value whose total bits fit the budget.  The total is a step
+// function of lambda that only changes at the products c_u * k_j, which are
+// exact in fp64, so a bisection over the ordered bit patterns of non-negative
+// doubles (at most 63 halvings) lands exactly on lambda*.
+//
+// Stage 3's unit variance is the exact population variance of a K channel over
+// the kept tokens: fp16 values are integers times 2^-24, so the sums are done
+// in 64- and 128-bit integers and the quotient is rounded once to fp32.
+#include "rdkv_internal.h"
+
+namespace rdkv {
+namespace {
+
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / 64;
+
+__device__ inline int block_sum(int v, int* s_red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  v = wave_sum_i(v);
+  __syncthreads();
+  if (lane == 0) s_red[wave] = v;
+  __syncthreads();
+  int t = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) t += s_red[w];
+  return t;
+}
+
+__device__ inline float block_max(float v, float* s_red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  v = wave_max(v);
+  __syncthreads();
+  if (lane == 0) s_red[wave] = v;
+  __syncthreads();
+  float t = s_red[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) t = fmaxf(t, s_red[w]);
+  return t;
+}
+
+// Bits of one unit for a multiplier lambda: sum of the steps with c*k_j > lambda.
+__device__ inline int unit_bits(float c, double lam) {
+  const double cd = double(c);
+  return 2 * (cd * 0.375 > lam) + 2 * (cd * 0.09375 > lam) + 4 * (cd * (15.0 / 1024.0) > lam) +
+         8 * (cd * (255.0 / 524288.0) > lam);
+}
+
+// lambda* for the units this thread sees through `cost_of`, shared by the block.
+template <typename CostFn>
+__device__ double find_lambda(float cmax, int64_t budget, CostFn cost_of) {
+  if (int64_t(cost_of(0.0)) <= budget) return 0.0;
+  // invariant: cost(pattern lo) > budget >= cost(pattern hi)
+  uint64_t lo = 0;
+  uint64_t hi = __double_as_longlong(double(cmax) * 0.375);
+  while (hi - lo > 1) {
+    const uint64_t mid = lo + (hi - lo) / 2;
+    if (int64_t(cost_of(__longlong_as_double(mid))) <= budget)
+      hi = mid;
+    else
+      lo = mid;
+  }
+  return __longlong_as_double(hi);
+}
+
+struct AllocVArgs {
+  int64_t N;
+  const float* w_tok;
+  const float* var_tok;
+  int64_t budget;
+  uint8_t* bits_tok;
+  double* lambda;
+};
+
+__global__ __launch_bounds__(kThreads) void alloc_v_kernel(AllocVArgs a) {
+  __shared__ int s_i[kWaves];
+  __shared__ float s_f[kWaves];
+  const int64_t seg = blockIdx.x;
+  const float* w = a.w_tok + seg * a.N;
+  const float* v = a.var_tok + seg * a.N;
+  float cmax = 0.0f;
+  for (int64_t t = threadIdx.x; t < a.N; t += kThreads) {
+    const float c = __fmul_rn(w[t], v[t]);
+    if (c > cmax) cmax = c;
+  }
+  cmax = block_max(cmax, s_f);
+  auto cost = [&](double lam) {
+    int n = 0;
+    for (int64_t t = threadIdx.x; t < a.N; t += kThreads) n += unit_bits(__fmul_rn(w[t], v[t]), lam);
+    return block_sum(n, s_i);
+  };
+  const double lam = find_lambda(cmax, a.budget, cost);
+  for (int64_t t = threadIdx.x; t < a.N; t += kThreads)
+    a.bits_tok[seg * a.N + t] = uint8_t(unit_bits(__fmul_rn(w[t], v[t]), lam));
+  if (threadIdx.x == 0) a.lambda[2 * seg] = lam;
+}
+
+// ---------------------------------------------------------------- exact variance
+
+struct U128 {
+  uint64_t hi, lo;
+};
+__device__ inline U128 add128(U128 a, U128 b) {
+  U128 r;
+  r.lo = a.lo + b.lo;
+  r.hi = a.hi + b.hi + (r.lo < a.lo);
+  return r;
+}
+__device__ inline U128 sub128(U128 a, U128 b) {
+  U128 r;
+  r.lo = a.lo - b.lo;
+  r.hi = a.hi - b.hi - (a.lo < b.lo);
+  return r;
+}
+__device__ inline U128 mul64(uint64_t a, uint64_t b) { return U128{__umul64hi(a, b), a * b}; }
+__device__ inline U128 mul128_64(U128 a, uint64_t b) {   // low 128 bits of a*b
+  U128 r = mul64(a.lo, b);
+  r.hi += a.hi * b;
+  return r;
+}
+__device__ inline int bitlen64(uint64_t x) { return x ? 64 - __clzll(x) : 0; }
+
+// Nearest-even fp32 of (M / D) * 2^e2 for M < 2^127, 1 <= D < 2^62; the result
+// must be a normal fp32 (true for every variance of fp16 data).
+__device__ float round_div_to_f32(U128 M, uint64_t D, int e2) {
+  if (M.hi == 0 && M.lo == 0) return 0.0f;
+  const int mb = M.hi ? 64 + bitlen64(M.hi) : bitlen64(M.lo);
+  const int db = bitlen64(D);
+  const int s = 26 - (mb - db);   // floor(M 2^s / D) lies in [2^25, 2^27)
+  uint64_t num;
+  bool sticky = false;
+  if (s >= 0) {
+    num = M.lo << s;               // M < 2^(db + 26 - s) <= 2^64 here
+  } else {
+    const int r = -s;
+    if (r >= 64) {
+      num = M.hi >> (r - 64);
+      sticky = M.lo != 0 || (r > 64 && (M.hi & ((uint64_t(1) << (r - 64)) - 1)) != 0);
+    } else {
+      num = (M.lo >> r) | (M.hi << (64 - r));
+      sticky = (M.lo & ((uint64_t(1) << r) - 1)) != 0;
+    }
+  }
+  uint64_t q = num / D;
+  sticky = sticky || (num - q * D) != 0;
+  const int drop = bitlen64(q) - 24;
+  uint64_t m = q >> drop;
+  const uint64_t rb = q & ((uint64_t(1) << drop) - 1), half = uint64_t(1) << (drop - 1);
+  if (rb > half || (rb == half && (sticky || (m & 1)))) ++m;
+  int e = drop - s + e2;
+  if (m == (uint64_t(1) << 24)) {
+    m >>= 1;
+    ++e;
+  }
+  return ldexpf(float(m), e);
+}
+
+struct AllocKArgs {
+  int64_t N;
+  const __half* K;
+  const uint8_t* bits_tok;
+  const float* w_chan;
+  int64_t budget;
+  uint8_t* bits_chan;
+  float* var_chan;
+  double* lambda;
+};
+
+__global__ __launch_bounds__(kThreads) void alloc_k_kernel(AllocKArgs a) {
+  __shared__ int s_i[kWaves];
+  __shared__ float s_f[kWaves];
+  __shared__ int64_t s_s1[kThreads / kHeadDim][kHeadDim];
+  __shared__ U128 s_s2[kThreads / kHeadDim][kHeadDim];
+  const int64_t seg = blockIdx.x;
+  const int c = threadIdx.x & (kHeadDim - 1), tr = threadIdx.x / kHeadDim;
+  constexpr int kRows = kThreads / kHeadDim;
+  const __half* Kseg = a.K + seg * a.N * kHeadDim;
+  const uint8_t* bt = a.bits_tok + seg * a.N;
+
+  // exact sums of X = x * 2^24 and X^2 over kept tokens
+  int64_t s1 = 0;
+  U128 s2{0, 0};
+  int n = 0;
+  for (int64_t t = tr; t < a.N; t += kRows) {
+    if (bits_group(bt[t]) < 0) continue;
+    const double x = double(__half2float(Kseg[t * kHeadDim + c]));
+    const int64_t X = int64_t(x * 16777216.0);
+    s1 += X;
+    const uint64_t ax = uint64_t(X < 0 ? -X : X);
+    s2 = add128(s2, mul64(ax, ax));
+    ++n;
+  }
+  s_s1[tr][c] = s1;
+  s_s2[tr][c] = s2;
+  n = block_sum(n, s_i) / kHeadDim;   // every channel counted each kept token
+  __syncthreads();
+  float var = 0.0f, cc = 0.0f;
+  if (tr == 0) {
+    for (int r = 1; r < kRows; ++r) {
+      s1 += s_s1[r][c];
+      s2 = add128(s2, s_s2[r][c]);
+    }
+    if (n > 0) {
+      const uint64_t a1 = uint64_t(s1 < 0 ? -s1 : s1);
+      const U128 M = sub128(mul128_64(s2, uint64_t(n)), mul64(a1, a1));   // n*S2 - S1^2 >= 0
+      var = round_div_to_f32(M, uint64_t(n) * uint64_t(n), -48);
+    }
+    cc = __fmul_rn(a.w_chan[seg * kHeadDim + c], var);
+    a.var_chan[seg * kHeadDim + c] = var;
+  }
+  const float cmax = block_max(tr == 0 && cc > 0.0f ? cc : 0.0f, s_f);
+  auto cost = [&](double lam) { return block_sum(tr == 0 ? unit_bits(cc, lam) : 0, s_i); };
+  const double lam = find_lambda(cmax, a.budget, cost);
+  if (tr == 0) a.bits_chan[seg * kHeadDim + c] = uint8_t(unit_bits(cc, lam));
+  if (threadIdx.x == 0) a.lambda[2 * seg + 1] = lam;
+}
+
+}  // namespace
+
+hipError_t launch_allocate(const AllocParams& p, hipStream_t stream) {
+  AllocVArgs va{p.n_tokens, p.w_tok, p.var_tok, p.budget_v, p.bits_tok, p.lambda};
+  hipLaunchKernelGGL(alloc_v_kernel, dim3(unsigned(p.n_seg)), dim3(kThreads), 0, stream, va);
+  AllocKArgs ka{p.n_tokens, p.K, p.bits_tok, p.w_chan, p.budget_k, p.bits_chan, p.var_chan, p.lambda};
+  hipLaunchKernelGGL(alloc_k_kernel, dim3(unsigned(p.n_seg)), dim3(kThreads), 0, stream, ka);
+  return hipGetLastError();
+}
+
+}  // namespace rdkv

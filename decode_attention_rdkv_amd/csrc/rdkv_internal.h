@@ -1,0 +1,188 @@
+// Internal declarations shared by the RDKV HIP translation units.
+//
+// Format constants follow the packed-cache specification (header, 256-byte
+// descriptors, fixed-size slots; see the TriZone zones of the RDKV summary,
+// section 2.3).  Nothing here is exported from the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+#include "../../include/rdkv.h"
+
+namespace rdkv {
+
+constexpr int kHeadDim = 128;
+constexpr int64_t kMaxTokens = int64_t(1) << 19;   // prefill tokens per sequence
+constexpr uint32_t kMagic = 0x564B4452u;  // "RDKV" little-endian
+constexpr int kFormatVersion = 1;
+constexpr int kHeaderBytes = 256;
+constexpr int kDescBytes = 256;
+constexpr int kAlign = 256;
+
+// Descriptor field byte offsets.
+constexpr int kDescNTok = 0;      // i32[4]: kept tokens at 2, 4, 8, 16 bits
+constexpr int kDescNKept = 16;    // i32
+constexpr int kDescNChan = 20;    // i32[4]: channels at 16, 8, 4, 2 bits
+constexpr int kDescRec = 36;      // i32: K record bytes of a 2/4/8-bit token
+constexpr int kDescCap = 40;      // i32: zone C capacity
+constexpr int kDescFlags = 44;    // i32: bit 0 = allocation did not fit, packed empty
+constexpr int kDescOffV = 48;     // u64[4]
+constexpr int kDescOffKrec = 80;  // u64
+constexpr int kDescOffPos = 88;   // u64
+constexpr int kDescOffKc = 96;    // u64
+constexpr int kDescOffVc = 104;   // u64
+constexpr int kDescPerm = 128;    // u8[128]
+
+// Split-K chunking of decode: tokens per chunk for V groups of 2, 4, 8, 16
+// bits (equal V bytes per chunk), and zone-C rows per chunk.
+constexpr int kChunkTok2 = 1024;
+__host__ __device__ constexpr int chunk_tokens(int group) { return kChunkTok2 >> group; }
+constexpr int kChunkRowsC = 256;
+// Floats per (chunk, query head) partial: m, l, 2 pad, o[128].
+constexpr int kPartialFloats = 4 + kHeadDim;
+
+__host__ __device__ inline uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
+__host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Word counts of a K record from the channel counts (n16, n8, n4, n2).
+struct RecordShape {
+  int w16, w8, w4, w2, n_meta;
+  __host__ __device__ int words_a() const { return w16 + w8 + w4 + w2 + n_meta + 1; }
+};
+__host__ __device__ inline RecordShape record_shape(int n16, int n8, int n4, int n2) {
+  RecordShape r;
+  r.w16 = (n16 + 1) / 2;
+  r.w8 = (n8 + 3) / 4;
+  r.w4 = (n4 + 7) / 8;
+  r.w2 = (n2 + 15) / 16;
+  r.n_meta = (n8 > 0) + (n4 > 0) + (n2 > 0);
+  return r;
+}
+
+// Bitwidth of token group g (0..3 -> 2, 4, 8, 16).
+__host__ __device__ constexpr int group_bits(int g) { return 2 << g; }
+// Token group of a bitwidth, -1 for anything that is not 2, 4, 8 or 16.
+__host__ __device__ inline int bits_group(int b) {
+  return b == 2 ? 0 : b == 4 ? 1 : b == 8 ? 2 : b == 16 ? 3 : -1;
+}
+
+// A decode chunk: kind 0..3 = rows [start, end) of token group `kind`,
+// kind 4 = zone-C rows [start, end), kind -1 = no work.
+struct Chunk {
+  int kind, start, end;
+};
+__host__ __device__ inline Chunk chunk_of(const int n_tok[4], int n_c, int k) {
+  for (int g = 0; g < 4; ++g) {
+    const int T = chunk_tokens(g);
+    const int nch = (n_tok[g] + T - 1) / T;
+    if (k < nch) return Chunk{g, k * T, min(n_tok[g], (k + 1) * T)};
+    k -= nch;
+  }
+  const int nch = (n_c + kChunkRowsC - 1) / kChunkRowsC;
+  if (k < nch) return Chunk{4, k * kChunkRowsC, min(n_c, (k + 1) * kChunkRowsC)};
+  return Chunk{-1, 0, 0};
+}
+__host__ __device__ inline int chunk_count(const int n_tok[4], int n_c) {
+  int n = 0;
+  for (int g = 0; g < 4; ++g) n += (n_tok[g] + chunk_tokens(g) - 1) / chunk_tokens(g);
+  return n + (n_c + kChunkRowsC - 1) / kChunkRowsC;
+}
+
+// ------------------------------------------------------------ device helpers
+
+__device__ inline float half_lo(uint32_t w) { return __half2float(__ushort_as_half((unsigned short)(w & 0xffffu))); }
+__device__ inline float half_hi(uint32_t w) { return __half2float(__ushort_as_half((unsigned short)(w >> 16))); }
+
+template <typename T>
+__device__ inline T wave_shfl_xor(T v, int mask) {
+  return __shfl_xor(v, mask, 64);
+}
+__device__ inline float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+__device__ inline float wave_min(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fminf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+__device__ inline int wave_sum_i(int v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+// ------------------------------------------------------------ launchers
+// Each returns hipSuccess or the launch error; arguments are already validated.
+
+struct DecodeParams {
+  uint8_t* cache;
+  uint64_t cache_bytes;
+  int64_t n_seg;
+  int64_t nk_max;
+  int32_t max_chunks;
+  int32_t rec_max;
+  int32_t group;           // G = Hq / Hkv
+  int32_t c_len;           // zone-C rows present before this step
+  int32_t n_c;             // zone-C rows attended this step
+  int32_t append;          // 1: row c_len comes from k_new/v_new and is written
+  const __half* q;         // [n_seg][G][128]
+  const __half* k_new;     // [n_seg][128] or null
+  const __half* v_new;
+  float* partials;         // [n_seg][max_chunks][G][kPartialFloats]
+  float* out;              // [n_seg][G][128]
+};
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
+
+struct PackParams {
+  uint8_t* cache;
+  uint64_t cache_bytes;
+  const rdkv_layout* lay;  // host copy, fields are read on the host only
+  int32_t layer_begin, n_layers_in;
+  const __half* K;         // [S][n_layers_in][Hkv][N][128]
+  const __half* V;
+  const uint8_t* bits_tok; // [S][n_layers_in][Hkv][N]
+  const uint8_t* bits_chan;// [S][n_layers_in][Hkv][128]
+};
+hipError_t launch_cache_init(uint8_t* cache, const rdkv_layout& lay, hipStream_t stream);
+hipError_t launch_pack(const PackParams& p, hipStream_t stream);
+hipError_t launch_unpack(const uint8_t* cache, uint64_t cache_bytes, const rdkv_layout& lay, int64_t seg,
+                         float* k_hat, float* v_hat, hipStream_t stream);
+
+struct AllocParams {
+  int64_t n_seg, n_tokens;
+  const float* w_tok;
+  const float* var_tok;
+  const float* w_chan;
+  const __half* K;         // [n_seg][N][128]
+  int64_t budget_v, budget_k;
+  uint8_t* bits_tok;
+  uint8_t* bits_chan;
+  float* var_chan;
+  double* lambda;
+};
+hipError_t launch_allocate(const AllocParams& p, hipStream_t stream);
+
+struct ScoreParams {
+  int64_t n_tokens;
+  int32_t S, L, Hq, Hkv;
+  const __half* Q;
+  const __half* K;
+  const __half* V;
+  float* w_tok;
+  float* var_tok;
+  float* w_chan;
+  float* lse;              // workspace [S][L][Hq][N]
+};
+hipError_t launch_score(const ScoreParams& p, hipStream_t stream);
+size_t score_workspace_bytes(int64_t S, int64_t L, int64_t Hq, int64_t N);
+
+}  // namespace rdkv

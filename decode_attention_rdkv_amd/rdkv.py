@@ -1,0 +1,253 @@
+"""Python binding of librdkv: argument marshalling only.
+
+Every function here checks tensor placement, dtype and shape, passes raw
+device pointers and the current HIP stream to the C ABI declared in
+include/rdkv.h, and raises RdkvError on a non-OK status.  All computation
+happens in the library's HIP kernels; torch only provides device memory and
+the stream.  If the library is missing, load() raises: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "librdkv.so")
+HEAD_DIM = 128
+
+c_i32, c_i64, c_u64, c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_void_p
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("n_tokens", c_i64), ("n_seq", c_i32), ("n_layers", c_i32), ("n_q_heads", c_i32),
+                ("n_kv_heads", c_i32), ("head_dim", c_i32), ("reserved", c_i32)]
+
+
+class Layout(ctypes.Structure):
+    _fields_ = [("dims", Dims), ("budget_v", c_i64), ("budget_k", c_i64), ("n_seg", c_i64), ("nk_max", c_i64),
+                ("cache_bytes", c_u64), ("slots_offset", c_u64), ("slot_bytes", c_u64), ("slot_off_v", c_u64),
+                ("slot_off_krec", c_u64), ("slot_off_pos", c_u64), ("decode_workspace_bytes", c_u64),
+                ("zone_c_capacity", c_i32), ("rec_max", c_i32), ("max_chunks", c_i32), ("reserved", c_i32)]
+
+    @property
+    def group(self) -> int:
+        return self.dims.n_q_heads // self.dims.n_kv_heads
+
+
+STATUS = ["RDKV_OK", "RDKV_ERR_NULL", "RDKV_ERR_SHAPE", "RDKV_ERR_UNSUPPORTED", "RDKV_ERR_BUDGET",
+          "RDKV_ERR_ALIGN", "RDKV_ERR_WORKSPACE", "RDKV_ERR_CAPACITY", "RDKV_ERR_HIP"]
+
+# exported symbol -> (restype, argtypes)
+SIGNATURES = {
+    "rdkv_version": (c_i32, []),
+    "rdkv_status_string": (ctypes.c_char_p, [c_i32]),
+    "rdkv_layout_init": (c_i32, [ctypes.POINTER(Dims), c_i64, c_i64, c_i32, ctypes.POINTER(Layout)]),
+    "rdkv_score_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(Dims)]),
+    "rdkv_score": (c_i32, [ctypes.POINTER(Dims), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, ctypes.c_size_t, c_vp]),
+    "rdkv_allocate": (c_i32, [ctypes.POINTER(Dims), c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp,
+                              c_vp]),
+    "rdkv_cache_init": (c_i32, [ctypes.POINTER(Layout), c_vp, ctypes.c_size_t, c_vp]),
+    "rdkv_pack": (c_i32, [ctypes.POINTER(Layout), c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, ctypes.c_size_t, c_vp]),
+    "rdkv_decode": (c_i32, [ctypes.POINTER(Layout), c_vp, ctypes.c_size_t, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp,
+                            ctypes.c_size_t, c_vp]),
+    "rdkv_unpack": (c_i32, [ctypes.POINTER(Layout), c_vp, ctypes.c_size_t, c_i64, c_vp, c_vp, c_vp]),
+}
+
+
+class RdkvError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        name = STATUS[status] if 0 <= status < len(STATUS) else str(status)
+        super().__init__(f"{where}: {name}")
+        self.status = status
+        self.name = name
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load librdkv.so (built in-tree); raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m decode_attention_rdkv_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise RdkvError(status, where)
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor], dtype, shape=None, name="tensor") -> int:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t.data_ptr()
+
+
+def make_dims(n_seq, n_layers, n_q_heads, n_kv_heads, n_tokens, head_dim=HEAD_DIM) -> Dims:
+    return Dims(n_tokens=n_tokens, n_seq=n_seq, n_layers=n_layers, n_q_heads=n_q_heads, n_kv_heads=n_kv_heads,
+                head_dim=head_dim, reserved=0)
+
+
+def version() -> int:
+    return load().rdkv_version()
+
+
+def layout(dims: Dims, budget_v: int, budget_k: int, zone_c_capacity: int) -> Layout:
+    out = Layout()
+    _check(load().rdkv_layout_init(ctypes.byref(dims), budget_v, budget_k, zone_c_capacity, ctypes.byref(out)),
+           "rdkv_layout_init")
+    return out
+
+
+def score(dims: Dims, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, workspace: Optional[torch.Tensor] = None):
+    """Stage-1 weights; returns (w_tok, var_tok, w_chan) fp32 tensors."""
+    lib = load()
+    S, L, Hq, Hk, N = dims.n_seq, dims.n_layers, dims.n_q_heads, dims.n_kv_heads, dims.n_tokens
+    dev = Q.device
+    w_tok = torch.empty((S, L, Hk, N), dtype=torch.float32, device=dev)
+    var_tok = torch.empty((S, L, Hk, N), dtype=torch.float32, device=dev)
+    w_chan = torch.empty((S, L, Hk, HEAD_DIM), dtype=torch.float32, device=dev)
+    ws_bytes = lib.rdkv_score_workspace_bytes(ctypes.byref(dims))
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    _check(lib.rdkv_score(ctypes.byref(dims), _ptr(Q, torch.float16, (S, L, Hq, N, HEAD_DIM), "Q"),
+                          _ptr(K, torch.float16, (S, L, Hk, N, HEAD_DIM), "K"),
+                          _ptr(V, torch.float16, (S, L, Hk, N, HEAD_DIM), "V"),
+                          w_tok.data_ptr(), var_tok.data_ptr(), w_chan.data_ptr(),
+                          _ptr(workspace, torch.uint8, None, "workspace"), workspace.numel(), _stream()),
+           "rdkv_score")
+    return w_tok, var_tok, w_chan
+
+
+def allocate(dims: Dims, w_tok, var_tok, w_chan, K, budget_v: int, budget_k: int):
+    """Bit allocation; returns (bits_tok u8, bits_chan u8, var_chan f32, lambda f64 [...,2])."""
+    lib = load()
+    S, L, Hk, N = dims.n_seq, dims.n_layers, dims.n_kv_heads, dims.n_tokens
+    dev = K.device
+    bits_tok = torch.empty((S, L, Hk, N), dtype=torch.uint8, device=dev)
+    bits_chan = torch.empty((S, L, Hk, HEAD_DIM), dtype=torch.uint8, device=dev)
+    var_chan = torch.empty((S, L, Hk, HEAD_DIM), dtype=torch.float32, device=dev)
+    lam = torch.empty((S, L, Hk, 2), dtype=torch.float64, device=dev)
+    _check(lib.rdkv_allocate(ctypes.byref(dims), _ptr(w_tok, torch.float32, (S, L, Hk, N), "w_tok"),
+                             _ptr(var_tok, torch.float32, (S, L, Hk, N), "var_tok"),
+                             _ptr(w_chan, torch.float32, (S, L, Hk, HEAD_DIM), "w_chan"),
+                             _ptr(K, torch.float16, (S, L, Hk, N, HEAD_DIM), "K"), budget_v, budget_k,
+                             bits_tok.data_ptr(), bits_chan.data_ptr(), var_chan.data_ptr(), lam.data_ptr(),
+                             _stream()),
+           "rdkv_allocate")
+    return bits_tok, bits_chan, var_chan, lam
+
+
+def cache_init(lay: Layout, cache: Optional[torch.Tensor] = None, device="cuda") -> torch.Tensor:
+    """A zeroed cache blob with header and empty descriptors (uint8 tensor)."""
+    if cache is None:
+        cache = torch.empty(lay.cache_bytes, dtype=torch.uint8, device=device)
+    _check(load().rdkv_cache_init(ctypes.byref(lay), _ptr(cache, torch.uint8, None, "cache"), cache.numel(),
+                                  _stream()), "rdkv_cache_init")
+    return cache
+
+
+def pack(lay: Layout, cache: torch.Tensor, K, V, bits_tok, bits_chan, layer_begin: int = 0):
+    """Quantize and pack layers [layer_begin, layer_begin + K.shape[1]) into the cache."""
+    d = lay.dims
+    S, Lin, Hk, N = d.n_seq, K.shape[1], d.n_kv_heads, d.n_tokens
+    _check(load().rdkv_pack(ctypes.byref(lay), layer_begin, Lin,
+                            _ptr(K, torch.float16, (S, Lin, Hk, N, HEAD_DIM), "K"),
+                            _ptr(V, torch.float16, (S, Lin, Hk, N, HEAD_DIM), "V"),
+                            _ptr(bits_tok, torch.uint8, (S, Lin, Hk, N), "bits_tok"),
+                            _ptr(bits_chan, torch.uint8, (S, Lin, Hk, HEAD_DIM), "bits_chan"),
+                            _ptr(cache, torch.uint8, None, "cache"), cache.numel(), _stream()),
+           "rdkv_pack")
+
+
+def decode_workspace(lay: Layout, device="cuda") -> torch.Tensor:
+    return torch.empty(max(int(lay.decode_workspace_bytes), 16), dtype=torch.uint8, device=device)
+
+
+def decode(lay: Layout, cache: torch.Tensor, c_len: int, q, k_new=None, v_new=None,
+           workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One decode step; returns out fp32 [S][L][Hq][128]."""
+    d = lay.dims
+    S, L, Hq, Hk = d.n_seq, d.n_layers, d.n_q_heads, d.n_kv_heads
+    if workspace is None:
+        workspace = decode_workspace(lay, q.device)
+    if out is None:
+        out = torch.empty((S, L, Hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+    _check(load().rdkv_decode(ctypes.byref(lay), _ptr(cache, torch.uint8, None, "cache"), cache.numel(), c_len,
+                              _ptr(q, torch.float16, (S, L, Hq, HEAD_DIM), "q"),
+                              _ptr(k_new, torch.float16, (S, L, Hk, HEAD_DIM), "k_new"),
+                              _ptr(v_new, torch.float16, (S, L, Hk, HEAD_DIM), "v_new"),
+                              _ptr(out, torch.float32, (S, L, Hq, HEAD_DIM), "out"),
+                              _ptr(workspace, torch.uint8, None, "workspace"), workspace.numel(), _stream()),
+           "rdkv_decode")
+    return out
+
+
+def unpack(lay: Layout, cache: torch.Tensor, seg: int):
+    """Dequantized kept rows of one segment: (k_hat, v_hat) fp32 [nk_max][128]."""
+    nk = max(int(lay.nk_max), 1)
+    k_hat = torch.zeros((nk, HEAD_DIM), dtype=torch.float32, device=cache.device)
+    v_hat = torch.zeros((nk, HEAD_DIM), dtype=torch.float32, device=cache.device)
+    _check(load().rdkv_unpack(ctypes.byref(lay), _ptr(cache, torch.uint8, None, "cache"), cache.numel(), seg,
+                              k_hat.data_ptr(), v_hat.data_ptr(), _stream()), "rdkv_unpack")
+    return k_hat, v_hat
+
+
+# ---------------------------------------------------------------- descriptor readout
+
+DESC_BYTES = 256
+HEADER_BYTES = 256
+
+
+def descriptors(lay: Layout, cache: torch.Tensor):
+    """Per-segment counts read back from the blob (host numpy dict of arrays).
+
+    n_tok [n_seg][4] (kept tokens at 2/4/8/16 bits), n_chan [n_seg][4] (channels
+    at 16/8/4/2 bits), rec [n_seg] (record bytes of a 2/4/8-bit token), flags.
+    """
+    import numpy as np
+    raw = cache[HEADER_BYTES:HEADER_BYTES + DESC_BYTES * lay.n_seg].cpu().numpy().reshape(lay.n_seg, DESC_BYTES)
+    i32 = raw[:, :48].copy().view(np.int32)
+    return dict(n_tok=i32[:, 0:4].copy(), n_kept=i32[:, 4].copy(), n_chan=i32[:, 5:9].copy(),
+                rec=i32[:, 9].copy(), flags=i32[:, 11].copy())
+
+
+def decode_bytes(lay: Layout, desc: dict, n_c: int) -> dict:
+    """Bytes one decode step reads and writes, from the descriptors.
+
+    V rows (2/4/8-bit codes, fp16 rows), K records (codes, fp16 channels,
+    scale/zero words; 16-bit tokens' records have no V word), zone-C rows, the
+    queries and the fp32 outputs.
+    """
+    import numpy as np
+    n_tok = desc["n_tok"].astype(np.int64)
+    v = int((n_tok * np.array([32, 64, 128, 256])).sum())
+    k = int((desc["n_kept"].astype(np.int64) * desc["rec"]).sum() - 4 * n_tok[:, 3].sum())
+    zc = int(lay.n_seg * n_c * 2 * HEAD_DIM * 2)
+    d = lay.dims
+    qo = d.n_seq * d.n_layers * d.n_q_heads * HEAD_DIM * (2 + 4)
+    return dict(v=v, k=k, zone_c=zc, q_out=qo, total=v + k + zc + qo)

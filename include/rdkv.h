@@ -1,0 +1,185 @@
+/*
+ * rdkv.h -- C ABI of the RDKV hot path on MI355X (gfx950).
+ *
+ * RDKV compresses a KV cache after prefill by rate-distortion bit allocation:
+ * every V token and every K channel of a (sequence, layer, KV head) "segment"
+ * gets a bitwidth in {0, 2, 4, 8, 16}, 0 meaning eviction, chosen to minimise
+ * sum_u w_u sigma_u 2^-b_u under a bit budget.  Sources, cited by page and
+ * section: the gist.science technical summary "RDKV - KV 캐시 공동 추방 및 양자화를
+ * 위한 왜곡-비트 할당" (paper 2605.08317), sections 2.1 (weights and objective),
+ * 2.2 (allocation pipeline), 2.3 (TriZone packed decode); the aistudio.id article
+ * "Matematika KV Cache Compression", section "Solusi 3" (asymmetric quantizer).
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ * - Tensor arguments are DEVICE pointers into memory the caller owns; struct
+ *   arguments (rdkv_dims, rdkv_layout) are HOST pointers read during the call.
+ *   The library allocates nothing, keeps no global state and is reentrant.
+ * - Tensors are dense row-major; fp16 tensors are passed as const void*.
+ *   Every device pointer must be 16-byte aligned (else RDKV_ERR_ALIGN).
+ * - A call validates its arguments on the host, then enqueues kernels on
+ *   `stream` and returns without waiting.  On any error status nothing has
+ *   been enqueued and no output has been touched.  Inputs must stay alive
+ *   and unmodified until the enqueued work has finished.
+ * - Only head_dim == 128 and n_q_heads / n_kv_heads in {1, 2, 4, 8} are
+ *   supported (else RDKV_ERR_UNSUPPORTED).
+ * - Segment index: seg = (s * n_layers + l) * n_kv_heads + h.  Query head g
+ *   belongs to KV head g / (n_q_heads / n_kv_heads).
+ */
+#ifndef RDKV_H
+#define RDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum rdkv_status {
+  RDKV_OK = 0,
+  RDKV_ERR_NULL = 1,         /* a required pointer is NULL                          */
+  RDKV_ERR_SHAPE = 2,        /* a size is out of range or sizes are inconsistent    */
+  RDKV_ERR_UNSUPPORTED = 3,  /* head_dim != 128 or an unsupported GQA group size     */
+  RDKV_ERR_BUDGET = 4,       /* a bit budget is negative                             */
+  RDKV_ERR_ALIGN = 5,        /* a device pointer is not 16-byte aligned              */
+  RDKV_ERR_WORKSPACE = 6,    /* a workspace or cache buffer is smaller than required */
+  RDKV_ERR_CAPACITY = 7,     /* zone C has no room for the requested rows            */
+  RDKV_ERR_HIP = 8           /* a HIP runtime call failed                            */
+} rdkv_status;
+
+/* Shapes.  Q is [S][L][Hq][N][d], K and V are [S][L][Hkv][N][d]. */
+typedef struct rdkv_dims {
+  int64_t n_tokens;          /* N: prefill tokens per sequence, 1..524288          */
+  int32_t n_seq;             /* S >= 1                                              */
+  int32_t n_layers;          /* L >= 1                                              */
+  int32_t n_q_heads;         /* Hq, a multiple of Hkv                               */
+  int32_t n_kv_heads;        /* Hkv >= 1                                            */
+  int32_t head_dim;          /* d, must be 128                                      */
+  int32_t reserved;          /* must be 0                                           */
+} rdkv_dims;
+
+/* Sizes of a packed cache, all derived on the host from the dimensions and the
+ * budgets (section 2.2 "sum_u b_u <= B" bounds every region), so no size ever
+ * has to be read back from the device.  Filled by rdkv_layout_init; treat as
+ * read-only. */
+typedef struct rdkv_layout {
+  rdkv_dims dims;
+  int64_t budget_v;              /* B_V: bits per segment for the V-token problem   */
+  int64_t budget_k;              /* B_K: bits per segment for the K-channel problem */
+  int64_t n_seg;                 /* S * L * Hkv                                     */
+  int64_t nk_max;                /* bound on kept tokens per segment, min(N, B_V/2) */
+  uint64_t cache_bytes;          /* bytes of the packed cache blob                  */
+  uint64_t slots_offset;         /* blob offset of segment 0's slot                 */
+  uint64_t slot_bytes;           /* bytes per segment slot                          */
+  uint64_t slot_off_v;           /* slot-relative offset of the V rows              */
+  uint64_t slot_off_krec;        /* slot-relative offset of the K records           */
+  uint64_t slot_off_pos;         /* slot-relative offset of the kept positions      */
+  uint64_t decode_workspace_bytes; /* workspace rdkv_decode needs                   */
+  int32_t zone_c_capacity;       /* rows of zone C per segment                      */
+  int32_t rec_max;               /* bound on K record bytes                         */
+  int32_t max_chunks;            /* split-K partial slots per segment in decode     */
+  int32_t reserved;
+} rdkv_layout;
+
+/* Library version (format version in the high 16 bits, build in the low 16). */
+int32_t rdkv_version(void);
+
+/* Human-readable name of a status code (static string). */
+const char* rdkv_status_string(rdkv_status status);
+
+/* Fill *out for a cache of the given dimensions and budgets.  budget_v and
+ * budget_k are bits per segment (the "B" of section 2.1), >= 0; zone_c_capacity
+ * >= 0 rows.  Host only; touches no device. */
+rdkv_status rdkv_layout_init(const rdkv_dims* dims, int64_t budget_v, int64_t budget_k,
+                             int32_t zone_c_capacity, rdkv_layout* out);
+
+/* ---------------------------------------------------------------- stage 1
+ * Distortion weights after prefill (section 2.1, section 2.2 stage 1).
+ *   w_tok[seg][t]  = sum over the G query heads g of KV head h and query rows
+ *                    tau >= t of softmax_{t' <= tau}(Q[g,tau].K[t']/sqrt(d))[t]
+ *                    (causal prefill attention);              fp32 [S][L][Hkv][N]
+ *   var_tok[seg][t]= population variance of V[h,t,0:128];      fp32 [S][L][Hkv][N]
+ *   w_chan[seg][c] = ||Q[group,:,c]||_2 * ||K[h,:,c]||_2 / sqrt(d), the query
+ *                    rows of the G heads stacked;               fp32 [S][L][Hkv][128]
+ * Inputs Q, K, V are fp16 as above.  `workspace` must hold
+ * rdkv_score_workspace_bytes(dims) bytes (device). */
+size_t rdkv_score_workspace_bytes(const rdkv_dims* dims);
+rdkv_status rdkv_score(const rdkv_dims* dims, const void* Q, const void* K, const void* V,
+                       float* w_tok, float* var_tok, float* w_chan,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------- stages 2-3
+ * Lagrangian bit allocation (section 2.1 objective, section 2.2 stages 2 and 3).
+ * Per segment, V tokens first: unit cost c_t = fl32(w_tok*var_tok); token t gets
+ * the sum of the steps j (2,2,4,8 bits) with c_t*k_j > lambda_V, k = (3/8, 3/32,
+ * 15/1024, 255/524288), lambda_V the smallest value in {0} U {c_t*k_j} whose
+ * total is <= budget_v.  Then var_chan[c] = fl32(exact population variance of
+ * K[h,t,c] over the kept tokens b_t > 0) (0 if none), and the same rule over the
+ * 128 channels with c_c = fl32(w_chan*var_chan) and budget_k.
+ *   bits_tok  u8 [S][L][Hkv][N], bits_chan u8 [S][L][Hkv][128] (values 0,2,4,8,16)
+ *   var_chan  fp32 [S][L][Hkv][128]; lambda fp64 [S][L][Hkv][2] (lambda_V, lambda_K)
+ * K is the fp16 prefill K [S][L][Hkv][N][128].  Budgets are bits per segment.
+ * The allocation is exact: same inputs give the same bits on every run. */
+rdkv_status rdkv_allocate(const rdkv_dims* dims, const float* w_tok, const float* var_tok,
+                          const float* w_chan, const void* K, int64_t budget_v, int64_t budget_k,
+                          uint8_t* bits_tok, uint8_t* bits_chan, float* var_chan, double* lambda,
+                          hipStream_t stream);
+
+/* ---------------------------------------------------------------- packing
+ * TriZone packing (section 2.3; quantizer of "Solusi 3").  The blob format is
+ * specified in the repository's design notes; every offset inside the blob is
+ * relative to its base, so a blob may be copied to another address.
+ *
+ * rdkv_cache_init: zero `cache` and write the header and an empty descriptor
+ * for every segment (no kept tokens; zone C empty).  cache_bytes must be
+ * >= layout->cache_bytes.
+ *
+ * rdkv_pack: quantize and pack the segments of layers [layer_begin,
+ * layer_begin + n_layers) of every sequence.  K, V are fp16 [S][n_layers][Hkv]
+ * [N][128]; bits_tok u8 [S][n_layers][Hkv][N]; bits_chan u8 [S][n_layers][Hkv]
+ * [128].  A value other than 2, 4, 8 or 16 counts as 0 (token evicted,
+ * channel dropped).  The allocation must respect the layout's budgets (per
+ * segment, sum of bits_tok <= budget_v and sum of bits_chan <= budget_k); a
+ * segment whose allocation does not fit its slot is written empty with bit 0
+ * of its descriptor's flags word set, never past its slot.  Zone C of every
+ * packed segment is cleared. */
+rdkv_status rdkv_cache_init(const rdkv_layout* layout, void* cache, size_t cache_bytes,
+                            hipStream_t stream);
+rdkv_status rdkv_pack(const rdkv_layout* layout, int32_t layer_begin, int32_t n_layers,
+                      const void* K, const void* V, const uint8_t* bits_tok,
+                      const uint8_t* bits_chan, void* cache, size_t cache_bytes,
+                      hipStream_t stream);
+
+/* ---------------------------------------------------------------- decode
+ * One decode step over every segment of the cache (section 2.3: fused
+ * dequantization inside attention over zones A, B and C).
+ *   q      fp16 [S][L][Hq][128]   the step's queries
+ *   k_new, v_new fp16 [S][L][Hkv][128] or both NULL.  When given they are
+ *          written to zone-C row c_len of every segment and attended to, so
+ *          the step sees c_len + 1 zone-C rows; when NULL it sees c_len rows.
+ *          The caller advances its c_len after an appending step.
+ *   out    fp32 [S][L][Hq][128]   softmax(q.k_hat/sqrt(128)) v_hat over the kept
+ *          tokens and zone-C rows; evicted tokens are absent; 0-bit K channels
+ *          contribute 0; a segment with nothing to attend to gives 0.
+ * c_len + (append ? 1 : 0) must be <= zone_c_capacity (else RDKV_ERR_CAPACITY).
+ * `workspace` must hold layout->decode_workspace_bytes bytes.  The cache must
+ * have been initialised and packed with the same layout. */
+rdkv_status rdkv_decode(const rdkv_layout* layout, void* cache, size_t cache_bytes, int32_t c_len,
+                        const void* q, const void* k_new, const void* v_new, float* out,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Test support: dequantized kept rows of one segment, in kept order, with the
+ * fused multiply-add dequantization x_hat = fmaf(code, scale, zero).
+ *   k_hat, v_hat fp32 [nk_max][128] (rows past the segment's kept count are
+ *   not written); K channels with 0 bits are written as 0, in original channel
+ *   order. */
+rdkv_status rdkv_unpack(const rdkv_layout* layout, const void* cache, size_t cache_bytes,
+                        int64_t seg, float* k_hat, float* v_hat, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RDKV_H */

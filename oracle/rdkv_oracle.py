@@ -453,7 +453,7 @@ def pack_segment(lay: Layout, blob: np.ndarray, seg: int, Kh, Vh, bits_tok, bits
         if n_chan[j] == 0:
             continue
         q, sc, z = quantize(kp[:, c[j]:c[j + 1]], b)
-        parts.append(pack_codes(q, b).reshape(nk, -1))
+        parts.append(pack_codes(q, b))
         metas.append(half2_words(sc, z).reshape(nk, 1))
     parts += metas
     parts.append(np.concatenate(vmeta).reshape(nk, 1))

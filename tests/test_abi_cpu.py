@@ -1,0 +1,140 @@
+"""The C ABI on a machine without a GPU: library loading, exported symbols,
+host-side layout arithmetic against the oracle's independent implementation,
+and argument validation (every error is returned before anything is enqueued,
+so none of these calls reaches the HIP runtime)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle as O
+from decode_attention_rdkv_amd import rdkv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rdkv.h")
+
+OK, NULL, SHAPE, UNSUP, BUDGET, ALIGN, WORKSPACE, CAPACITY, HIP = range(9)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return rdkv.load()
+
+
+def test_every_declared_entry_point_is_exported(lib):
+    text = open(HEADER).read()
+    declared = set(re.findall(r"^\s*(?:[a-z_0-9]+\s*\*?\s+)+(rdkv_[a-z_0-9]+)\s*\(", text, re.M))
+    assert declared == set(rdkv.SIGNATURES), declared ^ set(rdkv.SIGNATURES)
+    for name in declared:
+        assert getattr(lib, name) is not None
+
+
+def test_status_strings(lib):
+    for s in range(9):
+        assert lib.rdkv_status_string(s)
+    assert lib.rdkv_version() >> 16 == O.VERSION
+
+
+SHAPES = [
+    # (S, L, Hq, Hkv, N, budget_v, budget_k, cap)
+    (1, 1, 4, 1, 1024, 4096, 512, 128),
+    (1, 1, 32, 8, 32768, 65536, 256, 128),
+    (1, 32, 32, 8, 131072, 83886, 81, 128),
+    (16, 1, 32, 8, 32768, 98304, 384, 256),
+    (1, 80, 64, 8, 262144, 524288, 256, 128),
+    (2, 3, 8, 8, 1, 0, 0, 0),
+    (1, 1, 2, 1, 77, 10 ** 9, 10 ** 6, 5),
+    (3, 2, 16, 2, 1000, 7, 3, 1),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_layout_matches_oracle(shape):
+    S, L, Hq, Hkv, N, bv, bk, cap = shape
+    lay = rdkv.layout(rdkv.make_dims(S, L, Hq, Hkv, N), bv, bk, cap)
+    ol = O.Layout(S, L, Hq, Hkv, 128, N, bv, bk, cap)
+    assert lay.n_seg == ol.n_seg
+    assert lay.nk_max == ol.nk_max
+    assert lay.rec_max == ol.rec_max
+    assert lay.slot_bytes == ol.slot_bytes
+    assert lay.slots_offset == ol.slots_offset
+    assert lay.cache_bytes == ol.cache_bytes
+    assert (lay.slot_off_v, lay.slot_off_krec, lay.slot_off_pos) == (ol.off_v, ol.off_krec, ol.off_pos)
+
+
+def _dims(**kw):
+    base = dict(n_seq=1, n_layers=1, n_q_heads=4, n_kv_heads=1, n_tokens=64)
+    base.update(kw)
+    return rdkv.make_dims(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=64), UNSUP),
+    (dict(n_q_heads=3, n_kv_heads=1), UNSUP),
+    (dict(n_q_heads=32, n_kv_heads=1), UNSUP),
+    (dict(n_q_heads=6, n_kv_heads=4), SHAPE),
+    (dict(n_tokens=0), SHAPE),
+    (dict(n_tokens=(1 << 19) + 1), SHAPE),
+    (dict(n_seq=0), SHAPE),
+])
+def test_layout_rejects_bad_dims(lib, kw, status):
+    out = rdkv.Layout()
+    assert lib.rdkv_layout_init(ctypes.byref(_dims(**kw)), 128, 128, 4, ctypes.byref(out)) == status
+
+
+def test_layout_rejects_bad_budgets_and_null(lib):
+    out = rdkv.Layout()
+    d = _dims()
+    assert lib.rdkv_layout_init(ctypes.byref(d), -1, 128, 4, ctypes.byref(out)) == BUDGET
+    assert lib.rdkv_layout_init(ctypes.byref(d), 128, -1, 4, ctypes.byref(out)) == BUDGET
+    assert lib.rdkv_layout_init(ctypes.byref(d), 128, 128, -1, ctypes.byref(out)) == SHAPE
+    assert lib.rdkv_layout_init(None, 128, 128, 4, ctypes.byref(out)) == NULL
+    assert lib.rdkv_layout_init(ctypes.byref(d), 128, 128, 4, None) == NULL
+
+
+A = 0x7f0000000000  # a 256-aligned stand-in address; never dereferenced (validation fails first)
+
+
+def test_score_validation(lib):
+    d = _dims()
+    ws = lib.rdkv_score_workspace_bytes(ctypes.byref(d))
+    assert ws > 0
+    assert lib.rdkv_score(ctypes.byref(d), None, A, A, A, A, A, A, ws, None) == NULL
+    assert lib.rdkv_score(ctypes.byref(d), A + 8, A, A, A, A, A, A, ws, None) == ALIGN
+    assert lib.rdkv_score(ctypes.byref(d), A, A, A, A, A, A, A, ws - 1, None) == WORKSPACE
+    assert lib.rdkv_score(ctypes.byref(_dims(head_dim=96)), A, A, A, A, A, A, A, ws, None) == UNSUP
+
+
+def test_allocate_validation(lib):
+    d = _dims()
+    args = [A] * 4
+    assert lib.rdkv_allocate(ctypes.byref(d), *args, -5, 8, A, A, A, A, None) == BUDGET
+    assert lib.rdkv_allocate(ctypes.byref(d), *args, 8, -5, A, A, A, A, None) == BUDGET
+    assert lib.rdkv_allocate(ctypes.byref(d), *args, 8, 8, A, None, A, A, None) == NULL
+    assert lib.rdkv_allocate(ctypes.byref(d), *args, 8, 8, A, A, A + 4, A, None) == ALIGN
+
+
+def test_cache_pack_decode_validation(lib):
+    lay = rdkv.layout(_dims(n_layers=2), 64, 32, 4)
+    nb = lay.cache_bytes
+    ws = lay.decode_workspace_bytes
+    assert lib.rdkv_cache_init(ctypes.byref(lay), A, nb - 1, None) == WORKSPACE
+    assert lib.rdkv_cache_init(ctypes.byref(lay), A + 2, nb, None) == ALIGN
+    assert lib.rdkv_cache_init(ctypes.byref(lay), None, nb, None) == NULL
+    bad = rdkv.Layout.from_buffer_copy(lay)
+    bad.cache_bytes -= 256                       # not a layout rdkv_layout_init produced
+    assert lib.rdkv_cache_init(ctypes.byref(bad), A, nb, None) == SHAPE
+    # pack: layer range
+    assert lib.rdkv_pack(ctypes.byref(lay), 1, 2, A, A, A, A, A, nb, None) == SHAPE
+    assert lib.rdkv_pack(ctypes.byref(lay), -1, 1, A, A, A, A, A, nb, None) == SHAPE
+    assert lib.rdkv_pack(ctypes.byref(lay), 0, 0, A, A, A, A, A, nb, None) == SHAPE
+    assert lib.rdkv_pack(ctypes.byref(lay), 0, 1, A, A, None, A, A, nb, None) == NULL
+    # decode: zone-C capacity, append pair, workspace
+    assert lib.rdkv_decode(ctypes.byref(lay), A, nb, 4, A, A, A, A, A, ws, None) == CAPACITY
+    assert lib.rdkv_decode(ctypes.byref(lay), A, nb, 5, A, None, None, A, A, ws, None) == CAPACITY
+    assert lib.rdkv_decode(ctypes.byref(lay), A, nb, -1, A, None, None, A, A, ws, None) == CAPACITY
+    assert lib.rdkv_decode(ctypes.byref(lay), A, nb, 0, A, A, None, A, A, ws, None) == NULL
+    assert lib.rdkv_decode(ctypes.byref(lay), A, nb, 0, A, None, None, A, A, ws - 1, None) == WORKSPACE
+    assert lib.rdkv_decode(ctypes.byref(lay), A, nb, 0, A + 8, None, None, A, A, ws, None) == ALIGN
+    assert lib.rdkv_unpack(ctypes.byref(lay), A, nb, lay.n_seg, A, A, None) == SHAPE

@@ -468,3 +468,21 @@ def test_layout_bounds_hold_at_the_budget_extremes():
                 left -= 2
         w16, w8, w4, w2, nm = O.record_words([int(np.sum(bits_c == b)) for b in (16, 8, 4, 2)])
         assert 4 * (w16 + w8 + w4 + w2 + nm + 1) <= lay.rec_max
+
+
+def test_empty_segment_with_channel_bits_packs_and_decodes():
+    N = 20
+    lay = _layout(N, budget_v=64, budget_k=64, cap=2)
+    r = _rng(45)
+    K = r.standard_normal((N, 128)).astype(np.float16)
+    V = r.standard_normal((N, 128)).astype(np.float16)
+    bc = np.zeros(128, np.uint8)
+    bc[:3] = [8, 4, 2]
+    blob = O.pack_cache(lay, K[None, None, None], V[None, None, None], np.zeros((1, 1, 1, N), np.uint8),
+                        bc[None, None, None])
+    ds = O.read_descriptor(blob, lay, 0)
+    assert ds["n_kept"] == 0 and ds["n_chan"] == [0, 1, 1, 1] and ds["rec"] == 4 * (3 + 3 + 1)
+    Kh, Vh, pos, tb = O.unpack_segment(blob, lay, 0)
+    assert Kh.shape == (0, 128) and pos.size == 0
+    q = r.standard_normal((1, 1, 4, 128)).astype(np.float16)
+    assert np.all(O.decode_step(blob, lay, q, 0) == 0)
