@@ -1,0 +1,271 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark of the RDKV hot path on one MI355X.
+
+Workload (default): the Llama-3.1-8B-shaped 32-layer cache at 131,072 tokens,
+batch 1, 8 KV heads x 32 query heads, head dim 128, compressed to ~2.5%
+retention (0.64 bits per unit on average).  Setup, untimed: for every layer,
+seeded synthetic Q/K/V are drawn on the GPU, scored (rdkv_score), allocated
+(rdkv_allocate) and packed (rdkv_pack) into one blob.  Timed: exactly
+--steps decode steps (rdkv_decode: append one token to zone C and attend over
+every layer's kept tokens), each bracketed by HIP events on the stream the
+kernel runs on, with the 256 MB last-level cache flushed between steps so
+every step streams the cache from HBM.
+
+Prints one JSON line: the metric of the decode step (us per token), the
+roofline of the decode kernel (algorithmic bytes from the packed descriptors /
+measured kernel time, against 8 TB/s), an fp16 full-cache decode on the same
+GPU for comparison, and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0
+MFMA_FP16_PEAK_TFS = 2500.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def build_cache(rdkv, synth, torch, w, lay, dims1, fp16_only=False):
+    """Score, allocate and pack every layer into a fresh cache; returns stats."""
+    cache = rdkv.cache_init(lay)
+    S = w.n_seq
+    ws = None
+    hist_tok = np.zeros(5, np.int64)
+    hist_chan = np.zeros(5, np.int64)
+    score_ms = 0.0
+    t0 = time.time()
+    for l in range(w.n_layers):
+        parts = [synth.prefill_layer(w, s, l, device="cuda") for s in range(S)]
+        K = torch.stack([p[1] for p in parts])[:, None].contiguous()
+        V = torch.stack([p[2] for p in parts])[:, None].contiguous()
+        if fp16_only:
+            del parts
+            bt = torch.full((S, 1, w.n_kv_heads, w.n_tokens), 16, dtype=torch.uint8, device="cuda")
+            bc = torch.full((S, 1, w.n_kv_heads, 128), 16, dtype=torch.uint8, device="cuda")
+        else:
+            Q = torch.stack([p[0] for p in parts])[:, None].contiguous()
+            del parts
+            if ws is None:
+                ws = torch.empty(rdkv.score_workspace_bytes(dims1), dtype=torch.uint8, device="cuda")
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            wt, vt, wc = rdkv.score(dims1, Q, K, V, workspace=ws)
+            e1.record()
+            del Q
+            bt, bc, _, _ = rdkv.allocate(dims1, wt, vt, wc, K, w.budget_v, w.budget_k)
+            e1.synchronize()
+            score_ms += e0.elapsed_time(e1)
+            del wt, vt, wc
+        rdkv.pack(lay, cache, K, V, bt, bc, layer_begin=l)
+        for i, b in enumerate((0, 2, 4, 8, 16)):
+            hist_tok[i] += int((bt == b).sum())
+            hist_chan[i] += int((bc == b).sum())
+        del K, V, bt, bc
+        if l % 8 == 7 or l == w.n_layers - 1:
+            torch.cuda.synchronize()
+            log(f"{'fp16 ' if fp16_only else ''}layer {l + 1}/{w.n_layers} packed, {time.time() - t0:.1f}s")
+    torch.cuda.synchronize()
+    return cache, dict(hist_tok=hist_tok, hist_chan=hist_chan, score_ms=score_ms, setup_s=time.time() - t0)
+
+
+def time_decode(rdkv, torch, lay, cache, q, kn, vn, steps, warmup, flush):
+    """Mean event time (ms) of one rdkv_decode call over `steps` steps."""
+    ws = rdkv.decode_workspace(lay)
+    out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    fbuf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda") if flush else None
+
+    def step():
+        # every step appends its token at zone-C row 0 and attends over the cache
+        rdkv.decode(lay, cache, 0, q, kn, vn, workspace=ws, out=out)
+
+    for i in range(warmup):
+        step()
+        if flush:
+            fbuf.fill_(i & 255)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record()
+        step()
+        ev[i][1].record()
+        if flush:
+            fbuf.fill_((i + 7) & 255)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = [a.elapsed_time(b) for a, b in ev]
+    del fbuf
+    return float(np.mean(ms)), float(np.median(ms)), wall, out
+
+
+def cpu_baseline(w, hist_tok, hist_chan, n_seg, n_c, sample_segments):
+    """The oracle's decode of one step, timed on `sample_segments` segments of
+    the same shape (kept-token mix and K-channel mix of the measured
+    allocation; seeded K/V), scaled to the whole step."""
+    import oracle as O
+    from decode_attention_rdkv_amd import synth
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:
+        threadpool_limits = None
+    N = w.n_tokens
+    p_tok = hist_tok / hist_tok.sum()
+    p_chan = hist_chan / hist_chan.sum()
+    lay = O.Layout(1, 1, w.group, 1, 128, N, w.budget_v, w.budget_k, w.zone_c_capacity)
+    total = 0.0
+    ctx = threadpool_limits(1) if threadpool_limits else None
+    if ctx:
+        ctx.__enter__()
+    try:
+        for s in range(sample_segments):
+            bt, bc = synth.random_bits(1, N, 1000 + s, tok_p=p_tok, chan_p=p_chan)
+            # keep the allocation inside the budget the layout was sized for
+            while int(bt.astype(np.int64).sum()) > w.budget_v:
+                nz = np.nonzero(bt[0])[0]
+                bt[0, nz[: len(nz) // 100 + 1]] = 0
+            while int(bc.astype(np.int64).sum()) > w.budget_k:
+                bc[0, np.nonzero(bc[0])[0][0]] = 0
+            K, V = synth.random_kv(1, N, 2000 + s)
+            blob = O.pack_cache(lay, K[None, None], V[None, None], bt[None, None], bc[None, None])
+            r = np.random.default_rng(s)
+            q = r.standard_normal((1, 1, w.group, 128)).astype(np.float16)
+            kn = r.standard_normal((1, 1, 1, 128)).astype(np.float16)
+            vn = r.standard_normal((1, 1, 1, 128)).astype(np.float16)
+            t0 = time.perf_counter()
+            O.decode_step(blob, lay, q, n_c - 1, kn, vn)
+            total += time.perf_counter() - t0
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    per_step_s = total / sample_segments * n_seg
+    return dict(value=per_step_s * 1e6 / w.n_seq, unit="us/token", cores=1, kind="oracle",
+                sample=f"{sample_segments} of {n_seg} segments (one KV head of one layer each, {N} tokens, "
+                       f"measured bit mix, seeded K/V), oracle decode step timed single-threaded and scaled "
+                       f"by {n_seg}/{sample_segments}; host has {os.cpu_count()} cpus")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama8b-32layer-n128k")
+    ap.add_argument("--no-flush", action="store_true", help="do not flush the last-level cache between steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fp16-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-segments", type=int, default=8)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after timing, run one plain 512 MiB device copy (for counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU: the RDKV hot path has no "
+                                   "cross-GPU exchange (segments are independent); run with --gpus 1"}))
+        sys.exit(2)
+
+    import torch
+    from decode_attention_rdkv_amd import rdkv, synth
+    rdkv.load()
+    if not torch.cuda.is_available():
+        raise SystemExit("no GPU visible")
+    w = synth.WORKLOADS[args.workload]
+    log(f"workload {w.name}: S={w.n_seq} L={w.n_layers} Hq={w.n_q_heads} Hkv={w.n_kv_heads} N={w.n_tokens} "
+        f"avg bits {w.avg_bits} (B_V={w.budget_v}, B_K={w.budget_k})")
+    dims = rdkv.make_dims(w.n_seq, w.n_layers, w.n_q_heads, w.n_kv_heads, w.n_tokens)
+    dims1 = rdkv.make_dims(w.n_seq, 1, w.n_q_heads, w.n_kv_heads, w.n_tokens)
+    lay = rdkv.layout(dims, w.budget_v, w.budget_k, w.zone_c_capacity)
+    cache, st = build_cache(rdkv, synth, torch, w, lay, dims1)
+    q, kn, vn = synth.decode_inputs(w, 0, device="cuda")
+    n_c = 1
+    ms_mean, ms_med, wall, out = time_decode(rdkv, torch, lay, cache, q, kn, vn, args.steps, args.warmup,
+                                             not args.no_flush)
+    if args.calibrate_copy:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    log(f"decode: mean {ms_mean * 1e3:.1f} us, median {ms_med * 1e3:.1f} us per step")
+
+    desc = rdkv.descriptors(lay, cache)
+    b = rdkv.decode_bytes(lay, desc, n_c)
+    algo = b["total"] + lay.n_seg * (256 + 2 * 128 * 2)        # descriptors read, new row written
+    achieved = algo / (ms_mean * 1e-3) / 1e9
+    N, d = w.n_tokens, 128
+    payload_bits = float((st["hist_tok"] * np.array([0, 2, 4, 8, 16])).sum() * d)
+    kept = int(desc["n_kept"].sum())
+    payload_bits += float(sum(int(desc["n_kept"][i]) * int((desc["n_chan"][i] * np.array([16, 8, 4, 2])).sum())
+                              for i in range(lay.n_seg)))
+    retention = payload_bits / (32.0 * N * d * lay.n_seg)
+    score_flops = 2 * w.n_layers * w.n_seq * w.n_q_heads * (N * (N + 1) / 2) * 2 * d   # two passes
+    result = {
+        "metric": "decode-attention us/token at 128K, 8B shape (one decode step over all layers)",
+        "value": round(ms_mean * 1e3 / w.n_seq, 3),
+        "unit": "us/token",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_mean, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded N(0,1) fp16 activations with heavy-hitter and sink logit bias, "
+                "scored, allocated and packed on the GPU)",
+        "config": {"workload": w.name, "n_seq": w.n_seq, "n_layers": w.n_layers, "n_q_heads": w.n_q_heads,
+                   "n_kv_heads": w.n_kv_heads, "head_dim": d, "n_tokens": N, "avg_bits": w.avg_bits,
+                   "budget_v": w.budget_v, "budget_k": w.budget_k, "zone_c_rows": n_c,
+                   "retention": round(retention, 5), "kept_tokens": kept,
+                   "bits_tok_hist_0_2_4_8_16": st["hist_tok"].tolist(),
+                   "bits_chan_hist_0_2_4_8_16": st["hist_chan"].tolist(),
+                   "llc_flushed_between_steps": not args.no_flush, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "decode_chunk_kernel", "algorithmic_bytes_per_launch": int(algo),
+                     "bytes_breakdown": {k: int(v) for k, v in b.items()},
+                     "kernel_ms": round(ms_mean, 5), "kernel_ms_median": round(ms_med, 5)},
+        "stages": {"setup_s": round(st["setup_s"], 2), "score_ms_total": round(st["score_ms"], 2),
+                   "score_tflops_executed": round(score_flops / (st["score_ms"] * 1e-3) / 1e12, 2)
+                   if st["score_ms"] > 0 else None,
+                   "score_mfma_frac": round(score_flops / (st["score_ms"] * 1e-3) / 1e12 / MFMA_FP16_PEAK_TFS, 4)
+                   if st["score_ms"] > 0 else None},
+        "wall_s_timed_loop": round(wall, 4),
+    }
+    del cache
+    torch.cuda.empty_cache()
+    if not args.no_fp16_baseline:
+        lay16 = rdkv.layout(dims, 16 * w.n_tokens, 16 * 128, w.zone_c_capacity)
+        cache16, _ = build_cache(rdkv, synth, torch, w, lay16, dims1, fp16_only=True)
+        ms16, med16, _, _ = time_decode(rdkv, torch, lay16, cache16, q, kn, vn, max(3, args.steps // 4), 2,
+                                        not args.no_flush)
+        b16 = rdkv.decode_bytes(lay16, rdkv.descriptors(lay16, cache16), n_c)
+        result["fp16_full_cache"] = {
+            "us_per_token": round(ms16 * 1e3 / w.n_seq, 2),
+            "achieved_GBs": round(b16["total"] / (ms16 * 1e-3) / 1e9, 1),
+            "bytes_per_step": int(b16["total"]),
+            "speedup_of_rdkv": round(ms16 / ms_mean, 2),
+            "note": "same kernel on an all-16-bit, nothing-evicted cache (the exact fp16 K/V bytes)"}
+        del cache16
+        torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        t0 = time.time()
+        result["cpu_baseline"] = cpu_baseline(w, st["hist_tok"], st["hist_chan"], lay.n_seg, n_c,
+                                              args.cpu_sample_segments)
+        log(f"cpu baseline {time.time() - t0:.1f}s")
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -17,8 +17,9 @@
 //     of a V row and accumulates p*(s*code + z) = (p*s)*code + p*z per head,
 //     the p*z part summed once per token.
 // The 4 waves' partials are merged in LDS and one (m, l, o[128]) per query
-// head is written for the chunk.  decode_merge_kernel combines the chunks of
-// each segment.  No MFMA: a product with 1..8 query rows per KV head is a
+// head is written for the chunk; the last workgroup of a segment to finish
+// (a counter in the segment's descriptor) combines the segment's chunks, so a
+// decode step is a single launch.  No MFMA: a product with 1..8 query rows per KV head is a
 // matrix-vector stream, bounded by HBM bandwidth and VALU issue.
 #include "rdkv_internal.h"
 
@@ -315,15 +316,42 @@ __device__ void run_rows(const DecodeParams& p, const SegInfo& si, int64_t seg, 
   }
 }
 
+// out[seg][g][c] = sum_k e^{m_k - M} o_k[c] / sum_k e^{m_k - M} l_k over the
+// segment's chunks, in chunk order (so the result does not depend on which
+// workgroup merges).
+template <int G>
+__device__ void merge_segment(const DecodeParams& p, int64_t seg, int n) {
+  const float* part = p.partials + int64_t(seg) * p.max_chunks * G * kPartialFloats;
+  for (int i = threadIdx.x; i < G * kHeadDim; i += kThreads) {
+    const int g = i / kHeadDim, c = i % kHeadDim;
+    float M = -INFINITY;
+    for (int k = 0; k < n; ++k) M = fmaxf(M, part[(k * G + g) * kPartialFloats]);
+    float L = 0.f, O = 0.f;
+    for (int k = 0; k < n; ++k) {
+      const float* pk = part + (k * G + g) * kPartialFloats;
+      const float f = exp2f(pk[0] - M);
+      L = fmaf(pk[1], f, L);
+      O = fmaf(pk[4 + c], f, O);
+    }
+    p.out[(seg * G + g) * kHeadDim + c] = L > 0.f ? O / L : 0.f;
+  }
+}
+
 template <int G>
 __global__ __launch_bounds__(kThreads) void decode_chunk_kernel(DecodeParams p) {
   __shared__ Smem<G> sm;
   const int64_t seg = blockIdx.x / p.max_chunks;
   const int k = int(blockIdx.x % p.max_chunks);
   const SegInfo si = load_segment(p, seg);
+  const int n_chunks = min(chunk_count(si.n_tok, zone_c_rows(p, si)), p.max_chunks);
   const Chunk ch = chunk_of(si.n_tok, zone_c_rows(p, si), k);
-  if (ch.kind < 0) return;
   const int tid = threadIdx.x;
+  if (ch.kind < 0) {
+    // a segment with nothing to attend to has a zero output
+    if (k == 0 && n_chunks == 0)
+      for (int i = tid; i < G * kHeadDim; i += kThreads) p.out[seg * G * kHeadDim + i] = 0.f;
+    return;
+  }
 
   // query of the G heads, in the channel order the rows use
   const uint8_t* perm = p.cache + kHeaderBytes + uint64_t(seg) * kDescBytes + kDescPerm;
@@ -384,27 +412,22 @@ __global__ __launch_bounds__(kThreads) void decode_chunk_kernel(DecodeParams p) 
       out[g * kPartialFloats + 1] = L;
     }
   }
-}
 
-template <int G>
-__global__ __launch_bounds__(kThreads) void decode_merge_kernel(DecodeParams p) {
-  const int64_t seg = blockIdx.x;
-  const SegInfo si = load_segment(p, seg);
-  const int n = min(chunk_count(si.n_tok, zone_c_rows(p, si)), p.max_chunks);
-  const float* part = p.partials + int64_t(seg) * p.max_chunks * G * kPartialFloats;
-  for (int i = threadIdx.x; i < G * kHeadDim; i += kThreads) {
-    const int g = i / kHeadDim, c = i % kHeadDim;
-    float M = -INFINITY;
-    for (int k = 0; k < n; ++k) M = fmaxf(M, part[(k * G + g) * kPartialFloats]);
-    float L = 0.f, O = 0.f;
-    for (int k = 0; k < n; ++k) {
-      const float* pk = part + (k * G + g) * kPartialFloats;
-      const float f = exp2f(pk[0] - M);
-      L = fmaf(pk[1], f, L);
-      O = fmaf(pk[4 + c], f, O);
-    }
-    p.out[(seg * G + g) * kHeadDim + c] = n > 0 && L > 0.f ? O / L : 0.f;
+  // The last workgroup of the segment to finish merges all its chunks.  The
+  // counter lives in the descriptor, is 0 between calls and is reset here.
+  __shared__ int s_last;
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    int* counter = reinterpret_cast<int*>(p.cache + kHeaderBytes + uint64_t(seg) * kDescBytes + kDescCounter);
+    const int prev = atomicAdd(counter, 1);
+    s_last = prev == n_chunks - 1;
+    if (s_last) atomicExch(counter, 0);
   }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  merge_segment<G>(p, seg, n_chunks);
 }
 
 template <int G>
@@ -412,7 +435,6 @@ hipError_t launch_g(const DecodeParams& p, hipStream_t stream) {
   const uint64_t grid = uint64_t(p.n_seg) * p.max_chunks;
   if (grid == 0) return hipSuccess;
   hipLaunchKernelGGL(decode_chunk_kernel<G>, dim3(unsigned(grid)), dim3(kThreads), 0, stream, p);
-  hipLaunchKernelGGL(decode_merge_kernel<G>, dim3(unsigned(p.n_seg)), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

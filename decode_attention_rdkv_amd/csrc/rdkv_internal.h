@@ -33,6 +33,7 @@ constexpr int kDescOffKrec = 80;  // u64
 constexpr int kDescOffPos = 88;   // u64
 constexpr int kDescOffKc = 96;    // u64
 constexpr int kDescOffVc = 104;   // u64
+constexpr int kDescCounter = 112;  // i32: decode chunk counter, 0 between calls
 constexpr int kDescPerm = 128;    // u8[128]
 
 // Split-K chunking of decode: tokens per chunk for V groups of 2, 4, 8, 16

@@ -123,6 +123,10 @@ def layout(dims: Dims, budget_v: int, budget_k: int, zone_c_capacity: int) -> La
     return out
 
 
+def score_workspace_bytes(dims: Dims) -> int:
+    return int(load().rdkv_score_workspace_bytes(ctypes.byref(dims)))
+
+
 def score(dims: Dims, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, workspace: Optional[torch.Tensor] = None):
     """Stage-1 weights; returns (w_tok, var_tok, w_chan) fp32 tensors."""
     lib = load()
