@@ -79,33 +79,48 @@ def build_cache(rdkv, synth, torch, w, lay, dims1, fp16_only=False):
 
 
 def time_decode(rdkv, torch, lay, cache, q, kn, vn, steps, warmup, flush):
-    """Mean event time (ms) of one rdkv_decode call over `steps` steps."""
+    """Per-step event times (ms) of the two decode phases over `steps` steps.
+
+    Each step is rdkv_decode_partials (the chunk kernel: append + split-K
+    partials) then rdkv_decode_merge, i.e. exactly rdkv_decode, with an event
+    before, between and after on the stream both kernels run on.
+    """
     ws = rdkv.decode_workspace(lay)
     out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
     fbuf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda") if flush else None
+    n_c = 1
 
     def step():
         # every step appends its token at zone-C row 0 and attends over the cache
-        rdkv.decode(lay, cache, 0, q, kn, vn, workspace=ws, out=out)
+        rdkv.decode_partials(lay, cache, 0, q, kn, vn, workspace=ws)
+
+    def merge():
+        rdkv.decode_merge(lay, cache, n_c, ws, out)
 
     for i in range(warmup):
         step()
+        merge()
         if flush:
             fbuf.fill_(i & 255)
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
         ev[i][0].record()
         step()
         ev[i][1].record()
+        merge()
+        ev[i][2].record()
         if flush:
             fbuf.fill_((i + 7) & 255)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = [a.elapsed_time(b) for a, b in ev]
+    chunk = np.array([a.elapsed_time(b) for a, b, _ in ev])
+    merge_ms = np.array([b.elapsed_time(c) for _, b, c in ev])
+    total = np.array([a.elapsed_time(c) for a, _, c in ev])
     del fbuf
-    return float(np.mean(ms)), float(np.median(ms)), wall, out
+    return dict(step=float(total.mean()), step_median=float(np.median(total)), chunk=float(chunk.mean()),
+                chunk_median=float(np.median(chunk)), merge=float(merge_ms.mean()), wall=wall, out=out)
 
 
 def cpu_baseline(w, hist_tok, hist_chan, n_seg, n_c, sample_segments):
@@ -188,8 +203,8 @@ def main():
     cache, st = build_cache(rdkv, synth, torch, w, lay, dims1)
     q, kn, vn = synth.decode_inputs(w, 0, device="cuda")
     n_c = 1
-    ms_mean, ms_med, wall, out = time_decode(rdkv, torch, lay, cache, q, kn, vn, args.steps, args.warmup,
-                                             not args.no_flush)
+    tm = time_decode(rdkv, torch, lay, cache, q, kn, vn, args.steps, args.warmup, not args.no_flush)
+    ms_mean, ms_med, wall = tm["step"], tm["step_median"], tm["wall"]
     if args.calibrate_copy:
         src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
@@ -197,12 +212,13 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    log(f"decode: mean {ms_mean * 1e3:.1f} us, median {ms_med * 1e3:.1f} us per step")
+    log(f"decode: step mean {ms_mean * 1e3:.1f} us (chunk kernel {tm['chunk'] * 1e3:.1f} us, "
+        f"merge {tm['merge'] * 1e3:.1f} us)")
 
     desc = rdkv.descriptors(lay, cache)
     b = rdkv.decode_bytes(lay, desc, n_c)
     algo = b["total"] + lay.n_seg * (256 + 2 * 128 * 2)        # descriptors read, new row written
-    achieved = algo / (ms_mean * 1e-3) / 1e9
+    achieved = algo / (tm["chunk"] * 1e-3) / 1e9
     N, d = w.n_tokens, 128
     payload_bits = float((st["hist_tok"] * np.array([0, 2, 4, 8, 16])).sum() * d)
     kept = int(desc["n_kept"].sum())
@@ -235,7 +251,9 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "kernel": "decode_chunk_kernel", "algorithmic_bytes_per_launch": int(algo),
                      "bytes_breakdown": {k: int(v) for k, v in b.items()},
-                     "kernel_ms": round(ms_mean, 5), "kernel_ms_median": round(ms_med, 5)},
+                     "kernel_ms": round(tm["chunk"], 5), "kernel_ms_median": round(tm["chunk_median"], 5),
+                     "merge_kernel_ms": round(tm["merge"], 5),
+                     "step_GBs": round(algo / (ms_mean * 1e-3) / 1e9, 1)},
         "stages": {"setup_s": round(st["setup_s"], 2), "score_ms_total": round(st["score_ms"], 2),
                    "score_tflops_executed": round(score_flops / (st["score_ms"] * 1e-3) / 1e12, 2)
                    if st["score_ms"] > 0 else None,
@@ -248,8 +266,8 @@ def main():
     if not args.no_fp16_baseline:
         lay16 = rdkv.layout(dims, 16 * w.n_tokens, 16 * 128, w.zone_c_capacity)
         cache16, _ = build_cache(rdkv, synth, torch, w, lay16, dims1, fp16_only=True)
-        ms16, med16, _, _ = time_decode(rdkv, torch, lay16, cache16, q, kn, vn, max(3, args.steps // 4), 2,
-                                        not args.no_flush)
+        t16 = time_decode(rdkv, torch, lay16, cache16, q, kn, vn, max(3, args.steps // 4), 2, not args.no_flush)
+        ms16 = t16["step"]
         b16 = rdkv.decode_bytes(lay16, rdkv.descriptors(lay16, cache16), n_c)
         result["fp16_full_cache"] = {
             "us_per_token": round(ms16 * 1e3 / w.n_seq, 2),

@@ -37,6 +37,45 @@ rdkv_status check_layout(const rdkv_layout* lay) {
 
 rdkv_status hip_status(hipError_t e) { return e == hipSuccess ? RDKV_OK : RDKV_ERR_HIP; }
 
+DecodeParams base_params(const rdkv_layout* layout, void* cache, int n_c, int c_len, int append) {
+  DecodeParams p{};
+  p.cache = static_cast<uint8_t*>(cache);
+  p.cache_bytes = layout->cache_bytes;
+  p.n_seg = layout->n_seg;
+  p.nk_max = layout->nk_max;
+  p.max_chunks = layout->max_chunks;
+  p.rec_max = layout->rec_max;
+  p.group = layout->dims.n_q_heads / layout->dims.n_kv_heads;
+  p.c_len = c_len;
+  p.n_c = n_c;
+  p.append = append;
+  return p;
+}
+
+// Validation shared by rdkv_decode and rdkv_decode_partials.
+rdkv_status decode_params(const rdkv_layout* layout, void* cache, size_t cache_bytes, int32_t c_len, const void* q,
+                          const void* k_new, const void* v_new, void* workspace, size_t workspace_bytes,
+                          DecodeParams* out) {
+  rdkv_status st = check_layout(layout);
+  if (st != RDKV_OK) return st;
+  if (!cache || !q || !workspace) return RDKV_ERR_NULL;
+  if ((k_new == nullptr) != (v_new == nullptr)) return RDKV_ERR_NULL;
+  for (const void* ptr : {(const void*)cache, q, (const void*)workspace})
+    if (!aligned16(ptr)) return RDKV_ERR_ALIGN;
+  if (k_new && (!aligned16(k_new) || !aligned16(v_new))) return RDKV_ERR_ALIGN;
+  if (cache_bytes < layout->cache_bytes || workspace_bytes < layout->decode_workspace_bytes)
+    return RDKV_ERR_WORKSPACE;
+  const int append = k_new != nullptr;
+  if (c_len < 0 || int64_t(c_len) + append > layout->zone_c_capacity) return RDKV_ERR_CAPACITY;
+  DecodeParams p = base_params(layout, cache, c_len + append, c_len, append);
+  p.q = static_cast<const __half*>(q);
+  p.k_new = static_cast<const __half*>(k_new);
+  p.v_new = static_cast<const __half*>(v_new);
+  p.partials = static_cast<float*>(workspace);
+  *out = p;
+  return RDKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -186,37 +225,45 @@ rdkv_status rdkv_pack(const rdkv_layout* layout, int32_t layer_begin, int32_t n_
   return hip_status(launch_pack(p, stream));
 }
 
+rdkv_status rdkv_decode_partials(const rdkv_layout* layout, void* cache, size_t cache_bytes, int32_t c_len,
+                                 const void* q, const void* k_new, const void* v_new,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  DecodeParams p;
+  rdkv_status st = decode_params(layout, cache, cache_bytes, c_len, q, k_new, v_new, workspace, workspace_bytes, &p);
+  if (st != RDKV_OK) return st;
+  if (!q) return RDKV_ERR_NULL;
+  return hip_status(launch_decode_chunks(p, stream));
+}
+
+rdkv_status rdkv_decode_merge(const rdkv_layout* layout, const void* cache, size_t cache_bytes,
+                              int32_t zone_c_rows, float* out, const void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+  rdkv_status st = check_layout(layout);
+  if (st != RDKV_OK) return st;
+  if (!cache || !out || !workspace) return RDKV_ERR_NULL;
+  for (const void* ptr : {cache, (const void*)out, workspace})
+    if (!aligned16(ptr)) return RDKV_ERR_ALIGN;
+  if (cache_bytes < layout->cache_bytes || workspace_bytes < layout->decode_workspace_bytes)
+    return RDKV_ERR_WORKSPACE;
+  if (zone_c_rows < 0 || zone_c_rows > layout->zone_c_capacity) return RDKV_ERR_CAPACITY;
+  DecodeParams p = base_params(layout, const_cast<void*>(cache), zone_c_rows, 0, 0);
+  p.partials = static_cast<float*>(const_cast<void*>(workspace));
+  p.out = out;
+  return hip_status(launch_decode_merge(p, stream));
+}
+
 rdkv_status rdkv_decode(const rdkv_layout* layout, void* cache, size_t cache_bytes, int32_t c_len,
                         const void* q, const void* k_new, const void* v_new, float* out,
                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  rdkv_status st = check_layout(layout);
-  if (st != RDKV_OK) return st;
-  if (!cache || !q || !out || !workspace) return RDKV_ERR_NULL;
-  if ((k_new == nullptr) != (v_new == nullptr)) return RDKV_ERR_NULL;
-  for (const void* p : {(const void*)cache, q, (const void*)out, (const void*)workspace})
-    if (!aligned16(p)) return RDKV_ERR_ALIGN;
-  if (k_new && (!aligned16(k_new) || !aligned16(v_new))) return RDKV_ERR_ALIGN;
-  if (cache_bytes < layout->cache_bytes || workspace_bytes < layout->decode_workspace_bytes)
-    return RDKV_ERR_WORKSPACE;
-  const int append = k_new != nullptr;
-  if (c_len < 0 || int64_t(c_len) + append > layout->zone_c_capacity) return RDKV_ERR_CAPACITY;
   DecodeParams p;
-  p.cache = static_cast<uint8_t*>(cache);
-  p.cache_bytes = layout->cache_bytes;
-  p.n_seg = layout->n_seg;
-  p.nk_max = layout->nk_max;
-  p.max_chunks = layout->max_chunks;
-  p.rec_max = layout->rec_max;
-  p.group = layout->dims.n_q_heads / layout->dims.n_kv_heads;
-  p.c_len = c_len;
-  p.n_c = c_len + append;
-  p.append = append;
-  p.q = static_cast<const __half*>(q);
-  p.k_new = static_cast<const __half*>(k_new);
-  p.v_new = static_cast<const __half*>(v_new);
-  p.partials = static_cast<float*>(workspace);
+  rdkv_status st = decode_params(layout, cache, cache_bytes, c_len, q, k_new, v_new, workspace, workspace_bytes, &p);
+  if (st != RDKV_OK) return st;
+  if (!out) return RDKV_ERR_NULL;
+  if (!aligned16(out)) return RDKV_ERR_ALIGN;
   p.out = out;
-  return hip_status(launch_decode(p, stream));
+  hipError_t e = launch_decode_chunks(p, stream);
+  if (e == hipSuccess) e = launch_decode_merge(p, stream);
+  return hip_status(e);
 }
 
 rdkv_status rdkv_unpack(const rdkv_layout* layout, const void* cache, size_t cache_bytes, int64_t seg,

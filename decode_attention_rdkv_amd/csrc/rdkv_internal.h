@@ -9,7 +9,7 @@
 #include <hip/hip_fp16.h>
 #include <stdint.h>
 
-#include "../../include/rdkv.h"
+#include "rdkv.h"
 
 namespace rdkv {
 
@@ -33,7 +33,6 @@ constexpr int kDescOffKrec = 80;  // u64
 constexpr int kDescOffPos = 88;   // u64
 constexpr int kDescOffKc = 96;    // u64
 constexpr int kDescOffVc = 104;   // u64
-constexpr int kDescCounter = 112;  // i32: decode chunk counter, 0 between calls
 constexpr int kDescPerm = 128;    // u8[128]
 
 // Split-K chunking of decode: tokens per chunk for V groups of 2, 4, 8, 16
@@ -141,7 +140,8 @@ struct DecodeParams {
   float* partials;         // [n_seg][max_chunks][G][kPartialFloats]
   float* out;              // [n_seg][G][128]
 };
-hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_decode_chunks(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_decode_merge(const DecodeParams& p, hipStream_t stream);
 
 struct PackParams {
   uint8_t* cache;

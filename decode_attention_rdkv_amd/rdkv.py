@@ -53,6 +53,10 @@ SIGNATURES = {
     "rdkv_pack": (c_i32, [ctypes.POINTER(Layout), c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, ctypes.c_size_t, c_vp]),
     "rdkv_decode": (c_i32, [ctypes.POINTER(Layout), c_vp, ctypes.c_size_t, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp,
                             ctypes.c_size_t, c_vp]),
+    "rdkv_decode_partials": (c_i32, [ctypes.POINTER(Layout), c_vp, ctypes.c_size_t, c_i32, c_vp, c_vp, c_vp, c_vp,
+                                     ctypes.c_size_t, c_vp]),
+    "rdkv_decode_merge": (c_i32, [ctypes.POINTER(Layout), c_vp, ctypes.c_size_t, c_i32, c_vp, c_vp, ctypes.c_size_t,
+                                  c_vp]),
     "rdkv_unpack": (c_i32, [ctypes.POINTER(Layout), c_vp, ctypes.c_size_t, c_i64, c_vp, c_vp, c_vp]),
 }
 
@@ -208,6 +212,35 @@ def decode(lay: Layout, cache: torch.Tensor, c_len: int, q, k_new=None, v_new=No
                               _ptr(out, torch.float32, (S, L, Hq, HEAD_DIM), "out"),
                               _ptr(workspace, torch.uint8, None, "workspace"), workspace.numel(), _stream()),
            "rdkv_decode")
+    return out
+
+
+def decode_partials(lay: Layout, cache: torch.Tensor, c_len: int, q, k_new=None, v_new=None,
+                    workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """First split-K phase (append + per-chunk partials); returns the workspace."""
+    d = lay.dims
+    S, L, Hq, Hk = d.n_seq, d.n_layers, d.n_q_heads, d.n_kv_heads
+    if workspace is None:
+        workspace = decode_workspace(lay, q.device)
+    _check(load().rdkv_decode_partials(ctypes.byref(lay), _ptr(cache, torch.uint8, None, "cache"), cache.numel(),
+                                       c_len, _ptr(q, torch.float16, (S, L, Hq, HEAD_DIM), "q"),
+                                       _ptr(k_new, torch.float16, (S, L, Hk, HEAD_DIM), "k_new"),
+                                       _ptr(v_new, torch.float16, (S, L, Hk, HEAD_DIM), "v_new"),
+                                       _ptr(workspace, torch.uint8, None, "workspace"), workspace.numel(), _stream()),
+           "rdkv_decode_partials")
+    return workspace
+
+
+def decode_merge(lay: Layout, cache: torch.Tensor, zone_c_rows: int, workspace: torch.Tensor,
+                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Second split-K phase: merge the partials into out fp32 [S][L][Hq][128]."""
+    d = lay.dims
+    if out is None:
+        out = torch.empty((d.n_seq, d.n_layers, d.n_q_heads, HEAD_DIM), dtype=torch.float32, device=cache.device)
+    _check(load().rdkv_decode_merge(ctypes.byref(lay), _ptr(cache, torch.uint8, None, "cache"), cache.numel(),
+                                    zone_c_rows, _ptr(out, torch.float32, None, "out"),
+                                    _ptr(workspace, torch.uint8, None, "workspace"), workspace.numel(), _stream()),
+           "rdkv_decode_merge")
     return out
 
 

@@ -170,6 +170,23 @@ rdkv_status rdkv_decode(const rdkv_layout* layout, void* cache, size_t cache_byt
                         const void* q, const void* k_new, const void* v_new, float* out,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* The two split-K phases of rdkv_decode, for callers that time them, or that
+ * exchange the per-chunk partials between devices before merging.
+ *
+ * rdkv_decode_partials: the append and the per-chunk partial softmax state
+ * (running max m, sum l, unnormalised o[128] per query head and chunk) into
+ * `workspace`; arguments as rdkv_decode.
+ * rdkv_decode_merge: out = sum_k e^{m_k-M} o_k / sum_k e^{m_k-M} l_k over each
+ * segment's chunks, in chunk order.  zone_c_rows is the number of zone-C rows
+ * the partials phase attended (its c_len, plus 1 if it appended), which fixes
+ * the segment's chunk count; 0 <= zone_c_rows <= zone_c_capacity. */
+rdkv_status rdkv_decode_partials(const rdkv_layout* layout, void* cache, size_t cache_bytes, int32_t c_len,
+                                 const void* q, const void* k_new, const void* v_new,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+rdkv_status rdkv_decode_merge(const rdkv_layout* layout, const void* cache, size_t cache_bytes,
+                              int32_t zone_c_rows, float* out, const void* workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
 /* Test support: dequantized kept rows of one segment, in kept order, with the
  * fused multiply-add dequantization x_hat = fmaf(code, scale, zero).
  *   k_hat, v_hat fp32 [nk_max][128] (rows past the segment's kept count are

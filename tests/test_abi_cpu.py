@@ -138,3 +138,15 @@ def test_cache_pack_decode_validation(lib):
     assert lib.rdkv_decode(ctypes.byref(lay), A, nb, 0, A, None, None, A, A, ws - 1, None) == WORKSPACE
     assert lib.rdkv_decode(ctypes.byref(lay), A, nb, 0, A + 8, None, None, A, A, ws, None) == ALIGN
     assert lib.rdkv_unpack(ctypes.byref(lay), A, nb, lay.n_seg, A, A, None) == SHAPE
+
+
+def test_two_phase_decode_validation(lib):
+    lay = rdkv.layout(_dims(n_layers=2), 64, 32, 4)
+    nb, ws = lay.cache_bytes, lay.decode_workspace_bytes
+    assert lib.rdkv_decode_partials(ctypes.byref(lay), A, nb, 4, A, A, A, A, ws, None) == CAPACITY
+    assert lib.rdkv_decode_partials(ctypes.byref(lay), A, nb, 0, None, None, None, A, ws, None) == NULL
+    assert lib.rdkv_decode_partials(ctypes.byref(lay), A, nb, 0, A, None, None, A, ws - 16, None) == WORKSPACE
+    assert lib.rdkv_decode_merge(ctypes.byref(lay), A, nb, 5, A, A, ws, None) == CAPACITY
+    assert lib.rdkv_decode_merge(ctypes.byref(lay), A, nb, -1, A, A, ws, None) == CAPACITY
+    assert lib.rdkv_decode_merge(ctypes.byref(lay), A, nb, 0, None, A, ws, None) == NULL
+    assert lib.rdkv_decode_merge(ctypes.byref(lay), A, nb, 0, A + 4, A, ws, None) == ALIGN

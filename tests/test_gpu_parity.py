@@ -316,3 +316,21 @@ def test_end_to_end_tiny_workload(gpu_lib):
     print(f"end-to-end decode rel err vs oracle pipeline: {worst:.3g}")
     # allocations may differ on a handful of near-lambda tokens
     assert worst <= (TOL if agree_t == 1.0 and agree_c == 1.0 else 5e-2)
+
+
+def test_decode_equals_its_two_phases(gpu_lib):
+    rdkv = gpu_lib
+    lay, ol, oblob, (K, V, bt, bc) = _pack_case(("mixed", 2, 2, 4, 2, 777, 5))
+    c1 = rdkv.cache_init(lay)
+    rdkv.pack(lay, c1, dev(K), dev(V), dev(bt), dev(bc))
+    c2 = c1.clone()
+    r = np.random.default_rng(2)
+    q = dev(r.standard_normal((2, 2, 4, 128)).astype(np.float16))
+    kn = dev(r.standard_normal((2, 2, 2, 128)).astype(np.float16))
+    vn = dev(r.standard_normal((2, 2, 2, 128)).astype(np.float16))
+    a = rdkv.decode(lay, c1, 3, q, kn, vn)
+    ws = rdkv.decode_partials(lay, c2, 3, q, kn, vn)
+    b = rdkv.decode_merge(lay, c2, 4, ws)
+    assert torch.equal(a, b) and torch.equal(c1, c2)
+    # decode is deterministic run to run
+    assert torch.equal(rdkv.decode(lay, c1, 4, q), rdkv.decode(lay, c1, 4, q))
