@@ -6,24 +6,27 @@
 // decode_chunk_kernel: one 256-thread workgroup per (segment, chunk).  A chunk
 // is up to 1024 tokens of the 2-bit V group (512 of the 4-bit, 256 of the
 // 8-bit, 128 of the fp16 group) or up to 256 zone-C rows.  Each wave walks
-// 64-token tiles of the chunk.  Per tile, every load the tile needs is issued
-// first (the token's K record words into registers, the lane's parts of the
-// V rows), then:
-//   * logits, lane = token: q.k_hat for the G query heads of the KV head with
-//     each bit-segment's scale and zero factored out,
-//     q.(s*code + z) = s*(q.code) + z*sum(q); 0-bit channels are absent;
-//   * online softmax over the wave (DPP max), p*scale per token to LDS;
-//   * values, lane = (16-channel block, token pair): accumulates
-//     (p*s)*code per head for two tokens at a time; the p*z part is summed
-//     once per token.
+// 64-token tiles of the chunk:
+//   * the tile's K records, one contiguous block, are loaded with coalesced
+//     dword loads (one tile ahead, into a few registers per lane) and staged
+//     in a per-wave LDS buffer; the lane's parts of the tile's V rows are
+//     loaded one tile ahead into registers;
+//   * logits, lane = token: per bit-part of the record, code pairs (two
+//     channels of one word, fp16 subnormals code * 2^-24) meet the matching
+//     fp16 query pairs in v_dot2_f32_f16; each part's scale and zero are
+//     factored out: q.(s*code + z) = s*(q.code) + z*sum(q); 0-bit channels are
+//     absent;
+//   * online softmax over the wave (DPP max), fp16 p*scale per token to LDS;
+//   * values, lane = (16-channel block, token pair): code pairs of two tokens
+//     of one channel (built with v_perm, masked in place) meet the fp16
+//     (p*scale) pairs in v_dot2; the p*zero part is summed once per token.
 // The 4 waves' partials are merged in LDS into one (m, l, o[128]) per query
-// head and chunk.  decode_merge_kernel then combines each segment's chunks in
-// chunk order, so the result does not depend on scheduling.  Merging in a
-// second launch keeps the chunk kernel free of device-wide fences, which on a
-// multi-XCD part write back and invalidate the L2 and cost more than the
-// merge itself.
-// No MFMA: 1..8 query rows per KV head make this a matrix-vector stream,
-// bounded by HBM bandwidth and VALU issue.
+// head and chunk; decode_merge_kernel combines each segment's chunks in chunk
+// order, so the result does not depend on scheduling.  Merging in a second
+// launch keeps the chunk kernel free of device-wide fences, which on a
+// multi-XCD part write back and invalidate the L2.  No MFMA: 1..8 query rows
+// per KV head make this a matrix-vector stream, bounded by HBM bandwidth and
+// VALU issue.
 #include "rdkv_internal.h"
 
 namespace rdkv {
@@ -31,7 +34,11 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
+constexpr int kTile = 64;
 constexpr float kLog2eOverSqrtD = 1.4426950408889634f / 11.313708498984761f;
+constexpr float kTwo24 = 16777216.0f;   // codes enter dot2 as fp16 subnormals code * 2^-24
+constexpr int kPairSlots = 80;          // >= w16 + 2*w8 + 4*w4 + 8*w2 for any split of 128 channels
+constexpr int kMaxStagedWords = 16;     // longer K records are read from global directly
 
 // ---------------------------------------------------------------- wave reductions (DPP)
 
@@ -50,6 +57,25 @@ __device__ inline float wave_reduce(float v) {
   x = op(x, __builtin_amdgcn_update_dpp(id, x, 0x142, 0xa, 0xf, false));   // row_bcast:15
   x = op(x, __builtin_amdgcn_update_dpp(id, x, 0x143, 0xc, 0xf, false));   // row_bcast:31
   return __int_as_float(__builtin_amdgcn_readlane(x, 63));
+}
+
+__device__ inline void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+__device__ inline float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, a), __builtin_bit_cast(half2v, b), c, false);
+}
+// (byte k of lo) in bits 0-7 and (byte k of hi) in bits 16-23, zeros elsewhere
+__device__ inline uint32_t pair_bytes(uint32_t lo, uint32_t hi, int k) {
+  return __builtin_amdgcn_perm(hi, lo, uint32_t(k) | 0x0c00u | (uint32_t(4 + k) << 16) | 0x0c000000u);
+}
+// (half h of lo) in bits 0-15 and (half h of hi) in bits 16-31
+__device__ inline uint32_t pair_halves(uint32_t lo, uint32_t hi, int h) {
+  return h == 0 ? __builtin_amdgcn_perm(hi, lo, 0x05040100u) : __builtin_amdgcn_perm(hi, lo, 0x07060302u);
 }
 
 // ---------------------------------------------------------------- segment and chunk
@@ -142,18 +168,163 @@ __device__ inline Plan plan_chunk(const SegInfo& si, int n_c, int k) {
   return pl;
 }
 
-__device__ inline int n_chunks_of(const SegInfo& si, int n_c) { return chunk_count(si.n_tok, n_c); }
-
 // ---------------------------------------------------------------- shared memory
 
-template <int G>
-struct Smem {
-  float q[kHeadDim + 32][G];   // query in record channel order, zero padded
-  float qsum[3][G];            // sum of q over the 8-, 4-, 2-bit channel parts
-  float coef[kWaves][64][G];   // p * scale per token of the current tile
-  float part_o[kWaves][G][kHeadDim];
+// Per wave, the staged K records of the current tile and, once the wave's
+// last tile is done, its partial output share one region.
+template <int G, int SW>
+union __align__(16) WaveLds {
+  uint32_t rec[kTile * (SW > 0 ? SW : 1)];
+  float o[G][kHeadDim];
+};
+
+template <int G, int SW>
+struct __align__(16) Smem {
+  uint32_t qpair[kPairSlots][G];         // fp16 query pairs matching the records' code pairs
+  float qsum[4][G];                      // sum of q over the 8-, 4-, 2-bit channel parts
+  uint32_t coefh[kWaves][kTile / 2][G];  // fp16 (p*scale) of the tile's token pairs
+  WaveLds<G, SW> wv[kWaves];
   float part_ml[kWaves][G][2];
 };
+
+template <int G, int SW>
+__device__ inline void load_qp(const Smem<G, SW>& sm, int slot, uint32_t (&q)[G]) {
+  if constexpr (G % 4 == 0) {
+#pragma unroll
+    for (int j = 0; j < G / 4; ++j) {
+      const uint4 t = reinterpret_cast<const uint4*>(&sm.qpair[slot][0])[j];
+      q[4 * j] = t.x, q[4 * j + 1] = t.y, q[4 * j + 2] = t.z, q[4 * j + 3] = t.w;
+    }
+  } else if constexpr (G == 2) {
+    const uint2 t = *reinterpret_cast<const uint2*>(&sm.qpair[slot][0]);
+    q[0] = t.x, q[1] = t.y;
+  } else {
+    q[0] = sm.qpair[slot][0];
+  }
+}
+
+// fp16 query pairs in the order the rows' code pairs come in, and the sum of
+// q over each integer part (for the zero terms).  Zone C uses natural order.
+template <int G, int SW>
+__device__ void build_query_tables(const DecodeParams& p, const SegInfo& si, const Plan& pl, int64_t seg,
+                                   Smem<G, SW>& sm) {
+  const int tid = threadIdx.x;
+  const uint8_t* perm = p.cache + kHeaderBytes + uint64_t(seg) * kDescBytes + kDescPerm;
+  const RecordShape rs = record_shape(si.n_chan[0], si.n_chan[1], si.n_chan[2], si.n_chan[3]);
+  const int c8 = si.n_chan[0], c4 = c8 + si.n_chan[1], c2 = c4 + si.n_chan[2], c0 = c2 + si.n_chan[3];
+  const uint16_t* qh = reinterpret_cast<const uint16_t*>(p.q) + seg * G * kHeadDim;
+  for (int i = tid; i < kPairSlots * G; i += kThreads) {
+    const int sl = i / G, g = i % G;
+    int pa, pb, hi_end;   // permuted channel positions of the pair
+    if (pl.kind == 4) {
+      pa = 2 * sl, pb = 2 * sl + 1, hi_end = kHeadDim;
+    } else if (sl < rs.w16) {
+      pa = 2 * sl, pb = 2 * sl + 1, hi_end = c8;
+    } else if (sl < rs.w16 + 2 * rs.w8) {
+      const int t = sl - rs.w16;
+      pa = c8 + 4 * (t >> 1) + (t & 1), pb = pa + 2, hi_end = c4;
+    } else if (sl < rs.w16 + 2 * rs.w8 + 4 * rs.w4) {
+      const int t = sl - rs.w16 - 2 * rs.w8;
+      pa = c4 + 8 * (t >> 2) + (t & 3), pb = pa + 4, hi_end = c2;
+    } else {
+      const int t = sl - rs.w16 - 2 * rs.w8 - 4 * rs.w4;
+      pa = c2 + 16 * (t >> 3) + (t & 7), pb = pa + 8, hi_end = c0;
+    }
+    auto qbits = [&](int pos) -> uint32_t {
+      if (pos >= hi_end || pos >= kHeadDim) return 0u;
+      return qh[g * kHeadDim + (pl.kind == 4 ? pos : perm[pos])];
+    };
+    sm.qpair[sl][g] = qbits(pa) | (qbits(pb) << 16);
+  }
+  if (tid < 3 * G) {
+    const int j = tid / G, g = tid % G;
+    const int lo = j == 0 ? c8 : j == 1 ? c4 : c2;
+    const int hi = j == 0 ? c4 : j == 1 ? c2 : c0;
+    float acc = 0.f;
+    for (int c = lo; c < hi; ++c) acc += __half2float(__ushort_as_half(qh[g * kHeadDim + perm[c]]));
+    sm.qsum[j][g] = acc;
+  }
+}
+
+// ---------------------------------------------------------------- logits from a K record
+
+// s[g] = q_g . k_hat for one token whose record words are rec[0..).  The
+// record may live in LDS (staged) or in global memory.
+template <int G, int SW>
+__device__ inline void record_logits(const uint32_t* rec, const RecordShape& rs, int nw, bool has_vmeta,
+                                     const Smem<G, SW>& sm, float (&s)[G], float& vs, float& vz) {
+  uint32_t q[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) s[g] = 0.f;
+  int w = 0, sl = 0, mo = rs.w16 + rs.w8 + rs.w4 + rs.w2;
+  for (; w < rs.w16; ++w, ++sl) {
+    const uint32_t x = rec[w];
+    load_qp<G, SW>(sm, sl, q);
+#pragma unroll
+    for (int g = 0; g < G; ++g) s[g] = dot2(x, q[g], s[g]);
+  }
+  auto finish_part = [&](const float (&d)[G], int part) {
+    const uint32_t m = rec[mo++];
+    const float sc = half_lo(m) * kTwo24, z = half_hi(m);
+#pragma unroll
+    for (int g = 0; g < G; ++g) s[g] = fmaf(sc, d[g], fmaf(z, sm.qsum[part][g], s[g]));
+  };
+  if (rs.w8 > 0) {
+    float d[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) d[g] = 0.f;
+    for (int j = 0; j < rs.w8; ++j, ++w) {
+      const uint32_t x = rec[w];
+#pragma unroll
+      for (int e = 0; e < 2; ++e, ++sl) {
+        load_qp<G, SW>(sm, sl, q);
+        const uint32_t pr = (x >> (8 * e)) & 0x00FF00FFu;
+#pragma unroll
+        for (int g = 0; g < G; ++g) d[g] = dot2(pr, q[g], d[g]);
+      }
+    }
+    finish_part(d, 0);
+  }
+  if (rs.w4 > 0) {
+    float d[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) d[g] = 0.f;
+    for (int j = 0; j < rs.w4; ++j, ++w) {
+      const uint32_t x = rec[w];
+#pragma unroll
+      for (int e = 0; e < 4; ++e, ++sl) {
+        load_qp<G, SW>(sm, sl, q);
+        const uint32_t pr = (x >> (4 * e)) & 0x000F000Fu;
+#pragma unroll
+        for (int g = 0; g < G; ++g) d[g] = dot2(pr, q[g], d[g]);
+      }
+    }
+    finish_part(d, 1);
+  }
+  if (rs.w2 > 0) {
+    float d[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) d[g] = 0.f;
+    for (int j = 0; j < rs.w2; ++j, ++w) {
+      const uint32_t x = rec[w];
+#pragma unroll
+      for (int e = 0; e < 8; ++e, ++sl) {
+        load_qp<G, SW>(sm, sl, q);
+        const uint32_t pr = (x >> (2 * e)) & 0x00030003u;
+#pragma unroll
+        for (int g = 0; g < G; ++g) d[g] = dot2(pr, q[g], d[g]);
+      }
+    }
+    finish_part(d, 2);
+  }
+  vs = 1.f;
+  vz = 0.f;
+  if (has_vmeta) {
+    const uint32_t m = rec[nw - 1];
+    vs = half_lo(m);
+    vz = half_hi(m);
+  }
+}
 
 // ---------------------------------------------------------------- value rows
 
@@ -177,109 +348,56 @@ __device__ inline VPart<B> load_vpart(const uint8_t* row, int cb) {
   return v;
 }
 
-// The 16 values of a part: codes as floats, or fp16 values.
+// Scale that turns channel e's accumulator into p*code units: codes enter
+// dot2 as subnormals code * 2^-24, shifted left by the in-place mask
+// position (2e mod 8 bits for 2-bit codes, 4 for odd 4-bit channels).
 template <int B>
-__device__ inline void unpack_vpart(const VPart<B>& v, float (&x)[16]) {
-  if constexpr (B == 2) {
-#pragma unroll
-    for (int e = 0; e < 16; ++e) x[e] = float((v.w >> (2 * e)) & 3u);
-  } else if constexpr (B == 4) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      x[e] = float((v.w.x >> (4 * e)) & 15u);
-      x[8 + e] = float((v.w.y >> (4 * e)) & 15u);
-    }
-  } else if constexpr (B == 8) {
-    const uint32_t ws[4] = {v.w.x, v.w.y, v.w.z, v.w.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) x[4 * j + e] = float((ws[j] >> (8 * e)) & 255u);
-  } else {
-    const uint32_t ws[8] = {v.a.x, v.a.y, v.a.z, v.a.w, v.b.x, v.b.y, v.b.z, v.b.w};
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      x[2 * j] = half_lo(ws[j]);
-      x[2 * j + 1] = half_hi(ws[j]);
-    }
-  }
+__device__ constexpr float channel_scale(int e) {
+  if constexpr (B == 2) return kTwo24 / float(1 << (2 * (e & 3)));
+  if constexpr (B == 4) return kTwo24 / float(1 << (4 * (e & 1)));
+  if constexpr (B == 8) return kTwo24;
+  return 1.0f;
 }
 
-// ---------------------------------------------------------------- logits from a K record
-
-// s[g] = q_g . k_hat for one token whose record words are in kw[0..nw).
-template <int G, int KW>
-__device__ inline void record_logits(const uint32_t (&kw)[KW], int nw, const RecordShape& rs, int c8, int c4, int c2,
-                                     bool has_vmeta, const Smem<G>& sm, float (&s)[G], float& vs, float& vz) {
-  const int e16 = rs.w16, e8 = e16 + rs.w8, e4 = e8 + rs.w4, e2 = e4 + rs.w2;
-  int mi = e2;
-  const int m8 = c4 > c8 ? mi++ : -1;
-  const int m4 = c2 > c4 ? mi++ : -1;
-  const int m2 = rs.w2 > 0 ? mi++ : -1;
-  const int vm = has_vmeta ? mi : -1;
-  float d8[G], d4[G], d2[G];
-  uint32_t w8m = 0, w4m = 0, w2m = 0, wvm = 0;
+// acc[g][e] += dot2((x0[e], x1[e]), (c0[g], c1[g])) for the lane's 16 channels
+// of two tokens; codes masked in place (see channel_scale), fp16 values as is.
+template <int G, int B>
+__device__ inline void pv_pair(float (&acc)[G][16], const VPart<B>& v0, const VPart<B>& v1, const uint32_t (&cf)[G]) {
+  auto fma_e = [&](int e, uint32_t pr) {
 #pragma unroll
-  for (int g = 0; g < G; ++g) s[g] = d8[g] = d4[g] = d2[g] = 0.f;
+    for (int g = 0; g < G; ++g) acc[g][e] = dot2(pr, cf[g], acc[g][e]);
+  };
+  if constexpr (B == 2) {
 #pragma unroll
-  for (int w = 0; w < KW; ++w) {
-    if (w >= nw) break;
-    const uint32_t x = kw[w];
-    if (w < e16) {
-      const float k0 = half_lo(x), k1 = half_hi(x);
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t t = pair_bytes(v0.w, v1.w, k);
 #pragma unroll
-      for (int g = 0; g < G; ++g) s[g] = fmaf(sm.q[2 * w + 1][g], k1, fmaf(sm.q[2 * w][g], k0, s[g]));
-    } else if (w < e8) {
-      const int c = c8 + 4 * (w - e16);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float code = float((x >> (8 * e)) & 255u);
-#pragma unroll
-        for (int g = 0; g < G; ++g) d8[g] = fmaf(sm.q[c + e][g], code, d8[g]);
-      }
-    } else if (w < e4) {
-      const int c = c4 + 8 * (w - e8);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float code = float((x >> (4 * e)) & 15u);
-#pragma unroll
-        for (int g = 0; g < G; ++g) d4[g] = fmaf(sm.q[c + e][g], code, d4[g]);
-      }
-    } else if (w < e2) {
-      const int c = c2 + 16 * (w - e4);
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float code = float((x >> (2 * e)) & 3u);
-#pragma unroll
-        for (int g = 0; g < G; ++g) d2[g] = fmaf(sm.q[c + e][g], code, d2[g]);
-      }
-    } else {
-      if (w == m8) w8m = x;
-      if (w == m4) w4m = x;
-      if (w == m2) w2m = x;
-      if (w == vm) wvm = x;
+      for (int e = 0; e < 4; ++e) fma_e(4 * k + e, t & (0x00030003u << (2 * e)));
     }
-  }
-  if (m8 >= 0) {
-    const float sc = half_lo(w8m), z = half_hi(w8m);
+  } else if constexpr (B == 4) {
+    const uint32_t a0[2] = {v0.w.x, v0.w.y}, a1[2] = {v1.w.x, v1.w.y};
 #pragma unroll
-    for (int g = 0; g < G; ++g) s[g] = fmaf(sc, d8[g], fmaf(z, sm.qsum[0][g], s[g]));
-  }
-  if (m4 >= 0) {
-    const float sc = half_lo(w4m), z = half_hi(w4m);
+    for (int d = 0; d < 2; ++d)
 #pragma unroll
-    for (int g = 0; g < G; ++g) s[g] = fmaf(sc, d4[g], fmaf(z, sm.qsum[1][g], s[g]));
-  }
-  if (m2 >= 0) {
-    const float sc = half_lo(w2m), z = half_hi(w2m);
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t t = pair_bytes(a0[d], a1[d], k);
+        fma_e(8 * d + 2 * k, t & 0x000F000Fu);
+        fma_e(8 * d + 2 * k + 1, t & 0x00F000F0u);
+      }
+  } else if constexpr (B == 8) {
+    const uint32_t a0[4] = {v0.w.x, v0.w.y, v0.w.z, v0.w.w}, a1[4] = {v1.w.x, v1.w.y, v1.w.z, v1.w.w};
 #pragma unroll
-    for (int g = 0; g < G; ++g) s[g] = fmaf(sc, d2[g], fmaf(z, sm.qsum[2][g], s[g]));
-  }
-  vs = 1.f;
-  vz = 0.f;
-  if (has_vmeta) {
-    vs = half_lo(wvm);
-    vz = half_hi(wvm);
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) fma_e(4 * d + k, pair_bytes(a0[d], a1[d], k));
+  } else {
+    const uint32_t a0[8] = {v0.a.x, v0.a.y, v0.a.z, v0.a.w, v0.b.x, v0.b.y, v0.b.z, v0.b.w};
+    const uint32_t a1[8] = {v1.a.x, v1.a.y, v1.a.z, v1.a.w, v1.b.x, v1.b.y, v1.b.z, v1.b.w};
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      fma_e(2 * d, pair_halves(a0[d], a1[d], 0));
+      fma_e(2 * d + 1, pair_halves(a0[d], a1[d], 1));
+    }
   }
 }
 
@@ -302,52 +420,59 @@ __device__ inline void state_init(WaveState<G>& st) {
   }
 }
 
-// Online softmax update for one tile; writes p*vs per token to LDS.
-template <int G>
+// Online softmax update for one tile; writes fp16 p*vs per token to LDS.
+template <int G, int SW>
 __device__ inline void softmax_tile(WaveState<G>& st, const float (&s)[G], bool valid, float vs, float vz,
-                                    Smem<G>& sm, int wave, int lane) {
+                                    Smem<G, SW>& sm, int wave, int lane) {
+  float t[G], mnew[G];
+  bool grew = false;
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    const float t = valid ? s[g] * kLog2eOverSqrtD : -INFINITY;
-    const float mnew = fmaxf(st.m[g], wave_reduce<true>(t));
-    const float alpha = exp2f(st.m[g] - mnew);
-    const float pr = exp2f(t - mnew);
-    st.m[g] = mnew;
-    st.l[g] = fmaf(st.l[g], alpha, pr);
-    st.z[g] = fmaf(st.z[g], alpha, pr * vz);
+    t[g] = valid ? s[g] * kLog2eOverSqrtD : -INFINITY;
+    mnew[g] = fmaxf(st.m[g], wave_reduce<true>(t[g]));
+    grew = grew || mnew[g] != st.m[g];
+  }
+  if (grew) {   // uniform: rescale the running sums only when a running max moved
 #pragma unroll
-    for (int e = 0; e < 16; ++e) st.acc[g][e] *= alpha;
-    sm.coef[wave][lane][g] = pr * vs;
+    for (int g = 0; g < G; ++g) {
+      const float alpha = __builtin_amdgcn_exp2f(st.m[g] - mnew[g]);
+      st.m[g] = mnew[g];
+      st.l[g] *= alpha;
+      st.z[g] *= alpha;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) st.acc[g][e] *= alpha;
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const float pr = __builtin_amdgcn_exp2f(t[g] - st.m[g]);
+    st.l[g] += pr;
+    st.z[g] = fmaf(pr, vz, st.z[g]);
+    reinterpret_cast<uint16_t*>(&sm.coefh[wave][lane >> 1][g])[lane & 1] = __half_as_ushort(__float2half_rn(pr * vs));
   }
 }
 
-__device__ inline void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// acc[g][e] += c0[g] * x0[e] + c1[g] * x1[e]
-template <int G, int B>
-__device__ inline void accumulate_pair(WaveState<G>& st, const Smem<G>& sm, int wave, int j0, const VPart<B>& v0,
+// Values of token pair `pr` (tokens 2*pr, 2*pr+1 of the tile) into acc.
+template <int G, int B, int SW>
+__device__ inline void accumulate_pair(WaveState<G>& st, const Smem<G, SW>& sm, int wave, int pr, const VPart<B>& v0,
                                        const VPart<B>& v1) {
-  float c0[G], c1[G], x0[16], x1[16];
+  uint32_t cf[G];
+  if constexpr (G % 4 == 0) {
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    c0[g] = sm.coef[wave][j0][g];
-    c1[g] = sm.coef[wave][j0 + 1][g];
+    for (int j = 0; j < G / 4; ++j) {
+      const uint4 t = reinterpret_cast<const uint4*>(&sm.coefh[wave][pr][0])[j];
+      cf[4 * j] = t.x, cf[4 * j + 1] = t.y, cf[4 * j + 2] = t.z, cf[4 * j + 3] = t.w;
+    }
+  } else {
+#pragma unroll
+    for (int g = 0; g < G; ++g) cf[g] = sm.coefh[wave][pr][g];
   }
-  unpack_vpart<B>(v0, x0);
-  unpack_vpart<B>(v1, x1);
-#pragma unroll
-  for (int g = 0; g < G; ++g)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) st.acc[g][e] = fmaf(c1[g], x1[e], fmaf(c0[g], x0[e], st.acc[g][e]));
+  pv_pair<G, B>(st.acc, v0, v1, cf);
 }
 
 // Wave partial (m, l, o) into LDS.
-template <int G>
-__device__ inline void wave_finish(WaveState<G>& st, Smem<G>& sm, int wave, int lane) {
+template <int G, int B, int SW>
+__device__ inline void wave_finish(WaveState<G>& st, Smem<G, SW>& sm, int wave, int lane) {
   const int cb = lane & 7, ts = lane >> 3;
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -366,7 +491,8 @@ __device__ inline void wave_finish(WaveState<G>& st, Smem<G>& sm, int wave, int 
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) sm.part_o[wave][g][cb * 16 + e] = st.acc[g][e] + st.z[g];
+      for (int e = 0; e < 16; ++e)
+        sm.wv[wave].o[g][cb * 16 + e] = fmaf(st.acc[g][e], channel_scale<B>(e), st.z[g]);
   }
   if (lane == 0) {
 #pragma unroll
@@ -379,61 +505,107 @@ __device__ inline void wave_finish(WaveState<G>& st, Smem<G>& sm, int wave, int 
 
 // ---------------------------------------------------------------- token groups (zones A and B)
 
-template <int G, int B, int KW>
-__device__ void run_group(const DecodeParams& p, const SegInfo& si, const Plan& pl, Smem<G>& sm) {
+// Coalesced load of a tile's K records (a contiguous block of n_words words)
+// into registers: lane holds words lane, lane+64, ...
+template <int SW>
+__device__ inline void stage_load(uint32_t (&r)[SW], const uint32_t* src, int n_words, int lane) {
+#pragma unroll
+  for (int i = 0; i < SW; ++i) {
+    const int idx = i * kTile + lane;
+    r[i] = idx < n_words ? src[idx] : 0u;
+  }
+}
+template <int SW>
+__device__ inline void stage_store(const uint32_t (&r)[SW], uint32_t* dst, int n_words, int lane) {
+#pragma unroll
+  for (int i = 0; i < SW; ++i) {
+    const int idx = i * kTile + lane;
+    if (idx < n_words) dst[idx] = r[i];
+  }
+}
+
+// SW > 0: records (at most SW words) staged through LDS; SW == 0: read from
+// global memory by each lane.  PIPE: the next tile's V parts are loaded ahead.
+template <int G, int B, int SW, bool PIPE>
+__device__ void run_group(const DecodeParams& p, const SegInfo& si, const Plan& pl, int64_t seg, Smem<G, SW>& sm) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int cb = lane & 7, ts = lane >> 3;
   const RecordShape rs = record_shape(si.n_chan[0], si.n_chan[1], si.n_chan[2], si.n_chan[3]);
-  const int c8 = si.n_chan[0], c4 = c8 + si.n_chan[1], c2 = c4 + si.n_chan[2];
   const int nw = pl.rec_words;
   const uint32_t* rbase = reinterpret_cast<const uint32_t*>(p.cache + si.off_krec) + pl.rec0;
   const uint8_t* vbase = p.cache + pl.vbase;
   constexpr int kRowBytes = kHeadDim * B / 8;
-  constexpr int kPrefetch = B == 16 ? 2 : 4;   // token pairs whose V parts are loaded ahead
   const int last = pl.end - 1;
+  uint32_t* lrec = sm.wv[wave].rec;
+  auto vrow = [&](int row) { return vbase + int64_t(min(row, last)) * kRowBytes; };
+
+  constexpr int kSW = SW > 0 ? SW : 1;
+  uint32_t stg[kSW];
+  VPart<B> vcur[4][2], vnxt[4][2];
+  int base = pl.start + kTile * wave;
+  auto tile_words = [&](int b) { return min(kTile, pl.end - b) * nw; };
+  if (base < pl.end) {
+    if constexpr (SW > 0) stage_load<SW>(stg, rbase + int64_t(base) * nw, tile_words(base), lane);
+    if constexpr (PIPE) {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) vcur[rr][h] = load_vpart<B>(vrow(base + 16 * rr + 2 * ts + h), cb);
+    }
+  }
+  build_query_tables<G, SW>(p, si, pl, seg, sm);
+  __syncthreads();
+  if constexpr (SW > 0) {
+    if (base < pl.end) stage_store<SW>(stg, lrec, tile_words(base), lane);
+  }
 
   WaveState<G> st;
   state_init(st);
-  for (int base = pl.start + 64 * wave; base < pl.end; base += kThreads) {
-    // ---- loads for the whole tile
-    const int r = min(base + lane, last);
-    const uint32_t* rp = rbase + int64_t(r) * nw;
-    uint32_t kw[KW];
+  for (; base < pl.end; base += kThreads) {
+    const bool more = base + kThreads < pl.end;
+    if (more) {
+      if constexpr (SW > 0) stage_load<SW>(stg, rbase + int64_t(base + kThreads) * nw, tile_words(base + kThreads), lane);
+      if constexpr (PIPE) {
 #pragma unroll
-    for (int w = 0; w < KW; ++w) kw[w] = w < nw ? rp[w] : 0u;
-    VPart<B> vp[kPrefetch][2];
+        for (int rr = 0; rr < 4; ++rr)
 #pragma unroll
-    for (int rr = 0; rr < kPrefetch; ++rr)
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        vp[rr][h] = load_vpart<B>(vbase + int64_t(min(base + 16 * rr + 2 * ts + h, last)) * kRowBytes, cb);
-
-    // ---- logits and softmax, lane = token
-    float s[G], vs, vz;
-    record_logits<G, KW>(kw, nw, rs, c8, c4, c2, B < 16, sm, s, vs, vz);
-    softmax_tile<G>(st, s, base + lane < pl.end, vs, vz, sm, wave, lane);
-    wave_lds_sync();
-
-    // ---- values, lane = (channel block, token pair)
-#pragma unroll
-    for (int rr = 0; rr < kPrefetch; ++rr) accumulate_pair<G, B>(st, sm, wave, 16 * rr + 2 * ts, vp[rr][0], vp[rr][1]);
-    if constexpr (kPrefetch < 4) {
-#pragma unroll
-      for (int rr = kPrefetch; rr < 4; ++rr) {
-        VPart<B> a = load_vpart<B>(vbase + int64_t(min(base + 16 * rr + 2 * ts, last)) * kRowBytes, cb);
-        VPart<B> b = load_vpart<B>(vbase + int64_t(min(base + 16 * rr + 2 * ts + 1, last)) * kRowBytes, cb);
-        accumulate_pair<G, B>(st, sm, wave, 16 * rr + 2 * ts, a, b);
+          for (int h = 0; h < 2; ++h) vnxt[rr][h] = load_vpart<B>(vrow(base + kThreads + 16 * rr + 2 * ts + h), cb);
       }
     }
     wave_lds_sync();
+    const int r = min(base + lane, last);
+    const uint32_t* my = SW > 0 ? lrec + (r - base) * nw : rbase + int64_t(r) * nw;
+    float s[G], vs, vz;
+    record_logits<G, SW>(my, rs, nw, B < 16, sm, s, vs, vz);
+    softmax_tile<G, SW>(st, s, base + lane < pl.end, vs, vz, sm, wave, lane);
+    wave_lds_sync();
+    if constexpr (PIPE) {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) accumulate_pair<G, B, SW>(st, sm, wave, 8 * rr + ts, vcur[rr][0], vcur[rr][1]);
+    } else {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const VPart<B> a = load_vpart<B>(vrow(base + 16 * rr + 2 * ts), cb);
+        const VPart<B> b = load_vpart<B>(vrow(base + 16 * rr + 2 * ts + 1), cb);
+        accumulate_pair<G, B, SW>(st, sm, wave, 8 * rr + ts, a, b);
+      }
+    }
+    wave_lds_sync();
+    if (more) {
+      if constexpr (SW > 0) stage_store<SW>(stg, lrec, tile_words(base + kThreads), lane);
+      if constexpr (PIPE) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) vcur[rr][0] = vnxt[rr][0], vcur[rr][1] = vnxt[rr][1];
+      }
+    }
   }
-  wave_finish<G>(st, sm, wave, lane);
+  wave_finish<G, B, SW>(st, sm, wave, lane);
 }
 
 // ---------------------------------------------------------------- zone C (fp16 rows, natural order)
 
-template <int G>
-__device__ void run_zone_c(const DecodeParams& p, const SegInfo& si, int64_t seg, const Plan& pl, Smem<G>& sm) {
+template <int G, int SW>
+__device__ void run_zone_c(const DecodeParams& p, const SegInfo& si, int64_t seg, const Plan& pl, Smem<G, SW>& sm) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int cb = lane & 7, ts = lane >> 3;
   const int last = pl.end - 1;
@@ -444,99 +616,93 @@ __device__ void run_zone_c(const DecodeParams& p, const SegInfo& si, int64_t seg
   auto krow = [&](int r) { return (p.append && r == p.c_len) ? knew : kc + int64_t(r) * kHeadDim * 2; };
   auto vrow = [&](int r) { return (p.append && r == p.c_len) ? vnew : vc + int64_t(r) * kHeadDim * 2; };
 
+  build_query_tables<G, SW>(p, si, pl, seg, sm);
+  __syncthreads();
   WaveState<G> st;
   state_init(st);
-  for (int base = pl.start + 64 * wave; base < pl.end; base += kThreads) {
+  for (int base = pl.start + kTile * wave; base < pl.end; base += kThreads) {
     const int r = min(base + lane, last);
     const uint4* k4 = reinterpret_cast<const uint4*>(krow(r));
     float s[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) s[g] = 0.f;
-#pragma unroll 2
+#pragma unroll 4
     for (int c = 0; c < 16; ++c) {
       const uint4 x = k4[c];
       const uint32_t ws[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int ch = 8 * c + 2 * j;
-        const float k0 = half_lo(ws[j]), k1 = half_hi(ws[j]);
+        uint32_t q[G];
+        load_qp<G, SW>(sm, 4 * c + j, q);
 #pragma unroll
-        for (int g = 0; g < G; ++g) s[g] = fmaf(sm.q[ch + 1][g], k1, fmaf(sm.q[ch][g], k0, s[g]));
+        for (int g = 0; g < G; ++g) s[g] = dot2(ws[j], q[g], s[g]);
       }
     }
-    softmax_tile<G>(st, s, base + lane < pl.end, 1.f, 0.f, sm, wave, lane);
+    softmax_tile<G, SW>(st, s, base + lane < pl.end, 1.f, 0.f, sm, wave, lane);
     wave_lds_sync();
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
       const int j0 = 16 * rr + 2 * ts;
-      VPart<16> a = load_vpart<16>(vrow(min(base + j0, last)), cb);
-      VPart<16> b = load_vpart<16>(vrow(min(base + j0 + 1, last)), cb);
-      accumulate_pair<G, 16>(st, sm, wave, j0, a, b);
+      const VPart<16> a = load_vpart<16>(vrow(min(base + j0, last)), cb);
+      const VPart<16> b = load_vpart<16>(vrow(min(base + j0 + 1, last)), cb);
+      accumulate_pair<G, 16, SW>(st, sm, wave, 8 * rr + ts, a, b);
     }
     wave_lds_sync();
   }
-  wave_finish<G>(st, sm, wave, lane);
+  wave_finish<G, 16, SW>(st, sm, wave, lane);
 }
 
-// ---------------------------------------------------------------- kernel
+// ---------------------------------------------------------------- kernels
 
 // out[seg][g][c] = sum_k e^{m_k - M} o_k[c] / sum_k e^{m_k - M} l_k over the
-// segment's chunks, in chunk order; a segment with nothing to attend to gives 0.
+// segment's chunks, in chunk order; a segment with nothing to attend to gives
+// 0.  One 128-thread workgroup per (segment, query head): thread c owns
+// channel c; chunk weights are computed once per tile of chunks in LDS.
+constexpr int kMergeThreads = kHeadDim;
+
 template <int G>
-__global__ __launch_bounds__(kThreads) void decode_merge_kernel(DecodeParams p) {
-  const int64_t seg = blockIdx.x;
+__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParams p) {
+  __shared__ float s_f[kMergeThreads];
+  __shared__ float s_red[kMergeThreads / 64];
+  const int64_t seg = blockIdx.x / G;
+  const int g = int(blockIdx.x % G);
+  const int c = threadIdx.x;
   const SegInfo si = load_segment(p, seg);
-  const int n = min(n_chunks_of(si, si.zc_ok ? p.n_c : 0), p.max_chunks);
-  const float* part = p.partials + int64_t(seg) * p.max_chunks * G * kPartialFloats;
-  for (int i = threadIdx.x; i < G * kHeadDim; i += kThreads) {
-    const int g = i / kHeadDim, c = i % kHeadDim;
-    float M = -INFINITY;
-    for (int k = 0; k < n; ++k) M = fmaxf(M, part[(k * G + g) * kPartialFloats]);
-    float L = 0.f, O = 0.f;
-#pragma unroll 4
-    for (int k = 0; k < n; ++k) {
-      const float* pk = part + (k * G + g) * kPartialFloats;
-      const float f = exp2f(pk[0] - M);
-      L = fmaf(pk[1], f, L);
-      O = fmaf(pk[4 + c], f, O);
+  const int n = min(chunk_count(si.n_tok, si.zc_ok ? p.n_c : 0), p.max_chunks);
+  const float* part = p.partials + int64_t(seg) * p.max_chunks * G * kPartialFloats + g * kPartialFloats;
+  const int64_t stride = int64_t(G) * kPartialFloats;
+  float M = -INFINITY;
+  for (int k = c; k < n; k += kMergeThreads) M = fmaxf(M, part[k * stride]);
+  M = wave_reduce<true>(M);
+  if ((c & 63) == 0) s_red[c >> 6] = M;
+  __syncthreads();
+  M = fmaxf(s_red[0], s_red[1]);
+  float L = 0.f, O = 0.f;
+  for (int k0 = 0; k0 < n; k0 += kMergeThreads) {
+    __syncthreads();
+    if (k0 + c < n) s_f[c] = exp2f(part[(k0 + c) * stride] - M);
+    __syncthreads();
+    const int kn = min(kMergeThreads, n - k0);
+#pragma unroll 8
+    for (int j = 0; j < kn; ++j) {
+      const float* pk = part + (k0 + j) * stride;
+      L = fmaf(pk[1], s_f[j], L);
+      O = fmaf(pk[4 + c], s_f[j], O);
     }
-    p.out[(seg * G + g) * kHeadDim + c] = L > 0.f ? O / L : 0.f;
   }
+  p.out[(seg * G + g) * kHeadDim + c] = L > 0.f ? O / L : 0.f;
 }
 
-template <int G, int KW>
+template <int G, int SW>
 __global__ __launch_bounds__(kThreads) void decode_chunk_kernel(DecodeParams p) {
-  __shared__ Smem<G> sm;
+  __shared__ Smem<G, SW> sm;
   const int64_t seg = blockIdx.x / p.max_chunks;
   const int k = int(blockIdx.x % p.max_chunks);
   const SegInfo si = load_segment(p, seg);
-  const int n_c = si.zc_ok ? p.n_c : 0;
-  const Plan pl = plan_chunk(si, n_c, k);
+  const Plan pl = plan_chunk(si, si.zc_ok ? p.n_c : 0, k);
   const int tid = threadIdx.x;
   if (pl.kind < 0) return;
 
-  // query of the G heads, in the channel order the rows use
-  const uint8_t* perm = p.cache + kHeaderBytes + uint64_t(seg) * kDescBytes + kDescPerm;
-  const int c_stored = si.n_chan[0] + si.n_chan[1] + si.n_chan[2] + si.n_chan[3];
-  for (int i = tid; i < (kHeadDim + 32) * G; i += kThreads) {
-    const int pos = i / G, g = i % G;
-    float v = 0.f;
-    if (pl.kind == 4) {
-      if (pos < kHeadDim) v = __half2float(p.q[(seg * G + g) * kHeadDim + pos]);
-    } else if (pos < c_stored) {
-      v = __half2float(p.q[(seg * G + g) * kHeadDim + perm[pos]]);
-    }
-    sm.q[pos][g] = v;
-  }
-  __syncthreads();
-  if (tid < 3 * G) {
-    const int j = tid / G, g = tid % G;
-    const int lo = si.n_chan[0] + (j > 0 ? si.n_chan[1] : 0) + (j > 1 ? si.n_chan[2] : 0);
-    const int hi = lo + (j == 0 ? si.n_chan[1] : j == 1 ? si.n_chan[2] : si.n_chan[3]);
-    float acc = 0.f;
-    for (int c = lo; c < hi; ++c) acc += sm.q[c][g];
-    sm.qsum[j][g] = acc;
-  }
   // append the new token to zone C (only the chunk holding row c_len does it)
   if (pl.kind == 4 && p.append && p.c_len >= pl.start && p.c_len < pl.end) {
     uint32_t* kc = reinterpret_cast<uint32_t*>(p.cache + si.off_kc) + int64_t(p.c_len) * (kHeadDim / 2);
@@ -544,14 +710,13 @@ __global__ __launch_bounds__(kThreads) void decode_chunk_kernel(DecodeParams p) 
     if (tid < 64) kc[tid] = reinterpret_cast<const uint32_t*>(p.k_new + seg * kHeadDim)[tid];
     else if (tid < 128) vc[tid - 64] = reinterpret_cast<const uint32_t*>(p.v_new + seg * kHeadDim)[tid - 64];
   }
-  __syncthreads();
 
   switch (pl.kind) {
-    case 0: run_group<G, 2, KW>(p, si, pl, sm); break;
-    case 1: run_group<G, 4, KW>(p, si, pl, sm); break;
-    case 2: run_group<G, 8, KW>(p, si, pl, sm); break;
-    case 3: run_group<G, 16, KW>(p, si, pl, sm); break;
-    default: run_zone_c<G>(p, si, seg, pl, sm); break;
+    case 0: run_group<G, 2, SW, true>(p, si, pl, seg, sm); break;
+    case 1: run_group<G, 4, SW, true>(p, si, pl, seg, sm); break;
+    case 2: run_group<G, 8, SW, false>(p, si, pl, seg, sm); break;
+    case 3: run_group<G, 16, SW, false>(p, si, pl, seg, sm); break;
+    default: run_zone_c<G, SW>(p, si, seg, pl, sm); break;
   }
   __syncthreads();
 
@@ -567,7 +732,7 @@ __global__ __launch_bounds__(kThreads) void decode_chunk_kernel(DecodeParams p) 
     for (int w = 0; w < kWaves; ++w) {
       const float f = exp2f(sm.part_ml[w][g][0] - M);
       L = fmaf(sm.part_ml[w][g][1], f, L);
-      O = fmaf(sm.part_o[w][g][c], f, O);
+      O = fmaf(sm.wv[w].o[g][c], f, O);
     }
     out[g * kPartialFloats + 4 + c] = O;
     if (c == 0) {
@@ -577,28 +742,28 @@ __global__ __launch_bounds__(kThreads) void decode_chunk_kernel(DecodeParams p) 
   }
 }
 
-template <int G, int KW>
-hipError_t launch_chunks_gk(const DecodeParams& p, hipStream_t stream) {
+template <int G, int SW>
+hipError_t launch_chunks_gs(const DecodeParams& p, hipStream_t stream) {
   const uint64_t grid = uint64_t(p.n_seg) * p.max_chunks;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((decode_chunk_kernel<G, KW>), dim3(unsigned(grid)), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((decode_chunk_kernel<G, SW>), dim3(unsigned(grid)), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
 template <int G>
 hipError_t launch_chunks_g(const DecodeParams& p, hipStream_t stream) {
-  // record words held in registers: the layout's bound on a record
+  // K record words staged through LDS, from the layout's bound on a record
   const int words = (p.rec_max + 3) / 4;
-  if (words <= 8) return launch_chunks_gk<G, 8>(p, stream);
-  if (words <= 16) return launch_chunks_gk<G, 16>(p, stream);
-  if (words <= 32) return launch_chunks_gk<G, 32>(p, stream);
-  return launch_chunks_gk<G, 72>(p, stream);
+  if (words <= 8) return launch_chunks_gs<G, 8>(p, stream);
+  if (words <= 12) return launch_chunks_gs<G, 12>(p, stream);
+  if (words <= kMaxStagedWords) return launch_chunks_gs<G, 16>(p, stream);
+  return launch_chunks_gs<G, 0>(p, stream);
 }
 
 template <int G>
 hipError_t launch_merge_g(const DecodeParams& p, hipStream_t stream) {
   if (p.n_seg == 0) return hipSuccess;
-  hipLaunchKernelGGL(decode_merge_kernel<G>, dim3(unsigned(p.n_seg)), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL(decode_merge_kernel<G>, dim3(unsigned(p.n_seg * G)), dim3(kMergeThreads), 0, stream, p);
   return hipGetLastError();
 }
 
