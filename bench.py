@@ -31,8 +31,31 @@ HBM_PEAK_GBS = 8000.0
 MFMA_FP16_PEAK_TFS = 2500.0
 
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def counter_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, each scaled by a plain copy of known
+    size), or None when there is none or the kernel's source has changed
+    since the counters were taken."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}.md")
+    if not os.path.exists(path):
+        return None, None
+    text = open(path).read()
+    fields = dict(re.findall(r"^(kernel_source|kernel_source_sha256|traffic_bytes_per_launch): (\S+)$", text, re.M))
+    if len(fields) != 3:
+        return None, None
+    src = os.path.join(ROOT, fields["kernel_source"])
+    if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != fields["kernel_source_sha256"]:
+        return None, os.path.relpath(path, ROOT) + " (stale: kernel source changed)"
+    return int(fields["traffic_bytes_per_launch"]), os.path.relpath(path, ROOT)
 
 
 def build_cache(rdkv, synth, torch, w, lay, dims1, fp16_only=False):
@@ -180,7 +203,7 @@ def main():
     ap.add_argument("--no-fp16-baseline", action="store_true")
     ap.add_argument("--cpu-sample-segments", type=int, default=8)
     ap.add_argument("--calibrate-copy", action="store_true",
-                    help="after timing, run one plain 512 MiB device copy (for counter calibration)")
+                    help="after timing, run one plain 384 MiB device-to-device copy (for counter calibration)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -206,7 +229,7 @@ def main():
     tm = time_decode(rdkv, torch, lay, cache, q, kn, vn, args.steps, args.warmup, not args.no_flush)
     ms_mean, ms_med, wall = tm["step"], tm["step_median"], tm["wall"]
     if args.calibrate_copy:
-        src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        src = torch.empty(384 << 20, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
         dst.copy_(src)
@@ -219,6 +242,7 @@ def main():
     b = rdkv.decode_bytes(lay, desc, n_c)
     algo = b["total"] + lay.n_seg * (256 + 2 * 128 * 2)        # descriptors read, new row written
     achieved = algo / (tm["chunk"] * 1e-3) / 1e9
+    traffic, traffic_src = counter_traffic("decode_chunk_kernel", w.name)
     N, d = w.n_tokens, 128
     payload_bits = float((st["hist_tok"] * np.array([0, 2, 4, 8, 16])).sum() * d)
     kept = int(desc["n_kept"].sum())
@@ -248,7 +272,8 @@ def main():
                    "bits_chan_hist_0_2_4_8_16": st["hist_chan"].tolist(),
                    "llc_flushed_between_steps": not args.no_flush, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "traffic_unit": "bytes per launch", "traffic_source": traffic_src,
                      "kernel": "decode_chunk_kernel", "algorithmic_bytes_per_launch": int(algo),
                      "bytes_breakdown": {k: int(v) for k, v in b.items()},
                      "kernel_ms": round(tm["chunk"], 5), "kernel_ms_median": round(tm["chunk_median"], 5),
