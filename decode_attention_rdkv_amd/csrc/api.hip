@@ -44,6 +44,7 @@ DecodeParams base_params(const rdkv_layout* layout, void* cache, int n_c, int c_
   p.n_seg = layout->n_seg;
   p.nk_max = layout->nk_max;
   p.max_chunks = layout->max_chunks;
+  p.chunk_tok2 = layout->chunk_tok2;
   p.rec_max = layout->rec_max;
   p.group = layout->dims.n_q_heads / layout->dims.n_kv_heads;
   p.c_len = c_len;
@@ -126,7 +127,14 @@ rdkv_status rdkv_layout_init(const rdkv_dims* dims, int64_t budget_v, int64_t bu
   L.slot_bytes = L.slot_off_pos + align_up(uint64_t(4) * L.nk_max, kAlign);
   L.slots_offset = align_up(kHeaderBytes + uint64_t(kDescBytes) * L.n_seg, kAlign);
   L.cache_bytes = L.slots_offset + uint64_t(L.n_seg) * L.slot_bytes;
-  const int64_t tok_chunks = std::min<int64_t>(budget_v / (2 * kChunkTok2), N / 128) + 4;
+  // Split-K granularity.  A chunk of group g holds chunk_tok2 >> g tokens, so
+  // sum_g ceil(n_g / (chunk_tok2 >> g)) <= sum_g n_g 2^g / chunk_tok2 + 4, and
+  // sum_g n_g 2^g <= min(B_V / 2, 8 N) because a g-group token costs 2^(g+1) bits.
+  const int64_t v_units = std::min<int64_t>(budget_v / 2, 8 * N);
+  int64_t t2 = kChunkTok2Min;
+  while (t2 < kChunkTok2Max && L.n_seg * v_units / (2 * t2) >= kDecodeTargetChunks) t2 *= 2;
+  L.chunk_tok2 = int32_t(t2);
+  const int64_t tok_chunks = v_units / t2 + 4;
   L.max_chunks = int32_t(tok_chunks + cdiv(cap, kChunkRowsC));
   const int G = dims->n_q_heads / dims->n_kv_heads;
   L.decode_workspace_bytes = uint64_t(L.n_seg) * L.max_chunks * G * kPartialFloats * sizeof(float);

@@ -1,25 +1,26 @@
 // Fused split-K decode attention over the packed cache (RDKV summary, section
 // 2.3: dequantization fused into the logit and output products over zones A,
-// B and C; section 1: decode is bandwidth-bound, it rereads the cache every
-// step).
+// B and C; section 1: decode rereads the whole cache every step).
 //
 // decode_chunk_kernel: one 256-thread workgroup per (segment, chunk).  A chunk
-// is up to 1024 tokens of the 2-bit V group (512 of the 4-bit, 256 of the
-// 8-bit, 128 of the fp16 group) or up to 256 zone-C rows.  Each wave walks
-// 64-token tiles of the chunk:
-//   * the tile's K records, one contiguous block, are loaded with coalesced
-//     dword loads (one tile ahead, into a few registers per lane) and staged
-//     in a per-wave LDS buffer; the lane's parts of the tile's V rows are
-//     loaded one tile ahead into registers;
+// is chunk_tok2 >> g tokens of V group g (equal V bytes per chunk) or up to
+// 256 zone-C rows.  Each wave walks 64-token tiles of the chunk:
+//   * K records: each tile's records are one contiguous block, copied by
+//     global_load_lds (no registers) into a per-wave ring of LDS stages two
+//     tiles ahead; the wave waits on the memory counter for the stage it
+//     reads;
 //   * logits, lane = token: per bit-part of the record, code pairs (two
 //     channels of one word, fp16 subnormals code * 2^-24) meet the matching
 //     fp16 query pairs in v_dot2_f32_f16; each part's scale and zero are
 //     factored out: q.(s*code + z) = s*(q.code) + z*sum(q); 0-bit channels are
 //     absent;
-//   * online softmax over the wave (DPP max), fp16 p*scale per token to LDS;
-//   * values, lane = (16-channel block, token pair): code pairs of two tokens
-//     of one channel (built with v_perm, masked in place) meet the fp16
-//     (p*scale) pairs in v_dot2; the p*zero part is summed once per token.
+//   * online softmax: the running max moves (with a DPP wave reduction) only
+//     when some lane's logit exceeds it; fp16 p*scale per token goes to LDS;
+//   * values, lane = (8-channel block, token slot): a register holds the
+//     lane's channels of two tokens (j, j + 32) in its two halves, masked in
+//     place into fp16 subnormals and met with the fp16 (p*scale) pair in
+//     v_dot2; the p*zero part is summed once per token.  2- and 4-bit rows
+//     are loaded one tile ahead.
 // The 4 waves' partials are merged in LDS into one (m, l, o[128]) per query
 // head and chunk; decode_merge_kernel combines each segment's chunks in chunk
 // order, so the result does not depend on scheduling.  Merging in a second
@@ -27,6 +28,8 @@
 // multi-XCD part write back and invalidate the L2.  No MFMA: 1..8 query rows
 // per KV head make this a matrix-vector stream, bounded by HBM bandwidth and
 // VALU issue.
+#include <type_traits>
+
 #include "rdkv_internal.h"
 
 namespace rdkv {
@@ -38,7 +41,7 @@ constexpr int kTile = 64;
 constexpr float kLog2eOverSqrtD = 1.4426950408889634f / 11.313708498984761f;
 constexpr float kTwo24 = 16777216.0f;   // codes enter dot2 as fp16 subnormals code * 2^-24
 constexpr int kPairSlots = 80;          // >= w16 + 2*w8 + 4*w4 + 8*w2 for any split of 128 channels
-constexpr int kMaxStagedWords = 16;     // longer K records are read from global directly
+constexpr int kMaxStagedWords = 32;     // longer K records are read from global directly
 
 // ---------------------------------------------------------------- wave reductions (DPP)
 
@@ -134,12 +137,12 @@ struct Plan {
   int rec_words;     // words per record in this group
 };
 
-__device__ inline Plan plan_chunk(const SegInfo& si, int n_c, int k) {
+__device__ inline Plan plan_chunk(const SegInfo& si, int n_c, int chunk_tok2, int k) {
   Plan pl{-1, 0, 0, 0, 0, 0};
   int kept = 0;
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
-    const int T = chunk_tokens(g);
+    const int T = chunk_tokens(chunk_tok2, g);
     const int nch = (si.n_tok[g] + T - 1) / T;
     if (pl.kind < 0) {
       if (k < nch) {
@@ -170,11 +173,16 @@ __device__ inline Plan plan_chunk(const SegInfo& si, int n_c, int k) {
 
 // ---------------------------------------------------------------- shared memory
 
-// Per wave, the staged K records of the current tile and, once the wave's
-// last tile is done, its partial output share one region.
+// LDS ring of K-record stages per wave: three stages (two tiles in flight)
+// for records of up to 16 words, two (one in flight) for longer ones.
+template <int SW>
+__host__ __device__ constexpr int ring_stages() { return SW == 0 ? 0 : SW <= 16 ? 3 : 2; }
+
+// Per wave, the record ring and, once the wave's last tile is done, its
+// partial output share one region.
 template <int G, int SW>
 union __align__(16) WaveLds {
-  uint32_t rec[kTile * (SW > 0 ? SW : 1)];
+  uint32_t ring[SW > 0 ? ring_stages<SW>() * kTile * SW : 1];
   float o[G][kHeadDim];
 };
 
@@ -182,7 +190,8 @@ template <int G, int SW>
 struct __align__(16) Smem {
   uint32_t qpair[kPairSlots][G];         // fp16 query pairs matching the records' code pairs
   float qsum[4][G];                      // sum of q over the 8-, 4-, 2-bit channel parts
-  uint32_t coefh[kWaves][kTile / 2][G];  // fp16 (p*scale) of the tile's token pairs
+  uint16_t qperm[G][kHeadDim];           // query with channels in record order
+  uint32_t coefh[kWaves][kTile / 2][G];  // fp16 (p*scale) of tile tokens (j, j + 32)
   WaveLds<G, SW> wv[kWaves];
   float part_ml[kWaves][G][2];
 };
@@ -205,18 +214,26 @@ __device__ inline void load_qp(const Smem<G, SW>& sm, int slot, uint32_t (&q)[G]
 
 // fp16 query pairs in the order the rows' code pairs come in, and the sum of
 // q over each integer part (for the zero terms).  Zone C uses natural order.
+// The global reads are one channel per thread, all in flight together; the
+// part sums are wave reductions.
 template <int G, int SW>
 __device__ void build_query_tables(const DecodeParams& p, const SegInfo& si, const Plan& pl, int64_t seg,
                                    Smem<G, SW>& sm) {
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint8_t* perm = p.cache + kHeaderBytes + uint64_t(seg) * kDescBytes + kDescPerm;
   const RecordShape rs = record_shape(si.n_chan[0], si.n_chan[1], si.n_chan[2], si.n_chan[3]);
   const int c8 = si.n_chan[0], c4 = c8 + si.n_chan[1], c2 = c4 + si.n_chan[2], c0 = c2 + si.n_chan[3];
   const uint16_t* qh = reinterpret_cast<const uint16_t*>(p.q) + seg * G * kHeadDim;
+  const bool natural = pl.kind == 4;
+  for (int i = tid; i < G * kHeadDim; i += kThreads) {
+    const int g = i / kHeadDim, c = i % kHeadDim;
+    sm.qperm[g][c] = qh[g * kHeadDim + (natural ? c : perm[c])];
+  }
+  __syncthreads();
   for (int i = tid; i < kPairSlots * G; i += kThreads) {
     const int sl = i / G, g = i % G;
     int pa, pb, hi_end;   // permuted channel positions of the pair
-    if (pl.kind == 4) {
+    if (natural) {
       pa = 2 * sl, pb = 2 * sl + 1, hi_end = kHeadDim;
     } else if (sl < rs.w16) {
       pa = 2 * sl, pb = 2 * sl + 1, hi_end = c8;
@@ -230,93 +247,101 @@ __device__ void build_query_tables(const DecodeParams& p, const SegInfo& si, con
       const int t = sl - rs.w16 - 2 * rs.w8 - 4 * rs.w4;
       pa = c2 + 16 * (t >> 3) + (t & 7), pb = pa + 8, hi_end = c0;
     }
-    auto qbits = [&](int pos) -> uint32_t {
-      if (pos >= hi_end || pos >= kHeadDim) return 0u;
-      return qh[g * kHeadDim + (pl.kind == 4 ? pos : perm[pos])];
-    };
+    auto qbits = [&](int pos) -> uint32_t { return pos < hi_end && pos < kHeadDim ? sm.qperm[g][pos] : 0u; };
     sm.qpair[sl][g] = qbits(pa) | (qbits(pb) << 16);
   }
-  if (tid < 3 * G) {
-    const int j = tid / G, g = tid % G;
-    const int lo = j == 0 ? c8 : j == 1 ? c4 : c2;
-    const int hi = j == 0 ? c4 : j == 1 ? c2 : c0;
-    float acc = 0.f;
-    for (int c = lo; c < hi; ++c) acc += __half2float(__ushort_as_half(qh[g * kHeadDim + perm[c]]));
-    sm.qsum[j][g] = acc;
+  if (!natural) {
+    for (int i = wave; i < 3 * G; i += kWaves) {
+      const int j = i / G, g = i % G;
+      const int lo = j == 0 ? c8 : j == 1 ? c4 : c2;
+      const int hi = j == 0 ? c4 : j == 1 ? c2 : c0;
+      float v = 0.f;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int c = lane + 64 * h;
+        if (c >= lo && c < hi) v += __half2float(__ushort_as_half(sm.qperm[g][c]));
+      }
+      v = wave_reduce<false>(v);
+      if (lane == 0) sm.qsum[j][g] = v;
+    }
   }
 }
 
-// ---------------------------------------------------------------- logits from a K record
+// Word counts of a segment's K record as the logit loop walks it.
+struct QkShape {
+  int w16;        // fp16 words
+  int words[3];   // words of the 8-, 4-, 2-bit parts
+  int tail[3];    // pair slots the part's last word fills (a word of a b-bit part holds 32/b
+                  // channels as 16/b pairs (e, e + 16/b))
+  int meta;       // index of the first scale/zero word
+};
+
+__device__ inline QkShape qk_shape(const SegInfo& si) {
+  const RecordShape rs = record_shape(si.n_chan[0], si.n_chan[1], si.n_chan[2], si.n_chan[3]);
+  QkShape k;
+  k.w16 = rs.w16;
+  k.words[0] = rs.w8, k.words[1] = rs.w4, k.words[2] = rs.w2;
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    const int pairs = 2 << i;   // pair slots per word
+    k.tail[i] = k.words[i] > 0 ? min(pairs, si.n_chan[i + 1] - (k.words[i] - 1) * 2 * pairs) : 0;
+  }
+  k.meta = rs.w16 + rs.w8 + rs.w4 + rs.w2;
+  return k;
+}
+
+// d[g] += q_g . codes over one integer part (P pair slots per word).  Slots
+// past the part's last channel are skipped; their table entries stay unread.
+template <int G, int SW, int P>
+__device__ inline void int_part(const uint32_t* rec, int& w, int& sl, int words, int tail, const Smem<G, SW>& sm,
+                                float (&d)[G]) {
+  constexpr int kBits = 16 / P;
+  constexpr uint32_t kMask = ((1u << kBits) - 1u) * 0x00010001u;
+  uint32_t q[G];
+  for (int j = 0; j < words; ++j, ++w, sl += P) {
+    const uint32_t x = rec[w];
+    const int n = j + 1 < words ? P : tail;
+#pragma unroll
+    for (int e = 0; e < P; ++e) {
+      if (e < n) {
+        load_qp<G, SW>(sm, sl + e, q);
+        const uint32_t pr = (x >> (kBits * e)) & kMask;
+#pragma unroll
+        for (int g = 0; g < G; ++g) d[g] = dot2(pr, q[g], d[g]);
+      }
+    }
+  }
+}
 
 // s[g] = q_g . k_hat for one token whose record words are rec[0..).  The
 // record may live in LDS (staged) or in global memory.
 template <int G, int SW>
-__device__ inline void record_logits(const uint32_t* rec, const RecordShape& rs, int nw, bool has_vmeta,
+__device__ inline void record_logits(const uint32_t* rec, const QkShape& ks, int nw, bool has_vmeta,
                                      const Smem<G, SW>& sm, float (&s)[G], float& vs, float& vz) {
   uint32_t q[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) s[g] = 0.f;
-  int w = 0, sl = 0, mo = rs.w16 + rs.w8 + rs.w4 + rs.w2;
-  for (; w < rs.w16; ++w, ++sl) {
+  int w = 0, sl = 0, mo = ks.meta;
+  for (; w < ks.w16; ++w, ++sl) {
     const uint32_t x = rec[w];
     load_qp<G, SW>(sm, sl, q);
 #pragma unroll
     for (int g = 0; g < G; ++g) s[g] = dot2(x, q[g], s[g]);
   }
-  auto finish_part = [&](const float (&d)[G], int part) {
+  auto part = [&](auto pairs, int i) {
+    if (ks.words[i] == 0) return;
+    float d[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) d[g] = 0.f;
+    int_part<G, SW, decltype(pairs)::value>(rec, w, sl, ks.words[i], ks.tail[i], sm, d);
     const uint32_t m = rec[mo++];
     const float sc = half_lo(m) * kTwo24, z = half_hi(m);
 #pragma unroll
-    for (int g = 0; g < G; ++g) s[g] = fmaf(sc, d[g], fmaf(z, sm.qsum[part][g], s[g]));
+    for (int g = 0; g < G; ++g) s[g] = fmaf(sc, d[g], fmaf(z, sm.qsum[i][g], s[g]));
   };
-  if (rs.w8 > 0) {
-    float d[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) d[g] = 0.f;
-    for (int j = 0; j < rs.w8; ++j, ++w) {
-      const uint32_t x = rec[w];
-#pragma unroll
-      for (int e = 0; e < 2; ++e, ++sl) {
-        load_qp<G, SW>(sm, sl, q);
-        const uint32_t pr = (x >> (8 * e)) & 0x00FF00FFu;
-#pragma unroll
-        for (int g = 0; g < G; ++g) d[g] = dot2(pr, q[g], d[g]);
-      }
-    }
-    finish_part(d, 0);
-  }
-  if (rs.w4 > 0) {
-    float d[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) d[g] = 0.f;
-    for (int j = 0; j < rs.w4; ++j, ++w) {
-      const uint32_t x = rec[w];
-#pragma unroll
-      for (int e = 0; e < 4; ++e, ++sl) {
-        load_qp<G, SW>(sm, sl, q);
-        const uint32_t pr = (x >> (4 * e)) & 0x000F000Fu;
-#pragma unroll
-        for (int g = 0; g < G; ++g) d[g] = dot2(pr, q[g], d[g]);
-      }
-    }
-    finish_part(d, 1);
-  }
-  if (rs.w2 > 0) {
-    float d[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) d[g] = 0.f;
-    for (int j = 0; j < rs.w2; ++j, ++w) {
-      const uint32_t x = rec[w];
-#pragma unroll
-      for (int e = 0; e < 8; ++e, ++sl) {
-        load_qp<G, SW>(sm, sl, q);
-        const uint32_t pr = (x >> (2 * e)) & 0x00030003u;
-#pragma unroll
-        for (int g = 0; g < G; ++g) d[g] = dot2(pr, q[g], d[g]);
-      }
-    }
-    finish_part(d, 2);
-  }
+  part(std::integral_constant<int, 2>{}, 0);
+  part(std::integral_constant<int, 4>{}, 1);
+  part(std::integral_constant<int, 8>{}, 2);
   vs = 1.f;
   vz = 0.f;
   if (has_vmeta) {
@@ -328,75 +353,82 @@ __device__ inline void record_logits(const uint32_t* rec, const RecordShape& rs,
 
 // ---------------------------------------------------------------- value rows
 
-// A lane's part of one V row: 16 channels (cb*16 .. +16) at b bits.
-template <int B> struct VPart;
-template <> struct VPart<2> { uint32_t w; };
-template <> struct VPart<4> { uint2 w; };
-template <> struct VPart<8> { uint4 w; };
-template <> struct VPart<16> { uint4 a, b; };
+// PV lane layout: lane = 16 * ts + cb holds channels 8cb .. 8cb+7 and token
+// slot ts; a tile's 32 token pairs (j, j + 32) go to slots j mod 4.
+constexpr int kPairsPerLane = kTile / 2 / 4;
+
+// The lane's channels of tokens (j, j + 32) of one V group, as loaded.
+template <int B> struct VPair;
+template <> struct VPair<2> { uint32_t w; };         // 16 bits per token: t0 low half, t1 high half
+template <> struct VPair<4> { uint32_t a, b; };      // 32 bits per token
+template <> struct VPair<8> { uint2 a, b; };         // 64 bits per token
+template <> struct VPair<16> { uint4 a, b; };        // 8 fp16 per token
 
 template <int B>
-__device__ inline VPart<B> load_vpart(const uint8_t* row, int cb) {
-  VPart<B> v;
-  if constexpr (B == 2) v.w = reinterpret_cast<const uint32_t*>(row)[cb];
-  if constexpr (B == 4) v.w = reinterpret_cast<const uint2*>(row)[cb];
-  if constexpr (B == 8) v.w = reinterpret_cast<const uint4*>(row)[cb];
-  if constexpr (B == 16) {
-    v.a = reinterpret_cast<const uint4*>(row)[2 * cb];
-    v.b = reinterpret_cast<const uint4*>(row)[2 * cb + 1];
+__device__ inline VPair<B> load_vpair(const uint8_t* row0, const uint8_t* row1, int cb) {
+  VPair<B> v;
+  if constexpr (B == 2) {
+    const uint32_t lo = reinterpret_cast<const uint16_t*>(row0)[cb];
+    const uint32_t hi = reinterpret_cast<const uint16_t*>(row1)[cb];
+    v.w = lo | (hi << 16);
+  } else if constexpr (B == 4) {
+    v.a = reinterpret_cast<const uint32_t*>(row0)[cb];
+    v.b = reinterpret_cast<const uint32_t*>(row1)[cb];
+  } else if constexpr (B == 8) {
+    v.a = reinterpret_cast<const uint2*>(row0)[cb];
+    v.b = reinterpret_cast<const uint2*>(row1)[cb];
+  } else {
+    v.a = reinterpret_cast<const uint4*>(row0)[cb];
+    v.b = reinterpret_cast<const uint4*>(row1)[cb];
   }
   return v;
 }
 
 // Scale that turns channel e's accumulator into p*code units: codes enter
-// dot2 as subnormals code * 2^-24, shifted left by the in-place mask
-// position (2e mod 8 bits for 2-bit codes, 4 for odd 4-bit channels).
+// dot2 as subnormals code * 2^-24, shifted left by their in-place position.
+// A 2-bit code must stay below bit 10 (the fp16 exponent field): channels
+// 5..7 of the 16-bit lane part are shifted down by 10 first.
 template <int B>
 __device__ constexpr float channel_scale(int e) {
-  if constexpr (B == 2) return kTwo24 / float(1 << (2 * (e & 3)));
-  if constexpr (B == 4) return kTwo24 / float(1 << (4 * (e & 1)));
+  if constexpr (B == 2) return kTwo24 / float(1 << (2 * (e < 5 ? e : e - 5)));
+  if constexpr (B == 4) return (e & 1) ? kTwo24 / 16.0f : kTwo24;
   if constexpr (B == 8) return kTwo24;
   return 1.0f;
 }
 
-// acc[g][e] += dot2((x0[e], x1[e]), (c0[g], c1[g])) for the lane's 16 channels
-// of two tokens; codes masked in place (see channel_scale), fp16 values as is.
+// acc[g][e] += dot2((x_t0[e], x_t1[e]), (c_t0[g], c_t1[g])) for the lane's 8
+// channels (see channel_scale for the in-place code positions).
 template <int G, int B>
-__device__ inline void pv_pair(float (&acc)[G][16], const VPart<B>& v0, const VPart<B>& v1, const uint32_t (&cf)[G]) {
+__device__ inline void pv_pair(float (&acc)[G][8], const VPair<B>& v, const uint32_t (&cf)[G]) {
   auto fma_e = [&](int e, uint32_t pr) {
 #pragma unroll
     for (int g = 0; g < G; ++g) acc[g][e] = dot2(pr, cf[g], acc[g][e]);
   };
   if constexpr (B == 2) {
+    const uint32_t hi = v.w >> 10;
+#pragma unroll
+    for (int e = 0; e < 5; ++e) fma_e(e, v.w & (0x00030003u << (2 * e)));
+#pragma unroll
+    for (int e = 5; e < 8; ++e) fma_e(e, hi & (0x00030003u << (2 * (e - 5))));
+  } else if constexpr (B == 4) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const uint32_t t = pair_bytes(v0.w, v1.w, k);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) fma_e(4 * k + e, t & (0x00030003u << (2 * e)));
+      const uint32_t t = pair_bytes(v.a, v.b, k);
+      fma_e(2 * k, t & 0x000F000Fu);
+      fma_e(2 * k + 1, t & 0x00F000F0u);
     }
-  } else if constexpr (B == 4) {
-    const uint32_t a0[2] = {v0.w.x, v0.w.y}, a1[2] = {v1.w.x, v1.w.y};
+  } else if constexpr (B == 8) {
+    const uint32_t a[2] = {v.a.x, v.a.y}, b[2] = {v.b.x, v.b.y};
 #pragma unroll
     for (int d = 0; d < 2; ++d)
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t t = pair_bytes(a0[d], a1[d], k);
-        fma_e(8 * d + 2 * k, t & 0x000F000Fu);
-        fma_e(8 * d + 2 * k + 1, t & 0x00F000F0u);
-      }
-  } else if constexpr (B == 8) {
-    const uint32_t a0[4] = {v0.w.x, v0.w.y, v0.w.z, v0.w.w}, a1[4] = {v1.w.x, v1.w.y, v1.w.z, v1.w.w};
-#pragma unroll
-    for (int d = 0; d < 4; ++d)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) fma_e(4 * d + k, pair_bytes(a0[d], a1[d], k));
+      for (int k = 0; k < 4; ++k) fma_e(4 * d + k, pair_bytes(a[d], b[d], k));
   } else {
-    const uint32_t a0[8] = {v0.a.x, v0.a.y, v0.a.z, v0.a.w, v0.b.x, v0.b.y, v0.b.z, v0.b.w};
-    const uint32_t a1[8] = {v1.a.x, v1.a.y, v1.a.z, v1.a.w, v1.b.x, v1.b.y, v1.b.z, v1.b.w};
+    const uint32_t a[4] = {v.a.x, v.a.y, v.a.z, v.a.w}, b[4] = {v.b.x, v.b.y, v.b.z, v.b.w};
 #pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      fma_e(2 * d, pair_halves(a0[d], a1[d], 0));
-      fma_e(2 * d + 1, pair_halves(a0[d], a1[d], 1));
+    for (int d = 0; d < 4; ++d) {
+      fma_e(2 * d, pair_halves(a[d], b[d], 0));
+      fma_e(2 * d + 1, pair_halves(a[d], b[d], 1));
     }
   }
 }
@@ -405,7 +437,7 @@ __device__ inline void pv_pair(float (&acc)[G][16], const VPart<B>& v0, const VP
 
 template <int G>
 struct WaveState {
-  float m[G], l[G], z[G], acc[G][16];
+  float m[G], l[G], z[G], acc[G][8];
 };
 
 template <int G>
@@ -416,72 +448,60 @@ __device__ inline void state_init(WaveState<G>& st) {
     st.l[g] = 0.f;
     st.z[g] = 0.f;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) st.acc[g][e] = 0.f;
+    for (int e = 0; e < 8; ++e) st.acc[g][e] = 0.f;
   }
 }
 
-// Online softmax update for one tile; writes fp16 p*vs per token to LDS.
+// Online softmax update for one tile (lane = token): the running max m (log2
+// units, wave-uniform) is raised, with the sums rescaled, only when some
+// lane's logit exceeds it.  Writes fp16 p*vs per token to LDS.
 template <int G, int SW>
 __device__ inline void softmax_tile(WaveState<G>& st, const float (&s)[G], bool valid, float vs, float vz,
                                     Smem<G, SW>& sm, int wave, int lane) {
-  float t[G], mnew[G];
-  bool grew = false;
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    t[g] = valid ? s[g] * kLog2eOverSqrtD : -INFINITY;
-    mnew[g] = fmaxf(st.m[g], wave_reduce<true>(t[g]));
-    grew = grew || mnew[g] != st.m[g];
-  }
-  if (grew) {   // uniform: rescale the running sums only when a running max moved
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float alpha = __builtin_amdgcn_exp2f(st.m[g] - mnew[g]);
-      st.m[g] = mnew[g];
+    const float t = valid ? s[g] * kLog2eOverSqrtD : -INFINITY;
+    if (__builtin_amdgcn_ballot_w64(t > st.m[g]) != 0) {
+      const float mnew = fmaxf(st.m[g], wave_reduce<true>(t));
+      const float alpha = __builtin_amdgcn_exp2f(st.m[g] - mnew);
+      st.m[g] = mnew;
       st.l[g] *= alpha;
       st.z[g] *= alpha;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) st.acc[g][e] *= alpha;
+      for (int e = 0; e < 8; ++e) st.acc[g][e] *= alpha;
     }
-  }
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const float pr = __builtin_amdgcn_exp2f(t[g] - st.m[g]);
+    const float pr = __builtin_amdgcn_exp2f(t - st.m[g]);
     st.l[g] += pr;
     st.z[g] = fmaf(pr, vz, st.z[g]);
-    reinterpret_cast<uint16_t*>(&sm.coefh[wave][lane >> 1][g])[lane & 1] = __half_as_ushort(__float2half_rn(pr * vs));
+    reinterpret_cast<uint16_t*>(&sm.coefh[wave][lane & 31][g])[lane >> 5] = __half_as_ushort(__float2half_rn(pr * vs));
   }
 }
 
-// Values of token pair `pr` (tokens 2*pr, 2*pr+1 of the tile) into acc.
-template <int G, int B, int SW>
-__device__ inline void accumulate_pair(WaveState<G>& st, const Smem<G, SW>& sm, int wave, int pr, const VPart<B>& v0,
-                                       const VPart<B>& v1) {
-  uint32_t cf[G];
+template <int G, int SW>
+__device__ inline void load_coefs(const Smem<G, SW>& sm, int wave, int j, uint32_t (&cf)[G]) {
   if constexpr (G % 4 == 0) {
 #pragma unroll
-    for (int j = 0; j < G / 4; ++j) {
-      const uint4 t = reinterpret_cast<const uint4*>(&sm.coefh[wave][pr][0])[j];
-      cf[4 * j] = t.x, cf[4 * j + 1] = t.y, cf[4 * j + 2] = t.z, cf[4 * j + 3] = t.w;
+    for (int i = 0; i < G / 4; ++i) {
+      const uint4 t = reinterpret_cast<const uint4*>(&sm.coefh[wave][j][0])[i];
+      cf[4 * i] = t.x, cf[4 * i + 1] = t.y, cf[4 * i + 2] = t.z, cf[4 * i + 3] = t.w;
     }
   } else {
 #pragma unroll
-    for (int g = 0; g < G; ++g) cf[g] = sm.coefh[wave][pr][g];
+    for (int g = 0; g < G; ++g) cf[g] = sm.coefh[wave][j][g];
   }
-  pv_pair<G, B>(st.acc, v0, v1, cf);
 }
 
 // Wave partial (m, l, o) into LDS.
 template <int G, int B, int SW>
 __device__ inline void wave_finish(WaveState<G>& st, Smem<G, SW>& sm, int wave, int lane) {
-  const int cb = lane & 7, ts = lane >> 3;
+  const int cb = lane & 15, ts = lane >> 4;
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     st.l[g] = wave_reduce<false>(st.l[g]);
     st.z[g] = wave_reduce<false>(st.z[g]);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
+    for (int e = 0; e < 8; ++e) {
       float v = st.acc[g][e];
-      v += __shfl_xor(v, 8, 64);
       v += __shfl_xor(v, 16, 64);
       v += __shfl_xor(v, 32, 64);
       st.acc[g][e] = v;
@@ -491,8 +511,7 @@ __device__ inline void wave_finish(WaveState<G>& st, Smem<G, SW>& sm, int wave, 
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
-        sm.wv[wave].o[g][cb * 16 + e] = fmaf(st.acc[g][e], channel_scale<B>(e), st.z[g]);
+      for (int e = 0; e < 8; ++e) sm.wv[wave].o[g][cb * 8 + e] = fmaf(st.acc[g][e], channel_scale<B>(e), st.z[g]);
   }
   if (lane == 0) {
 #pragma unroll
@@ -503,101 +522,114 @@ __device__ inline void wave_finish(WaveState<G>& st, Smem<G, SW>& sm, int wave, 
   }
 }
 
+// ---------------------------------------------------------------- K-record ring
+
+// Copies a tile's K records (the n_words >= 1 words at src) into an LDS stage
+// of kTile * SW words: SW dword copies of 64 lanes; indices past the block
+// reread its last word.  Always exactly SW memory instructions.
+template <int SW>
+__device__ inline void dma_records(const uint32_t* src, int n_words, uint32_t* stage, int lane) {
+#pragma unroll
+  for (int i = 0; i < SW; ++i)
+    __builtin_amdgcn_global_load_lds(src + min(i * 64 + lane, n_words - 1), stage + i * 64, 4, 0, 0);
+}
+
+// Waits until at most N vector-memory instructions of this wave are in
+// flight.  Loads complete in issue order, so this also completes every load
+// issued before the N most recent ones.  The scheduling barriers keep the
+// compiler from moving memory instructions across the wait.
+template <int N>
+__device__ inline void wait_vmem() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // ---------------------------------------------------------------- token groups (zones A and B)
 
-// Coalesced load of a tile's K records (a contiguous block of n_words words)
-// into registers: lane holds words lane, lane+64, ...
-template <int SW>
-__device__ inline void stage_load(uint32_t (&r)[SW], const uint32_t* src, int n_words, int lane) {
-#pragma unroll
-  for (int i = 0; i < SW; ++i) {
-    const int idx = i * kTile + lane;
-    r[i] = idx < n_words ? src[idx] : 0u;
-  }
-}
-template <int SW>
-__device__ inline void stage_store(const uint32_t (&r)[SW], uint32_t* dst, int n_words, int lane) {
-#pragma unroll
-  for (int i = 0; i < SW; ++i) {
-    const int idx = i * kTile + lane;
-    if (idx < n_words) dst[idx] = r[i];
-  }
-}
-
-// SW > 0: records (at most SW words) staged through LDS; SW == 0: read from
-// global memory by each lane.  PIPE: the next tile's V parts are loaded ahead.
+// SW > 0: records (at most SW words) go through the wave's LDS ring; SW == 0:
+// each lane reads its record from global memory.  PIPE: the lane's V pairs
+// are loaded one tile ahead (two register sets used in turn); otherwise at
+// the start of the tile, before the logits.
 template <int G, int B, int SW, bool PIPE>
 __device__ void run_group(const DecodeParams& p, const SegInfo& si, const Plan& pl, int64_t seg, Smem<G, SW>& sm) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int cb = lane & 7, ts = lane >> 3;
-  const RecordShape rs = record_shape(si.n_chan[0], si.n_chan[1], si.n_chan[2], si.n_chan[3]);
+  const int cb = lane & 15, ts = lane >> 4;
+  const QkShape ks = qk_shape(si);
   const int nw = pl.rec_words;
   const uint32_t* rbase = reinterpret_cast<const uint32_t*>(p.cache + si.off_krec) + pl.rec0;
   const uint8_t* vbase = p.cache + pl.vbase;
   constexpr int kRowBytes = kHeadDim * B / 8;
   const int last = pl.end - 1;
-  uint32_t* lrec = sm.wv[wave].rec;
+  const int first = pl.start + kTile * wave;                       // the wave's tiles: first + 256 i
+  const int n_tiles = first < pl.end ? (pl.end - first + kThreads - 1) / kThreads : 0;
+  auto tile_row = [&](int i) { return first + kThreads * min(i, n_tiles - 1); };
   auto vrow = [&](int row) { return vbase + int64_t(min(row, last)) * kRowBytes; };
 
-  constexpr int kSW = SW > 0 ? SW : 1;
-  uint32_t stg[kSW];
-  VPart<B> vcur[4][2], vnxt[4][2];
-  int base = pl.start + kTile * wave;
-  auto tile_words = [&](int b) { return min(kTile, pl.end - b) * nw; };
-  if (base < pl.end) {
-    if constexpr (SW > 0) stage_load<SW>(stg, rbase + int64_t(base) * nw, tile_words(base), lane);
-    if constexpr (PIPE) {
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) vcur[rr][h] = load_vpart<B>(vrow(base + 16 * rr + 2 * ts + h), cb);
+  constexpr int kStages = ring_stages<SW>();
+  constexpr int kAhead = kStages > 0 ? kStages - 1 : 0;           // tiles of records in flight
+  const bool use_ring = SW > 0 && nw > 0 && n_tiles > 0;           // uniform
+  auto stage = [&](int i) { return sm.wv[wave].ring + (i % (kStages > 0 ? kStages : 1)) * kTile * SW; };
+  auto fetch_records = [&](int i) {
+    if constexpr (SW > 0) {
+      const int b = tile_row(i);
+      dma_records<SW>(rbase + int64_t(b) * nw, min(kTile, pl.end - b) * nw, stage(i), lane);
     }
+  };
+  auto load_pairs = [&](VPair<B> (&v)[kPairsPerLane], int i) {
+    const int b = tile_row(i);
+#pragma unroll
+    for (int k = 0; k < kPairsPerLane; ++k) {
+      const int j = ts + 4 * k;
+      v[k] = load_vpair<B>(vrow(b + j), vrow(b + j + 32), cb);
+    }
+  };
+
+  VPair<B> va[kPairsPerLane], vb[kPairsPerLane];
+  if (use_ring) {
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) fetch_records(i);
+  }
+  if constexpr (PIPE) {
+    if (n_tiles > 0) load_pairs(va, 0);
   }
   build_query_tables<G, SW>(p, si, pl, seg, sm);
   __syncthreads();
-  if constexpr (SW > 0) {
-    if (base < pl.end) stage_store<SW>(stg, lrec, tile_words(base), lane);
-  }
 
   WaveState<G> st;
   state_init(st);
-  for (; base < pl.end; base += kThreads) {
-    const bool more = base + kThreads < pl.end;
-    if (more) {
-      if constexpr (SW > 0) stage_load<SW>(stg, rbase + int64_t(base + kThreads) * nw, tile_words(base + kThreads), lane);
-      if constexpr (PIPE) {
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-#pragma unroll
-          for (int h = 0; h < 2; ++h) vnxt[rr][h] = load_vpart<B>(vrow(base + kThreads + 16 * rr + 2 * ts + h), cb);
-      }
+  auto tile = [&](int i, VPair<B> (&cur)[kPairsPerLane], VPair<B> (&nxt)[kPairsPerLane]) {
+    const int b = tile_row(i);
+    constexpr int kPipeLoads = PIPE ? kPairsPerLane * (B == 2 ? 2 : 2) : 0;
+    if (use_ring) fetch_records(i + kAhead);
+    if constexpr (PIPE) load_pairs(nxt, i + 1);
+    if constexpr (!PIPE) load_pairs(cur, i);
+    if (use_ring) {
+      // in flight after tile i's records: the next kAhead tiles' records and
+      // V loads (at least kAhead * (SW + kPipeLoads) instructions)
+      constexpr int kAfter = kAhead * (SW + kPipeLoads);
+      wait_vmem<(kAfter < 63 ? kAfter : 63)>();
     }
-    wave_lds_sync();
-    const int r = min(base + lane, last);
-    const uint32_t* my = SW > 0 ? lrec + (r - base) * nw : rbase + int64_t(r) * nw;
+    const int r = min(b + lane, last);
+    // (with SW > 0 and no record words, nothing is read from the stage)
+    const uint32_t* my = SW > 0 ? stage(i) + (r - b) * nw : rbase + int64_t(r) * nw;
     float s[G], vs, vz;
-    record_logits<G, SW>(my, rs, nw, B < 16, sm, s, vs, vz);
-    softmax_tile<G, SW>(st, s, base + lane < pl.end, vs, vz, sm, wave, lane);
+    record_logits<G, SW>(my, ks, nw, B < 16, sm, s, vs, vz);
+    softmax_tile<G, SW>(st, s, b + lane < pl.end, vs, vz, sm, wave, lane);
     wave_lds_sync();
-    if constexpr (PIPE) {
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) accumulate_pair<G, B, SW>(st, sm, wave, 8 * rr + ts, vcur[rr][0], vcur[rr][1]);
-    } else {
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const VPart<B> a = load_vpart<B>(vrow(base + 16 * rr + 2 * ts), cb);
-        const VPart<B> b = load_vpart<B>(vrow(base + 16 * rr + 2 * ts + 1), cb);
-        accumulate_pair<G, B, SW>(st, sm, wave, 8 * rr + ts, a, b);
-      }
+    for (int k = 0; k < kPairsPerLane; ++k) {
+      uint32_t cf[G];
+      load_coefs<G, SW>(sm, wave, ts + 4 * k, cf);
+      pv_pair<G, B>(st.acc, cur[k], cf);
     }
     wave_lds_sync();
-    if (more) {
-      if constexpr (SW > 0) stage_store<SW>(stg, lrec, tile_words(base + kThreads), lane);
-      if constexpr (PIPE) {
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) vcur[rr][0] = vnxt[rr][0], vcur[rr][1] = vnxt[rr][1];
-      }
-    }
+  };
+  for (int i = 0; i < n_tiles; i += 2) {
+    tile(i, va, vb);
+    if (i + 1 >= n_tiles) break;
+    tile(i + 1, vb, va);
   }
   wave_finish<G, B, SW>(st, sm, wave, lane);
 }
@@ -607,20 +639,26 @@ __device__ void run_group(const DecodeParams& p, const SegInfo& si, const Plan& 
 template <int G, int SW>
 __device__ void run_zone_c(const DecodeParams& p, const SegInfo& si, int64_t seg, const Plan& pl, Smem<G, SW>& sm) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int cb = lane & 7, ts = lane >> 3;
+  const int cb = lane & 15, ts = lane >> 4;
   const int last = pl.end - 1;
   const uint8_t* kc = p.cache + si.off_kc;
   const uint8_t* vc = p.cache + si.off_vc;
   const uint8_t* knew = reinterpret_cast<const uint8_t*>(p.k_new + seg * kHeadDim);
   const uint8_t* vnew = reinterpret_cast<const uint8_t*>(p.v_new + seg * kHeadDim);
   auto krow = [&](int r) { return (p.append && r == p.c_len) ? knew : kc + int64_t(r) * kHeadDim * 2; };
-  auto vrow = [&](int r) { return (p.append && r == p.c_len) ? vnew : vc + int64_t(r) * kHeadDim * 2; };
+  auto vrow = [&](int r) {
+    r = min(r, last);
+    return (p.append && r == p.c_len) ? vnew : vc + int64_t(r) * kHeadDim * 2;
+  };
 
   build_query_tables<G, SW>(p, si, pl, seg, sm);
   __syncthreads();
   WaveState<G> st;
   state_init(st);
   for (int base = pl.start + kTile * wave; base < pl.end; base += kThreads) {
+    VPair<16> v[kPairsPerLane];
+#pragma unroll
+    for (int k = 0; k < kPairsPerLane; ++k) v[k] = load_vpair<16>(vrow(base + ts + 4 * k), vrow(base + ts + 4 * k + 32), cb);
     const int r = min(base + lane, last);
     const uint4* k4 = reinterpret_cast<const uint4*>(krow(r));
     float s[G];
@@ -641,11 +679,10 @@ __device__ void run_zone_c(const DecodeParams& p, const SegInfo& si, int64_t seg
     softmax_tile<G, SW>(st, s, base + lane < pl.end, 1.f, 0.f, sm, wave, lane);
     wave_lds_sync();
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int j0 = 16 * rr + 2 * ts;
-      const VPart<16> a = load_vpart<16>(vrow(min(base + j0, last)), cb);
-      const VPart<16> b = load_vpart<16>(vrow(min(base + j0 + 1, last)), cb);
-      accumulate_pair<G, 16, SW>(st, sm, wave, 8 * rr + ts, a, b);
+    for (int k = 0; k < kPairsPerLane; ++k) {
+      uint32_t cf[G];
+      load_coefs<G, SW>(sm, wave, ts + 4 * k, cf);
+      pv_pair<G, 16>(st.acc, v[k], cf);
     }
     wave_lds_sync();
   }
@@ -668,7 +705,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParam
   const int g = int(blockIdx.x % G);
   const int c = threadIdx.x;
   const SegInfo si = load_segment(p, seg);
-  const int n = min(chunk_count(si.n_tok, si.zc_ok ? p.n_c : 0), p.max_chunks);
+  const int n = min(chunk_count(si.n_tok, si.zc_ok ? p.n_c : 0, p.chunk_tok2), p.max_chunks);
   const float* part = p.partials + int64_t(seg) * p.max_chunks * G * kPartialFloats + g * kPartialFloats;
   const int64_t stride = int64_t(G) * kPartialFloats;
   float M = -INFINITY;
@@ -694,12 +731,12 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParam
 }
 
 template <int G, int SW>
-__global__ __launch_bounds__(kThreads) void decode_chunk_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G >= 8 ? 2 : 3))) void decode_chunk_kernel(DecodeParams p) {
   __shared__ Smem<G, SW> sm;
   const int64_t seg = blockIdx.x / p.max_chunks;
   const int k = int(blockIdx.x % p.max_chunks);
   const SegInfo si = load_segment(p, seg);
-  const Plan pl = plan_chunk(si, si.zc_ok ? p.n_c : 0, k);
+  const Plan pl = plan_chunk(si, si.zc_ok ? p.n_c : 0, p.chunk_tok2, k);
   const int tid = threadIdx.x;
   if (pl.kind < 0) return;
 
@@ -756,7 +793,9 @@ hipError_t launch_chunks_g(const DecodeParams& p, hipStream_t stream) {
   const int words = (p.rec_max + 3) / 4;
   if (words <= 8) return launch_chunks_gs<G, 8>(p, stream);
   if (words <= 12) return launch_chunks_gs<G, 12>(p, stream);
-  if (words <= kMaxStagedWords) return launch_chunks_gs<G, 16>(p, stream);
+  if (words <= 16) return launch_chunks_gs<G, 16>(p, stream);
+  if (words <= 24) return launch_chunks_gs<G, 24>(p, stream);
+  if (words <= kMaxStagedWords) return launch_chunks_gs<G, 32>(p, stream);
   return launch_chunks_gs<G, 0>(p, stream);
 }
 

@@ -35,10 +35,17 @@ constexpr int kDescOffKc = 96;    // u64
 constexpr int kDescOffVc = 104;   // u64
 constexpr int kDescPerm = 128;    // u8[128]
 
-// Split-K chunking of decode: tokens per chunk for V groups of 2, 4, 8, 16
-// bits (equal V bytes per chunk), and zone-C rows per chunk.
-constexpr int kChunkTok2 = 1024;
-__host__ __device__ constexpr int chunk_tokens(int group) { return kChunkTok2 >> group; }
+// Split-K chunking of decode: a chunk holds chunk_tok2 >> g tokens of V group
+// g (2, 4, 8, 16 bits: equal V bytes per chunk), or kChunkRowsC zone-C rows.
+// chunk_tok2 is a power of two in [kChunkTok2Min, kChunkTok2Max], chosen per
+// layout so that one launch has about kDecodeTargetChunks chunks.
+#ifndef RDKV_DECODE_TARGET_CHUNKS
+#define RDKV_DECODE_TARGET_CHUNKS 2048
+#endif
+constexpr int64_t kDecodeTargetChunks = RDKV_DECODE_TARGET_CHUNKS;
+constexpr int kChunkTok2Min = 512;
+constexpr int kChunkTok2Max = 8192;
+__host__ __device__ constexpr int chunk_tokens(int chunk_tok2, int group) { return chunk_tok2 >> group; }
 constexpr int kChunkRowsC = 256;
 // Floats per (chunk, query head) partial: m, l, 2 pad, o[128].
 constexpr int kPartialFloats = 4 + kHeadDim;
@@ -68,25 +75,10 @@ __host__ __device__ inline int bits_group(int b) {
   return b == 2 ? 0 : b == 4 ? 1 : b == 8 ? 2 : b == 16 ? 3 : -1;
 }
 
-// A decode chunk: kind 0..3 = rows [start, end) of token group `kind`,
-// kind 4 = zone-C rows [start, end), kind -1 = no work.
-struct Chunk {
-  int kind, start, end;
-};
-__host__ __device__ inline Chunk chunk_of(const int n_tok[4], int n_c, int k) {
-  for (int g = 0; g < 4; ++g) {
-    const int T = chunk_tokens(g);
-    const int nch = (n_tok[g] + T - 1) / T;
-    if (k < nch) return Chunk{g, k * T, min(n_tok[g], (k + 1) * T)};
-    k -= nch;
-  }
-  const int nch = (n_c + kChunkRowsC - 1) / kChunkRowsC;
-  if (k < nch) return Chunk{4, k * kChunkRowsC, min(n_c, (k + 1) * kChunkRowsC)};
-  return Chunk{-1, 0, 0};
-}
-__host__ __device__ inline int chunk_count(const int n_tok[4], int n_c) {
+// Chunks of a segment: each token group in order 2, 4, 8, 16 bits, then zone C.
+__host__ __device__ inline int chunk_count(const int n_tok[4], int n_c, int chunk_tok2) {
   int n = 0;
-  for (int g = 0; g < 4; ++g) n += (n_tok[g] + chunk_tokens(g) - 1) / chunk_tokens(g);
+  for (int g = 0; g < 4; ++g) n += (n_tok[g] + chunk_tokens(chunk_tok2, g) - 1) / chunk_tokens(chunk_tok2, g);
   return n + (n_c + kChunkRowsC - 1) / kChunkRowsC;
 }
 
@@ -129,6 +121,7 @@ struct DecodeParams {
   int64_t n_seg;
   int64_t nk_max;
   int32_t max_chunks;
+  int32_t chunk_tok2;
   int32_t rec_max;
   int32_t group;           // G = Hq / Hkv
   int32_t c_len;           // zone-C rows present before this step

@@ -30,7 +30,7 @@ class Layout(ctypes.Structure):
     _fields_ = [("dims", Dims), ("budget_v", c_i64), ("budget_k", c_i64), ("n_seg", c_i64), ("nk_max", c_i64),
                 ("cache_bytes", c_u64), ("slots_offset", c_u64), ("slot_bytes", c_u64), ("slot_off_v", c_u64),
                 ("slot_off_krec", c_u64), ("slot_off_pos", c_u64), ("decode_workspace_bytes", c_u64),
-                ("zone_c_capacity", c_i32), ("rec_max", c_i32), ("max_chunks", c_i32), ("reserved", c_i32)]
+                ("zone_c_capacity", c_i32), ("rec_max", c_i32), ("max_chunks", c_i32), ("chunk_tok2", c_i32)]
 
     @property
     def group(self) -> int:

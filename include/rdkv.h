@@ -80,7 +80,8 @@ typedef struct rdkv_layout {
   int32_t zone_c_capacity;       /* rows of zone C per segment                      */
   int32_t rec_max;               /* bound on K record bytes                         */
   int32_t max_chunks;            /* split-K partial slots per segment in decode     */
-  int32_t reserved;
+  int32_t chunk_tok2;            /* decode split-K chunk: tokens of the 2-bit group */
+                                 /* (4/8/16-bit groups: 1/2, 1/4, 1/8 of it)        */
 } rdkv_layout;
 
 /* Library version (format version in the high 16 bits, build in the low 16). */
