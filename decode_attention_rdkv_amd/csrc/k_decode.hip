@@ -62,6 +62,9 @@ __device__ inline float wave_reduce(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(x, 63));
 }
 
+// The wave's index in the workgroup, as a wave-uniform (scalar) value.
+__device__ inline int wave_id() { return __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6); }
+
 __device__ inline void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -219,7 +222,7 @@ __device__ inline void load_qp(const Smem<G, SW>& sm, int slot, uint32_t (&q)[G]
 template <int G, int SW>
 __device__ void build_query_tables(const DecodeParams& p, const SegInfo& si, const Plan& pl, int64_t seg,
                                    Smem<G, SW>& sm) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const uint8_t* perm = p.cache + kHeaderBytes + uint64_t(seg) * kDescBytes + kDescPerm;
   const RecordShape rs = record_shape(si.n_chan[0], si.n_chan[1], si.n_chan[2], si.n_chan[3]);
   const int c8 = si.n_chan[0], c4 = c8 + si.n_chan[1], c2 = c4 + si.n_chan[2], c0 = c2 + si.n_chan[3];
@@ -525,13 +528,21 @@ __device__ inline void wave_finish(WaveState<G>& st, Smem<G, SW>& sm, int wave, 
 // ---------------------------------------------------------------- K-record ring
 
 // Copies a tile's K records (the n_words >= 1 words at src) into an LDS stage
-// of kTile * SW words: SW dword copies of 64 lanes; indices past the block
-// reread its last word.  Always exactly SW memory instructions.
+// of kTile * SW words: always exactly SW dword copies of 64 lanes.  A full
+// tile (n_words = 64 nw) copies whole 64-word rows; the copies past them
+// reread the first row, so lane offsets stay fixed and no index is clamped
+// per lane.  A partial tile clamps each lane's index to the block.
 template <int SW>
-__device__ inline void dma_records(const uint32_t* src, int n_words, uint32_t* stage, int lane) {
+__device__ inline void dma_records(const uint32_t* src, int nw, int n_words, uint32_t* stage, int lane) {
+  if (n_words == kTile * nw) {
 #pragma unroll
-  for (int i = 0; i < SW; ++i)
-    __builtin_amdgcn_global_load_lds(src + min(i * 64 + lane, n_words - 1), stage + i * 64, 4, 0, 0);
+    for (int i = 0; i < SW; ++i)
+      __builtin_amdgcn_global_load_lds(src + (i < nw ? i * 64 : 0) + lane, stage + i * 64, 4, 0, 0);
+  } else {
+#pragma unroll
+    for (int i = 0; i < SW; ++i)
+      __builtin_amdgcn_global_load_lds(src + min(i * 64 + lane, n_words - 1), stage + i * 64, 4, 0, 0);
+  }
 }
 
 // Waits until at most N vector-memory instructions of this wave are in
@@ -554,7 +565,7 @@ __device__ inline void wait_vmem() {
 // the start of the tile, before the logits.
 template <int G, int B, int SW, bool PIPE>
 __device__ void run_group(const DecodeParams& p, const SegInfo& si, const Plan& pl, int64_t seg, Smem<G, SW>& sm) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int cb = lane & 15, ts = lane >> 4;
   const QkShape ks = qk_shape(si);
   const int nw = pl.rec_words;
@@ -574,15 +585,24 @@ __device__ void run_group(const DecodeParams& p, const SegInfo& si, const Plan& 
   auto fetch_records = [&](int i) {
     if constexpr (SW > 0) {
       const int b = tile_row(i);
-      dma_records<SW>(rbase + int64_t(b) * nw, min(kTile, pl.end - b) * nw, stage(i), lane);
+      dma_records<SW>(rbase + int64_t(b) * nw, nw, min(kTile, pl.end - b) * nw, stage(i), lane);
     }
   };
+  // V pairs of tile i: a full tile addresses rows from one uniform tile base
+  // plus a fixed lane offset; a partial one clamps each row to the chunk.
+  const uint32_t lane_off = uint32_t(ts * kRowBytes + cb * (kRowBytes / 16));
   auto load_pairs = [&](VPair<B> (&v)[kPairsPerLane], int i) {
     const int b = tile_row(i);
+    if (b + kTile <= pl.end) {
+      const uint8_t* lp = vbase + int64_t(b) * kRowBytes + lane_off;
 #pragma unroll
-    for (int k = 0; k < kPairsPerLane; ++k) {
-      const int j = ts + 4 * k;
-      v[k] = load_vpair<B>(vrow(b + j), vrow(b + j + 32), cb);
+      for (int k = 0; k < kPairsPerLane; ++k) v[k] = load_vpair<B>(lp + 4 * k * kRowBytes, lp + (4 * k + 32) * kRowBytes, 0);
+    } else {
+#pragma unroll
+      for (int k = 0; k < kPairsPerLane; ++k) {
+        const int j = ts + 4 * k;
+        v[k] = load_vpair<B>(vrow(b + j), vrow(b + j + 32), cb);
+      }
     }
   };
 
@@ -638,7 +658,7 @@ __device__ void run_group(const DecodeParams& p, const SegInfo& si, const Plan& 
 
 template <int G, int SW>
 __device__ void run_zone_c(const DecodeParams& p, const SegInfo& si, int64_t seg, const Plan& pl, Smem<G, SW>& sm) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int cb = lane & 15, ts = lane >> 4;
   const int last = pl.end - 1;
   const uint8_t* kc = p.cache + si.off_kc;
