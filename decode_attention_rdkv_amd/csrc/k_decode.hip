@@ -362,7 +362,8 @@ constexpr int kPairsPerLane = kTile / 2 / 4;
 
 // The lane's channels of tokens (j, j + 32) of one V group, as loaded.
 template <int B> struct VPair;
-template <> struct VPair<2> { uint32_t w; };         // 16 bits per token: t0 low half, t1 high half
+template <> struct VPair<2> { uint32_t a, b; };      // 16 bits per token (joined at use, so a
+                                                     // prefetch is not waited for at its load)
 template <> struct VPair<4> { uint32_t a, b; };      // 32 bits per token
 template <> struct VPair<8> { uint2 a, b; };         // 64 bits per token
 template <> struct VPair<16> { uint4 a, b; };        // 8 fp16 per token
@@ -371,9 +372,8 @@ template <int B>
 __device__ inline VPair<B> load_vpair(const uint8_t* row0, const uint8_t* row1, int cb) {
   VPair<B> v;
   if constexpr (B == 2) {
-    const uint32_t lo = reinterpret_cast<const uint16_t*>(row0)[cb];
-    const uint32_t hi = reinterpret_cast<const uint16_t*>(row1)[cb];
-    v.w = lo | (hi << 16);
+    v.a = reinterpret_cast<const uint16_t*>(row0)[cb];
+    v.b = reinterpret_cast<const uint16_t*>(row1)[cb];
   } else if constexpr (B == 4) {
     v.a = reinterpret_cast<const uint32_t*>(row0)[cb];
     v.b = reinterpret_cast<const uint32_t*>(row1)[cb];
@@ -408,9 +408,10 @@ __device__ inline void pv_pair(float (&acc)[G][8], const VPair<B>& v, const uint
     for (int g = 0; g < G; ++g) acc[g][e] = dot2(pr, cf[g], acc[g][e]);
   };
   if constexpr (B == 2) {
-    const uint32_t hi = v.w >> 10;
+    const uint32_t w = v.a | (v.b << 16);   // t0 in the low half, t1 in the high half
+    const uint32_t hi = w >> 10;
 #pragma unroll
-    for (int e = 0; e < 5; ++e) fma_e(e, v.w & (0x00030003u << (2 * e)));
+    for (int e = 0; e < 5; ++e) fma_e(e, w & (0x00030003u << (2 * e)));
 #pragma unroll
     for (int e = 5; e < 8; ++e) fma_e(e, hi & (0x00030003u << (2 * (e - 5))));
   } else if constexpr (B == 4) {
@@ -527,21 +528,55 @@ __device__ inline void wave_finish(WaveState<G>& st, Smem<G, SW>& sm, int wave, 
 
 // ---------------------------------------------------------------- K-record ring
 
+// LDS byte address of a pointer into shared memory.
+__device__ inline uint32_t lds_addr(const void* p) {
+  return uint32_t(size_t((const __attribute__((address_space(3))) void*)p));
+}
+
+// One global_load_lds_dword: 64 lanes each copy a dword into LDS at
+// lds + 4 * lane.  Written as inline assembly, so the compiler's memory-
+// counter bookkeeping does not see it (it would otherwise wait for every
+// outstanding copy before any LDS read); the tile loop waits explicitly.
+// M0 (the LDS base of the copy) is saved and restored around it.
+__device__ inline void lds_copy_s(const uint32_t* base, uint32_t voff, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(base), "s"(lds)
+      : "memory");
+}
+__device__ inline void lds_copy_v(const uint32_t* addr, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(addr), "s"(lds)
+      : "memory");
+}
+
 // Copies a tile's K records (the n_words >= 1 words at src) into an LDS stage
-// of kTile * SW words: always exactly SW dword copies of 64 lanes.  A full
-// tile (n_words = 64 nw) copies whole 64-word rows; the copies past them
-// reread the first row, so lane offsets stay fixed and no index is clamped
-// per lane.  A partial tile clamps each lane's index to the block.
+// of kTile * SW words: always exactly SW copies of 64 dwords.  A full tile
+// (n_words = 64 nw) copies whole 64-word rows from a uniform base at a fixed
+// lane offset; the copies past them reread the first row.  A partial tile
+// clamps each lane's index to the block.
 template <int SW>
 __device__ inline void dma_records(const uint32_t* src, int nw, int n_words, uint32_t* stage, int lane) {
+  const uint32_t lds = lds_addr(stage);
   if (n_words == kTile * nw) {
 #pragma unroll
-    for (int i = 0; i < SW; ++i)
-      __builtin_amdgcn_global_load_lds(src + (i < nw ? i * 64 : 0) + lane, stage + i * 64, 4, 0, 0);
+    for (int i = 0; i < SW; ++i) lds_copy_s(src + (i < nw ? i * 64 : 0), uint32_t(lane) * 4u, lds + i * 256);
   } else {
 #pragma unroll
-    for (int i = 0; i < SW; ++i)
-      __builtin_amdgcn_global_load_lds(src + min(i * 64 + lane, n_words - 1), stage + i * 64, 4, 0, 0);
+    for (int i = 0; i < SW; ++i) lds_copy_v(src + min(i * 64 + lane, n_words - 1), lds + i * 256);
   }
 }
 
