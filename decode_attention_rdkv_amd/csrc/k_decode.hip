@@ -613,10 +613,22 @@ __device__ void run_group(const DecodeParams& p, const SegInfo& si, const Plan& 
   auto tile_row = [&](int i) { return first + kThreads * min(i, n_tiles - 1); };
   auto vrow = [&](int row) { return vbase + int64_t(min(row, last)) * kRowBytes; };
 
+  // Ring: tile i's records live in stage i mod S.  The first S - 1 tiles are
+  // copied up front; the end of step i copies tile i + S - 1 into the stage
+  // of tile i - 1.  Each step begins with its V loads (for the next tile, or
+  // this tile without PIPE), so the compiler's own wait for V data never
+  // covers a record copy issued in the same step.
   constexpr int kStages = ring_stages<SW>();
-  constexpr int kAhead = kStages > 0 ? kStages - 1 : 0;           // tiles of records in flight
+  constexpr int kS = kStages > 0 ? kStages : 1;
+  constexpr int kAhead = kS - 1;
+  constexpr int kNV = kPairsPerLane * 2;                           // V load instructions per step
+  // Issued after tile i's record copies by the time step i waits for them, at
+  // the least (step 0 with the prologue): the copies of kAhead - 1 step ends
+  // and the V loads of kAhead step starts (PIPE; one fewer without, but at
+  // least step i's own).
+  constexpr int kWaitRec = (kAhead - 1) * SW + (PIPE ? kAhead : (kAhead > 1 ? kAhead - 1 : 1)) * kNV;
   const bool use_ring = SW > 0 && nw > 0 && n_tiles > 0;           // uniform
-  auto stage = [&](int i) { return sm.wv[wave].ring + (i % (kStages > 0 ? kStages : 1)) * kTile * SW; };
+  auto stage = [&](int i) { return sm.wv[wave].ring + (i % kS) * kTile * SW; };
   auto fetch_records = [&](int i) {
     if constexpr (SW > 0) {
       const int b = tile_row(i);
@@ -656,16 +668,9 @@ __device__ void run_group(const DecodeParams& p, const SegInfo& si, const Plan& 
   state_init(st);
   auto tile = [&](int i, VPair<B> (&cur)[kPairsPerLane], VPair<B> (&nxt)[kPairsPerLane]) {
     const int b = tile_row(i);
-    constexpr int kPipeLoads = PIPE ? kPairsPerLane * (B == 2 ? 2 : 2) : 0;
-    if (use_ring) fetch_records(i + kAhead);
     if constexpr (PIPE) load_pairs(nxt, i + 1);
     if constexpr (!PIPE) load_pairs(cur, i);
-    if (use_ring) {
-      // in flight after tile i's records: the next kAhead tiles' records and
-      // V loads (at least kAhead * (SW + kPipeLoads) instructions)
-      constexpr int kAfter = kAhead * (SW + kPipeLoads);
-      wait_vmem<(kAfter < 63 ? kAfter : 63)>();
-    }
+    if (use_ring) wait_vmem<(kWaitRec < 63 ? kWaitRec : 63)>();
     const int r = min(b + lane, last);
     // (with SW > 0 and no record words, nothing is read from the stage)
     const uint32_t* my = SW > 0 ? stage(i) + (r - b) * nw : rbase + int64_t(r) * nw;
@@ -680,6 +685,7 @@ __device__ void run_group(const DecodeParams& p, const SegInfo& si, const Plan& 
       pv_pair<G, B>(st.acc, cur[k], cf);
     }
     wave_lds_sync();
+    if (use_ring) fetch_records(i + kAhead);
   };
   for (int i = 0; i < n_tiles; i += 2) {
     tile(i, va, vb);
