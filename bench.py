@@ -201,7 +201,7 @@ def main():
     ap.add_argument("--no-flush", action="store_true", help="do not flush the last-level cache between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp16-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-segments", type=int, default=8)
+    ap.add_argument("--cpu-sample-segments", type=int, default=32)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run one plain 384 MiB device-to-device copy (for counter calibration)")
     args = ap.parse_args()
