@@ -204,13 +204,14 @@ def _apply_k_structure(w, K, seq, layer, scales, beta, device):
     return K
 
 
-def prefill_layer(w: Workload, seq: int, layer: int, device=None):
-    """Q [Hq][N][d], K [Hkv][N][d], V [Hkv][N][d] fp16 for one (sequence, layer)."""
+def prefill_layer(w: Workload, seq: int, layer: int, device=None, kv_only: bool = False):
+    """Q [Hq][N][d], K [Hkv][N][d], V [Hkv][N][d] fp16 for one (sequence, layer).
+    With kv_only, Q is not drawn (returned as None); K and V are unchanged."""
     H, Hk, N, d = w.n_q_heads, w.n_kv_heads, w.n_tokens, w.head_dim
-    Q = _normal_f16(w, (H, N, d), seq, layer, T_Q, device=device)
+    Q = None if kv_only else _normal_f16(w, (H, N, d), seq, layer, T_Q, device=device)
     K = _normal_f16(w, (Hk, N, d), seq, layer, T_K, device=device)
     V = _normal_f16(w, (Hk, N, d), seq, layer, T_V, device=device)
-    if w.biased:
+    if w.biased and Q is not None:
         Q[..., 0] = BIAS_ALPHA
     K = _apply_k_structure(w, K, seq, layer, k_channel_scales(w, seq, layer),
                            bias_per_token(w, seq, layer), device)

@@ -633,13 +633,19 @@ def decode_step(blob, lay: Layout, q, c_len: int, k_new=None, v_new=None):
         for l in range(lay.L):
             for h in range(lay.Hkv):
                 seg = lay.seg_index(s, l, h)
-                Kh, Vh, _, _ = unpack_segment(blob, lay, seg)
-                kc, vc = zone_c_rows(blob, lay, seg, n_c)
-                Ka = np.concatenate([Kh, kc])
-                Va = np.concatenate([Vh, vc])
-                qg = np.asarray(q[s, l, h * G:(h + 1) * G], np.float16).astype(np.float64)
-                out[s, l, h * G:(h + 1) * G] = attention(qg, Ka, Va)
+                out[s, l, h * G:(h + 1) * G] = decode_segment(blob, lay, seg, q[s, l, h * G:(h + 1) * G], n_c)
     return out
+
+
+def decode_segment(blob, lay: Layout, seg: int, qg, n_c: int):
+    """Attention output [G][d] (float64) of one segment's G query heads over its
+    kept tokens and its first n_c zone-C rows (the per-segment part of
+    decode_step; segments are independent)."""
+    Kh, Vh, _, _ = unpack_segment(blob, lay, seg)
+    kc, vc = zone_c_rows(blob, lay, seg, n_c)
+    Ka = np.concatenate([Kh, kc])
+    Va = np.concatenate([Vh, vc])
+    return attention(np.asarray(qg, np.float16).astype(np.float64), Ka, Va)
 
 
 # --------------------------------------------------------------------------

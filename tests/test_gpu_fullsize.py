@@ -1,0 +1,121 @@
+"""Pack and decode at the workloads' full sizes, checked on sampled segments.
+
+Each workload's full layout (every layer, every KV head, full context) is
+packed on the GPU layer by layer and decoded in the launch configuration the
+benchmark uses (one launch over all segments).  The oracle cannot score a
+128K or 256K context in reasonable time, so the allocation here is drawn at
+random with a bit mix like the workload's (fitted to the per-segment budgets)
+instead of being scored; the K/V values are the workload's own synthetic
+prefill tensors.  For a few sampled segments the oracle packs the same inputs
+(bytes compared exactly) and decodes them (outputs within 2e-3); segments
+are independent in both the format and the kernel.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from decode_attention_rdkv_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+TOL = 2e-3
+
+# workload -> (token bit mix over 0/2/4/8/16, channel bit mix)
+MIXES = {
+    "llama8b-32layer-n128k": ((0.83, 0.16, 0.062, 0.008, 0.00005), (0.71, 0.28, 0.0, 0.008, 0.0)),
+    "llama8b-layer-n32k": ((0.6, 0.2, 0.1, 0.05, 0.05), (0.5, 0.25, 0.15, 0.08, 0.02)),
+    "llama8b-batch16-n32k": ((0.5, 0.2, 0.15, 0.1, 0.05), (0.3, 0.3, 0.2, 0.15, 0.05)),
+    "qwen72b-80layer-n256k": ((0.6, 0.2, 0.1, 0.05, 0.05), (0.5, 0.25, 0.15, 0.08, 0.02)),
+}
+
+
+@pytest.fixture(scope="module")
+def gpu_lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from decode_attention_rdkv_amd import rdkv
+    rdkv.load()
+    return rdkv
+
+
+def _fit(bits: np.ndarray, budget: int) -> np.ndarray:
+    """Zero the units past the point where the running bit count exceeds the
+    budget, row by row (keeps a valid allocation: sum <= budget)."""
+    over = np.cumsum(bits.astype(np.int64), axis=-1) > budget
+    return np.where(over, 0, bits).astype(np.uint8)
+
+
+def _layer_bits(w, seq, layer):
+    tok_p, chan_p = MIXES[w.name]
+    bt, bc = synth.random_bits(w.n_kv_heads, w.n_tokens, 1000 * w.wid + 37 * seq + layer, tok_p=tok_p,
+                               chan_p=chan_p)
+    return _fit(bt, w.budget_v), _fit(bc, w.budget_k)
+
+
+@pytest.mark.parametrize("name", list(MIXES))
+def test_full_size_pack_and_decode_sampled(gpu_lib, name):
+    rdkv = gpu_lib
+    w = synth.WORKLOADS[name]
+    S, L, Hq, Hkv, N, G = w.n_seq, w.n_layers, w.n_q_heads, w.n_kv_heads, w.n_tokens, w.group
+    lay = rdkv.layout(rdkv.make_dims(S, L, Hq, Hkv, N), w.budget_v, w.budget_k, w.zone_c_capacity)
+    ol = O.Layout(S, L, Hq, Hkv, 128, N, w.budget_v, w.budget_k, w.zone_c_capacity)
+    n_seg = lay.n_seg
+    sampled = sorted({0, n_seg // 2 + 1, n_seg - 1})
+    print(f"{name}: {n_seg} segments, blob {lay.cache_bytes / 2**30:.2f} GiB, sampled {sampled}", flush=True)
+
+    cache = rdkv.cache_init(lay)
+    oblob = np.zeros(ol.cache_bytes, np.uint8)    # pages of unsampled segments stay untouched
+    oblob[:O.HEADER_BYTES] = np.frombuffer(ol.header_bytes(), np.uint8)
+    for seg in range(n_seg):                      # empty descriptors, as rdkv_cache_init writes them
+        O.pack_segment(ol, oblob, seg, np.zeros((0, 128), np.float16), np.zeros((0, 128), np.float16),
+                       np.zeros(0, np.uint8), np.zeros(128, np.uint8))
+    for l in range(L):                            # one pack call per layer, all sequences
+        Ks, Vs, bts, bcs = [], [], [], []
+        for s in range(S):
+            _, K, V = synth.prefill_layer(w, s, l, device=DEV, kv_only=True)
+            bt, bc = _layer_bits(w, s, l)
+            Ks.append(K), Vs.append(V), bts.append(bt), bcs.append(bc)
+            for h in range(Hkv):
+                seg = ol.seg_index(s, l, h)
+                if seg in sampled:
+                    O.pack_segment(ol, oblob, seg, K[h].cpu().numpy(), V[h].cpu().numpy(), bt[h], bc[h])
+        rdkv.pack(lay, cache, torch.stack(Ks)[:, None], torch.stack(Vs)[:, None],
+                  torch.from_numpy(np.stack(bts)[:, None]).to(DEV), torch.from_numpy(np.stack(bcs)[:, None]).to(DEV),
+                  layer_begin=l)
+        del Ks, Vs
+    torch.cuda.synchronize()
+
+    def seg_bytes(blob_slice, seg):
+        d0 = ol.desc_offset + seg * O.DESC_BYTES
+        b0 = ol.slot_base(seg)
+        return blob_slice(d0, d0 + O.DESC_BYTES), blob_slice(b0, b0 + ol.slot_bytes)
+
+    gpu_slice = lambda a, b: cache[a:b].cpu().numpy()
+    ora_slice = lambda a, b: oblob[a:b]
+    for seg in sampled:
+        gd, gs = seg_bytes(gpu_slice, seg)
+        od, os_ = seg_bytes(ora_slice, seg)
+        assert np.array_equal(gd, od), f"descriptor of segment {seg}"
+        assert np.array_equal(gs, os_), f"slot of segment {seg}"
+
+    ws = rdkv.decode_workspace(lay)
+    for step, append in enumerate((True, False)):
+        q, kn, vn = synth.decode_inputs(w, step)
+        c_len = 0 if append else 1
+        out = rdkv.decode(lay, cache, c_len, torch.from_numpy(q).to(DEV),
+                          torch.from_numpy(kn).to(DEV) if append else None,
+                          torch.from_numpy(vn).to(DEV) if append else None, workspace=ws)
+        out = out.cpu().numpy()
+        if append:
+            O.append_zone_c(oblob, ol, c_len, kn, vn)
+        n_c = c_len + 1 if append else c_len
+        for seg in sampled:
+            s, rem = divmod(seg, L * Hkv)
+            l, h = divmod(rem, Hkv)
+            ref = O.decode_segment(oblob, ol, seg, q[s, l, h * G:(h + 1) * G], n_c)
+            got = out[s, l, h * G:(h + 1) * G].astype(np.float64)
+            err = float((np.abs(got - ref).max(axis=-1) / np.maximum(np.abs(ref).max(axis=-1), 1e-30)).max())
+            print(f"  step {step} segment {seg}: rel err {err:.3g}", flush=True)
+            assert err <= TOL, f"step {step} segment {seg}: rel err {err:.3g}"
