@@ -194,6 +194,8 @@ struct __align__(16) Smem {
   uint32_t qpair[kPairSlots][G];         // fp16 query pairs matching the records' code pairs
   float qsum[4][G];                      // sum of q over the 8-, 4-, 2-bit channel parts
   uint16_t qperm[G][kHeadDim];           // query with channels in record order
+  uint16_t qnat[G][kHeadDim];            // query as given
+  uint8_t perm[kHeadDim];                // record order -> channel
   uint32_t coefh[kWaves][kTile / 2][G];  // fp16 (p*scale) of tile tokens (j, j + 32)
   WaveLds<G, SW> wv[kWaves];
   float part_ml[kWaves][G][2];
@@ -228,9 +230,14 @@ __device__ void build_query_tables(const DecodeParams& p, const SegInfo& si, con
   const int c8 = si.n_chan[0], c4 = c8 + si.n_chan[1], c2 = c4 + si.n_chan[2], c0 = c2 + si.n_chan[3];
   const uint16_t* qh = reinterpret_cast<const uint16_t*>(p.q) + seg * G * kHeadDim;
   const bool natural = pl.kind == 4;
+  // q and the permutation are read together (no dependent global read); the
+  // permutation is applied in LDS
+  for (int i = tid; i < G * kHeadDim; i += kThreads) sm.qnat[i / kHeadDim][i % kHeadDim] = qh[i];
+  if (tid < kHeadDim) sm.perm[tid] = natural ? uint8_t(tid) : perm[tid];
+  __syncthreads();
   for (int i = tid; i < G * kHeadDim; i += kThreads) {
     const int g = i / kHeadDim, c = i % kHeadDim;
-    sm.qperm[g][c] = qh[g * kHeadDim + (natural ? c : perm[c])];
+    sm.qperm[g][c] = sm.qnat[g][sm.perm[c]];
   }
   __syncthreads();
   for (int i = tid; i < kPairSlots * G; i += kThreads) {
@@ -794,8 +801,13 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParam
 template <int G, int SW>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G >= 8 ? 2 : 3))) void decode_chunk_kernel(DecodeParams p) {
   __shared__ Smem<G, SW> sm;
-  const int64_t seg = blockIdx.x / p.max_chunks;
-  const int k = int(blockIdx.x % p.max_chunks);
+  // Chunk-major order: every segment's first chunk, then every second chunk,
+  // ...  The full 2-bit chunks come first and the short tails, fp16 and zone-C
+  // chunks last, so the dispatcher's in-order fill ends on light work; and
+  // with n_seg a multiple of 8 all chunks of a segment land on one XCD (whose
+  // L2 then holds the segment's descriptor and query).
+  const int64_t seg = blockIdx.x % p.n_seg;
+  const int k = int(blockIdx.x / p.n_seg);
   const SegInfo si = load_segment(p, seg);
   const Plan pl = plan_chunk(si, si.zc_ok ? p.n_c : 0, p.chunk_tok2, k);
   const int tid = threadIdx.x;
@@ -853,6 +865,7 @@ hipError_t launch_chunks_g(const DecodeParams& p, hipStream_t stream) {
   // K record words staged through LDS, from the layout's bound on a record
   const int words = (p.rec_max + 3) / 4;
   if (words <= 8) return launch_chunks_gs<G, 8>(p, stream);
+  if (words <= 10) return launch_chunks_gs<G, 10>(p, stream);
   if (words <= 12) return launch_chunks_gs<G, 12>(p, stream);
   if (words <= 16) return launch_chunks_gs<G, 16>(p, stream);
   if (words <= 24) return launch_chunks_gs<G, 24>(p, stream);
