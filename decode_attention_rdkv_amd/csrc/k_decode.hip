@@ -308,19 +308,23 @@ __device__ inline void int_part(const uint32_t* rec, int& w, int& sl, int words,
   constexpr int kBits = 16 / P;
   constexpr uint32_t kMask = ((1u << kBits) - 1u) * 0x00010001u;
   uint32_t q[G];
-  for (int j = 0; j < words; ++j, ++w, sl += P) {
+  auto slot = [&](uint32_t x, int e) {
+    load_qp<G, SW>(sm, sl + e, q);
+    const uint32_t pr = (x >> (kBits * e)) & kMask;
+#pragma unroll
+    for (int g = 0; g < G; ++g) d[g] = dot2(pr, q[g], d[g]);
+  };
+  // full words without per-slot tests, then the last word's `tail` slots
+  for (int j = 0; j + 1 < words; ++j, ++w, sl += P) {
     const uint32_t x = rec[w];
-    const int n = j + 1 < words ? P : tail;
 #pragma unroll
-    for (int e = 0; e < P; ++e) {
-      if (e < n) {
-        load_qp<G, SW>(sm, sl + e, q);
-        const uint32_t pr = (x >> (kBits * e)) & kMask;
-#pragma unroll
-        for (int g = 0; g < G; ++g) d[g] = dot2(pr, q[g], d[g]);
-      }
-    }
+    for (int e = 0; e < P; ++e) slot(x, e);
   }
+  const uint32_t x = rec[w++];
+#pragma unroll
+  for (int e = 0; e < P; ++e)
+    if (e < tail) slot(x, e);
+  sl += P;
 }
 
 // s[g] = q_g . k_hat for one token whose record words are rec[0..).  The
@@ -502,27 +506,40 @@ __device__ inline void load_coefs(const Smem<G, SW>& sm, int wave, int j, uint32
   }
 }
 
-// Wave partial (m, l, o) into LDS.
+// Wave partial (m, l, o) into LDS.  acc is summed over the 4 token slots
+// (lanes cb, cb + 16, cb + 32, cb + 48) by two rounds of lane-half swaps:
+// v_permlane32_swap pairs values (2j, 2j + 1) into one register holding
+// their lane-32 sums in its two halves, v_permlane16_swap pairs those again,
+// so quarter q of register k ends up with value 4k + {0, 2, 1, 3}[q] of the
+// flat index 8g + e.
 template <int G, int B, int SW>
 __device__ inline void wave_finish(WaveState<G>& st, Smem<G, SW>& sm, int wave, int lane) {
-  const int cb = lane & 15, ts = lane >> 4;
+  const int cb = lane & 15, qr = lane >> 4;
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     st.l[g] = wave_reduce<false>(st.l[g]);
     st.z[g] = wave_reduce<false>(st.z[g]);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float v = st.acc[g][e];
-      v += __shfl_xor(v, 16, 64);
-      v += __shfl_xor(v, 32, 64);
-      st.acc[g][e] = v;
-    }
   }
-  if (ts == 0) {
+  constexpr int kN = 8 * G;
+  float u[kN / 2];
 #pragma unroll
-    for (int g = 0; g < G; ++g)
+  for (int j = 0; j < kN / 2; ++j) {
+    const float v0 = st.acc[(2 * j) / 8][(2 * j) % 8], v1 = st.acc[(2 * j + 1) / 8][(2 * j + 1) % 8];
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v0), __float_as_uint(v1), false, false);
+    u[j] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  const int sel = ((qr & 1) << 1) | (qr >> 1);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sm.wv[wave].o[g][cb * 8 + e] = fmaf(st.acc[g][e], channel_scale<B>(e), st.z[g]);
+  for (int k = 0; k < kN / 4; ++k) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(u[2 * k]), __float_as_uint(u[2 * k + 1]), false,
+                                                    false);
+    const float t = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    const int g = k / 2, e = 4 * (k & 1) + sel;
+    float sc;
+    if constexpr (B == 2) sc = ldexpf(1.0f, 24 - 2 * (e < 5 ? e : e - 5));
+    else if constexpr (B == 4) sc = (e & 1) ? kTwo24 / 16.0f : kTwo24;
+    else sc = channel_scale<B>(0);
+    sm.wv[wave].o[g][cb * 8 + e] = fmaf(t, sc, st.z[g]);
   }
   if (lane == 0) {
 #pragma unroll
