@@ -176,16 +176,23 @@ __device__ inline Plan plan_chunk(const SegInfo& si, int n_c, int chunk_tok2, in
 
 // ---------------------------------------------------------------- shared memory
 
-// LDS ring of K-record stages per wave: three stages (two tiles in flight)
-// for records of up to 16 words, two (one in flight) for longer ones.
+// LDS ring of K-record stages per wave.  A stage holds a tile's record block
+// copied in 16-byte chunks from the 16-byte-aligned address at or below its
+// start (up to 3 words before it): stage_copies 1-KiB copies of 64 lanes.
+// Three stages (two tiles in flight) while that stays within 9 KiB per wave,
+// else two (one in flight).
 template <int SW>
-__host__ __device__ constexpr int ring_stages() { return SW == 0 ? 0 : SW <= 16 ? 3 : 2; }
+__host__ __device__ constexpr int stage_copies() { return (kTile * SW + 3 + 255) / 256; }
+template <int SW>
+__host__ __device__ constexpr int stage_words() { return stage_copies<SW>() * 256; }
+template <int SW>
+__host__ __device__ constexpr int ring_stages() { return SW == 0 ? 0 : 3 * stage_words<SW>() <= 2304 ? 3 : 2; }
 
 // Per wave, the record ring and, once the wave's last tile is done, its
 // partial output share one region.
 template <int G, int SW>
 union __align__(16) WaveLds {
-  uint32_t ring[SW > 0 ? ring_stages<SW>() * kTile * SW : 1];
+  uint32_t ring[SW > 0 ? ring_stages<SW>() * stage_words<SW>() : 1];
   float o[G][kHeadDim];
 };
 
@@ -557,51 +564,40 @@ __device__ inline uint32_t lds_addr(const void* p) {
   return uint32_t(size_t((const __attribute__((address_space(3))) void*)p));
 }
 
-// One global_load_lds_dword: 64 lanes each copy a dword into LDS at
-// lds + 4 * lane.  Written as inline assembly, so the compiler's memory-
-// counter bookkeeping does not see it (it would otherwise wait for every
-// outstanding copy before any LDS read); the tile loop waits explicitly.
-// M0 (the LDS base of the copy) is saved and restored around it.
-__device__ inline void lds_copy_s(const uint32_t* base, uint32_t voff, uint32_t lds) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dword %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(voff), "s"(base), "s"(lds)
-      : "memory");
-}
-__device__ inline void lds_copy_v(const uint32_t* addr, uint32_t lds) {
+// One global_load_lds_dwordx4: 64 lanes each copy 16 bytes (from a 16-byte-
+// aligned address) into LDS at lds + 16 * lane.  Written as inline assembly,
+// so the compiler's memory-counter bookkeeping does not see it (it would
+// otherwise wait for every outstanding copy before any LDS read); the tile
+// loop waits explicitly.  M0 (the LDS base of the copy) is saved and restored
+// around it.
+__device__ inline void lds_copy16(const uint32_t* addr, uint32_t lds) {
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dword %1, off\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
       : "v"(addr), "s"(lds)
       : "memory");
 }
 
-// Copies a tile's K records (the n_words >= 1 words at src) into an LDS stage
-// of kTile * SW words: always exactly SW copies of 64 dwords.  A full tile
-// (n_words = 64 nw) copies whole 64-word rows from a uniform base at a fixed
-// lane offset; the copies past them reread the first row.  A partial tile
-// clamps each lane's index to the block.
+// Words between the 16-byte-aligned address at or below p and p.
+__device__ inline int misalign_words(const uint32_t* p) { return int((reinterpret_cast<uintptr_t>(p) >> 2) & 3); }
+
+// Copies a tile's K records (the n_words >= 1 words at src) into an LDS stage:
+// always exactly stage_copies<SW> copies; the 16-byte chunks past the block
+// reread its last chunk, which lies inside the 256-aligned record region.
+// The block starts misalign_words(src) words into the stage.
 template <int SW>
-__device__ inline void dma_records(const uint32_t* src, int nw, int n_words, uint32_t* stage, int lane) {
+__device__ inline void dma_records(const uint32_t* src, int n_words, uint32_t* stage, int lane) {
+  const int m = misalign_words(src);
+  const uint32_t* base = src - m;
+  const int n16 = (m + n_words + 3) >> 2;
   const uint32_t lds = lds_addr(stage);
-  if (n_words == kTile * nw) {
 #pragma unroll
-    for (int i = 0; i < SW; ++i) lds_copy_s(src + (i < nw ? i * 64 : 0), uint32_t(lane) * 4u, lds + i * 256);
-  } else {
-#pragma unroll
-    for (int i = 0; i < SW; ++i) lds_copy_v(src + min(i * 64 + lane, n_words - 1), lds + i * 256);
-  }
+  for (int i = 0; i < stage_copies<SW>(); ++i) lds_copy16(base + 4 * min(i * 64 + lane, n16 - 1), lds + i * 1024);
 }
 
 // Waits until at most N vector-memory instructions of this wave are in
@@ -650,13 +646,14 @@ __device__ void run_group(const DecodeParams& p, const SegInfo& si, const Plan& 
   // the least (step 0 with the prologue): the copies of kAhead - 1 step ends
   // and the V loads of kAhead step starts (PIPE; one fewer without, but at
   // least step i's own).
-  constexpr int kWaitRec = (kAhead - 1) * SW + (PIPE ? kAhead : (kAhead > 1 ? kAhead - 1 : 1)) * kNV;
+  constexpr int kCopies = SW > 0 ? stage_copies<SW>() : 0;          // record copies per step
+  constexpr int kWaitRec = (kAhead - 1) * kCopies + (PIPE ? kAhead : (kAhead > 1 ? kAhead - 1 : 1)) * kNV;
   const bool use_ring = SW > 0 && nw > 0 && n_tiles > 0;           // uniform
-  auto stage = [&](int i) { return sm.wv[wave].ring + (i % kS) * kTile * SW; };
+  auto stage = [&](int i) { return sm.wv[wave].ring + (i % kS) * (SW > 0 ? stage_words<SW>() : 0); };
   auto fetch_records = [&](int i) {
     if constexpr (SW > 0) {
       const int b = tile_row(i);
-      dma_records<SW>(rbase + int64_t(b) * nw, nw, min(kTile, pl.end - b) * nw, stage(i), lane);
+      dma_records<SW>(rbase + int64_t(b) * nw, min(kTile, pl.end - b) * nw, stage(i), lane);
     }
   };
   // V pairs of tile i: a full tile addresses rows from one uniform tile base
@@ -697,7 +694,8 @@ __device__ void run_group(const DecodeParams& p, const SegInfo& si, const Plan& 
     if (use_ring) wait_vmem<(kWaitRec < 63 ? kWaitRec : 63)>();
     const int r = min(b + lane, last);
     // (with SW > 0 and no record words, nothing is read from the stage)
-    const uint32_t* my = SW > 0 ? stage(i) + (r - b) * nw : rbase + int64_t(r) * nw;
+    const uint32_t* my = SW > 0 ? stage(i) + misalign_words(rbase + int64_t(b) * nw) + (r - b) * nw
+                                : rbase + int64_t(r) * nw;
     float s[G], vs, vz;
     record_logits<G, SW>(my, ks, nw, B < 16, sm, s, vs, vz);
     softmax_tile<G, SW>(st, s, b + lane < pl.end, vs, vz, sm, wave, lane);
