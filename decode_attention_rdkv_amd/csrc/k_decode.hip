@@ -642,12 +642,17 @@ __device__ void run_group(const DecodeParams& p, const SegInfo& si, const Plan& 
   constexpr int kS = kStages > 0 ? kStages : 1;
   constexpr int kAhead = kS - 1;
   constexpr int kNV = kPairsPerLane * 2;                           // V load instructions per step
-  // Issued after tile i's record copies by the time step i waits for them, at
-  // the least (step 0 with the prologue): the copies of kAhead - 1 step ends
-  // and the V loads of kAhead step starts (PIPE; one fewer without, but at
-  // least step i's own).
+  // V loads per step issued before the wait (PIPE: tile i + 1's; 8-bit: this
+  // tile's) and after it (fp16 rows: each pair just before its products).
+  constexpr bool kLateV = !PIPE && B == 16;
+  constexpr int kPre = kLateV ? 0 : kNV, kPost = kLateV ? kNV : 0;
   constexpr int kCopies = SW > 0 ? stage_copies<SW>() : 0;          // record copies per step
-  constexpr int kWaitRec = (kAhead - 1) * kCopies + (PIPE ? kAhead : (kAhead > 1 ? kAhead - 1 : 1)) * kNV;
+  // Issued after tile i's record copies by the time step i waits for them,
+  // at the least: with three stages, step 0 (after the prologue) or a steady
+  // step (two step starts, one step body, one refill); with two, one start.
+  constexpr int kWaitRec =
+      kS == 3 ? kCopies + (((PIPE ? kNV : 0) + kPre) < (2 * kPre + kPost) ? (PIPE ? kNV : 0) + kPre : 2 * kPre + kPost)
+              : kPre;
   const bool use_ring = SW > 0 && nw > 0 && n_tiles > 0;           // uniform
   auto stage = [&](int i) { return sm.wv[wave].ring + (i % kS) * (SW > 0 ? stage_words<SW>() : 0); };
   auto fetch_records = [&](int i) {
@@ -659,6 +664,14 @@ __device__ void run_group(const DecodeParams& p, const SegInfo& si, const Plan& 
   // V pairs of tile i: a full tile addresses rows from one uniform tile base
   // plus a fixed lane offset; a partial one clamps each row to the chunk.
   const uint32_t lane_off = uint32_t(ts * kRowBytes + cb * (kRowBytes / 16));
+  auto load_pair = [&](int i, int k) {
+    const int b = tile_row(i), j = ts + 4 * k;
+    if (b + kTile <= pl.end) {
+      const uint8_t* lp = vbase + int64_t(b) * kRowBytes + lane_off;
+      return load_vpair<B>(lp + 4 * k * kRowBytes, lp + (4 * k + 32) * kRowBytes, 0);
+    }
+    return load_vpair<B>(vrow(b + j), vrow(b + j + 32), cb);
+  };
   auto load_pairs = [&](VPair<B> (&v)[kPairsPerLane], int i) {
     const int b = tile_row(i);
     if (b + kTile <= pl.end) {
@@ -690,7 +703,7 @@ __device__ void run_group(const DecodeParams& p, const SegInfo& si, const Plan& 
   auto tile = [&](int i, VPair<B> (&cur)[kPairsPerLane], VPair<B> (&nxt)[kPairsPerLane]) {
     const int b = tile_row(i);
     if constexpr (PIPE) load_pairs(nxt, i + 1);
-    if constexpr (!PIPE) load_pairs(cur, i);
+    if constexpr (!PIPE && !kLateV) load_pairs(cur, i);
     if (use_ring) wait_vmem<(kWaitRec < 63 ? kWaitRec : 63)>();
     const int r = min(b + lane, last);
     // (with SW > 0 and no record words, nothing is read from the stage)
@@ -704,7 +717,12 @@ __device__ void run_group(const DecodeParams& p, const SegInfo& si, const Plan& 
     for (int k = 0; k < kPairsPerLane; ++k) {
       uint32_t cf[G];
       load_coefs<G, SW>(sm, wave, ts + 4 * k, cf);
-      pv_pair<G, B>(st.acc, cur[k], cf);
+      if constexpr (kLateV) {
+        const VPair<B> v = load_pair(i, k);
+        pv_pair<G, B>(st.acc, v, cf);
+      } else {
+        pv_pair<G, B>(st.acc, cur[k], cf);
+      }
     }
     wave_lds_sync();
     if (use_ring) fetch_records(i + kAhead);
