@@ -4,7 +4,7 @@
 //   w_tok[h][t] = sum_{g in group(h)} sum_{tau >= t} exp(s_{g,tau,t} - LSE_{g,tau})
 //   with s = Q_g[tau].K_h[t] / sqrt(d) and LSE the causal row log-sum-exp.
 //
-// Two passes over the causal score matrix on MFMA (v_mfma_f32_16x16x16_f16,
+// Two passes over the causal score matrix on MFMA (v_mfma_f32_16x16x32_f16,
 // fp16 inputs, fp32 accumulation):
 //   score_lse_kernel     workgroup = 64 query rows of one query head; walks the
 //                        key blocks 0..diagonal, keeps a per-lane online
@@ -14,6 +14,10 @@
 //                        summing exp2(s' - LSE') down each key column.  A key
 //                        block is owned by one workgroup, so no atomics and the
 //                        summation order is fixed.
+// The streamed 64x128 tile (K rows, or Q rows and their LSE) is double
+// buffered in LDS: the next tile's global loads are in flight while the
+// current one is multiplied.  Masks are applied only on the diagonal block
+// and the ragged last block.
 // Plus two bandwidth kernels: var_tok (one wave per token) and the column
 // norms behind w_chan (partial sums in fp64, reduced in a fixed order).
 #include "rdkv_internal.h"
@@ -21,7 +25,6 @@
 namespace rdkv {
 namespace {
 
-typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
 constexpr int kB = 64;           // rows per block (queries or keys)
@@ -39,47 +42,57 @@ struct ScoreArgs {
   float* w_tok;    // [S*L][Hkv][N]
 };
 
-// Cooperative load of 64 rows x 128 halves into an LDS tile; rows >= N are 0.
-__device__ inline void load_tile(_Float16 (*tile)[kPad], const __half* src, int64_t row0, int64_t N) {
-  for (int idx = threadIdx.x; idx < kB * 16; idx += kThreads) {
-    const int r = idx >> 4, c = idx & 15;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (row0 + r < N) v = reinterpret_cast<const uint4*>(src + (row0 + r) * kHeadDim)[c];
-    *reinterpret_cast<uint4*>(&tile[r][c * 8]) = v;
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+
+// A 64 x 128 fp16 tile moving global -> registers -> LDS: each thread holds
+// 4 of its 1024 16-byte pieces; rows >= N are 0.
+struct TileRegs {
+  uint4 v[4];
+};
+__device__ inline void tile_fetch(TileRegs& t, const __half* src, int64_t row0, int64_t N) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = threadIdx.x + kThreads * i, r = idx >> 4, c = idx & 15;
+    t.v[i] = row0 + r < N ? reinterpret_cast<const uint4*>(src + (row0 + r) * kHeadDim)[c] : make_uint4(0, 0, 0, 0);
+  }
+}
+__device__ inline void tile_store(const TileRegs& t, _Float16 (*tile)[kPad]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = threadIdx.x + kThreads * i, r = idx >> 4, c = idx & 15;
+    *reinterpret_cast<uint4*>(&tile[r][c * 8]) = t.v[i];
   }
 }
 
-// A-operand fragments of 16 rows: lane holds row (lane % 16), halves
-// 16*kk + 4*(lane/16) .. +3 for kk = 0..7.
-__device__ inline void load_rows_frag(h4 (&a)[8], const __half* src, int64_t row, int64_t N) {
+// A-operand fragments of 16 rows for the 16x16x32 MFMA: lane holds row
+// (lane % 16), halves 32*kk + 8*(lane/16) .. +7 for kk = 0..3.
+__device__ inline void load_rows_frag(h8 (&a)[4], const __half* src, int64_t row, int64_t N) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) {
-    if (row < N) {
-      const uint2 v = *reinterpret_cast<const uint2*>(src + row * kHeadDim + 16 * kk + 4 * (lane >> 4));
-      a[kk] = __builtin_bit_cast(h4, v);
-    } else {
-      a[kk] = h4{0, 0, 0, 0};
-    }
+  for (int kk = 0; kk < 4; ++kk) {
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (row < N) v = *reinterpret_cast<const uint4*>(src + row * kHeadDim + 32 * kk + 8 * (lane >> 4));
+    a[kk] = __builtin_bit_cast(h8, v);
   }
 }
 
 // C[i][j] = sum_k A[i][k] * T[16*sub + j][k] for the wave's 16 rows of A and
-// 16 rows of the LDS tile T.  Lane holds C[4*(lane/16) + r][lane % 16].
-__device__ inline f4 tile_product(const h4 (&a)[8], const _Float16 (*tile)[kPad], int sub) {
+// 16 rows of the LDS tile T (B fragments in the same k order as A).  Lane
+// holds C[4*(lane/16) + r][lane % 16].
+__device__ inline f4 tile_product(const h8 (&a)[4], const _Float16 (*tile)[kPad], int sub) {
   const int lane = threadIdx.x & 63;
   f4 c = {0.f, 0.f, 0.f, 0.f};
-  const _Float16* trow = &tile[16 * sub + (lane & 15)][4 * (lane >> 4)];
+  const _Float16* trow = &tile[16 * sub + (lane & 15)][8 * (lane >> 4)];
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) {
-    const h4 b = *reinterpret_cast<const h4*>(trow + 16 * kk);
-    c = __builtin_amdgcn_mfma_f32_16x16x16f16(a[kk], b, c, 0, 0, 0);
+  for (int kk = 0; kk < 4; ++kk) {
+    const h8 b = *reinterpret_cast<const h8*>(trow + 32 * kk);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[kk], b, c, 0, 0, 0);
   }
   return c;
 }
 
 __global__ __launch_bounds__(kThreads) void score_lse_kernel(ScoreArgs a) {
-  __shared__ _Float16 ks[kB][kPad];
+  __shared__ _Float16 ks[2][kB][kPad];
   const int64_t N = a.N;
   const int nqb = int(cdiv(N, kB));
   const int qb = nqb - 1 - int(blockIdx.x);   // long rows first
@@ -91,7 +104,7 @@ __global__ __launch_bounds__(kThreads) void score_lse_kernel(ScoreArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t row0 = int64_t(qb) * kB + 16 * wave;
 
-  h4 qa[8];
+  h8 qa[4];
   load_rows_frag(qa, Qh, row0 + (lane & 15), N);
   float m[4], s[4];
 #pragma unroll
@@ -99,19 +112,23 @@ __global__ __launch_bounds__(kThreads) void score_lse_kernel(ScoreArgs a) {
     m[r] = -INFINITY;
     s[r] = 0.f;
   }
+  TileRegs nxt;
+  tile_fetch(nxt, Kh, 0, N);
+  tile_store(nxt, ks[0]);
   for (int kb = 0; kb <= qb; ++kb) {
+    if (kb < qb) tile_fetch(nxt, Kh, int64_t(kb + 1) * kB, N);
     __syncthreads();
-    load_tile(ks, Kh, int64_t(kb) * kB, N);
-    __syncthreads();
+    const _Float16 (*cur)[kPad] = ks[kb & 1];
+    const bool edge = kb == qb || int64_t(kb + 1) * kB > N;   // diagonal or ragged block
     float t[4][4];
 #pragma unroll
     for (int sub = 0; sub < 4; ++sub) {
-      const f4 c = tile_product(qa, ks, sub);
+      const f4 c = tile_product(qa, cur, sub);
       const int64_t key = int64_t(kb) * kB + 16 * sub + (lane & 15);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int64_t row = row0 + 4 * (lane >> 4) + r;
-        t[sub][r] = (key > row || key >= N) ? -INFINITY : c[r] * kLog2eOverSqrtD;
+        t[sub][r] = (edge && (key > row || key >= N)) ? -INFINITY : c[r] * kLog2eOverSqrtD;
       }
     }
 #pragma unroll
@@ -119,12 +136,14 @@ __global__ __launch_bounds__(kThreads) void score_lse_kernel(ScoreArgs a) {
       const float mb = fmaxf(fmaxf(t[0][r], t[1][r]), fmaxf(t[2][r], t[3][r]));
       const float mn = fmaxf(m[r], mb);
       if (mn == -INFINITY) continue;
-      float acc = (m[r] == -INFINITY) ? 0.f : s[r] * exp2f(m[r] - mn);
+      float acc = s[r];
+      if (mn > m[r]) acc = m[r] == -INFINITY ? 0.f : acc * __builtin_amdgcn_exp2f(m[r] - mn);
 #pragma unroll
-      for (int sub = 0; sub < 4; ++sub) acc += (t[sub][r] == -INFINITY) ? 0.f : exp2f(t[sub][r] - mn);
+      for (int sub = 0; sub < 4; ++sub) acc += __builtin_amdgcn_exp2f(t[sub][r] - mn);
       s[r] = acc;
       m[r] = mn;
     }
+    if (kb < qb) tile_store(nxt, ks[(kb + 1) & 1]);
   }
   // merge the 16 lanes that hold the same rows
 #pragma unroll
@@ -144,8 +163,8 @@ __global__ __launch_bounds__(kThreads) void score_lse_kernel(ScoreArgs a) {
 }
 
 __global__ __launch_bounds__(kThreads) void score_colsum_kernel(ScoreArgs a) {
-  __shared__ _Float16 qs[kB][kPad];
-  __shared__ float ls[kB];
+  __shared__ _Float16 qs[2][kB][kPad];
+  __shared__ float ls[2][kB];
   const int64_t N = a.N;
   const int nqb = int(cdiv(N, kB));
   const int kb = blockIdx.x;                  // short key indices have the most rows: first
@@ -155,36 +174,59 @@ __global__ __launch_bounds__(kThreads) void score_colsum_kernel(ScoreArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t key0 = int64_t(kb) * kB + 16 * wave;
 
-  h4 ka[8];
+  h8 ka[4];
   load_rows_frag(ka, Kh, key0 + (lane & 15), N);
   double tot[4] = {0.0, 0.0, 0.0, 0.0};
-  for (int g = 0; g < a.G; ++g) {
+  // steps: (g, qb) for g in heads, qb in [kb, nqb)
+  const int per = nqb - kb, n_steps = a.G * per;
+  auto step_src = [&](int st, const __half*& Qh, const float*& lse, int& qb) {
+    const int g = st / per;
+    qb = kb + st % per;
     const int hq = h * a.G + g;
-    const __half* Qh = a.Q + ((sl * a.Hq + hq) * N) * kHeadDim;
-    const float* lse = a.lse + (sl * a.Hq + hq) * N;
-    for (int qb = kb; qb < nqb; ++qb) {
-      __syncthreads();
-      load_tile(qs, Qh, int64_t(qb) * kB, N);
-      if (threadIdx.x < kB) {
-        const int64_t row = int64_t(qb) * kB + threadIdx.x;
-        ls[threadIdx.x] = row < N ? lse[row] : 0.f;
-      }
-      __syncthreads();
-      float part[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int sub = 0; sub < 4; ++sub) {
-        const f4 c = tile_product(ka, qs, sub);
-        const int64_t query = int64_t(qb) * kB + 16 * sub + (lane & 15);
-        const float lq = ls[16 * sub + (lane & 15)];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int64_t key = key0 + 4 * (lane >> 4) + r;
-          if (query >= key && query < N) part[r] += exp2f(c[r] * kLog2eOverSqrtD - lq);
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) tot[r] += double(part[r]);
+    Qh = a.Q + ((sl * a.Hq + hq) * N) * kHeadDim;
+    lse = a.lse + (sl * a.Hq + hq) * N;
+  };
+  TileRegs nxt;
+  float lnext = 0.f;
+  auto fetch = [&](int st) {
+    const __half* Qh;
+    const float* lse;
+    int qb;
+    step_src(st, Qh, lse, qb);
+    tile_fetch(nxt, Qh, int64_t(qb) * kB, N);
+    if (threadIdx.x < kB) {
+      const int64_t row = int64_t(qb) * kB + threadIdx.x;
+      lnext = row < N ? lse[row] : 0.f;
     }
+  };
+  auto store = [&](int buf) {
+    tile_store(nxt, qs[buf]);
+    if (threadIdx.x < kB) ls[buf][threadIdx.x] = lnext;
+  };
+  fetch(0);
+  store(0);
+  for (int st = 0; st < n_steps; ++st) {
+    if (st + 1 < n_steps) fetch(st + 1);
+    __syncthreads();
+    const int buf = st & 1;
+    const int qb = kb + st % per;
+    const bool edge = qb == kb || int64_t(qb + 1) * kB > N;
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int sub = 0; sub < 4; ++sub) {
+      const f4 c = tile_product(ka, qs[buf], sub);
+      const int64_t query = int64_t(qb) * kB + 16 * sub + (lane & 15);
+      const float lq = ls[buf][16 * sub + (lane & 15)];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t key = key0 + 4 * (lane >> 4) + r;
+        const float e = __builtin_amdgcn_exp2f(fmaf(c[r], kLog2eOverSqrtD, -lq));
+        part[r] += (edge && (query < key || query >= N)) ? 0.f : e;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) tot[r] += double(part[r]);
+    if (st + 1 < n_steps) store((st + 1) & 1);
   }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
