@@ -8,7 +8,8 @@ seeded synthetic Q/K/V are drawn on the GPU, scored (rdkv_score), allocated
 (rdkv_allocate) and packed (rdkv_pack) into one blob.  Timed: exactly
 --steps decode steps (rdkv_decode: append one token to zone C and attend over
 every layer's kept tokens), each bracketed by HIP events on the stream the
-kernel runs on, with the 256 MB last-level cache flushed between steps so
+kernel runs on, with the 256 MB last-level cache cleared between steps (by
+reading a 1 GiB buffer, which leaves no dirty lines behind) so
 every step streams the cache from HBM.
 
 Prints one JSON line: the metric of the decode step (us per token), the
@@ -110,7 +111,17 @@ def time_decode(rdkv, torch, lay, cache, q, kn, vn, steps, warmup, flush):
     """
     ws = rdkv.decode_workspace(lay)
     out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
-    fbuf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda") if flush else None
+    # The caches are cleared between steps by READING a 1 GiB buffer: it
+    # evicts the blob from the L2s and the 256 MB last-level cache without
+    # leaving dirty lines whose write-back would land inside the next step
+    # (a 1 GiB fill costs the following decode step ~20-50 us of such
+    # write-back traffic that is not the decode's own).
+    fbuf = torch.ones(1 << 27, dtype=torch.int64, device="cuda") if flush else None
+
+    def clear_caches():
+        if fbuf is not None:
+            fbuf.sum()
+
     n_c = 1
 
     def step():
@@ -123,8 +134,7 @@ def time_decode(rdkv, torch, lay, cache, q, kn, vn, steps, warmup, flush):
     for i in range(warmup):
         step()
         merge()
-        if flush:
-            fbuf.fill_(i & 255)
+        clear_caches()
     torch.cuda.synchronize()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     t0 = time.perf_counter()
@@ -134,8 +144,7 @@ def time_decode(rdkv, torch, lay, cache, q, kn, vn, steps, warmup, flush):
         ev[i][1].record()
         merge()
         ev[i][2].record()
-        if flush:
-            fbuf.fill_((i + 7) & 255)
+        clear_caches()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     chunk = np.array([a.elapsed_time(b) for a, b, _ in ev])
