@@ -250,6 +250,7 @@ __device__ void build_query_tables(const DecodeParams& p, const SegInfo& si, con
   for (int i = tid; i < kPairSlots * G; i += kThreads) {
     const int sl = i / G, g = i % G;
     int pa, pb, hi_end;   // permuted channel positions of the pair
+    int shift = 0;        // log2 of the in-place position scale of the slot's codes
     if (natural) {
       pa = 2 * sl, pb = 2 * sl + 1, hi_end = kHeadDim;
     } else if (sl < rs.w16) {
@@ -260,11 +261,20 @@ __device__ void build_query_tables(const DecodeParams& p, const SegInfo& si, con
     } else if (sl < rs.w16 + 2 * rs.w8 + 4 * rs.w4) {
       const int t = sl - rs.w16 - 2 * rs.w8;
       pa = c4 + 8 * (t >> 2) + (t & 3), pb = pa + 4, hi_end = c2;
+      shift = 4 * (t & 1);
     } else {
       const int t = sl - rs.w16 - 2 * rs.w8 - 4 * rs.w4;
       pa = c2 + 16 * (t >> 3) + (t & 7), pb = pa + 8, hi_end = c0;
+      shift = 2 * (t & 3);
     }
-    auto qbits = [&](int pos) -> uint32_t { return pos < hi_end && pos < kHeadDim ? sm.qperm[g][pos] : 0u; };
+    // the slot's codes reach dot2 as code * 2^shift (masked in place), so the
+    // query is stored divided by 2^shift (exact unless it becomes subnormal)
+    auto qbits = [&](int pos) -> uint32_t {
+      if (pos >= hi_end || pos >= kHeadDim) return 0u;
+      const uint16_t h = sm.qperm[g][pos];
+      if (shift == 0) return h;
+      return __half_as_ushort(__float2half_rn(ldexpf(__half2float(__ushort_as_half(h)), -shift)));
+    };
     sm.qpair[sl][g] = qbits(pa) | (qbits(pb) << 16);
   }
   if (!natural) {
@@ -309,6 +319,10 @@ __device__ inline QkShape qk_shape(const SegInfo& si) {
 
 // d[g] += q_g . codes over one integer part (P pair slots per word).  Slots
 // past the part's last channel are skipped; their table entries stay unread.
+// A word's pair e = (channel e, channel e + P) sits at bits kBits*e of both
+// halves; the first P/2 pairs are masked in place, the rest after one shift
+// by 8, so a code arrives as code * 2^(kBits * (e mod P/2)) * 2^-24, which the
+// query table has divided out.
 template <int G, int SW, int P>
 __device__ inline void int_part(const uint32_t* rec, int& w, int& sl, int words, int tail, const Smem<G, SW>& sm,
                                 float (&d)[G]) {
@@ -317,7 +331,8 @@ __device__ inline void int_part(const uint32_t* rec, int& w, int& sl, int words,
   uint32_t q[G];
   auto slot = [&](uint32_t x, int e) {
     load_qp<G, SW>(sm, sl + e, q);
-    const uint32_t pr = (x >> (kBits * e)) & kMask;
+    const int half = e >= P / 2;
+    const uint32_t pr = (half ? x >> 8 : x) & (kMask << (kBits * (e - half * (P / 2))));
 #pragma unroll
     for (int g = 0; g < G; ++g) d[g] = dot2(pr, q[g], d[g]);
   };
