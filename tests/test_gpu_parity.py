@@ -58,6 +58,10 @@ def _bits_case(name, n_seg, N, seed):
         bc[:, :5] = 16
         bc[:, 5:8] = 8
         bc[:, 8:9] = 2
+    elif name == "mid_k":                    # 12-word record bound: the SW = 12 decode path
+        bc[:] = 0
+        bc[:, 10:30] = 8
+        bc[:, 40:45] = 2
     elif name == "empty_and_single":
         bt[0] = 0
         if n_seg > 1:
@@ -76,6 +80,7 @@ PACK_CASES = [
     ("k_dropped", 2, 1, 4, 2, 64, 1),
     ("odd16", 1, 1, 4, 1, 1500, 3),
     ("empty_and_single", 1, 1, 2, 2, 200, 2),
+    ("mid_k", 1, 1, 8, 2, 700, 4),
 ]
 
 
