@@ -747,6 +747,9 @@ __device__ void run_group(const DecodeParams& p, const SegInfo& si, const Plan& 
     if (i + 1 >= n_tiles) break;
     tile(i + 1, vb, va);
   }
+  // The last steps copied (clamped) records into ring stages that the partial
+  // output below overwrites; those copies must land before it does.
+  if (use_ring) wait_vmem<0>();
   wave_finish<G, B, SW>(st, sm, wave, lane);
 }
 

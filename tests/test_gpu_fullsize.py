@@ -119,3 +119,13 @@ def test_full_size_pack_and_decode_sampled(gpu_lib, name):
             err = float((np.abs(got - ref).max(axis=-1) / np.maximum(np.abs(ref).max(axis=-1), 1e-30)).max())
             print(f"  step {step} segment {seg}: rel err {err:.3g}", flush=True)
             assert err <= TOL, f"step {step} segment {seg}: rel err {err:.3g}"
+
+    # Every segment (not only the sampled ones): repeated decodes of the same
+    # cache and query agree bit for bit.  The chunk kernel's LDS record ring is
+    # filled by asynchronous copies; a copy landing late (for instance in the
+    # region a wave's partial output reuses) shows up here as a difference.
+    q = torch.from_numpy(synth.decode_inputs(w, 1)[0]).to(DEV)
+    outs = [rdkv.decode(lay, cache, 1, q, None, None, workspace=ws) for _ in range(3)]
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0]), "repeated decodes differ"
+    assert bool(torch.isfinite(outs[0]).all()), "non-finite decode output"
