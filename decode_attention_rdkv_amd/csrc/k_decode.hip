@@ -395,28 +395,52 @@ constexpr int kPairsPerLane = kTile / 2 / 4;
 
 // The lane's channels of tokens (j, j + 32) of one V group, as loaded.
 template <int B> struct VPair;
-template <> struct VPair<2> { uint32_t a, b; };      // 16 bits per token (joined at use, so a
-                                                     // prefetch is not waited for at its load)
+template <> struct VPair<2> { uint32_t a, b; };      // the dword holding the lane's 16 bits of each
+                                                     // token (the half is picked at use)
 template <> struct VPair<4> { uint32_t a, b; };      // 32 bits per token
 template <> struct VPair<8> { uint2 a, b; };         // 64 bits per token
 template <> struct VPair<16> { uint4 a, b; };        // 8 fp16 per token
 
+// Byte offset, within a V row of B-bit codes, of what lane block cb loads.
 template <int B>
-__device__ inline VPair<B> load_vpair(const uint8_t* row0, const uint8_t* row1, int cb) {
+__device__ constexpr int lane_row_offset(int cb) {
+  return B == 2 ? (cb >> 1) * 4 : cb * (kHeadDim * B / 8 / 16);
+}
+
+// Raw buffer resource over [p, p + bytes): stride 0, range checked per dword,
+// so reads at or past `bytes` return zeros and touch no memory.
+constexpr int kBufferFlags = 0x00020000;
+__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, int(bytes), kBufferFlags);
+}
+
+// Tokens (j, j + 32) from a buffer whose range starts at the tile's first row:
+// the lane's parts of the rows at byte offsets off0 and off1.
+template <int B>
+__device__ inline VPair<B> load_vpair_buf(__amdgpu_buffer_rsrc_t r, uint32_t off0, uint32_t off1) {
   VPair<B> v;
-  if constexpr (B == 2) {
-    v.a = reinterpret_cast<const uint16_t*>(row0)[cb];
-    v.b = reinterpret_cast<const uint16_t*>(row1)[cb];
-  } else if constexpr (B == 4) {
-    v.a = reinterpret_cast<const uint32_t*>(row0)[cb];
-    v.b = reinterpret_cast<const uint32_t*>(row1)[cb];
+  if constexpr (B <= 4) {
+    v.a = __builtin_amdgcn_raw_buffer_load_b32(r, off0, 0, 0);
+    v.b = __builtin_amdgcn_raw_buffer_load_b32(r, off1, 0, 0);
   } else if constexpr (B == 8) {
-    v.a = reinterpret_cast<const uint2*>(row0)[cb];
-    v.b = reinterpret_cast<const uint2*>(row1)[cb];
+    const auto x = __builtin_amdgcn_raw_buffer_load_b64(r, off0, 0, 0);
+    const auto y = __builtin_amdgcn_raw_buffer_load_b64(r, off1, 0, 0);
+    v.a = make_uint2(x[0], x[1]);
+    v.b = make_uint2(y[0], y[1]);
   } else {
-    v.a = reinterpret_cast<const uint4*>(row0)[cb];
-    v.b = reinterpret_cast<const uint4*>(row1)[cb];
+    const auto x = __builtin_amdgcn_raw_buffer_load_b128(r, off0, 0, 0);
+    const auto y = __builtin_amdgcn_raw_buffer_load_b128(r, off1, 0, 0);
+    v.a = make_uint4(x[0], x[1], x[2], x[3]);
+    v.b = make_uint4(y[0], y[1], y[2], y[3]);
   }
+  return v;
+}
+
+// Zone C: fp16 rows through plain pointers.
+__device__ inline VPair<16> load_vpair16(const uint8_t* row0, const uint8_t* row1, int cb) {
+  VPair<16> v;
+  v.a = reinterpret_cast<const uint4*>(row0)[cb];
+  v.b = reinterpret_cast<const uint4*>(row1)[cb];
   return v;
 }
 
@@ -433,15 +457,16 @@ __device__ constexpr float channel_scale(int e) {
 }
 
 // acc[g][e] += dot2((x_t0[e], x_t1[e]), (c_t0[g], c_t1[g])) for the lane's 8
-// channels (see channel_scale for the in-place code positions).
+// channels (see channel_scale for the in-place code positions).  sel2 picks
+// the lane's halves of the two 2-bit dwords.
 template <int G, int B>
-__device__ inline void pv_pair(float (&acc)[G][8], const VPair<B>& v, const uint32_t (&cf)[G]) {
+__device__ inline void pv_pair(float (&acc)[G][8], const VPair<B>& v, const uint32_t (&cf)[G], uint32_t sel2) {
   auto fma_e = [&](int e, uint32_t pr) {
 #pragma unroll
     for (int g = 0; g < G; ++g) acc[g][e] = dot2(pr, cf[g], acc[g][e]);
   };
   if constexpr (B == 2) {
-    const uint32_t w = v.a | (v.b << 16);   // t0 in the low half, t1 in the high half
+    const uint32_t w = __builtin_amdgcn_perm(v.b, v.a, sel2);   // t0 in the low half, t1 in the high half
     const uint32_t hi = w >> 10;
 #pragma unroll
     for (int e = 0; e < 5; ++e) fma_e(e, w & (0x00030003u << (2 * e)));
@@ -492,12 +517,12 @@ __device__ inline void state_init(WaveState<G>& st) {
 // Online softmax update for one tile (lane = token): the running max m (log2
 // units, wave-uniform) is raised, with the sums rescaled, only when some
 // lane's logit exceeds it.  Writes fp16 p*vs per token to LDS.
-template <int G, int SW>
+template <int G, int SW, bool kMasked>
 __device__ inline void softmax_tile(WaveState<G>& st, const float (&s)[G], bool valid, float vs, float vz,
                                     Smem<G, SW>& sm, int wave, int lane) {
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    const float t = valid ? s[g] * kLog2eOverSqrtD : -INFINITY;
+    const float t = (!kMasked || valid) ? s[g] * kLog2eOverSqrtD : -INFINITY;
     if (__builtin_amdgcn_ballot_w64(t > st.m[g]) != 0) {
       const float mnew = fmaxf(st.m[g], wave_reduce<true>(t));
       const float alpha = __builtin_amdgcn_exp2f(st.m[g] - mnew);
@@ -579,40 +604,62 @@ __device__ inline uint32_t lds_addr(const void* p) {
   return uint32_t(size_t((const __attribute__((address_space(3))) void*)p));
 }
 
-// One global_load_lds_dwordx4: 64 lanes each copy 16 bytes (from a 16-byte-
-// aligned address) into LDS at lds + 16 * lane.  Written as inline assembly,
-// so the compiler's memory-counter bookkeeping does not see it (it would
-// otherwise wait for every outstanding copy before any LDS read); the tile
-// loop waits explicitly.  M0 (the LDS base of the copy) is saved and restored
-// around it.
-__device__ inline void lds_copy16(const uint32_t* addr, uint32_t lds) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(addr), "s"(lds)
-      : "memory");
+// The same resource as four scalar registers, for inline assembly.
+typedef int rsrc4 __attribute__((ext_vector_type(4)));
+__device__ inline rsrc4 buffer_rsrc4(const void* p, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  rsrc4 r;
+  r.x = __builtin_amdgcn_readfirstlane(int(uint32_t(a)));
+  r.y = __builtin_amdgcn_readfirstlane(int(uint32_t(a >> 32) & 0xffff));   // stride 0
+  r.z = __builtin_amdgcn_readfirstlane(int(bytes));
+  r.w = kBufferFlags;
+  return r;
 }
 
-// Words between the 16-byte-aligned address at or below p and p.
-__device__ inline int misalign_words(const uint32_t* p) { return int((reinterpret_cast<uintptr_t>(p) >> 2) & 3); }
+// N (1..4) buffer_load_dwordx4 ... lds: copy j moves the 16 bytes at range
+// offset voff + 1024 j (voff = 16 * lane) to LDS byte lds + 1024 j + 16 * lane;
+// the instruction offset moves both addresses.  Dwords past the range arrive
+// as zeros.  Inline assembly, so the compiler's memory-counter bookkeeping
+// does not see the copies (it would otherwise wait for every outstanding copy
+// before any LDS read); the tile loop waits explicitly.  M0 (the LDS base) is
+// saved and restored around them.
+#define RDKV_LDS_COPY(off) "buffer_load_dwordx4 %1, %2, 0 offen offset:" #off " lds\n\t"
+template <int N>
+__device__ inline void lds_copy_block(rsrc4 r, uint32_t voff, uint32_t lds) {
+  static_assert(N >= 1 && N <= 4, "copies per block");
+  uint32_t saved;
+  if constexpr (N == 1) {
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t" RDKV_LDS_COPY(0) "s_mov_b32 m0, %0"
+                 : "=&s"(saved) : "v"(voff), "s"(r), "s"(lds) : "memory");
+  } else if constexpr (N == 2) {
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t" RDKV_LDS_COPY(0) RDKV_LDS_COPY(1024)
+                 "s_mov_b32 m0, %0"
+                 : "=&s"(saved) : "v"(voff), "s"(r), "s"(lds) : "memory");
+  } else if constexpr (N == 3) {
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t" RDKV_LDS_COPY(0) RDKV_LDS_COPY(1024)
+                 RDKV_LDS_COPY(2048) "s_mov_b32 m0, %0"
+                 : "=&s"(saved) : "v"(voff), "s"(r), "s"(lds) : "memory");
+  } else {
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t" RDKV_LDS_COPY(0) RDKV_LDS_COPY(1024)
+                 RDKV_LDS_COPY(2048) RDKV_LDS_COPY(3072) "s_mov_b32 m0, %0"
+                 : "=&s"(saved) : "v"(voff), "s"(r), "s"(lds) : "memory");
+  }
+}
+#undef RDKV_LDS_COPY
 
-// Copies a tile's K records (the n_words >= 1 words at src) into an LDS stage:
-// always exactly stage_copies<SW> copies; the 16-byte chunks past the block
-// reread its last chunk, which lies inside the 256-aligned record region.
-// The block starts misalign_words(src) words into the stage.
-template <int SW>
-__device__ inline void dma_records(const uint32_t* src, int n_words, uint32_t* stage, int lane) {
-  const int m = misalign_words(src);
-  const uint32_t* base = src - m;
-  const int n16 = (m + n_words + 3) >> 2;
-  const uint32_t lds = lds_addr(stage);
-#pragma unroll
-  for (int i = 0; i < stage_copies<SW>(); ++i) lds_copy16(base + 4 * min(i * 64 + lane, n16 - 1), lds + i * 1024);
+// Copies a tile's K-record block (`bytes` bytes from the 16-byte-aligned
+// src) into an LDS stage with exactly stage_copies<SW> copies, in blocks of
+// four (one M0 and one resource per block).  Past `bytes` the stage gets
+// zeros; no memory beyond the block is read.
+template <int SW, int C0 = 0>
+__device__ inline void dma_records(const uint8_t* src, uint32_t bytes, uint32_t* stage, uint32_t voff) {
+  constexpr int n = stage_copies<SW>();
+  if constexpr (C0 < n) {
+    constexpr uint32_t off = uint32_t(C0) * 1024;
+    const rsrc4 r = buffer_rsrc4(src + off, bytes > off ? bytes - off : 0u);
+    lds_copy_block<(n - C0 < 4 ? n - C0 : 4)>(r, voff, lds_addr(stage) + off);
+    dma_records<SW, C0 + 4>(src, bytes, stage, voff);
+  }
 }
 
 // Waits until at most N vector-memory instructions of this wave are in
@@ -633,20 +680,25 @@ __device__ inline void wait_vmem() {
 // each lane reads its record from global memory.  PIPE: the lane's V pairs
 // are loaded one tile ahead (two register sets used in turn); otherwise at
 // the start of the tile, before the logits.
+//
+// Every tile's V rows and record block are read through buffer resources that
+// end at the chunk's last row, so the rows of a partial tile past the chunk
+// (and the whole of a tile past the wave's last) read as zeros without
+// touching memory: no per-lane clamping, and tile addresses stay scalar.
 template <int G, int B, int SW, bool PIPE>
 __device__ void run_group(const DecodeParams& p, const SegInfo& si, const Plan& pl, int64_t seg, Smem<G, SW>& sm) {
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int cb = lane & 15, ts = lane >> 4;
   const QkShape ks = qk_shape(si);
   const int nw = pl.rec_words;
-  const uint32_t* rbase = reinterpret_cast<const uint32_t*>(p.cache + si.off_krec) + pl.rec0;
+  const uint8_t* rbytes = p.cache + si.off_krec;                   // 256-byte aligned
   const uint8_t* vbase = p.cache + pl.vbase;
   constexpr int kRowBytes = kHeadDim * B / 8;
-  const int last = pl.end - 1;
   const int first = pl.start + kTile * wave;                       // the wave's tiles: first + 256 i
   const int n_tiles = first < pl.end ? (pl.end - first + kThreads - 1) / kThreads : 0;
   auto tile_row = [&](int i) { return first + kThreads * min(i, n_tiles - 1); };
-  auto vrow = [&](int row) { return vbase + int64_t(min(row, last)) * kRowBytes; };
+  // rows of tile i inside the chunk; none for the tiles past the wave's last
+  auto tile_rows = [&](int i) { return i < n_tiles ? min(kTile, pl.end - (first + kThreads * i)) : 0; };
 
   // Ring: tile i's records live in stage i mod S.  The first S - 1 tiles are
   // copied up front; the end of step i copies tile i + S - 1 into the stage
@@ -665,41 +717,37 @@ __device__ void run_group(const DecodeParams& p, const SegInfo& si, const Plan& 
   // Issued after tile i's record copies by the time step i waits for them,
   // at the least: with three stages, step 0 (after the prologue) or a steady
   // step (two step starts, one step body, one refill); with two, one start.
+  // Every step issues the same instructions (tiles past the last read zeros).
   constexpr int kWaitRec =
       kS == 3 ? kCopies + (((PIPE ? kNV : 0) + kPre) < (2 * kPre + kPost) ? (PIPE ? kNV : 0) + kPre : 2 * kPre + kPost)
               : kPre;
   const bool use_ring = SW > 0 && nw > 0 && n_tiles > 0;           // uniform
   auto stage = [&](int i) { return sm.wv[wave].ring + (i % kS) * (SW > 0 ? stage_words<SW>() : 0); };
+  // word offset (from off_krec) of tile i's first record
+  auto rec_word = [&](int i) { return pl.rec0 + int64_t(tile_row(i)) * nw; };
+  const uint32_t voff16 = uint32_t(lane) * 16u;
   auto fetch_records = [&](int i) {
     if constexpr (SW > 0) {
-      const int b = tile_row(i);
-      dma_records<SW>(rbase + int64_t(b) * nw, min(kTile, pl.end - b) * nw, stage(i), lane);
+      const int64_t w0 = rec_word(i);
+      const int m = int(w0 & 3);                                   // block start within its 16 bytes
+      const int rows = tile_rows(i);
+      dma_records<SW>(rbytes + uint64_t(w0 - m) * 4, rows > 0 ? uint32_t(m + rows * nw) * 4u : 0u, stage(i), voff16);
     }
   };
-  // V pairs of tile i: a full tile addresses rows from one uniform tile base
-  // plus a fixed lane offset; a partial one clamps each row to the chunk.
-  const uint32_t lane_off = uint32_t(ts * kRowBytes + cb * (kRowBytes / 16));
-  auto load_pair = [&](int i, int k) {
-    const int b = tile_row(i), j = ts + 4 * k;
-    if (b + kTile <= pl.end) {
-      const uint8_t* lp = vbase + int64_t(b) * kRowBytes + lane_off;
-      return load_vpair<B>(lp + 4 * k * kRowBytes, lp + (4 * k + 32) * kRowBytes, 0);
-    }
-    return load_vpair<B>(vrow(b + j), vrow(b + j + 32), cb);
+  // V pairs of tile i: one resource per tile, a fixed lane offset, and the
+  // pair's rows as instruction offsets.
+  const uint32_t lane_off = uint32_t(ts * kRowBytes + lane_row_offset<B>(cb));
+  const uint32_t sel2 = (cb & 1) ? 0x07060302u : 0x05040100u;      // the lane's half of a 2-bit dword
+  auto vrsrc = [&](int i) {
+    return buffer_rsrc(vbase + int64_t(tile_row(i)) * kRowBytes, uint32_t(tile_rows(i) * kRowBytes));
+  };
+  auto load_pair = [&](__amdgpu_buffer_rsrc_t r, int k) {
+    return load_vpair_buf<B>(r, lane_off + 4 * k * kRowBytes, lane_off + (4 * k + 32) * kRowBytes);
   };
   auto load_pairs = [&](VPair<B> (&v)[kPairsPerLane], int i) {
-    const int b = tile_row(i);
-    if (b + kTile <= pl.end) {
-      const uint8_t* lp = vbase + int64_t(b) * kRowBytes + lane_off;
+    const __amdgpu_buffer_rsrc_t r = vrsrc(i);
 #pragma unroll
-      for (int k = 0; k < kPairsPerLane; ++k) v[k] = load_vpair<B>(lp + 4 * k * kRowBytes, lp + (4 * k + 32) * kRowBytes, 0);
-    } else {
-#pragma unroll
-      for (int k = 0; k < kPairsPerLane; ++k) {
-        const int j = ts + 4 * k;
-        v[k] = load_vpair<B>(vrow(b + j), vrow(b + j + 32), cb);
-      }
-    }
+    for (int k = 0; k < kPairsPerLane; ++k) v[k] = load_pair(r, k);
   };
 
   VPair<B> va[kPairsPerLane], vb[kPairsPerLane];
@@ -715,28 +763,38 @@ __device__ void run_group(const DecodeParams& p, const SegInfo& si, const Plan& 
 
   WaveState<G> st;
   state_init(st);
+  const int lane_rec = lane * nw;                                  // the lane's record in a stage
   auto tile = [&](int i, VPair<B> (&cur)[kPairsPerLane], VPair<B> (&nxt)[kPairsPerLane]) {
     const int b = tile_row(i);
     if constexpr (PIPE) load_pairs(nxt, i + 1);
     if constexpr (!PIPE && !kLateV) load_pairs(cur, i);
     if (use_ring) wait_vmem<(kWaitRec < 63 ? kWaitRec : 63)>();
-    const int r = min(b + lane, last);
     // (with SW > 0 and no record words, nothing is read from the stage)
-    const uint32_t* my = SW > 0 ? stage(i) + misalign_words(rbase + int64_t(b) * nw) + (r - b) * nw
-                                : rbase + int64_t(r) * nw;
+    const uint32_t* my;
+    if constexpr (SW > 0) {
+      my = stage(i) + int(rec_word(i) & 3) + lane_rec;
+    } else {
+      my = reinterpret_cast<const uint32_t*>(rbytes) + pl.rec0 + int64_t(min(b + lane, pl.end - 1)) * nw;
+    }
     float s[G], vs, vz;
     record_logits<G, SW>(my, ks, nw, B < 16, sm, s, vs, vz);
-    softmax_tile<G, SW>(st, s, b + lane < pl.end, vs, vz, sm, wave, lane);
+    if (b + kTile <= pl.end) {
+      softmax_tile<G, SW, false>(st, s, true, vs, vz, sm, wave, lane);
+    } else {
+      softmax_tile<G, SW, true>(st, s, b + lane < pl.end, vs, vz, sm, wave, lane);
+    }
     wave_lds_sync();
+    __amdgpu_buffer_rsrc_t rl;
+    if constexpr (kLateV) rl = vrsrc(i);
 #pragma unroll
     for (int k = 0; k < kPairsPerLane; ++k) {
       uint32_t cf[G];
       load_coefs<G, SW>(sm, wave, ts + 4 * k, cf);
       if constexpr (kLateV) {
-        const VPair<B> v = load_pair(i, k);
-        pv_pair<G, B>(st.acc, v, cf);
+        const VPair<B> v = load_pair(rl, k);
+        pv_pair<G, B>(st.acc, v, cf, sel2);
       } else {
-        pv_pair<G, B>(st.acc, cur[k], cf);
+        pv_pair<G, B>(st.acc, cur[k], cf, sel2);
       }
     }
     wave_lds_sync();
@@ -747,7 +805,7 @@ __device__ void run_group(const DecodeParams& p, const SegInfo& si, const Plan& 
     if (i + 1 >= n_tiles) break;
     tile(i + 1, vb, va);
   }
-  // The last steps copied (clamped) records into ring stages that the partial
+  // The last steps copied (zero) blocks into ring stages that the partial
   // output below overwrites; those copies must land before it does.
   if (use_ring) wait_vmem<0>();
   wave_finish<G, B, SW>(st, sm, wave, lane);
@@ -777,7 +835,7 @@ __device__ void run_zone_c(const DecodeParams& p, const SegInfo& si, int64_t seg
   for (int base = pl.start + kTile * wave; base < pl.end; base += kThreads) {
     VPair<16> v[kPairsPerLane];
 #pragma unroll
-    for (int k = 0; k < kPairsPerLane; ++k) v[k] = load_vpair<16>(vrow(base + ts + 4 * k), vrow(base + ts + 4 * k + 32), cb);
+    for (int k = 0; k < kPairsPerLane; ++k) v[k] = load_vpair16(vrow(base + ts + 4 * k), vrow(base + ts + 4 * k + 32), cb);
     const int r = min(base + lane, last);
     const uint4* k4 = reinterpret_cast<const uint4*>(krow(r));
     float s[G];
@@ -795,13 +853,13 @@ __device__ void run_zone_c(const DecodeParams& p, const SegInfo& si, int64_t seg
         for (int g = 0; g < G; ++g) s[g] = dot2(ws[j], q[g], s[g]);
       }
     }
-    softmax_tile<G, SW>(st, s, base + lane < pl.end, 1.f, 0.f, sm, wave, lane);
+    softmax_tile<G, SW, true>(st, s, base + lane < pl.end, 1.f, 0.f, sm, wave, lane);
     wave_lds_sync();
 #pragma unroll
     for (int k = 0; k < kPairsPerLane; ++k) {
       uint32_t cf[G];
       load_coefs<G, SW>(sm, wave, ts + 4 * k, cf);
-      pv_pair<G, 16>(st.acc, v[k], cf);
+      pv_pair<G, 16>(st.acc, v[k], cf, 0u);
     }
     wave_lds_sync();
   }
