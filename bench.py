@@ -59,9 +59,12 @@ def counter_traffic(kernel, workload):
     return int(fields["traffic_bytes_per_launch"]), os.path.relpath(path, ROOT)
 
 
-def build_cache(rdkv, synth, torch, w, lay, dims1, fp16_only=False):
-    """Score, allocate and pack every layer into a fresh cache; returns stats."""
+def build_cache(rdkv, synth, torch, w, lay, dims1, fp16_only=False, lay1=None):
+    """Score, allocate and pack every layer into a fresh cache; returns stats.
+    With `lay1` (a one-layer layout), each layer is also packed into a blob of
+    its own (stats["layer_caches"]), for the per-layer decode loop."""
     cache = rdkv.cache_init(lay)
+    layer_caches = []
     S = w.n_seq
     ws = None
     hist_tok = np.zeros(5, np.int64)
@@ -91,6 +94,9 @@ def build_cache(rdkv, synth, torch, w, lay, dims1, fp16_only=False):
             score_ms += e0.elapsed_time(e1)
             del wt, vt, wc
         rdkv.pack(lay, cache, K, V, bt, bc, layer_begin=l)
+        if lay1 is not None:
+            layer_caches.append(rdkv.cache_init(lay1))
+            rdkv.pack(lay1, layer_caches[-1], K, V, bt, bc, layer_begin=0)
         for i, b in enumerate((0, 2, 4, 8, 16)):
             hist_tok[i] += int((bt == b).sum())
             hist_chan[i] += int((bc == b).sum())
@@ -99,7 +105,8 @@ def build_cache(rdkv, synth, torch, w, lay, dims1, fp16_only=False):
             torch.cuda.synchronize()
             log(f"{'fp16 ' if fp16_only else ''}layer {l + 1}/{w.n_layers} packed, {time.time() - t0:.1f}s")
     torch.cuda.synchronize()
-    return cache, dict(hist_tok=hist_tok, hist_chan=hist_chan, score_ms=score_ms, setup_s=time.time() - t0)
+    return cache, dict(hist_tok=hist_tok, hist_chan=hist_chan, score_ms=score_ms, setup_s=time.time() - t0,
+                       layer_caches=layer_caches)
 
 
 def time_decode(rdkv, torch, lay, cache, q, kn, vn, steps, warmup, flush, grow=False):
@@ -158,6 +165,61 @@ def time_decode(rdkv, torch, lay, cache, q, kn, vn, steps, warmup, flush, grow=F
     return dict(step=float(total.mean()), step_median=float(np.median(total)), chunk=float(chunk.mean()),
                 chunk_median=float(np.median(chunk)), merge=float(merge_ms.mean()), wall=wall, out=out,
                 mean_zone_c_rows=mean_rows, total_ms=float(total.sum()))
+
+
+def time_layer_graph(rdkv, torch, lay1, caches, q, kn, vn, steps, warmup, flush, ref):
+    """The same decode step issued the way a model's layer loop issues it: one
+    rdkv_decode (chunk + merge kernel) per layer on that layer's own blob, the
+    whole loop captured once in a HIP graph and replayed per step.  Returns
+    the mean/median replay time (ms) and the largest relative difference of
+    any replay's output from `ref` (the single-launch output)."""
+    L = len(caches)
+    ws = rdkv.decode_workspace(lay1)
+    ql = [q[:, l:l + 1].contiguous() for l in range(L)]
+    kl = [kn[:, l:l + 1].contiguous() for l in range(L)]
+    vl = [vn[:, l:l + 1].contiguous() for l in range(L)]
+    outs = [torch.empty(x.shape, dtype=torch.float32, device="cuda") for x in ql]
+
+    def loop():
+        for l in range(L):
+            rdkv.decode(lay1, caches[l], 0, ql[l], kl[l], vl[l], workspace=ws, out=outs[l])
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        loop()                      # eager pass on the capture stream before capturing
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    eager = torch.cat(outs, dim=1).clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        loop()
+    fbuf = torch.ones(1 << 27, dtype=torch.int64, device="cuda") if flush else None
+    worst = 0.0
+    for i in range(warmup):
+        g.replay()
+        if fbuf is not None:
+            fbuf.sum()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record()
+        g.replay()
+        ev[i][1].record()
+        if fbuf is not None:
+            fbuf.sum()
+        # every replay must reproduce the eager per-layer loop exactly
+        if i < 3:
+            torch.cuda.synchronize()
+            got = torch.cat(outs, dim=1)
+            if not torch.equal(got, eager):
+                raise RuntimeError(f"graph replay {i} differs from the eager per-layer loop")
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in ev])
+    got = torch.cat(outs, dim=1)
+    rel = ((got - ref).abs().amax(-1) / ref.abs().amax(-1).clamp_min(1e-30)).max().item()
+    del g, fbuf
+    return dict(step=float(t.mean()), step_median=float(np.median(t)), rel_diff=rel)
 
 
 def cpu_baseline(w, hist_tok, hist_chan, n_seg, n_c, sample_segments):
@@ -223,6 +285,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp16-baseline", action="store_true")
     ap.add_argument("--cpu-sample-segments", type=int, default=32)
+    ap.add_argument("--no-layer-loop", action="store_true",
+                    help="skip the per-layer decode loop (one launch pair per layer, captured in a HIP graph)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run one plain 384 MiB device-to-device copy (for counter calibration)")
     args = ap.parse_args()
@@ -244,7 +308,9 @@ def main():
     dims = rdkv.make_dims(w.n_seq, w.n_layers, w.n_q_heads, w.n_kv_heads, w.n_tokens)
     dims1 = rdkv.make_dims(w.n_seq, 1, w.n_q_heads, w.n_kv_heads, w.n_tokens)
     lay = rdkv.layout(dims, w.budget_v, w.budget_k, w.zone_c_capacity)
-    cache, st = build_cache(rdkv, synth, torch, w, lay, dims1)
+    per_layer = w.n_layers > 1 and not args.no_layer_loop
+    lay1 = rdkv.layout(dims1, w.budget_v, w.budget_k, w.zone_c_capacity) if per_layer else None
+    cache, st = build_cache(rdkv, synth, torch, w, lay, dims1, lay1=lay1)
     q, kn, vn = synth.decode_inputs(w, 0, device="cuda")
     batched = w.n_seq > 1
     grow = args.grow or batched
@@ -260,6 +326,18 @@ def main():
         del src, dst
     log(f"decode: step mean {ms_mean * 1e3:.1f} us (chunk kernel {tm['chunk'] * 1e3:.1f} us, "
         f"merge {tm['merge'] * 1e3:.1f} us)")
+
+    layer_loop = None
+    if per_layer:
+        tg = time_layer_graph(rdkv, torch, lay1, st["layer_caches"], q, kn, vn, args.steps, args.warmup,
+                              not args.no_flush, tm["out"])
+        layer_loop = {"us_per_token": round(tg["step"] * 1e3 / w.n_seq, 2),
+                      "us_per_token_median": round(tg["step_median"] * 1e3 / w.n_seq, 2),
+                      "launches_per_step": 2 * w.n_layers, "max_rel_diff_vs_single_launch": tg["rel_diff"],
+                      "note": "one rdkv_decode per layer on its own one-layer blob, the loop captured in a "
+                              "HIP graph and replayed per step (every replay checked against the eager loop)"}
+        log(f"per-layer graph loop: {tg['step'] * 1e3:.1f} us per step")
+    st.pop("layer_caches", None)
 
     desc = rdkv.descriptors(lay, cache)
     b = rdkv.decode_bytes(lay, desc, n_c)
@@ -306,6 +384,8 @@ def main():
                      "traffic_unit": "bytes per launch", "traffic_source": traffic_src,
                      "kernel": "decode_chunk_kernel", "algorithmic_bytes_per_launch": int(algo),
                      "bytes_breakdown": {k: int(v) for k, v in b.items()},
+                     "metadata_share": round((b["v_meta"] + b["k_meta"]) / algo, 4),
+                     "record_padding_share_of_reads": round(b["k_padding"] / (algo + b["k_padding"]), 4),
                      "kernel_ms": round(tm["chunk"], 5), "kernel_ms_median": round(tm["chunk_median"], 5),
                      "merge_kernel_ms": round(tm["merge"], 5),
                      "step_GBs": round(algo / (ms_mean * 1e-3) / 1e9, 1)},
@@ -316,6 +396,8 @@ def main():
                    if st["score_ms"] > 0 else None},
         "wall_s_timed_loop": round(wall, 4),
     }
+    if layer_loop is not None:
+        result["per_layer_graph_loop"] = layer_loop
     del cache
     torch.cuda.empty_cache()
     if not args.no_fp16_baseline:

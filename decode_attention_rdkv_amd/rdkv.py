@@ -274,17 +274,28 @@ def descriptors(lay: Layout, cache: torch.Tensor):
 
 
 def decode_bytes(lay: Layout, desc: dict, n_c: int) -> dict:
-    """Bytes one decode step reads and writes, from the descriptors.
+    """Bytes of one decode step, from the descriptors.
 
-    V rows (2/4/8-bit codes, fp16 rows), K records (codes, fp16 channels,
-    scale/zero words; 16-bit tokens' records have no V word), zone-C rows, the
-    queries and the fp32 outputs.
+    Algorithmic bytes (what the method has to move): V codes or fp16 rows of
+    every kept token, one (scale, zero) word per 2/4/8-bit V row, K codes and
+    fp16 channels (sum over kept channels of their bits, per kept token), one
+    (scale, zero) word per present integer K part per kept token, zone-C rows,
+    the queries and the fp32 outputs; `total` is their sum.  `k_padding` is
+    what the stored K records add on top (each part rounded up to a word):
+    read by the kernel, but not counted as algorithmic.
     """
     import numpy as np
     n_tok = desc["n_tok"].astype(np.int64)
+    n_kept = desc["n_kept"].astype(np.int64)
+    n_chan = desc["n_chan"].astype(np.int64)                      # channels at 16, 8, 4, 2 bits
     v = int((n_tok * np.array([32, 64, 128, 256])).sum())
-    k = int((desc["n_kept"].astype(np.int64) * desc["rec"]).sum() - 4 * n_tok[:, 3].sum())
+    v_meta = int(4 * n_tok[:, :3].sum())
+    k_bits = int((n_kept * (n_chan * np.array([16, 8, 4, 2])).sum(axis=1)).sum())
+    k = (k_bits + 7) // 8
+    k_meta = int(4 * (n_kept * (n_chan[:, 1:] > 0).sum(axis=1)).sum())
+    k_read = int((n_kept * desc["rec"]).sum() - 4 * n_tok[:, 3].sum())
     zc = int(lay.n_seg * n_c * 2 * HEAD_DIM * 2)
     d = lay.dims
     qo = d.n_seq * d.n_layers * d.n_q_heads * HEAD_DIM * (2 + 4)
-    return dict(v=v, k=k, zone_c=zc, q_out=qo, total=v + k + zc + qo)
+    return dict(v=v, v_meta=v_meta, k=k, k_meta=k_meta, zone_c=zc, q_out=qo,
+                total=v + v_meta + k + k_meta + zc + qo, k_padding=k_read - (k + k_meta + v_meta))

@@ -150,3 +150,39 @@ def test_two_phase_decode_validation(lib):
     assert lib.rdkv_decode_merge(ctypes.byref(lay), A, nb, -1, A, A, ws, None) == CAPACITY
     assert lib.rdkv_decode_merge(ctypes.byref(lay), A, nb, 0, None, A, ws, None) == NULL
     assert lib.rdkv_decode_merge(ctypes.byref(lay), A, nb, 0, A + 4, A, ws, None) == ALIGN
+
+
+def test_decode_byte_accounting_against_the_oracle_blob():
+    """The benchmark's algorithmic bytes per decode step (read from the
+    descriptors) equal the oracle's count of payload bits plus one
+    (scale, zero) word per quantized V row and per present K part; adding the
+    record padding gives exactly the bytes the packed segments hold."""
+    import numpy as np
+    import torch
+    from decode_attention_rdkv_amd import synth
+    S, L, Hq, Hkv, N, cap = 1, 2, 4, 2, 300, 3
+    bt, bc = synth.random_bits(L * Hkv, N, 5)
+    bc[1] = 0
+    bc[1, :7] = 2                        # a segment with a single, partly filled 2-bit K part
+    bv, bk = int(bt.sum(axis=1).max()), int(bc.sum(axis=1).max())
+    ol = O.Layout(S, L, Hq, Hkv, 128, N, bv, bk, cap)
+    K, V = synth.random_kv(L * Hkv, N, 6)
+    shp = (S, L, Hkv)
+    blob = O.pack_cache(ol, K.reshape(shp + (N, 128)), V.reshape(shp + (N, 128)), bt.reshape(shp + (N,)),
+                        bc.reshape(shp + (128,)))
+    lay = rdkv.layout(rdkv.make_dims(S, L, Hq, Hkv, N), bv, bk, cap)
+    desc = rdkv.descriptors(lay, torch.from_numpy(blob))
+    n_c = 2
+    b = rdkv.decode_bytes(lay, desc, n_c)
+    n_seg = L * Hkv
+    payload = sum(O.segment_payload_bytes(blob, ol, s) for s in range(n_seg))
+    stored = sum(O.segment_decode_bytes(blob, ol, s, n_c) for s in range(n_seg))
+    assert abs((b["v"] + b["k"]) - payload) < 1
+    n_zone_a = int((bt > 0).sum() - (bt == 16).sum())
+    assert b["v_meta"] == 4 * n_zone_a
+    kept = (bt > 0).sum(axis=1)
+    parts = [sum(int((bc[s] == w).any()) for w in (8, 4, 2)) for s in range(n_seg)]
+    assert b["k_meta"] == 4 * int(sum(k * p for k, p in zip(kept, parts)))
+    assert b["v"] + b["v_meta"] + b["k"] + b["k_meta"] + b["k_padding"] + b["zone_c"] == stored
+    assert b["k_padding"] >= 0
+    assert b["total"] == b["v"] + b["v_meta"] + b["k"] + b["k_meta"] + b["zone_c"] + b["q_out"]

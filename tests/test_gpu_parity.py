@@ -339,3 +339,44 @@ def test_decode_equals_its_two_phases(gpu_lib):
     assert torch.equal(a, b) and torch.equal(c1, c2)
     # decode is deterministic run to run
     assert torch.equal(rdkv.decode(lay, c1, 4, q), rdkv.decode(lay, c1, 4, q))
+
+
+def test_decode_captured_in_a_graph_replays_like_eager(gpu_lib):
+    """rdkv_decode enqueues only kernels (no memset, no allocation), so a
+    caller can capture a per-layer decode loop in a HIP graph.  Every replay,
+    with eager work and synchronisation between replays, must equal the eager
+    call bit for bit, and the oracle within the tolerance."""
+    rdkv = gpu_lib
+    lay, ol, oblob, (K, V, bt, bc) = _pack_case(("mixed", 1, 2, 4, 2, 777, 5))
+    cache = rdkv.cache_init(lay)
+    rdkv.pack(lay, cache, dev(K), dev(V), dev(bt), dev(bc))
+    r = np.random.default_rng(9)
+    q = r.standard_normal((1, 2, 4, 128)).astype(np.float16)
+    kn = r.standard_normal((1, 2, 2, 128)).astype(np.float16)
+    vn = r.standard_normal((1, 2, 2, 128)).astype(np.float16)
+    qd, knd, vnd = dev(q), dev(kn), dev(vn)
+    ws = rdkv.decode_workspace(lay)
+    out = torch.empty((1, 2, 4, 128), dtype=torch.float32, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        rdkv.decode(lay, cache, 0, qd, knd, vnd, workspace=ws, out=out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    ref = O.decode_step(oblob, ol, q, 0, kn, vn)
+    assert rel_err_rows(host(eager), ref) <= TOL
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        rdkv.decode(lay, cache, 0, qd, knd, vnd, workspace=ws, out=out)
+    junk = torch.empty_like(out)
+    for i in range(4):
+        out.fill_(float("nan"))
+        junk.normal_()                           # eager work between replays
+        ws.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {i} differs from the eager call"
+    # the appended zone-C row is the same bytes the oracle wrote
+    assert np.array_equal(host(cache), oblob)
