@@ -29,6 +29,8 @@ import time
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0
+# VALU issue peak: 256 CUs x 4 SIMDs, one wave64 instruction per 4 cycles each, at 2.4 GHz
+VALU_PEAK_GINSTR = 256 * 4 / 4 * 2.4
 MFMA_FP16_PEAK_TFS = 2500.0
 
 
@@ -40,23 +42,26 @@ def log(msg):
 
 
 def counter_traffic(kernel, workload):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary (FETCH_SIZE + WRITE_SIZE, each scaled by a plain copy of known
-    size), or None when there is none or the kernel's source has changed
+    """HBM bytes and VALU instructions per launch of `kernel` from the
+    committed rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE, each scaled
+    by a plain copy of known size; SQ_INSTS_VALU), as (traffic, valu, source);
+    None for each when there is no summary or the kernel's source has changed
     since the counters were taken."""
     import hashlib
     import re
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}.md")
     if not os.path.exists(path):
-        return None, None
+        return None, None, None
     text = open(path).read()
-    fields = dict(re.findall(r"^(kernel_source|kernel_source_sha256|traffic_bytes_per_launch): (\S+)$", text, re.M))
-    if len(fields) != 3:
-        return None, None
+    fields = dict(re.findall(r"^(kernel_source|kernel_source_sha256|traffic_bytes_per_launch|"
+                             r"valu_instructions_per_launch): (\S+)$", text, re.M))
+    if not {"kernel_source", "kernel_source_sha256", "traffic_bytes_per_launch"} <= set(fields):
+        return None, None, None
     src = os.path.join(ROOT, fields["kernel_source"])
     if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != fields["kernel_source_sha256"]:
-        return None, os.path.relpath(path, ROOT) + " (stale: kernel source changed)"
-    return int(fields["traffic_bytes_per_launch"]), os.path.relpath(path, ROOT)
+        return None, None, os.path.relpath(path, ROOT) + " (stale: kernel source changed)"
+    valu = int(fields["valu_instructions_per_launch"]) if "valu_instructions_per_launch" in fields else None
+    return int(fields["traffic_bytes_per_launch"]), valu, os.path.relpath(path, ROOT)
 
 
 def build_cache(rdkv, synth, torch, w, lay, dims1, fp16_only=False, lay1=None):
@@ -343,7 +348,7 @@ def main():
     b = rdkv.decode_bytes(lay, desc, n_c)
     algo = b["total"] + lay.n_seg * (256 + 2 * 128 * 2)        # descriptors read, new row written
     achieved = algo / (tm["chunk"] * 1e-3) / 1e9
-    traffic, traffic_src = counter_traffic("decode_chunk_kernel", w.name)
+    traffic, valu, traffic_src = counter_traffic("decode_chunk_kernel", w.name)
     N, d = w.n_tokens, 128
     payload_bits = float((st["hist_tok"] * np.array([0, 2, 4, 8, 16])).sum() * d)
     kept = int(desc["n_kept"].sum())
@@ -388,7 +393,14 @@ def main():
                      "record_padding_share_of_reads": round(b["k_padding"] / (algo + b["k_padding"]), 4),
                      "kernel_ms": round(tm["chunk"], 5), "kernel_ms_median": round(tm["chunk_median"], 5),
                      "merge_kernel_ms": round(tm["merge"], 5),
-                     "step_GBs": round(algo / (ms_mean * 1e-3) / 1e9, 1)},
+                     "step_GBs": round(algo / (ms_mean * 1e-3) / 1e9, 1),
+                     "valu": None if valu is None else {
+                         "instructions_per_launch": valu, "source": traffic_src,
+                         "achieved_Ginstr_per_s": round(valu / (tm["chunk"] * 1e-3) / 1e9, 1),
+                         "peak_Ginstr_per_s": VALU_PEAK_GINSTR,
+                         "frac": round(valu / (tm["chunk"] * 1e-3) / 1e9 / VALU_PEAK_GINSTR, 4),
+                         "note": "wave64 VALU instructions (SQ_INSTS_VALU) over the same kernel time; the "
+                                 "co-limit of this kernel at low bitwidths"}},
         "stages": {"setup_s": round(st["setup_s"], 2), "score_ms_total": round(st["score_ms"], 2),
                    "score_tflops_executed": round(score_flops / (st["score_ms"] * 1e-3) / 1e12, 2)
                    if st["score_ms"] > 0 else None,
