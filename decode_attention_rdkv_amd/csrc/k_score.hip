@@ -6,18 +6,20 @@
 //
 // Two passes over the causal score matrix on MFMA (v_mfma_f32_16x16x32_f16,
 // fp16 inputs, fp32 accumulation):
-//   score_lse_kernel     workgroup = 64 query rows of one query head; walks the
-//                        key blocks 0..diagonal, keeps a per-lane online
-//                        (max, sum) in base 2, then merges across lanes.
-//   score_colsum_kernel  workgroup = 64 keys of one KV head; walks the G query
-//                        heads and every query block at or after the keys,
-//                        summing exp2(s' - LSE') down each key column.  A key
-//                        block is owned by one workgroup, so no atomics and the
-//                        summation order is fixed.
-// The streamed 64x128 tile (K rows, or Q rows and their LSE) is double
-// buffered in LDS: the next tile's global loads are in flight while the
-// current one is multiplied.  Masks are applied only on the diagonal block
-// and the ragged last block.
+//   score_lse_kernel     workgroup = 128 query rows of one query head; walks
+//                        the key tiles up to its last row, keeps a per-lane
+//                        online (max, sum) in base 2, then merges across lanes.
+//   score_colsum_kernel  workgroup = 128 keys of one KV head; walks the G
+//                        query heads and every query tile at or after the
+//                        keys, summing exp2(s' - LSE') down each key column.
+//                        A key block is owned by one workgroup, so no atomics
+//                        and the summation order is fixed.
+// Each wave keeps 32 rows of its resident operand (Q rows, or K rows) in
+// registers as two 16-row MFMA fragments, so every fragment of the streamed
+// 64-row tile it reads from LDS feeds two products.  The streamed tile is
+// double buffered in LDS: the next tile's global loads are in flight while the
+// current one is multiplied.  Masks are applied only on diagonal and ragged
+// tiles; tiles entirely outside a wave's triangle are skipped by that wave.
 // Plus two bandwidth kernels: var_tok (one wave per token) and the column
 // norms behind w_chan (partial sums in fp64, reduced in a fixed order).
 #include "rdkv_internal.h"
@@ -27,7 +29,9 @@ namespace {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 
-constexpr int kB = 64;           // rows per block (queries or keys)
+constexpr int kKT = 64;                     // rows of the streamed LDS tile (keys, or query rows)
+constexpr int kWaveRows = 32;               // rows of the resident operand per wave (two 16-row fragments)
+constexpr int kBlockRows = 4 * kWaveRows;   // per workgroup
 constexpr int kPad = kHeadDim + 8;  // LDS row stride in halves (272 bytes)
 constexpr int kThreads = 256;
 constexpr float kLog2eOverSqrtD = 1.4426950408889634f / 11.313708498984761f;
@@ -76,25 +80,32 @@ __device__ inline void load_rows_frag(h8 (&a)[4], const __half* src, int64_t row
   }
 }
 
-// C[i][j] = sum_k A[i][k] * T[16*sub + j][k] for the wave's 16 rows of A and
-// 16 rows of the LDS tile T (B fragments in the same k order as A).  Lane
-// holds C[4*(lane/16) + r][lane % 16].
-__device__ inline f4 tile_product(const h8 (&a)[4], const _Float16 (*tile)[kPad], int sub) {
+// B-operand fragments of rows 16*sub .. 16*sub + 15 of an LDS tile, in the
+// same k order as the A fragments.
+__device__ inline void load_tile_frag(h8 (&b)[4], const _Float16 (*tile)[kPad], int sub) {
   const int lane = threadIdx.x & 63;
-  f4 c = {0.f, 0.f, 0.f, 0.f};
   const _Float16* trow = &tile[16 * sub + (lane & 15)][8 * (lane >> 4)];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    const h8 b = *reinterpret_cast<const h8*>(trow + 32 * kk);
-    c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[kk], b, c, 0, 0, 0);
-  }
+  for (int kk = 0; kk < 4; ++kk) b[kk] = *reinterpret_cast<const h8*>(trow + 32 * kk);
+}
+
+// C[i][j] = sum_k A[i][k] * B[j][k] over k = 0..127 for 16 rows of A and 16 of
+// B.  Lane holds C[4*(lane/16) + r][lane % 16].
+__device__ inline f4 mfma_16x16x128(const h8 (&a)[4], const h8 (&b)[4]) {
+  f4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[kk], b[kk], c, 0, 0, 0);
   return c;
 }
 
-__global__ __launch_bounds__(kThreads) void score_lse_kernel(ScoreArgs a) {
-  __shared__ _Float16 ks[2][kB][kPad];
+// Pass 1: workgroup = 128 query rows of one query head (32 per wave, two
+// 16-row fragments sharing every K fragment read from LDS); walks the key
+// tiles up to the block's last row.  Per lane and row an online (max, sum)
+// in base 2, merged across the 16 lanes of a row at the end.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void score_lse_kernel(ScoreArgs a) {
+  __shared__ _Float16 ks[2][kKT][kPad];
   const int64_t N = a.N;
-  const int nqb = int(cdiv(N, kB));
+  const int nqb = int(cdiv(N, kBlockRows));
   const int qb = nqb - 1 - int(blockIdx.x);   // long rows first
   const int hq = blockIdx.y;
   const int64_t sl = blockIdx.z;
@@ -102,86 +113,119 @@ __global__ __launch_bounds__(kThreads) void score_lse_kernel(ScoreArgs a) {
   const __half* Qh = a.Q + ((sl * a.Hq + hq) * N) * kHeadDim;
   const __half* Kh = a.K + ((sl * a.Hkv + h) * N) * kHeadDim;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t row0 = int64_t(qb) * kB + 16 * wave;
+  const int64_t wrow0 = int64_t(qb) * kBlockRows + kWaveRows * wave;       // the wave's first row
+  const int n_kt = int(cdiv(min(N, int64_t(qb + 1) * kBlockRows), kKT));   // key tiles the block needs
 
-  h8 qa[4];
-  load_rows_frag(qa, Qh, row0 + (lane & 15), N);
-  float m[4], s[4];
+  h8 qa[2][4];
+  load_rows_frag(qa[0], Qh, wrow0 + (lane & 15), N);
+  load_rows_frag(qa[1], Qh, wrow0 + 16 + (lane & 15), N);
+  float m[2][4], s[2][4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    m[r] = -INFINITY;
-    s[r] = 0.f;
-  }
+  for (int f = 0; f < 2; ++f)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      m[f][r] = -INFINITY;
+      s[f][r] = 0.f;
+    }
   TileRegs nxt;
   tile_fetch(nxt, Kh, 0, N);
   tile_store(nxt, ks[0]);
-  for (int kb = 0; kb <= qb; ++kb) {
-    if (kb < qb) tile_fetch(nxt, Kh, int64_t(kb + 1) * kB, N);
+  for (int kt = 0; kt < n_kt; ++kt) {
+    if (kt + 1 < n_kt) tile_fetch(nxt, Kh, int64_t(kt + 1) * kKT, N);
     __syncthreads();
-    const _Float16 (*cur)[kPad] = ks[kb & 1];
-    const bool edge = kb == qb || int64_t(kb + 1) * kB > N;   // diagonal or ragged block
-    float t[4][4];
+    const int64_t key0 = int64_t(kt) * kKT;
+    // (wave-uniform) skip a tile whose keys all lie after the wave's rows
+    if (key0 <= wrow0 + kWaveRows - 1 && wrow0 < N) {
+      const _Float16 (*cur)[kPad] = ks[kt & 1];
+      const bool edge = key0 + kKT - 1 > wrow0 || key0 + kKT > N;   // diagonal or ragged tile
+      float c[2][4][4];                                             // [fragment][sub][r]
 #pragma unroll
-    for (int sub = 0; sub < 4; ++sub) {
-      const f4 c = tile_product(qa, cur, sub);
-      const int64_t key = int64_t(kb) * kB + 16 * sub + (lane & 15);
+      for (int sub = 0; sub < 4; ++sub) {
+        h8 b[4];
+        load_tile_frag(b, cur, sub);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t row = row0 + 4 * (lane >> 4) + r;
-        t[sub][r] = (edge && (key > row || key >= N)) ? -INFINITY : c[r] * kLog2eOverSqrtD;
+        for (int f = 0; f < 2; ++f) {
+          const f4 v = mfma_16x16x128(qa[f], b);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) c[f][sub][r] = v[r];
+        }
       }
-    }
+      if (edge) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float mb = fmaxf(fmaxf(t[0][r], t[1][r]), fmaxf(t[2][r], t[3][r]));
-      const float mn = fmaxf(m[r], mb);
-      if (mn == -INFINITY) continue;
-      float acc = s[r];
-      if (mn > m[r]) acc = m[r] == -INFINITY ? 0.f : acc * __builtin_amdgcn_exp2f(m[r] - mn);
+        for (int f = 0; f < 2; ++f)
 #pragma unroll
-      for (int sub = 0; sub < 4; ++sub) acc += __builtin_amdgcn_exp2f(t[sub][r] - mn);
-      s[r] = acc;
-      m[r] = mn;
+          for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int64_t key = key0 + 16 * sub + (lane & 15);
+              const int64_t row = wrow0 + 16 * f + 4 * (lane >> 4) + r;
+              if (key > row || key >= N) c[f][sub][r] = -INFINITY;
+            }
+      }
+      // base-2 units: t = c * log2(e) / sqrt(d); the maximum is taken on c
+#pragma unroll
+      for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float cm = fmaxf(fmaxf(c[f][0][r], c[f][1][r]), fmaxf(c[f][2][r], c[f][3][r]));
+          const float mn = fmaxf(m[f][r], cm * kLog2eOverSqrtD);
+          if (mn == -INFINITY) continue;
+          float acc = s[f][r] * __builtin_amdgcn_exp2f(m[f][r] - mn);   // (0 while nothing was seen)
+#pragma unroll
+          for (int sub = 0; sub < 4; ++sub) acc += __builtin_amdgcn_exp2f(fmaf(c[f][sub][r], kLog2eOverSqrtD, -mn));
+          s[f][r] = acc;
+          m[f][r] = mn;
+        }
     }
-    if (kb < qb) tile_store(nxt, ks[(kb + 1) & 1]);
+    if (kt + 1 < n_kt) tile_store(nxt, ks[(kt + 1) & 1]);
   }
   // merge the 16 lanes that hold the same rows
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
+  for (int f = 0; f < 2; ++f)
 #pragma unroll
-    for (int x = 1; x < 16; x <<= 1) {
-      const float mo = __shfl_xor(m[r], x, 64), so = __shfl_xor(s[r], x, 64);
-      const float mn = fmaxf(m[r], mo);
-      if (mn != -INFINITY) {
-        s[r] = (m[r] == -INFINITY ? 0.f : s[r] * exp2f(m[r] - mn)) + (mo == -INFINITY ? 0.f : so * exp2f(mo - mn));
-        m[r] = mn;
+    for (int r = 0; r < 4; ++r) {
+      float mm = m[f][r], ss = s[f][r];
+#pragma unroll
+      for (int x = 1; x < 16; x <<= 1) {
+        const float mo = __shfl_xor(mm, x, 64), so = __shfl_xor(ss, x, 64);
+        const float mn = fmaxf(mm, mo);
+        if (mn != -INFINITY) {
+          ss = (mm == -INFINITY ? 0.f : ss * exp2f(mm - mn)) + (mo == -INFINITY ? 0.f : so * exp2f(mo - mn));
+          mm = mn;
+        }
       }
+      const int64_t row = wrow0 + 16 * f + 4 * (lane >> 4) + r;
+      if ((lane & 15) == 0 && row < N) a.lse[(sl * a.Hq + hq) * N + row] = mm + log2f(ss);
     }
-    const int64_t row = row0 + 4 * (lane >> 4) + r;
-    if ((lane & 15) == 0 && row < N) a.lse[(sl * a.Hq + hq) * N + row] = m[r] + log2f(s[r]);
-  }
 }
 
-__global__ __launch_bounds__(kThreads) void score_colsum_kernel(ScoreArgs a) {
-  __shared__ _Float16 qs[2][kB][kPad];
-  __shared__ float ls[2][kB];
+// Pass 2: workgroup = 128 keys of one KV head (32 per wave, two 16-key
+// fragments sharing every Q fragment read from LDS); walks the G query heads
+// and every 64-row query tile at or after the block's first key, summing
+// exp2(t - LSE) down each key column.  A key block is owned by one
+// workgroup, so no atomics and the summation order is fixed.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void score_colsum_kernel(ScoreArgs a) {
+  __shared__ _Float16 qs[2][kKT][kPad];
+  __shared__ float ls[2][kKT];
   const int64_t N = a.N;
-  const int nqb = int(cdiv(N, kB));
+  const int nqt = int(cdiv(N, kKT));
   const int kb = blockIdx.x;                  // short key indices have the most rows: first
   const int h = blockIdx.y;
   const int64_t sl = blockIdx.z;
   const __half* Kh = a.K + ((sl * a.Hkv + h) * N) * kHeadDim;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t key0 = int64_t(kb) * kB + 16 * wave;
+  const int64_t wkey0 = int64_t(kb) * kBlockRows + kWaveRows * wave;     // the wave's first key
 
-  h8 ka[4];
-  load_rows_frag(ka, Kh, key0 + (lane & 15), N);
-  double tot[4] = {0.0, 0.0, 0.0, 0.0};
-  // steps: (g, qb) for g in heads, qb in [kb, nqb)
-  const int per = nqb - kb, n_steps = a.G * per;
-  auto step_src = [&](int st, const __half*& Qh, const float*& lse, int& qb) {
+  h8 ka[2][4];
+  load_rows_frag(ka[0], Kh, wkey0 + (lane & 15), N);
+  load_rows_frag(ka[1], Kh, wkey0 + 16 + (lane & 15), N);
+  double tot[2][4] = {{0.0, 0.0, 0.0, 0.0}, {0.0, 0.0, 0.0, 0.0}};
+  // steps: (g, qt) for g in heads, qt in [qt0, nqt)
+  const int qt0 = int(int64_t(kb) * kBlockRows / kKT);
+  const int per = nqt - qt0, n_steps = a.G * per;
+  auto step_src = [&](int st, const __half*& Qh, const float*& lse, int& qt) {
     const int g = st / per;
-    qb = kb + st % per;
+    qt = qt0 + st % per;
     const int hq = h * a.G + g;
     Qh = a.Q + ((sl * a.Hq + hq) * N) * kHeadDim;
     lse = a.lse + (sl * a.Hq + hq) * N;
@@ -191,17 +235,17 @@ __global__ __launch_bounds__(kThreads) void score_colsum_kernel(ScoreArgs a) {
   auto fetch = [&](int st) {
     const __half* Qh;
     const float* lse;
-    int qb;
-    step_src(st, Qh, lse, qb);
-    tile_fetch(nxt, Qh, int64_t(qb) * kB, N);
-    if (threadIdx.x < kB) {
-      const int64_t row = int64_t(qb) * kB + threadIdx.x;
+    int qt;
+    step_src(st, Qh, lse, qt);
+    tile_fetch(nxt, Qh, int64_t(qt) * kKT, N);
+    if (threadIdx.x < kKT) {
+      const int64_t row = int64_t(qt) * kKT + threadIdx.x;
       lnext = row < N ? lse[row] : 0.f;
     }
   };
   auto store = [&](int buf) {
     tile_store(nxt, qs[buf]);
-    if (threadIdx.x < kB) ls[buf][threadIdx.x] = lnext;
+    if (threadIdx.x < kKT) ls[buf][threadIdx.x] = lnext;
   };
   fetch(0);
   store(0);
@@ -209,33 +253,49 @@ __global__ __launch_bounds__(kThreads) void score_colsum_kernel(ScoreArgs a) {
     if (st + 1 < n_steps) fetch(st + 1);
     __syncthreads();
     const int buf = st & 1;
-    const int qb = kb + st % per;
-    const bool edge = qb == kb || int64_t(qb + 1) * kB > N;
-    float part[4] = {0.f, 0.f, 0.f, 0.f};
+    const int64_t qrow0 = int64_t(qt0 + st % per) * kKT;
+    // (wave-uniform) skip a tile whose rows all lie before the wave's keys
+    if (qrow0 + kKT - 1 >= wkey0 && wkey0 < N) {
+      const bool edge = qrow0 < wkey0 + kWaveRows - 1 || qrow0 + kKT > N;
+      float part[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int sub = 0; sub < 4; ++sub) {
-      const f4 c = tile_product(ka, qs[buf], sub);
-      const int64_t query = int64_t(qb) * kB + 16 * sub + (lane & 15);
-      const float lq = ls[buf][16 * sub + (lane & 15)];
+      for (int sub = 0; sub < 4; ++sub) {
+        h8 b[4];
+        load_tile_frag(b, qs[buf], sub);
+        const int64_t query = qrow0 + 16 * sub + (lane & 15);
+        const float lq = ls[buf][16 * sub + (lane & 15)];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t key = key0 + 4 * (lane >> 4) + r;
-        const float e = __builtin_amdgcn_exp2f(fmaf(c[r], kLog2eOverSqrtD, -lq));
-        part[r] += (edge && (query < key || query >= N)) ? 0.f : e;
+        for (int f = 0; f < 2; ++f) {
+          const f4 c = mfma_16x16x128(ka[f], b);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float e = __builtin_amdgcn_exp2f(fmaf(c[r], kLog2eOverSqrtD, -lq));
+            if (edge) {
+              const int64_t key = wkey0 + 16 * f + 4 * (lane >> 4) + r;
+              part[f][r] += (query < key || query >= N) ? 0.f : e;
+            } else {
+              part[f][r] += e;
+            }
+          }
+        }
       }
-    }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) tot[r] += double(part[r]);
+      for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) tot[f][r] += double(part[f][r]);
+    }
     if (st + 1 < n_steps) store((st + 1) & 1);
   }
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    double v = tot[r];
+  for (int f = 0; f < 2; ++f)
 #pragma unroll
-    for (int x = 1; x < 16; x <<= 1) v += __shfl_xor(v, x, 64);
-    const int64_t key = key0 + 4 * (lane >> 4) + r;
-    if ((lane & 15) == 0 && key < N) a.w_tok[(sl * a.Hkv + h) * N + key] = float(v);
-  }
+    for (int r = 0; r < 4; ++r) {
+      double v = tot[f][r];
+#pragma unroll
+      for (int x = 1; x < 16; x <<= 1) v += __shfl_xor(v, x, 64);
+      const int64_t key = wkey0 + 16 * f + 4 * (lane >> 4) + r;
+      if ((lane & 15) == 0 && key < N) a.w_tok[(sl * a.Hkv + h) * N + key] = float(v);
+    }
 }
 
 // Population variance of each V row: one wave per token, two passes in registers.
@@ -315,7 +375,7 @@ hipError_t launch_score(const ScoreParams& p, hipStream_t stream) {
   const int G = p.Hq / p.Hkv;
   ScoreArgs a{p.n_tokens, p.Hq, p.Hkv, G, p.Q, p.K, p.lse, p.w_tok};
   const int64_t SL = int64_t(p.S) * p.L;
-  const unsigned nb = unsigned(cdiv(p.n_tokens, kB));
+  const unsigned nb = unsigned(cdiv(p.n_tokens, kBlockRows));
   hipLaunchKernelGGL(score_lse_kernel, dim3(nb, unsigned(p.Hq), unsigned(SL)), dim3(kThreads), 0, stream, a);
   hipLaunchKernelGGL(score_colsum_kernel, dim3(nb, unsigned(p.Hkv), unsigned(SL)), dim3(kThreads), 0, stream, a);
   const int64_t rows = SL * p.Hkv * p.n_tokens;

@@ -129,3 +129,47 @@ def test_full_size_pack_and_decode_sampled(gpu_lib, name):
     for o in outs[1:]:
         assert torch.equal(o, outs[0]), "repeated decodes differ"
     assert bool(torch.isfinite(outs[0]).all()), "non-finite decode output"
+
+
+# ------------------------------------------------------------------ scoring at full context length
+
+def test_score_uniform_attention_closed_form_at_256k(gpu_lib):
+    """With Q = 0 every causal row attends uniformly, so the token weight has
+    the closed form w_t = G * (H_N - H_t), H_n the n-th harmonic number
+    (t 0-indexed; the weight of a token is the summed attention it receives,
+    RDKV summary section 2.1).  At N = 262,144, the 72B-shaped stack's context
+    (G = 8), this pins both scoring passes over their longest accumulations
+    without an oracle run."""
+    rdkv = gpu_lib
+    G, N = 8, 262144
+    dims = rdkv.make_dims(1, 1, G, 1, N)
+    Q = torch.zeros((1, 1, G, N, 128), dtype=torch.float16, device=DEV)
+    gen = torch.Generator(device=DEV).manual_seed(11)
+    K = torch.randn((1, 1, 1, N, 128), generator=gen, device=DEV).half()
+    V = torch.randn((1, 1, 1, N, 128), generator=gen, device=DEV).half()
+    wt, _, _ = rdkv.score(dims, Q, K, V)
+    got = wt[0, 0, 0].double().cpu().numpy()
+    inv = 1.0 / np.arange(1, N + 1, dtype=np.float64)
+    suffix = np.cumsum(inv[::-1])[::-1]          # sum_{tau >= t} 1 / (tau + 1) = H_N - H_t
+    ref = G * suffix
+    err = float(np.max(np.abs(got - ref) / ref))
+    print(f"closed-form w_t at N={N}: max rel err {err:.3g}")
+    assert err <= TOL
+    assert abs(got.sum() - G * N) <= TOL * G * N
+
+
+def test_score_weights_sum_to_query_rows_on_a_128k_layer(gpu_lib):
+    """On one layer of the 128K, 8B-shaped workload (32 query heads over 8 KV
+    heads, biased synthetic activations) every KV head's token weights sum to
+    G * N, the number of query rows that each distribute one unit of
+    attention, and all are positive."""
+    rdkv = gpu_lib
+    w = synth.WORKLOADS["llama8b-32layer-n128k"]
+    Q, K, V = synth.prefill_layer(w, 0, 5, device=DEV)
+    dims = rdkv.make_dims(1, 1, w.n_q_heads, w.n_kv_heads, w.n_tokens)
+    wt, vt, wc = rdkv.score(dims, Q[None, None].contiguous(), K[None, None].contiguous(), V[None, None].contiguous())
+    sums = wt[0, 0].double().sum(dim=-1).cpu().numpy()
+    G = w.n_q_heads // w.n_kv_heads
+    print(f"sum of w_t per KV head / (G N): {sums / (G * w.n_tokens)}")
+    assert np.all(np.abs(sums - G * w.n_tokens) <= TOL * G * w.n_tokens)
+    assert bool((wt > 0).all()) and bool((vt > 0).all()) and bool((wc > 0).all())
