@@ -8,7 +8,7 @@
 // fp16 inputs, fp32 accumulation):
 //   score_lse_kernel     workgroup = 128 query rows of one query head; walks
 //                        the key tiles up to its last row, keeps a per-lane
-//                        online (max, sum) in base 2, then merges across lanes.
+//                        online (max, sum), then merges across lanes.
 //   score_colsum_kernel  workgroup = 128 keys of one KV head; walks the G
 //                        query heads and every query tile at or after the
 //                        keys, summing exp2(s' - LSE') down each key column.
@@ -98,10 +98,66 @@ __device__ inline f4 mfma_16x16x128(const h8 (&a)[4], const h8 (&b)[4]) {
   return c;
 }
 
+// max(a, b, c) in one instruction (inputs are finite or -inf).
+__device__ inline float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// One key tile of pass 1 for a wave's 32 rows: scores by MFMA, then the
+// online update of the row's running maximum m of the raw scores c and of
+// s = sum exp2((c - m) * log2(e) / sqrt(d)).  kEdge: keys after a row, or at
+// or past N, are masked.
+template <bool kEdge>
+__device__ inline void lse_tile(const h8 (&qa)[2][4], const _Float16 (*cur)[kPad], int key0, int wrow0, int N,
+                                float (&m)[2][4], float (&s)[2][4]) {
+  const int lane = threadIdx.x & 63;
+  float c[2][4][4];   // [fragment][sub][r]
+#pragma unroll
+  for (int sub = 0; sub < 4; ++sub) {
+    h8 b[4];
+    load_tile_frag(b, cur, sub);
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      const f4 v = mfma_16x16x128(qa[f], b);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) c[f][sub][r] = v[r];
+    }
+  }
+  if constexpr (kEdge) {
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = key0 + 16 * sub + (lane & 15);
+          const int row = wrow0 + 16 * f + 4 * (lane >> 4) + r;
+          if (key > row || key >= N) c[f][sub][r] = -INFINITY;
+        }
+  }
+#pragma unroll
+  for (int f = 0; f < 2; ++f)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float mn = max3f(max3f(c[f][0][r], c[f][1][r], c[f][2][r]), c[f][3][r], m[f][r]);
+      if constexpr (kEdge) {
+        if (mn == -INFINITY) continue;   // nothing visible to this row yet
+      }
+      const float mk = mn * kLog2eOverSqrtD;
+      float acc = s[f][r] * __builtin_amdgcn_exp2f(fmaf(m[f][r], kLog2eOverSqrtD, -mk));   // (0 while nothing was seen)
+#pragma unroll
+      for (int sub = 0; sub < 4; ++sub) acc += __builtin_amdgcn_exp2f(fmaf(c[f][sub][r], kLog2eOverSqrtD, -mk));
+      s[f][r] = acc;
+      m[f][r] = mn;
+    }
+}
+
 // Pass 1: workgroup = 128 query rows of one query head (32 per wave, two
 // 16-row fragments sharing every K fragment read from LDS); walks the key
-// tiles up to the block's last row.  Per lane and row an online (max, sum)
-// in base 2, merged across the 16 lanes of a row at the end.
+// tiles up to the block's last row.  Per lane and row an online (max, sum),
+// merged across the 16 lanes of a row at the end in base 2.
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void score_lse_kernel(ScoreArgs a) {
   __shared__ _Float16 ks[2][kKT][kPad];
   const int64_t N = a.N;
@@ -137,45 +193,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     // (wave-uniform) skip a tile whose keys all lie after the wave's rows
     if (key0 <= wrow0 + kWaveRows - 1 && wrow0 < N) {
       const _Float16 (*cur)[kPad] = ks[kt & 1];
-      const bool edge = key0 + kKT - 1 > wrow0 || key0 + kKT > N;   // diagonal or ragged tile
-      float c[2][4][4];                                             // [fragment][sub][r]
-#pragma unroll
-      for (int sub = 0; sub < 4; ++sub) {
-        h8 b[4];
-        load_tile_frag(b, cur, sub);
-#pragma unroll
-        for (int f = 0; f < 2; ++f) {
-          const f4 v = mfma_16x16x128(qa[f], b);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) c[f][sub][r] = v[r];
-        }
+      // diagonal or ragged tile: masks; otherwise every key precedes every row
+      if (key0 + kKT - 1 > wrow0 || key0 + kKT > N) {
+        lse_tile<true>(qa, cur, int(key0), int(wrow0), int(N), m, s);
+      } else {
+        lse_tile<false>(qa, cur, int(key0), int(wrow0), int(N), m, s);
       }
-      if (edge) {
-#pragma unroll
-        for (int f = 0; f < 2; ++f)
-#pragma unroll
-          for (int sub = 0; sub < 4; ++sub)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int64_t key = key0 + 16 * sub + (lane & 15);
-              const int64_t row = wrow0 + 16 * f + 4 * (lane >> 4) + r;
-              if (key > row || key >= N) c[f][sub][r] = -INFINITY;
-            }
-      }
-      // base-2 units: t = c * log2(e) / sqrt(d); the maximum is taken on c
-#pragma unroll
-      for (int f = 0; f < 2; ++f)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float cm = fmaxf(fmaxf(c[f][0][r], c[f][1][r]), fmaxf(c[f][2][r], c[f][3][r]));
-          const float mn = fmaxf(m[f][r], cm * kLog2eOverSqrtD);
-          if (mn == -INFINITY) continue;
-          float acc = s[f][r] * __builtin_amdgcn_exp2f(m[f][r] - mn);   // (0 while nothing was seen)
-#pragma unroll
-          for (int sub = 0; sub < 4; ++sub) acc += __builtin_amdgcn_exp2f(fmaf(c[f][sub][r], kLog2eOverSqrtD, -mn));
-          s[f][r] = acc;
-          m[f][r] = mn;
-        }
     }
     if (kt + 1 < n_kt) tile_store(nxt, ks[(kt + 1) & 1]);
   }
@@ -184,7 +207,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   for (int f = 0; f < 2; ++f)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float mm = m[f][r], ss = s[f][r];
+      float mm = m[f][r] * kLog2eOverSqrtD, ss = s[f][r];   // base-2 units (-inf stays -inf)
 #pragma unroll
       for (int x = 1; x < 16; x <<= 1) {
         const float mo = __shfl_xor(mm, x, 64), so = __shfl_xor(ss, x, 64);
@@ -197,6 +220,41 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
       const int64_t row = wrow0 + 16 * f + 4 * (lane >> 4) + r;
       if ((lane & 15) == 0 && row < N) a.lse[(sl * a.Hq + hq) * N + row] = mm + log2f(ss);
     }
+}
+
+// One query tile of pass 2 for a wave's 32 keys: scores by MFMA and
+// exp2(t - LSE) summed per key, added to the fp64 totals.  kEdge: queries
+// before a key, or at or past N, are masked.
+template <bool kEdge>
+__device__ inline void colsum_tile(const h8 (&ka)[2][4], const _Float16 (*cur)[kPad], const float* lse, int qrow0,
+                                   int wkey0, int N, double (&tot)[2][4]) {
+  const int lane = threadIdx.x & 63;
+  float part[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int sub = 0; sub < 4; ++sub) {
+    h8 b[4];
+    load_tile_frag(b, cur, sub);
+    const int query = qrow0 + 16 * sub + (lane & 15);
+    const float lq = lse[16 * sub + (lane & 15)];
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      const f4 c = mfma_16x16x128(ka[f], b);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float e = __builtin_amdgcn_exp2f(fmaf(c[r], kLog2eOverSqrtD, -lq));
+        if constexpr (kEdge) {
+          const int key = wkey0 + 16 * f + 4 * (lane >> 4) + r;
+          part[f][r] += (query < key || query >= N) ? 0.f : e;
+        } else {
+          part[f][r] += e;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int f = 0; f < 2; ++f)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) tot[f][r] += double(part[f][r]);
 }
 
 // Pass 2: workgroup = 128 keys of one KV head (32 per wave, two 16-key
@@ -256,33 +314,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     const int64_t qrow0 = int64_t(qt0 + st % per) * kKT;
     // (wave-uniform) skip a tile whose rows all lie before the wave's keys
     if (qrow0 + kKT - 1 >= wkey0 && wkey0 < N) {
-      const bool edge = qrow0 < wkey0 + kWaveRows - 1 || qrow0 + kKT > N;
-      float part[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-      for (int sub = 0; sub < 4; ++sub) {
-        h8 b[4];
-        load_tile_frag(b, qs[buf], sub);
-        const int64_t query = qrow0 + 16 * sub + (lane & 15);
-        const float lq = ls[buf][16 * sub + (lane & 15)];
-#pragma unroll
-        for (int f = 0; f < 2; ++f) {
-          const f4 c = mfma_16x16x128(ka[f], b);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float e = __builtin_amdgcn_exp2f(fmaf(c[r], kLog2eOverSqrtD, -lq));
-            if (edge) {
-              const int64_t key = wkey0 + 16 * f + 4 * (lane >> 4) + r;
-              part[f][r] += (query < key || query >= N) ? 0.f : e;
-            } else {
-              part[f][r] += e;
-            }
-          }
-        }
+      // diagonal or ragged tile: masks; otherwise every row follows every key
+      if (qrow0 < wkey0 + kWaveRows - 1 || qrow0 + kKT > N) {
+        colsum_tile<true>(ka, qs[buf], ls[buf], int(qrow0), int(wkey0), int(N), tot);
+      } else {
+        colsum_tile<false>(ka, qs[buf], ls[buf], int(qrow0), int(wkey0), int(N), tot);
       }
-#pragma unroll
-      for (int f = 0; f < 2; ++f)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) tot[f][r] += double(part[f][r]);
     }
     if (st + 1 < n_steps) store((st + 1) & 1);
   }
