@@ -105,13 +105,17 @@ __device__ inline float max3f(float a, float b, float c) {
   return r;
 }
 
-// One key tile of pass 1 for a wave's 32 rows: scores by MFMA, then the
-// online update of the row's running maximum m of the raw scores c and of
-// s = sum exp2((c - m) * log2(e) / sqrt(d)).  kEdge: keys after a row, or at
-// or past N, are masked.
+// One key tile of pass 1 for a wave's 32 rows: scores c by MFMA, then per
+// row the running sum s = sum exp2(c * k - mk) (k = log2(e) / sqrt(d)) over a
+// reference mk = m * k.  The reference m is the row's maximum score when it was
+// last raised; it is raised (and s rescaled) only when a score exceeds it by
+// more than kSlack / k, so the terms stay below 2^kSlack and, after the first
+// tiles, most tiles rescale nothing.  kEdge: keys after a row, or at or past
+// N, are masked.
+constexpr float kSlack = 8.0f;   // base-2 headroom of a term above the reference
 template <bool kEdge>
 __device__ inline void lse_tile(const h8 (&qa)[2][4], const _Float16 (*cur)[kPad], int key0, int wrow0, int N,
-                                float (&m)[2][4], float (&s)[2][4]) {
+                                float (&thr)[2][4], float (&mk)[2][4], float (&s)[2][4]) {
   const int lane = threadIdx.x & 63;
   float c[2][4][4];   // [fragment][sub][r]
 #pragma unroll
@@ -137,20 +141,38 @@ __device__ inline void lse_tile(const h8 (&qa)[2][4], const _Float16 (*cur)[kPad
           if (key > row || key >= N) c[f][sub][r] = -INFINITY;
         }
   }
+  float cm[2][4];
+  bool up = false;
 #pragma unroll
   for (int f = 0; f < 2; ++f)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float mn = max3f(max3f(c[f][0][r], c[f][1][r], c[f][2][r]), c[f][3][r], m[f][r]);
-      if constexpr (kEdge) {
-        if (mn == -INFINITY) continue;   // nothing visible to this row yet
-      }
-      const float mk = mn * kLog2eOverSqrtD;
-      float acc = s[f][r] * __builtin_amdgcn_exp2f(fmaf(m[f][r], kLog2eOverSqrtD, -mk));   // (0 while nothing was seen)
+      cm[f][r] = fmaxf(max3f(c[f][0][r], c[f][1][r], c[f][2][r]), c[f][3][r]);
+      up = up || cm[f][r] > thr[f][r];
+    }
+  if (__builtin_amdgcn_ballot_w64(up) != 0) {   // (wave-uniform; rare after the first tiles)
 #pragma unroll
-      for (int sub = 0; sub < 4; ++sub) acc += __builtin_amdgcn_exp2f(fmaf(c[f][sub][r], kLog2eOverSqrtD, -mk));
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (cm[f][r] > thr[f][r]) {
+          const float mnew = cm[f][r] * kLog2eOverSqrtD;
+          s[f][r] *= __builtin_amdgcn_exp2f(mk[f][r] - mnew);   // (0 while nothing was seen)
+          mk[f][r] = mnew;
+          thr[f][r] = cm[f][r] + kSlack / kLog2eOverSqrtD;
+        }
+  }
+#pragma unroll
+  for (int f = 0; f < 2; ++f)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if constexpr (kEdge) {
+        if (mk[f][r] == -INFINITY) continue;   // nothing visible to this row yet
+      }
+      float acc = s[f][r];
+#pragma unroll
+      for (int sub = 0; sub < 4; ++sub) acc += __builtin_amdgcn_exp2f(fmaf(c[f][sub][r], kLog2eOverSqrtD, -mk[f][r]));
       s[f][r] = acc;
-      m[f][r] = mn;
     }
 }
 
@@ -175,12 +197,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   h8 qa[2][4];
   load_rows_frag(qa[0], Qh, wrow0 + (lane & 15), N);
   load_rows_frag(qa[1], Qh, wrow0 + 16 + (lane & 15), N);
-  float m[2][4], s[2][4];
+  float thr[2][4], mk[2][4], s[2][4];   // raise threshold (raw units), reference (base 2), sum
 #pragma unroll
   for (int f = 0; f < 2; ++f)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      m[f][r] = -INFINITY;
+      thr[f][r] = -INFINITY;
+      mk[f][r] = -INFINITY;
       s[f][r] = 0.f;
     }
   TileRegs nxt;
@@ -195,9 +218,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
       const _Float16 (*cur)[kPad] = ks[kt & 1];
       // diagonal or ragged tile: masks; otherwise every key precedes every row
       if (key0 + kKT - 1 > wrow0 || key0 + kKT > N) {
-        lse_tile<true>(qa, cur, int(key0), int(wrow0), int(N), m, s);
+        lse_tile<true>(qa, cur, int(key0), int(wrow0), int(N), thr, mk, s);
       } else {
-        lse_tile<false>(qa, cur, int(key0), int(wrow0), int(N), m, s);
+        lse_tile<false>(qa, cur, int(key0), int(wrow0), int(N), thr, mk, s);
       }
     }
     if (kt + 1 < n_kt) tile_store(nxt, ks[(kt + 1) & 1]);
@@ -207,7 +230,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   for (int f = 0; f < 2; ++f)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float mm = m[f][r] * kLog2eOverSqrtD, ss = s[f][r];   // base-2 units (-inf stays -inf)
+      float mm = mk[f][r], ss = s[f][r];
 #pragma unroll
       for (int x = 1; x < 16; x <<= 1) {
         const float mo = __shfl_xor(mm, x, 64), so = __shfl_xor(ss, x, 64);
