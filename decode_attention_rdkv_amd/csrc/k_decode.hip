@@ -37,6 +37,13 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
+// Query heads a wave carries.  With 8 heads per KV head the waves split them:
+// waves w and w + 2 walk the same tiles for heads 0-3 and 4-7, so a wave keeps
+// the 4-head register footprint (accumulators, coefficients) of the smaller
+// groups instead of spilling.
+template <int G> constexpr int kHeadsPerWave = G > 4 ? 4 : G;
+// Tile streams of a workgroup: waves with the same stream index walk the same tiles.
+template <int G> constexpr int kStreams = kWaves / (G / kHeadsPerWave<G>);
 constexpr int kTile = 64;
 constexpr float kLog2eOverSqrtD = 1.4426950408889634f / 11.313708498984761f;
 constexpr float kTwo24 = 16777216.0f;   // codes enter dot2 as fp16 subnormals code * 2^-24
@@ -190,10 +197,10 @@ __host__ __device__ constexpr int ring_stages() { return SW == 0 ? 0 : 3 * stage
 
 // Per wave, the record ring and, once the wave's last tile is done, its
 // partial output share one region.
-template <int G, int SW>
+template <int GW, int SW>
 union __align__(16) WaveLds {
   uint32_t ring[SW > 0 ? ring_stages<SW>() * stage_words<SW>() : 1];
-  float o[G][kHeadDim];
+  float o[GW][kHeadDim];
 };
 
 template <int G, int SW>
@@ -203,24 +210,22 @@ struct __align__(16) Smem {
   uint16_t qperm[G][kHeadDim];           // query with channels in record order
   uint16_t qnat[G][kHeadDim];            // query as given
   uint8_t perm[kHeadDim];                // record order -> channel
-  uint32_t coefh[kWaves][kTile / 2][G];  // fp16 (p*scale) of tile tokens (j, j + 32)
-  WaveLds<G, SW> wv[kWaves];
-  float part_ml[kWaves][G][2];
+  uint32_t coefh[kWaves][kTile / 2][kHeadsPerWave<G>];  // fp16 (p*scale) of tile tokens (j, j + 32)
+  WaveLds<kHeadsPerWave<G>, SW> wv[kWaves];
+  float part_ml[kWaves][kHeadsPerWave<G>][2];
 };
 
-template <int G, int SW>
-__device__ inline void load_qp(const Smem<G, SW>& sm, int slot, uint32_t (&q)[G]) {
-  if constexpr (G % 4 == 0) {
-#pragma unroll
-    for (int j = 0; j < G / 4; ++j) {
-      const uint4 t = reinterpret_cast<const uint4*>(&sm.qpair[slot][0])[j];
-      q[4 * j] = t.x, q[4 * j + 1] = t.y, q[4 * j + 2] = t.z, q[4 * j + 3] = t.w;
-    }
-  } else if constexpr (G == 2) {
-    const uint2 t = *reinterpret_cast<const uint2*>(&sm.qpair[slot][0]);
+// The query pairs of heads hb .. hb + GW - 1 for one pair slot.
+template <int GW, int G, int SW>
+__device__ inline void load_qp(const Smem<G, SW>& sm, int slot, int hb, uint32_t (&q)[GW]) {
+  if constexpr (GW == 4) {
+    const uint4 t = *reinterpret_cast<const uint4*>(&sm.qpair[slot][hb]);
+    q[0] = t.x, q[1] = t.y, q[2] = t.z, q[3] = t.w;
+  } else if constexpr (GW == 2) {
+    const uint2 t = *reinterpret_cast<const uint2*>(&sm.qpair[slot][hb]);
     q[0] = t.x, q[1] = t.y;
   } else {
-    q[0] = sm.qpair[slot][0];
+    q[0] = sm.qpair[slot][hb];
   }
 }
 
@@ -323,18 +328,18 @@ __device__ inline QkShape qk_shape(const SegInfo& si) {
 // halves; the first P/2 pairs are masked in place, the rest after one shift
 // by 8, so a code arrives as code * 2^(kBits * (e mod P/2)) * 2^-24, which the
 // query table has divided out.
-template <int G, int SW, int P>
+template <int GW, int G, int SW, int P>
 __device__ inline void int_part(const uint32_t* rec, int& w, int& sl, int words, int tail, const Smem<G, SW>& sm,
-                                float (&d)[G]) {
+                                int hb, float (&d)[GW]) {
   constexpr int kBits = 16 / P;
   constexpr uint32_t kMask = ((1u << kBits) - 1u) * 0x00010001u;
-  uint32_t q[G];
+  uint32_t q[GW];
   auto slot = [&](uint32_t x, int e) {
-    load_qp<G, SW>(sm, sl + e, q);
+    load_qp<GW>(sm, sl + e, hb, q);
     const int half = e >= P / 2;
     const uint32_t pr = (half ? x >> 8 : x) & (kMask << (kBits * (e - half * (P / 2))));
 #pragma unroll
-    for (int g = 0; g < G; ++g) d[g] = dot2(pr, q[g], d[g]);
+    for (int g = 0; g < GW; ++g) d[g] = dot2(pr, q[g], d[g]);
   };
   // full words without per-slot tests, then the last word's `tail` slots
   for (int j = 0; j + 1 < words; ++j, ++w, sl += P) {
@@ -351,29 +356,29 @@ __device__ inline void int_part(const uint32_t* rec, int& w, int& sl, int words,
 
 // s[g] = q_g . k_hat for one token whose record words are rec[0..).  The
 // record may live in LDS (staged) or in global memory.
-template <int G, int SW>
+template <int GW, int G, int SW>
 __device__ inline void record_logits(const uint32_t* rec, const QkShape& ks, int nw, bool has_vmeta,
-                                     const Smem<G, SW>& sm, float (&s)[G], float& vs, float& vz) {
-  uint32_t q[G];
+                                     const Smem<G, SW>& sm, int hb, float (&s)[GW], float& vs, float& vz) {
+  uint32_t q[GW];
 #pragma unroll
-  for (int g = 0; g < G; ++g) s[g] = 0.f;
+  for (int g = 0; g < GW; ++g) s[g] = 0.f;
   int w = 0, sl = 0, mo = ks.meta;
   for (; w < ks.w16; ++w, ++sl) {
     const uint32_t x = rec[w];
-    load_qp<G, SW>(sm, sl, q);
+    load_qp<GW>(sm, sl, hb, q);
 #pragma unroll
-    for (int g = 0; g < G; ++g) s[g] = dot2(x, q[g], s[g]);
+    for (int g = 0; g < GW; ++g) s[g] = dot2(x, q[g], s[g]);
   }
   auto part = [&](auto pairs, int i) {
     if (ks.words[i] == 0) return;
-    float d[G];
+    float d[GW];
 #pragma unroll
-    for (int g = 0; g < G; ++g) d[g] = 0.f;
-    int_part<G, SW, decltype(pairs)::value>(rec, w, sl, ks.words[i], ks.tail[i], sm, d);
+    for (int g = 0; g < GW; ++g) d[g] = 0.f;
+    int_part<GW, G, SW, decltype(pairs)::value>(rec, w, sl, ks.words[i], ks.tail[i], sm, hb, d);
     const uint32_t m = rec[mo++];
     const float sc = half_lo(m) * kTwo24, z = half_hi(m);
 #pragma unroll
-    for (int g = 0; g < G; ++g) s[g] = fmaf(sc, d[g], fmaf(z, sm.qsum[i][g], s[g]));
+    for (int g = 0; g < GW; ++g) s[g] = fmaf(sc, d[g], fmaf(z, sm.qsum[i][hb + g], s[g]));
   };
   part(std::integral_constant<int, 2>{}, 0);
   part(std::integral_constant<int, 4>{}, 1);
@@ -517,11 +522,11 @@ __device__ inline void state_init(WaveState<G>& st) {
 // Online softmax update for one tile (lane = token): the running max m (log2
 // units, wave-uniform) is raised, with the sums rescaled, only when some
 // lane's logit exceeds it.  Writes fp16 p*vs per token to LDS.
-template <int G, int SW, bool kMasked>
-__device__ inline void softmax_tile(WaveState<G>& st, const float (&s)[G], bool valid, float vs, float vz,
+template <int GW, int G, int SW, bool kMasked>
+__device__ inline void softmax_tile(WaveState<GW>& st, const float (&s)[GW], bool valid, float vs, float vz,
                                     Smem<G, SW>& sm, int wave, int lane) {
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
+  for (int g = 0; g < GW; ++g) {
     const float t = (!kMasked || valid) ? s[g] * kLog2eOverSqrtD : -INFINITY;
     if (__builtin_amdgcn_ballot_w64(t > st.m[g]) != 0) {
       const float mnew = fmaxf(st.m[g], wave_reduce<true>(t));
@@ -539,17 +544,14 @@ __device__ inline void softmax_tile(WaveState<G>& st, const float (&s)[G], bool 
   }
 }
 
-template <int G, int SW>
-__device__ inline void load_coefs(const Smem<G, SW>& sm, int wave, int j, uint32_t (&cf)[G]) {
-  if constexpr (G % 4 == 0) {
-#pragma unroll
-    for (int i = 0; i < G / 4; ++i) {
-      const uint4 t = reinterpret_cast<const uint4*>(&sm.coefh[wave][j][0])[i];
-      cf[4 * i] = t.x, cf[4 * i + 1] = t.y, cf[4 * i + 2] = t.z, cf[4 * i + 3] = t.w;
-    }
+template <int GW, int G, int SW>
+__device__ inline void load_coefs(const Smem<G, SW>& sm, int wave, int j, uint32_t (&cf)[GW]) {
+  if constexpr (GW == 4) {
+    const uint4 t = *reinterpret_cast<const uint4*>(&sm.coefh[wave][j][0]);
+    cf[0] = t.x, cf[1] = t.y, cf[2] = t.z, cf[3] = t.w;
   } else {
 #pragma unroll
-    for (int g = 0; g < G; ++g) cf[g] = sm.coefh[wave][j][g];
+    for (int g = 0; g < GW; ++g) cf[g] = sm.coefh[wave][j][g];
   }
 }
 
@@ -559,15 +561,15 @@ __device__ inline void load_coefs(const Smem<G, SW>& sm, int wave, int j, uint32
 // their lane-32 sums in its two halves, v_permlane16_swap pairs those again,
 // so quarter q of register k ends up with value 4k + {0, 2, 1, 3}[q] of the
 // flat index 8g + e.
-template <int G, int B, int SW>
-__device__ inline void wave_finish(WaveState<G>& st, Smem<G, SW>& sm, int wave, int lane) {
+template <int GW, int B, int G, int SW>
+__device__ inline void wave_finish(WaveState<GW>& st, Smem<G, SW>& sm, int wave, int lane) {
   const int cb = lane & 15, qr = lane >> 4;
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
+  for (int g = 0; g < GW; ++g) {
     st.l[g] = wave_reduce<false>(st.l[g]);
     st.z[g] = wave_reduce<false>(st.z[g]);
   }
-  constexpr int kN = 8 * G;
+  constexpr int kN = 8 * GW;
   float u[kN / 2];
 #pragma unroll
   for (int j = 0; j < kN / 2; ++j) {
@@ -590,7 +592,7 @@ __device__ inline void wave_finish(WaveState<G>& st, Smem<G, SW>& sm, int wave, 
   }
   if (lane == 0) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
+    for (int g = 0; g < GW; ++g) {
       sm.part_ml[wave][g][0] = st.m[g];
       sm.part_ml[wave][g][1] = st.l[g];
     }
@@ -687,18 +689,20 @@ __device__ inline void wait_vmem() {
 // touching memory: no per-lane clamping, and tile addresses stay scalar.
 template <int G, int B, int SW, bool PIPE>
 __device__ void run_group(const DecodeParams& p, const SegInfo& si, const Plan& pl, int64_t seg, Smem<G, SW>& sm) {
+  constexpr int GW = kHeadsPerWave<G>, kNS = kStreams<G>, kStride = kTile * kNS;
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int cb = lane & 15, ts = lane >> 4;
+  const int hb = kNS == kWaves ? 0 : (wave / kNS) * GW;           // the wave's first query head
   const QkShape ks = qk_shape(si);
   const int nw = pl.rec_words;
   const uint8_t* rbytes = p.cache + si.off_krec;                   // 256-byte aligned
   const uint8_t* vbase = p.cache + pl.vbase;
   constexpr int kRowBytes = kHeadDim * B / 8;
-  const int first = pl.start + kTile * wave;                       // the wave's tiles: first + 256 i
-  const int n_tiles = first < pl.end ? (pl.end - first + kThreads - 1) / kThreads : 0;
-  auto tile_row = [&](int i) { return first + kThreads * min(i, n_tiles - 1); };
+  const int first = pl.start + kTile * (wave % kNS);               // the wave's tiles: first + kStride i
+  const int n_tiles = first < pl.end ? (pl.end - first + kStride - 1) / kStride : 0;
+  auto tile_row = [&](int i) { return first + kStride * min(i, n_tiles - 1); };
   // rows of tile i inside the chunk; none for the tiles past the wave's last
-  auto tile_rows = [&](int i) { return i < n_tiles ? min(kTile, pl.end - (first + kThreads * i)) : 0; };
+  auto tile_rows = [&](int i) { return i < n_tiles ? min(kTile, pl.end - (first + kStride * i)) : 0; };
 
   // Ring: tile i's records live in stage i mod S.  The first S - 1 tiles are
   // copied up front; the end of step i copies tile i + S - 1 into the stage
@@ -761,7 +765,7 @@ __device__ void run_group(const DecodeParams& p, const SegInfo& si, const Plan& 
   build_query_tables<G, SW>(p, si, pl, seg, sm);
   __syncthreads();
 
-  WaveState<G> st;
+  WaveState<GW> st;
   state_init(st);
   const int lane_rec = lane * nw;                                  // the lane's record in a stage
   auto tile = [&](int i, VPair<B> (&cur)[kPairsPerLane], VPair<B> (&nxt)[kPairsPerLane]) {
@@ -776,25 +780,25 @@ __device__ void run_group(const DecodeParams& p, const SegInfo& si, const Plan& 
     } else {
       my = reinterpret_cast<const uint32_t*>(rbytes) + pl.rec0 + int64_t(min(b + lane, pl.end - 1)) * nw;
     }
-    float s[G], vs, vz;
-    record_logits<G, SW>(my, ks, nw, B < 16, sm, s, vs, vz);
+    float s[GW], vs, vz;
+    record_logits<GW>(my, ks, nw, B < 16, sm, hb, s, vs, vz);
     if (b + kTile <= pl.end) {
-      softmax_tile<G, SW, false>(st, s, true, vs, vz, sm, wave, lane);
+      softmax_tile<GW, G, SW, false>(st, s, true, vs, vz, sm, wave, lane);
     } else {
-      softmax_tile<G, SW, true>(st, s, b + lane < pl.end, vs, vz, sm, wave, lane);
+      softmax_tile<GW, G, SW, true>(st, s, b + lane < pl.end, vs, vz, sm, wave, lane);
     }
     wave_lds_sync();
     __amdgpu_buffer_rsrc_t rl;
     if constexpr (kLateV) rl = vrsrc(i);
 #pragma unroll
     for (int k = 0; k < kPairsPerLane; ++k) {
-      uint32_t cf[G];
-      load_coefs<G, SW>(sm, wave, ts + 4 * k, cf);
+      uint32_t cf[GW];
+      load_coefs<GW>(sm, wave, ts + 4 * k, cf);
       if constexpr (kLateV) {
         const VPair<B> v = load_pair(rl, k);
-        pv_pair<G, B>(st.acc, v, cf, sel2);
+        pv_pair<GW, B>(st.acc, v, cf, sel2);
       } else {
-        pv_pair<G, B>(st.acc, cur[k], cf, sel2);
+        pv_pair<GW, B>(st.acc, cur[k], cf, sel2);
       }
     }
     wave_lds_sync();
@@ -808,7 +812,7 @@ __device__ void run_group(const DecodeParams& p, const SegInfo& si, const Plan& 
   // The last steps copied (zero) blocks into ring stages that the partial
   // output below overwrites; those copies must land before it does.
   if (use_ring) wait_vmem<0>();
-  wave_finish<G, B, SW>(st, sm, wave, lane);
+  wave_finish<GW, B>(st, sm, wave, lane);
 }
 
 // ---------------------------------------------------------------- zone C (fp16 rows, natural order)
@@ -828,42 +832,44 @@ __device__ void run_zone_c(const DecodeParams& p, const SegInfo& si, int64_t seg
     return (p.append && r == p.c_len) ? vnew : vc + int64_t(r) * kHeadDim * 2;
   };
 
+  constexpr int GW = kHeadsPerWave<G>, kNS = kStreams<G>;
+  const int hb = kNS == kWaves ? 0 : (wave / kNS) * GW;           // the wave's first query head
   build_query_tables<G, SW>(p, si, pl, seg, sm);
   __syncthreads();
-  WaveState<G> st;
+  WaveState<GW> st;
   state_init(st);
-  for (int base = pl.start + kTile * wave; base < pl.end; base += kThreads) {
+  for (int base = pl.start + kTile * (wave % kNS); base < pl.end; base += kTile * kNS) {
     VPair<16> v[kPairsPerLane];
 #pragma unroll
     for (int k = 0; k < kPairsPerLane; ++k) v[k] = load_vpair16(vrow(base + ts + 4 * k), vrow(base + ts + 4 * k + 32), cb);
     const int r = min(base + lane, last);
     const uint4* k4 = reinterpret_cast<const uint4*>(krow(r));
-    float s[G];
+    float s[GW];
 #pragma unroll
-    for (int g = 0; g < G; ++g) s[g] = 0.f;
+    for (int g = 0; g < GW; ++g) s[g] = 0.f;
 #pragma unroll 4
     for (int c = 0; c < 16; ++c) {
       const uint4 x = k4[c];
       const uint32_t ws[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        uint32_t q[G];
-        load_qp<G, SW>(sm, 4 * c + j, q);
+        uint32_t q[GW];
+        load_qp<GW>(sm, 4 * c + j, hb, q);
 #pragma unroll
-        for (int g = 0; g < G; ++g) s[g] = dot2(ws[j], q[g], s[g]);
+        for (int g = 0; g < GW; ++g) s[g] = dot2(ws[j], q[g], s[g]);
       }
     }
-    softmax_tile<G, SW, true>(st, s, base + lane < pl.end, 1.f, 0.f, sm, wave, lane);
+    softmax_tile<GW, G, SW, true>(st, s, base + lane < pl.end, 1.f, 0.f, sm, wave, lane);
     wave_lds_sync();
 #pragma unroll
     for (int k = 0; k < kPairsPerLane; ++k) {
-      uint32_t cf[G];
-      load_coefs<G, SW>(sm, wave, ts + 4 * k, cf);
-      pv_pair<G, 16>(st.acc, v[k], cf, 0u);
+      uint32_t cf[GW];
+      load_coefs<GW>(sm, wave, ts + 4 * k, cf);
+      pv_pair<GW, 16>(st.acc, v[k], cf, 0u);
     }
     wave_lds_sync();
   }
-  wave_finish<G, 16, SW>(st, sm, wave, lane);
+  wave_finish<GW, 16>(st, sm, wave, lane);
 }
 
 // ---------------------------------------------------------------- kernels
@@ -908,7 +914,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParam
 }
 
 template <int G, int SW>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G >= 8 ? 2 : 3))) void decode_chunk_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void decode_chunk_kernel(DecodeParams p) {
   __shared__ Smem<G, SW> sm;
   // Chunk-major order: every segment's first chunk, then every second chunk,
   // ...  The full 2-bit chunks come first and the short tails, fp16 and zone-C
@@ -939,19 +945,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G >= 8
   }
   __syncthreads();
 
-  // merge the waves' partials into the chunk's partial
+  // merge the waves' partials into the chunk's partial: head g was carried
+  // by the kNS waves (g / GW) * kNS ... as their head g % GW
+  constexpr int GW = kHeadsPerWave<G>, kNS = kStreams<G>;
   float* out = p.partials + (int64_t(seg) * p.max_chunks + k) * G * kPartialFloats;
   for (int i = tid; i < G * kHeadDim; i += kThreads) {
     const int g = i / kHeadDim, c = i % kHeadDim;
+    const int w0 = (g / GW) * kNS, gl = g % GW;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.part_ml[w][g][0]);
+    for (int j = 0; j < kNS; ++j) M = fmaxf(M, sm.part_ml[w0 + j][gl][0]);
     float L = 0.f, O = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float f = exp2f(sm.part_ml[w][g][0] - M);
-      L = fmaf(sm.part_ml[w][g][1], f, L);
-      O = fmaf(sm.wv[w].o[g][c], f, O);
+    for (int j = 0; j < kNS; ++j) {
+      const float f = exp2f(sm.part_ml[w0 + j][gl][0] - M);
+      L = fmaf(sm.part_ml[w0 + j][gl][1], f, L);
+      O = fmaf(sm.wv[w0 + j].o[gl][c], f, O);
     }
     out[g * kPartialFloats + 4 + c] = O;
     if (c == 0) {
