@@ -21,9 +21,11 @@
 //     place into fp16 subnormals and met with the fp16 (p*scale) pair in
 //     v_dot2; the p*zero part is summed once per token.  2- and 4-bit rows
 //     are loaded one tile ahead.
-// The 4 waves' partials are merged in LDS into one (m, l, o[128]) per query
-// head and chunk; decode_merge_kernel combines each segment's chunks in chunk
-// order, so the result does not depend on scheduling.  Merging in a second
+// With 8 query heads per KV head, pairs of waves walk the same tiles for the
+// two halves of the heads.  The waves' partials are merged in LDS into one
+// (m, l, o[128]) per query head and chunk; decode_merge_kernel combines each
+// segment's chunks in chunk order, so the result does not depend on
+// scheduling.  Merging in a second
 // launch keeps the chunk kernel free of device-wide fences, which on a
 // multi-XCD part write back and invalidate the L2.  No MFMA: 1..8 query rows
 // per KV head make this a matrix-vector stream, bounded by HBM bandwidth and
@@ -876,39 +878,50 @@ __device__ void run_zone_c(const DecodeParams& p, const SegInfo& si, int64_t seg
 
 // out[seg][g][c] = sum_k e^{m_k - M} o_k[c] / sum_k e^{m_k - M} l_k over the
 // segment's chunks, in chunk order; a segment with nothing to attend to gives
-// 0.  One 128-thread workgroup per (segment, query head): thread c owns
-// channel c; chunk weights are computed once per tile of chunks in LDS.
+// 0.  One 128-thread workgroup per (segment, query head), thread c owning
+// channel c; per round of up to 128 chunk slots, thread k reads slot k's
+// (m, l) once and publishes its weight in LDS, then every thread sums its
+// channel over the slots.  Every slot up to max_chunks was written by the
+// chunk kernel; slots past the segment's last chunk hold (-inf, 0, 0...), so
+// the merge needs nothing from the blob.
 constexpr int kMergeThreads = kHeadDim;
 
 template <int G>
 __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParams p) {
-  __shared__ float s_f[kMergeThreads];
+  __shared__ float s_w[kMergeThreads], s_lw[kMergeThreads];
   __shared__ float s_red[kMergeThreads / 64];
   const int64_t seg = blockIdx.x / G;
   const int g = int(blockIdx.x % G);
   const int c = threadIdx.x;
-  const SegInfo si = load_segment(p, seg);
-  const int n = min(chunk_count(si.n_tok, si.zc_ok ? p.n_c : 0, p.chunk_tok2), p.max_chunks);
-  const float* part = p.partials + int64_t(seg) * p.max_chunks * G * kPartialFloats + g * kPartialFloats;
+  const int n = p.max_chunks;
+  const float* part = p.partials + int64_t(seg) * n * G * kPartialFloats + g * kPartialFloats;
   const int64_t stride = int64_t(G) * kPartialFloats;
-  float M = -INFINITY;
-  for (int k = c; k < n; k += kMergeThreads) M = fmaxf(M, part[k * stride]);
-  M = wave_reduce<true>(M);
-  if ((c & 63) == 0) s_red[c >> 6] = M;
-  __syncthreads();
-  M = fmaxf(s_red[0], s_red[1]);
-  float L = 0.f, O = 0.f;
+  float M = -INFINITY, L = 0.f, O = 0.f;
   for (int k0 = 0; k0 < n; k0 += kMergeThreads) {
-    __syncthreads();
-    if (k0 + c < n) s_f[c] = exp2f(part[(k0 + c) * stride] - M);
-    __syncthreads();
     const int kn = min(kMergeThreads, n - k0);
+    const float* pr = part + k0 * stride;
+    const float mc = c < kn ? pr[c * stride] : -INFINITY;
+    const float lc = c < kn ? pr[c * stride + 1] : 0.f;
+    const float wm = wave_reduce<true>(mc);
+    if ((c & 63) == 0) s_red[c >> 6] = wm;
+    __syncthreads();
+    const float mb = fmaxf(M, fmaxf(s_red[0], s_red[1]));
+    const float w = mc == -INFINITY ? 0.f : exp2f(mc - mb);
+    s_w[c] = w;
+    s_lw[c] = lc * w;
+    __syncthreads();
+    if (mb != -INFINITY) {
+      const float a = exp2f(M - mb);   // (0 while nothing was merged)
+      L *= a;
+      O *= a;
 #pragma unroll 8
-    for (int j = 0; j < kn; ++j) {
-      const float* pk = part + (k0 + j) * stride;
-      L = fmaf(pk[1], s_f[j], L);
-      O = fmaf(pk[4 + c], s_f[j], O);
+      for (int j = 0; j < kn; ++j) {
+        L += s_lw[j];
+        O = fmaf(pr[j * stride + 4 + c], s_w[j], O);
+      }
+      M = mb;
     }
+    __syncthreads();
   }
   p.out[(seg * G + g) * kHeadDim + c] = L > 0.f ? O / L : 0.f;
 }
@@ -926,7 +939,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   const SegInfo si = load_segment(p, seg);
   const Plan pl = plan_chunk(si, si.zc_ok ? p.n_c : 0, p.chunk_tok2, k);
   const int tid = threadIdx.x;
-  if (pl.kind < 0) return;
+  float* out = p.partials + (int64_t(seg) * p.max_chunks + k) * G * kPartialFloats;
+  if (pl.kind < 0) {   // a slot past the segment's last chunk: (m, l, o) = (-inf, 0, 0)
+    for (int i = tid; i < G * kPartialFloats; i += kThreads) out[i] = i % kPartialFloats == 0 ? -INFINITY : 0.f;
+    return;
+  }
 
   // append the new token to zone C (only the chunk holding row c_len does it)
   if (pl.kind == 4 && p.append && p.c_len >= pl.start && p.c_len < pl.end) {
@@ -948,7 +965,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   // merge the waves' partials into the chunk's partial: head g was carried
   // by the kNS waves (g / GW) * kNS ... as their head g % GW
   constexpr int GW = kHeadsPerWave<G>, kNS = kStreams<G>;
-  float* out = p.partials + (int64_t(seg) * p.max_chunks + k) * G * kPartialFloats;
   for (int i = tid; i < G * kHeadDim; i += kThreads) {
     const int g = i / kHeadDim, c = i % kHeadDim;
     const int w0 = (g / GW) * kNS, gl = g % GW;

@@ -75,13 +75,6 @@ __host__ __device__ inline int bits_group(int b) {
   return b == 2 ? 0 : b == 4 ? 1 : b == 8 ? 2 : b == 16 ? 3 : -1;
 }
 
-// Chunks of a segment: each token group in order 2, 4, 8, 16 bits, then zone C.
-__host__ __device__ inline int chunk_count(const int n_tok[4], int n_c, int chunk_tok2) {
-  int n = 0;
-  for (int g = 0; g < 4; ++g) n += (n_tok[g] + chunk_tokens(chunk_tok2, g) - 1) / chunk_tokens(chunk_tok2, g);
-  return n + (n_c + kChunkRowsC - 1) / kChunkRowsC;
-}
-
 // ------------------------------------------------------------ device helpers
 
 __device__ inline float half_lo(uint32_t w) { return __half2float(__ushort_as_half((unsigned short)(w & 0xffffu))); }

@@ -178,9 +178,11 @@ rdkv_status rdkv_decode(const rdkv_layout* layout, void* cache, size_t cache_byt
  * (running max m, sum l, unnormalised o[128] per query head and chunk) into
  * `workspace`; arguments as rdkv_decode.
  * rdkv_decode_merge: out = sum_k e^{m_k-M} o_k / sum_k e^{m_k-M} l_k over each
- * segment's chunks, in chunk order.  zone_c_rows is the number of zone-C rows
- * the partials phase attended (its c_len, plus 1 if it appended), which fixes
- * the segment's chunk count; 0 <= zone_c_rows <= zone_c_capacity. */
+ * segment's chunks, in chunk order.  The partials phase writes every chunk
+ * slot of the workspace (slots past a segment's last chunk are marked empty),
+ * so the merge needs nothing else from the blob.  zone_c_rows is the number of
+ * zone-C rows the partials phase attended (its c_len, plus 1 if it appended);
+ * it is checked, 0 <= zone_c_rows <= zone_c_capacity, else RDKV_ERR_CAPACITY. */
 rdkv_status rdkv_decode_partials(const rdkv_layout* layout, void* cache, size_t cache_bytes, int32_t c_len,
                                  const void* q, const void* k_new, const void* v_new,
                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
