@@ -40,11 +40,17 @@ constexpr int kDescPerm = 128;    // u8[128]
 // chunk_tok2 is a power of two in [kChunkTok2Min, kChunkTok2Max], chosen per
 // layout so that one launch has about kDecodeTargetChunks chunks.
 #ifndef RDKV_DECODE_TARGET_CHUNKS
-#define RDKV_DECODE_TARGET_CHUNKS 1024
+#define RDKV_DECODE_TARGET_CHUNKS 512
 #endif
 constexpr int64_t kDecodeTargetChunks = RDKV_DECODE_TARGET_CHUNKS;
-constexpr int kChunkTok2Min = 512;
-constexpr int kChunkTok2Max = 16384;
+#ifndef RDKV_CHUNK_TOK2_MIN
+#define RDKV_CHUNK_TOK2_MIN 512
+#endif
+constexpr int kChunkTok2Min = RDKV_CHUNK_TOK2_MIN;
+#ifndef RDKV_CHUNK_TOK2_MAX
+#define RDKV_CHUNK_TOK2_MAX 16384
+#endif
+constexpr int kChunkTok2Max = RDKV_CHUNK_TOK2_MAX;
 __host__ __device__ constexpr int chunk_tokens(int chunk_tok2, int group) { return chunk_tok2 >> group; }
 constexpr int kChunkRowsC = 256;
 // Floats per (chunk, query head) partial: m, l, 2 pad, o[128].
