@@ -380,3 +380,23 @@ def test_decode_captured_in_a_graph_replays_like_eager(gpu_lib):
         assert torch.equal(out, eager), f"replay {i} differs from the eager call"
     # the appended zone-C row is the same bytes the oracle wrote
     assert np.array_equal(host(cache), oblob)
+
+
+def test_decode_merge_ignores_stale_workspace(gpu_lib):
+    """The partials phase writes every chunk slot of the workspace (slots past
+    a segment's last chunk as empty), so whatever the workspace held before
+    (here NaN everywhere) cannot leak into the merged output."""
+    rdkv = gpu_lib
+    lay, ol, oblob, (K, V, bt, bc) = _pack_case(("empty_and_single", 1, 2, 8, 2, 300, 4))
+    cache = rdkv.cache_init(lay)
+    rdkv.pack(lay, cache, dev(K), dev(V), dev(bt), dev(bc))
+    r = np.random.default_rng(4)
+    q = r.standard_normal((1, 2, 8, 128)).astype(np.float16)
+    ws = rdkv.decode_workspace(lay)
+    clean = rdkv.decode(lay, cache.clone(), 1, dev(q), workspace=ws.zero_())
+    ws.view(torch.float32).fill_(float("nan"))
+    dirty = rdkv.decode(lay, cache, 1, dev(q), workspace=ws)
+    assert torch.equal(clean, dirty)
+    assert not torch.isnan(dirty).any()
+    ref = O.decode_step(oblob, ol, q, 1)
+    assert rel_err_rows(host(dirty), ref) <= TOL
