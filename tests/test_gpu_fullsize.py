@@ -22,6 +22,10 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 TOL = 2e-3
 
+
+def host(t):
+    return t.detach().cpu().numpy()
+
 # workload -> (token bit mix over 0/2/4/8/16, channel bit mix)
 MIXES = {
     "llama8b-32layer-n128k": ((0.83, 0.16, 0.062, 0.008, 0.00005), (0.71, 0.28, 0.0, 0.008, 0.0)),
@@ -173,3 +177,39 @@ def test_score_weights_sum_to_query_rows_on_a_128k_layer(gpu_lib):
     print(f"sum of w_t per KV head / (G N): {sums / (G * w.n_tokens)}")
     assert np.all(np.abs(sums - G * w.n_tokens) <= TOL * G * w.n_tokens)
     assert bool((wt > 0).all()) and bool((vt > 0).all()) and bool((wc > 0).all())
+
+
+# ------------------------------------------------------------------ allocation at full context length
+
+@pytest.mark.parametrize("name,seq,layer,heads", [
+    ("llama8b-layer-n32k", 0, 0, range(8)),
+    ("llama8b-batch16-n32k", 5, 0, range(8)),
+    ("llama8b-32layer-n128k", 0, 7, (0, 3, 7)),
+    ("qwen72b-80layer-n256k", 0, 40, (0, 5)),
+])
+def test_full_size_allocation_bit_exact_on_scored_weights(gpu_lib, name, seq, layer, heads):
+    """One layer of each workload at its full context: scored on the GPU, then
+    allocated on the GPU and by the oracle from the same fp32 weights and
+    variances (the allocation is a deterministic function of them).  Bits,
+    lambdas and the kept-token channel variances agree bit for bit."""
+    rdkv = gpu_lib
+    w = synth.WORKLOADS[name]
+    Hq, Hkv, N = w.n_q_heads, w.n_kv_heads, w.n_tokens
+    Q, K, V = synth.prefill_layer(w, seq, layer, device=DEV)
+    dims = rdkv.make_dims(1, 1, Hq, Hkv, N)
+    K5 = K[None, None].contiguous()
+    wt, vt, wc = rdkv.score(dims, Q[None, None].contiguous(), K5, V[None, None].contiguous())
+    del Q, V
+    bt, bc, vc, lam = rdkv.allocate(dims, wt, vt, wc, K5, w.budget_v, w.budget_k)
+    wt, vt, wc = host(wt)[0, 0], host(vt)[0, 0], host(wc)[0, 0]
+    bt, bc, vc, lam = host(bt)[0, 0], host(bc)[0, 0], host(vc)[0, 0], host(lam)[0, 0]
+    for h in heads:
+        ref = O.allocate_segment(wt[h], vt[h], wc[h], host(K[h]), w.budget_v, w.budget_k)
+        hist = np.bincount(bt[h], minlength=17)[[0, 2, 4, 8, 16]]
+        print(f"{name} layer {layer} head {h}: token bits 0/2/4/8/16 {hist.tolist()}, "
+              f"channels {np.bincount(bc[h], minlength=17)[[0, 2, 4, 8, 16]].tolist()}", flush=True)
+        assert np.array_equal(bt[h], ref["bits_tok"]), f"head {h}: V bits differ"
+        assert lam[h, 0] == ref["lambda_v"]
+        assert np.array_equal(vc[h].view(np.uint32), ref["var_chan"].view(np.uint32)), f"head {h}: var_chan"
+        assert np.array_equal(bc[h], ref["bits_chan"]), f"head {h}: K bits differ"
+        assert lam[h, 1] == ref["lambda_k"]
