@@ -9,19 +9,21 @@
 //   score_lse_kernel     workgroup = 128 query rows of one query head; walks
 //                        the key tiles up to its last row, keeps a per-lane
 //                        online (max, sum), then merges across lanes.
-//   score_colsum_kernel  workgroup = 128 keys of one KV head; walks the G
-//                        query heads and every query tile at or after the
-//                        keys, summing exp2(s' - LSE') down each key column.
-//                        A key block is owned by one workgroup, so no atomics
+//   score_colsum_kernel  workgroup = 128 keys of one KV head; walks every
+//                        query tile at or after the keys (last tile first,
+//                        the G query heads innermost, so the workgroups of a
+//                        KV head read the same tiles at the same time),
+//                        summing exp2(s' - LSE') down each key column.  A
+//                        key block is owned by one workgroup, so no atomics
 //                        and the summation order is fixed.
 // Each wave keeps 32 rows of its resident operand (Q rows, or K rows) in
 // registers as two 16-row MFMA fragments, so every fragment of the streamed
-// 64-row tile it reads from LDS feeds two products.  The streamed tile is
-// double buffered in LDS: the next tile's global loads are in flight while the
-// current one is multiplied.  Masks are applied only on diagonal and ragged
-// tiles; tiles entirely outside a wave's triangle are skipped by that wave.
-// Plus two bandwidth kernels: var_tok (one wave per token) and the column
-// norms behind w_chan (partial sums in fp64, reduced in a fixed order).
+// 64-row tile it reads from LDS feeds two products.  The streamed tiles go
+// straight from memory into a three-stage LDS ring (no registers), two tiles
+// ahead of the one being multiplied.  Masks are applied only on diagonal and
+// ragged tiles; tiles entirely outside a wave's triangle are skipped by that
+// wave.  Plus two bandwidth kernels: var_tok (one wave per token) and the
+// column norms behind w_chan (partial sums in fp64, reduced in a fixed order).
 #include "rdkv_internal.h"
 
 namespace rdkv {
@@ -32,10 +34,10 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 constexpr int kKT = 64;                     // rows of the streamed LDS tile (keys, or query rows)
 constexpr int kWaveRows = 32;               // rows of the resident operand per wave (two 16-row fragments)
 constexpr int kBlockRows = 4 * kWaveRows;   // per workgroup
-constexpr int kPad = kHeadDim + 8;  // LDS row stride in halves (272 bytes)
 constexpr int kThreads = 256;
 constexpr float kLog2eOverSqrtD = 1.4426950408889634f / 11.313708498984761f;
 constexpr int kNormSplits = 64;
+constexpr int kRunTiles = 8;   // pass-2 tiles summed in fp32 before moving into fp64 (<= 32 terms of at most 1)
 
 struct ScoreArgs {
   int64_t N;
@@ -48,24 +50,97 @@ struct ScoreArgs {
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 
-// A 64 x 128 fp16 tile moving global -> registers -> LDS: each thread holds
-// 4 of its 1024 16-byte pieces; rows >= N are 0.
-struct TileRegs {
-  uint4 v[4];
-};
-__device__ inline void tile_fetch(TileRegs& t, const __half* src, int64_t row0, int64_t N) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int idx = threadIdx.x + kThreads * i, r = idx >> 4, c = idx & 15;
-    t.v[i] = row0 + r < N ? reinterpret_cast<const uint4*>(src + (row0 + r) * kHeadDim)[c] : make_uint4(0, 0, 0, 0);
-  }
+// ---------------------------------------------------------------- LDS tiles
+// A streamed tile is 64 rows x 128 halves (16 KiB) in LDS without padding;
+// the 16-byte piece c of row r sits at piece c ^ (r % 16) of its row, so the
+// 16 rows one fragment read touches fall in 16 distinct bank groups.  Tiles
+// are copied global -> LDS by buffer_load_dwordx4 ... lds (no registers), in
+// a ring of kStages tiles issued kStages - 1 tiles ahead: each wave copies
+// 16 rows with 4 instructions.  The copies are inline assembly, so the
+// compiler's memory-counter bookkeeping does not see them; the loops wait for
+// them explicitly.
+constexpr int kStages = 3;
+constexpr int kTileBytes = kKT * kHeadDim * 2;
+constexpr int kBufferFlags = 0x00020000;   // raw buffer: range-checked, out-of-range reads return 0
+
+__device__ inline uint32_t lds_addr(const void* p) {
+  return uint32_t(size_t((const __attribute__((address_space(3))) void*)p));
 }
-__device__ inline void tile_store(const TileRegs& t, _Float16 (*tile)[kPad]) {
+
+typedef int rsrc4 __attribute__((ext_vector_type(4)));
+__device__ inline rsrc4 buffer_rsrc4(const void* p, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  rsrc4 r;
+  r.x = __builtin_amdgcn_readfirstlane(int(uint32_t(a)));
+  r.y = __builtin_amdgcn_readfirstlane(int(uint32_t(a >> 32) & 0xffff));   // stride 0
+  r.z = __builtin_amdgcn_readfirstlane(int(bytes));
+  r.w = kBufferFlags;
+  return r;
+}
+
+// Per-lane range offsets of a wave's 4 copies: copy j fills LDS bytes
+// 1024 j + 16 lane of the wave's quarter, i.e. row 4 j + lane / 16, piece
+// p = lane % 16, which holds the row's piece p ^ (row % 16).  The instruction
+// offset (1024 j) moves the range offset too, so it is taken out here.
+struct CopyOffsets {
+  uint32_t v[4];
+};
+__device__ inline CopyOffsets copy_offsets() {
+  const int lane = threadIdx.x & 63;
+  CopyOffsets o;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int idx = threadIdx.x + kThreads * i, r = idx >> 4, c = idx & 15;
-    *reinterpret_cast<uint4*>(&tile[r][c * 8]) = t.v[i];
+  for (int j = 0; j < 4; ++j) {
+    const int r = 4 * j + (lane >> 4), c = (lane & 15) ^ (r & 15);
+    o.v[j] = uint32_t(256 * (lane >> 4) + 16 * c);
   }
+  return o;
+}
+
+// The wave's 16 rows (row0 .. row0 + 15 of src, each 256 bytes) into LDS at
+// byte lds; rows at or past N arrive as zeros without being read.
+__device__ inline void copy_rows16(const __half* src, int64_t row0, int64_t N, const CopyOffsets& o, uint32_t lds) {
+  const int64_t left = N - row0;
+  const uint32_t bytes = left <= 0 ? 0u : left >= 16 ? 4096u : uint32_t(left) * 256u;
+  const rsrc4 r = buffer_rsrc4(src + row0 * kHeadDim, bytes);
+  lds = __builtin_amdgcn_readfirstlane(lds);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %6\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %5, 0 offen offset:0 lds\n\t"
+      "buffer_load_dwordx4 %2, %5, 0 offen offset:1024 lds\n\t"
+      "buffer_load_dwordx4 %3, %5, 0 offen offset:2048 lds\n\t"
+      "buffer_load_dwordx4 %4, %5, 0 offen offset:3072 lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(o.v[0]), "v"(o.v[1]), "v"(o.v[2]), "v"(o.v[3]), "s"(r), "s"(lds)
+      : "memory");
+}
+
+// 64 fp32 values (src[row0 .. row0 + 63], zeros at or past N) into LDS at
+// byte lds, one dword per lane.
+__device__ inline void copy_floats64(const float* src, int64_t row0, int64_t N, uint32_t lds) {
+  const int64_t left = N - row0;
+  const uint32_t bytes = left <= 0 ? 0u : left >= 64 ? 256u : uint32_t(left) * 4u;
+  const rsrc4 r = buffer_rsrc4(src + row0, bytes);
+  const uint32_t voff = 4u * (threadIdx.x & 63);
+  lds = __builtin_amdgcn_readfirstlane(lds);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
+      "buffer_load_dword %1, %2, 0 offen offset:0 lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(r), "s"(lds)
+      : "memory");
+}
+
+// Waits until at most N vector-memory instructions of this wave are in
+// flight (they complete in issue order).
+template <int N>
+__device__ inline void wait_vmem() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // A-operand fragments of 16 rows for the 16x16x32 MFMA: lane holds row
@@ -81,12 +156,12 @@ __device__ inline void load_rows_frag(h8 (&a)[4], const __half* src, int64_t row
 }
 
 // B-operand fragments of rows 16*sub .. 16*sub + 15 of an LDS tile, in the
-// same k order as the A fragments.
-__device__ inline void load_tile_frag(h8 (&b)[4], const _Float16 (*tile)[kPad], int sub) {
+// same k order as the A fragments (piece 4 kk + lane / 16 of the row).
+__device__ inline void load_tile_frag(h8 (&b)[4], const _Float16 (*tile)[kHeadDim], int sub) {
   const int lane = threadIdx.x & 63;
-  const _Float16* trow = &tile[16 * sub + (lane & 15)][8 * (lane >> 4)];
+  const _Float16* trow = &tile[16 * sub + (lane & 15)][0];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) b[kk] = *reinterpret_cast<const h8*>(trow + 32 * kk);
+  for (int kk = 0; kk < 4; ++kk) b[kk] = *reinterpret_cast<const h8*>(trow + 8 * (((lane >> 4) + 4 * kk) ^ (lane & 15)));
 }
 
 // C[i][j] = sum_k A[i][k] * B[j][k] over k = 0..127 for 16 rows of A and 16 of
@@ -107,15 +182,18 @@ __device__ inline float max3f(float a, float b, float c) {
 
 // One key tile of pass 1 for a wave's 32 rows: scores c by MFMA, then per
 // row the running sum s = sum exp2(c * k - mk) (k = log2(e) / sqrt(d)) over a
-// reference mk = m * k.  The reference m is the row's maximum score when it was
-// last raised; it is raised (and s rescaled) only when a score exceeds it by
-// more than kSlack / k, so the terms stay below 2^kSlack and, after the first
-// tiles, most tiles rescale nothing.  kEdge: keys after a row, or at or past
-// N, are masked.
-constexpr float kSlack = 8.0f;   // base-2 headroom of a term above the reference
+// reference mk, a maximum of the row's scores (times k) seen so far.  The
+// reference is raised only when a tile's terms for some row sum past 2^64,
+// which after the first tile needs a score 64 base-2 units above it: the tile
+// is then redone over the raised reference (the branch is wave-uniform and
+// rare).  Terms below the reference's own scale lose nothing that matters, and
+// s stays far below the fp32 range.  mk starts at -FLT_MAX, not -inf, so a
+// visible score always overflows the first tile's sum and masked scores (-inf)
+// give exact zeros.  kEdge: keys after a row, or at or past N, are masked.
+constexpr float kRaiseBound = 18446744073709551616.0f;   // 2^64
 template <bool kEdge>
-__device__ inline void lse_tile(const h8 (&qa)[2][4], const _Float16 (*cur)[kPad], int key0, int wrow0, int N,
-                                float (&thr)[2][4], float (&mk)[2][4], float (&s)[2][4]) {
+__device__ inline void lse_tile(const h8 (&qa)[2][4], const _Float16 (*cur)[kHeadDim], int key0, int wrow0, int N,
+                                float (&mk)[2][4], float (&s)[2][4]) {
   const int lane = threadIdx.x & 63;
   float c[2][4][4];   // [fragment][sub][r]
 #pragma unroll
@@ -141,39 +219,37 @@ __device__ inline void lse_tile(const h8 (&qa)[2][4], const _Float16 (*cur)[kPad
           if (key > row || key >= N) c[f][sub][r] = -INFINITY;
         }
   }
-  float cm[2][4];
-  bool up = false;
+  float t[2][4];
+  bool big = false;
 #pragma unroll
   for (int f = 0; f < 2; ++f)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      cm[f][r] = fmaxf(max3f(c[f][0][r], c[f][1][r], c[f][2][r]), c[f][3][r]);
-      up = up || cm[f][r] > thr[f][r];
+      float e[4];
+#pragma unroll
+      for (int sub = 0; sub < 4; ++sub) e[sub] = __builtin_amdgcn_exp2f(fmaf(c[f][sub][r], kLog2eOverSqrtD, -mk[f][r]));
+      t[f][r] = (e[0] + e[1]) + (e[2] + e[3]);
+      big = big || !(t[f][r] <= kRaiseBound);
     }
-  if (__builtin_amdgcn_ballot_w64(up) != 0) {   // (wave-uniform; rare after the first tiles)
+  if (__builtin_amdgcn_ballot_w64(big) != 0) {
 #pragma unroll
     for (int f = 0; f < 2; ++f)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (cm[f][r] > thr[f][r]) {
-          const float mnew = cm[f][r] * kLog2eOverSqrtD;
-          s[f][r] *= __builtin_amdgcn_exp2f(mk[f][r] - mnew);   // (0 while nothing was seen)
-          mk[f][r] = mnew;
-          thr[f][r] = cm[f][r] + kSlack / kLog2eOverSqrtD;
-        }
+      for (int r = 0; r < 4; ++r) {
+        const float cm = fmaxf(fmaxf(c[f][0][r], c[f][1][r]), fmaxf(c[f][2][r], c[f][3][r]));
+        const float mnew = fmaxf(mk[f][r], cm * kLog2eOverSqrtD);
+        s[f][r] *= __builtin_amdgcn_exp2f(mk[f][r] - mnew);
+        mk[f][r] = mnew;
+        float e[4];
+#pragma unroll
+        for (int sub = 0; sub < 4; ++sub) e[sub] = __builtin_amdgcn_exp2f(fmaf(c[f][sub][r], kLog2eOverSqrtD, -mnew));
+        t[f][r] = (e[0] + e[1]) + (e[2] + e[3]);
+      }
   }
 #pragma unroll
   for (int f = 0; f < 2; ++f)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if constexpr (kEdge) {
-        if (mk[f][r] == -INFINITY) continue;   // nothing visible to this row yet
-      }
-      float acc = s[f][r];
-#pragma unroll
-      for (int sub = 0; sub < 4; ++sub) acc += __builtin_amdgcn_exp2f(fmaf(c[f][sub][r], kLog2eOverSqrtD, -mk[f][r]));
-      s[f][r] = acc;
-    }
+    for (int r = 0; r < 4; ++r) s[f][r] += t[f][r];
 }
 
 // Pass 1: workgroup = 128 query rows of one query head (32 per wave, two
@@ -181,7 +257,7 @@ __device__ inline void lse_tile(const h8 (&qa)[2][4], const _Float16 (*cur)[kPad
 // tiles up to the block's last row.  Per lane and row an online (max, sum),
 // merged across the 16 lanes of a row at the end in base 2.
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void score_lse_kernel(ScoreArgs a) {
-  __shared__ _Float16 ks[2][kKT][kPad];
+  __shared__ _Float16 ks[kStages][kKT][kHeadDim];
   const int64_t N = a.N;
   const int nqb = int(cdiv(N, kBlockRows));
   const int qb = nqb - 1 - int(blockIdx.x);   // long rows first
@@ -197,33 +273,37 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   h8 qa[2][4];
   load_rows_frag(qa[0], Qh, wrow0 + (lane & 15), N);
   load_rows_frag(qa[1], Qh, wrow0 + 16 + (lane & 15), N);
-  float thr[2][4], mk[2][4], s[2][4];   // raise threshold (raw units), reference (base 2), sum
+  float mk[2][4], s[2][4];   // reference (base 2), sum
 #pragma unroll
   for (int f = 0; f < 2; ++f)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      thr[f][r] = -INFINITY;
-      mk[f][r] = -INFINITY;
+      mk[f][r] = -__FLT_MAX__;
       s[f][r] = 0.f;
     }
-  TileRegs nxt;
-  tile_fetch(nxt, Kh, 0, N);
-  tile_store(nxt, ks[0]);
+  const CopyOffsets co = copy_offsets();
+  const uint32_t lds0 = lds_addr(&ks[0][0][0]) + uint32_t(kTileBytes / 4) * wave;
+  auto issue = [&](int kt) {
+    copy_rows16(Kh, int64_t(kt) * kKT + 16 * wave, N, co, lds0 + uint32_t(kTileBytes) * (kt % kStages));
+  };
+  issue(0);
+  if (n_kt > 1) issue(1);
   for (int kt = 0; kt < n_kt; ++kt) {
-    if (kt + 1 < n_kt) tile_fetch(nxt, Kh, int64_t(kt + 1) * kKT, N);
-    __syncthreads();
+    if (kt + 1 < n_kt) wait_vmem<4>();   // this wave's copies of tile kt have landed
+    else wait_vmem<0>();
+    __syncthreads();                     // ... and every wave's; tile kt - 1 is no longer read
+    if (kt + 2 < n_kt) issue(kt + 2);
     const int64_t key0 = int64_t(kt) * kKT;
     // (wave-uniform) skip a tile whose keys all lie after the wave's rows
     if (key0 <= wrow0 + kWaveRows - 1 && wrow0 < N) {
-      const _Float16 (*cur)[kPad] = ks[kt & 1];
+      const _Float16 (*cur)[kHeadDim] = ks[kt % kStages];
       // diagonal or ragged tile: masks; otherwise every key precedes every row
       if (key0 + kKT - 1 > wrow0 || key0 + kKT > N) {
-        lse_tile<true>(qa, cur, int(key0), int(wrow0), int(N), thr, mk, s);
+        lse_tile<true>(qa, cur, int(key0), int(wrow0), int(N), mk, s);
       } else {
-        lse_tile<false>(qa, cur, int(key0), int(wrow0), int(N), thr, mk, s);
+        lse_tile<false>(qa, cur, int(key0), int(wrow0), int(N), mk, s);
       }
     }
-    if (kt + 1 < n_kt) tile_store(nxt, ks[(kt + 1) & 1]);
   }
   // merge the 16 lanes that hold the same rows
 #pragma unroll
@@ -234,11 +314,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
 #pragma unroll
       for (int x = 1; x < 16; x <<= 1) {
         const float mo = __shfl_xor(mm, x, 64), so = __shfl_xor(ss, x, 64);
-        const float mn = fmaxf(mm, mo);
-        if (mn != -INFINITY) {
-          ss = (mm == -INFINITY ? 0.f : ss * exp2f(mm - mn)) + (mo == -INFINITY ? 0.f : so * exp2f(mo - mn));
-          mm = mn;
-        }
+        const float mn = fmaxf(mm, mo);   // (references are finite)
+        ss = ss * exp2f(mm - mn) + so * exp2f(mo - mn);
+        mm = mn;
       }
       const int64_t row = wrow0 + 16 * f + 4 * (lane >> 4) + r;
       if ((lane & 15) == 0 && row < N) a.lse[(sl * a.Hq + hq) * N + row] = mm + log2f(ss);
@@ -246,38 +324,38 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
 }
 
 // One query tile of pass 2 for a wave's 32 keys: scores by MFMA and
-// exp2(t - LSE) summed per key, added to the fp64 totals.  kEdge: queries
-// before a key, or at or past N, are masked.
+// exp2(t - LSE) summed per key into fp32 run sums (each term is at most 1; the
+// caller moves them into fp64 totals every few tiles).  kEdge: queries before
+// a key, or at or past N, are masked.
 template <bool kEdge>
-__device__ inline void colsum_tile(const h8 (&ka)[2][4], const _Float16 (*cur)[kPad], const float* lse, int qrow0,
-                                   int wkey0, int N, double (&tot)[2][4]) {
+__device__ inline void colsum_tile(const h8 (&ka)[2][4], const _Float16 (*cur)[kHeadDim], const float* lse, int qrow0,
+                                   int wkey0, int N, float (&run)[2][4]) {
   const int lane = threadIdx.x & 63;
-  float part[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  f4 c[4][2];   // [sub][fragment]: every product of the tile first, then the exponentials
 #pragma unroll
   for (int sub = 0; sub < 4; ++sub) {
     h8 b[4];
     load_tile_frag(b, cur, sub);
+#pragma unroll
+    for (int f = 0; f < 2; ++f) c[sub][f] = mfma_16x16x128(ka[f], b);
+  }
+#pragma unroll
+  for (int sub = 0; sub < 4; ++sub) {
     const int query = qrow0 + 16 * sub + (lane & 15);
     const float lq = lse[16 * sub + (lane & 15)];
 #pragma unroll
-    for (int f = 0; f < 2; ++f) {
-      const f4 c = mfma_16x16x128(ka[f], b);
+    for (int f = 0; f < 2; ++f)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float e = __builtin_amdgcn_exp2f(fmaf(c[r], kLog2eOverSqrtD, -lq));
+        const float e = __builtin_amdgcn_exp2f(fmaf(c[sub][f][r], kLog2eOverSqrtD, -lq));
         if constexpr (kEdge) {
           const int key = wkey0 + 16 * f + 4 * (lane >> 4) + r;
-          part[f][r] += (query < key || query >= N) ? 0.f : e;
+          run[f][r] += (query < key || query >= N) ? 0.f : e;
         } else {
-          part[f][r] += e;
+          run[f][r] += e;
         }
       }
-    }
   }
-#pragma unroll
-  for (int f = 0; f < 2; ++f)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) tot[f][r] += double(part[f][r]);
 }
 
 // Pass 2: workgroup = 128 keys of one KV head (32 per wave, two 16-key
@@ -286,8 +364,8 @@ __device__ inline void colsum_tile(const h8 (&ka)[2][4], const _Float16 (*cur)[k
 // exp2(t - LSE) down each key column.  A key block is owned by one
 // workgroup, so no atomics and the summation order is fixed.
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void score_colsum_kernel(ScoreArgs a) {
-  __shared__ _Float16 qs[2][kKT][kPad];
-  __shared__ float ls[2][kKT];
+  __shared__ _Float16 qs[kStages][kKT][kHeadDim];
+  __shared__ float ls[kStages][kKT];
   const int64_t N = a.N;
   const int nqt = int(cdiv(N, kKT));
   const int kb = blockIdx.x;                  // short key indices have the most rows: first
@@ -301,51 +379,70 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   load_rows_frag(ka[0], Kh, wkey0 + (lane & 15), N);
   load_rows_frag(ka[1], Kh, wkey0 + 16 + (lane & 15), N);
   double tot[2][4] = {{0.0, 0.0, 0.0, 0.0}, {0.0, 0.0, 0.0, 0.0}};
-  // steps: (g, qt) for g in heads, qt in [qt0, nqt)
-  const int qt0 = int(int64_t(kb) * kBlockRows / kKT);
-  const int per = nqt - qt0, n_steps = a.G * per;
-  auto step_src = [&](int st, const __half*& Qh, const float*& lse, int& qt) {
-    const int g = st / per;
-    qt = qt0 + st % per;
-    const int hq = h * a.G + g;
-    Qh = a.Q + ((sl * a.Hq + hq) * N) * kHeadDim;
-    lse = a.lse + (sl * a.Hq + hq) * N;
+  float run[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  int n_run = 0;   // tiles summed into run since the last move into tot
+  auto flush = [&]() {
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        tot[f][r] += double(run[f][r]);
+        run[f][r] = 0.f;
+      }
+    n_run = 0;
   };
-  TileRegs nxt;
-  float lnext = 0.f;
-  auto fetch = [&](int st) {
-    const __half* Qh;
-    const float* lse;
-    int qt;
-    step_src(st, Qh, lse, qt);
-    tile_fetch(nxt, Qh, int64_t(qt) * kKT, N);
-    if (threadIdx.x < kKT) {
-      const int64_t row = int64_t(qt) * kKT + threadIdx.x;
-      lnext = row < N ? lse[row] : 0.f;
+  const int qt0 = int(int64_t(kb) * kBlockRows / kKT);
+  const int n_steps = a.G * (nqt - qt0);
+  // steps walk the query tiles from the last one back to qt0, the G heads
+  // innermost, so the workgroups of one KV head read the same tiles together
+  int f_g = 0, f_qt = nqt - 1;   // the next tile to copy
+  const CopyOffsets co = copy_offsets();
+  const uint32_t q_lds0 = lds_addr(&qs[0][0][0]) + uint32_t(kTileBytes / 4) * wave;
+  const uint32_t l_lds0 = lds_addr(&ls[0][0]);
+  // copies of step f into stage f % kStages: 4 per wave, plus the 64 LSE
+  // values by wave 0
+  auto issue = [&](int f) {
+    const int64_t hq = int64_t(h) * a.G + f_g;
+    const __half* Qh = a.Q + ((sl * a.Hq + hq) * N) * kHeadDim;
+    const int64_t row0 = int64_t(f_qt) * kKT;
+    copy_rows16(Qh, row0 + 16 * wave, N, co, q_lds0 + uint32_t(kTileBytes) * (f % kStages));
+    if (wave == 0) copy_floats64(a.lse + (sl * a.Hq + hq) * N, row0, N, l_lds0 + uint32_t(kKT * 4) * (f % kStages));
+    if (++f_g == a.G) {
+      f_g = 0;
+      --f_qt;
     }
   };
-  auto store = [&](int buf) {
-    tile_store(nxt, qs[buf]);
-    if (threadIdx.x < kKT) ls[buf][threadIdx.x] = lnext;
-  };
-  fetch(0);
-  store(0);
+  issue(0);
+  if (n_steps > 1) issue(1);
+  int qt = nqt - 1, g_cur = 0;   // the current tile
   for (int st = 0; st < n_steps; ++st) {
-    if (st + 1 < n_steps) fetch(st + 1);
-    __syncthreads();
-    const int buf = st & 1;
-    const int64_t qrow0 = int64_t(qt0 + st % per) * kKT;
+    // this wave's copies of step st have landed (wave 0 issues 5 per step)
+    if (st + 1 < n_steps) {
+      if (wave == 0) wait_vmem<5>();
+      else wait_vmem<4>();
+    } else {
+      wait_vmem<0>();
+    }
+    __syncthreads();   // ... and every wave's; step st - 1 is no longer read
+    if (st + 2 < n_steps) issue(st + 2);
+    const int buf = st % kStages;
+    const int64_t qrow0 = int64_t(qt) * kKT;
+    if (++g_cur == a.G) {
+      g_cur = 0;
+      --qt;
+    }
     // (wave-uniform) skip a tile whose rows all lie before the wave's keys
     if (qrow0 + kKT - 1 >= wkey0 && wkey0 < N) {
       // diagonal or ragged tile: masks; otherwise every row follows every key
       if (qrow0 < wkey0 + kWaveRows - 1 || qrow0 + kKT > N) {
-        colsum_tile<true>(ka, qs[buf], ls[buf], int(qrow0), int(wkey0), int(N), tot);
+        colsum_tile<true>(ka, qs[buf], ls[buf], int(qrow0), int(wkey0), int(N), run);
       } else {
-        colsum_tile<false>(ka, qs[buf], ls[buf], int(qrow0), int(wkey0), int(N), tot);
+        colsum_tile<false>(ka, qs[buf], ls[buf], int(qrow0), int(wkey0), int(N), run);
       }
+      if (++n_run == kRunTiles) flush();
     }
-    if (st + 1 < n_steps) store((st + 1) & 1);
   }
+  flush();
 #pragma unroll
   for (int f = 0; f < 2; ++f)
 #pragma unroll
