@@ -75,6 +75,7 @@ def build_cache(rdkv, synth, torch, w, lay, dims1, fp16_only=False, lay1=None):
     hist_tok = np.zeros(5, np.int64)
     hist_chan = np.zeros(5, np.int64)
     score_ms = 0.0
+    halves = None   # layer 0: the two halves of scoring on their own (prefill-LSE reuse)
     t0 = time.time()
     for l in range(w.n_layers):
         parts = [synth.prefill_layer(w, s, l, device="cuda") for s in range(S)]
@@ -89,6 +90,16 @@ def build_cache(rdkv, synth, torch, w, lay, dims1, fp16_only=False, lay1=None):
             del parts
             if ws is None:
                 ws = torch.empty(rdkv.score_workspace_bytes(dims1), dtype=torch.uint8, device="cuda")
+            if l == 0:
+                ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+                ev[0].record()
+                lse = rdkv.score_lse(dims1, Q, K)
+                ev[1].record()
+                rdkv.score_from_lse(dims1, Q, K, V, lse, workspace=ws)
+                ev[2].record()
+                ev[2].synchronize()
+                halves = (ev[0].elapsed_time(ev[1]), ev[1].elapsed_time(ev[2]))
+                del lse
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
             wt, vt, wc = rdkv.score(dims1, Q, K, V, workspace=ws)
@@ -97,6 +108,8 @@ def build_cache(rdkv, synth, torch, w, lay, dims1, fp16_only=False, lay1=None):
             bt, bc, _, _ = rdkv.allocate(dims1, wt, vt, wc, K, w.budget_v, w.budget_k)
             e1.synchronize()
             score_ms += e0.elapsed_time(e1)
+            if l == 0:
+                halves = halves + (e0.elapsed_time(e1),)
             del wt, vt, wc
         rdkv.pack(lay, cache, K, V, bt, bc, layer_begin=l)
         if lay1 is not None:
@@ -111,7 +124,7 @@ def build_cache(rdkv, synth, torch, w, lay, dims1, fp16_only=False, lay1=None):
             log(f"{'fp16 ' if fp16_only else ''}layer {l + 1}/{w.n_layers} packed, {time.time() - t0:.1f}s")
     torch.cuda.synchronize()
     return cache, dict(hist_tok=hist_tok, hist_chan=hist_chan, score_ms=score_ms, setup_s=time.time() - t0,
-                       layer_caches=layer_caches)
+                       layer_caches=layer_caches, score_halves=halves)
 
 
 def time_decode(rdkv, torch, lay, cache, q, kn, vn, steps, warmup, flush, grow=False):
@@ -405,7 +418,13 @@ def main():
                    "score_tflops_executed": round(score_flops / (st["score_ms"] * 1e-3) / 1e12, 2)
                    if st["score_ms"] > 0 else None,
                    "score_mfma_frac": round(score_flops / (st["score_ms"] * 1e-3) / 1e12 / MFMA_FP16_PEAK_TFS, 4)
-                   if st["score_ms"] > 0 else None},
+                   if st["score_ms"] > 0 else None,
+                   "score_layer0_ms": None if st.get("score_halves") is None else {
+                       "rdkv_score": round(st["score_halves"][2], 2),
+                       "rdkv_score_lse": round(st["score_halves"][0], 2),
+                       "rdkv_score_from_lse": round(st["score_halves"][1], 2),
+                       "note": "layer 0 alone; rdkv_score_from_lse is what scoring costs when the prefill "
+                               "forward supplies the row LSE"}},
         "wall_s_timed_loop": round(wall, 4),
     }
     if layer_loop is not None:

@@ -156,7 +156,7 @@ rdkv_status rdkv_score(const rdkv_dims* dims, const void* Q, const void* K, cons
   for (const void* p : {Q, K, V, (const void*)w_tok, (const void*)var_tok, (const void*)w_chan, (const void*)workspace})
     if (!aligned16(p)) return RDKV_ERR_ALIGN;
   if (workspace_bytes < rdkv_score_workspace_bytes(dims)) return RDKV_ERR_WORKSPACE;
-  ScoreParams p;
+  ScoreParams p{};
   p.n_tokens = dims->n_tokens;
   p.S = dims->n_seq;
   p.L = dims->n_layers;
@@ -170,6 +170,51 @@ rdkv_status rdkv_score(const rdkv_dims* dims, const void* Q, const void* K, cons
   p.w_chan = w_chan;
   p.lse = static_cast<float*>(workspace);
   return hip_status(launch_score(p, stream));
+}
+
+rdkv_status rdkv_score_lse(const rdkv_dims* dims, const void* Q, const void* K, float* lse, hipStream_t stream) {
+  rdkv_status st = check_dims(dims);
+  if (st != RDKV_OK) return st;
+  if (!Q || !K || !lse) return RDKV_ERR_NULL;
+  for (const void* p : {Q, K, (const void*)lse})
+    if (!aligned16(p)) return RDKV_ERR_ALIGN;
+  ScoreParams p{};
+  p.n_tokens = dims->n_tokens;
+  p.S = dims->n_seq;
+  p.L = dims->n_layers;
+  p.Hq = dims->n_q_heads;
+  p.Hkv = dims->n_kv_heads;
+  p.Q = static_cast<const __half*>(Q);
+  p.K = static_cast<const __half*>(K);
+  p.lse = lse;
+  return hip_status(launch_score_lse(p, stream));
+}
+
+rdkv_status rdkv_score_from_lse(const rdkv_dims* dims, const void* Q, const void* K, const void* V,
+                                const float* lse, float* w_tok, float* var_tok, float* w_chan,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  rdkv_status st = check_dims(dims);
+  if (st != RDKV_OK) return st;
+  if (!Q || !K || !V || !lse || !w_tok || !var_tok || !w_chan || !workspace) return RDKV_ERR_NULL;
+  for (const void* p : {Q, K, V, (const void*)lse, (const void*)w_tok, (const void*)var_tok, (const void*)w_chan,
+                        (const void*)workspace})
+    if (!aligned16(p)) return RDKV_ERR_ALIGN;
+  if (workspace_bytes < rdkv_score_workspace_bytes(dims)) return RDKV_ERR_WORKSPACE;
+  ScoreParams p{};
+  p.n_tokens = dims->n_tokens;
+  p.S = dims->n_seq;
+  p.L = dims->n_layers;
+  p.Hq = dims->n_q_heads;
+  p.Hkv = dims->n_kv_heads;
+  p.Q = static_cast<const __half*>(Q);
+  p.K = static_cast<const __half*>(K);
+  p.V = static_cast<const __half*>(V);
+  p.w_tok = w_tok;
+  p.var_tok = var_tok;
+  p.w_chan = w_chan;
+  p.lse = static_cast<float*>(workspace);
+  p.lse_in = lse;
+  return hip_status(launch_score_from_lse(p, stream));
 }
 
 rdkv_status rdkv_allocate(const rdkv_dims* dims, const float* w_tok, const float* var_tok,

@@ -44,8 +44,9 @@ struct ScoreArgs {
   int32_t Hq, Hkv, G;
   const __half* Q;
   const __half* K;
-  float* lse;      // [S*L][Hq][N], base-2 log-sum-exp of the scaled scores
+  float* lse;      // [S*L][Hq][N], log-sum-exp of the scaled scores: base 2, times lse_scale on output
   float* w_tok;    // [S*L][Hkv][N]
+  float lse_scale; // pass 1 writes (base-2 LSE) * lse_scale: 1, or ln 2 for a natural-log LSE
 };
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
@@ -319,7 +320,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         mm = mn;
       }
       const int64_t row = wrow0 + 16 * f + 4 * (lane >> 4) + r;
-      if ((lane & 15) == 0 && row < N) a.lse[(sl * a.Hq + hq) * N + row] = mm + log2f(ss);
+      if ((lane & 15) == 0 && row < N) a.lse[(sl * a.Hq + hq) * N + row] = (mm + log2f(ss)) * a.lse_scale;
     }
 }
 
@@ -455,6 +456,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     }
 }
 
+// A natural-log LSE (as a prefill attention forward returns it) in base 2.
+__global__ __launch_bounds__(kThreads) void lse_to_base2_kernel(const float* in, float* out, int64_t n) {
+  const int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  if (i < n) out[i] = in[i] * 1.4426950408889634f;
+}
+
 // Population variance of each V row: one wave per token, two passes in registers.
 __global__ __launch_bounds__(kThreads) void var_tok_kernel(const __half* V, float* var, int64_t rows) {
   const int64_t row = int64_t(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);
@@ -528,12 +535,23 @@ size_t score_workspace_bytes(int64_t S, int64_t L, int64_t Hq, int64_t N) {
   return lse + size_t(S * L * Hq) * kNormSplits * 2 * kHeadDim * sizeof(double);
 }
 
-hipError_t launch_score(const ScoreParams& p, hipStream_t stream) {
-  const int G = p.Hq / p.Hkv;
-  ScoreArgs a{p.n_tokens, p.Hq, p.Hkv, G, p.Q, p.K, p.lse, p.w_tok};
+namespace {
+
+ScoreArgs score_args(const ScoreParams& p, float lse_scale) {
+  return ScoreArgs{p.n_tokens, p.Hq, p.Hkv, p.Hq / p.Hkv, p.Q, p.K, p.lse, p.w_tok, lse_scale};
+}
+
+void launch_pass1(const ScoreParams& p, float lse_scale, hipStream_t stream) {
+  const unsigned nb = unsigned(cdiv(p.n_tokens, kBlockRows));
+  hipLaunchKernelGGL(score_lse_kernel, dim3(nb, unsigned(p.Hq), unsigned(int64_t(p.S) * p.L)), dim3(kThreads), 0,
+                     stream, score_args(p, lse_scale));
+}
+
+// Pass 2 from the base-2 LSE in p.lse, then var_tok and w_chan.
+hipError_t launch_rest(const ScoreParams& p, hipStream_t stream) {
+  const ScoreArgs a = score_args(p, 1.0f);
   const int64_t SL = int64_t(p.S) * p.L;
   const unsigned nb = unsigned(cdiv(p.n_tokens, kBlockRows));
-  hipLaunchKernelGGL(score_lse_kernel, dim3(nb, unsigned(p.Hq), unsigned(SL)), dim3(kThreads), 0, stream, a);
   hipLaunchKernelGGL(score_colsum_kernel, dim3(nb, unsigned(p.Hkv), unsigned(SL)), dim3(kThreads), 0, stream, a);
   const int64_t rows = SL * p.Hkv * p.n_tokens;
   hipLaunchKernelGGL(var_tok_kernel, dim3(unsigned(cdiv(rows, kThreads / 64))), dim3(kThreads), 0, stream, p.V,
@@ -544,6 +562,26 @@ hipError_t launch_score(const ScoreParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(chan_norm_partial_kernel, dim3(kNormSplits, unsigned(n_seg)), dim3(kThreads), 0, stream, a, part);
   hipLaunchKernelGGL(chan_norm_final_kernel, dim3(unsigned(n_seg)), dim3(kHeadDim), 0, stream, part, p.w_chan);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_score(const ScoreParams& p, hipStream_t stream) {
+  launch_pass1(p, 1.0f, stream);
+  return launch_rest(p, stream);
+}
+
+hipError_t launch_score_lse(const ScoreParams& p, hipStream_t stream) {
+  launch_pass1(p, 0.69314718055994531f, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_score_from_lse(const ScoreParams& p, hipStream_t stream) {
+  const int64_t n = int64_t(p.S) * p.L * p.Hq * p.n_tokens;
+  if (n > 0)
+    hipLaunchKernelGGL(lse_to_base2_kernel, dim3(unsigned(cdiv(n, kThreads))), dim3(kThreads), 0, stream, p.lse_in,
+                       p.lse, n);
+  return launch_rest(p, stream);
 }
 
 }  // namespace rdkv

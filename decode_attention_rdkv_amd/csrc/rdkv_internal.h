@@ -173,9 +173,15 @@ struct ScoreParams {
   float* w_tok;
   float* var_tok;
   float* w_chan;
-  float* lse;              // workspace [S][L][Hq][N]
+  float* lse;              // workspace [S][L][Hq][N], base-2 log-sum-exp of the scaled scores
+  const float* lse_in;     // launch_score_from_lse: natural-log LSE given by the caller
 };
+// The two passes and the bandwidth kernels (launch_score), pass 1 alone
+// writing p.lse in natural log (launch_score_lse), or everything but pass 1
+// from p.lse_in (launch_score_from_lse).
 hipError_t launch_score(const ScoreParams& p, hipStream_t stream);
+hipError_t launch_score_lse(const ScoreParams& p, hipStream_t stream);
+hipError_t launch_score_from_lse(const ScoreParams& p, hipStream_t stream);
 size_t score_workspace_bytes(int64_t S, int64_t L, int64_t Hq, int64_t N);
 
 }  // namespace rdkv

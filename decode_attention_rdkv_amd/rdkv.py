@@ -47,6 +47,9 @@ SIGNATURES = {
     "rdkv_layout_init": (c_i32, [ctypes.POINTER(Dims), c_i64, c_i64, c_i32, ctypes.POINTER(Layout)]),
     "rdkv_score_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(Dims)]),
     "rdkv_score": (c_i32, [ctypes.POINTER(Dims), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, ctypes.c_size_t, c_vp]),
+    "rdkv_score_lse": (c_i32, [ctypes.POINTER(Dims), c_vp, c_vp, c_vp, c_vp]),
+    "rdkv_score_from_lse": (c_i32, [ctypes.POINTER(Dims), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                    ctypes.c_size_t, c_vp]),
     "rdkv_allocate": (c_i32, [ctypes.POINTER(Dims), c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp,
                               c_vp]),
     "rdkv_cache_init": (c_i32, [ctypes.POINTER(Layout), c_vp, ctypes.c_size_t, c_vp]),
@@ -148,6 +151,41 @@ def score(dims: Dims, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, workspa
                           w_tok.data_ptr(), var_tok.data_ptr(), w_chan.data_ptr(),
                           _ptr(workspace, torch.uint8, None, "workspace"), workspace.numel(), _stream()),
            "rdkv_score")
+    return w_tok, var_tok, w_chan
+
+
+def score_lse(dims: Dims, Q: torch.Tensor, K: torch.Tensor, out: Optional[torch.Tensor] = None):
+    """Row log-sum-exp (natural log) of the causal scaled scores: fp32 [S][L][Hq][N]."""
+    lib = load()
+    S, L, Hq, Hk, N = dims.n_seq, dims.n_layers, dims.n_q_heads, dims.n_kv_heads, dims.n_tokens
+    if out is None:
+        out = torch.empty((S, L, Hq, N), dtype=torch.float32, device=Q.device)
+    _check(lib.rdkv_score_lse(ctypes.byref(dims), _ptr(Q, torch.float16, (S, L, Hq, N, HEAD_DIM), "Q"),
+                              _ptr(K, torch.float16, (S, L, Hk, N, HEAD_DIM), "K"),
+                              _ptr(out, torch.float32, (S, L, Hq, N), "lse"), _stream()),
+           "rdkv_score_lse")
+    return out
+
+
+def score_from_lse(dims: Dims, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, lse: torch.Tensor,
+                   workspace: Optional[torch.Tensor] = None):
+    """Stage-1 weights from a given natural-log row LSE; returns (w_tok, var_tok, w_chan)."""
+    lib = load()
+    S, L, Hq, Hk, N = dims.n_seq, dims.n_layers, dims.n_q_heads, dims.n_kv_heads, dims.n_tokens
+    dev = Q.device
+    w_tok = torch.empty((S, L, Hk, N), dtype=torch.float32, device=dev)
+    var_tok = torch.empty((S, L, Hk, N), dtype=torch.float32, device=dev)
+    w_chan = torch.empty((S, L, Hk, HEAD_DIM), dtype=torch.float32, device=dev)
+    ws_bytes = lib.rdkv_score_workspace_bytes(ctypes.byref(dims))
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    _check(lib.rdkv_score_from_lse(ctypes.byref(dims), _ptr(Q, torch.float16, (S, L, Hq, N, HEAD_DIM), "Q"),
+                                   _ptr(K, torch.float16, (S, L, Hk, N, HEAD_DIM), "K"),
+                                   _ptr(V, torch.float16, (S, L, Hk, N, HEAD_DIM), "V"),
+                                   _ptr(lse, torch.float32, (S, L, Hq, N), "lse"),
+                                   w_tok.data_ptr(), var_tok.data_ptr(), w_chan.data_ptr(),
+                                   _ptr(workspace, torch.uint8, None, "workspace"), workspace.numel(), _stream()),
+           "rdkv_score_from_lse")
     return w_tok, var_tok, w_chan
 
 

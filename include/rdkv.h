@@ -111,6 +111,23 @@ rdkv_status rdkv_score(const rdkv_dims* dims, const void* Q, const void* K, cons
                        float* w_tok, float* var_tok, float* w_chan,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Stage 1 in two halves, for callers that already have the row log-sum-exp of
+ * their causal prefill attention (section 2.2 stage 1 runs after prefill, whose
+ * attention forward computes it): rdkv_score = rdkv_score_lse, then
+ * rdkv_score_from_lse, up to rounding.
+ *   rdkv_score_lse: lse[s][l][hq][tau] = ln sum_{t <= tau} exp(Q[hq,tau].K[h,t]/sqrt(d)),
+ *     h = hq / G, natural log, fp32 [S][L][Hq][N] (device, caller-owned); Q, K
+ *     fp16 as for rdkv_score.  No workspace.
+ *   rdkv_score_from_lse: w_tok, var_tok, w_chan as rdkv_score, from that lse
+ *     (read only) instead of recomputing it: half of rdkv_score's matrix work.
+ *     `workspace` as for rdkv_score.
+ * Errors as rdkv_score (RDKV_ERR_NULL, _ALIGN for pointers not 16-byte
+ * aligned, _WORKSPACE, _SHAPE / _UNSUPPORTED for dims). */
+rdkv_status rdkv_score_lse(const rdkv_dims* dims, const void* Q, const void* K, float* lse, hipStream_t stream);
+rdkv_status rdkv_score_from_lse(const rdkv_dims* dims, const void* Q, const void* K, const void* V,
+                                const float* lse, float* w_tok, float* var_tok, float* w_chan,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* ---------------------------------------------------------------- stages 2-3
  * Lagrangian bit allocation (section 2.1 objective, section 2.2 stages 2 and 3).
  * Per segment, V tokens first: unit cost c_t = fl32(w_tok*var_tok); token t gets

@@ -92,6 +92,49 @@ def token_weights(Qg: np.ndarray, Kh: np.ndarray, block: int = 512) -> np.ndarra
     return w
 
 
+def row_lse(Qh: np.ndarray, Kh: np.ndarray, block: int = 512) -> np.ndarray:
+    """LSE_tau = ln sum_{t <= tau} exp(Q[tau].K[t] / sqrt(d)) for one query head.
+
+    The normaliser of the causal prefill softmax whose entries a_{tau,t}
+    [RDKV] 2.1 sums into w_t (a_{tau,t} = exp(s_{tau,t} - LSE_tau)); stage 1
+    runs after prefill ([RDKV] 2.2), whose attention forward yields it.
+    READING as in token_weights (causal, every prefill position a query).
+    Qh: [N][d] fp16, Kh: [N][d] fp16.  Returns [N] float64 (natural log).
+    """
+    N, d = Qh.shape
+    Q64, K64 = Qh.astype(np.float64), Kh.astype(np.float64)
+    inv = 1.0 / math.sqrt(d)
+    out = np.empty(N)
+    for r0 in range(0, N, block):
+        r1 = min(N, r0 + block)
+        S = (Q64[r0:r1] @ K64[:r1].T) * inv
+        S[np.arange(r1)[None, :] > np.arange(r0, r1)[:, None]] = -np.inf
+        m = S.max(axis=1)
+        out[r0:r1] = m + np.log(np.exp(S - m[:, None]).sum(axis=1))
+    return out
+
+
+def token_weights_from_lse(Qg: np.ndarray, Kh: np.ndarray, lse: np.ndarray, block: int = 512) -> np.ndarray:
+    """w_t of token_weights, with each row's normaliser taken as given.
+
+    w_t = sum_g sum_{tau >= t} exp(Q_g[tau].K[t] / sqrt(d) - lse[g][tau])
+    ([RDKV] 2.1, a_{tau,t} written with its log-normaliser).  Qg: [G][N][d]
+    fp16, Kh: [N][d] fp16, lse: [G][N].  Returns [N] float64.
+    """
+    G, N, d = Qg.shape
+    K64 = Kh.astype(np.float64)
+    inv = 1.0 / math.sqrt(d)
+    w = np.zeros(N)
+    for g in range(G):
+        Q64 = Qg[g].astype(np.float64)
+        for r0 in range(0, N, block):
+            r1 = min(N, r0 + block)
+            S = (Q64[r0:r1] @ K64[:r1].T) * inv - np.asarray(lse[g][r0:r1], dtype=np.float64)[:, None]
+            S[np.arange(r1)[None, :] > np.arange(r0, r1)[:, None]] = -np.inf
+            w[:r1] += np.exp(S).sum(axis=0)
+    return w
+
+
 def channel_weights(Qg: np.ndarray, Kh: np.ndarray) -> np.ndarray:
     """w_c = ||Q_{:,c}||_2 * ||K_{:,c}||_2 / sqrt(d)   ([RDKV] 2.1).
 

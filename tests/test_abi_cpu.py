@@ -106,6 +106,18 @@ def test_score_validation(lib):
     assert lib.rdkv_score(ctypes.byref(_dims(head_dim=96)), A, A, A, A, A, A, A, ws, None) == UNSUP
 
 
+def test_score_halves_validation(lib):
+    d = _dims()
+    ws = lib.rdkv_score_workspace_bytes(ctypes.byref(d))
+    assert lib.rdkv_score_lse(ctypes.byref(d), A, A, None, None) == NULL
+    assert lib.rdkv_score_lse(ctypes.byref(d), A, A + 4, A, None) == ALIGN
+    assert lib.rdkv_score_lse(ctypes.byref(_dims(head_dim=96)), A, A, A, None) == UNSUP
+    assert lib.rdkv_score_from_lse(ctypes.byref(d), A, A, A, None, A, A, A, A, ws, None) == NULL
+    assert lib.rdkv_score_from_lse(ctypes.byref(d), A, A, A, A + 8, A, A, A, A, ws, None) == ALIGN
+    assert lib.rdkv_score_from_lse(ctypes.byref(d), A, A, A, A, A, A, A, A, ws - 1, None) == WORKSPACE
+    assert lib.rdkv_score_from_lse(ctypes.byref(_dims(head_dim=96)), A, A, A, A, A, A, A, A, ws, None) == UNSUP
+
+
 def test_allocate_validation(lib):
     d = _dims()
     args = [A] * 4

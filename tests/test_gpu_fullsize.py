@@ -179,6 +179,24 @@ def test_score_weights_sum_to_query_rows_on_a_128k_layer(gpu_lib):
     assert bool((wt > 0).all()) and bool((vt > 0).all()) and bool((wc > 0).all())
 
 
+def test_score_halves_compose_to_score_on_a_128k_layer(gpu_lib):
+    """On the same 128K layer, rdkv_score_lse followed by rdkv_score_from_lse
+    (the launch configuration of both halves at full size) gives rdkv_score's
+    weights up to the rounding of the natural-log round trip of the LSE."""
+    rdkv = gpu_lib
+    w = synth.WORKLOADS["llama8b-32layer-n128k"]
+    Q, K, V = synth.prefill_layer(w, 0, 5, device=DEV)
+    dims = rdkv.make_dims(1, 1, w.n_q_heads, w.n_kv_heads, w.n_tokens)
+    Qd, Kd, Vd = Q[None, None].contiguous(), K[None, None].contiguous(), V[None, None].contiguous()
+    wt = rdkv.score(dims, Qd, Kd, Vd)[0]
+    lse = rdkv.score_lse(dims, Qd, Kd)
+    wt2, vt2, wc2 = rdkv.score_from_lse(dims, Qd, Kd, Vd, lse)
+    rel = float(((wt2.double() - wt.double()).abs() / wt.double()).max())
+    print(f"max rel diff of w_t, halves vs rdkv_score: {rel:.2e}")
+    assert rel <= 1e-4
+    assert bool(torch.isfinite(lse).all())
+
+
 # ------------------------------------------------------------------ allocation at full context length
 
 @pytest.mark.parametrize("name,seq,layer,heads", [

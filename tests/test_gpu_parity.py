@@ -280,6 +280,33 @@ def test_score_matches_oracle(gpu_lib, G, Hkv, N):
         assert abs(wt[h].astype(np.float64).sum() - G * N) <= TOL * G * N
 
 
+@pytest.mark.parametrize("G,Hkv,N", [(4, 2, 900), (1, 1, 65)])
+def test_score_halves_match_oracle_and_compose_to_score(gpu_lib, G, Hkv, N):
+    """rdkv_score_lse against the oracle's row LSE (an LSE error of 2e-3 is a
+    2e-3 relative error in every attention weight of the row); rdkv_score_from_lse
+    fed the oracle's LSE, as a model's prefill forward would feed it, against
+    the oracle's weights; and the two halves in a row against rdkv_score."""
+    rdkv = gpu_lib
+    w = synth.WORKLOADS["tiny-gqa4-n1k"].with_(n_q_heads=G * Hkv, n_kv_heads=Hkv, n_tokens=N)
+    Q, K, V = _score_case(w)
+    dims = rdkv.make_dims(1, 1, G * Hkv, Hkv, N)
+    Qd, Kd, Vd = dev(Q[None, None]), dev(K[None, None]), dev(V[None, None])
+    lse = host(rdkv.score_lse(dims, Qd, Kd))[0, 0]
+    ref_lse = np.stack([O.row_lse(Q[hq], K[hq // G]) for hq in range(G * Hkv)])
+    assert np.max(np.abs(lse - ref_lse)) <= TOL
+    wt, vt, wc = rdkv.score_from_lse(dims, Qd, Kd, Vd, dev(ref_lse.astype(np.float32)[None, None]))
+    wt, vt, wc = host(wt)[0, 0], host(vt)[0, 0], host(wc)[0, 0]
+    for h in range(Hkv):
+        ref_w = O.token_weights_from_lse(Q[h * G:(h + 1) * G], K[h], ref_lse[h * G:(h + 1) * G])
+        _, ref_v, ref_c = O.score_segment(Q[h * G:(h + 1) * G], K[h], V[h])
+        assert np.max(np.abs(wt[h] - ref_w) / ref_w) <= TOL
+        assert np.max(np.abs(vt[h] - ref_v) / ref_v) <= TOL
+        assert np.max(np.abs(wc[h] - ref_c) / ref_c) <= TOL
+    full = host(rdkv.score(dims, Qd, Kd, Vd)[0])
+    comp = host(rdkv.score_from_lse(dims, Qd, Kd, Vd, rdkv.score_lse(dims, Qd, Kd))[0])
+    assert np.max(np.abs(comp - full) / full) <= 1e-5
+
+
 # ------------------------------------------------------------------ end to end, tiny workload
 
 def test_end_to_end_tiny_workload(gpu_lib):

@@ -45,6 +45,50 @@ def test_token_weights_match_sdpa_column_sums(G, N):
     np.testing.assert_allclose(w, ref, rtol=1e-12, atol=1e-12)
 
 
+@pytest.mark.parametrize("N", [1, 9, 70])
+def test_row_lse_normalises_the_sdpa_attention_rows(N):
+    # exp(s - LSE) must reproduce torch's causal attention matrix row by row
+    r = _rng(11)
+    Q = r.standard_normal((1, N, 128)).astype(np.float16)
+    K = r.standard_normal((N, 128)).astype(np.float16)
+    lse = O.row_lse(Q[0], K, block=8)
+    S = Q[0].astype(np.float64) @ K.astype(np.float64).T / math.sqrt(128)
+    A = np.where(np.tril(np.ones((N, N), dtype=bool)), np.exp(S - lse[:, None]), 0.0)
+    np.testing.assert_allclose(A, _attention_matrix_sdpa(Q, K)[0], rtol=1e-12, atol=1e-15)
+
+
+def test_row_lse_closed_forms():
+    # Q = 0: every visible score is 0, so LSE_tau = ln(tau + 1)
+    N = 300
+    K = _rng(12).standard_normal((N, 128)).astype(np.float16)
+    lse = O.row_lse(np.zeros((N, 128), np.float16), K, block=64)
+    np.testing.assert_allclose(lse, np.log(np.arange(1, N + 1)), rtol=0, atol=1e-12)
+    # one visible key: row 0's LSE is its only score, and a key far above the
+    # rest dominates later rows: LSE -> its score
+    Q = np.zeros((3, 128), np.float16)
+    Q[:, 0] = 1.0
+    Kb = np.zeros((3, 128), np.float16)
+    Kb[0, 0] = 2.0
+    Kb[1, 0] = 300.0
+    l3 = O.row_lse(Q, Kb)
+    s0, s1 = 2.0 / math.sqrt(128), 300.0 / math.sqrt(128)   # row 2 also sees key 2, score 0
+    assert l3[0] == pytest.approx(s0, abs=1e-14)
+    assert l3[2] == pytest.approx(s1 + math.log1p(math.exp(s0 - s1) + math.exp(-s1)), abs=1e-12)
+
+
+@pytest.mark.parametrize("G,N", [(1, 40), (4, 97)])
+def test_token_weights_from_lse_agree_with_token_weights(G, N):
+    r = _rng(13)
+    Q = r.standard_normal((G, N, 128)).astype(np.float16)
+    K = r.standard_normal((N, 128)).astype(np.float16)
+    lse = np.stack([O.row_lse(Q[g], K, block=16) for g in range(G)])
+    w = O.token_weights_from_lse(Q, K, lse, block=32)
+    np.testing.assert_allclose(w, O.token_weights(Q, K, block=16), rtol=1e-12, atol=1e-14)
+    assert w.sum() == pytest.approx(G * N, rel=1e-12)
+    # a wrong normaliser scales each row's mass: LSE + ln 2 halves every weight
+    np.testing.assert_allclose(O.token_weights_from_lse(Q, K, lse + math.log(2.0)), w / 2, rtol=1e-12)
+
+
 def test_token_weights_sum_to_number_of_query_rows():
     r = _rng(2)
     G, N = 4, 300
