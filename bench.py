@@ -105,11 +105,21 @@ def build_cache(rdkv, synth, torch, w, lay, dims1, fp16_only=False, lay1=None):
             wt, vt, wc = rdkv.score(dims1, Q, K, V, workspace=ws)
             e1.record()
             del Q
+            e2 = torch.cuda.Event(enable_timing=True)
             bt, bc, _, _ = rdkv.allocate(dims1, wt, vt, wc, K, w.budget_v, w.budget_k)
-            e1.synchronize()
+            e2.record()
+            e2.synchronize()
             score_ms += e0.elapsed_time(e1)
             if l == 0:
-                halves = halves + (e0.elapsed_time(e1),)
+                halves = halves + (e0.elapsed_time(e1), e1.elapsed_time(e2))
+                # the same layer with one budget shared by its KV heads
+                e3, e4 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e3.record()
+                rdkv.allocate_shared(dims1, wt, vt, wc, K, w.budget_v * w.n_kv_heads, w.budget_k * w.n_kv_heads,
+                                     w.n_kv_heads)
+                e4.record()
+                e4.synchronize()
+                halves = halves + (e3.elapsed_time(e4),)
             del wt, vt, wc
         rdkv.pack(lay, cache, K, V, bt, bc, layer_begin=l)
         if lay1 is not None:
@@ -424,7 +434,11 @@ def main():
                        "rdkv_score_lse": round(st["score_halves"][0], 2),
                        "rdkv_score_from_lse": round(st["score_halves"][1], 2),
                        "note": "layer 0 alone; rdkv_score_from_lse is what scoring costs when the prefill "
-                               "forward supplies the row LSE"}},
+                               "forward supplies the row LSE"},
+                   "allocate_layer0_ms": None if st.get("score_halves") is None else {
+                       "rdkv_allocate": round(st["score_halves"][3], 2),
+                       "rdkv_allocate_shared_per_layer": round(st["score_halves"][4], 2),
+                       "note": "per-segment budgets, and one budget shared by the layer's KV heads"}},
         "wall_s_timed_loop": round(wall, 4),
     }
     if layer_loop is not None:

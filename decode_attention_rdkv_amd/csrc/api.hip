@@ -217,10 +217,10 @@ rdkv_status rdkv_score_from_lse(const rdkv_dims* dims, const void* Q, const void
   return hip_status(launch_score_from_lse(p, stream));
 }
 
-rdkv_status rdkv_allocate(const rdkv_dims* dims, const float* w_tok, const float* var_tok,
-                          const float* w_chan, const void* K, int64_t budget_v, int64_t budget_k,
-                          uint8_t* bits_tok, uint8_t* bits_chan, float* var_chan, double* lambda,
-                          hipStream_t stream) {
+rdkv_status rdkv_allocate_shared(const rdkv_dims* dims, const float* w_tok, const float* var_tok,
+                                 const float* w_chan, const void* K, int64_t budget_v, int64_t budget_k,
+                                 int32_t group, uint8_t* bits_tok, uint8_t* bits_chan, float* var_chan,
+                                 double* lambda, hipStream_t stream) {
   rdkv_status st = check_dims(dims);
   if (st != RDKV_OK) return st;
   if (!w_tok || !var_tok || !w_chan || !K || !bits_tok || !bits_chan || !var_chan || !lambda)
@@ -231,6 +231,8 @@ rdkv_status rdkv_allocate(const rdkv_dims* dims, const float* w_tok, const float
   if (budget_v < 0 || budget_k < 0) return RDKV_ERR_BUDGET;
   AllocParams p;
   p.n_seg = int64_t(dims->n_seq) * dims->n_layers * dims->n_kv_heads;
+  if (group < 1 || p.n_seg % group != 0) return RDKV_ERR_SHAPE;
+  p.group = group;
   p.n_tokens = dims->n_tokens;
   p.w_tok = w_tok;
   p.var_tok = var_tok;
@@ -243,6 +245,14 @@ rdkv_status rdkv_allocate(const rdkv_dims* dims, const float* w_tok, const float
   p.var_chan = var_chan;
   p.lambda = lambda;
   return hip_status(launch_allocate(p, stream));
+}
+
+rdkv_status rdkv_allocate(const rdkv_dims* dims, const float* w_tok, const float* var_tok,
+                          const float* w_chan, const void* K, int64_t budget_v, int64_t budget_k,
+                          uint8_t* bits_tok, uint8_t* bits_chan, float* var_chan, double* lambda,
+                          hipStream_t stream) {
+  return rdkv_allocate_shared(dims, w_tok, var_tok, w_chan, K, budget_v, budget_k, 1, bits_tok, bits_chan, var_chan,
+                              lambda, stream);
 }
 
 rdkv_status rdkv_cache_init(const rdkv_layout* layout, void* cache, size_t cache_bytes, hipStream_t stream) {

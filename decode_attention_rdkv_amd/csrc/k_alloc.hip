@@ -12,6 +12,10 @@
 // exact in fp64, so a bisection over the ordered bit patterns of non-negative
 // doubles (at most 63 halvings) lands exactly on lambda*.
 //
+// A budget may be shared by a group of consecutive segments (the heads of a
+// layer, or all of a sequence): the group's units then form one problem with
+// one lambda, the same rule over their union.
+//
 // Stage 3's unit variance is the exact population variance of a K channel over
 // the kept tokens: fp16 values are integers times 2^-24, so the sums are done
 // in 64- and 128-bit integers and the quotient is rounded once to fp32.
@@ -23,13 +27,13 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 
-__device__ inline int block_sum(int v, int* s_red) {
+__device__ inline int64_t block_sum64(int v, int64_t* s_red) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   v = wave_sum_i(v);
   __syncthreads();
   if (lane == 0) s_red[wave] = v;
   __syncthreads();
-  int t = 0;
+  int64_t t = 0;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) t += s_red[w];
   return t;
@@ -57,13 +61,13 @@ __device__ inline int unit_bits(float c, double lam) {
 // lambda* for the units this thread sees through `cost_of`, shared by the block.
 template <typename CostFn>
 __device__ double find_lambda(float cmax, int64_t budget, CostFn cost_of) {
-  if (int64_t(cost_of(0.0)) <= budget) return 0.0;
+  if (cost_of(0.0) <= budget) return 0.0;
   // invariant: cost(pattern lo) > budget >= cost(pattern hi)
   uint64_t lo = 0;
   uint64_t hi = __double_as_longlong(double(cmax) * 0.375);
   while (hi - lo > 1) {
     const uint64_t mid = lo + (hi - lo) / 2;
-    if (int64_t(cost_of(__longlong_as_double(mid))) <= budget)
+    if (cost_of(__longlong_as_double(mid)) <= budget)
       hi = mid;
     else
       lo = mid;
@@ -73,6 +77,7 @@ __device__ double find_lambda(float cmax, int64_t budget, CostFn cost_of) {
 
 struct AllocVArgs {
   int64_t N;
+  int32_t group;       // consecutive segments sharing the budget
   const float* w_tok;
   const float* var_tok;
   int64_t budget;
@@ -80,27 +85,29 @@ struct AllocVArgs {
   double* lambda;
 };
 
+// One workgroup per group of segments: its group * N tokens are one problem.
+// (A thread's bit count stays far below 2^31; the block total is 64-bit.)
 __global__ __launch_bounds__(kThreads) void alloc_v_kernel(AllocVArgs a) {
-  __shared__ int s_i[kWaves];
+  __shared__ int64_t s_i[kWaves];
   __shared__ float s_f[kWaves];
-  const int64_t seg = blockIdx.x;
-  const float* w = a.w_tok + seg * a.N;
-  const float* v = a.var_tok + seg * a.N;
+  const int64_t n = a.N * a.group;
+  const int64_t base = int64_t(blockIdx.x) * n;
+  const float* w = a.w_tok + base;
+  const float* v = a.var_tok + base;
   float cmax = 0.0f;
-  for (int64_t t = threadIdx.x; t < a.N; t += kThreads) {
+  for (int64_t t = threadIdx.x; t < n; t += kThreads) {
     const float c = __fmul_rn(w[t], v[t]);
     if (c > cmax) cmax = c;
   }
   cmax = block_max(cmax, s_f);
   auto cost = [&](double lam) {
-    int n = 0;
-    for (int64_t t = threadIdx.x; t < a.N; t += kThreads) n += unit_bits(__fmul_rn(w[t], v[t]), lam);
-    return block_sum(n, s_i);
+    int k = 0;
+    for (int64_t t = threadIdx.x; t < n; t += kThreads) k += unit_bits(__fmul_rn(w[t], v[t]), lam);
+    return block_sum64(k, s_i);
   };
   const double lam = find_lambda(cmax, a.budget, cost);
-  for (int64_t t = threadIdx.x; t < a.N; t += kThreads)
-    a.bits_tok[seg * a.N + t] = uint8_t(unit_bits(__fmul_rn(w[t], v[t]), lam));
-  if (threadIdx.x == 0) a.lambda[2 * seg] = lam;
+  for (int64_t t = threadIdx.x; t < n; t += kThreads) a.bits_tok[base + t] = uint8_t(unit_bits(__fmul_rn(w[t], v[t]), lam));
+  for (int s = threadIdx.x; s < a.group; s += kThreads) a.lambda[2 * (int64_t(blockIdx.x) * a.group + s)] = lam;
 }
 
 // ---------------------------------------------------------------- exact variance
@@ -165,6 +172,7 @@ __device__ float round_div_to_f32(U128 M, uint64_t D, int e2) {
 
 struct AllocKArgs {
   int64_t N;
+  int32_t group;       // consecutive segments sharing the budget
   const __half* K;
   const uint8_t* bits_tok;
   const float* w_chan;
@@ -174,9 +182,10 @@ struct AllocKArgs {
   double* lambda;
 };
 
-__global__ __launch_bounds__(kThreads) void alloc_k_kernel(AllocKArgs a) {
-  __shared__ int s_i[kWaves];
-  __shared__ float s_f[kWaves];
+// One workgroup per segment: the exact variance of each K channel over the
+// segment's kept tokens.
+__global__ __launch_bounds__(kThreads) void alloc_kvar_kernel(AllocKArgs a) {
+  __shared__ int64_t s_i[kWaves];
   __shared__ int64_t s_s1[kThreads / kHeadDim][kHeadDim];
   __shared__ U128 s_s2[kThreads / kHeadDim][kHeadDim];
   const int64_t seg = blockIdx.x;
@@ -200,36 +209,56 @@ __global__ __launch_bounds__(kThreads) void alloc_k_kernel(AllocKArgs a) {
   }
   s_s1[tr][c] = s1;
   s_s2[tr][c] = s2;
-  n = block_sum(n, s_i) / kHeadDim;   // every channel counted each kept token
+  n = int(block_sum64(n, s_i) / kHeadDim);   // every channel counted each kept token
   __syncthreads();
-  float var = 0.0f, cc = 0.0f;
   if (tr == 0) {
     for (int r = 1; r < kRows; ++r) {
       s1 += s_s1[r][c];
       s2 = add128(s2, s_s2[r][c]);
     }
+    float var = 0.0f;
     if (n > 0) {
       const uint64_t a1 = uint64_t(s1 < 0 ? -s1 : s1);
       const U128 M = sub128(mul128_64(s2, uint64_t(n)), mul64(a1, a1));   // n*S2 - S1^2 >= 0
       var = round_div_to_f32(M, uint64_t(n) * uint64_t(n), -48);
     }
-    cc = __fmul_rn(a.w_chan[seg * kHeadDim + c], var);
     a.var_chan[seg * kHeadDim + c] = var;
   }
-  const float cmax = block_max(tr == 0 && cc > 0.0f ? cc : 0.0f, s_f);
-  auto cost = [&](double lam) { return block_sum(tr == 0 ? unit_bits(cc, lam) : 0, s_i); };
+}
+
+// One workgroup per group of segments: the group * 128 channels are one
+// problem with unit costs fl32(w_chan * var_chan).
+__global__ __launch_bounds__(kThreads) void alloc_kbits_kernel(AllocKArgs a) {
+  __shared__ int64_t s_i[kWaves];
+  __shared__ float s_f[kWaves];
+  const int64_t n = int64_t(kHeadDim) * a.group;
+  const int64_t base = int64_t(blockIdx.x) * n;
+  auto cost_at = [&](int64_t u) { return __fmul_rn(a.w_chan[base + u], a.var_chan[base + u]); };
+  float cmax = 0.0f;
+  for (int64_t u = threadIdx.x; u < n; u += kThreads) {
+    const float cc = cost_at(u);
+    if (cc > cmax) cmax = cc;
+  }
+  cmax = block_max(cmax, s_f);
+  auto cost = [&](double lam) {
+    int k = 0;
+    for (int64_t u = threadIdx.x; u < n; u += kThreads) k += unit_bits(cost_at(u), lam);
+    return block_sum64(k, s_i);
+  };
   const double lam = find_lambda(cmax, a.budget, cost);
-  if (tr == 0) a.bits_chan[seg * kHeadDim + c] = uint8_t(unit_bits(cc, lam));
-  if (threadIdx.x == 0) a.lambda[2 * seg + 1] = lam;
+  for (int64_t u = threadIdx.x; u < n; u += kThreads) a.bits_chan[base + u] = uint8_t(unit_bits(cost_at(u), lam));
+  for (int s = threadIdx.x; s < a.group; s += kThreads) a.lambda[2 * (int64_t(blockIdx.x) * a.group + s) + 1] = lam;
 }
 
 }  // namespace
 
 hipError_t launch_allocate(const AllocParams& p, hipStream_t stream) {
-  AllocVArgs va{p.n_tokens, p.w_tok, p.var_tok, p.budget_v, p.bits_tok, p.lambda};
-  hipLaunchKernelGGL(alloc_v_kernel, dim3(unsigned(p.n_seg)), dim3(kThreads), 0, stream, va);
-  AllocKArgs ka{p.n_tokens, p.K, p.bits_tok, p.w_chan, p.budget_k, p.bits_chan, p.var_chan, p.lambda};
-  hipLaunchKernelGGL(alloc_k_kernel, dim3(unsigned(p.n_seg)), dim3(kThreads), 0, stream, ka);
+  const unsigned n_groups = unsigned(p.n_seg / p.group);
+  AllocVArgs va{p.n_tokens, p.group, p.w_tok, p.var_tok, p.budget_v, p.bits_tok, p.lambda};
+  hipLaunchKernelGGL(alloc_v_kernel, dim3(n_groups), dim3(kThreads), 0, stream, va);
+  AllocKArgs ka{p.n_tokens, p.group, p.K, p.bits_tok, p.w_chan, p.budget_k, p.bits_chan, p.var_chan, p.lambda};
+  hipLaunchKernelGGL(alloc_kvar_kernel, dim3(unsigned(p.n_seg)), dim3(kThreads), 0, stream, ka);
+  hipLaunchKernelGGL(alloc_kbits_kernel, dim3(n_groups), dim3(kThreads), 0, stream, ka);
   return hipGetLastError();
 }
 

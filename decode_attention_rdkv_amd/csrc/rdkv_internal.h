@@ -152,6 +152,7 @@ hipError_t launch_unpack(const uint8_t* cache, uint64_t cache_bytes, const rdkv_
 
 struct AllocParams {
   int64_t n_seg, n_tokens;
+  int32_t group;           // consecutive segments sharing one budget (divides n_seg)
   const float* w_tok;
   const float* var_tok;
   const float* w_chan;

@@ -52,6 +52,8 @@ SIGNATURES = {
                                     ctypes.c_size_t, c_vp]),
     "rdkv_allocate": (c_i32, [ctypes.POINTER(Dims), c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp,
                               c_vp]),
+    "rdkv_allocate_shared": (c_i32, [ctypes.POINTER(Dims), c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i32, c_vp, c_vp,
+                                     c_vp, c_vp, c_vp]),
     "rdkv_cache_init": (c_i32, [ctypes.POINTER(Layout), c_vp, ctypes.c_size_t, c_vp]),
     "rdkv_pack": (c_i32, [ctypes.POINTER(Layout), c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, ctypes.c_size_t, c_vp]),
     "rdkv_decode": (c_i32, [ctypes.POINTER(Layout), c_vp, ctypes.c_size_t, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp,
@@ -205,6 +207,25 @@ def allocate(dims: Dims, w_tok, var_tok, w_chan, K, budget_v: int, budget_k: int
                              bits_tok.data_ptr(), bits_chan.data_ptr(), var_chan.data_ptr(), lam.data_ptr(),
                              _stream()),
            "rdkv_allocate")
+    return bits_tok, bits_chan, var_chan, lam
+
+
+def allocate_shared(dims: Dims, w_tok, var_tok, w_chan, K, budget_v: int, budget_k: int, group: int):
+    """Bit allocation with one budget per group of `group` consecutive segments."""
+    lib = load()
+    S, L, Hk, N = dims.n_seq, dims.n_layers, dims.n_kv_heads, dims.n_tokens
+    dev = K.device
+    bits_tok = torch.empty((S, L, Hk, N), dtype=torch.uint8, device=dev)
+    bits_chan = torch.empty((S, L, Hk, HEAD_DIM), dtype=torch.uint8, device=dev)
+    var_chan = torch.empty((S, L, Hk, HEAD_DIM), dtype=torch.float32, device=dev)
+    lam = torch.empty((S, L, Hk, 2), dtype=torch.float64, device=dev)
+    _check(lib.rdkv_allocate_shared(ctypes.byref(dims), _ptr(w_tok, torch.float32, (S, L, Hk, N), "w_tok"),
+                                    _ptr(var_tok, torch.float32, (S, L, Hk, N), "var_tok"),
+                                    _ptr(w_chan, torch.float32, (S, L, Hk, HEAD_DIM), "w_chan"),
+                                    _ptr(K, torch.float16, (S, L, Hk, N, HEAD_DIM), "K"), budget_v, budget_k, group,
+                                    bits_tok.data_ptr(), bits_chan.data_ptr(), var_chan.data_ptr(), lam.data_ptr(),
+                                    _stream()),
+           "rdkv_allocate_shared")
     return bits_tok, bits_chan, var_chan, lam
 
 

@@ -145,6 +145,23 @@ rdkv_status rdkv_allocate(const rdkv_dims* dims, const float* w_tok, const float
                           uint8_t* bits_tok, uint8_t* bits_chan, float* var_chan, double* lambda,
                           hipStream_t stream);
 
+/* The same allocation with one budget shared by each group of `group`
+ * consecutive segments (section 2.1 states B as the total bit budget; segments
+ * are ordered [S][L][Hkv], so group = Hkv shares a layer's budget across its
+ * KV heads and group = L*Hkv a sequence's across all layers and heads).  Each
+ * group's V tokens form one problem with one lambda_V and budget_v bits, then
+ * its K channels (variances still per segment over that segment's kept
+ * tokens) one problem with one lambda_K and budget_k bits; lambda is written
+ * for every segment of the group.  rdkv_allocate is group = 1.  A segment may
+ * now receive up to its group's whole budget, so a blob packed from this
+ * allocation needs a layout made with the group budgets as the per-segment
+ * budgets (rdkv_pack marks a segment that does not fit as empty).
+ * group must be >= 1 and divide S*L*Hkv, else RDKV_ERR_SHAPE. */
+rdkv_status rdkv_allocate_shared(const rdkv_dims* dims, const float* w_tok, const float* var_tok,
+                                 const float* w_chan, const void* K, int64_t budget_v, int64_t budget_k,
+                                 int32_t group, uint8_t* bits_tok, uint8_t* bits_chan, float* var_chan,
+                                 double* lambda, hipStream_t stream);
+
 /* ---------------------------------------------------------------- packing
  * TriZone packing (section 2.3; quantizer of "Solusi 3").  The blob format is
  * specified in the repository's design notes; every offset inside the blob is

@@ -290,6 +290,28 @@ def allocate_segment(w_tok, var_tok, w_chan, Kh, budget_v: int, budget_k: int):
     return dict(bits_tok=bt, bits_chan=bc, var_chan=vc, lambda_v=lv, lambda_k=lk)
 
 
+def allocate_group(w_toks, var_toks, w_chans, Ks, budget_v: int, budget_k: int):
+    """Stages 2 and 3 with one budget for a group of segments.
+
+    [RDKV] 2.1 states B as the total bit budget; here the units of several
+    segments (e.g. the KV heads of a layer) are pooled into one problem per
+    stage, each with one multiplier: the V tokens of all segments, then the K
+    channels of all segments, whose variances stay per segment over that
+    segment's kept tokens.  Inputs are lists (or stacked arrays) over the
+    group's segments.  Returns dict(bits_tok [n][N], bits_chan [n][d],
+    var_chan [n][d], lambda_v, lambda_k).
+    """
+    n = len(w_toks)
+    N = len(w_toks[0])
+    c_v = np.concatenate([unit_costs(w_toks[i], var_toks[i]) for i in range(n)])
+    bt, lv = lagrangian_allocate(c_v, budget_v)
+    bt = bt.reshape(n, N)
+    vc = np.stack([masked_channel_variance(Ks[i], bt[i]) for i in range(n)])
+    c_k = np.concatenate([unit_costs(w_chans[i], vc[i]) for i in range(n)])
+    bc, lk = lagrangian_allocate(c_k, budget_k)
+    return dict(bits_tok=bt, bits_chan=bc.reshape(n, -1), var_chan=vc, lambda_v=lv, lambda_k=lk)
+
+
 # --------------------------------------------------------------------------
 # Quantizer  ([KVMATH] Solusi 3; fp16 scale/zero per (token, bit-segment))
 # --------------------------------------------------------------------------

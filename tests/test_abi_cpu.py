@@ -127,6 +127,15 @@ def test_allocate_validation(lib):
     assert lib.rdkv_allocate(ctypes.byref(d), *args, 8, 8, A, A, A + 4, A, None) == ALIGN
 
 
+def test_allocate_shared_validation(lib):
+    d = _dims(n_layers=3, n_kv_heads=2)   # 6 segments
+    args = lambda g: (ctypes.byref(d), A, A, A, A, 10, 10, g, A, A, A, A, None)
+    for g in (0, -1, 4, 5, 7):
+        assert lib.rdkv_allocate_shared(*args(g)) == SHAPE, g
+    assert lib.rdkv_allocate_shared(ctypes.byref(d), None, A, A, A, 10, 10, 1, A, A, A, A, None) == NULL
+    assert lib.rdkv_allocate_shared(ctypes.byref(d), A, A, A, A, -1, 10, 1, A, A, A, A, None) == BUDGET
+
+
 def test_cache_pack_decode_validation(lib):
     lay = rdkv.layout(_dims(n_layers=2), 64, 32, 4)
     nb = lay.cache_bytes

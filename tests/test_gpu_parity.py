@@ -257,6 +257,65 @@ def test_allocate_bit_exact(gpu_lib, N, budget_avg):
         assert int(bits_tok[s].astype(np.int64).sum()) <= bv and int(bits_chan[s].astype(np.int64).sum()) <= bk
 
 
+@pytest.mark.parametrize("group", [1, 2, 4, 8])
+def test_allocate_shared_bit_exact(gpu_lib, group):
+    """One budget per group of consecutive segments (2 layers x 4 KV heads:
+    group 4 = per layer, 8 = the whole sequence) against the oracle's pooled
+    allocation on the same fp32 inputs; group 1 is rdkv_allocate."""
+    rdkv = gpu_lib
+    S, L, Hkv, N = 1, 2, 4, 600
+    n_seg = S * L * Hkv
+    w_tok, var_tok, w_chan = synth.random_unit_inputs(n_seg, N, seed=41)
+    w_tok *= np.arange(1, n_seg + 1, dtype=np.float32)[:, None]   # heads of unequal importance
+    K, _ = synth.random_kv(n_seg, N, seed=42)
+    K[:, :, :4] *= np.float16(8)
+    bv, bk = int(1.5 * N) * group, 96 * group
+    dims = rdkv.make_dims(S, L, 4 * Hkv, Hkv, N)
+    shp = (S, L, Hkv)
+    args = (dims, dev(w_tok.reshape(shp + (N,))), dev(var_tok.reshape(shp + (N,))), dev(w_chan.reshape(shp + (128,))),
+            dev(K.reshape(shp + (N, 128))), bv, bk)
+    bt, bc, vc, lam = (host(x) for x in rdkv.allocate_shared(*args, group))
+    bt, bc, vc, lam = bt.reshape(n_seg, N), bc.reshape(n_seg, 128), vc.reshape(n_seg, 128), lam.reshape(n_seg, 2)
+    for g0 in range(0, n_seg, group):
+        sl = slice(g0, g0 + group)
+        ref = O.allocate_group(w_tok[sl], var_tok[sl], w_chan[sl], K[sl], bv, bk)
+        assert np.array_equal(bt[sl], ref["bits_tok"]), f"group at {g0}: V bits differ"
+        assert np.array_equal(vc[sl].view(np.uint32), ref["var_chan"].view(np.uint32))
+        assert np.array_equal(bc[sl], ref["bits_chan"]), f"group at {g0}: K bits differ"
+        assert np.all(lam[sl, 0] == ref["lambda_v"]) and np.all(lam[sl, 1] == ref["lambda_k"])
+        assert int(bt[sl].astype(np.int64).sum()) <= bv and int(bc[sl].astype(np.int64).sum()) <= bk
+    if group == 1:
+        one = [host(x) for x in rdkv.allocate(*args)]
+        assert all(np.array_equal(a.reshape(-1), b.reshape(-1)) for a, b in zip(one, (bt, bc, vc, lam)))
+
+
+def test_shared_budget_cache_packs_and_decodes(gpu_lib):
+    """A per-layer budget (group = the KV heads of a layer) moves bits between
+    heads; the blob, laid out with the group budget as each segment's bound,
+    packs byte for byte as the oracle's and decodes within 2e-3."""
+    rdkv = gpu_lib
+    S, L, Hq, Hkv, N, cap = 1, 2, 8, 2, 900, 8
+    n_seg = S * L * Hkv
+    w_tok, var_tok, w_chan = synth.random_unit_inputs(n_seg, N, seed=43)
+    w_tok[1::2] *= np.float32(20.0)                                # the second head of each layer matters more
+    K, V = synth.random_kv(n_seg, N, seed=44)
+    bv, bk = int(1.2 * N) * Hkv, 80 * Hkv
+    dims = rdkv.make_dims(S, L, Hq, Hkv, N)
+    shp = (S, L, Hkv)
+    bt, bc, _, _ = rdkv.allocate_shared(dims, dev(w_tok.reshape(shp + (N,))), dev(var_tok.reshape(shp + (N,))),
+                                        dev(w_chan.reshape(shp + (128,))), dev(K.reshape(shp + (N, 128))), bv, bk,
+                                        Hkv)
+    per_seg = host(bt).reshape(n_seg, N).astype(np.int64).sum(axis=1)
+    assert per_seg[1] > bv // Hkv and per_seg[0] < bv // Hkv      # not an even split
+    lay = rdkv.layout(dims, bv, bk, cap)
+    ol = O.Layout(S, L, Hq, Hkv, 128, N, bv, bk, cap)
+    cache = rdkv.cache_init(lay)
+    rdkv.pack(lay, cache, dev(K.reshape(shp + (N, 128))), dev(V.reshape(shp + (N, 128))), bt, bc)
+    oblob = O.pack_cache(ol, K.reshape(shp + (N, 128)), V.reshape(shp + (N, 128)), host(bt), host(bc))
+    assert np.array_equal(host(cache), oblob)
+    _decode_run(rdkv, lay, ol, cache, oblob, 4, 45)
+
+
 # ------------------------------------------------------------------ scoring
 
 def _score_case(w, seq=0, layer=0):

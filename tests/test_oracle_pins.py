@@ -278,6 +278,48 @@ def test_allocation_is_lagrangian_and_hull_optimal_bruteforce(seed):
     assert dist == best
 
 
+def test_group_allocation_of_one_segment_is_the_segment_allocation():
+    r = _rng(31)
+    N = 200
+    w = np.exp(r.standard_normal(N)).astype(np.float32)
+    v = (r.chisquare(128, N) / 128).astype(np.float32)
+    wc = np.exp(r.standard_normal(128)).astype(np.float32)
+    K = r.standard_normal((N, 128)).astype(np.float16)
+    g = O.allocate_group([w], [v], [wc], [K], 700, 150)
+    s = O.allocate_segment(w, v, wc, K, 700, 150)
+    assert np.array_equal(g["bits_tok"][0], s["bits_tok"]) and np.array_equal(g["bits_chan"][0], s["bits_chan"])
+    assert g["lambda_v"] == s["lambda_v"] and g["lambda_k"] == s["lambda_k"]
+    assert np.array_equal(g["var_chan"][0].view(np.uint32), s["var_chan"].view(np.uint32))
+
+
+def test_group_allocation_pools_the_budget():
+    r = _rng(32)
+    n, N, B = 3, 150, 900
+    w = [np.exp(r.standard_normal(N) * (1 + i)).astype(np.float32) for i in range(n)]
+    v = [(r.chisquare(128, N) / 128).astype(np.float32) for _ in range(n)]
+    wc = [np.exp(r.standard_normal(128)).astype(np.float32) for _ in range(n)]
+    K = [r.standard_normal((N, 128)).astype(np.float16) for _ in range(n)]
+    g = O.allocate_group(w, v, wc, K, B, 300)
+    assert int(g["bits_tok"].astype(np.int64).sum()) <= B
+    assert int(g["bits_chan"].astype(np.int64).sum()) <= 300
+
+    def distortion(bits, costs):
+        return float(sum(np.sum(c.astype(np.float64) * 2.0 ** -b.astype(np.float64)) for b, c in zip(bits, costs)))
+    costs = [O.unit_costs(w[i], v[i]) for i in range(n)]
+    split = [O.lagrangian_allocate(costs[i], B // n)[0] for i in range(n)]
+    # one multiplier over the pooled units is at least as good as any split of the budget
+    assert distortion(g["bits_tok"], costs) <= distortion(split, costs) + 1e-9
+    # the bits follow the weights: the segment with the heaviest tail gets the most
+    per_seg = g["bits_tok"].astype(np.int64).sum(axis=1)
+    assert per_seg[2] > per_seg[0]
+    # a segment with all-zero weights gets nothing; the others share the whole budget
+    w0 = [np.zeros(N, np.float32)] + w[1:]
+    g0 = O.allocate_group(w0, v, wc, K, B, 300)
+    assert g0["bits_tok"][0].sum() == 0
+    assert np.array_equal(g0["bits_tok"][1:].reshape(-1),
+                          O.lagrangian_allocate(np.concatenate(costs[1:]), B)[0])
+
+
 def test_allocation_special_cases():
     c = np.array([1.0, 2.0, 0.5, 3.0], np.float32)
     assert list(O.lagrangian_allocate(c, 64)[0]) == [16] * 4          # budget covers all 16
