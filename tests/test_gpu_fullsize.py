@@ -231,3 +231,31 @@ def test_full_size_allocation_bit_exact_on_scored_weights(gpu_lib, name, seq, la
         assert np.array_equal(vc[h].view(np.uint32), ref["var_chan"].view(np.uint32)), f"head {h}: var_chan"
         assert np.array_equal(bc[h], ref["bits_chan"]), f"head {h}: K bits differ"
         assert lam[h, 1] == ref["lambda_k"]
+
+
+def test_full_size_shared_budget_allocation_bit_exact(gpu_lib):
+    """One 128K layer of the 8B-shaped workload scored on the GPU, then
+    allocated with one budget shared by its 8 KV heads (8x the per-head budget)
+    on the GPU and by the oracle's pooled allocation from the same fp32
+    inputs: bits, lambdas and variances agree bit for bit, and the heads'
+    shares differ (the pooled budget moves bits between heads)."""
+    rdkv = gpu_lib
+    w = synth.WORKLOADS["llama8b-32layer-n128k"]
+    Hq, Hkv, N = w.n_q_heads, w.n_kv_heads, w.n_tokens
+    Q, K, V = synth.prefill_layer(w, 0, 11, device=DEV)
+    dims = rdkv.make_dims(1, 1, Hq, Hkv, N)
+    K5 = K[None, None].contiguous()
+    wt, vt, wc = rdkv.score(dims, Q[None, None].contiguous(), K5, V[None, None].contiguous())
+    del Q, V
+    bv, bk = w.budget_v * Hkv, w.budget_k * Hkv
+    bt, bc, vc, lam = rdkv.allocate_shared(dims, wt, vt, wc, K5, bv, bk, Hkv)
+    wt, vt, wc = host(wt)[0, 0], host(vt)[0, 0], host(wc)[0, 0]
+    bt, bc, vc, lam = host(bt)[0, 0], host(bc)[0, 0], host(vc)[0, 0], host(lam)[0, 0]
+    ref = O.allocate_group(wt, vt, wc, host(K), bv, bk)
+    per_head = bt.astype(np.int64).sum(axis=1)
+    print(f"V bits per head with one layer budget of {bv}: {per_head.tolist()}", flush=True)
+    assert np.array_equal(bt, ref["bits_tok"])
+    assert np.array_equal(vc.view(np.uint32), ref["var_chan"].view(np.uint32))
+    assert np.array_equal(bc, ref["bits_chan"])
+    assert np.all(lam[:, 0] == ref["lambda_v"]) and np.all(lam[:, 1] == ref["lambda_k"])
+    assert int(per_head.sum()) <= bv and per_head.max() > per_head.min()
