@@ -422,13 +422,23 @@ def main():
                          "achieved_Ginstr_per_s": round(valu / (tm["chunk"] * 1e-3) / 1e9, 1),
                          "peak_Ginstr_per_s": VALU_PEAK_GINSTR,
                          "frac": round(valu / (tm["chunk"] * 1e-3) / 1e9 / VALU_PEAK_GINSTR, 4),
+                         "lane_instructions_per_algorithmic_byte": round(valu * 64 / algo, 2),
                          "note": "wave64 VALU instructions (SQ_INSTS_VALU) over the same kernel time; the "
                                  "co-limit of this kernel at low bitwidths"}},
+        "memory": {"blob_bytes": int(lay.cache_bytes),
+                   "fp16_kv_bytes": int(2 * w.n_seq * w.n_layers * w.n_kv_heads * N * d * 2),
+                   "kv_bytes_read_per_step": int(algo - b["q_out"]),
+                   "blob_vs_fp16": round(lay.cache_bytes / (2 * w.n_seq * w.n_layers * w.n_kv_heads * N * d * 2), 4),
+                   "hbm_capacity_share": round(lay.cache_bytes / 288e9, 4),
+                   "note": "the blob is allocated for the budget bounds (slot capacity); kv_bytes_read_per_step is "
+                           "what the packed cache actually holds and decode reads"},
         "stages": {"setup_s": round(st["setup_s"], 2), "score_ms_total": round(st["score_ms"], 2),
                    "score_tflops_executed": round(score_flops / (st["score_ms"] * 1e-3) / 1e12, 2)
                    if st["score_ms"] > 0 else None,
                    "score_mfma_frac": round(score_flops / (st["score_ms"] * 1e-3) / 1e12 / MFMA_FP16_PEAK_TFS, 4)
                    if st["score_ms"] > 0 else None,
+                   "score_mfma_frac_algorithmic": round(score_flops / 2 / (st["score_ms"] * 1e-3) / 1e12 /
+                                                        MFMA_FP16_PEAK_TFS, 4) if st["score_ms"] > 0 else None,
                    "score_layer0_ms": None if st.get("score_halves") is None else {
                        "rdkv_score": round(st["score_halves"][2], 2),
                        "rdkv_score_lse": round(st["score_halves"][0], 2),
