@@ -257,8 +257,8 @@ def test_allocate_bit_exact(gpu_lib, N, budget_avg):
         assert int(bits_tok[s].astype(np.int64).sum()) <= bv and int(bits_chan[s].astype(np.int64).sum()) <= bk
 
 
-@pytest.mark.parametrize("group", [1, 2, 4, 8])
-def test_allocate_shared_bit_exact(gpu_lib, group):
+@pytest.mark.parametrize("group,budget_scale", [(1, 1.0), (2, 1.0), (4, 1.0), (8, 1.0), (4, 0.0), (8, 40.0)])
+def test_allocate_shared_bit_exact(gpu_lib, group, budget_scale):
     """One budget per group of consecutive segments (2 layers x 4 KV heads:
     group 4 = per layer, 8 = the whole sequence) against the oracle's pooled
     allocation on the same fp32 inputs; group 1 is rdkv_allocate."""
@@ -269,7 +269,8 @@ def test_allocate_shared_bit_exact(gpu_lib, group):
     w_tok *= np.arange(1, n_seg + 1, dtype=np.float32)[:, None]   # heads of unequal importance
     K, _ = synth.random_kv(n_seg, N, seed=42)
     K[:, :, :4] *= np.float16(8)
-    bv, bk = int(1.5 * N) * group, 96 * group
+    # budget_scale 0: everything evicted; 40: more than 16 bits for every unit
+    bv, bk = int(1.5 * N * budget_scale) * group, int(96 * budget_scale) * group
     dims = rdkv.make_dims(S, L, 4 * Hkv, Hkv, N)
     shp = (S, L, Hkv)
     args = (dims, dev(w_tok.reshape(shp + (N,))), dev(var_tok.reshape(shp + (N,))), dev(w_chan.reshape(shp + (128,))),
@@ -284,6 +285,10 @@ def test_allocate_shared_bit_exact(gpu_lib, group):
         assert np.array_equal(bc[sl], ref["bits_chan"]), f"group at {g0}: K bits differ"
         assert np.all(lam[sl, 0] == ref["lambda_v"]) and np.all(lam[sl, 1] == ref["lambda_k"])
         assert int(bt[sl].astype(np.int64).sum()) <= bv and int(bc[sl].astype(np.int64).sum()) <= bk
+    if budget_scale == 0.0:
+        assert not bt.any() and not bc.any()
+    if budget_scale == 40.0:
+        assert np.all(bt == 16) and np.all(lam[:, 0] == 0.0)
     if group == 1:
         one = [host(x) for x in rdkv.allocate(*args)]
         assert all(np.array_equal(a.reshape(-1), b.reshape(-1)) for a, b in zip(one, (bt, bc, vc, lam)))
@@ -339,7 +344,7 @@ def test_score_matches_oracle(gpu_lib, G, Hkv, N):
         assert abs(wt[h].astype(np.float64).sum() - G * N) <= TOL * G * N
 
 
-@pytest.mark.parametrize("G,Hkv,N", [(4, 2, 900), (1, 1, 65)])
+@pytest.mark.parametrize("G,Hkv,N", [(4, 2, 900), (1, 1, 65), (8, 1, 200)])
 def test_score_halves_match_oracle_and_compose_to_score(gpu_lib, G, Hkv, N):
     """rdkv_score_lse against the oracle's row LSE (an LSE error of 2e-3 is a
     2e-3 relative error in every attention weight of the row); rdkv_score_from_lse
