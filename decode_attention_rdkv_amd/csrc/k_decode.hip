@@ -32,10 +32,17 @@
 // VALU issue.
 #include <type_traits>
 
+#include "lds_dma.h"
 #include "rdkv_internal.h"
 
 namespace rdkv {
 namespace {
+
+using dma::buffer_rsrc;
+using dma::buffer_rsrc4;
+using dma::lds_addr;
+using dma::rsrc4;
+using dma::wait_vmem;
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
@@ -414,13 +421,6 @@ __device__ constexpr int lane_row_offset(int cb) {
   return B == 2 ? (cb >> 1) * 4 : cb * (kHeadDim * B / 8 / 16);
 }
 
-// Raw buffer resource over [p, p + bytes): stride 0, range checked per dword,
-// so reads at or past `bytes` return zeros and touch no memory.
-constexpr int kBufferFlags = 0x00020000;
-__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, int(bytes), kBufferFlags);
-}
-
 // Tokens (j, j + 32) from a buffer whose range starts at the tile's first row:
 // the lane's parts of the rows at byte offsets off0 and off1.
 template <int B>
@@ -603,23 +603,6 @@ __device__ inline void wave_finish(WaveState<GW>& st, Smem<G, SW>& sm, int wave,
 
 // ---------------------------------------------------------------- K-record ring
 
-// LDS byte address of a pointer into shared memory.
-__device__ inline uint32_t lds_addr(const void* p) {
-  return uint32_t(size_t((const __attribute__((address_space(3))) void*)p));
-}
-
-// The same resource as four scalar registers, for inline assembly.
-typedef int rsrc4 __attribute__((ext_vector_type(4)));
-__device__ inline rsrc4 buffer_rsrc4(const void* p, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(p);
-  rsrc4 r;
-  r.x = __builtin_amdgcn_readfirstlane(int(uint32_t(a)));
-  r.y = __builtin_amdgcn_readfirstlane(int(uint32_t(a >> 32) & 0xffff));   // stride 0
-  r.z = __builtin_amdgcn_readfirstlane(int(bytes));
-  r.w = kBufferFlags;
-  return r;
-}
-
 // N (1..4) buffer_load_dwordx4 ... lds: copy j moves the 16 bytes at range
 // offset voff + 1024 j (voff = 16 * lane) to LDS byte lds + 1024 j + 16 * lane;
 // the instruction offset moves both addresses.  Dwords past the range arrive
@@ -664,18 +647,6 @@ __device__ inline void dma_records(const uint8_t* src, uint32_t bytes, uint32_t*
     lds_copy_block<(n - C0 < 4 ? n - C0 : 4)>(r, voff, lds_addr(stage) + off);
     dma_records<SW, C0 + 4>(src, bytes, stage, voff);
   }
-}
-
-// Waits until at most N vector-memory instructions of this wave are in
-// flight.  Loads complete in issue order, so this also completes every load
-// issued before the N most recent ones.  The scheduling barriers keep the
-// compiler from moving memory instructions across the wait.
-template <int N>
-__device__ inline void wait_vmem() {
-  static_assert(N >= 0 && N <= 63, "vmcnt range");
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-  __builtin_amdgcn_sched_barrier(0);
 }
 
 // ---------------------------------------------------------------- token groups (zones A and B)

@@ -24,10 +24,16 @@
 // ragged tiles; tiles entirely outside a wave's triangle are skipped by that
 // wave.  Plus two bandwidth kernels: var_tok (one wave per token) and the
 // column norms behind w_chan (partial sums in fp64, reduced in a fixed order).
+#include "lds_dma.h"
 #include "rdkv_internal.h"
 
 namespace rdkv {
 namespace {
+
+using dma::buffer_rsrc4;
+using dma::lds_addr;
+using dma::rsrc4;
+using dma::wait_vmem;
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 
@@ -62,23 +68,6 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 // them explicitly.
 constexpr int kStages = 3;
 constexpr int kTileBytes = kKT * kHeadDim * 2;
-constexpr int kBufferFlags = 0x00020000;   // raw buffer: range-checked, out-of-range reads return 0
-
-__device__ inline uint32_t lds_addr(const void* p) {
-  return uint32_t(size_t((const __attribute__((address_space(3))) void*)p));
-}
-
-typedef int rsrc4 __attribute__((ext_vector_type(4)));
-__device__ inline rsrc4 buffer_rsrc4(const void* p, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(p);
-  rsrc4 r;
-  r.x = __builtin_amdgcn_readfirstlane(int(uint32_t(a)));
-  r.y = __builtin_amdgcn_readfirstlane(int(uint32_t(a >> 32) & 0xffff));   // stride 0
-  r.z = __builtin_amdgcn_readfirstlane(int(bytes));
-  r.w = kBufferFlags;
-  return r;
-}
-
 // Per-lane range offsets of a wave's 4 copies: copy j fills LDS bytes
 // 1024 j + 16 lane of the wave's quarter, i.e. row 4 j + lane / 16, piece
 // p = lane % 16, which holds the row's piece p ^ (row % 16).  The instruction
@@ -133,15 +122,6 @@ __device__ inline void copy_floats64(const float* src, int64_t row0, int64_t N, 
       : "=&s"(saved)
       : "v"(voff), "s"(r), "s"(lds)
       : "memory");
-}
-
-// Waits until at most N vector-memory instructions of this wave are in
-// flight (they complete in issue order).
-template <int N>
-__device__ inline void wait_vmem() {
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-  __builtin_amdgcn_sched_barrier(0);
 }
 
 // A-operand fragments of 16 rows for the 16x16x32 MFMA: lane holds row
