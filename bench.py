@@ -250,6 +250,35 @@ def time_layer_graph(rdkv, torch, lay1, caches, q, kn, vn, steps, warmup, flush,
     return dict(step=float(t.mean()), step_median=float(np.median(t)), rel_diff=rel)
 
 
+def cpu_scoring_baseline(w, n_sample: int = 8192):
+    """The oracle's stage-1 token weights of one (layer, KV head), timed on the
+    first n_sample prefill rows and keys of a seeded layer (its G query heads)
+    and scaled by (N / n_sample)^2, the causal score count; single-threaded."""
+    import oracle as O
+    from decode_attention_rdkv_amd import synth
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:
+        threadpool_limits = None
+    n = min(n_sample, w.n_tokens)
+    Q, K, _ = synth.prefill_layer(w.with_(n_tokens=n), 0, 0)
+    G = w.group
+    ctx = threadpool_limits(1) if threadpool_limits else None
+    if ctx:
+        ctx.__enter__()
+    try:
+        t0 = time.perf_counter()
+        O.token_weights(Q[:G], K[0])
+        dt = time.perf_counter() - t0
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    scale = (w.n_tokens / n) ** 2
+    return dict(value=round(dt * scale, 2), unit="s per (layer, KV head)", cores=1, kind="oracle",
+                sample=f"token weights of one KV head ({G} query heads) over the first {n} of {w.n_tokens} "
+                       f"prefill positions, {dt:.2f} s, scaled by (N/{n})^2")
+
+
 def cpu_baseline(w, hist_tok, hist_chan, n_seg, n_c, sample_segments):
     """The oracle's decode of one step, timed on `sample_segments` segments of
     the same shape (kept-token mix and K-channel mix of the measured
@@ -474,6 +503,9 @@ def main():
         result["cpu_baseline"] = cpu_baseline(w, st["hist_tok"], st["hist_chan"], lay.n_seg, n_c,
                                               args.cpu_sample_segments)
         log(f"cpu baseline {time.time() - t0:.1f}s")
+        t0 = time.time()
+        result["cpu_baseline_scoring"] = cpu_scoring_baseline(w)
+        log(f"cpu scoring baseline {time.time() - t0:.1f}s")
     print(json.dumps(result), flush=True)
 
 
