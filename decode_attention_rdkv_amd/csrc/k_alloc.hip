@@ -183,43 +183,75 @@ struct AllocKArgs {
 };
 
 // One workgroup per segment: the exact variance of each K channel over the
-// segment's kept tokens.
+// segment's kept tokens.  A thread takes 8 channels of a row with one 16-byte
+// load (16 threads per row, 64 rows in flight); the integer sums are merged
+// across the rows' threads by shuffles, then across waves in LDS (exact, so
+// the order does not matter).
 __global__ __launch_bounds__(kThreads) void alloc_kvar_kernel(AllocKArgs a) {
+  constexpr int kCB = kHeadDim / 8;            // 8-channel blocks per row
+  constexpr int kRowLanes = kThreads / kCB;    // rows in flight
   __shared__ int64_t s_i[kWaves];
-  __shared__ int64_t s_s1[kThreads / kHeadDim][kHeadDim];
-  __shared__ U128 s_s2[kThreads / kHeadDim][kHeadDim];
+  __shared__ int64_t s_s1[kWaves][kHeadDim];
+  __shared__ U128 s_s2[kWaves][kHeadDim];
   const int64_t seg = blockIdx.x;
-  const int c = threadIdx.x & (kHeadDim - 1), tr = threadIdx.x / kHeadDim;
-  constexpr int kRows = kThreads / kHeadDim;
-  const __half* Kseg = a.K + seg * a.N * kHeadDim;
+  const int cb = threadIdx.x % kCB, tr = threadIdx.x / kCB;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint4* Kseg = reinterpret_cast<const uint4*>(a.K + seg * a.N * kHeadDim);
   const uint8_t* bt = a.bits_tok + seg * a.N;
 
-  // exact sums of X = x * 2^24 and X^2 over kept tokens
-  int64_t s1 = 0;
-  U128 s2{0, 0};
+  // exact sums of X = x * 2^24 and X^2 over kept tokens, channels 8 cb + e
+  int64_t s1[8];
+  U128 s2[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    s1[e] = 0;
+    s2[e] = U128{0, 0};
+  }
   int n = 0;
-  for (int64_t t = tr; t < a.N; t += kRows) {
+  for (int64_t t = tr; t < a.N; t += kRowLanes) {
     if (bits_group(bt[t]) < 0) continue;
-    const double x = double(__half2float(Kseg[t * kHeadDim + c]));
-    const int64_t X = int64_t(x * 16777216.0);
-    s1 += X;
-    const uint64_t ax = uint64_t(X < 0 ? -X : X);
-    s2 = add128(s2, mul64(ax, ax));
+    const uint4 v = Kseg[t * kCB + cb];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = (e & 1) ? half_hi(w[e >> 1]) : half_lo(w[e >> 1]);
+      const int64_t X = int64_t(double(x) * 16777216.0);
+      s1[e] += X;
+      const uint64_t ax = uint64_t(X < 0 ? -X : X);
+      s2[e] = add128(s2[e], mul64(ax, ax));
+    }
     ++n;
   }
-  s_s1[tr][c] = s1;
-  s_s2[tr][c] = s2;
-  n = int(block_sum64(n, s_i) / kHeadDim);   // every channel counted each kept token
+  // the wave's 4 row lanes of each channel block: lanes cb, cb + 16, cb + 32, cb + 48
+#pragma unroll
+  for (int x = 16; x < 64; x <<= 1)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      s1[e] += __shfl_xor(s1[e], x, 64);
+      const U128 o{__shfl_xor(s2[e].hi, x, 64), __shfl_xor(s2[e].lo, x, 64)};
+      s2[e] = add128(s2[e], o);
+    }
+  if (lane < kCB) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      s_s1[wave][8 * cb + e] = s1[e];
+      s_s2[wave][8 * cb + e] = s2[e];
+    }
+  }
+  n = int(block_sum64(n, s_i) / kCB);   // every kept row counted by its kCB threads
   __syncthreads();
-  if (tr == 0) {
-    for (int r = 1; r < kRows; ++r) {
-      s1 += s_s1[r][c];
-      s2 = add128(s2, s_s2[r][c]);
+  if (threadIdx.x < kHeadDim) {
+    const int c = threadIdx.x;
+    int64_t S1 = 0;
+    U128 S2{0, 0};
+    for (int w = 0; w < kWaves; ++w) {
+      S1 += s_s1[w][c];
+      S2 = add128(S2, s_s2[w][c]);
     }
     float var = 0.0f;
     if (n > 0) {
-      const uint64_t a1 = uint64_t(s1 < 0 ? -s1 : s1);
-      const U128 M = sub128(mul128_64(s2, uint64_t(n)), mul64(a1, a1));   // n*S2 - S1^2 >= 0
+      const uint64_t a1 = uint64_t(S1 < 0 ? -S1 : S1);
+      const U128 M = sub128(mul128_64(S2, uint64_t(n)), mul64(a1, a1));   // n*S2 - S1^2 >= 0
       var = round_div_to_f32(M, uint64_t(n) * uint64_t(n), -48);
     }
     a.var_chan[seg * kHeadDim + c] = var;
