@@ -413,6 +413,8 @@ def main():
         value = round(w.n_seq * args.steps / (tm["total_ms"] * 1e-3), 1)
     else:
         metric, unit, hib = "decode-attention us/token & effective HBM GB/s (% of peak), one decode step over all layers", "us/token", False
+        if w.name == "llama8b-32layer-n128k":
+            metric = "decode-attention \u00b5s/token & effective HBM GB/s (% of peak) at 128K, 8B-shape"
         value = round(ms_mean * 1e3 / w.n_seq, 3)
     result = {
         "metric": metric,
