@@ -350,8 +350,9 @@ def dequantize(codes, scale, zero) -> np.ndarray:
     evaluation is exact and the one rounding to fp32 is that of the fused
     multiply-add.
     """
-    return (np.asarray(codes, np.float64) * np.float64(np.float16(scale))
-            + np.float64(np.float16(zero))).astype(np.float32)
+    s64 = np.asarray(scale, np.float16).astype(np.float64)
+    z64 = np.asarray(zero, np.float16).astype(np.float64)
+    return (np.asarray(codes, np.float64) * s64 + z64).astype(np.float32)
 
 
 # --------------------------------------------------------------------------

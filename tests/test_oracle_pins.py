@@ -320,6 +320,35 @@ def test_group_allocation_pools_the_budget():
                           O.lagrangian_allocate(np.concatenate(costs[1:]), B)[0])
 
 
+def test_unit_cost_is_rounded_once_to_fp32():
+    """c_u = fl32(w_u * sigma_u) with both factors fp32: the one rounding that
+    makes lambda* and the bits unique.  w1*s1 = 1 + 2^-22 + 2^-46 rounds to
+    1 + 2^-22 = w2*s2, so the two units tie and a 2-bit budget (one step for
+    one unit) leaves both at 0 bits (ties stay at the lower bitwidth).  With
+    an unrounded fp64 product the first unit would be strictly dearer and
+    take the 2 bits alone."""
+    e = np.float32(2.0 ** -23)
+    w = np.array([1 + e, np.float32(1 + 2 * e)], np.float32)
+    s = np.array([1 + e, 1.0], np.float32)
+    c = O.unit_costs(w, s)
+    assert c.dtype == np.float32
+    assert c[0] == c[1] == np.float32(1 + 2.0 ** -22)
+    assert Fraction(float(w[0])) * Fraction(float(s[0])) > Fraction(float(w[1])) * Fraction(float(s[1]))
+    bits, lam = O.lagrangian_allocate(c, 2)
+    assert list(bits) == [0, 0] and lam == float(c[0]) * 3 / 8
+    # the same through the whole segment allocation (V problem)
+    K = np.zeros((2, 128), np.float16)
+    a = O.allocate_segment(w, s, np.ones(128, np.float32), K, 2, 0)
+    assert list(a["bits_tok"]) == [0, 0]
+    # and the rounding is to nearest, not truncation: a product just above a
+    # half ulp rounds up
+    x = np.float32(1 + 2.0 ** -12)
+    y = np.float32(1 + 2.0 ** -12 + 2.0 ** -23)
+    ex = Fraction(float(x)) * Fraction(float(y))          # 1 + 2^-11 + 2^-23 + 2^-24 + 2^-35
+    assert O.unit_costs(np.array([x]), np.array([y]))[0] == np.float32(1 + 2.0 ** -11 + 2.0 ** -22)
+    assert ex > Fraction(1) + Fraction(1, 2 ** 11) + Fraction(1, 2 ** 23) + Fraction(1, 2 ** 24)
+
+
 def test_allocation_special_cases():
     c = np.array([1.0, 2.0, 0.5, 3.0], np.float32)
     assert list(O.lagrangian_allocate(c, 64)[0]) == [16] * 4          # budget covers all 16
@@ -404,6 +433,30 @@ def test_dequantize_is_single_rounding_fma():
         else:
             ref = -O.round_rational_to_f32((-ex).numerator, (-ex).denominator)
         assert got[i] == ref
+
+
+def test_oracle_decode_path_emits_no_numpy_deprecation_warnings():
+    """Every shape the decode path hands to dequantize (one row, a column of
+    per-row scales) stays on supported numpy idioms, so a numpy release that
+    turns today's deprecations into errors cannot break the oracle."""
+    import warnings
+    r = _rng(33)
+    with warnings.catch_warnings(record=True) as caught:
+        warnings.simplefilter("always")
+        for shape in [(1,), (1, 1), (5, 1), ()]:
+            s = np.asarray(np.abs(r.standard_normal(shape)) + 0.1, np.float16)
+            z = np.asarray(r.standard_normal(shape), np.float16)
+            O.dequantize(r.integers(0, 4, shape[:1] + (3,) if shape else (3,)), s, z)
+        lay = O.Layout(1, 1, 2, 1, 128, 20, 40, 64, 2)
+        K, V = r.standard_normal((2, 20, 128)).astype(np.float16)
+        bt = np.array([2] * 10 + [0] * 10, np.uint8)
+        bc = np.array([2] * 32 + [0] * 96, np.uint8)
+        blob = O.pack_cache(lay, K[None, None, None], V[None, None, None], bt[None, None, None], bc[None, None, None])
+        O.decode_step(blob, lay, r.standard_normal((1, 1, 2, 128)).astype(np.float16), 0,
+                      r.standard_normal((1, 1, 1, 128)).astype(np.float16),
+                      r.standard_normal((1, 1, 1, 128)).astype(np.float16))
+    dep = [w for w in caught if issubclass(w.category, DeprecationWarning)]
+    assert not dep, [str(w.message) for w in dep]
 
 
 def test_pack_codes_bit_order():
