@@ -94,6 +94,7 @@ const char* rdkv_status_string(rdkv_status s) {
     case RDKV_ERR_WORKSPACE: return "buffer too small";
     case RDKV_ERR_CAPACITY: return "zone C capacity exceeded";
     case RDKV_ERR_HIP: return "HIP runtime error";
+    case RDKV_ERR_OVERFLOW: return "allocation exceeds the layout's budget bounds";
   }
   return "unknown status";
 }
@@ -286,6 +287,16 @@ rdkv_status rdkv_pack(const rdkv_layout* layout, int32_t layer_begin, int32_t n_
   p.bits_tok = bits_tok;
   p.bits_chan = bits_chan;
   return hip_status(launch_pack(p, stream));
+}
+
+rdkv_status rdkv_pack_status(const rdkv_layout* layout, const void* cache, size_t cache_bytes, int32_t* n_dropped,
+                             hipStream_t stream) {
+  rdkv_status st = check_layout(layout);
+  if (st != RDKV_OK) return st;
+  if (!cache || !n_dropped) return RDKV_ERR_NULL;
+  if (!aligned16(cache)) return RDKV_ERR_ALIGN;
+  if (cache_bytes < layout->cache_bytes) return RDKV_ERR_WORKSPACE;
+  return hip_status(launch_pack_status(static_cast<const uint8_t*>(cache), layout->n_seg, n_dropped, stream));
 }
 
 rdkv_status rdkv_decode_partials(const rdkv_layout* layout, void* cache, size_t cache_bytes, int32_t c_len,

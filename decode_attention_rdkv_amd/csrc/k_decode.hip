@@ -138,6 +138,15 @@ __device__ inline SegInfo load_segment(const DecodeParams& p, int64_t seg) {
   for (int i = 0; i < 4; ++i)
     ok = ok && s.off_v[i] + uint64_t(s.n_tok[i]) * (kHeadDim * group_bits(i) / 8) <= p.cache_bytes;
   ok = ok && s.off_krec + uint64_t(n_kept) * rec <= p.cache_bytes;
+  // the layout sized the chunk slots for sum_g n_g 2^g <= min(B_V / 2, 8 N); a
+  // descriptor with more chunks than its slots would leave chunks unlaunched
+  int n_chunks = int((p.n_c + kChunkRowsC - 1) / kChunkRowsC);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int T = chunk_tokens(p.chunk_tok2, i);
+    n_chunks += (max(s.n_tok[i], 0) + T - 1) / T;
+  }
+  ok = ok && n_chunks <= p.max_chunks;
   if (!ok) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) s.n_tok[i] = s.n_chan[i] = 0;

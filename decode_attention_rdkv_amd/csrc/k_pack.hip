@@ -11,6 +11,8 @@
 // Quantizer, bit-exact with the format specification: zero = fp16 min,
 // scale = fp16_rne(fl32(fl32(max - min) / (2^b - 1))),
 // q = clamp(rint_even(fl32(fl32(x - zero) / scale)), 0, 2^b - 1), scale 0 -> q 0.
+#include <algorithm>
+
 #include "rdkv_internal.h"
 
 namespace rdkv {
@@ -25,6 +27,7 @@ struct SegGeom {
   int64_t n_tok_total;   // N
   int64_t nk_max;
   int64_t v_reserve;
+  int64_t v_units;       // bound on sum_g n_g 2^g: min(B_V / 2, 8 N) (decode's chunk count follows from it)
   int32_t cap, rec_max;
 };
 
@@ -102,6 +105,7 @@ SegGeom geom_of(const rdkv_layout& lay) {
   g.n_tok_total = lay.dims.n_tokens;
   g.nk_max = lay.nk_max;
   g.v_reserve = int64_t(lay.slot_off_krec - lay.slot_off_v);
+  g.v_units = std::min<int64_t>(lay.budget_v / 2, 8 * lay.dims.n_tokens);
   g.cap = lay.zone_c_capacity;
   g.rec_max = lay.rec_max;
   return g;
@@ -182,7 +186,10 @@ __global__ __launch_bounds__(kIndexThreads) void pack_index_kernel(IndexArgs a) 
     vbytes += uint64_t(n_tok[i]) * (kHeadDim * group_bits(i) / 8);
   }
   const RecordShape rs = record_shape(n_chan[0], n_chan[1], n_chan[2], n_chan[3]);
-  const bool fits = n_kept <= a.g.nk_max && int64_t(vbytes) <= a.g.v_reserve && 4 * rs.words_a() <= a.g.rec_max;
+  // a g-group token costs 2^(g+1) bits, so sum_b b_t <= B_V gives sum_g n_g 2^g <= B_V / 2
+  const int64_t v_units = int64_t(n_tok[0]) + 2 * int64_t(n_tok[1]) + 4 * int64_t(n_tok[2]) + 8 * int64_t(n_tok[3]);
+  const bool fits = n_kept <= a.g.nk_max && int64_t(vbytes) <= a.g.v_reserve && v_units <= a.g.v_units &&
+                    4 * rs.words_a() <= a.g.rec_max;
   if (!fits) {
     const int z[4] = {0, 0, 0, 0};
     write_descriptor(a.cache, seg, a.g, z, z, 1, nullptr, tid, kIndexThreads);
@@ -466,7 +473,28 @@ __global__ __launch_bounds__(256) void unpack_kernel(UnpackArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ status
+
+// out[0] = number of segments whose descriptor carries the "did not fit"
+// flag (bit 0): their allocation exceeded the layout's bounds and they were
+// packed empty.  One workgroup; a fixed-order reduction.
+__global__ __launch_bounds__(256) void pack_status_kernel(const uint8_t* cache, int64_t n_seg, int32_t* out) {
+  __shared__ int s_part[4];
+  int n = 0;
+  for (int64_t seg = threadIdx.x; seg < n_seg; seg += 256)
+    n += *reinterpret_cast<const int32_t*>(cache + kHeaderBytes + uint64_t(seg) * kDescBytes + kDescFlags) & 1;
+  n = wave_sum_i(n);
+  if ((threadIdx.x & 63) == 0) s_part[threadIdx.x >> 6] = n;
+  __syncthreads();
+  if (threadIdx.x == 0) out[0] = s_part[0] + s_part[1] + s_part[2] + s_part[3];
+}
+
 }  // namespace
+
+hipError_t launch_pack_status(const uint8_t* cache, int64_t n_seg, int32_t* out, hipStream_t stream) {
+  hipLaunchKernelGGL(pack_status_kernel, dim3(1), dim3(256), 0, stream, cache, n_seg, out);
+  return hipGetLastError();
+}
 
 hipError_t launch_cache_init(uint8_t* cache, const rdkv_layout& lay, hipStream_t stream) {
   const uint64_t n16 = lay.cache_bytes / 16;

@@ -147,6 +147,7 @@ struct PackParams {
 };
 hipError_t launch_cache_init(uint8_t* cache, const rdkv_layout& lay, hipStream_t stream);
 hipError_t launch_pack(const PackParams& p, hipStream_t stream);
+hipError_t launch_pack_status(const uint8_t* cache, int64_t n_seg, int32_t* out, hipStream_t stream);
 hipError_t launch_unpack(const uint8_t* cache, uint64_t cache_bytes, const rdkv_layout& lay, int64_t seg,
                          float* k_hat, float* v_hat, hipStream_t stream);
 

@@ -38,7 +38,8 @@ class Layout(ctypes.Structure):
 
 
 STATUS = ["RDKV_OK", "RDKV_ERR_NULL", "RDKV_ERR_SHAPE", "RDKV_ERR_UNSUPPORTED", "RDKV_ERR_BUDGET",
-          "RDKV_ERR_ALIGN", "RDKV_ERR_WORKSPACE", "RDKV_ERR_CAPACITY", "RDKV_ERR_HIP"]
+          "RDKV_ERR_ALIGN", "RDKV_ERR_WORKSPACE", "RDKV_ERR_CAPACITY", "RDKV_ERR_HIP", "RDKV_ERR_OVERFLOW"]
+RDKV_ERR_OVERFLOW = 9
 
 # exported symbol -> (restype, argtypes)
 SIGNATURES = {
@@ -56,6 +57,7 @@ SIGNATURES = {
                                      c_vp, c_vp, c_vp]),
     "rdkv_cache_init": (c_i32, [ctypes.POINTER(Layout), c_vp, ctypes.c_size_t, c_vp]),
     "rdkv_pack": (c_i32, [ctypes.POINTER(Layout), c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, ctypes.c_size_t, c_vp]),
+    "rdkv_pack_status": (c_i32, [ctypes.POINTER(Layout), c_vp, ctypes.c_size_t, c_vp, c_vp]),
     "rdkv_decode": (c_i32, [ctypes.POINTER(Layout), c_vp, ctypes.c_size_t, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp,
                             ctypes.c_size_t, c_vp]),
     "rdkv_decode_partials": (c_i32, [ctypes.POINTER(Layout), c_vp, ctypes.c_size_t, c_i32, c_vp, c_vp, c_vp, c_vp,
@@ -238,8 +240,13 @@ def cache_init(lay: Layout, cache: Optional[torch.Tensor] = None, device="cuda")
     return cache
 
 
-def pack(lay: Layout, cache: torch.Tensor, K, V, bits_tok, bits_chan, layer_begin: int = 0):
-    """Quantize and pack layers [layer_begin, layer_begin + K.shape[1]) into the cache."""
+def pack(lay: Layout, cache: torch.Tensor, K, V, bits_tok, bits_chan, layer_begin: int = 0, check: bool = True):
+    """Quantize and pack layers [layer_begin, layer_begin + K.shape[1]) into the cache.
+
+    With `check` (the default), waits for the stream and raises
+    RdkvError(RDKV_ERR_OVERFLOW) if any segment of the cache was packed empty
+    because its allocation exceeded the layout's budgets (rdkv_pack_status).
+    """
     d = lay.dims
     S, Lin, Hk, N = d.n_seq, K.shape[1], d.n_kv_heads, d.n_tokens
     _check(load().rdkv_pack(ctypes.byref(lay), layer_begin, Lin,
@@ -249,6 +256,19 @@ def pack(lay: Layout, cache: torch.Tensor, K, V, bits_tok, bits_chan, layer_begi
                             _ptr(bits_chan, torch.uint8, (S, Lin, Hk, HEAD_DIM), "bits_chan"),
                             _ptr(cache, torch.uint8, None, "cache"), cache.numel(), _stream()),
            "rdkv_pack")
+    if check:
+        n = pack_status(lay, cache).item()
+        if n:
+            raise RdkvError(RDKV_ERR_OVERFLOW, f"rdkv_pack: {n} segment(s) exceed the layout's budgets and were "
+                                               f"packed empty")
+
+
+def pack_status(lay: Layout, cache: torch.Tensor) -> torch.Tensor:
+    """Device int32[1]: segments packed empty because their allocation did not fit."""
+    out = torch.empty(4, dtype=torch.int32, device=cache.device)
+    _check(load().rdkv_pack_status(ctypes.byref(lay), _ptr(cache, torch.uint8, None, "cache"), cache.numel(),
+                                   out.data_ptr(), _stream()), "rdkv_pack_status")
+    return out[:1]
 
 
 def decode_workspace(lay: Layout, device="cuda") -> torch.Tensor:

@@ -46,7 +46,9 @@ typedef enum rdkv_status {
   RDKV_ERR_ALIGN = 5,        /* a device pointer is not 16-byte aligned              */
   RDKV_ERR_WORKSPACE = 6,    /* a workspace or cache buffer is smaller than required */
   RDKV_ERR_CAPACITY = 7,     /* zone C has no room for the requested rows            */
-  RDKV_ERR_HIP = 8           /* a HIP runtime call failed                            */
+  RDKV_ERR_HIP = 8,          /* a HIP runtime call failed                            */
+  RDKV_ERR_OVERFLOW = 9      /* an allocation exceeded the layout's budget bounds     */
+                             /* (reported by the binding from rdkv_pack_status)       */
 } rdkv_status;
 
 /* Shapes.  Q is [S][L][Hq][N][d], K and V are [S][L][Hkv][N][d]. */
@@ -178,14 +180,27 @@ rdkv_status rdkv_allocate_shared(const rdkv_dims* dims, const float* w_tok, cons
  * channel dropped).  The allocation must respect the layout's budgets (per
  * segment, sum of bits_tok <= budget_v and sum of bits_chan <= budget_k); a
  * segment whose allocation does not fit its slot is written empty with bit 0
- * of its descriptor's flags word set, never past its slot.  Zone C of every
- * packed segment is cleared. */
+ * of its descriptor's flags word set, never past its slot; rdkv_pack_status
+ * counts such segments.  Zone C of every packed segment is cleared. */
 rdkv_status rdkv_cache_init(const rdkv_layout* layout, void* cache, size_t cache_bytes,
                             hipStream_t stream);
 rdkv_status rdkv_pack(const rdkv_layout* layout, int32_t layer_begin, int32_t n_layers,
                       const void* K, const void* V, const uint8_t* bits_tok,
                       const uint8_t* bits_chan, void* cache, size_t cache_bytes,
                       hipStream_t stream);
+
+/* How many segments of the cache were packed empty because their allocation
+ * did not fit the layout (descriptor flag bit 0): more kept tokens than
+ * nk_max, V payload or V units (sum over kept tokens of b_t / 2) above what
+ * budget_v bounds, or a K record longer than rec_max -- section 2.2's
+ * "sum_u b_u <= B" violated for the layout's B.  rdkv_pack cannot report this
+ * itself without waiting for the device; this call enqueues one small kernel
+ * that writes the count to n_dropped (device int32[1], caller-owned), which
+ * the caller reads once the stream has reached it.  Errors: RDKV_ERR_NULL,
+ * _ALIGN (cache), _WORKSPACE (cache_bytes below the layout's), _SHAPE (a
+ * layout rdkv_layout_init did not produce). */
+rdkv_status rdkv_pack_status(const rdkv_layout* layout, const void* cache, size_t cache_bytes,
+                             int32_t* n_dropped, hipStream_t stream);
 
 /* ---------------------------------------------------------------- decode
  * One decode step over every segment of the cache (section 2.3: fused

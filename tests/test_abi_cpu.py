@@ -14,7 +14,7 @@ from decode_attention_rdkv_amd import rdkv
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "rdkv.h")
 
-OK, NULL, SHAPE, UNSUP, BUDGET, ALIGN, WORKSPACE, CAPACITY, HIP = range(9)
+OK, NULL, SHAPE, UNSUP, BUDGET, ALIGN, WORKSPACE, CAPACITY, HIP, OVERFLOW = range(10)
 
 
 @pytest.fixture(scope="module")
@@ -31,8 +31,9 @@ def test_every_declared_entry_point_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for s in range(9):
-        assert lib.rdkv_status_string(s)
+    for s in range(10):
+        assert lib.rdkv_status_string(s) != b"unknown status"
+    assert lib.rdkv_status_string(10) == b"unknown status"
     assert lib.rdkv_version() >> 16 == O.VERSION
 
 
@@ -151,6 +152,11 @@ def test_cache_pack_decode_validation(lib):
     assert lib.rdkv_pack(ctypes.byref(lay), -1, 1, A, A, A, A, A, nb, None) == SHAPE
     assert lib.rdkv_pack(ctypes.byref(lay), 0, 0, A, A, A, A, A, nb, None) == SHAPE
     assert lib.rdkv_pack(ctypes.byref(lay), 0, 1, A, A, None, A, A, nb, None) == NULL
+    # pack status
+    assert lib.rdkv_pack_status(ctypes.byref(lay), A, nb, None, None) == NULL
+    assert lib.rdkv_pack_status(ctypes.byref(lay), A + 4, nb, A, None) == ALIGN
+    assert lib.rdkv_pack_status(ctypes.byref(lay), A, nb - 1, A, None) == WORKSPACE
+    assert lib.rdkv_pack_status(ctypes.byref(bad), A, nb, A, None) == SHAPE
     # decode: zone-C capacity, append pair, workspace
     assert lib.rdkv_decode(ctypes.byref(lay), A, nb, 4, A, A, A, A, A, ws, None) == CAPACITY
     assert lib.rdkv_decode(ctypes.byref(lay), A, nb, 5, A, None, None, A, A, ws, None) == CAPACITY
