@@ -53,18 +53,19 @@ DecodeParams base_params(const rdkv_layout* layout, void* cache, int n_c, int c_
   return p;
 }
 
-// Validation shared by rdkv_decode and rdkv_decode_partials.
+// Validation shared by the decode entry points.  With own_workspace (the
+// library's static scratch, set by the caller afterwards) the workspace
+// arguments are not checked.
 rdkv_status decode_params(const rdkv_layout* layout, void* cache, size_t cache_bytes, int32_t c_len, const void* q,
                           const void* k_new, const void* v_new, void* workspace, size_t workspace_bytes,
-                          DecodeParams* out) {
+                          DecodeParams* out, bool own_workspace = false) {
   rdkv_status st = check_layout(layout);
   if (st != RDKV_OK) return st;
-  if (!cache || !q || !workspace) return RDKV_ERR_NULL;
+  if (!cache || !q || (!workspace && !own_workspace)) return RDKV_ERR_NULL;
   if ((k_new == nullptr) != (v_new == nullptr)) return RDKV_ERR_NULL;
-  for (const void* ptr : {(const void*)cache, q, (const void*)workspace})
-    if (!aligned16(ptr)) return RDKV_ERR_ALIGN;
+  if (!aligned16(cache) || !aligned16(q) || (!own_workspace && !aligned16(workspace))) return RDKV_ERR_ALIGN;
   if (k_new && (!aligned16(k_new) || !aligned16(v_new))) return RDKV_ERR_ALIGN;
-  if (cache_bytes < layout->cache_bytes || workspace_bytes < layout->decode_workspace_bytes)
+  if (cache_bytes < layout->cache_bytes || (!own_workspace && workspace_bytes < layout->decode_workspace_bytes))
     return RDKV_ERR_WORKSPACE;
   const int append = k_new != nullptr;
   if (c_len < 0 || int64_t(c_len) + append > layout->zone_c_capacity) return RDKV_ERR_CAPACITY;
@@ -334,6 +335,27 @@ rdkv_status rdkv_decode(const rdkv_layout* layout, void* cache, size_t cache_byt
   if (st != RDKV_OK) return st;
   if (!out) return RDKV_ERR_NULL;
   if (!aligned16(out)) return RDKV_ERR_ALIGN;
+  p.out = out;
+  hipError_t e = launch_decode_chunks(p, stream);
+  if (e == hipSuccess) e = launch_decode_merge(p, stream);
+  return hip_status(e);
+}
+
+rdkv_status rdkv_decode_static(const rdkv_layout* layout, void* cache, size_t cache_bytes, int32_t c_len,
+                               const void* q, const void* k_new, const void* v_new, float* out,
+                               hipStream_t stream) {
+  rdkv_status st = check_layout(layout);
+  if (st != RDKV_OK) return st;
+  if (layout->decode_workspace_bytes > kStaticScratchBytes) return RDKV_ERR_WORKSPACE;
+  if (!out) return RDKV_ERR_NULL;
+  if (!aligned16(out)) return RDKV_ERR_ALIGN;
+  // every argument is validated before the device is touched
+  DecodeParams p;
+  st = decode_params(layout, cache, cache_bytes, c_len, q, k_new, v_new, nullptr, 0, &p, true);
+  if (st != RDKV_OK) return st;
+  void* scratch = nullptr;
+  if (static_scratch(&scratch) != hipSuccess) return RDKV_ERR_HIP;
+  p.partials = static_cast<float*>(scratch);
   p.out = out;
   hipError_t e = launch_decode_chunks(p, stream);
   if (e == hipSuccess) e = launch_decode_merge(p, stream);

@@ -133,6 +133,10 @@ struct DecodeParams {
   float* out;              // [n_seg][G][128]
 };
 hipError_t launch_decode_chunks(const DecodeParams& p, hipStream_t stream);
+// Device address (on the current device) of the library-owned decode scratch
+// of kStaticScratchBytes bytes used by rdkv_decode_static.
+constexpr uint64_t kStaticScratchBytes = RDKV_STATIC_SCRATCH_BYTES;
+hipError_t static_scratch(void** out);
 hipError_t launch_decode_merge(const DecodeParams& p, hipStream_t stream);
 
 struct PackParams {

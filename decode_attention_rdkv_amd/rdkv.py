@@ -60,6 +60,8 @@ SIGNATURES = {
     "rdkv_pack_status": (c_i32, [ctypes.POINTER(Layout), c_vp, ctypes.c_size_t, c_vp, c_vp]),
     "rdkv_decode": (c_i32, [ctypes.POINTER(Layout), c_vp, ctypes.c_size_t, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp,
                             ctypes.c_size_t, c_vp]),
+    "rdkv_decode_static": (c_i32, [ctypes.POINTER(Layout), c_vp, ctypes.c_size_t, c_i32, c_vp, c_vp, c_vp, c_vp,
+                                   c_vp]),
     "rdkv_decode_partials": (c_i32, [ctypes.POINTER(Layout), c_vp, ctypes.c_size_t, c_i32, c_vp, c_vp, c_vp, c_vp,
                                      ctypes.c_size_t, c_vp]),
     "rdkv_decode_merge": (c_i32, [ctypes.POINTER(Layout), c_vp, ctypes.c_size_t, c_i32, c_vp, c_vp, ctypes.c_size_t,
@@ -291,6 +293,27 @@ def decode(lay: Layout, cache: torch.Tensor, c_len: int, q, k_new=None, v_new=No
                               _ptr(out, torch.float32, (S, L, Hq, HEAD_DIM), "out"),
                               _ptr(workspace, torch.uint8, None, "workspace"), workspace.numel(), _stream()),
            "rdkv_decode")
+    return out
+
+
+STATIC_SCRATCH_BYTES = 64 << 20
+
+
+def decode_static(lay: Layout, cache: torch.Tensor, c_len: int, q, k_new=None, v_new=None,
+                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """rdkv_decode_static: one decode step with the library's own device
+    scratch instead of a workspace (the C call allocates nothing; pass `out`
+    to keep this wrapper from allocating it)."""
+    d = lay.dims
+    S, L, Hq, Hk = d.n_seq, d.n_layers, d.n_q_heads, d.n_kv_heads
+    if out is None:
+        out = torch.empty((S, L, Hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+    _check(load().rdkv_decode_static(ctypes.byref(lay), _ptr(cache, torch.uint8, None, "cache"), cache.numel(), c_len,
+                                     _ptr(q, torch.float16, (S, L, Hq, HEAD_DIM), "q"),
+                                     _ptr(k_new, torch.float16, (S, L, Hk, HEAD_DIM), "k_new"),
+                                     _ptr(v_new, torch.float16, (S, L, Hk, HEAD_DIM), "v_new"),
+                                     _ptr(out, torch.float32, (S, L, Hq, HEAD_DIM), "out"), _stream()),
+           "rdkv_decode_static")
     return out
 
 

@@ -220,6 +220,23 @@ rdkv_status rdkv_decode(const rdkv_layout* layout, void* cache, size_t cache_byt
                         const void* q, const void* k_new, const void* v_new, float* out,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* rdkv_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): no
+ * workspace argument; the split-K partials go to a library-owned device array
+ * of RDKV_STATIC_SCRATCH_BYTES bytes per GPU, part of the library's code
+ * object and held by every GPU the library runs on until the process ends.
+ * Results are those of rdkv_decode, bit for bit (same kernels).  Allocates
+ * nothing: the first call on a device only looks up that device's array
+ * address.  Every call on one GPU uses the same array, so calls that overlap
+ * on one GPU (other streams, or other host threads without ordering) race;
+ * nothing in the array needs to start at zero.  Errors: as rdkv_decode, and
+ * RDKV_ERR_WORKSPACE when layout->decode_workspace_bytes exceeds
+ * RDKV_STATIC_SCRATCH_BYTES. */
+#define RDKV_STATIC_SCRATCH_BYTES (64u << 20)
+rdkv_status rdkv_decode_static(const rdkv_layout* layout, void* cache, size_t cache_bytes, int32_t c_len,
+                               const void* q, const void* k_new, const void* v_new, float* out,
+                               hipStream_t stream);
+
 /* The two split-K phases of rdkv_decode, for callers that time them, or that
  * exchange the per-chunk partials between devices before merging.
  *

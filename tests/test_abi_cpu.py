@@ -179,6 +179,29 @@ def test_two_phase_decode_validation(lib):
     assert lib.rdkv_decode_merge(ctypes.byref(lay), A, nb, 0, A + 4, A, ws, None) == ALIGN
 
 
+def test_static_decode_validation(lib):
+    """rdkv_decode_static validates like rdkv_decode (minus the workspace) and
+    refuses layouts whose split-K partials exceed its static scratch, all
+    before touching the device."""
+    lay = rdkv.layout(_dims(n_layers=2), 64, 32, 4)
+    nb = lay.cache_bytes
+    assert lay.decode_workspace_bytes <= rdkv.STATIC_SCRATCH_BYTES
+    assert lib.rdkv_decode_static(ctypes.byref(lay), A, nb, 4, A, A, A, A, None) == CAPACITY
+    assert lib.rdkv_decode_static(ctypes.byref(lay), A, nb, -1, A, None, None, A, None) == CAPACITY
+    assert lib.rdkv_decode_static(ctypes.byref(lay), A, nb, 0, A, A, None, A, None) == NULL
+    assert lib.rdkv_decode_static(ctypes.byref(lay), A, nb, 0, A, None, None, None, None) == NULL
+    assert lib.rdkv_decode_static(ctypes.byref(lay), None, nb, 0, A, None, None, A, None) == NULL
+    assert lib.rdkv_decode_static(ctypes.byref(lay), A, nb, 0, A + 8, None, None, A, None) == ALIGN
+    assert lib.rdkv_decode_static(ctypes.byref(lay), A, nb, 0, A, None, None, A + 4, None) == ALIGN
+    assert lib.rdkv_decode_static(ctypes.byref(lay), A, nb - 1, 0, A, None, None, A, None) == WORKSPACE
+    big = rdkv.layout(rdkv.make_dims(8, 80, 64, 8, 262144), 524288, 256, 128)
+    assert big.decode_workspace_bytes > rdkv.STATIC_SCRATCH_BYTES
+    assert lib.rdkv_decode_static(ctypes.byref(big), A, big.cache_bytes, 0, A, None, None, A, None) == WORKSPACE
+    # the largest workload's partials fit
+    c5 = rdkv.layout(rdkv.make_dims(1, 80, 64, 8, 262144), 524288, 256, 128)
+    assert c5.decode_workspace_bytes <= rdkv.STATIC_SCRATCH_BYTES
+
+
 def test_decode_byte_accounting_against_the_oracle_blob():
     """The benchmark's algorithmic bytes per decode step (read from the
     descriptors) equal the oracle's count of payload bits plus one
