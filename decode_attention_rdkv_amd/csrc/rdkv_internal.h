@@ -16,7 +16,7 @@ namespace rdkv {
 constexpr int kHeadDim = 128;
 constexpr int64_t kMaxTokens = int64_t(1) << 19;   // prefill tokens per sequence
 constexpr uint32_t kMagic = 0x564B4452u;  // "RDKV" little-endian
-constexpr int kFormatVersion = 1;
+constexpr int kFormatVersion = 2;
 constexpr int kHeaderBytes = 256;
 constexpr int kDescBytes = 256;
 constexpr int kAlign = 256;

@@ -54,7 +54,7 @@ STEP_BITS = np.array([b1 - b0 for b0, b1 in zip(_STEP_FROM, _STEP_TO)], dtype=np
 STEP_SLOPE = np.array([(2.0 ** -b0 - 2.0 ** -b1) / (b1 - b0) for b0, b1 in zip(_STEP_FROM, _STEP_TO)])
 
 MAGIC = 0x564B4452            # "RDKV" little-endian
-VERSION = 1
+VERSION = 2
 HEADER_BYTES = 256
 DESC_BYTES = 256
 ALIGN = 256
@@ -377,10 +377,17 @@ class Layout:
     2/4/8-bit code rows then fp16 rows, each group 256-byte aligned), the
     per-token K records and the int32 original positions of kept tokens.
     Region sizes are bounds that follow from the budgets alone.
+
+    With n_generations > 0 the blob also reserves that many generation blobs,
+    each a complete blob of this same format (own header, descriptors, slots;
+    offsets relative to its own start) for cap tokens per segment, the
+    generation budgets, and no zone C: zone C rolls over into the next one
+    when it fills (see rollover_pack).  They follow the main blob at
+    gen_offset, gen_bytes apart.
     """
 
     def __init__(self, n_seq, n_layers, n_q_heads, n_kv_heads, head_dim, n_tokens,
-                 budget_v, budget_k, zone_c_capacity):
+                 budget_v, budget_k, zone_c_capacity, n_generations=0, gen_budget_v=0, gen_budget_k=0):
         if head_dim != D:
             raise ValueError("head_dim must be 128")
         self.S, self.L, self.Hq, self.Hkv = n_seq, n_layers, n_q_heads, n_kv_heads
@@ -400,6 +407,21 @@ class Layout:
         self.desc_offset = HEADER_BYTES
         self.slots_offset = _align(HEADER_BYTES + DESC_BYTES * self.n_seg)
         self.cache_bytes = self.slots_offset + self.n_seg * self.slot_bytes
+        self.n_gen = n_generations
+        self.gen_budget_v, self.gen_budget_k = gen_budget_v, gen_budget_k
+        self.gen = None
+        self.gen_offset = self.gen_bytes = 0
+        if n_generations > 0:
+            if zone_c_capacity < 1:
+                raise ValueError("generations need a zone C to roll over")
+            self.gen = Layout(n_seq, n_layers, n_q_heads, n_kv_heads, head_dim, zone_c_capacity,
+                              gen_budget_v, gen_budget_k, 0)
+            self.gen_offset = self.cache_bytes
+            self.gen_bytes = _align(self.gen.cache_bytes)
+            self.cache_bytes = self.gen_offset + n_generations * self.gen_bytes
+
+    def gen_base(self, g):
+        return self.gen_offset + g * self.gen_bytes
 
     def seg_index(self, s, l, h):
         return (s * self.L + l) * self.Hkv + h
@@ -414,6 +436,10 @@ class Layout:
         i64 = [self.N, self.budget_v, self.budget_k, self.n_seg, self.desc_offset,
                self.slots_offset, self.slot_bytes]
         h[32:88] = np.array(i64, np.int64).view(np.uint8)
+        # generations: count reserved, count in use (0 until a rollover), where
+        h[88:96] = np.array([self.n_gen, 0], np.int32).view(np.uint8)
+        h[96:128] = np.array([self.gen_offset, self.gen_bytes, self.gen_budget_v, self.gen_budget_k],
+                             np.int64).view(np.uint8)
         return h.tobytes()
 
 
@@ -550,13 +576,28 @@ def pack_segment(lay: Layout, blob: np.ndarray, seg: int, Kh, Vh, bits_tok, bits
 
 
 def empty_blob(lay: Layout) -> np.ndarray:
-    """A cache with every segment empty: header, descriptors with zero counts."""
+    """A cache with every segment empty: header, descriptors with zero counts
+    (and the same for every reserved generation blob)."""
     blob = np.zeros(lay.cache_bytes, np.uint8)
     blob[:HEADER_BYTES] = np.frombuffer(lay.header_bytes(), np.uint8)
     for seg in range(lay.n_seg):
         pack_segment(lay, blob, seg, np.zeros((0, D), np.float16), np.zeros((0, D), np.float16),
                      np.zeros(0, np.uint8), np.zeros(D, np.uint8))
+    if lay.n_gen:
+        empty_gen = empty_blob(lay.gen)
+        for g in range(lay.n_gen):
+            gen_view(blob, lay, g)[:lay.gen.cache_bytes] = empty_gen
     return blob
+
+
+def gen_view(blob, lay: Layout, g: int) -> np.ndarray:
+    """The bytes of generation blob g (a view: writes go to `blob`)."""
+    return blob[lay.gen_base(g):lay.gen_base(g) + lay.gen_bytes]
+
+
+def gens_in_use(blob) -> int:
+    """Generation blobs filled by rollovers so far (header field)."""
+    return int(blob[92:96].view(np.int32)[0])
 
 
 def pack_cache(lay: Layout, K, V, bits_tok, bits_chan, layer_begin: int = 0, blob=None):
@@ -703,15 +744,135 @@ def decode_step(blob, lay: Layout, q, c_len: int, k_new=None, v_new=None):
     return out
 
 
+def kept_rows(blob, lay: Layout, seg: int):
+    """Dequantized K and V rows of every kept token of a segment: the prefill
+    generation, then each rolled-over generation in use, in that order."""
+    Ks, Vs = [], []
+    Kh, Vh, _, _ = unpack_segment(blob, lay, seg)
+    Ks.append(Kh), Vs.append(Vh)
+    for g in range(gens_in_use(blob) if lay.n_gen else 0):
+        Kg, Vg, _, _ = unpack_segment(gen_view(blob, lay, g), lay.gen, seg)
+        Ks.append(Kg), Vs.append(Vg)
+    return np.concatenate(Ks), np.concatenate(Vs)
+
+
 def decode_segment(blob, lay: Layout, seg: int, qg, n_c: int):
     """Attention output [G][d] (float64) of one segment's G query heads over its
-    kept tokens and its first n_c zone-C rows (the per-segment part of
-    decode_step; segments are independent)."""
-    Kh, Vh, _, _ = unpack_segment(blob, lay, seg)
+    kept tokens (every generation) and its first n_c zone-C rows (the
+    per-segment part of decode_step; segments are independent)."""
+    Kh, Vh = kept_rows(blob, lay, seg)
     kc, vc = zone_c_rows(blob, lay, seg, n_c)
     Ka = np.concatenate([Kh, kc])
     Va = np.concatenate([Vh, vc])
     return attention(np.asarray(qg, np.float16).astype(np.float64), Ka, Va)
+
+
+# --------------------------------------------------------------------------
+# Zone-C rollover: decode-time scoring of the new tokens, then allocation and
+# packing into a new generation ([RDKV] 2.3 zone C holds the new tokens;
+# [KVMATH] "Solusi 2": attention accumulated over decode steps, summed over
+# heads, as the importance of a token; [RDKV] 2.1-2.2 for the weights and the
+# allocation)
+# --------------------------------------------------------------------------
+
+def new_zone_c_stats(lay: Layout) -> np.ndarray:
+    """Decode-time statistics of zone C, float64 [n_seg][G][cap + d]: per query
+    head, the attention mass each zone-C row has received so far, then the sum
+    of squares of each query channel over the steps so far."""
+    return np.zeros((lay.n_seg, lay.Hq // lay.Hkv, lay.cap + D))
+
+
+def decode_step_accumulate(blob, lay: Layout, q, c_len: int, k_new, v_new, stats):
+    """decode_step that also accumulates the step into `stats`.
+
+    READING ([RDKV] 2.1 applied to the decode queries, [KVMATH] Solusi 2): the
+    weight of a new token is the attention it receives from every query that
+    sees it -- each decode step's query heads, the token's own step included --
+    taken from the step's softmax over the whole cache (every generation and
+    zone C).  Per head g and zone-C row j < n_c, stats[seg][g][j] gains that
+    softmax probability; stats[seg][g][cap + c] gains q_g[c]^2, the square of
+    the fp16 query value (the query side of the channel weight).
+    Returns out [S][L][Hq][d] like decode_step.
+    """
+    n_c = c_len
+    if k_new is not None:
+        append_zone_c(blob, lay, c_len, k_new, v_new)
+        n_c = c_len + 1
+    G = lay.Hq // lay.Hkv
+    out = np.zeros((lay.S, lay.L, lay.Hq, D))
+    for s in range(lay.S):
+        for l in range(lay.L):
+            for h in range(lay.Hkv):
+                seg = lay.seg_index(s, l, h)
+                qg = np.asarray(q[s, l, h * G:(h + 1) * G], np.float16).astype(np.float64)
+                Kh, Vh = kept_rows(blob, lay, seg)
+                kc, vc = zone_c_rows(blob, lay, seg, n_c)
+                Ka, Va = np.concatenate([Kh, kc]), np.concatenate([Vh, vc])
+                if Ka.shape[0]:
+                    sc = (qg @ Ka.astype(np.float64).T) / math.sqrt(D)
+                    p = np.exp(sc - sc.max(axis=1, keepdims=True))
+                    p /= p.sum(axis=1, keepdims=True)
+                    out[s, l, h * G:(h + 1) * G] = p @ Va.astype(np.float64)
+                    stats[seg, :, :n_c] += p[:, Kh.shape[0]:]
+                stats[seg, :, lay.cap:] += qg * qg
+    return out
+
+
+def rollover_weights(blob, lay: Layout, stats):
+    """Stage-1 weights of the cap zone-C tokens of every segment, from the
+    decode-time statistics ([RDKV] 2.1 with the decode queries in place of the
+    prefill rows):
+      w_tok[seg][j]  = sum over heads of the accumulated attention mass of row j
+      var_tok[seg][j]= population variance of V_C row j (as token_variance)
+      w_chan[seg][c] = ||Q_{:,c}|| ||K_C[:, c]|| / sqrt(d), with ||Q_{:,c}||^2
+                       the accumulated sum of squares over heads and steps
+    Returns float64 arrays [n_seg][cap], [n_seg][cap], [n_seg][d]."""
+    n = lay.n_seg
+    w_tok = stats[:, :, :lay.cap].sum(axis=1)
+    var_tok = np.zeros((n, lay.cap))
+    w_chan = np.zeros((n, D))
+    for seg in range(n):
+        kc, vc = zone_c_rows(blob, lay, seg, lay.cap)
+        var_tok[seg] = token_variance(vc)
+        qn = np.sqrt(stats[seg, :, lay.cap:].sum(axis=0))
+        kn = np.sqrt(np.sum(kc.astype(np.float64) ** 2, axis=0))
+        w_chan[seg] = qn * kn / math.sqrt(D)
+    return w_tok, var_tok, w_chan
+
+
+def rollover_pack(blob, lay: Layout, gen: int, w_tok, var_tok, w_chan):
+    """Roll the full zone C of every segment into generation blob `gen`.
+
+    The cap zone-C tokens of a segment are one more unit set of the problem of
+    [RDKV] 2.1, allocated by the same stages ([RDKV] 2.2: V tokens with the
+    generation's V budget, then K channels over the kept ones with its K
+    budget) from the given fp32 weights (rounded to fp32 here), quantized and
+    packed like the prefill generation ([RDKV] 2.3) into the generation blob,
+    whose descriptors then hold them.  Afterwards zone C is cleared and the
+    header counts gen + 1 generations in use.  Generations are filled in
+    order (gen == generations in use so far).  Returns the per-segment
+    allocations (dicts of allocate_segment).
+    """
+    if not (0 <= gen < lay.n_gen) or gen != gens_in_use(blob):
+        raise ValueError("generation index out of order or beyond the reserved ones")
+    view = gen_view(blob, lay, gen)
+    allocs = []
+    for s in range(lay.S):
+        for l in range(lay.L):
+            for h in range(lay.Hkv):
+                seg = lay.seg_index(s, l, h)
+                kc, vc = zone_c_rows(blob, lay, seg, lay.cap)
+                k16, v16 = kc.astype(np.float16), vc.astype(np.float16)
+                a = allocate_segment(np.asarray(w_tok[seg], np.float32), np.asarray(var_tok[seg], np.float32),
+                                     np.asarray(w_chan[seg], np.float32), k16, lay.gen_budget_v, lay.gen_budget_k)
+                pack_segment(lay.gen, view, seg, k16, v16, a["bits_tok"], a["bits_chan"])
+                allocs.append(a)
+    for seg in range(lay.n_seg):
+        ds = read_descriptor(blob, lay, seg)
+        blob[ds["off_kc"]:ds["off_kc"] + lay.cap * D * 2] = 0
+        blob[ds["off_vc"]:ds["off_vc"] + lay.cap * D * 2] = 0
+    blob[92:96] = np.array([gen + 1], np.int32).view(np.uint8)
+    return allocs
 
 
 # --------------------------------------------------------------------------
