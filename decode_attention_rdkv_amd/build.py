@@ -18,7 +18,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "librdkv.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "k_decode.hip", "k_pack.hip", "k_alloc.hip", "k_score.hip", "scratch.hip"]
+SOURCES = ["api.hip", "k_decode.hip", "k_pack.hip", "k_alloc.hip", "k_score.hip", "k_rollover.hip", "scratch.hip"]
 
 # No fast-math: the quantizer relies on IEEE fp32 division and rounding.
 # Packed fp32 VALU instructions are disabled for device code.

@@ -26,13 +26,27 @@ rdkv_status check_dims(const rdkv_dims* d) {
   return RDKV_OK;
 }
 
+rdkv_status layout_init(const rdkv_dims* dims, int64_t budget_v, int64_t budget_k, int32_t zone_c_capacity,
+                        int32_t n_gen, int64_t gen_budget_v, int64_t gen_budget_k, rdkv_layout* out);
+
 rdkv_status check_layout(const rdkv_layout* lay) {
   if (!lay) return RDKV_ERR_NULL;
   rdkv_layout ref;
-  rdkv_status st = rdkv_layout_init(&lay->dims, lay->budget_v, lay->budget_k, lay->zone_c_capacity, &ref);
+  rdkv_status st = layout_init(&lay->dims, lay->budget_v, lay->budget_k, lay->zone_c_capacity, lay->n_generations,
+                               lay->gen_budget_v, lay->gen_budget_k, &ref);
   if (st != RDKV_OK) return st;
-  if (std::memcmp(&ref, lay, sizeof(ref)) != 0) return RDKV_ERR_SHAPE;  // not from rdkv_layout_init
+  if (std::memcmp(&ref, lay, sizeof(ref)) != 0) return RDKV_ERR_SHAPE;  // not from rdkv_layout_init*
   return RDKV_OK;
+}
+
+// The layout of one generation blob of a rollover layout: the same format
+// for zone_c_capacity tokens per segment, the generation budgets, no zone C.
+rdkv_layout generation_layout(const rdkv_layout& lay) {
+  rdkv_dims d = lay.dims;
+  d.n_tokens = lay.zone_c_capacity;
+  rdkv_layout g;
+  layout_init(&d, lay.gen_budget_v, lay.gen_budget_k, 0, 0, 0, 0, &g);
+  return g;
 }
 
 rdkv_status hip_status(hipError_t e) { return e == hipSuccess ? RDKV_OK : RDKV_ERR_HIP; }
@@ -41,16 +55,46 @@ DecodeParams base_params(const rdkv_layout* layout, void* cache, int n_c, int c_
   DecodeParams p{};
   p.cache = static_cast<uint8_t*>(cache);
   p.cache_bytes = layout->cache_bytes;
+  p.main_bytes = layout->n_generations > 0 ? layout->gen_offset : layout->cache_bytes;
   p.n_seg = layout->n_seg;
   p.nk_max = layout->nk_max;
   p.max_chunks = layout->max_chunks;
+  p.token_slots = layout->token_slots;
   p.chunk_tok2 = layout->chunk_tok2;
   p.rec_max = layout->rec_max;
   p.group = layout->dims.n_q_heads / layout->dims.n_kv_heads;
+  p.zc_cap = layout->zone_c_capacity;
   p.c_len = c_len;
   p.n_c = n_c;
   p.append = append;
+  if (layout->n_generations > 0) {
+    const rdkv_layout g = generation_layout(*layout);
+    p.n_gen = layout->n_generations;
+    p.gen_slots = g.max_chunks;
+    p.gen_chunk_tok2 = g.chunk_tok2;
+    p.gen_rec_max = g.rec_max;
+    p.gen_nk_max = g.nk_max;
+    p.gen_offset = layout->gen_offset;
+    p.gen_bytes = layout->gen_bytes;
+    p.gen_cache_bytes = g.cache_bytes;
+  }
   return p;
+}
+
+RolloverParams rollover_params(const rdkv_layout& lay, void* cache, float* zc_stats) {
+  RolloverParams r{};
+  r.cache = static_cast<uint8_t*>(cache);
+  r.main_bytes = lay.gen_offset;
+  r.n_seg = lay.n_seg;
+  r.G = lay.dims.n_q_heads / lay.dims.n_kv_heads;
+  r.cap = lay.zone_c_capacity;
+  r.n_layers = lay.dims.n_layers;
+  r.gen_offset = lay.gen_offset;
+  r.gen_bytes = lay.gen_bytes;
+  r.gen_budget_v = lay.gen_budget_v;
+  r.gen_budget_k = lay.gen_budget_k;
+  r.stats = zc_stats;
+  return r;
 }
 
 // Validation shared by the decode entry points.  With own_workspace (the
@@ -100,8 +144,12 @@ const char* rdkv_status_string(rdkv_status s) {
   return "unknown status";
 }
 
-rdkv_status rdkv_layout_init(const rdkv_dims* dims, int64_t budget_v, int64_t budget_k,
-                             int32_t zone_c_capacity, rdkv_layout* out) {
+}  // extern "C"
+
+namespace {
+
+rdkv_status layout_init(const rdkv_dims* dims, int64_t budget_v, int64_t budget_k, int32_t zone_c_capacity,
+                        int32_t n_gen, int64_t gen_budget_v, int64_t gen_budget_k, rdkv_layout* out) {
   if (!out) return RDKV_ERR_NULL;
   rdkv_status st = check_dims(dims);
   if (st != RDKV_OK) return st;
@@ -137,11 +185,44 @@ rdkv_status rdkv_layout_init(const rdkv_dims* dims, int64_t budget_v, int64_t bu
   while (t2 < kChunkTok2Max && L.n_seg * v_units / (2 * t2) >= kDecodeTargetChunks) t2 *= 2;
   L.chunk_tok2 = int32_t(t2);
   const int64_t tok_chunks = v_units / t2 + 4;
+  L.token_slots = int32_t(tok_chunks);
   L.max_chunks = int32_t(tok_chunks + cdiv(cap, kChunkRowsC));
   const int G = dims->n_q_heads / dims->n_kv_heads;
+  if (n_gen != 0) {
+    // generation blobs after the main blob, one per rollover of zone C
+    if (n_gen < 0 || n_gen > kMaxGenerations || cap < 1) return RDKV_ERR_SHAPE;
+    if (gen_budget_v < 0 || gen_budget_k < 0) return RDKV_ERR_BUDGET;
+    if (gen_budget_v > (int64_t(1) << 40) || gen_budget_k > (int64_t(1) << 40)) return RDKV_ERR_BUDGET;
+    L.n_generations = n_gen;
+    L.gen_budget_v = gen_budget_v;
+    L.gen_budget_k = gen_budget_k;
+    const rdkv_layout g = generation_layout(L);
+    L.gen_offset = L.cache_bytes;
+    L.gen_bytes = align_up(g.cache_bytes, kAlign);
+    L.cache_bytes = L.gen_offset + uint64_t(n_gen) * L.gen_bytes;
+    L.max_chunks = int32_t(tok_chunks + int64_t(n_gen) * g.max_chunks + cdiv(cap, kChunkRowsC));
+    L.zc_stats_bytes = uint64_t(L.n_seg) * G * (cap + kHeadDim) * sizeof(float);
+    L.rollover_workspace_bytes = rollover_workspace_bytes(L.n_seg, cap);
+  }
   L.decode_workspace_bytes = uint64_t(L.n_seg) * L.max_chunks * G * kPartialFloats * sizeof(float);
   *out = L;
   return RDKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+rdkv_status rdkv_layout_init(const rdkv_dims* dims, int64_t budget_v, int64_t budget_k,
+                             int32_t zone_c_capacity, rdkv_layout* out) {
+  return layout_init(dims, budget_v, budget_k, zone_c_capacity, 0, 0, 0, out);
+}
+
+rdkv_status rdkv_layout_init_rollover(const rdkv_dims* dims, int64_t budget_v, int64_t budget_k,
+                                      int32_t zone_c_capacity, int32_t n_generations, int64_t gen_budget_v,
+                                      int64_t gen_budget_k, rdkv_layout* out) {
+  if (n_generations < 1) return RDKV_ERR_SHAPE;
+  return layout_init(dims, budget_v, budget_k, zone_c_capacity, n_generations, gen_budget_v, gen_budget_k, out);
 }
 
 size_t rdkv_score_workspace_bytes(const rdkv_dims* dims) {
@@ -263,7 +344,11 @@ rdkv_status rdkv_cache_init(const rdkv_layout* layout, void* cache, size_t cache
   if (!cache) return RDKV_ERR_NULL;
   if (!aligned16(cache)) return RDKV_ERR_ALIGN;
   if (cache_bytes < layout->cache_bytes) return RDKV_ERR_WORKSPACE;
-  return hip_status(launch_cache_init(static_cast<uint8_t*>(cache), *layout, stream));
+  if (layout->n_generations > 0) {
+    const rdkv_layout g = generation_layout(*layout);
+    return hip_status(launch_cache_init(static_cast<uint8_t*>(cache), *layout, &g, stream));
+  }
+  return hip_status(launch_cache_init(static_cast<uint8_t*>(cache), *layout, nullptr, stream));
 }
 
 rdkv_status rdkv_pack(const rdkv_layout* layout, int32_t layer_begin, int32_t n_layers,
@@ -360,6 +445,56 @@ rdkv_status rdkv_decode_static(const rdkv_layout* layout, void* cache, size_t ca
   hipError_t e = launch_decode_chunks(p, stream);
   if (e == hipSuccess) e = launch_decode_merge(p, stream);
   return hip_status(e);
+}
+
+rdkv_status rdkv_decode_accumulate(const rdkv_layout* layout, void* cache, size_t cache_bytes, int32_t c_len,
+                                   const void* q, const void* k_new, const void* v_new, float* out,
+                                   float* zc_stats, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream) {
+  DecodeParams p;
+  rdkv_status st = decode_params(layout, cache, cache_bytes, c_len, q, k_new, v_new, workspace, workspace_bytes, &p);
+  if (st != RDKV_OK) return st;
+  if (layout->n_generations < 1) return RDKV_ERR_SHAPE;
+  if (!out || !zc_stats) return RDKV_ERR_NULL;
+  if (!aligned16(out) || !aligned16(zc_stats)) return RDKV_ERR_ALIGN;
+  p.out = out;
+  p.zc_stats = zc_stats;
+  hipError_t e = launch_decode_chunks(p, stream);
+  if (e == hipSuccess) e = launch_decode_merge(p, stream);
+  return hip_status(e);
+}
+
+rdkv_status rdkv_rollover_score(const rdkv_layout* layout, const void* cache, size_t cache_bytes,
+                                const float* zc_stats, float* w_tok, float* var_tok, float* w_chan,
+                                hipStream_t stream) {
+  rdkv_status st = check_layout(layout);
+  if (st != RDKV_OK) return st;
+  if (layout->n_generations < 1) return RDKV_ERR_SHAPE;
+  if (!cache || !zc_stats || !w_tok || !var_tok || !w_chan) return RDKV_ERR_NULL;
+  for (const void* ptr : {cache, (const void*)zc_stats, (const void*)w_tok, (const void*)var_tok, (const void*)w_chan})
+    if (!aligned16(ptr)) return RDKV_ERR_ALIGN;
+  if (cache_bytes < layout->cache_bytes) return RDKV_ERR_WORKSPACE;
+  RolloverParams r = rollover_params(*layout, const_cast<void*>(cache), const_cast<float*>(zc_stats));
+  r.w_tok = w_tok;
+  r.var_tok = var_tok;
+  r.w_chan = w_chan;
+  return hip_status(launch_rollover_score(r, stream));
+}
+
+rdkv_status rdkv_rollover(const rdkv_layout* layout, void* cache, size_t cache_bytes, int32_t generation,
+                          float* zc_stats, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  rdkv_status st = check_layout(layout);
+  if (st != RDKV_OK) return st;
+  if (layout->n_generations < 1) return RDKV_ERR_SHAPE;
+  if (!cache || !zc_stats || !workspace) return RDKV_ERR_NULL;
+  for (const void* ptr : {(const void*)cache, (const void*)zc_stats, (const void*)workspace})
+    if (!aligned16(ptr)) return RDKV_ERR_ALIGN;
+  if (cache_bytes < layout->cache_bytes || workspace_bytes < layout->rollover_workspace_bytes)
+    return RDKV_ERR_WORKSPACE;
+  if (generation < 0 || generation >= layout->n_generations) return RDKV_ERR_CAPACITY;
+  RolloverParams r = rollover_params(*layout, cache, zc_stats);
+  const rdkv_layout g = generation_layout(*layout);
+  return hip_status(launch_rollover(r, g, generation, static_cast<uint8_t*>(workspace), stream));
 }
 
 rdkv_status rdkv_unpack(const rdkv_layout* layout, const void* cache, size_t cache_bytes, int64_t seg,

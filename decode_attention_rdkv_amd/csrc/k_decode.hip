@@ -106,15 +106,34 @@ struct SegInfo {
   int n_tok[4];
   int n_chan[4];
   int rec_a;        // words of a zone-A record
-  uint64_t off_v[4], off_krec, off_kc, off_vc;
+  uint64_t off_v[4], off_krec, off_kc, off_vc;   // from the cache base
+  uint64_t desc;                                 // offset of the segment's descriptor
   bool zc_ok;
 };
 
+// One blob inside the cache: the prefill generation (base 0) or a rolled-over
+// generation blob.  Its descriptors' offsets are relative to its own base.
+struct BlobRef {
+  uint64_t base, bytes;
+  int64_t nk_max;
+  int rec_max, chunk_tok2, token_slots;
+};
+
+__device__ inline BlobRef main_blob(const DecodeParams& p) {
+  return BlobRef{0, p.main_bytes, p.nk_max, p.rec_max, p.chunk_tok2, p.token_slots};
+}
+__device__ inline BlobRef gen_blob(const DecodeParams& p, int g) {
+  return BlobRef{p.gen_offset + uint64_t(g) * p.gen_bytes, p.gen_cache_bytes, p.gen_nk_max, p.gen_rec_max,
+                 p.gen_chunk_tok2, p.gen_slots};
+}
+
 // Reads a descriptor and treats anything inconsistent with the layout as an
 // empty segment, so a damaged blob can never drive reads out of bounds.
-__device__ inline SegInfo load_segment(const DecodeParams& p, int64_t seg) {
-  const uint8_t* d = p.cache + kHeaderBytes + uint64_t(seg) * kDescBytes;
+// n_c: zone-C rows to check room for (prefill generation only).
+__device__ inline SegInfo load_segment(const DecodeParams& p, const BlobRef& b, int64_t seg, int n_c) {
+  const uint8_t* d = p.cache + b.base + kHeaderBytes + uint64_t(seg) * kDescBytes;
   SegInfo s;
+  s.desc = b.base + kHeaderBytes + uint64_t(seg) * kDescBytes;
   int n_kept_sum = 0, n_chan_sum = 0;
   bool ok = true;
 #pragma unroll
@@ -132,28 +151,32 @@ __device__ inline SegInfo load_segment(const DecodeParams& p, int64_t seg) {
   s.off_kc = *reinterpret_cast<const uint64_t*>(d + kDescOffKc);
   s.off_vc = *reinterpret_cast<const uint64_t*>(d + kDescOffVc);
   const RecordShape rs = record_shape(s.n_chan[0], s.n_chan[1], s.n_chan[2], s.n_chan[3]);
-  ok = ok && n_kept == n_kept_sum && n_kept <= p.nk_max && n_chan_sum <= kHeadDim && rec == 4 * rs.words_a() &&
-       rec <= p.rec_max;
+  ok = ok && n_kept == n_kept_sum && n_kept <= b.nk_max && n_chan_sum <= kHeadDim && rec == 4 * rs.words_a() &&
+       rec <= b.rec_max;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    ok = ok && s.off_v[i] + uint64_t(s.n_tok[i]) * (kHeadDim * group_bits(i) / 8) <= p.cache_bytes;
-  ok = ok && s.off_krec + uint64_t(n_kept) * rec <= p.cache_bytes;
+    ok = ok && s.off_v[i] + uint64_t(s.n_tok[i]) * (kHeadDim * group_bits(i) / 8) <= b.bytes;
+  ok = ok && s.off_krec + uint64_t(n_kept) * rec <= b.bytes;
   // the layout sized the chunk slots for sum_g n_g 2^g <= min(B_V / 2, 8 N); a
   // descriptor with more chunks than its slots would leave chunks unlaunched
-  int n_chunks = int((p.n_c + kChunkRowsC - 1) / kChunkRowsC);
+  int n_chunks = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int T = chunk_tokens(p.chunk_tok2, i);
+    const int T = chunk_tokens(b.chunk_tok2, i);
     n_chunks += (max(s.n_tok[i], 0) + T - 1) / T;
   }
-  ok = ok && n_chunks <= p.max_chunks;
+  ok = ok && n_chunks <= b.token_slots;
   if (!ok) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) s.n_tok[i] = s.n_chan[i] = 0;
   }
   s.rec_a = ok ? rec / 4 : 1;
-  s.zc_ok = s.off_vc + uint64_t(p.n_c) * kHeadDim * 2 <= p.cache_bytes &&
-            s.off_kc + uint64_t(p.n_c) * kHeadDim * 2 <= p.cache_bytes;
+  s.zc_ok = s.off_vc + uint64_t(n_c) * kHeadDim * 2 <= b.bytes && s.off_kc + uint64_t(n_c) * kHeadDim * 2 <= b.bytes;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s.off_v[i] += b.base;
+  s.off_krec += b.base;
+  s.off_kc += b.base;
+  s.off_vc += b.base;
   return s;
 }
 
@@ -165,7 +188,9 @@ struct Plan {
   int rec_words;     // words per record in this group
 };
 
-__device__ inline Plan plan_chunk(const SegInfo& si, int n_c, int chunk_tok2, int k) {
+// Chunk k of a segment's kept tokens: groups 2, 4, 8, 16 bits in turn, each
+// cut into chunks of chunk_tok2 >> g tokens; kind -1 past the last one.
+__device__ inline Plan plan_tokens(const SegInfo& si, int chunk_tok2, int k) {
   Plan pl{-1, 0, 0, 0, 0, 0};
   int kept = 0;
 #pragma unroll
@@ -187,14 +212,18 @@ __device__ inline Plan plan_chunk(const SegInfo& si, int n_c, int chunk_tok2, in
     }
     kept += si.n_tok[g];
   }
-  if (pl.kind < 0) {
-    const int nch = (n_c + kChunkRowsC - 1) / kChunkRowsC;
-    if (k < nch) {
-      pl.kind = 4;
-      pl.start = k * kChunkRowsC;
-      pl.end = min(n_c, (k + 1) * kChunkRowsC);
-      pl.vbase = si.off_vc;
-    }
+  return pl;
+}
+
+// Zone-C chunk k: rows [256 k, min(n_c, 256 (k + 1))); kind -1 past the last.
+__device__ inline Plan plan_zone_c(const SegInfo& si, int n_c, int k) {
+  Plan pl{-1, 0, 0, 0, 0, 0};
+  const int nch = (n_c + kChunkRowsC - 1) / kChunkRowsC;
+  if (k < nch) {
+    pl.kind = 4;
+    pl.start = k * kChunkRowsC;
+    pl.end = min(n_c, (k + 1) * kChunkRowsC);
+    pl.vbase = si.off_vc;
   }
   return pl;
 }
@@ -255,7 +284,7 @@ template <int G, int SW>
 __device__ void build_query_tables(const DecodeParams& p, const SegInfo& si, const Plan& pl, int64_t seg,
                                    Smem<G, SW>& sm) {
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
-  const uint8_t* perm = p.cache + kHeaderBytes + uint64_t(seg) * kDescBytes + kDescPerm;
+  const uint8_t* perm = p.cache + si.desc + kDescPerm;
   const RecordShape rs = record_shape(si.n_chan[0], si.n_chan[1], si.n_chan[2], si.n_chan[3]);
   const int c8 = si.n_chan[0], c4 = c8 + si.n_chan[1], c2 = c4 + si.n_chan[2], c0 = c2 + si.n_chan[3];
   const uint16_t* qh = reinterpret_cast<const uint16_t*>(p.q) + seg * G * kHeadDim;
@@ -866,7 +895,13 @@ __device__ void run_zone_c(const DecodeParams& p, const SegInfo& si, int64_t seg
 // the merge needs nothing from the blob.
 constexpr int kMergeThreads = kHeadDim;
 
-template <int G>
+// With kAccum (rdkv_decode_accumulate), the workgroup of (segment, head g)
+// then adds the step's final softmax probability of every zone-C row j < n_c,
+// exp2(t_j - M) / L with t_j = q_g.k_j log2(e) / sqrt(d) recomputed from the
+// zone-C key (fp32 products of the fp16 values), to zc_stats[seg][g][j], and
+// q_g[c]^2 to zc_stats[seg][g][cap + c]; one thread per element, so no
+// atomics and a fixed order.
+template <int G, bool kAccum>
 __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParams p) {
   __shared__ float s_w[kMergeThreads], s_lw[kMergeThreads];
   __shared__ float s_red[kMergeThreads / 64];
@@ -904,6 +939,32 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParam
     __syncthreads();
   }
   p.out[(seg * G + g) * kHeadDim + c] = L > 0.f ? O / L : 0.f;
+  if constexpr (kAccum) {
+    float* st = p.zc_stats + (seg * G + g) * int64_t(p.zc_cap + kHeadDim);
+    const float qc = __half2float(p.q[(seg * G + g) * kHeadDim + c]);
+    st[p.zc_cap + c] += qc * qc;
+    s_w[c] = qc;                   // free since the last barrier of the loop
+    __syncthreads();
+    const uint8_t* d = p.cache + kHeaderBytes + uint64_t(seg) * kDescBytes;
+    const uint64_t off_kc = *reinterpret_cast<const uint64_t*>(d + kDescOffKc);
+    if (L > 0.f && off_kc + uint64_t(p.n_c) * kHeadDim * 2 <= p.main_bytes) {
+      for (int j = c; j < p.n_c; j += kMergeThreads) {
+        const uint4* kr = reinterpret_cast<const uint4*>(p.cache + off_kc + uint64_t(j) * kHeadDim * 2);
+        float t = 0.f;
+#pragma unroll 4
+        for (int i = 0; i < kHeadDim / 8; ++i) {
+          const uint4 x = kr[i];
+          const uint32_t w4[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            t = fmaf(s_w[8 * i + 2 * e], half_lo(w4[e]), t);
+            t = fmaf(s_w[8 * i + 2 * e + 1], half_hi(w4[e]), t);
+          }
+        }
+        st[j] += exp2f(t * kLog2eOverSqrtD - M) / L;
+      }
+    }
+  }
 }
 
 template <int G, int SW>
@@ -916,8 +977,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   // L2 then holds the segment's descriptor and query).
   const int64_t seg = blockIdx.x % p.n_seg;
   const int k = int(blockIdx.x / p.n_seg);
-  const SegInfo si = load_segment(p, seg);
-  const Plan pl = plan_chunk(si, si.zc_ok ? p.n_c : 0, p.chunk_tok2, k);
+  // slot k: the prefill tokens' chunks, the generations' chunks, zone C
+  const int gen_end = p.token_slots + p.n_gen * p.gen_slots;
+  SegInfo si;
+  Plan pl;
+  if (k < p.token_slots) {
+    si = load_segment(p, main_blob(p), seg, 0);
+    pl = plan_tokens(si, p.chunk_tok2, k);
+  } else if (k < gen_end) {
+    const int g = (k - p.token_slots) / p.gen_slots;
+    const int n_used = *reinterpret_cast<const int32_t*>(p.cache + kHdrNGenUsed);
+    if (g < n_used) {
+      const BlobRef b = gen_blob(p, g);
+      si = load_segment(p, b, seg, 0);
+      pl = plan_tokens(si, b.chunk_tok2, k - p.token_slots - g * p.gen_slots);
+    } else {
+      pl.kind = -1;
+    }
+  } else {
+    si = load_segment(p, main_blob(p), seg, p.n_c);
+    pl = plan_zone_c(si, si.zc_ok ? p.n_c : 0, k - gen_end);
+  }
   const int tid = threadIdx.x;
   float* out = p.partials + (int64_t(seg) * p.max_chunks + k) * G * kPartialFloats;
   if (pl.kind < 0) {   // a slot past the segment's last chunk: (m, l, o) = (-inf, 0, 0)
@@ -977,7 +1057,7 @@ hipError_t launch_chunks_gs(const DecodeParams& p, hipStream_t stream) {
 template <int G>
 hipError_t launch_chunks_g(const DecodeParams& p, hipStream_t stream) {
   // K record words staged through LDS, from the layout's bound on a record
-  const int words = (p.rec_max + 3) / 4;
+  const int words = (max(p.rec_max, p.gen_rec_max) + 3) / 4;
   if (words <= 8) return launch_chunks_gs<G, 8>(p, stream);
   if (words <= 10) return launch_chunks_gs<G, 10>(p, stream);
   if (words <= 12) return launch_chunks_gs<G, 12>(p, stream);
@@ -990,7 +1070,10 @@ hipError_t launch_chunks_g(const DecodeParams& p, hipStream_t stream) {
 template <int G>
 hipError_t launch_merge_g(const DecodeParams& p, hipStream_t stream) {
   if (p.n_seg == 0) return hipSuccess;
-  hipLaunchKernelGGL(decode_merge_kernel<G>, dim3(unsigned(p.n_seg * G)), dim3(kMergeThreads), 0, stream, p);
+  if (p.zc_stats)
+    hipLaunchKernelGGL((decode_merge_kernel<G, true>), dim3(unsigned(p.n_seg * G)), dim3(kMergeThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((decode_merge_kernel<G, false>), dim3(unsigned(p.n_seg * G)), dim3(kMergeThreads), 0, stream, p);
   return hipGetLastError();
 }
 

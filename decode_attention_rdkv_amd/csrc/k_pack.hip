@@ -89,6 +89,13 @@ __global__ void cache_header_kernel(uint8_t* cache, rdkv_layout lay, SegGeom g) 
     const int64_t h64[7] = {lay.dims.n_tokens, lay.budget_v, lay.budget_k, lay.n_seg,
                             int64_t(kHeaderBytes), int64_t(lay.slots_offset), int64_t(lay.slot_bytes)};
     for (int i = 0; i < 7; ++i) st_u64(cache, 32 + 8 * i, uint64_t(h64[i]));
+    // generations (all zero without rollover): reserved, in use, where, budgets
+    st_i32(cache, kHdrNGen, lay.n_generations);
+    st_i32(cache, kHdrNGenUsed, 0);
+    st_u64(cache, kHdrGenOffset, lay.gen_offset);
+    st_u64(cache, kHdrGenBytes, lay.gen_bytes);
+    st_u64(cache, kHdrGenBudgetV, uint64_t(lay.gen_budget_v));
+    st_u64(cache, kHdrGenBudgetK, uint64_t(lay.gen_budget_k));
   }
   if (seg >= lay.n_seg) return;
   const int z[4] = {0, 0, 0, 0};
@@ -496,12 +503,16 @@ hipError_t launch_pack_status(const uint8_t* cache, int64_t n_seg, int32_t* out,
   return hipGetLastError();
 }
 
-hipError_t launch_cache_init(uint8_t* cache, const rdkv_layout& lay, hipStream_t stream) {
+hipError_t launch_cache_init(uint8_t* cache, const rdkv_layout& lay, const rdkv_layout* gen, hipStream_t stream) {
   const uint64_t n16 = lay.cache_bytes / 16;
   const unsigned grid = unsigned(std::min<uint64_t>(cdiv(n16, 256), 8192));
   hipLaunchKernelGGL(cache_zero_kernel, dim3(grid), dim3(256), 0, stream, reinterpret_cast<uint4*>(cache), n16);
   const unsigned ggrid = unsigned(cdiv(lay.n_seg, 4));
   hipLaunchKernelGGL(cache_header_kernel, dim3(ggrid), dim3(256), 0, stream, cache, lay, geom_of(lay));
+  // every generation blob starts as an empty blob of its own layout
+  for (int g = 0; gen && g < lay.n_generations; ++g)
+    hipLaunchKernelGGL(cache_header_kernel, dim3(ggrid), dim3(256), 0, stream, cache + lay.gen_offset + g * lay.gen_bytes,
+                       *gen, geom_of(*gen));
   return hipGetLastError();
 }
 

@@ -114,23 +114,45 @@ __device__ inline int wave_sum_i(int v) {
 // ------------------------------------------------------------ launchers
 // Each returns hipSuccess or the launch error; arguments are already validated.
 
+// Zone-C rollover: generation blobs reserved per layout, at most.
+constexpr int kMaxGenerations = 4096;
+// Blob header fields of the generations (bytes): count reserved, count in
+// use, offset of generation 0, stride, V and K budgets per generation.
+constexpr int kHdrNGen = 88;
+constexpr int kHdrNGenUsed = 92;
+constexpr int kHdrGenOffset = 96;
+constexpr int kHdrGenBytes = 104;
+constexpr int kHdrGenBudgetV = 112;
+constexpr int kHdrGenBudgetK = 120;
+
+// Split-K chunk slots of a segment in decode: [0, token_slots) the prefill
+// tokens' chunks, then n_gen * gen_slots for the generation blobs (empty
+// while a generation is not in use), then the zone-C chunks.
 struct DecodeParams {
   uint8_t* cache;
-  uint64_t cache_bytes;
+  uint64_t cache_bytes;    // whole blob, generations included
+  uint64_t main_bytes;     // the prefill generation's part (descriptors, slots)
   int64_t n_seg;
   int64_t nk_max;
   int32_t max_chunks;
+  int32_t token_slots;
   int32_t chunk_tok2;
   int32_t rec_max;
   int32_t group;           // G = Hq / Hkv
+  int32_t zc_cap;          // zone-C capacity (stride of the zone-C statistics)
   int32_t c_len;           // zone-C rows present before this step
   int32_t n_c;             // zone-C rows attended this step
   int32_t append;          // 1: row c_len comes from k_new/v_new and is written
+  // generation blobs (all 0 without rollover)
+  int32_t n_gen, gen_slots, gen_chunk_tok2, gen_rec_max;
+  int64_t gen_nk_max;
+  uint64_t gen_offset, gen_bytes, gen_cache_bytes;
   const __half* q;         // [n_seg][G][128]
   const __half* k_new;     // [n_seg][128] or null
   const __half* v_new;
   float* partials;         // [n_seg][max_chunks][G][kPartialFloats]
   float* out;              // [n_seg][G][128]
+  float* zc_stats;         // merge: [n_seg][G][zc_cap + 128] statistics to accumulate, or null
 };
 hipError_t launch_decode_chunks(const DecodeParams& p, hipStream_t stream);
 // Device address (on the current device) of the library-owned decode scratch
@@ -149,11 +171,32 @@ struct PackParams {
   const uint8_t* bits_tok; // [S][n_layers_in][Hkv][N]
   const uint8_t* bits_chan;// [S][n_layers_in][Hkv][128]
 };
-hipError_t launch_cache_init(uint8_t* cache, const rdkv_layout& lay, hipStream_t stream);
+// gen: the layout of each generation blob (rollover layouts), else null
+hipError_t launch_cache_init(uint8_t* cache, const rdkv_layout& lay, const rdkv_layout* gen, hipStream_t stream);
 hipError_t launch_pack(const PackParams& p, hipStream_t stream);
 hipError_t launch_pack_status(const uint8_t* cache, int64_t n_seg, int32_t* out, hipStream_t stream);
 hipError_t launch_unpack(const uint8_t* cache, uint64_t cache_bytes, const rdkv_layout& lay, int64_t seg,
                          float* k_hat, float* v_hat, hipStream_t stream);
+
+struct RolloverParams {
+  uint8_t* cache;
+  uint64_t main_bytes;     // bytes of the prefill generation's part (zone-C offsets are checked against it)
+  int64_t n_seg;
+  int32_t G, cap, n_layers;
+  uint64_t gen_offset, gen_bytes;
+  int64_t gen_budget_v, gen_budget_k;
+  const float* stats;      // [n_seg][G][cap + 128]
+  float* w_tok;            // [n_seg][cap]
+  float* var_tok;          // [n_seg][cap]
+  float* w_chan;           // [n_seg][128]
+};
+// Workspace of a rollover: zone-C rows gathered per segment, weights, bits.
+uint64_t rollover_workspace_bytes(int64_t n_seg, int64_t cap);
+hipError_t launch_rollover_score(const RolloverParams& r, hipStream_t stream);
+// Score (into the workspace), allocate, pack into generation blob `gen`
+// (laid out by `gen_layout`), clear zone C and the statistics.
+hipError_t launch_rollover(RolloverParams r, const rdkv_layout& gen_layout, int32_t gen, uint8_t* workspace,
+                           hipStream_t stream);
 
 struct AllocParams {
   int64_t n_seg, n_tokens;

@@ -30,7 +30,10 @@ class Layout(ctypes.Structure):
     _fields_ = [("dims", Dims), ("budget_v", c_i64), ("budget_k", c_i64), ("n_seg", c_i64), ("nk_max", c_i64),
                 ("cache_bytes", c_u64), ("slots_offset", c_u64), ("slot_bytes", c_u64), ("slot_off_v", c_u64),
                 ("slot_off_krec", c_u64), ("slot_off_pos", c_u64), ("decode_workspace_bytes", c_u64),
-                ("zone_c_capacity", c_i32), ("rec_max", c_i32), ("max_chunks", c_i32), ("chunk_tok2", c_i32)]
+                ("zone_c_capacity", c_i32), ("rec_max", c_i32), ("max_chunks", c_i32), ("chunk_tok2", c_i32),
+                ("n_generations", c_i32), ("token_slots", c_i32), ("gen_budget_v", c_i64), ("gen_budget_k", c_i64),
+                ("gen_offset", c_u64), ("gen_bytes", c_u64), ("zc_stats_bytes", c_u64),
+                ("rollover_workspace_bytes", c_u64)]
 
     @property
     def group(self) -> int:
@@ -46,6 +49,8 @@ SIGNATURES = {
     "rdkv_version": (c_i32, []),
     "rdkv_status_string": (ctypes.c_char_p, [c_i32]),
     "rdkv_layout_init": (c_i32, [ctypes.POINTER(Dims), c_i64, c_i64, c_i32, ctypes.POINTER(Layout)]),
+    "rdkv_layout_init_rollover": (c_i32, [ctypes.POINTER(Dims), c_i64, c_i64, c_i32, c_i32, c_i64, c_i64,
+                                          ctypes.POINTER(Layout)]),
     "rdkv_score_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(Dims)]),
     "rdkv_score": (c_i32, [ctypes.POINTER(Dims), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, ctypes.c_size_t, c_vp]),
     "rdkv_score_lse": (c_i32, [ctypes.POINTER(Dims), c_vp, c_vp, c_vp, c_vp]),
@@ -60,6 +65,11 @@ SIGNATURES = {
     "rdkv_pack_status": (c_i32, [ctypes.POINTER(Layout), c_vp, ctypes.c_size_t, c_vp, c_vp]),
     "rdkv_decode": (c_i32, [ctypes.POINTER(Layout), c_vp, ctypes.c_size_t, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp,
                             ctypes.c_size_t, c_vp]),
+    "rdkv_decode_accumulate": (c_i32, [ctypes.POINTER(Layout), c_vp, ctypes.c_size_t, c_i32, c_vp, c_vp, c_vp, c_vp,
+                                       c_vp, c_vp, ctypes.c_size_t, c_vp]),
+    "rdkv_rollover_score": (c_i32, [ctypes.POINTER(Layout), c_vp, ctypes.c_size_t, c_vp, c_vp, c_vp, c_vp, c_vp]),
+    "rdkv_rollover": (c_i32, [ctypes.POINTER(Layout), c_vp, ctypes.c_size_t, c_i32, c_vp, c_vp, ctypes.c_size_t,
+                              c_vp]),
     "rdkv_decode_static": (c_i32, [ctypes.POINTER(Layout), c_vp, ctypes.c_size_t, c_i32, c_vp, c_vp, c_vp, c_vp,
                                    c_vp]),
     "rdkv_decode_partials": (c_i32, [ctypes.POINTER(Layout), c_vp, ctypes.c_size_t, c_i32, c_vp, c_vp, c_vp, c_vp,
@@ -133,6 +143,16 @@ def layout(dims: Dims, budget_v: int, budget_k: int, zone_c_capacity: int) -> La
     out = Layout()
     _check(load().rdkv_layout_init(ctypes.byref(dims), budget_v, budget_k, zone_c_capacity, ctypes.byref(out)),
            "rdkv_layout_init")
+    return out
+
+
+def layout_rollover(dims: Dims, budget_v: int, budget_k: int, zone_c_capacity: int, n_generations: int,
+                    gen_budget_v: int, gen_budget_k: int) -> Layout:
+    """Layout whose zone C rolls over into up to n_generations generation blobs."""
+    out = Layout()
+    _check(load().rdkv_layout_init_rollover(ctypes.byref(dims), budget_v, budget_k, zone_c_capacity, n_generations,
+                                            gen_budget_v, gen_budget_k, ctypes.byref(out)),
+           "rdkv_layout_init_rollover")
     return out
 
 
@@ -294,6 +314,56 @@ def decode(lay: Layout, cache: torch.Tensor, c_len: int, q, k_new=None, v_new=No
                               _ptr(workspace, torch.uint8, None, "workspace"), workspace.numel(), _stream()),
            "rdkv_decode")
     return out
+
+
+def zone_c_stats(lay: Layout, device="cuda") -> torch.Tensor:
+    """Zeroed decode-time statistics of zone C: fp32 [S][L][Hkv][G][cap + 128]."""
+    d = lay.dims
+    return torch.zeros((d.n_seq, d.n_layers, d.n_kv_heads, lay.group, lay.zone_c_capacity + HEAD_DIM),
+                       dtype=torch.float32, device=device)
+
+
+def decode_accumulate(lay: Layout, cache: torch.Tensor, c_len: int, q, k_new, v_new, stats: torch.Tensor,
+                      workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """rdkv_decode_accumulate: one decode step that also adds each zone-C row's
+    attention mass and the query channel squares to `stats`."""
+    d = lay.dims
+    S, L, Hq, Hk = d.n_seq, d.n_layers, d.n_q_heads, d.n_kv_heads
+    if workspace is None:
+        workspace = decode_workspace(lay, q.device)
+    if out is None:
+        out = torch.empty((S, L, Hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+    _check(load().rdkv_decode_accumulate(
+        ctypes.byref(lay), _ptr(cache, torch.uint8, None, "cache"), cache.numel(), c_len,
+        _ptr(q, torch.float16, (S, L, Hq, HEAD_DIM), "q"), _ptr(k_new, torch.float16, (S, L, Hk, HEAD_DIM), "k_new"),
+        _ptr(v_new, torch.float16, (S, L, Hk, HEAD_DIM), "v_new"), _ptr(out, torch.float32, (S, L, Hq, HEAD_DIM), "out"),
+        _ptr(stats, torch.float32, (S, L, Hk, lay.group, lay.zone_c_capacity + HEAD_DIM), "stats"),
+        _ptr(workspace, torch.uint8, None, "workspace"), workspace.numel(), _stream()), "rdkv_decode_accumulate")
+    return out
+
+
+def rollover_score(lay: Layout, cache: torch.Tensor, stats: torch.Tensor):
+    """Stage-1 weights of the zone-C tokens: (w_tok [S][L][Hkv][cap], var_tok, w_chan [S][L][Hkv][128])."""
+    d = lay.dims
+    S, L, Hk, cap = d.n_seq, d.n_layers, d.n_kv_heads, lay.zone_c_capacity
+    w_tok = torch.empty((S, L, Hk, cap), dtype=torch.float32, device=cache.device)
+    var_tok = torch.empty_like(w_tok)
+    w_chan = torch.empty((S, L, Hk, HEAD_DIM), dtype=torch.float32, device=cache.device)
+    _check(load().rdkv_rollover_score(ctypes.byref(lay), _ptr(cache, torch.uint8, None, "cache"), cache.numel(),
+                                      _ptr(stats, torch.float32, None, "stats"), w_tok.data_ptr(), var_tok.data_ptr(),
+                                      w_chan.data_ptr(), _stream()), "rdkv_rollover_score")
+    return w_tok, var_tok, w_chan
+
+
+def rollover(lay: Layout, cache: torch.Tensor, generation: int, stats: torch.Tensor,
+             workspace: Optional[torch.Tensor] = None):
+    """rdkv_rollover: pack the full zone C into generation blob `generation`, clear zone C and `stats`."""
+    if workspace is None:
+        workspace = torch.empty(max(int(lay.rollover_workspace_bytes), 16), dtype=torch.uint8, device=cache.device)
+    _check(load().rdkv_rollover(ctypes.byref(lay), _ptr(cache, torch.uint8, None, "cache"), cache.numel(), generation,
+                                _ptr(stats, torch.float32, None, "stats"),
+                                _ptr(workspace, torch.uint8, None, "workspace"), workspace.numel(), _stream()),
+           "rdkv_rollover")
 
 
 STATIC_SCRATCH_BYTES = 64 << 20

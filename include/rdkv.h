@@ -84,6 +84,15 @@ typedef struct rdkv_layout {
   int32_t max_chunks;            /* split-K partial slots per segment in decode     */
   int32_t chunk_tok2;            /* decode split-K chunk: tokens of the 2-bit group */
                                  /* (4/8/16-bit groups: 1/2, 1/4, 1/8 of it)        */
+  /* zone-C rollover (rdkv_layout_init_rollover; all 0 from rdkv_layout_init) */
+  int32_t n_generations;         /* generation blobs reserved for rollovers         */
+  int32_t token_slots;           /* chunk slots per segment of the prefill tokens    */
+  int64_t gen_budget_v;          /* bits per segment per generation, V tokens       */
+  int64_t gen_budget_k;          /* bits per segment per generation, K channels     */
+  uint64_t gen_offset;           /* blob offset of generation blob 0                */
+  uint64_t gen_bytes;            /* bytes from one generation blob to the next      */
+  uint64_t zc_stats_bytes;       /* rdkv_decode_accumulate statistics buffer        */
+  uint64_t rollover_workspace_bytes; /* workspace rdkv_rollover needs               */
 } rdkv_layout;
 
 /* Library version (format version in the high 16 bits, build in the low 16). */
@@ -97,6 +106,21 @@ const char* rdkv_status_string(rdkv_status status);
  * >= 0 rows.  Host only; touches no device. */
 rdkv_status rdkv_layout_init(const rdkv_dims* dims, int64_t budget_v, int64_t budget_k,
                              int32_t zone_c_capacity, rdkv_layout* out);
+
+/* The same layout, plus room for the cache to grow past its zone C: when
+ * zone C is full, rdkv_rollover scores its zone_c_capacity tokens, allocates
+ * them with gen_budget_v / gen_budget_k bits per segment (the budgets of
+ * section 2.1 for the new tokens) and packs them, like the prefill tokens,
+ * into the next of n_generations generation blobs (n_generations >= 1,
+ * zone_c_capacity >= 1), after which zone C is empty again.  Each generation
+ * blob is a complete blob of this format for zone_c_capacity tokens per
+ * segment and no zone C of its own, placed at gen_offset + g * gen_bytes in
+ * the cache; decode attends over every generation in use.  Host only.
+ * Errors: as rdkv_layout_init; RDKV_ERR_SHAPE for n_generations < 1 (or above
+ * 4096) or zone_c_capacity < 1, RDKV_ERR_BUDGET for a negative budget. */
+rdkv_status rdkv_layout_init_rollover(const rdkv_dims* dims, int64_t budget_v, int64_t budget_k,
+                                      int32_t zone_c_capacity, int32_t n_generations, int64_t gen_budget_v,
+                                      int64_t gen_budget_k, rdkv_layout* out);
 
 /* ---------------------------------------------------------------- stage 1
  * Distortion weights after prefill (section 2.1, section 2.2 stage 1).
@@ -219,6 +243,52 @@ rdkv_status rdkv_pack_status(const rdkv_layout* layout, const void* cache, size_
 rdkv_status rdkv_decode(const rdkv_layout* layout, void* cache, size_t cache_bytes, int32_t c_len,
                         const void* q, const void* k_new, const void* v_new, float* out,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------- zone-C rollover
+ * Decode-time scoring of the new tokens, for caches made with
+ * rdkv_layout_init_rollover.  Section 2.1's token weight is the attention a
+ * token receives from the queries that see it; for a token of zone C these
+ * are the decode steps' query heads from its own step on (the accumulated
+ * attention score of the aistudio.id article's "Solusi 2").
+ *
+ * rdkv_decode_accumulate: rdkv_decode, plus, after the step's softmax over
+ * the whole cache is known, for every segment, query head g and zone-C row
+ * j < n_c (the rows this step attended):
+ *   zc_stats[seg][g][j]       += exp(q_g.k_j / sqrt(d) - LSE_g)  (its attention mass)
+ *   zc_stats[seg][g][cap + c] += q_g[c]^2                        (c = 0..127)
+ * zc_stats is fp32 [n_seg][G][cap + 128] (layout->zc_stats_bytes, device,
+ * caller-owned), all zero before the first step after rdkv_cache_init
+ * (rdkv_rollover zeroes it again).  Arguments and errors otherwise as
+ * rdkv_decode; RDKV_ERR_SHAPE if the layout has no generations. */
+rdkv_status rdkv_decode_accumulate(const rdkv_layout* layout, void* cache, size_t cache_bytes, int32_t c_len,
+                                   const void* q, const void* k_new, const void* v_new, float* out,
+                                   float* zc_stats, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream);
+
+/* rdkv_rollover_score: stage 1 (section 2.1) for the cap zone-C tokens of
+ * every segment, from zc_stats:
+ *   w_tok[seg][j]   = sum over g of zc_stats[seg][g][j]           fp32 [n_seg][cap]
+ *   var_tok[seg][j] = population variance of zone-C V row j        fp32 [n_seg][cap]
+ *   w_chan[seg][c]  = sqrt(sum_g zc_stats[seg][g][cap + c]) * ||K_C[:, c]||_2 / sqrt(d)
+ *                                                                  fp32 [n_seg][128]
+ * Rows never appended are zero (weight 0, variance 0).  Reads only. */
+rdkv_status rdkv_rollover_score(const rdkv_layout* layout, const void* cache, size_t cache_bytes,
+                                const float* zc_stats, float* w_tok, float* var_tok, float* w_chan,
+                                hipStream_t stream);
+
+/* rdkv_rollover: roll zone C into generation blob `generation`: the weights
+ * of rdkv_rollover_score, the allocation of rdkv_allocate (section 2.2: V
+ * tokens with gen_budget_v, then K channels over the kept ones with
+ * gen_budget_k; 0 bits = evicted), the packing of rdkv_pack into that blob;
+ * then zone C and zc_stats are zeroed and the blob header counts
+ * generation + 1 generations in use.  Call it when zone C is full (the
+ * caller's c_len == zone_c_capacity) and continue decoding with c_len = 0.
+ * `generation` is the number of rollovers done so far (0, 1, ...), which the
+ * caller tracks like c_len; generation >= layout->n_generations gives
+ * RDKV_ERR_CAPACITY.  `workspace` must hold layout->rollover_workspace_bytes.
+ * Other errors: RDKV_ERR_NULL, _ALIGN, _WORKSPACE, _SHAPE (no generations). */
+rdkv_status rdkv_rollover(const rdkv_layout* layout, void* cache, size_t cache_bytes, int32_t generation,
+                          float* zc_stats, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* rdkv_decode for callers that cannot allocate device memory (code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc): no

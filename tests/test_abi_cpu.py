@@ -179,6 +179,56 @@ def test_two_phase_decode_validation(lib):
     assert lib.rdkv_decode_merge(ctypes.byref(lay), A, nb, 0, A + 4, A, ws, None) == ALIGN
 
 
+@pytest.mark.parametrize("shape", [(1, 1, 4, 1, 1024, 4096, 512, 128, 3, 512, 512),
+                                   (2, 3, 8, 2, 777, 1500, 300, 64, 5, 128, 256),
+                                   (16, 1, 32, 8, 32768, 98304, 384, 256, 2, 768, 384),
+                                   (1, 2, 16, 2, 300, 0, 0, 300, 1, 0, 0)])
+def test_rollover_layout_matches_oracle(shape):
+    S, L, Hq, Hkv, N, bv, bk, cap, n_gen, gbv, gbk = shape
+    lay = rdkv.layout_rollover(rdkv.make_dims(S, L, Hq, Hkv, N), bv, bk, cap, n_gen, gbv, gbk)
+    ol = O.Layout(S, L, Hq, Hkv, 128, N, bv, bk, cap, n_generations=n_gen, gen_budget_v=gbv, gen_budget_k=gbk)
+    plain = rdkv.layout(rdkv.make_dims(S, L, Hq, Hkv, N), bv, bk, cap)
+    assert (lay.cache_bytes, lay.gen_offset, lay.gen_bytes) == (ol.cache_bytes, ol.gen_offset, ol.gen_bytes)
+    assert lay.slot_bytes == plain.slot_bytes and lay.gen_offset == plain.cache_bytes
+    gen = rdkv.layout(rdkv.make_dims(S, L, Hq, Hkv, cap), gbv, gbk, 0)
+    assert lay.max_chunks == plain.token_slots + n_gen * gen.max_chunks + -(-cap // 256)
+    assert lay.token_slots == plain.token_slots
+    assert lay.zc_stats_bytes == S * L * Hkv * (Hq // Hkv) * (cap + 128) * 4
+    assert lay.decode_workspace_bytes == S * L * Hkv * lay.max_chunks * (Hq // Hkv) * 132 * 4
+    assert lay.rollover_workspace_bytes >= S * L * Hkv * cap * 2 * 256
+
+
+def test_rollover_validation(lib):
+    d = _dims(n_layers=2)
+    out = rdkv.Layout()
+    assert lib.rdkv_layout_init_rollover(ctypes.byref(d), 64, 32, 4, 0, 8, 8, ctypes.byref(out)) == SHAPE
+    assert lib.rdkv_layout_init_rollover(ctypes.byref(d), 64, 32, 0, 2, 8, 8, ctypes.byref(out)) == SHAPE
+    assert lib.rdkv_layout_init_rollover(ctypes.byref(d), 64, 32, 4, 2, -1, 8, ctypes.byref(out)) == BUDGET
+    assert lib.rdkv_layout_init_rollover(ctypes.byref(d), 64, 32, 4, 5000, 8, 8, ctypes.byref(out)) == SHAPE
+    plain = rdkv.layout(d, 64, 32, 4)
+    assert plain.n_generations == 0 and plain.zc_stats_bytes == 0 and plain.gen_offset == 0
+    lay = rdkv.layout_rollover(d, 64, 32, 4, 2, 8, 8)
+    nb, ws, rws = lay.cache_bytes, lay.decode_workspace_bytes, lay.rollover_workspace_bytes
+    # decode with accumulation
+    assert lib.rdkv_decode_accumulate(ctypes.byref(plain), A, plain.cache_bytes, 0, A, None, None, A, A, A,
+                                      plain.decode_workspace_bytes, None) == SHAPE
+    assert lib.rdkv_decode_accumulate(ctypes.byref(lay), A, nb, 0, A, None, None, A, None, A, ws, None) == NULL
+    assert lib.rdkv_decode_accumulate(ctypes.byref(lay), A, nb, 0, A, None, None, A, A + 4, A, ws, None) == ALIGN
+    assert lib.rdkv_decode_accumulate(ctypes.byref(lay), A, nb, 4, A, A, A, A, A, A, ws, None) == CAPACITY
+    # scoring and rolling over
+    assert lib.rdkv_rollover_score(ctypes.byref(plain), A, plain.cache_bytes, A, A, A, A, None) == SHAPE
+    assert lib.rdkv_rollover_score(ctypes.byref(lay), A, nb, A, None, A, A, None) == NULL
+    assert lib.rdkv_rollover_score(ctypes.byref(lay), A, nb - 1, A, A, A, A, None) == WORKSPACE
+    assert lib.rdkv_rollover(ctypes.byref(lay), A, nb, 2, A, A, rws, None) == CAPACITY
+    assert lib.rdkv_rollover(ctypes.byref(lay), A, nb, -1, A, A, rws, None) == CAPACITY
+    assert lib.rdkv_rollover(ctypes.byref(lay), A, nb, 0, A, A, rws - 1, None) == WORKSPACE
+    assert lib.rdkv_rollover(ctypes.byref(lay), A, nb, 0, None, A, rws, None) == NULL
+    assert lib.rdkv_rollover(ctypes.byref(plain), A, plain.cache_bytes, 0, A, A, rws, None) == SHAPE
+    bad = rdkv.Layout.from_buffer_copy(lay)
+    bad.gen_bytes += 256
+    assert lib.rdkv_rollover(ctypes.byref(bad), A, nb, 0, A, A, rws, None) == SHAPE
+
+
 def test_static_decode_validation(lib):
     """rdkv_decode_static validates like rdkv_decode (minus the workspace) and
     refuses layouts whose split-K partials exceed its static scratch, all
