@@ -565,11 +565,19 @@ __device__ inline void state_init(WaveState<G>& st) {
 template <int GW, int G, int SW, bool kMasked>
 __device__ inline void softmax_tile(WaveState<GW>& st, const float (&s)[GW], bool valid, float vs, float vz,
                                     Smem<G, SW>& sm, int wave, int lane) {
+  float t[GW];
+  bool up = false;
 #pragma unroll
   for (int g = 0; g < GW; ++g) {
-    const float t = (!kMasked || valid) ? s[g] * kLog2eOverSqrtD : -INFINITY;
-    if (__builtin_amdgcn_ballot_w64(t > st.m[g]) != 0) {
-      const float mnew = fmaxf(st.m[g], wave_reduce<true>(t));
+    t[g] = (!kMasked || valid) ? s[g] * kLog2eOverSqrtD : -INFINITY;
+    up = up || t[g] > st.m[g];
+  }
+  // one wave-uniform branch per tile: some lane's logit exceeds its head's
+  // running max, so every such head's max moves and its sums are rescaled
+  if (__builtin_amdgcn_ballot_w64(up) != 0) {
+#pragma unroll
+    for (int g = 0; g < GW; ++g) {
+      const float mnew = fmaxf(st.m[g], wave_reduce<true>(t[g]));
       const float alpha = __builtin_amdgcn_exp2f(st.m[g] - mnew);
       st.m[g] = mnew;
       st.l[g] *= alpha;
@@ -577,7 +585,10 @@ __device__ inline void softmax_tile(WaveState<GW>& st, const float (&s)[GW], boo
 #pragma unroll
       for (int e = 0; e < 8; ++e) st.acc[g][e] *= alpha;
     }
-    const float pr = __builtin_amdgcn_exp2f(t - st.m[g]);
+  }
+#pragma unroll
+  for (int g = 0; g < GW; ++g) {
+    const float pr = __builtin_amdgcn_exp2f(t[g] - st.m[g]);
     st.l[g] += pr;
     st.z[g] = fmaf(pr, vz, st.z[g]);
     reinterpret_cast<uint16_t*>(&sm.coefh[wave][lane & 31][g])[lane >> 5] = __half_as_ushort(__float2half_rn(pr * vs));
@@ -793,11 +804,9 @@ __device__ void run_group(const DecodeParams& p, const SegInfo& si, const Plan& 
     }
     float s[GW], vs, vz;
     record_logits<GW>(my, ks, nw, B < 16, sm, hb, s, vs, vz);
-    if (b + kTile <= pl.end) {
-      softmax_tile<GW, G, SW, false>(st, s, true, vs, vz, sm, wave, lane);
-    } else {
-      softmax_tile<GW, G, SW, true>(st, s, b + lane < pl.end, vs, vz, sm, wave, lane);
-    }
+    // one softmax body for full and partial tiles (the validity test costs a
+    // compare and a select per head; two bodies cost register moves to merge)
+    softmax_tile<GW, G, SW, true>(st, s, b + lane < pl.end, vs, vz, sm, wave, lane);
     wave_lds_sync();
     __amdgpu_buffer_rsrc_t rl;
     if constexpr (kLateV) rl = vrsrc(i);
