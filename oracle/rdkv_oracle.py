@@ -489,8 +489,8 @@ def record_words(n_chan):
     return _cdiv(n16, 2), _cdiv(n8, 4), _cdiv(n4, 8), _cdiv(n2, 16), n_meta
 
 
-def pack_segment(lay: Layout, blob: np.ndarray, seg: int, Kh, Vh, bits_tok, bits_chan):
-    """Write one segment's descriptor and slot into `blob` (uint8 array).
+def segment_content(Kh, Vh, bits_tok, bits_chan) -> dict:
+    """What one segment's packed form holds, independent of where it is placed.
 
     Kept tokens (b_t > 0) are grouped by bitwidth 2, 4, 8 (zone A) and 16
     (zone B), ascending position inside a group ([RDKV] 2.3, rows grouped by
@@ -502,8 +502,11 @@ def pack_segment(lay: Layout, blob: np.ndarray, seg: int, Kh, Vh, bits_tok, bits
     (scale, zero) fp16 pair per present integer part (order 8, 4, 2), then,
     for a 2/4/8-bit token only, the (scale, zero) of its V row; the records of
     16-bit tokens are one word shorter.  0-bit channels are not stored.
+
+    Returns dict(n_tok [4], n_kept, n_chan [4] (16, 8, 4, 2 bits), rec (bytes of
+    a zone-A record), perm uint8 [128], v_rows (4 uint8 arrays, one per group),
+    records (4 uint32 arrays [n_g][words], one per group), positions int32).
     """
-    base = lay.slot_base(seg)
     bits_tok = np.asarray(bits_tok)
     bits_chan = np.asarray(bits_chan)
     Kh = np.asarray(Kh, np.float16)
@@ -517,21 +520,16 @@ def pack_segment(lay: Layout, blob: np.ndarray, seg: int, Kh, Vh, bits_tok, bits
     rec_words = w16 + w8 + w4 + w2 + n_meta + 1
 
     # V rows group by group, and the (scale, zero) word of each kept V row
-    off_v = []
+    v_rows = []
     vmeta = []
-    cur = base + lay.off_v
     for b, toks in zip((2, 4, 8, 16), groups):
-        off_v.append(cur)
-        row = D * b // 8
         if b == 16:
-            data = Vh[toks].reshape(len(toks), D).view(np.uint8)
+            v_rows.append(Vh[toks].reshape(len(toks), D).view(np.uint8).reshape(-1))
             vmeta.append(np.zeros(len(toks), np.uint32))
         else:
             q, sc, z = quantize(Vh[toks].reshape(len(toks), D), b)
-            data = pack_codes(q, b).view(np.uint8)
+            v_rows.append(pack_codes(q, b).view(np.uint8).reshape(-1))
             vmeta.append(half2_words(sc, z))
-        blob[cur:cur + len(toks) * row] = data.reshape(-1)
-        cur = _align(cur + len(toks) * row)
 
     # K records
     kp = Kh[kept][:, perm.astype(np.int64)].reshape(nk, D)
@@ -551,26 +549,40 @@ def pack_segment(lay: Layout, blob: np.ndarray, seg: int, Kh, Vh, bits_tok, bits
     parts.append(np.concatenate(vmeta).reshape(nk, 1))
     words = np.concatenate(parts, axis=1).astype(np.uint32)
     assert words.shape == (nk, rec_words)
-    # zone-A tokens take the full record; 16-bit tokens (last in kept order)
-    # drop the trailing V word, which they do not have
-    n_a = nk - len(groups[3])
-    off_rec = base + lay.off_krec
-    ra = words[:n_a].reshape(-1).view(np.uint8)
-    rb = np.ascontiguousarray(words[n_a:, :-1]).reshape(-1).view(np.uint8)
-    blob[off_rec:off_rec + ra.size] = ra
-    blob[off_rec + ra.size:off_rec + ra.size + rb.size] = rb
+    # zone-A tokens take the full record; 16-bit tokens drop the trailing V
+    # word, which they do not have
+    starts = np.cumsum([0] + [len(g) for g in groups])
+    records = [np.ascontiguousarray(words[starts[g]:starts[g + 1], :rec_words - (g == 3)]) for g in range(4)]
+    return dict(n_tok=[len(g) for g in groups], n_kept=nk, n_chan=n_chan, rec=4 * rec_words, perm=perm,
+                v_rows=v_rows, records=records, positions=kept.astype(np.int32))
 
-    # positions
+
+def pack_segment(lay: Layout, blob: np.ndarray, seg: int, Kh, Vh, bits_tok, bits_chan):
+    """Write one segment's descriptor and slot into `blob` (uint8 array), the
+    content of segment_content placed in the segment's fixed-size slot: V rows
+    group after group (each group 256-byte aligned), the K records of all kept
+    tokens back to back in kept order, the positions."""
+    base = lay.slot_base(seg)
+    sc = segment_content(Kh, Vh, bits_tok, bits_chan)
+    off_v = []
+    cur = base + lay.off_v
+    for g in range(4):
+        off_v.append(cur)
+        blob[cur:cur + sc["v_rows"][g].size] = sc["v_rows"][g]
+        cur = _align(cur + sc["v_rows"][g].size)
+    off_rec = cur = base + lay.off_krec
+    for g in range(4):
+        r = sc["records"][g].reshape(-1).view(np.uint8)
+        blob[cur:cur + r.size] = r
+        cur += r.size
     pos0 = base + lay.off_pos
-    blob[pos0: pos0 + 4 * nk] = kept.astype(np.int32).view(np.uint8)
-
-    # descriptor
+    blob[pos0: pos0 + 4 * sc["n_kept"]] = sc["positions"].view(np.uint8)
     dsc = np.zeros(DESC_BYTES, np.uint8)
-    i32 = [len(g) for g in groups] + [nk] + n_chan + [4 * rec_words, lay.cap, 0]
+    i32 = sc["n_tok"] + [sc["n_kept"]] + sc["n_chan"] + [sc["rec"], lay.cap, 0]
     dsc[0:48] = np.array(i32, np.int32).view(np.uint8)
     u64 = off_v + [off_rec, pos0, base + lay.off_kc, base + lay.off_vc]
     dsc[48:112] = np.array(u64, np.uint64).view(np.uint8)
-    dsc[128:256] = perm
+    dsc[128:256] = sc["perm"]
     d0 = lay.desc_offset + seg * DESC_BYTES
     blob[d0:d0 + DESC_BYTES] = dsc
 
@@ -643,36 +655,29 @@ def read_descriptor(blob, lay: Layout, seg: int) -> dict:
                 perm=blob[d0 + 128:d0 + 256].copy())
 
 
-def unpack_segment(blob, lay: Layout, seg: int):
-    """Dequantized kept rows of one segment, in kept order.
+def dequantize_content(n_tok, n_chan, rec, perm, v_rows, words):
+    """Dequantized kept rows from a segment's content (any placement).
 
-    Returns (K_hat [n_kept][128] float32 with 0 on 0-bit channels,
-    V_hat [n_kept][128] float32, positions [n_kept] int32, bits [n_kept]).
-    """
-    ds = read_descriptor(blob, lay, seg)
-    nk, rec = ds["n_kept"], ds["rec"]
-    n16, n8, n4, n2 = ds["n_chan"]
-    w16, w8, w4, w2, n_meta = record_words(ds["n_chan"])
-    n_a = nk - ds["n_tok"][3]
-    ra = _u32(blob, ds["off_krec"], n_a * rec // 4).reshape(n_a, rec // 4)
-    rb = _u32(blob, ds["off_krec"] + n_a * rec, (nk - n_a) * (rec // 4 - 1)).reshape(nk - n_a, rec // 4 - 1)
-    words = np.concatenate([ra, np.concatenate([rb, np.zeros((nk - n_a, 1), np.uint32)], axis=1)])
+    v_rows: the 4 groups' V row bytes; words: uint32 [n_kept][rec/4] records
+    in kept order (a 16-bit token's missing V word as 0).  Returns (K_hat,
+    V_hat) float32 [n_kept][128], K_hat in original channel order with 0 on
+    0-bit channels."""
+    nk = sum(n_tok)
+    n16, n8, n4, n2 = n_chan
+    w16, w8, w4, w2, n_meta = record_words(n_chan)
     vs, vz = _half_pairs(words[:, -1])
-    tb = np.concatenate([np.full(n, b, np.int32) for n, b in zip(ds["n_tok"], (2, 4, 8, 16))])
-    # V rows
     Vh = np.zeros((nk, D), np.float32)
     i = 0
     for gi, b in enumerate((2, 4, 8, 16)):
-        n = ds["n_tok"][gi]
+        n = n_tok[gi]
         row = D * b // 8
-        raw = blob[ds["off_v"][gi]:ds["off_v"][gi] + n * row]
+        raw = np.asarray(v_rows[gi][:n * row], np.uint8)
         if b == 16:
             Vh[i:i + n] = raw.view(np.float16).reshape(n, D).astype(np.float32)
         else:
             codes = unpack_codes(raw.view(np.uint32).reshape(n, row // 4), b, D)
             Vh[i:i + n] = dequantize(codes, vs[i:i + n, None], vz[i:i + n, None])
         i += n
-    # K records
     kp = np.zeros((nk, D), np.float32)
     kp[:, :n16] = words[:, :w16].copy().view(np.float16)[:, :n16].astype(np.float32)
     wo, mo, c0 = w16, w16 + w8 + w4 + w2, n16
@@ -683,7 +688,25 @@ def unpack_segment(blob, lay: Layout, seg: int):
         kp[:, c0:c0 + n] = dequantize(unpack_codes(words[:, wo:wo + nw], b, n), s[:, None], z[:, None])
         mo, wo, c0 = mo + 1, wo + nw, c0 + n
     Kh = np.zeros((nk, D), np.float32)
-    Kh[:, ds["perm"].astype(np.int64)] = kp
+    Kh[:, np.asarray(perm).astype(np.int64)] = kp
+    return Kh, Vh
+
+
+def unpack_segment(blob, lay: Layout, seg: int):
+    """Dequantized kept rows of one segment, in kept order.
+
+    Returns (K_hat [n_kept][128] float32 with 0 on 0-bit channels,
+    V_hat [n_kept][128] float32, positions [n_kept] int32, bits [n_kept]).
+    """
+    ds = read_descriptor(blob, lay, seg)
+    nk, rec = ds["n_kept"], ds["rec"]
+    n_a = nk - ds["n_tok"][3]
+    ra = _u32(blob, ds["off_krec"], n_a * rec // 4).reshape(n_a, rec // 4)
+    rb = _u32(blob, ds["off_krec"] + n_a * rec, (nk - n_a) * (rec // 4 - 1)).reshape(nk - n_a, rec // 4 - 1)
+    words = np.concatenate([ra, np.concatenate([rb, np.zeros((nk - n_a, 1), np.uint32)], axis=1)])
+    tb = np.concatenate([np.full(n, b, np.int32) for n, b in zip(ds["n_tok"], (2, 4, 8, 16))])
+    v_rows = [blob[ds["off_v"][g]:ds["off_v"][g] + ds["n_tok"][g] * D * (2 << g) // 8] for g in range(4)]
+    Kh, Vh = dequantize_content(ds["n_tok"], ds["n_chan"], rec, ds["perm"], v_rows, words)
     pos = blob[ds["off_pos"]:ds["off_pos"] + 4 * nk].view(np.int32).copy()
     return Kh, Vh, pos, tb
 
@@ -873,6 +896,263 @@ def rollover_pack(blob, lay: Layout, gen: int, w_tok, var_tok, w_chan):
         blob[ds["off_vc"]:ds["off_vc"] + lay.cap * D * 2] = 0
     blob[92:96] = np.array([gen + 1], np.int32).view(np.uint8)
     return allocs
+
+
+# --------------------------------------------------------------------------
+# Paged cache for batched serving ([KVMATH] "Solusi 1": the KV cache cut into
+# fixed-size blocks of a shared pool, non-contiguous, found through a block
+# table per sequence; here the blocks hold the packed zones of [RDKV] 2.3)
+# --------------------------------------------------------------------------
+
+PAGED_MAGIC = 0x504B4452      # "RDKP" little-endian
+PAGE_BYTES = 32768
+TILE = 64
+# Regions of a segment, each an array of 64-row tiles laid page by page
+# (a tile never straddles a page; a page holds PAGE_BYTES // tile bytes
+# tiles): V rows of the 2/4/8/16-bit groups, K records of the same groups,
+# zone-C keys, zone-C values, kept positions.
+N_REGIONS = 11
+R_V, R_REC, R_KC, R_VC, R_POS = 0, 4, 8, 9, 10
+
+
+def region_tile_bytes(region: int, rec: int) -> int:
+    """Bytes of a 64-row tile of a region; rec = bytes of a zone-A K record."""
+    if region < R_REC:
+        return TILE * D * (2 << region) // 8
+    if region < R_KC:
+        return TILE * (rec - 4 * (region - R_REC == 3))
+    if region < R_POS:
+        return TILE * D * 2
+    return TILE * 4
+
+
+def region_pages(rows: int, tile_bytes: int) -> int:
+    if rows <= 0 or tile_bytes <= 0:
+        return 0
+    return _cdiv(_cdiv(rows, TILE), PAGE_BYTES // tile_bytes)
+
+
+def segment_region_pages(n_tok, n_kept, rec, cap):
+    """Pages of each of the 11 regions of a segment."""
+    rows = list(n_tok) + list(n_tok) + [cap, cap, n_kept]
+    return [region_pages(rows[r], region_tile_bytes(r, rec)) for r in range(N_REGIONS)]
+
+
+class PagedLayout:
+    """A paged cache: 256-byte header, one 256-byte descriptor per segment
+    slot (sequence slot s, layer, KV head), the block table int32
+    [n_seg][max_pages] (physical page of each virtual page of a segment, -1
+    where unused), then the pool of n_pages pages of PAGE_BYTES.  Sequences
+    come and go: each is packed with its own prefill length and budgets (up
+    to the layout's bounds) into pages its caller gives it.
+    """
+
+    def __init__(self, n_seq, n_layers, n_q_heads, n_kv_heads, n_tokens_max, budget_v_max, budget_k_max,
+                 zone_c_capacity, n_pages):
+        self.S, self.L, self.Hq, self.Hkv = n_seq, n_layers, n_q_heads, n_kv_heads
+        self.N, self.bv, self.bk, self.cap, self.n_pages = n_tokens_max, budget_v_max, budget_k_max, \
+            zone_c_capacity, n_pages
+        self.n_seg = n_seq * n_layers * n_kv_heads
+        nk_max = min(n_tokens_max, budget_v_max // 2)
+        rec_max = 4 * ((min(budget_k_max, 16 * D) + 98) // 32 + 4)
+        rows = [min(n_tokens_max, budget_v_max // (2 << g)) for g in range(4)]
+        self.max_pages = (sum(region_pages(rows[g], region_tile_bytes(R_V + g, rec_max)) for g in range(4))
+                          + sum(region_pages(rows[g], TILE * rec_max) for g in range(4))
+                          + 2 * region_pages(zone_c_capacity, TILE * D * 2) + region_pages(nk_max, TILE * 4))
+        self.desc_offset = HEADER_BYTES
+        self.table_offset = _align(HEADER_BYTES + DESC_BYTES * self.n_seg)
+        self.pool_offset = _align(self.table_offset + 4 * self.n_seg * self.max_pages, 4096)
+        self.cache_bytes = self.pool_offset + n_pages * PAGE_BYTES
+
+    def seg_index(self, s, l, h):
+        return (s * self.L + l) * self.Hkv + h
+
+    def header_bytes(self) -> bytes:
+        h = np.zeros(HEADER_BYTES, np.uint8)
+        i32 = [PAGED_MAGIC, VERSION, self.S, self.L, self.Hq, self.Hkv, D, self.cap]
+        h[0:32] = np.array(i32, np.uint32).view(np.uint8)
+        i64 = [self.N, self.bv, self.bk, self.n_seg, self.desc_offset, self.table_offset, self.pool_offset,
+               self.max_pages, self.n_pages, PAGE_BYTES]
+        h[32:112] = np.array(i64, np.int64).view(np.uint8)
+        return h.tobytes()
+
+
+def paged_empty(play: PagedLayout) -> np.ndarray:
+    """A paged cache with every sequence slot free: header, zero descriptors
+    (zone-C capacity 0 marks a free slot), block table all -1, pool zero."""
+    blob = np.zeros(play.cache_bytes, np.uint8)
+    blob[:HEADER_BYTES] = np.frombuffer(play.header_bytes(), np.uint8)
+    blob[play.table_offset:play.table_offset + 4 * play.n_seg * play.max_pages] = 0xFF
+    return blob
+
+
+def _paged_table(blob, play: PagedLayout, seg: int) -> np.ndarray:
+    o = play.table_offset + 4 * seg * play.max_pages
+    return blob[o:o + 4 * play.max_pages].view(np.int32)
+
+
+def paged_pages_needed(play: PagedLayout, content: dict) -> int:
+    """Pages one segment of this content takes (its zone C included)."""
+    return sum(segment_region_pages(content["n_tok"], content["n_kept"], content["rec"], play.cap))
+
+
+def _tile_offset(blob, play: PagedLayout, seg: int, vpage: int, tile: int, tile_bytes: int) -> int:
+    """Blob offset of tile `tile` of the region starting at virtual page vpage."""
+    tpp = PAGE_BYTES // tile_bytes
+    phys = int(_paged_table(blob, play, seg)[vpage + tile // tpp])
+    if not (0 <= phys < play.n_pages):
+        raise ValueError("block table entry outside the pool")
+    return play.pool_offset + phys * PAGE_BYTES + (tile % tpp) * tile_bytes
+
+
+def _region_rw(blob, play, seg, vpage, tile_bytes, row_bytes, nrows, data=None):
+    """Write (data given) or read the nrows rows of a region, tile by tile.
+    Rows of 0 bytes (the K record of a 16-bit token when every K channel has
+    0 bits) take no pages."""
+    if row_bytes == 0:
+        return None if data is not None else np.zeros(0, np.uint8)
+    out = []
+    for t in range(_cdiv(nrows, TILE)):
+        r = min(TILE, nrows - t * TILE)
+        o = _tile_offset(blob, play, seg, vpage, t, tile_bytes)
+        if data is None:
+            out.append(blob[o:o + r * row_bytes].copy())
+        else:
+            blob[o:o + r * row_bytes] = data[t * TILE * row_bytes:(t * TILE + r) * row_bytes]
+    return None if data is not None else (np.concatenate(out) if out else np.zeros(0, np.uint8))
+
+
+def paged_pack_sequence(blob, play: PagedLayout, s: int, K, V, bits_tok, bits_chan, pages):
+    """Pack one sequence into slot s of the paged cache.
+
+    K, V: fp16 [L][Hkv][N_s][d] (the sequence's own prefill length N_s <= the
+    layout's bound); bits_tok [L][Hkv][N_s], bits_chan [L][Hkv][d] within the
+    layout's budget bounds; pages: for each of its L*Hkv segments (layer-major,
+    then KV head) the list of physical pages it takes, paged_pages_needed of
+    them.  Regions are laid out in order, each from a fresh virtual page;
+    zone C starts empty.
+    """
+    for l in range(play.L):
+        for h in range(play.Hkv):
+            seg = play.seg_index(s, l, h)
+            sc = segment_content(K[l][h], V[l][h], bits_tok[l][h], bits_chan[l][h])
+            rp = segment_region_pages(sc["n_tok"], sc["n_kept"], sc["rec"], play.cap)
+            pg = list(pages[l * play.Hkv + h])
+            if len(pg) != sum(rp) or sum(rp) > play.max_pages or sc["n_kept"] > min(play.N, play.bv // 2) \
+                    or sc["rec"] > 4 * ((min(play.bk, 16 * D) + 98) // 32 + 4):
+                raise ValueError("allocation beyond the layout's bounds or wrong page count")
+            table = _paged_table(blob, play, seg)
+            table[:] = -1
+            table[:len(pg)] = pg
+            vpage = np.concatenate([[0], np.cumsum(rp)[:-1]]).astype(np.int64)
+            for g in range(4):
+                rb = D * (2 << g) // 8
+                _region_rw(blob, play, seg, int(vpage[R_V + g]), region_tile_bytes(R_V + g, sc["rec"]), rb,
+                           sc["n_tok"][g], sc["v_rows"][g])
+                recb = sc["rec"] - 4 * (g == 3)
+                _region_rw(blob, play, seg, int(vpage[R_REC + g]), region_tile_bytes(R_REC + g, sc["rec"]), recb,
+                           sc["n_tok"][g], sc["records"][g].reshape(-1).view(np.uint8))
+            zero = np.zeros(play.cap * D * 2, np.uint8)
+            for r in (R_KC, R_VC):
+                _region_rw(blob, play, seg, int(vpage[r]), region_tile_bytes(r, sc["rec"]), D * 2, play.cap, zero)
+            _region_rw(blob, play, seg, int(vpage[R_POS]), TILE * 4, 4, sc["n_kept"], sc["positions"].view(np.uint8))
+            dsc = np.zeros(DESC_BYTES, np.uint8)
+            i32 = sc["n_tok"] + [sc["n_kept"]] + sc["n_chan"] + [sc["rec"], play.cap, 0]
+            dsc[0:48] = np.array(i32, np.int32).view(np.uint8)
+            dsc[48:96] = np.array(list(vpage) + [sum(rp)], np.int32).view(np.uint8)
+            dsc[128:256] = sc["perm"]
+            d0 = play.desc_offset + seg * DESC_BYTES
+            blob[d0:d0 + DESC_BYTES] = dsc
+
+
+def paged_release_sequence(blob, play: PagedLayout, s: int):
+    """Free slot s: its descriptors become empty (capacity 0) and its block
+    table rows -1.  Returns the physical pages it held, for the caller to reuse."""
+    freed = []
+    for l in range(play.L):
+        for h in range(play.Hkv):
+            seg = play.seg_index(s, l, h)
+            t = _paged_table(blob, play, seg)
+            freed += [int(x) for x in t if x >= 0]
+            t[:] = -1
+            d0 = play.desc_offset + seg * DESC_BYTES
+            blob[d0:d0 + DESC_BYTES] = 0
+    return freed
+
+
+def paged_read_descriptor(blob, play: PagedLayout, seg: int) -> dict:
+    d0 = play.desc_offset + seg * DESC_BYTES
+    i32 = blob[d0:d0 + 96].view(np.int32)
+    return dict(n_tok=[int(x) for x in i32[0:4]], n_kept=int(i32[4]), n_chan=[int(x) for x in i32[5:9]],
+                rec=int(i32[9]), cap=int(i32[10]), flags=int(i32[11]), vpage=[int(x) for x in i32[12:23]],
+                n_pages=int(i32[23]), perm=blob[d0 + 128:d0 + 256].copy())
+
+
+def paged_segment_rows(blob, play: PagedLayout, seg: int, n_c: int):
+    """Dequantized kept rows and the first n_c zone-C rows of a segment, read
+    through its block table: (K_hat, V_hat, K_C, V_C) float32."""
+    ds = paged_read_descriptor(blob, play, seg)
+    if ds["cap"] == 0:
+        z = np.zeros((0, D), np.float32)
+        return z, z, z, z
+    rec, vp = ds["rec"], ds["vpage"]
+    v_rows = [_region_rw(blob, play, seg, vp[R_V + g], region_tile_bytes(R_V + g, rec), D * (2 << g) // 8,
+                         ds["n_tok"][g]) for g in range(4)]
+    words = []
+    for g in range(4):
+        recb = rec - 4 * (g == 3)
+        w = _region_rw(blob, play, seg, vp[R_REC + g], region_tile_bytes(R_REC + g, rec), recb,
+                       ds["n_tok"][g]).view(np.uint32).reshape(ds["n_tok"][g], recb // 4)
+        if g == 3:
+            w = np.concatenate([w, np.zeros((w.shape[0], 1), np.uint32)], axis=1)
+        words.append(w)
+    Kh, Vh = dequantize_content(ds["n_tok"], ds["n_chan"], rec, ds["perm"], v_rows, np.concatenate(words))
+    kc = _region_rw(blob, play, seg, vp[R_KC], TILE * D * 2, D * 2, n_c).view(np.float16).reshape(n_c, D)
+    vc = _region_rw(blob, play, seg, vp[R_VC], TILE * D * 2, D * 2, n_c).view(np.float16).reshape(n_c, D)
+    return Kh, Vh, kc.astype(np.float32), vc.astype(np.float32)
+
+
+def paged_positions(blob, play: PagedLayout, seg: int) -> np.ndarray:
+    ds = paged_read_descriptor(blob, play, seg)
+    return _region_rw(blob, play, seg, ds["vpage"][R_POS], TILE * 4, 4, ds["n_kept"]).view(np.int32)
+
+
+def paged_write_zone_c(blob, play: PagedLayout, seg: int, row: int, k, v):
+    """Write fp16 k, v [d] at zone-C row `row` of a segment, through its pages."""
+    ds = paged_read_descriptor(blob, play, seg)
+    for r, src in ((R_KC, k), (R_VC, v)):
+        o = _tile_offset(blob, play, seg, ds["vpage"][r], row // TILE, TILE * D * 2) + (row % TILE) * D * 2
+        blob[o:o + D * 2] = np.asarray(src, np.float16).view(np.uint8)
+
+
+def paged_decode_step(blob, play: PagedLayout, q, c_len, k_new=None, v_new=None):
+    """One decode step over every sequence slot in use; out [S][L][Hq][d].
+
+    c_len[s]: zone-C rows of sequence s before the step.  With k_new/v_new
+    (fp16 [S][L][Hkv][d]) each sequence in use appends its token at its own row
+    c_len[s] and attends c_len[s] + 1 rows.  Attention as decode_step: kept
+    tokens (dequantized) and zone C, evicted tokens absent; free slots give 0.
+    """
+    G = play.Hq // play.Hkv
+    out = np.zeros((play.S, play.L, play.Hq, D))
+    for s in range(play.S):
+        for l in range(play.L):
+            for h in range(play.Hkv):
+                seg = play.seg_index(s, l, h)
+                ds = paged_read_descriptor(blob, play, seg)
+                if ds["cap"] == 0:
+                    continue
+                n_c = int(c_len[s])
+                if k_new is not None:
+                    if not (0 <= n_c < play.cap):
+                        raise ValueError("zone C is full")
+                    paged_write_zone_c(blob, play, seg, n_c, k_new[s, l, h], v_new[s, l, h])
+                    n_c += 1
+                Kh, Vh, kc, vc = paged_segment_rows(blob, play, seg, n_c)
+                out[s, l, h * G:(h + 1) * G] = attention(np.asarray(q[s, l, h * G:(h + 1) * G], np.float16)
+                                                         .astype(np.float64), np.concatenate([Kh, kc]),
+                                                         np.concatenate([Vh, vc]))
+    return out
 
 
 # --------------------------------------------------------------------------
