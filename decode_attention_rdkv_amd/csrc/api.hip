@@ -497,6 +497,206 @@ rdkv_status rdkv_rollover(const rdkv_layout* layout, void* cache, size_t cache_b
   return hip_status(launch_rollover(r, g, generation, static_cast<uint8_t*>(workspace), stream));
 }
 
+// ------------------------------------------------------------------ paged cache
+
+rdkv_status rdkv_paged_layout_init(const rdkv_dims* dims_max, int64_t budget_v_max, int64_t budget_k_max,
+                                   int32_t zone_c_capacity, int64_t n_pages, rdkv_paged_layout* out) {
+  if (!out) return RDKV_ERR_NULL;
+  rdkv_layout b;   // the bounds, as a contiguous layout of the same shape
+  rdkv_status st = layout_init(dims_max, budget_v_max, budget_k_max, zone_c_capacity, 0, 0, 0, &b);
+  if (st != RDKV_OK) return st;
+  if (dims_max->n_seq > kMaxPagedSeqs || n_pages < 1 || n_pages > (int64_t(1) << 30)) return RDKV_ERR_SHAPE;
+  rdkv_paged_layout P;
+  std::memset(&P, 0, sizeof(P));
+  P.dims = *dims_max;
+  P.budget_v_max = budget_v_max;
+  P.budget_k_max = budget_k_max;
+  P.n_seg = b.n_seg;
+  P.n_pages = n_pages;
+  P.nk_max = b.nk_max;
+  P.zone_c_capacity = zone_c_capacity;
+  P.rec_max = b.rec_max;
+  P.token_slots = b.token_slots;
+  P.chunk_tok2 = b.chunk_tok2;
+  P.max_chunks = b.max_chunks;
+  // block-table width: every region at its own worst case within the bounds
+  const int64_t N = dims_max->n_tokens;
+  int64_t pages = 0;
+  for (int g = 0; g < 4; ++g) {
+    const int64_t rows = std::min<int64_t>(N, budget_v_max / (int64_t(2) << g));
+    pages += paged_region_pages(rows, paged_tile_bytes(kRegV + g, 0));
+    pages += paged_region_pages(rows, uint32_t(kPagedTile) * uint32_t(b.rec_max));
+  }
+  pages += 2 * paged_region_pages(zone_c_capacity, paged_tile_bytes(kRegKC, 0));
+  pages += paged_region_pages(b.nk_max, paged_tile_bytes(kRegPos, 0));
+  P.max_pages = std::max<int64_t>(pages, 1);
+  P.table_offset = align_up(kHeaderBytes + uint64_t(kDescBytes) * P.n_seg, kAlign);
+  P.pool_offset = align_up(P.table_offset + 4 * uint64_t(P.n_seg) * P.max_pages, 4096);
+  P.cache_bytes = P.pool_offset + uint64_t(n_pages) * kPageBytes;
+  const int G = dims_max->n_q_heads / dims_max->n_kv_heads;
+  P.decode_workspace_bytes = uint64_t(P.n_seg) * P.max_chunks * G * kPartialFloats * sizeof(float);
+  *out = P;
+  return RDKV_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+rdkv_status check_paged(const rdkv_paged_layout* pl) {
+  if (!pl) return RDKV_ERR_NULL;
+  rdkv_paged_layout ref;
+  rdkv_status st = rdkv_paged_layout_init(&pl->dims, pl->budget_v_max, pl->budget_k_max, pl->zone_c_capacity,
+                                          pl->n_pages, &ref);
+  if (st != RDKV_OK) return st;
+  if (std::memcmp(&ref, pl, sizeof(ref)) != 0) return RDKV_ERR_SHAPE;
+  return RDKV_OK;
+}
+
+// The contiguous layout one sequence is staged in: its own length and
+// budgets, within the paged layout's bounds, no zone C.
+rdkv_status staging_layout(const rdkv_paged_layout* pl, int64_t n_tokens, int64_t budget_v, int64_t budget_k,
+                           rdkv_layout* out) {
+  if (n_tokens < 1 || n_tokens > pl->dims.n_tokens) return RDKV_ERR_SHAPE;
+  if (budget_v < 0 || budget_k < 0 || budget_v > pl->budget_v_max || budget_k > pl->budget_k_max)
+    return RDKV_ERR_BUDGET;
+  rdkv_dims d = pl->dims;
+  d.n_seq = 1;
+  d.n_tokens = n_tokens;
+  return layout_init(&d, budget_v, budget_k, 0, 0, 0, 0, out);
+}
+
+}  // namespace
+
+extern "C" {
+
+rdkv_status rdkv_paged_cache_init(const rdkv_paged_layout* layout, void* cache, size_t cache_bytes,
+                                  hipStream_t stream) {
+  rdkv_status st = check_paged(layout);
+  if (st != RDKV_OK) return st;
+  if (!cache) return RDKV_ERR_NULL;
+  if (!aligned16(cache)) return RDKV_ERR_ALIGN;
+  if (cache_bytes < layout->cache_bytes) return RDKV_ERR_WORKSPACE;
+  return hip_status(launch_paged_init(static_cast<uint8_t*>(cache), *layout, stream));
+}
+
+size_t rdkv_paged_staging_bytes(const rdkv_paged_layout* layout, int64_t n_tokens, int64_t budget_v,
+                                int64_t budget_k) {
+  if (check_paged(layout) != RDKV_OK) return 0;
+  rdkv_layout s;
+  if (staging_layout(layout, n_tokens, budget_v, budget_k, &s) != RDKV_OK) return 0;
+  return s.cache_bytes;
+}
+
+rdkv_status rdkv_paged_stage(const rdkv_paged_layout* layout, int64_t n_tokens, int64_t budget_v,
+                             int64_t budget_k, const void* K, const void* V, const uint8_t* bits_tok,
+                             const uint8_t* bits_chan, void* staging, size_t staging_bytes,
+                             int32_t* pages_needed, hipStream_t stream) {
+  rdkv_status st = check_paged(layout);
+  if (st != RDKV_OK) return st;
+  rdkv_layout sl;
+  st = staging_layout(layout, n_tokens, budget_v, budget_k, &sl);
+  if (st != RDKV_OK) return st;
+  if (!K || !V || !bits_tok || !bits_chan || !staging || !pages_needed) return RDKV_ERR_NULL;
+  for (const void* ptr : {K, V, (const void*)bits_tok, (const void*)bits_chan, (const void*)staging,
+                          (const void*)pages_needed})
+    if (!aligned16(ptr)) return RDKV_ERR_ALIGN;
+  if (staging_bytes < sl.cache_bytes) return RDKV_ERR_WORKSPACE;
+  hipError_t e = launch_cache_init(static_cast<uint8_t*>(staging), sl, nullptr, stream);
+  if (e != hipSuccess) return RDKV_ERR_HIP;
+  PackParams pp;
+  pp.cache = static_cast<uint8_t*>(staging);
+  pp.cache_bytes = staging_bytes;
+  pp.lay = &sl;
+  pp.layer_begin = 0;
+  pp.n_layers_in = sl.dims.n_layers;
+  pp.K = static_cast<const __half*>(K);
+  pp.V = static_cast<const __half*>(V);
+  pp.bits_tok = bits_tok;
+  pp.bits_chan = bits_chan;
+  e = launch_pack(pp, stream);
+  if (e != hipSuccess) return RDKV_ERR_HIP;
+  PagedPackParams q{nullptr, layout, static_cast<const uint8_t*>(staging), sl.cache_bytes, 0, nullptr, pages_needed};
+  return hip_status(launch_paged_plan(q, stream));
+}
+
+rdkv_status rdkv_paged_commit(const rdkv_paged_layout* layout, int32_t seq, int64_t n_tokens, int64_t budget_v,
+                              int64_t budget_k, const void* staging, size_t staging_bytes, const int32_t* pages,
+                              void* cache, size_t cache_bytes, hipStream_t stream) {
+  rdkv_status st = check_paged(layout);
+  if (st != RDKV_OK) return st;
+  rdkv_layout sl;
+  st = staging_layout(layout, n_tokens, budget_v, budget_k, &sl);
+  if (st != RDKV_OK) return st;
+  if (!staging || !pages || !cache) return RDKV_ERR_NULL;
+  for (const void* ptr : {staging, (const void*)pages, (const void*)cache})
+    if (!aligned16(ptr)) return RDKV_ERR_ALIGN;
+  if (staging_bytes < sl.cache_bytes || cache_bytes < layout->cache_bytes) return RDKV_ERR_WORKSPACE;
+  if (seq < 0 || seq >= layout->dims.n_seq) return RDKV_ERR_SHAPE;
+  PagedPackParams q{static_cast<uint8_t*>(cache), layout, static_cast<const uint8_t*>(staging), sl.cache_bytes, seq,
+                    pages, nullptr};
+  return hip_status(launch_paged_commit(q, stream));
+}
+
+rdkv_status rdkv_paged_release(const rdkv_paged_layout* layout, int32_t seq, void* cache, size_t cache_bytes,
+                               hipStream_t stream) {
+  rdkv_status st = check_paged(layout);
+  if (st != RDKV_OK) return st;
+  if (!cache) return RDKV_ERR_NULL;
+  if (!aligned16(cache)) return RDKV_ERR_ALIGN;
+  if (cache_bytes < layout->cache_bytes) return RDKV_ERR_WORKSPACE;
+  if (seq < 0 || seq >= layout->dims.n_seq) return RDKV_ERR_SHAPE;
+  return hip_status(launch_paged_release(static_cast<uint8_t*>(cache), *layout, seq, stream));
+}
+
+rdkv_status rdkv_paged_decode(const rdkv_paged_layout* layout, void* cache, size_t cache_bytes,
+                              const int32_t* c_len, const void* q, const void* k_new, const void* v_new,
+                              float* out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  rdkv_status st = check_paged(layout);
+  if (st != RDKV_OK) return st;
+  if (!cache || !c_len || !q || !out || !workspace) return RDKV_ERR_NULL;
+  if ((k_new == nullptr) != (v_new == nullptr)) return RDKV_ERR_NULL;
+  for (const void* ptr : {(const void*)cache, q, (const void*)out, (const void*)workspace})
+    if (!aligned16(ptr)) return RDKV_ERR_ALIGN;
+  if (k_new && (!aligned16(k_new) || !aligned16(v_new))) return RDKV_ERR_ALIGN;
+  if (cache_bytes < layout->cache_bytes || workspace_bytes < layout->decode_workspace_bytes)
+    return RDKV_ERR_WORKSPACE;
+  const int append = k_new != nullptr;
+  PagedSeqLens lens;
+  std::memset(&lens, 0, sizeof(lens));
+  for (int s = 0; s < layout->dims.n_seq; ++s) {
+    if (c_len[s] < 0 || int64_t(c_len[s]) + append > layout->zone_c_capacity) return RDKV_ERR_CAPACITY;
+    lens.c_len[s] = c_len[s];
+  }
+  DecodeParams p{};
+  p.cache = static_cast<uint8_t*>(cache);
+  p.cache_bytes = layout->cache_bytes;
+  p.main_bytes = layout->cache_bytes;
+  p.n_seg = layout->n_seg;
+  p.nk_max = layout->nk_max;
+  p.max_chunks = layout->max_chunks;
+  p.token_slots = layout->token_slots;
+  p.chunk_tok2 = layout->chunk_tok2;
+  p.rec_max = layout->rec_max;
+  p.group = layout->dims.n_q_heads / layout->dims.n_kv_heads;
+  p.zc_cap = layout->zone_c_capacity;
+  p.append = append;
+  p.q = static_cast<const __half*>(q);
+  p.k_new = static_cast<const __half*>(k_new);
+  p.v_new = static_cast<const __half*>(v_new);
+  p.partials = static_cast<float*>(workspace);
+  p.out = out;
+  p.paged = 1;
+  p.seg_per_seq = layout->dims.n_layers * layout->dims.n_kv_heads;
+  p.max_pages = int32_t(layout->max_pages);
+  p.pool_pages = layout->n_pages;
+  p.table_offset = layout->table_offset;
+  p.pool_offset = layout->pool_offset;
+  hipError_t e = launch_decode_chunks_paged(p, lens, stream);
+  if (e == hipSuccess) e = launch_decode_merge(p, stream);
+  return hip_status(e);
+}
+
 rdkv_status rdkv_unpack(const rdkv_layout* layout, const void* cache, size_t cache_bytes, int64_t seg,
                         float* k_hat, float* v_hat, hipStream_t stream) {
   rdkv_status st = check_layout(layout);

@@ -109,6 +109,9 @@ struct SegInfo {
   uint64_t off_v[4], off_krec, off_kc, off_vc;   // from the cache base
   uint64_t desc;                                 // offset of the segment's descriptor
   bool zc_ok;
+  // paged cache: the segment's block-table row and each region's first virtual page
+  const int32_t* table;
+  int vpage[kRegions];
 };
 
 // One blob inside the cache: the prefill generation (base 0) or a rolled-over
@@ -134,6 +137,9 @@ __device__ inline SegInfo load_segment(const DecodeParams& p, const BlobRef& b, 
   const uint8_t* d = p.cache + b.base + kHeaderBytes + uint64_t(seg) * kDescBytes;
   SegInfo s;
   s.desc = b.base + kHeaderBytes + uint64_t(seg) * kDescBytes;
+  s.table = nullptr;
+#pragma unroll
+  for (int r = 0; r < kRegions; ++r) s.vpage[r] = 0;
   int n_kept_sum = 0, n_chan_sum = 0;
   bool ok = true;
 #pragma unroll
@@ -180,18 +186,90 @@ __device__ inline SegInfo load_segment(const DecodeParams& p, const BlobRef& b, 
   return s;
 }
 
+// Blob offset of tile `tile` of a paged segment's region that starts at
+// virtual page vp0 (tpp tiles of tile_bytes per page).  An entry outside the
+// block table or the pool gives page 0 and ok = false: callers then read
+// nothing through it.
+__device__ inline uint64_t paged_tile(const DecodeParams& p, const int32_t* table, int vp0, int tile, uint32_t tpp,
+                                      uint32_t tile_bytes, bool& ok) {
+  const int vp = vp0 + int(uint32_t(tile) / tpp);
+  const int phys = (vp >= 0 && vp < p.max_pages) ? table[vp] : -1;
+  ok = phys >= 0 && phys < p.pool_pages;
+  return p.pool_offset + uint64_t(ok ? phys : 0) * kPageBytes + uint64_t(uint32_t(tile) % tpp) * tile_bytes;
+}
+
+// A paged segment's descriptor (the contiguous fields' meaning for counts,
+// then the regions' first virtual pages).  Anything inconsistent with the
+// layout, or a free slot, reads as an empty segment.  n_c: zone-C rows this
+// step attends; their pages must be in the pool.
+__device__ inline SegInfo load_segment_paged(const DecodeParams& p, int64_t seg, int n_c) {
+  const uint8_t* d = p.cache + kHeaderBytes + uint64_t(seg) * kDescBytes;
+  SegInfo s;
+  s.desc = kHeaderBytes + uint64_t(seg) * kDescBytes;
+  s.table = reinterpret_cast<const int32_t*>(p.cache + p.table_offset) + seg * p.max_pages;
+  int n_kept_sum = 0, n_chan_sum = 0;
+  bool ok = true;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    s.n_tok[i] = *reinterpret_cast<const int32_t*>(d + kDescNTok + 4 * i);
+    s.n_chan[i] = *reinterpret_cast<const int32_t*>(d + kDescNChan + 4 * i);
+    ok = ok && s.n_tok[i] >= 0 && s.n_chan[i] >= 0;
+    n_kept_sum += s.n_tok[i];
+    n_chan_sum += s.n_chan[i];
+  }
+  const int n_kept = *reinterpret_cast<const int32_t*>(d + kDescNKept);
+  const int rec = *reinterpret_cast<const int32_t*>(d + kDescRec);
+  const int cap = *reinterpret_cast<const int32_t*>(d + kDescCap);
+  const int n_pages = *reinterpret_cast<const int32_t*>(d + kPDescNPages);
+  const RecordShape rs = record_shape(s.n_chan[0], s.n_chan[1], s.n_chan[2], s.n_chan[3]);
+  ok = ok && cap == p.zc_cap && n_kept == n_kept_sum && n_kept <= p.nk_max && n_chan_sum <= kHeadDim &&
+       rec == 4 * rs.words_a() && rec <= p.rec_max && n_pages >= 0 && n_pages <= p.max_pages;
+  const int rows[kRegions] = {s.n_tok[0], s.n_tok[1], s.n_tok[2], s.n_tok[3], s.n_tok[0], s.n_tok[1], s.n_tok[2],
+                              s.n_tok[3], cap, cap, n_kept};
+#pragma unroll
+  for (int r = 0; r < kRegions; ++r) {
+    s.vpage[r] = *reinterpret_cast<const int32_t*>(d + kPDescVpage + 4 * r);
+    ok = ok && s.vpage[r] >= 0 && s.vpage[r] + paged_region_pages(rows[r], paged_tile_bytes(r, rec)) <= n_pages;
+  }
+  int n_chunks = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int T = chunk_tokens(p.chunk_tok2, i);
+    n_chunks += (max(s.n_tok[i], 0) + T - 1) / T;
+  }
+  ok = ok && n_chunks <= p.token_slots;
+  if (!ok) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s.n_tok[i] = s.n_chan[i] = 0;
+  }
+  s.rec_a = ok ? rec / 4 : 1;
+  // the zone-C pages this step touches (at most a few)
+  bool zc = ok && n_c <= cap;
+  const int zc_pages = paged_region_pages(n_c, paged_tile_bytes(kRegKC, 0));
+  for (int t = 0; zc && t < zc_pages; ++t) {
+    const int a = s.table[s.vpage[kRegKC] + t], b = s.table[s.vpage[kRegVC] + t];
+    zc = a >= 0 && a < p.pool_pages && b >= 0 && b < p.pool_pages;
+  }
+  s.zc_ok = zc;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s.off_v[i] = 0;
+  s.off_krec = s.off_kc = s.off_vc = 0;
+  return s;
+}
+
 struct Plan {
   int kind;          // 0..3 token group, 4 zone C, -1 none
   int start, end;    // rows of the group (or zone C) in this chunk
   uint64_t vbase;    // blob offset of the group's first V row (or of V_C)
   int64_t rec0;      // word offset of the group's first K record from off_krec
   int rec_words;     // words per record in this group
+  int vp_a, vp_b;    // paged: first virtual page of the group's V rows and K records (or of K_C and V_C)
 };
 
 // Chunk k of a segment's kept tokens: groups 2, 4, 8, 16 bits in turn, each
 // cut into chunks of chunk_tok2 >> g tokens; kind -1 past the last one.
 __device__ inline Plan plan_tokens(const SegInfo& si, int chunk_tok2, int k) {
-  Plan pl{-1, 0, 0, 0, 0, 0};
+  Plan pl{-1, 0, 0, 0, 0, 0, 0, 0};
   int kept = 0;
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
@@ -206,6 +284,8 @@ __device__ inline Plan plan_tokens(const SegInfo& si, int chunk_tok2, int k) {
         // zone-A records come first; the fp16 group's shorter records follow them
         pl.rec0 = int64_t(kept) * si.rec_a;
         pl.rec_words = g < 3 ? si.rec_a : si.rec_a - 1;
+        pl.vp_a = si.vpage[kRegV + g];
+        pl.vp_b = si.vpage[kRegRec + g];
       } else {
         k -= nch;
       }
@@ -217,7 +297,7 @@ __device__ inline Plan plan_tokens(const SegInfo& si, int chunk_tok2, int k) {
 
 // Zone-C chunk k: rows [256 k, min(n_c, 256 (k + 1))); kind -1 past the last.
 __device__ inline Plan plan_zone_c(const SegInfo& si, int n_c, int k) {
-  Plan pl{-1, 0, 0, 0, 0, 0};
+  Plan pl{-1, 0, 0, 0, 0, 0, si.vpage[kRegKC], si.vpage[kRegVC]};
   const int nch = (n_c + kChunkRowsC - 1) / kChunkRowsC;
   if (k < nch) {
     pl.kind = 4;
@@ -709,7 +789,12 @@ __device__ inline void dma_records(const uint8_t* src, uint32_t bytes, uint32_t*
 // end at the chunk's last row, so the rows of a partial tile past the chunk
 // (and the whole of a tile past the wave's last) read as zeros without
 // touching memory: no per-lane clamping, and tile addresses stay scalar.
-template <int G, int B, int SW, bool PIPE>
+//
+// kPaged: the group's V rows and K records are 64-row tiles on pages found
+// through the segment's block table (a chunk starts on a tile boundary, so
+// tile i is the group's tile tile_row(i) / 64, whole on one page); each
+// tile's resource or copy covers just that tile.
+template <int G, int B, int SW, bool PIPE, bool kPaged>
 __device__ void run_group(const DecodeParams& p, const SegInfo& si, const Plan& pl, int64_t seg, Smem<G, SW>& sm) {
   constexpr int GW = kHeadsPerWave<G>, kNS = kStreams<G>, kStride = kTile * kNS;
   const int lane = threadIdx.x & 63, wave = wave_id();
@@ -752,12 +837,25 @@ __device__ void run_group(const DecodeParams& p, const SegInfo& si, const Plan& 
   // word offset (from off_krec) of tile i's first record
   auto rec_word = [&](int i) { return pl.rec0 + int64_t(tile_row(i)) * nw; };
   const uint32_t voff16 = uint32_t(lane) * 16u;
+  // paged: record tiles of 64 * nw words, kPageBytes / that per page
+  const uint32_t rec_tile_bytes = uint32_t(kTile) * 4u * uint32_t(nw);
+  const uint32_t rec_tpp = nw > 0 ? uint32_t(kPageBytes) / rec_tile_bytes : 1u;
+  auto rec_tile = [&](int i, bool& ok) {
+    return paged_tile(p, si.table, pl.vp_b, tile_row(i) / kTile, rec_tpp, rec_tile_bytes, ok);
+  };
   auto fetch_records = [&](int i) {
     if constexpr (SW > 0) {
-      const int64_t w0 = rec_word(i);
-      const int m = int(w0 & 3);                                   // block start within its 16 bytes
       const int rows = tile_rows(i);
-      dma_records<SW>(rbytes + uint64_t(w0 - m) * 4, rows > 0 ? uint32_t(m + rows * nw) * 4u : 0u, stage(i), voff16);
+      if constexpr (kPaged) {
+        bool ok;
+        const uint64_t t = rec_tile(i, ok);
+        dma_records<SW>(p.cache + t, (rows > 0 && ok) ? uint32_t(rows * nw) * 4u : 0u, stage(i), voff16);
+      } else {
+        const int64_t w0 = rec_word(i);
+        const int m = int(w0 & 3);                                 // block start within its 16 bytes
+        dma_records<SW>(rbytes + uint64_t(w0 - m) * 4, rows > 0 ? uint32_t(m + rows * nw) * 4u : 0u, stage(i),
+                        voff16);
+      }
     }
   };
   // V pairs of tile i: one resource per tile, a fixed lane offset, and the
@@ -765,7 +863,14 @@ __device__ void run_group(const DecodeParams& p, const SegInfo& si, const Plan& 
   const uint32_t lane_off = uint32_t(ts * kRowBytes + lane_row_offset<B>(cb));
   const uint32_t sel2 = (cb & 1) ? 0x07060302u : 0x05040100u;      // the lane's half of a 2-bit dword
   auto vrsrc = [&](int i) {
-    return buffer_rsrc(vbase + int64_t(tile_row(i)) * kRowBytes, uint32_t(tile_rows(i) * kRowBytes));
+    if constexpr (kPaged) {
+      constexpr uint32_t kTileBytes = uint32_t(kTile) * kRowBytes;
+      bool ok;
+      const uint64_t t = paged_tile(p, si.table, pl.vp_a, tile_row(i) / kTile, kPageBytes / kTileBytes, kTileBytes, ok);
+      return buffer_rsrc(p.cache + t, ok ? uint32_t(tile_rows(i) * kRowBytes) : 0u);
+    } else {
+      return buffer_rsrc(vbase + int64_t(tile_row(i)) * kRowBytes, uint32_t(tile_rows(i) * kRowBytes));
+    }
   };
   auto load_pair = [&](__amdgpu_buffer_rsrc_t r, int k) {
     return load_vpair_buf<B>(r, lane_off + 4 * k * kRowBytes, lane_off + (4 * k + 32) * kRowBytes);
@@ -798,7 +903,10 @@ __device__ void run_group(const DecodeParams& p, const SegInfo& si, const Plan& 
     // (with SW > 0 and no record words, nothing is read from the stage)
     const uint32_t* my;
     if constexpr (SW > 0) {
-      my = stage(i) + int(rec_word(i) & 3) + lane_rec;
+      my = stage(i) + (kPaged ? 0 : int(rec_word(i) & 3)) + lane_rec;
+    } else if constexpr (kPaged) {
+      bool ok;   // (an entry outside the pool reads page 0: in memory, the segment's output is then wrong)
+      my = reinterpret_cast<const uint32_t*>(p.cache + rec_tile(i, ok)) + (min(b + lane, pl.end - 1) - b) * nw;
     } else {
       my = reinterpret_cast<const uint32_t*>(rbytes) + pl.rec0 + int64_t(min(b + lane, pl.end - 1)) * nw;
     }
@@ -837,8 +945,12 @@ __device__ void run_group(const DecodeParams& p, const SegInfo& si, const Plan& 
 
 // ---------------------------------------------------------------- zone C (fp16 rows, natural order)
 
-template <int G, int SW>
-__device__ void run_zone_c(const DecodeParams& p, const SegInfo& si, int64_t seg, const Plan& pl, Smem<G, SW>& sm) {
+// Zone-C rows [pl.start, pl.end); row c_len comes from k_new / v_new when
+// `append` (this step's new token).  kPaged: rows are 64-row tiles on the
+// segment's pages, one page lookup per tile.
+template <int G, int SW, bool kPaged>
+__device__ void run_zone_c(const DecodeParams& p, const SegInfo& si, int64_t seg, const Plan& pl, int c_len,
+                           bool append, Smem<G, SW>& sm) {
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int cb = lane & 15, ts = lane >> 4;
   const int last = pl.end - 1;
@@ -846,10 +958,17 @@ __device__ void run_zone_c(const DecodeParams& p, const SegInfo& si, int64_t seg
   const uint8_t* vc = p.cache + si.off_vc;
   const uint8_t* knew = reinterpret_cast<const uint8_t*>(p.k_new + seg * kHeadDim);
   const uint8_t* vnew = reinterpret_cast<const uint8_t*>(p.v_new + seg * kHeadDim);
-  auto krow = [&](int r) { return (p.append && r == p.c_len) ? knew : kc + int64_t(r) * kHeadDim * 2; };
-  auto vrow = [&](int r) {
-    r = min(r, last);
-    return (p.append && r == p.c_len) ? vnew : vc + int64_t(r) * kHeadDim * 2;
+  constexpr uint32_t kTileBytes = uint32_t(kTile) * kHeadDim * 2;
+  // Row 0 of the tile holding row `base` (a multiple of 64): every row a
+  // tile step touches lies in that tile, so one lookup per tile; the zone-C
+  // pages were checked when the segment was loaded.
+  auto tile0 = [&](const uint8_t* flat, int vp0, int base) -> const uint8_t* {
+    if constexpr (kPaged) {
+      bool ok;
+      return p.cache + paged_tile(p, si.table, vp0, base / kTile, kPageBytes / kTileBytes, kTileBytes, ok);
+    } else {
+      return flat + int64_t(base) * kHeadDim * 2;
+    }
   };
 
   constexpr int GW = kHeadsPerWave<G>, kNS = kStreams<G>;
@@ -859,11 +978,17 @@ __device__ void run_zone_c(const DecodeParams& p, const SegInfo& si, int64_t seg
   WaveState<GW> st;
   state_init(st);
   for (int base = pl.start + kTile * (wave % kNS); base < pl.end; base += kTile * kNS) {
+    const uint8_t* kt = tile0(kc, pl.vp_a, base);
+    const uint8_t* vt = tile0(vc, pl.vp_b, base);
+    auto vrow = [&](int r) {
+      r = min(r, last);
+      return (append && r == c_len) ? vnew : vt + int64_t(r - base) * kHeadDim * 2;
+    };
     VPair<16> v[kPairsPerLane];
 #pragma unroll
     for (int k = 0; k < kPairsPerLane; ++k) v[k] = load_vpair16(vrow(base + ts + 4 * k), vrow(base + ts + 4 * k + 32), cb);
     const int r = min(base + lane, last);
-    const uint4* k4 = reinterpret_cast<const uint4*>(krow(r));
+    const uint4* k4 = reinterpret_cast<const uint4*>((append && r == c_len) ? knew : kt + int64_t(r - base) * kHeadDim * 2);
     float s[GW];
 #pragma unroll
     for (int g = 0; g < GW; ++g) s[g] = 0.f;
@@ -976,8 +1101,15 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParam
   }
 }
 
-template <int G, int SW>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void decode_chunk_kernel(DecodeParams p) {
+// The zone-C lengths of a paged cache's sequences (a contiguous cache has
+// one, in DecodeParams).
+struct NoSeqLens {};
+template <typename Lens> constexpr bool kIsPaged = std::is_same<Lens, PagedSeqLens>::value;
+
+template <int G, int SW, typename Lens>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void decode_chunk_kernel(DecodeParams p,
+                                                                                                       Lens lens) {
+  constexpr bool kPaged = kIsPaged<Lens>;
   __shared__ Smem<G, SW> sm;
   // Chunk-major order: every segment's first chunk, then every second chunk,
   // ...  The full 2-bit chunks come first and the short tails, fp16 and zone-C
@@ -986,11 +1118,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   // L2 then holds the segment's descriptor and query).
   const int64_t seg = blockIdx.x % p.n_seg;
   const int k = int(blockIdx.x / p.n_seg);
+  // this step's zone C: rows before it and whether it appends one
+  int c_len = p.c_len;
+  bool append = p.append != 0;
+  if constexpr (kPaged) c_len = lens.c_len[seg / p.seg_per_seq];
   // slot k: the prefill tokens' chunks, the generations' chunks, zone C
   const int gen_end = p.token_slots + p.n_gen * p.gen_slots;
   SegInfo si;
   Plan pl;
-  if (k < p.token_slots) {
+  if constexpr (kPaged) {
+    si = load_segment_paged(p, seg, c_len + int(append));
+    if (k < p.token_slots) pl = plan_tokens(si, p.chunk_tok2, k);
+    else pl = plan_zone_c(si, si.zc_ok ? c_len + int(append) : 0, k - gen_end);
+  } else if (k < p.token_slots) {
     si = load_segment(p, main_blob(p), seg, 0);
     pl = plan_tokens(si, p.chunk_tok2, k);
   } else if (k < gen_end) {
@@ -1015,19 +1155,32 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   }
 
   // append the new token to zone C (only the chunk holding row c_len does it)
-  if (pl.kind == 4 && p.append && p.c_len >= pl.start && p.c_len < pl.end) {
-    uint32_t* kc = reinterpret_cast<uint32_t*>(p.cache + si.off_kc) + int64_t(p.c_len) * (kHeadDim / 2);
-    uint32_t* vc = reinterpret_cast<uint32_t*>(p.cache + si.off_vc) + int64_t(p.c_len) * (kHeadDim / 2);
+  if (pl.kind == 4 && append && c_len >= pl.start && c_len < pl.end) {
+    uint32_t *kc, *vc;
+    if constexpr (kPaged) {
+      constexpr uint32_t kTileBytes = uint32_t(kTile) * kHeadDim * 2;
+      bool ok;
+      const uint64_t row = uint64_t(c_len % kTile) * kHeadDim * 2;
+      kc = reinterpret_cast<uint32_t*>(p.cache + row +
+                                       paged_tile(p, si.table, pl.vp_a, c_len / kTile, kPageBytes / kTileBytes,
+                                                  kTileBytes, ok));
+      vc = reinterpret_cast<uint32_t*>(p.cache + row +
+                                       paged_tile(p, si.table, pl.vp_b, c_len / kTile, kPageBytes / kTileBytes,
+                                                  kTileBytes, ok));
+    } else {
+      kc = reinterpret_cast<uint32_t*>(p.cache + si.off_kc) + int64_t(c_len) * (kHeadDim / 2);
+      vc = reinterpret_cast<uint32_t*>(p.cache + si.off_vc) + int64_t(c_len) * (kHeadDim / 2);
+    }
     if (tid < 64) kc[tid] = reinterpret_cast<const uint32_t*>(p.k_new + seg * kHeadDim)[tid];
     else if (tid < 128) vc[tid - 64] = reinterpret_cast<const uint32_t*>(p.v_new + seg * kHeadDim)[tid - 64];
   }
 
   switch (pl.kind) {
-    case 0: run_group<G, 2, SW, true>(p, si, pl, seg, sm); break;
-    case 1: run_group<G, 4, SW, true>(p, si, pl, seg, sm); break;
-    case 2: run_group<G, 8, SW, false>(p, si, pl, seg, sm); break;
-    case 3: run_group<G, 16, SW, false>(p, si, pl, seg, sm); break;
-    default: run_zone_c<G, SW>(p, si, seg, pl, sm); break;
+    case 0: run_group<G, 2, SW, true, kPaged>(p, si, pl, seg, sm); break;
+    case 1: run_group<G, 4, SW, true, kPaged>(p, si, pl, seg, sm); break;
+    case 2: run_group<G, 8, SW, false, kPaged>(p, si, pl, seg, sm); break;
+    case 3: run_group<G, 16, SW, false, kPaged>(p, si, pl, seg, sm); break;
+    default: run_zone_c<G, SW, kPaged>(p, si, seg, pl, c_len, append, sm); break;
   }
   __syncthreads();
 
@@ -1055,11 +1208,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   }
 }
 
-template <int G, int SW>
-hipError_t launch_chunks_gs(const DecodeParams& p, hipStream_t stream) {
+template <int G, int SW, typename Lens>
+hipError_t launch_chunks_gs(const DecodeParams& p, const Lens& lens, hipStream_t stream) {
   const uint64_t grid = uint64_t(p.n_seg) * p.max_chunks;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((decode_chunk_kernel<G, SW>), dim3(unsigned(grid)), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((decode_chunk_kernel<G, SW, Lens>), dim3(unsigned(grid)), dim3(kThreads), 0, stream, p, lens);
   return hipGetLastError();
 }
 
@@ -1067,13 +1220,26 @@ template <int G>
 hipError_t launch_chunks_g(const DecodeParams& p, hipStream_t stream) {
   // K record words staged through LDS, from the layout's bound on a record
   const int words = (max(p.rec_max, p.gen_rec_max) + 3) / 4;
-  if (words <= 8) return launch_chunks_gs<G, 8>(p, stream);
-  if (words <= 10) return launch_chunks_gs<G, 10>(p, stream);
-  if (words <= 12) return launch_chunks_gs<G, 12>(p, stream);
-  if (words <= 16) return launch_chunks_gs<G, 16>(p, stream);
-  if (words <= 24) return launch_chunks_gs<G, 24>(p, stream);
-  if (words <= kMaxStagedWords) return launch_chunks_gs<G, 32>(p, stream);
-  return launch_chunks_gs<G, 0>(p, stream);
+  const NoSeqLens none;
+  if (words <= 8) return launch_chunks_gs<G, 8>(p, none, stream);
+  if (words <= 10) return launch_chunks_gs<G, 10>(p, none, stream);
+  if (words <= 12) return launch_chunks_gs<G, 12>(p, none, stream);
+  if (words <= 16) return launch_chunks_gs<G, 16>(p, none, stream);
+  if (words <= 24) return launch_chunks_gs<G, 24>(p, none, stream);
+  if (words <= kMaxStagedWords) return launch_chunks_gs<G, 32>(p, none, stream);
+  return launch_chunks_gs<G, 0>(p, none, stream);
+}
+
+// Paged caches: fewer record-stage variants (a layout's record bound is set
+// by the largest budget it admits).
+template <int G>
+hipError_t launch_chunks_paged_g(const DecodeParams& p, const PagedSeqLens& lens, hipStream_t stream) {
+  const int words = (p.rec_max + 3) / 4;
+  if (words <= 10) return launch_chunks_gs<G, 10>(p, lens, stream);
+  if (words <= 16) return launch_chunks_gs<G, 16>(p, lens, stream);
+  if (words <= 24) return launch_chunks_gs<G, 24>(p, lens, stream);
+  if (words <= kMaxStagedWords) return launch_chunks_gs<G, 32>(p, lens, stream);
+  return launch_chunks_gs<G, 0>(p, lens, stream);
 }
 
 template <int G>
@@ -1094,6 +1260,16 @@ hipError_t launch_decode_chunks(const DecodeParams& p, hipStream_t stream) {
     case 2: return launch_chunks_g<2>(p, stream);
     case 4: return launch_chunks_g<4>(p, stream);
     case 8: return launch_chunks_g<8>(p, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_chunks_paged(const DecodeParams& p, const PagedSeqLens& lens, hipStream_t stream) {
+  switch (p.group) {
+    case 1: return launch_chunks_paged_g<1>(p, lens, stream);
+    case 2: return launch_chunks_paged_g<2>(p, lens, stream);
+    case 4: return launch_chunks_paged_g<4>(p, lens, stream);
+    case 8: return launch_chunks_paged_g<8>(p, lens, stream);
   }
   return hipErrorInvalidValue;
 }

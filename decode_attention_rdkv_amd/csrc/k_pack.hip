@@ -496,7 +496,204 @@ __global__ __launch_bounds__(256) void pack_status_kernel(const uint8_t* cache, 
   if (threadIdx.x == 0) out[0] = s_part[0] + s_part[1] + s_part[2] + s_part[3];
 }
 
+// ------------------------------------------------------------------ paged cache
+
+__global__ void paged_header_kernel(uint8_t* cache, rdkv_paged_layout pl) {
+  const uint64_t n = uint64_t(pl.n_seg) * pl.max_pages;
+  int32_t* table = reinterpret_cast<int32_t*>(cache + pl.table_offset);
+  const uint64_t stride = uint64_t(gridDim.x) * blockDim.x;
+  for (uint64_t i = uint64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) table[i] = -1;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    const int32_t h32[8] = {int32_t(kPagedMagic), kFormatVersion, pl.dims.n_seq, pl.dims.n_layers,
+                            pl.dims.n_q_heads, pl.dims.n_kv_heads, pl.dims.head_dim, pl.zone_c_capacity};
+    for (int i = 0; i < 8; ++i) st_i32(cache, 4 * i, h32[i]);
+    const int64_t h64[10] = {pl.dims.n_tokens, pl.budget_v_max, pl.budget_k_max, pl.n_seg, int64_t(kHeaderBytes),
+                             int64_t(pl.table_offset), int64_t(pl.pool_offset), pl.max_pages, pl.n_pages,
+                             int64_t(kPageBytes)};
+    for (int i = 0; i < 10; ++i) st_u64(cache, 32 + 8 * i, uint64_t(h64[i]));
+  }
+}
+
+// What the staged (contiguous-format) descriptor of one segment says, and
+// where its regions would go in pages.
+struct StagedSeg {
+  int n_tok[4], n_kept, n_chan[4], rec;
+  uint64_t src[kRegions];      // staging offset of each region's first row (zone-C regions: none)
+  int rows[kRegions];
+  int row_bytes[kRegions];
+  int pages[kRegions];
+  int vpage[kRegions];
+  int total;
+  bool ok;
+};
+
+__device__ StagedSeg read_staged(const uint8_t* staging, uint64_t staging_bytes, int si, int cap, int64_t nk_max,
+                                 int rec_max) {
+  const uint8_t* d = staging + kHeaderBytes + uint64_t(si) * kDescBytes;
+  StagedSeg g;
+  int sum = 0;
+  g.ok = true;
+  for (int i = 0; i < 4; ++i) {
+    g.n_tok[i] = *reinterpret_cast<const int32_t*>(d + kDescNTok + 4 * i);
+    g.n_chan[i] = *reinterpret_cast<const int32_t*>(d + kDescNChan + 4 * i);
+    g.ok = g.ok && g.n_tok[i] >= 0 && g.n_chan[i] >= 0;
+    sum += g.n_tok[i];
+  }
+  g.n_kept = *reinterpret_cast<const int32_t*>(d + kDescNKept);
+  g.rec = *reinterpret_cast<const int32_t*>(d + kDescRec);
+  const RecordShape rs = record_shape(g.n_chan[0], g.n_chan[1], g.n_chan[2], g.n_chan[3]);
+  g.ok = g.ok && sum == g.n_kept && g.n_kept <= nk_max && g.rec == 4 * rs.words_a() && g.rec <= rec_max;
+  if (!g.ok) {
+    for (int i = 0; i < 4; ++i) g.n_tok[i] = 0;
+    g.n_kept = 0;
+    g.rec = 4;
+  }
+  const uint64_t off_krec = *reinterpret_cast<const uint64_t*>(d + kDescOffKrec);
+  uint64_t rec_at = off_krec;
+  for (int i = 0; i < 4; ++i) {
+    g.rows[kRegV + i] = g.n_tok[i];
+    g.row_bytes[kRegV + i] = kHeadDim * group_bits(i) / 8;
+    g.src[kRegV + i] = *reinterpret_cast<const uint64_t*>(d + kDescOffV + 8 * i);
+    g.rows[kRegRec + i] = g.n_tok[i];
+    g.row_bytes[kRegRec + i] = g.rec - 4 * (i == 3);
+    g.src[kRegRec + i] = rec_at;
+    rec_at += uint64_t(g.n_tok[i]) * g.row_bytes[kRegRec + i];
+  }
+  g.rows[kRegKC] = g.rows[kRegVC] = cap;
+  g.row_bytes[kRegKC] = g.row_bytes[kRegVC] = kHeadDim * 2;
+  g.src[kRegKC] = g.src[kRegVC] = 0;
+  g.rows[kRegPos] = g.n_kept;
+  g.row_bytes[kRegPos] = 4;
+  g.src[kRegPos] = *reinterpret_cast<const uint64_t*>(d + kDescOffPos);
+  g.total = 0;
+  for (int r = 0; r < kRegions; ++r) {
+    g.pages[r] = paged_region_pages(g.rows[r], paged_tile_bytes(r, g.rec));
+    g.vpage[r] = g.total;
+    g.total += g.pages[r];
+    if (r != kRegKC && r != kRegVC && g.rows[r] > 0)
+      g.ok = g.ok && g.src[r] + uint64_t(g.rows[r]) * g.row_bytes[r] <= staging_bytes;
+  }
+  return g;
+}
+
+struct PagedKArgs {
+  uint8_t* cache;
+  rdkv_paged_layout pl;
+  const uint8_t* staging;
+  uint64_t staging_bytes;
+  int32_t seq;
+  const int32_t* pages;
+  int32_t* pages_needed;
+};
+
+// pages_needed[si] for the staged segments; one thread per segment
+__global__ void paged_plan_kernel(PagedKArgs a) {
+  const int seg_per_seq = a.pl.dims.n_layers * a.pl.dims.n_kv_heads;
+  const int si = blockIdx.x * blockDim.x + threadIdx.x;
+  if (si >= seg_per_seq) return;
+  const StagedSeg g = read_staged(a.staging, a.staging_bytes, si, a.pl.zone_c_capacity, a.pl.nk_max, a.pl.rec_max);
+  a.pages_needed[si] = g.total;
+}
+
+// One workgroup per segment of the sequence: block-table row, descriptor,
+// and the regions' rows copied tile by tile into the given pages (zone C
+// zeroed).  Invalid page lists leave the slot's segment empty and flagged.
+__global__ __launch_bounds__(256) void paged_commit_kernel(PagedKArgs a) {
+  const int seg_per_seq = a.pl.dims.n_layers * a.pl.dims.n_kv_heads;
+  const int si = blockIdx.x;
+  const int64_t seg = int64_t(a.seq) * seg_per_seq + si;
+  const int tid = threadIdx.x;
+  const int cap = a.pl.zone_c_capacity;
+  const StagedSeg g = read_staged(a.staging, a.staging_bytes, si, cap, a.pl.nk_max, a.pl.rec_max);
+  const int32_t* pg = a.pages + int64_t(si) * a.pl.max_pages;
+  __shared__ int s_bad;
+  if (tid == 0) s_bad = !g.ok || g.total > a.pl.max_pages;
+  __syncthreads();
+  for (int i = tid; i < g.total && i < a.pl.max_pages; i += 256)
+    if (pg[i] < 0 || pg[i] >= a.pl.n_pages) s_bad = 1;
+  __syncthreads();
+  const bool ok = !s_bad;
+  int32_t* row = reinterpret_cast<int32_t*>(a.cache + a.pl.table_offset) + seg * a.pl.max_pages;
+  for (int i = tid; i < a.pl.max_pages; i += 256) row[i] = (ok && i < g.total) ? pg[i] : -1;
+  uint8_t* d = a.cache + kHeaderBytes + uint64_t(seg) * kDescBytes;
+  const uint8_t* sd = a.staging + kHeaderBytes + uint64_t(si) * kDescBytes;
+  if (tid < kDescBytes / 4) {
+    uint32_t w = 0;
+    const int b = 4 * tid;
+    if (ok) {
+      if (b < kDescNTok + 16) w = uint32_t(g.n_tok[b / 4]);
+      else if (b == kDescNKept) w = uint32_t(g.n_kept);
+      else if (b < kDescNChan + 16) w = uint32_t(g.n_chan[(b - kDescNChan) / 4]);
+      else if (b == kDescRec) w = uint32_t(g.rec);
+      else if (b == kDescCap) w = uint32_t(cap);
+      else if (b >= kPDescVpage && b < kPDescVpage + 4 * kRegions) w = uint32_t(g.vpage[(b - kPDescVpage) / 4]);
+      else if (b == kPDescNPages) w = uint32_t(g.total);
+      else if (b >= kDescPerm) w = *reinterpret_cast<const uint32_t*>(sd + b);
+    } else if (b == kDescFlags) {
+      w = 1u;
+    }
+    st_u32(d, b, w);
+  }
+  if (!ok) return;
+  uint8_t* pool = a.cache + a.pl.pool_offset;
+  for (int r = 0; r < kRegions; ++r) {
+    const int rb = g.row_bytes[r];
+    if (g.rows[r] == 0 || rb == 0) continue;
+    const uint32_t tb = paged_tile_bytes(r, g.rec);
+    const int tpp = int(kPageBytes / tb);
+    const bool zero = r == kRegKC || r == kRegVC;
+    // whole tiles of zone C are cleared; the other regions copy their rows
+    const int64_t words = zero ? int64_t((g.rows[r] + kPagedTile - 1) / kPagedTile) * (tb / 4)
+                               : int64_t(g.rows[r]) * (rb / 4);
+    for (int64_t j = tid; j < words; j += 256) {
+      const int64_t byte = j * 4;
+      const int64_t tile = zero ? byte / tb : (byte / rb) / kPagedTile;
+      const int64_t in_tile = zero ? byte % tb : byte - tile * kPagedTile * rb;
+      const int page = pg[g.vpage[r] + int(tile / tpp)];
+      uint32_t* dst = reinterpret_cast<uint32_t*>(pool + uint64_t(page) * kPageBytes + (tile % tpp) * tb + in_tile);
+      *dst = zero ? 0u : *reinterpret_cast<const uint32_t*>(a.staging + g.src[r] + byte);
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void paged_release_kernel(uint8_t* cache, rdkv_paged_layout pl, int32_t seq) {
+  const int seg_per_seq = pl.dims.n_layers * pl.dims.n_kv_heads;
+  const int64_t seg = int64_t(seq) * seg_per_seq + blockIdx.x;
+  int32_t* row = reinterpret_cast<int32_t*>(cache + pl.table_offset) + seg * pl.max_pages;
+  for (int i = threadIdx.x; i < pl.max_pages; i += 256) row[i] = -1;
+  if (threadIdx.x < kDescBytes / 4) st_u32(cache + kHeaderBytes + uint64_t(seg) * kDescBytes, 4 * threadIdx.x, 0u);
+}
+
 }  // namespace
+
+hipError_t launch_paged_init(uint8_t* cache, const rdkv_paged_layout& pl, hipStream_t stream) {
+  const uint64_t n16 = pl.cache_bytes / 16;
+  const unsigned grid = unsigned(std::min<uint64_t>(cdiv(n16, 256), 8192));
+  hipLaunchKernelGGL(cache_zero_kernel, dim3(grid), dim3(256), 0, stream, reinterpret_cast<uint4*>(cache), n16);
+  const unsigned tgrid = unsigned(std::min<uint64_t>(cdiv(uint64_t(pl.n_seg) * pl.max_pages, 256) + 1, 4096));
+  hipLaunchKernelGGL(paged_header_kernel, dim3(tgrid), dim3(256), 0, stream, cache, pl);
+  return hipGetLastError();
+}
+
+hipError_t launch_paged_plan(const PagedPackParams& p, hipStream_t stream) {
+  const int seg_per_seq = p.play->dims.n_layers * p.play->dims.n_kv_heads;
+  PagedKArgs a{p.cache, *p.play, p.staging, p.staging_bytes, p.seq, p.pages, p.pages_needed};
+  hipLaunchKernelGGL(paged_plan_kernel, dim3(unsigned(cdiv(seg_per_seq, 64))), dim3(64), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_paged_commit(const PagedPackParams& p, hipStream_t stream) {
+  const int seg_per_seq = p.play->dims.n_layers * p.play->dims.n_kv_heads;
+  PagedKArgs a{p.cache, *p.play, p.staging, p.staging_bytes, p.seq, p.pages, p.pages_needed};
+  hipLaunchKernelGGL(paged_commit_kernel, dim3(unsigned(seg_per_seq)), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_paged_release(uint8_t* cache, const rdkv_paged_layout& pl, int32_t seq, hipStream_t stream) {
+  const int seg_per_seq = pl.dims.n_layers * pl.dims.n_kv_heads;
+  hipLaunchKernelGGL(paged_release_kernel, dim3(unsigned(seg_per_seq)), dim3(256), 0, stream, cache, pl, seq);
+  return hipGetLastError();
+}
 
 hipError_t launch_pack_status(const uint8_t* cache, int64_t n_seg, int32_t* out, hipStream_t stream) {
   hipLaunchKernelGGL(pack_status_kernel, dim3(1), dim3(256), 0, stream, cache, n_seg, out);

@@ -125,6 +125,37 @@ constexpr int kHdrGenBytes = 104;
 constexpr int kHdrGenBudgetV = 112;
 constexpr int kHdrGenBudgetK = 120;
 
+// ------------------------------------------------------------ paged cache
+// Pages of RDKV_PAGE_BYTES; each region of a segment is an array of 64-row
+// tiles laid page after page, a page holding kPageBytes / tile-bytes tiles.
+constexpr int kPageBytes = RDKV_PAGE_BYTES;
+constexpr int kMaxPagedSeqs = RDKV_MAX_PAGED_SEQS;
+constexpr uint32_t kPagedMagic = 0x504B4452u;  // "RDKP"
+constexpr int kPagedTile = 64;
+// regions: V rows of groups 0..3, K records of groups 0..3, zone-C K, zone-C V, positions
+constexpr int kRegions = 11;
+constexpr int kRegV = 0, kRegRec = 4, kRegKC = 8, kRegVC = 9, kRegPos = 10;
+// paged descriptor: the first 48 bytes as the contiguous descriptor, then
+// i32 vpage[11] (first virtual page of each region) and i32 n_pages
+constexpr int kPDescVpage = 48;
+constexpr int kPDescNPages = 92;
+// paged header: i64 table_offset, pool_offset, max_pages, n_pages, page bytes
+constexpr int kPHdrTable = 72;
+
+// Bytes of a 64-row tile of region r; rec = bytes of a zone-A K record.
+__host__ __device__ inline uint32_t paged_tile_bytes(int r, int rec) {
+  if (r < kRegRec) return uint32_t(kPagedTile) * (kHeadDim * (2 << r) / 8);
+  if (r < kRegKC) return uint32_t(kPagedTile) * uint32_t(rec - 4 * (r - kRegRec == 3));
+  if (r < kRegPos) return uint32_t(kPagedTile) * kHeadDim * 2;
+  return uint32_t(kPagedTile) * 4;
+}
+__host__ __device__ inline int paged_region_pages(int64_t rows, uint32_t tile_bytes) {
+  if (rows <= 0 || tile_bytes == 0) return 0;
+  const int64_t tiles = (rows + kPagedTile - 1) / kPagedTile;
+  const int64_t tpp = kPageBytes / tile_bytes;
+  return int((tiles + tpp - 1) / tpp);
+}
+
 // Split-K chunk slots of a segment in decode: [0, token_slots) the prefill
 // tokens' chunks, then n_gen * gen_slots for the generation blobs (empty
 // while a generation is not in use), then the zone-C chunks.
@@ -153,7 +184,19 @@ struct DecodeParams {
   float* partials;         // [n_seg][max_chunks][G][kPartialFloats]
   float* out;              // [n_seg][G][128]
   float* zc_stats;         // merge: [n_seg][G][zc_cap + 128] statistics to accumulate, or null
+  // paged cache (paged = 0 for a contiguous blob): descriptors at 256, the
+  // block table [n_seg][max_pages] at table_offset, pages at pool_offset
+  int32_t paged;
+  int32_t seg_per_seq;     // L * Hkv (the sequence of a segment is seg / seg_per_seq)
+  int32_t max_pages;
+  int64_t pool_pages;
+  uint64_t table_offset, pool_offset;
 };
+// Zone-C rows of each sequence slot before a paged decode step.
+struct PagedSeqLens {
+  int32_t c_len[kMaxPagedSeqs];
+};
+hipError_t launch_decode_chunks_paged(const DecodeParams& p, const PagedSeqLens& lens, hipStream_t stream);
 hipError_t launch_decode_chunks(const DecodeParams& p, hipStream_t stream);
 // Device address (on the current device) of the library-owned decode scratch
 // of kStaticScratchBytes bytes used by rdkv_decode_static.
@@ -175,6 +218,20 @@ struct PackParams {
 hipError_t launch_cache_init(uint8_t* cache, const rdkv_layout& lay, const rdkv_layout* gen, hipStream_t stream);
 hipError_t launch_pack(const PackParams& p, hipStream_t stream);
 hipError_t launch_pack_status(const uint8_t* cache, int64_t n_seg, int32_t* out, hipStream_t stream);
+
+struct PagedPackParams {
+  uint8_t* cache;          // the paged cache
+  const rdkv_paged_layout* play;   // host copy
+  const uint8_t* staging;  // a contiguous one-sequence blob packed by launch_pack
+  uint64_t staging_bytes;
+  int32_t seq;             // slot
+  const int32_t* pages;    // [L*Hkv][max_pages]
+  int32_t* pages_needed;   // [L*Hkv]
+};
+hipError_t launch_paged_init(uint8_t* cache, const rdkv_paged_layout& play, hipStream_t stream);
+hipError_t launch_paged_plan(const PagedPackParams& p, hipStream_t stream);
+hipError_t launch_paged_commit(const PagedPackParams& p, hipStream_t stream);
+hipError_t launch_paged_release(uint8_t* cache, const rdkv_paged_layout& play, int32_t seq, hipStream_t stream);
 hipError_t launch_unpack(const uint8_t* cache, uint64_t cache_bytes, const rdkv_layout& lay, int64_t seg,
                          float* k_hat, float* v_hat, hipStream_t stream);
 

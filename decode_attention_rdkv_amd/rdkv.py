@@ -40,6 +40,18 @@ class Layout(ctypes.Structure):
         return self.dims.n_q_heads // self.dims.n_kv_heads
 
 
+class PagedLayout(ctypes.Structure):
+    _fields_ = [("dims", Dims), ("budget_v_max", c_i64), ("budget_k_max", c_i64), ("n_seg", c_i64),
+                ("n_pages", c_i64), ("max_pages", c_i64), ("nk_max", c_i64), ("table_offset", c_u64),
+                ("pool_offset", c_u64), ("cache_bytes", c_u64), ("decode_workspace_bytes", c_u64),
+                ("zone_c_capacity", c_i32), ("rec_max", c_i32), ("max_chunks", c_i32), ("token_slots", c_i32),
+                ("chunk_tok2", c_i32), ("reserved", c_i32)]
+
+    @property
+    def group(self) -> int:
+        return self.dims.n_q_heads // self.dims.n_kv_heads
+
+
 STATUS = ["RDKV_OK", "RDKV_ERR_NULL", "RDKV_ERR_SHAPE", "RDKV_ERR_UNSUPPORTED", "RDKV_ERR_BUDGET",
           "RDKV_ERR_ALIGN", "RDKV_ERR_WORKSPACE", "RDKV_ERR_CAPACITY", "RDKV_ERR_HIP", "RDKV_ERR_OVERFLOW"]
 RDKV_ERR_OVERFLOW = 9
@@ -76,6 +88,17 @@ SIGNATURES = {
                                      ctypes.c_size_t, c_vp]),
     "rdkv_decode_merge": (c_i32, [ctypes.POINTER(Layout), c_vp, ctypes.c_size_t, c_i32, c_vp, c_vp, ctypes.c_size_t,
                                   c_vp]),
+    "rdkv_paged_layout_init": (c_i32, [ctypes.POINTER(Dims), c_i64, c_i64, c_i32, c_i64,
+                                       ctypes.POINTER(PagedLayout)]),
+    "rdkv_paged_cache_init": (c_i32, [ctypes.POINTER(PagedLayout), c_vp, ctypes.c_size_t, c_vp]),
+    "rdkv_paged_staging_bytes": (ctypes.c_size_t, [ctypes.POINTER(PagedLayout), c_i64, c_i64, c_i64]),
+    "rdkv_paged_stage": (c_i32, [ctypes.POINTER(PagedLayout), c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                 ctypes.c_size_t, c_vp, c_vp]),
+    "rdkv_paged_commit": (c_i32, [ctypes.POINTER(PagedLayout), c_i32, c_i64, c_i64, c_i64, c_vp, ctypes.c_size_t,
+                                  c_vp, c_vp, ctypes.c_size_t, c_vp]),
+    "rdkv_paged_release": (c_i32, [ctypes.POINTER(PagedLayout), c_i32, c_vp, ctypes.c_size_t, c_vp]),
+    "rdkv_paged_decode": (c_i32, [ctypes.POINTER(PagedLayout), c_vp, ctypes.c_size_t, ctypes.POINTER(c_i32), c_vp,
+                                  c_vp, c_vp, c_vp, c_vp, ctypes.c_size_t, c_vp]),
     "rdkv_unpack": (c_i32, [ctypes.POINTER(Layout), c_vp, ctypes.c_size_t, c_i64, c_vp, c_vp, c_vp]),
 }
 
@@ -424,6 +447,92 @@ def unpack(lay: Layout, cache: torch.Tensor, seg: int):
     _check(load().rdkv_unpack(ctypes.byref(lay), _ptr(cache, torch.uint8, None, "cache"), cache.numel(), seg,
                               k_hat.data_ptr(), v_hat.data_ptr(), _stream()), "rdkv_unpack")
     return k_hat, v_hat
+
+
+# ---------------------------------------------------------------- paged cache
+
+PAGE_BYTES = 32768
+
+
+def paged_layout(dims_max: Dims, budget_v_max: int, budget_k_max: int, zone_c_capacity: int,
+                 n_pages: int) -> PagedLayout:
+    out = PagedLayout()
+    _check(load().rdkv_paged_layout_init(ctypes.byref(dims_max), budget_v_max, budget_k_max, zone_c_capacity,
+                                         n_pages, ctypes.byref(out)), "rdkv_paged_layout_init")
+    return out
+
+
+def paged_cache_init(pl: PagedLayout, cache: Optional[torch.Tensor] = None, device="cuda") -> torch.Tensor:
+    if cache is None:
+        cache = torch.empty(pl.cache_bytes, dtype=torch.uint8, device=device)
+    _check(load().rdkv_paged_cache_init(ctypes.byref(pl), _ptr(cache, torch.uint8, None, "cache"), cache.numel(),
+                                        _stream()), "rdkv_paged_cache_init")
+    return cache
+
+
+def paged_staging_bytes(pl: PagedLayout, n_tokens: int, budget_v: int, budget_k: int) -> int:
+    return int(load().rdkv_paged_staging_bytes(ctypes.byref(pl), n_tokens, budget_v, budget_k))
+
+
+def paged_stage(pl: PagedLayout, n_tokens: int, budget_v: int, budget_k: int, K, V, bits_tok, bits_chan,
+                staging: Optional[torch.Tensor] = None):
+    """Pack one sequence into a staging buffer; returns (staging, pages_needed
+    device int32 [L*Hkv])."""
+    d = pl.dims
+    L, Hk = d.n_layers, d.n_kv_heads
+    if staging is None:
+        staging = torch.empty(max(paged_staging_bytes(pl, n_tokens, budget_v, budget_k), 16), dtype=torch.uint8,
+                              device=K.device)
+    need = torch.empty(max(L * Hk, 4), dtype=torch.int32, device=K.device)
+    _check(load().rdkv_paged_stage(ctypes.byref(pl), n_tokens, budget_v, budget_k,
+                                   _ptr(K, torch.float16, (L, Hk, n_tokens, HEAD_DIM), "K"),
+                                   _ptr(V, torch.float16, (L, Hk, n_tokens, HEAD_DIM), "V"),
+                                   _ptr(bits_tok, torch.uint8, (L, Hk, n_tokens), "bits_tok"),
+                                   _ptr(bits_chan, torch.uint8, (L, Hk, HEAD_DIM), "bits_chan"),
+                                   _ptr(staging, torch.uint8, None, "staging"), staging.numel(), need.data_ptr(),
+                                   _stream()), "rdkv_paged_stage")
+    return staging, need[:L * Hk]
+
+
+def paged_commit(pl: PagedLayout, cache: torch.Tensor, seq: int, n_tokens: int, budget_v: int, budget_k: int,
+                 staging: torch.Tensor, pages: torch.Tensor):
+    """Commit a staged sequence into slot `seq` on the given pages (device int32 [L*Hkv][max_pages])."""
+    d = pl.dims
+    _check(load().rdkv_paged_commit(ctypes.byref(pl), seq, n_tokens, budget_v, budget_k,
+                                    _ptr(staging, torch.uint8, None, "staging"), staging.numel(),
+                                    _ptr(pages, torch.int32, (d.n_layers * d.n_kv_heads, pl.max_pages), "pages"),
+                                    _ptr(cache, torch.uint8, None, "cache"), cache.numel(), _stream()),
+           "rdkv_paged_commit")
+
+
+def paged_release(pl: PagedLayout, cache: torch.Tensor, seq: int):
+    _check(load().rdkv_paged_release(ctypes.byref(pl), seq, _ptr(cache, torch.uint8, None, "cache"), cache.numel(),
+                                     _stream()), "rdkv_paged_release")
+
+
+def paged_decode_workspace(pl: PagedLayout, device="cuda") -> torch.Tensor:
+    return torch.empty(max(int(pl.decode_workspace_bytes), 16), dtype=torch.uint8, device=device)
+
+
+def paged_decode(pl: PagedLayout, cache: torch.Tensor, c_len, q, k_new=None, v_new=None,
+                 workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One decode step over every sequence slot; c_len: host sequence of the
+    slots' zone-C rows before the step.  Returns out fp32 [S][L][Hq][128]."""
+    d = pl.dims
+    S, L, Hq, Hk = d.n_seq, d.n_layers, d.n_q_heads, d.n_kv_heads
+    cl = (c_i32 * S)(*[int(x) for x in c_len])
+    if workspace is None:
+        workspace = paged_decode_workspace(pl, q.device)
+    if out is None:
+        out = torch.empty((S, L, Hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+    _check(load().rdkv_paged_decode(ctypes.byref(pl), _ptr(cache, torch.uint8, None, "cache"), cache.numel(), cl,
+                                    _ptr(q, torch.float16, (S, L, Hq, HEAD_DIM), "q"),
+                                    _ptr(k_new, torch.float16, (S, L, Hk, HEAD_DIM), "k_new"),
+                                    _ptr(v_new, torch.float16, (S, L, Hk, HEAD_DIM), "v_new"),
+                                    _ptr(out, torch.float32, (S, L, Hq, HEAD_DIM), "out"),
+                                    _ptr(workspace, torch.uint8, None, "workspace"), workspace.numel(), _stream()),
+           "rdkv_paged_decode")
+    return out
 
 
 # ---------------------------------------------------------------- descriptor readout

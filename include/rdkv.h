@@ -326,6 +326,90 @@ rdkv_status rdkv_decode_merge(const rdkv_layout* layout, const void* cache, size
                               int32_t zone_c_rows, float* out, const void* workspace, size_t workspace_bytes,
                               hipStream_t stream);
 
+/* ---------------------------------------------------------------- paged zones
+ * A paged cache for batched serving: the packed zones of every segment live
+ * in fixed-size pages of one shared pool, found through a block table per
+ * segment (the aistudio.id article's "Solusi 1": KV blocks, non-contiguous,
+ * mapped per sequence), so sequences of different lengths take exactly the
+ * pages they need, and the pages of a finished sequence go to the next one.
+ * The caller owns the pages (its own allocator hands them out and takes them
+ * back, as a serving block manager does); the library writes and reads them.
+ *
+ * Layout of the buffer: 256-byte header; a 256-byte descriptor per segment
+ * slot (sequence slot s < n_seq, layer, KV head: seg = (s*L + l)*Hkv + h);
+ * the block table int32 [n_seg][max_pages] (physical page of each virtual
+ * page of a segment, -1 unused); the pool of n_pages pages of
+ * RDKV_PAGE_BYTES.  A segment's regions -- V rows of its 2/4/8/16-bit token
+ * groups, their K records, zone-C keys, zone-C values, kept positions -- are
+ * each an array of 64-row tiles laid page after page (a tile never straddles
+ * a page), starting at a fresh virtual page; the tiles' content is that of
+ * the contiguous format.  A free slot has zone-C capacity 0. */
+#define RDKV_PAGE_BYTES 32768
+#define RDKV_MAX_PAGED_SEQS 256
+typedef struct rdkv_paged_layout {
+  rdkv_dims dims;                /* n_seq = sequence slots (<= 256), n_tokens = bound on a prefill length */
+  int64_t budget_v_max;          /* bound on a sequence's V budget (bits per segment) */
+  int64_t budget_k_max;          /* bound on a sequence's K budget                   */
+  int64_t n_seg;                 /* n_seq * n_layers * n_kv_heads                    */
+  int64_t n_pages;               /* pages in the pool                                */
+  int64_t max_pages;             /* block-table entries per segment                  */
+  int64_t nk_max;                /* bound on kept tokens per segment                 */
+  uint64_t table_offset;         /* byte offset of the block table                   */
+  uint64_t pool_offset;          /* byte offset of page 0                            */
+  uint64_t cache_bytes;          /* bytes of the whole paged cache                   */
+  uint64_t decode_workspace_bytes;
+  int32_t zone_c_capacity;       /* zone-C rows of every sequence                     */
+  int32_t rec_max, max_chunks, token_slots, chunk_tok2, reserved;
+} rdkv_paged_layout;
+
+/* Host only.  dims_max: sequence slots, layers, heads, and the bound on any
+ * sequence's prefill length; budget bounds per segment; zone-C capacity;
+ * n_pages >= 1.  Errors as rdkv_layout_init, RDKV_ERR_SHAPE for n_seq >
+ * RDKV_MAX_PAGED_SEQS or n_pages < 1. */
+rdkv_status rdkv_paged_layout_init(const rdkv_dims* dims_max, int64_t budget_v_max, int64_t budget_k_max,
+                                   int32_t zone_c_capacity, int64_t n_pages, rdkv_paged_layout* out);
+/* Zero the buffer, write the header, every slot free, the table -1. */
+rdkv_status rdkv_paged_cache_init(const rdkv_paged_layout* layout, void* cache, size_t cache_bytes,
+                                  hipStream_t stream);
+/* Adding a sequence, in two calls around the caller's page allocation:
+ * rdkv_paged_stage packs one sequence -- its own prefill length n_tokens <=
+ * the bound, its own budgets within the bounds -- with rdkv_pack into a
+ * caller-provided staging buffer of rdkv_paged_staging_bytes bytes, and
+ * writes to pages_needed (device int32 [L*Hkv]) how many pages each of its
+ * segments takes (zone C included).  K, V fp16 [L][Hkv][n_tokens][128],
+ * bits_tok u8 [L][Hkv][n_tokens], bits_chan u8 [L][Hkv][128], as for
+ * rdkv_pack (an allocation over its budgets packs empty, see
+ * rdkv_pack_status).  The caller then reads pages_needed, takes that many
+ * pages from its pool and calls rdkv_paged_commit with them: pages is device
+ * int32 [L*Hkv][max_pages], row i listing segment i's pages in order (row
+ * entries past its count are ignored); entries outside [0, n_pages) make
+ * that segment empty (descriptor flag bit 0).  The sequence lands in slot
+ * `seq`, its zone C empty.  staging must still hold what rdkv_paged_stage
+ * wrote.  rdkv_paged_release frees slot `seq` (descriptors empty, table -1);
+ * the caller takes back the pages it gave. */
+size_t rdkv_paged_staging_bytes(const rdkv_paged_layout* layout, int64_t n_tokens, int64_t budget_v,
+                                int64_t budget_k);
+rdkv_status rdkv_paged_stage(const rdkv_paged_layout* layout, int64_t n_tokens, int64_t budget_v,
+                             int64_t budget_k, const void* K, const void* V, const uint8_t* bits_tok,
+                             const uint8_t* bits_chan, void* staging, size_t staging_bytes,
+                             int32_t* pages_needed, hipStream_t stream);
+rdkv_status rdkv_paged_commit(const rdkv_paged_layout* layout, int32_t seq, int64_t n_tokens, int64_t budget_v,
+                              int64_t budget_k, const void* staging, size_t staging_bytes, const int32_t* pages,
+                              void* cache, size_t cache_bytes, hipStream_t stream);
+rdkv_status rdkv_paged_release(const rdkv_paged_layout* layout, int32_t seq, void* cache, size_t cache_bytes,
+                               hipStream_t stream);
+/* One decode step over every sequence slot (section 2.3 decode, as
+ * rdkv_decode): c_len is a HOST array [n_seq] of each slot's zone-C rows
+ * before the step (0 for free slots); with k_new/v_new every slot in use
+ * appends its token at its own row c_len[s] (so c_len[s] < capacity) and
+ * attends c_len[s] + 1 rows; the caller then advances its c_len.  q, k_new,
+ * v_new, out as rdkv_decode over [n_seq][L]...; free slots give 0.
+ * workspace: layout->decode_workspace_bytes.  Errors: RDKV_ERR_CAPACITY for a
+ * c_len out of range, others as rdkv_decode. */
+rdkv_status rdkv_paged_decode(const rdkv_paged_layout* layout, void* cache, size_t cache_bytes,
+                              const int32_t* c_len, const void* q, const void* k_new, const void* v_new,
+                              float* out, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Test support: dequantized kept rows of one segment, in kept order, with the
  * fused multiply-add dequantization x_hat = fmaf(code, scale, zero).
  *   k_hat, v_hat fp32 [nk_max][128] (rows past the segment's kept count are

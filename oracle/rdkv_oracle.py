@@ -956,9 +956,10 @@ class PagedLayout:
         nk_max = min(n_tokens_max, budget_v_max // 2)
         rec_max = 4 * ((min(budget_k_max, 16 * D) + 98) // 32 + 4)
         rows = [min(n_tokens_max, budget_v_max // (2 << g)) for g in range(4)]
-        self.max_pages = (sum(region_pages(rows[g], region_tile_bytes(R_V + g, rec_max)) for g in range(4))
-                          + sum(region_pages(rows[g], TILE * rec_max) for g in range(4))
-                          + 2 * region_pages(zone_c_capacity, TILE * D * 2) + region_pages(nk_max, TILE * 4))
+        # (at least one entry per segment, so every table row exists)
+        self.max_pages = max(1, sum(region_pages(rows[g], region_tile_bytes(R_V + g, rec_max)) for g in range(4))
+                             + sum(region_pages(rows[g], TILE * rec_max) for g in range(4))
+                             + 2 * region_pages(zone_c_capacity, TILE * D * 2) + region_pages(nk_max, TILE * 4))
         self.desc_offset = HEADER_BYTES
         self.table_offset = _align(HEADER_BYTES + DESC_BYTES * self.n_seg)
         self.pool_offset = _align(self.table_offset + 4 * self.n_seg * self.max_pages, 4096)
@@ -1052,9 +1053,11 @@ def paged_pack_sequence(blob, play: PagedLayout, s: int, K, V, bits_tok, bits_ch
                 recb = sc["rec"] - 4 * (g == 3)
                 _region_rw(blob, play, seg, int(vpage[R_REC + g]), region_tile_bytes(R_REC + g, sc["rec"]), recb,
                            sc["n_tok"][g], sc["records"][g].reshape(-1).view(np.uint8))
-            zero = np.zeros(play.cap * D * 2, np.uint8)
+            # zone C starts empty: its tiles are cleared whole
+            rows_c = _cdiv(play.cap, TILE) * TILE
+            zero = np.zeros(rows_c * D * 2, np.uint8)
             for r in (R_KC, R_VC):
-                _region_rw(blob, play, seg, int(vpage[r]), region_tile_bytes(r, sc["rec"]), D * 2, play.cap, zero)
+                _region_rw(blob, play, seg, int(vpage[r]), region_tile_bytes(r, sc["rec"]), D * 2, rows_c, zero)
             _region_rw(blob, play, seg, int(vpage[R_POS]), TILE * 4, 4, sc["n_kept"], sc["positions"].view(np.uint8))
             dsc = np.zeros(DESC_BYTES, np.uint8)
             i32 = sc["n_tok"] + [sc["n_kept"]] + sc["n_chan"] + [sc["rec"], play.cap, 0]

@@ -286,3 +286,50 @@ def test_decode_byte_accounting_against_the_oracle_blob():
     assert b["v"] + b["v_meta"] + b["k"] + b["k_meta"] + b["k_padding"] + b["zone_c"] == stored
     assert b["k_padding"] >= 0
     assert b["total"] == b["v"] + b["v_meta"] + b["k"] + b["k_meta"] + b["zone_c"] + b["q_out"]
+
+
+@pytest.mark.parametrize("shape", [(16, 1, 32, 8, 32768, 98304, 384, 256, 4096), (4, 2, 8, 2, 333, 900, 512, 40, 300),
+                                   (1, 1, 4, 1, 64, 1, 0, 1, 1), (2, 3, 16, 2, 5000, 80000, 2048, 130, 77)])
+def test_paged_layout_matches_oracle(shape):
+    S, L, Hq, Hkv, N, bv, bk, cap, n_pages = shape
+    pl = rdkv.paged_layout(rdkv.make_dims(S, L, Hq, Hkv, N), bv, bk, cap, n_pages)
+    op = O.PagedLayout(S, L, Hq, Hkv, N, bv, bk, cap, n_pages)
+    assert (pl.max_pages, pl.table_offset, pl.pool_offset, pl.cache_bytes) == \
+        (op.max_pages, op.table_offset, op.pool_offset, op.cache_bytes)
+    flat = rdkv.layout(rdkv.make_dims(S, L, Hq, Hkv, N), bv, bk, cap)
+    assert (pl.max_chunks, pl.chunk_tok2, pl.rec_max, pl.nk_max) == (flat.max_chunks, flat.chunk_tok2, flat.rec_max,
+                                                                     flat.nk_max)
+    assert pl.decode_workspace_bytes == flat.decode_workspace_bytes
+
+
+def test_paged_validation(lib):
+    d = rdkv.make_dims(3, 2, 8, 2, 300)
+    pl = rdkv.paged_layout(d, 600, 256, 32, 50)
+    out = rdkv.PagedLayout()
+    assert lib.rdkv_paged_layout_init(ctypes.byref(rdkv.make_dims(257, 1, 4, 1, 10)), 10, 10, 4, 5,
+                                      ctypes.byref(out)) == SHAPE
+    assert lib.rdkv_paged_layout_init(ctypes.byref(d), 600, 256, 32, 0, ctypes.byref(out)) == SHAPE
+    nb, ws = pl.cache_bytes, pl.decode_workspace_bytes
+    assert lib.rdkv_paged_cache_init(ctypes.byref(pl), A, nb - 1, None) == WORKSPACE
+    bad = rdkv.PagedLayout.from_buffer_copy(pl)
+    bad.max_pages += 1
+    assert lib.rdkv_paged_cache_init(ctypes.byref(bad), A, nb, None) == SHAPE
+    # staging: length and budgets within the bounds
+    assert lib.rdkv_paged_staging_bytes(ctypes.byref(pl), 301, 100, 100) == 0
+    assert lib.rdkv_paged_staging_bytes(ctypes.byref(pl), 300, 601, 100) == 0
+    sb = lib.rdkv_paged_staging_bytes(ctypes.byref(pl), 200, 300, 100)
+    assert sb == rdkv.layout(rdkv.make_dims(1, 2, 8, 2, 200), 300, 100, 0).cache_bytes
+    assert lib.rdkv_paged_stage(ctypes.byref(pl), 200, 300, 100, A, A, A, A, A, sb - 1, A, None) == WORKSPACE
+    assert lib.rdkv_paged_stage(ctypes.byref(pl), 200, 300, 257, A, A, A, A, A, sb, A, None) == BUDGET
+    assert lib.rdkv_paged_stage(ctypes.byref(pl), 0, 300, 100, A, A, A, A, A, sb, A, None) == SHAPE
+    assert lib.rdkv_paged_stage(ctypes.byref(pl), 200, 300, 100, A, A, A, A, A, sb, None, None) == NULL
+    assert lib.rdkv_paged_commit(ctypes.byref(pl), 3, 200, 300, 100, A, sb, A, A, nb, None) == SHAPE
+    assert lib.rdkv_paged_commit(ctypes.byref(pl), -1, 200, 300, 100, A, sb, A, A, nb, None) == SHAPE
+    assert lib.rdkv_paged_commit(ctypes.byref(pl), 0, 200, 300, 100, A, sb, None, A, nb, None) == NULL
+    assert lib.rdkv_paged_release(ctypes.byref(pl), 3, A, nb, None) == SHAPE
+    c_ok = (ctypes.c_int32 * 3)(0, 5, 31)
+    c_full = (ctypes.c_int32 * 3)(0, 32, 1)
+    assert lib.rdkv_paged_decode(ctypes.byref(pl), A, nb, c_full, A, A, A, A, A, ws, None) == CAPACITY
+    assert lib.rdkv_paged_decode(ctypes.byref(pl), A, nb, c_ok, A, A, None, A, A, ws, None) == NULL
+    assert lib.rdkv_paged_decode(ctypes.byref(pl), A, nb, c_ok, A, None, None, A, A, ws - 1, None) == WORKSPACE
+    assert lib.rdkv_paged_decode(ctypes.byref(pl), A, nb, None, A, None, None, A, A, ws, None) == NULL

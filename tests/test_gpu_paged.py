@@ -1,0 +1,188 @@
+"""Paged zones (a shared pool of fixed-size pages found through a block table
+per segment, the aistudio.id article's "Solusi 1") on the GPU against the
+oracle, through the C ABI.
+
+Sequences of different prefill lengths and budgets are staged, given pages
+by a host allocator that hands them out shuffled (so no segment's pages are
+contiguous), committed, decoded with per-sequence zone-C lengths, released
+and replaced.  Bars: the whole paged cache byte-equal to the oracle's after
+every commit, release and decode step (descriptors, block table, every page);
+the page counts the library asks for equal the oracle's; decode outputs within
+2e-3; and, for equal-length sequences, the paged decode bit-identical to the
+contiguous one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from decode_attention_rdkv_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+TOL = 2e-3
+
+
+@pytest.fixture(scope="module")
+def rdkv():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from decode_attention_rdkv_amd import rdkv as lib
+    lib.load()
+    return lib
+
+
+def host(t):
+    return t.detach().cpu().numpy()
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def rel_err(got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    return float((np.abs(got - ref).max(axis=-1) / np.maximum(np.abs(ref).max(axis=-1), 1e-30)).max())
+
+
+class Pool:
+    """Host page allocator: a free list handed out in shuffled order."""
+
+    def __init__(self, n, seed):
+        self.free = [int(x) for x in np.random.default_rng(seed).permutation(n)]
+
+    def take(self, k):
+        assert k <= len(self.free), "pool exhausted"
+        out, self.free = self.free[:k], self.free[k:]
+        return out
+
+    def give(self, pages):
+        self.free = list(pages) + self.free
+
+
+def _sequence(L, Hkv, N, bv, bk, seed):
+    n = L * Hkv
+    bt, bc = synth.random_bits(n, N, seed)
+    K, V = synth.random_kv(n, N, seed + 1)
+    K[..., 5] *= np.float16(6)
+    for i in range(n):
+        while int(bt[i].astype(np.int64).sum()) > bv:
+            bt[i, np.nonzero(bt[i])[0][: max(1, len(np.nonzero(bt[i])[0]) // 50)]] = 0
+        while int(bc[i].astype(np.int64).sum()) > bk:
+            bc[i, np.nonzero(bc[i])[0][0]] = 0
+    shp = (L, Hkv)
+    return K.reshape(shp + (N, 128)), V.reshape(shp + (N, 128)), bt.reshape(shp + (N,)), bc.reshape(shp + (128,))
+
+
+def _add(rdkv, pl, cache, oblob, op, pool, s, shape, seq):
+    """Stage, allocate and commit one sequence on both sides; returns its pages."""
+    N, bv, bk = shape
+    K, V, bt, bc = seq
+    staging, need = rdkv.paged_stage(pl, N, bv, bk, dev(K), dev(V), dev(bt), dev(bc))
+    need = host(need)
+    ref_need = [O.paged_pages_needed(op, O.segment_content(K[l, h], V[l, h], bt[l, h], bc[l, h]))
+                for l in range(pl.dims.n_layers) for h in range(pl.dims.n_kv_heads)]
+    assert list(need) == ref_need
+    pages = [pool.take(int(k)) for k in need]
+    table = np.full((len(pages), pl.max_pages), -1, np.int32)
+    for i, p in enumerate(pages):
+        table[i, :len(p)] = p
+    rdkv.paged_commit(pl, cache, s, N, bv, bk, staging, dev(table))
+    O.paged_pack_sequence(oblob, op, s, K, V, bt, bc, pages)
+    return [x for p in pages for x in p]
+
+
+def _same_bytes(cache, oblob, what):
+    got = host(cache)
+    if not np.array_equal(got, oblob):
+        diff = np.nonzero(got != oblob)[0]
+        pytest.fail(f"{what}: {diff.size} bytes differ, first at {diff[:6]}")
+
+
+@pytest.mark.parametrize("G", [4, 8, 1])
+def test_variable_length_batch_on_shuffled_pages(rdkv, G):
+    L, Hkv, cap = 2, 2, 80
+    Hq = G * Hkv
+    shapes = [(700, 1400, 256), (2100, 6000, 512), (300, 300, 100), (1500, 3000, 384)]   # (N, bv, bk)
+    N_max, bv_max, bk_max = 2100, 6000, 512
+    n_pages = 900
+    pl = rdkv.paged_layout(rdkv.make_dims(len(shapes), L, Hq, Hkv, N_max), bv_max, bk_max, cap, n_pages)
+    op = O.PagedLayout(len(shapes), L, Hq, Hkv, N_max, bv_max, bk_max, cap, n_pages)
+    cache = rdkv.paged_cache_init(pl)
+    oblob = O.paged_empty(op)
+    _same_bytes(cache, oblob, "empty cache")
+    pool = Pool(n_pages, 7 + G)
+    seqs = [_sequence(L, Hkv, *sh, seed=10 * i + G) for i, sh in enumerate(shapes)]
+    held = {}
+    for s, (sh, seq) in enumerate(zip(shapes, seqs)):
+        held[s] = _add(rdkv, pl, cache, oblob, op, pool, s, sh, seq)
+    _same_bytes(cache, oblob, "after commits")
+    r = np.random.default_rng(G)
+    ws = rdkv.paged_decode_workspace(pl)
+    c_len = [0, 3, 17, 64]                                   # each sequence at its own zone-C length
+    for s in range(len(shapes)):                             # bring zone C there (oracle and GPU alike)
+        for i in range(c_len[s]):
+            k = r.standard_normal((L, Hkv, 128)).astype(np.float16)
+            v = r.standard_normal((L, Hkv, 128)).astype(np.float16)
+            for l in range(L):
+                for h in range(Hkv):
+                    O.paged_write_zone_c(oblob, op, op.seg_index(s, l, h), i, k[l, h], v[l, h])
+    cache.copy_(dev(oblob))
+    worst = 0.0
+    for step in range(12):
+        q = r.standard_normal((len(shapes), L, Hq, 128)).astype(np.float16)
+        kn = r.standard_normal((len(shapes), L, Hkv, 128)).astype(np.float16)
+        vn = r.standard_normal((len(shapes), L, Hkv, 128)).astype(np.float16)
+        append = step % 4 != 3
+        out = rdkv.paged_decode(pl, cache, c_len, dev(q), dev(kn) if append else None, dev(vn) if append else None,
+                                workspace=ws)
+        ref = O.paged_decode_step(oblob, op, q, c_len, kn if append else None, vn if append else None)
+        e = rel_err(host(out), ref)
+        worst = max(worst, e)
+        assert e <= TOL, f"step {step}: rel err {e:.3g}"
+        if append:
+            c_len = [c + 1 for c in c_len]
+    _same_bytes(cache, oblob, "after decode steps")
+    # a sequence leaves; a longer one takes its pages (and more)
+    freed = O.paged_release_sequence(oblob, op, 2)
+    rdkv.paged_release(pl, cache, 2)
+    assert sorted(freed) == sorted(held[2])
+    pool.give(freed)
+    _same_bytes(cache, oblob, "after release")
+    new_shape = (1900, 5000, 448)
+    held[2] = _add(rdkv, pl, cache, oblob, op, pool, 2, new_shape, _sequence(L, Hkv, *new_shape, seed=99 + G))
+    _same_bytes(cache, oblob, "after the new sequence")
+    c_len[2] = 0
+    q = r.standard_normal((len(shapes), L, Hq, 128)).astype(np.float16)
+    out = rdkv.paged_decode(pl, cache, c_len, dev(q), workspace=ws)
+    e = rel_err(host(out), O.paged_decode_step(oblob, op, q, c_len))
+    assert e <= TOL
+    print(f"G={G}: worst rel err {max(worst, e):.3g}; pages in use {sum(len(v) for v in held.values())} of {n_pages}")
+
+
+def test_paged_decode_equals_contiguous_decode(rdkv):
+    """Equal-length sequences: the paged cache on shuffled pages decodes to the
+    same bits as the contiguous blob (same chunks, same arithmetic, same merge
+    order), with appends."""
+    S, L, Hq, Hkv, N, bv, bk, cap = 3, 2, 8, 2, 1500, 3200, 300, 70
+    seqs = [_sequence(L, Hkv, N, bv, bk, seed=200 + s) for s in range(S)]
+    lay = rdkv.layout(rdkv.make_dims(S, L, Hq, Hkv, N), bv, bk, cap)
+    flat = rdkv.cache_init(lay)
+    rdkv.pack(lay, flat, *(dev(np.stack([q[i] for q in seqs])) for i in range(4)))
+    pl = rdkv.paged_layout(rdkv.make_dims(S, L, Hq, Hkv, N), bv, bk, cap, 400)
+    op = O.PagedLayout(S, L, Hq, Hkv, N, bv, bk, cap, 400)
+    paged = rdkv.paged_cache_init(pl)
+    oblob = O.paged_empty(op)
+    pool = Pool(400, 5)
+    for s in range(S):
+        _add(rdkv, pl, paged, oblob, op, pool, s, (N, bv, bk), seqs[s])
+    r = np.random.default_rng(1)
+    for step in range(cap):
+        q = dev(r.standard_normal((S, L, Hq, 128)).astype(np.float16))
+        kn = dev(r.standard_normal((S, L, Hkv, 128)).astype(np.float16))
+        vn = dev(r.standard_normal((S, L, Hkv, 128)).astype(np.float16))
+        a = rdkv.decode(lay, flat, step, q, kn, vn)
+        b = rdkv.paged_decode(pl, paged, [step] * S, q, kn, vn)
+        assert torch.equal(a, b), f"step {step}"
