@@ -64,12 +64,24 @@ def counter_traffic(kernel, workload):
     return int(fields["traffic_bytes_per_launch"]), valu, os.path.relpath(path, ROOT)
 
 
-def build_cache(rdkv, synth, torch, w, lay, dims1, fp16_only=False, lay1=None):
+def build_cache(rdkv, synth, torch, w, lay, dims1, fp16_only=False, lay1=None, keep=False):
     """Score, allocate and pack every layer into a fresh cache; returns stats.
     With `lay1` (a one-layer layout), each layer is also packed into a blob of
-    its own (stats["layer_caches"]), for the per-layer decode loop."""
+    its own (stats["layer_caches"]), for the per-layer decode loop.  With
+    `keep`, stats["kept"] holds every layer's K, V and allocation
+    ([S][L][Hkv]...) and the allocation with one budget per layer shared by
+    its KV heads, for the paged and rollover measurements."""
     cache = rdkv.cache_init(lay)
     layer_caches = []
+    kept = None
+    if keep:
+        shp = (w.n_seq, w.n_layers, w.n_kv_heads)
+        kept = dict(K=torch.empty(shp + (w.n_tokens, 128), dtype=torch.float16, device="cuda"),
+                    V=torch.empty(shp + (w.n_tokens, 128), dtype=torch.float16, device="cuda"),
+                    bt=torch.empty(shp + (w.n_tokens,), dtype=torch.uint8, device="cuda"),
+                    bc=torch.empty(shp + (128,), dtype=torch.uint8, device="cuda"),
+                    bt_shared=torch.empty(shp + (w.n_tokens,), dtype=torch.uint8, device="cuda"),
+                    bc_shared=torch.empty(shp + (128,), dtype=torch.uint8, device="cuda"))
     S = w.n_seq
     ws = None
     hist_tok = np.zeros(5, np.int64)
@@ -110,16 +122,20 @@ def build_cache(rdkv, synth, torch, w, lay, dims1, fp16_only=False, lay1=None):
             e2.record()
             e2.synchronize()
             score_ms += e0.elapsed_time(e1)
-            if l == 0:
-                halves = halves + (e0.elapsed_time(e1), e1.elapsed_time(e2))
+            if l == 0 or keep:
                 # the same layer with one budget shared by its KV heads
                 e3, e4 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e3.record()
-                rdkv.allocate_shared(dims1, wt, vt, wc, K, w.budget_v * w.n_kv_heads, w.budget_k * w.n_kv_heads,
-                                     w.n_kv_heads)
+                bts, bcs, _, _ = rdkv.allocate_shared(dims1, wt, vt, wc, K, w.budget_v * w.n_kv_heads,
+                                                      w.budget_k * w.n_kv_heads, w.n_kv_heads)
                 e4.record()
                 e4.synchronize()
-                halves = halves + (e3.elapsed_time(e4),)
+                if l == 0:
+                    halves = halves + (e0.elapsed_time(e1), e1.elapsed_time(e2), e3.elapsed_time(e4))
+                if keep:
+                    kept["bt_shared"][:, l] = bts[:, 0]
+                    kept["bc_shared"][:, l] = bcs[:, 0]
+                del bts, bcs
             del wt, vt, wc
         rdkv.pack(lay, cache, K, V, bt, bc, layer_begin=l)
         if lay1 is not None:
@@ -128,13 +144,18 @@ def build_cache(rdkv, synth, torch, w, lay, dims1, fp16_only=False, lay1=None):
         for i, b in enumerate((0, 2, 4, 8, 16)):
             hist_tok[i] += int((bt == b).sum())
             hist_chan[i] += int((bc == b).sum())
+        if keep:
+            kept["K"][:, l] = K[:, 0]
+            kept["V"][:, l] = V[:, 0]
+            kept["bt"][:, l] = bt[:, 0]
+            kept["bc"][:, l] = bc[:, 0]
         del K, V, bt, bc
         if l % 8 == 7 or l == w.n_layers - 1:
             torch.cuda.synchronize()
             log(f"{'fp16 ' if fp16_only else ''}layer {l + 1}/{w.n_layers} packed, {time.time() - t0:.1f}s")
     torch.cuda.synchronize()
     return cache, dict(hist_tok=hist_tok, hist_chan=hist_chan, score_ms=score_ms, setup_s=time.time() - t0,
-                       layer_caches=layer_caches, score_halves=halves)
+                       layer_caches=layer_caches, score_halves=halves, kept=kept)
 
 
 def time_decode(rdkv, torch, lay, cache, q, kn, vn, steps, warmup, flush, grow=False):
@@ -250,6 +271,169 @@ def time_layer_graph(rdkv, torch, lay1, caches, q, kn, vn, steps, warmup, flush,
     return dict(step=float(t.mean()), step_median=float(np.median(t)), rel_diff=rel)
 
 
+def time_calls(torch, call, steps, warmup, flush):
+    """Event time (ms) of call(i), i = 0..steps-1, after call(0..warmup-1),
+    with the caches cleared between calls (see time_decode): mean, median."""
+    fbuf = torch.ones(1 << 27, dtype=torch.int64, device="cuda") if flush else None
+    for i in range(warmup):
+        call(i)
+        if fbuf is not None:
+            fbuf.sum()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record()
+        call(i)
+        ev[i][1].record()
+        if fbuf is not None:
+            fbuf.sum()
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in ev])
+    del fbuf
+    return float(t.mean()), float(np.median(t))
+
+
+def chunk_stats(chunk_tok2, token_slots, desc):
+    """Decode chunks per segment (the token groups' chunks of chunk_tok2 >> g
+    tokens) against the chunk slots the layout reserves."""
+    n = np.zeros(len(desc["n_tok"]), np.int64)
+    for g in range(4):
+        t = chunk_tok2 >> g
+        n += (desc["n_tok"][:, g] + t - 1) // t
+    return {"chunk_tok2": int(chunk_tok2), "slots_per_segment": int(token_slots), "total": int(n.sum()),
+            "per_segment_max": int(n.max()), "per_segment_mean": round(float(n.mean()), 2)}
+
+
+def build_paged(rdkv, torch, w, K, V, bt, bc, budget_v, budget_k, seed=0):
+    """Every sequence of K, V, bt, bc ([S][L][Hkv]...) staged, given pages
+    from a host free list in shuffled order (no segment's pages contiguous)
+    and committed into a paged cache whose pool holds exactly the pages
+    needed.  Returns (paged layout, cache, pages in use)."""
+    S, L, Hkv, N = K.shape[0], K.shape[1], K.shape[2], K.shape[3]
+    dims = rdkv.make_dims(S, L, w.n_q_heads, Hkv, N)
+    staged, total = [], 0
+    pl0 = rdkv.paged_layout(dims, budget_v, budget_k, w.zone_c_capacity, 1)
+    for s in range(S):
+        stg, need = rdkv.paged_stage(pl0, N, budget_v, budget_k, K[s], V[s], bt[s], bc[s])
+        need = need.cpu().numpy()
+        staged.append((stg, need))
+        total += int(need.sum())
+    pl = rdkv.paged_layout(dims, budget_v, budget_k, w.zone_c_capacity, total)
+    cache = rdkv.paged_cache_init(pl)
+    free = np.random.default_rng(seed).permutation(total).astype(np.int32)
+    at = 0
+    for s, (stg, need) in enumerate(staged):
+        table = np.full((L * Hkv, pl.max_pages), -1, np.int32)
+        for i, k in enumerate(need):
+            table[i, :k] = free[at:at + k]
+            at += int(k)
+        rdkv.paged_commit(pl, cache, s, N, budget_v, budget_k, stg, torch.from_numpy(table).cuda())
+    torch.cuda.synchronize()
+    del staged
+    flags = cache[256:256 + 256 * pl.n_seg].view(-1, 256)[:, 44:48].cpu().numpy().view(np.int32)
+    if flags.any():
+        raise RuntimeError(f"{int((flags != 0).sum())} segments did not fit their pages")
+    return pl, cache, total
+
+
+def extras(rdkv, torch, w, lay, cache, kept, q, kn, vn, ref_out, steps, warmup, flush, grow, n_c):
+    """Paged zones (per-segment budgets, and one budget per layer shared by
+    its KV heads) and zone-C rollover on the same data as the headline
+    decode."""
+    res = {}
+    S, cap = w.n_seq, w.zone_c_capacity
+    row = (lambda i: i % cap) if grow else (lambda i: 0)
+    K, V = kept["K"], kept["V"]
+    out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+
+    def algo_bytes(cache):
+        # the paged descriptors carry the counts at the contiguous offsets
+        b = rdkv.decode_bytes(lay, rdkv.descriptors(lay, cache), n_c)
+        return b["total"] + lay.n_seg * (256 + 2 * 128 * 2)
+
+    # per-segment budgets on pages: the same allocation as the contiguous blob
+    pl, pc, used = build_paged(rdkv, torch, w, K, V, kept["bt"], kept["bc"], w.budget_v, w.budget_k, seed=1)
+    ws = rdkv.paged_decode_workspace(pl)
+    wsc = rdkv.decode_workspace(lay)
+    outc = torch.empty_like(out)
+    tc, _ = time_calls(torch, lambda i: rdkv.decode(lay, cache, row(i), q, kn, vn, workspace=wsc, out=outc),
+                       steps, warmup, flush)
+    t, tm = time_calls(torch, lambda i: rdkv.paged_decode(pl, pc, [row(i)] * S, q, kn, vn, workspace=ws, out=out),
+                       steps, warmup, flush)
+    del wsc, outc
+    res["paged"] = {
+        "us_per_step": round(t * 1e3, 2), "us_per_step_median": round(tm * 1e3, 2),
+        "contiguous_us_per_step_just_before": round(tc * 1e3, 2),
+        "bit_identical_to_contiguous": bool(torch.equal(out, ref_out)),
+        "achieved_GBs": round(algo_bytes(pc) / (t * 1e-3) / 1e9, 1),
+        "chunks": chunk_stats(pl.chunk_tok2, pl.token_slots, rdkv.descriptors(lay, pc)),
+        "pages_in_use": used, "page_bytes": rdkv.PAGE_BYTES, "resident_bytes": int(pl.pool_offset + used * rdkv.PAGE_BYTES),
+        "contiguous_blob_bytes": int(lay.cache_bytes),
+        "note": "the same packed segments on 32 KiB pages of a shared pool, given out shuffled; one rdkv_paged_decode "
+                "(chunk + merge kernels) per step; resident bytes = header, descriptors, block table and the pages in use"}
+    log(f"paged: {t * 1e3:.1f} us per step, {used} pages, bit-identical {res['paged']['bit_identical_to_contiguous']}")
+    del pc, ws
+    torch.cuda.empty_cache()
+
+    # one budget per layer, shared by its KV heads, on pages
+    Hkv = w.n_kv_heads
+    bvs, bks = w.budget_v * Hkv, w.budget_k * Hkv
+    pl, pc, used = build_paged(rdkv, torch, w, K, V, kept["bt_shared"], kept["bc_shared"], bvs, bks, seed=2)
+    ws = rdkv.paged_decode_workspace(pl)
+    t, tm = time_calls(torch, lambda i: rdkv.paged_decode(pl, pc, [row(i)] * S, q, kn, vn, workspace=ws, out=out),
+                       steps, warmup, flush)
+    lay_shared = rdkv.layout(rdkv.make_dims(S, w.n_layers, w.n_q_heads, Hkv, w.n_tokens), bvs, bks, cap)
+    res["shared_budget_paged"] = {
+        "us_per_step": round(t * 1e3, 2), "us_per_step_median": round(tm * 1e3, 2),
+        "budget_v_per_layer": bvs, "budget_k_per_layer": bks,
+        "algorithmic_bytes_per_step": int(algo_bytes(pc)), "achieved_GBs": round(algo_bytes(pc) / (t * 1e-3) / 1e9, 1),
+        "pages_in_use": used, "resident_bytes": int(pl.pool_offset + used * rdkv.PAGE_BYTES),
+        "contiguous_blob_bytes_same_budgets": int(lay_shared.cache_bytes),
+        "contiguous_blob_bytes_per_segment_budgets": int(lay.cache_bytes),
+        "resident_vs_per_segment_blob": round((pl.pool_offset + used * rdkv.PAGE_BYTES) / lay.cache_bytes, 4),
+        "chunks": chunk_stats(pl.chunk_tok2, pl.token_slots, rdkv.descriptors(lay, pc)),
+        "note": "rdkv_allocate_shared with one budget per layer (its KV heads' budgets pooled), packed on pages: "
+                "memory follows what each segment keeps instead of a slot sized for the whole layer's budget"}
+    log(f"shared budget on pages: {t * 1e3:.1f} us per step, {used} pages")
+    del pc, ws
+    torch.cuda.empty_cache()
+
+    # zone-C rollover, n_gen times: cap steps with the decode-time statistics,
+    # then a rollover; then decode over the prefill blob and the generations
+    n_gen = 4
+    gbv, gbk = max(1, w.budget_v * cap // w.n_tokens), w.budget_k
+    dims = rdkv.make_dims(S, w.n_layers, w.n_q_heads, Hkv, w.n_tokens)
+    lr = rdkv.layout_rollover(dims, w.budget_v, w.budget_k, cap, n_gen, gbv, gbk)
+    cr = rdkv.cache_init(lr)
+    rdkv.pack(lr, cr, K, V, kept["bt"], kept["bc"])
+    ws = rdkv.decode_workspace(lr)
+    stats = rdkv.zone_c_stats(lr)
+    rws = torch.empty(max(int(lr.rollover_workspace_bytes), 16), dtype=torch.uint8, device="cuda")
+    t_plain, _ = time_calls(torch, lambda i: rdkv.decode(lr, cr, i, q, kn, vn, workspace=ws, out=out), cap, 0, flush)
+    t_acc, t_roll = [], []
+    for g in range(n_gen):
+        t_acc.append(time_calls(torch, lambda i: rdkv.decode_accumulate(lr, cr, i, q, kn, vn, stats, workspace=ws,
+                                                                        out=out), cap, 0, flush)[0])
+        t_roll.append(time_calls(torch, lambda i: rdkv.rollover(lr, cr, g, stats, workspace=rws), 1, 0, flush)[0])
+    t_gen, t_gen_med = time_calls(torch, lambda i: rdkv.decode(lr, cr, row(i), q, kn, vn, workspace=ws, out=out),
+                                  steps, warmup, flush)
+    res["rollover"] = {
+        "zone_c_capacity": cap, "generations": n_gen, "gen_budget_v": gbv, "gen_budget_k": gbk,
+        "decode_us_per_step": round(t_plain * 1e3, 2),
+        "decode_accumulate_us_per_step": round(float(np.mean(t_acc)) * 1e3, 2),
+        "rollover_us": [round(x * 1e3, 1) for x in t_roll],
+        "decode_us_per_step_all_generations": round(t_gen * 1e3, 2),
+        "generation_blob_bytes": int(lr.gen_bytes),
+        "note": "decode and decode_accumulate averaged over zone-C lengths 1..cap (accumulate over every generation's "
+                "fill); rollover = score, allocate and pack the full zone C of every segment into the next generation "
+                "blob and clear it, once per generation; then decode over the prefill blob and every generation"}
+    log(f"rollover: decode {t_plain * 1e3:.1f} us, accumulate {np.mean(t_acc) * 1e3:.1f} us, rollover "
+        f"{[round(x * 1e3, 1) for x in t_roll]} us, decode with {n_gen} generations {t_gen * 1e3:.1f} us")
+    del cr, ws, stats, rws
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_scoring_baseline(w, n_sample: int = 8192):
     """The oracle's stage-1 token weights of one (layer, KV head), timed on the
     first n_sample prefill rows and keys of a seeded layer (its G query heads)
@@ -344,6 +528,9 @@ def main():
     ap.add_argument("--cpu-sample-segments", type=int, default=32)
     ap.add_argument("--no-layer-loop", action="store_true",
                     help="skip the per-layer decode loop (one launch pair per layer, captured in a HIP graph)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the paged-zone, shared-budget and rollover measurements (on by default when the "
+                         "workload's fp16 K/V fits in 40 GB)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run one plain 384 MiB device-to-device copy (for counter calibration)")
     args = ap.parse_args()
@@ -367,7 +554,9 @@ def main():
     lay = rdkv.layout(dims, w.budget_v, w.budget_k, w.zone_c_capacity)
     per_layer = w.n_layers > 1 and not args.no_layer_loop
     lay1 = rdkv.layout(dims1, w.budget_v, w.budget_k, w.zone_c_capacity) if per_layer else None
-    cache, st = build_cache(rdkv, synth, torch, w, lay, dims1, lay1=lay1)
+    kv_bytes = 2 * w.n_seq * w.n_layers * w.n_kv_heads * w.n_tokens * 128 * 2
+    do_extras = not args.no_extras and kv_bytes <= 40e9
+    cache, st = build_cache(rdkv, synth, torch, w, lay, dims1, lay1=lay1, keep=do_extras)
     q, kn, vn = synth.decode_inputs(w, 0, device="cuda")
     batched = w.n_seq > 1
     grow = args.grow or batched
@@ -395,6 +584,12 @@ def main():
                               "HIP graph and replayed per step (every replay checked against the eager loop)"}
         log(f"per-layer graph loop: {tg['step'] * 1e3:.1f} us per step")
     st.pop("layer_caches", None)
+    extra = None
+    if do_extras:
+        extra = extras(rdkv, torch, w, lay, cache, st["kept"], q, kn, vn, tm["out"], args.steps, args.warmup,
+                       not args.no_flush, grow, n_c)
+    st.pop("kept", None)
+    torch.cuda.empty_cache()
 
     desc = rdkv.descriptors(lay, cache)
     b = rdkv.decode_bytes(lay, desc, n_c)
@@ -484,6 +679,8 @@ def main():
     }
     if layer_loop is not None:
         result["per_layer_graph_loop"] = layer_loop
+    if extra is not None:
+        result.update(extra)
     del cache
     torch.cuda.empty_cache()
     if not args.no_fp16_baseline:

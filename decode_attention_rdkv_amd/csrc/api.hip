@@ -533,6 +533,7 @@ rdkv_status rdkv_paged_layout_init(const rdkv_dims* dims_max, int64_t budget_v_m
   P.table_offset = align_up(kHeaderBytes + uint64_t(kDescBytes) * P.n_seg, kAlign);
   P.pool_offset = align_up(P.table_offset + 4 * uint64_t(P.n_seg) * P.max_pages, 4096);
   P.cache_bytes = P.pool_offset + uint64_t(n_pages) * kPageBytes;
+  if (P.cache_bytes >= kPagedMaxCacheBytes) return RDKV_ERR_SHAPE;   // tile offsets fit 32 bits in 256-byte units
   const int G = dims_max->n_q_heads / dims_max->n_kv_heads;
   P.decode_workspace_bytes = uint64_t(P.n_seg) * P.max_chunks * G * kPartialFloats * sizeof(float);
   *out = P;

@@ -54,6 +54,14 @@ template <int G> constexpr int kHeadsPerWave = G > 4 ? 4 : G;
 // Tile streams of a workgroup: waves with the same stream index walk the same tiles.
 template <int G> constexpr int kStreams = kWaves / (G / kHeadsPerWave<G>);
 constexpr int kTile = 64;
+// Paged decode: the most tiles one wave walks in a chunk, and whether its tile
+// offsets go through LDS (more than 64: one list per tile stream, [stream][V,
+// records][tile], which the two waves of a stream write alike) instead of a
+// register per lane.
+template <int G> constexpr int kWaveTilesMax = kChunkTok2Max / kTile / kStreams<G>;
+template <int G, bool kPaged> constexpr bool kPgLds = kPaged && (kWaveTilesMax<G> > 64);
+template <int G, bool kPaged>
+constexpr int kPgLdsWords = kPgLds<G, kPaged> ? kStreams<G> * 2 * kWaveTilesMax<G> : 1;
 constexpr float kLog2eOverSqrtD = 1.4426950408889634f / 11.313708498984761f;
 constexpr float kTwo24 = 16777216.0f;   // codes enter dot2 as fp16 subnormals code * 2^-24
 constexpr int kPairSlots = 80;          // >= w16 + 2*w8 + 4*w4 + 8*w2 for any split of 128 channels
@@ -196,6 +204,18 @@ __device__ inline uint64_t paged_tile(const DecodeParams& p, const int32_t* tabl
   const int phys = (vp >= 0 && vp < p.max_pages) ? table[vp] : -1;
   ok = phys >= 0 && phys < p.pool_pages;
   return p.pool_offset + uint64_t(ok ? phys : 0) * kPageBytes + uint64_t(uint32_t(tile) % tpp) * tile_bytes;
+}
+
+// The same offset in 256-byte units (every tile of a paged cache starts on a
+// 256-byte boundary and the cache is below 2^40 bytes, so it fits 32 bits);
+// kNoPage for an entry outside the block table or the pool.
+constexpr uint32_t kNoPage = 0xffffffffu;
+__device__ inline uint32_t paged_tile_units(const DecodeParams& p, const int32_t* table, int vp0, uint32_t tile,
+                                            uint32_t tpp, uint32_t tile_bytes) {
+  const int vp = vp0 + int(tile / tpp);
+  const int phys = (vp >= 0 && vp < p.max_pages) ? table[vp] : -1;
+  if (phys < 0 || phys >= p.pool_pages) return kNoPage;
+  return uint32_t((p.pool_offset + uint64_t(phys) * kPageBytes + uint64_t(tile % tpp) * tile_bytes) >> 8);
 }
 
 // A paged segment's descriptor (the contiguous fields' meaning for counts,
@@ -793,9 +813,13 @@ __device__ inline void dma_records(const uint8_t* src, uint32_t bytes, uint32_t*
 // kPaged: the group's V rows and K records are 64-row tiles on pages found
 // through the segment's block table (a chunk starts on a tile boundary, so
 // tile i is the group's tile tile_row(i) / 64, whole on one page); each
-// tile's resource or copy covers just that tile.
+// tile's resource or copy covers just that tile.  The wave looks its tiles up
+// once, at the start of the chunk (lane j: the wave's tiles j, j + 64, ...),
+// and a tile step takes its two offsets with a readlane each, so no table
+// read sits between a tile's turn and its loads.
 template <int G, int B, int SW, bool PIPE, bool kPaged>
-__device__ void run_group(const DecodeParams& p, const SegInfo& si, const Plan& pl, int64_t seg, Smem<G, SW>& sm) {
+__device__ void run_group(const DecodeParams& p, const SegInfo& si, const Plan& pl, int64_t seg, Smem<G, SW>& sm,
+                          uint32_t* pg_lds) {
   constexpr int GW = kHeadsPerWave<G>, kNS = kStreams<G>, kStride = kTile * kNS;
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int cb = lane & 15, ts = lane >> 4;
@@ -837,19 +861,58 @@ __device__ void run_group(const DecodeParams& p, const SegInfo& si, const Plan& 
   // word offset (from off_krec) of tile i's first record
   auto rec_word = [&](int i) { return pl.rec0 + int64_t(tile_row(i)) * nw; };
   const uint32_t voff16 = uint32_t(lane) * 16u;
-  // paged: record tiles of 64 * nw words, kPageBytes / that per page
-  const uint32_t rec_tile_bytes = uint32_t(kTile) * 4u * uint32_t(nw);
-  const uint32_t rec_tpp = nw > 0 ? uint32_t(kPageBytes) / rec_tile_bytes : 1u;
-  auto rec_tile = [&](int i, bool& ok) {
-    return paged_tile(p, si.table, pl.vp_b, tile_row(i) / kTile, rec_tpp, rec_tile_bytes, ok);
+  // paged: per lane, the V and record tile offsets (256-byte units) of the
+  // wave's tiles lane + 64 k; record tiles are 64 * nw words, kPageBytes /
+  // that per page
+  // (at most 64 tiles per wave: one register per lane and region; more
+  // (G = 8) go through the stream's LDS list, pg_lds)
+  constexpr int kWaveTiles = kWaveTilesMax<G>;
+  constexpr bool kLds = kPgLds<G, kPaged>;
+  uint32_t* const pgl = pg_lds + (wave % kNS) * 2 * kWaveTiles;
+  uint32_t pg_v = kNoPage, pg_r = kNoPage;
+  if constexpr (kPaged) {
+    constexpr uint32_t kVTileBytes = uint32_t(kTile) * kRowBytes;
+    const uint32_t rec_tile_bytes = uint32_t(kTile) * 4u * uint32_t(nw);
+    const uint32_t rec_tpp = nw > 0 ? uint32_t(kPageBytes) / rec_tile_bytes : 1u;
+#pragma unroll
+    for (int k = 0; k < (kWaveTiles + 63) / 64; ++k) {
+      const int j = lane + 64 * k;
+      uint32_t v = kNoPage, r = kNoPage;
+      if (j < n_tiles) {
+        const uint32_t t = uint32_t(first + kStride * j) / kTile;
+        v = paged_tile_units(p, si.table, pl.vp_a, t, kPageBytes / kVTileBytes, kVTileBytes);
+        if (nw > 0) r = paged_tile_units(p, si.table, pl.vp_b, t, rec_tpp, rec_tile_bytes);
+      }
+      if constexpr (kLds) {
+        pgl[j] = v;                  // (the stream's other wave writes the same values)
+        pgl[kWaveTiles + j] = r;
+      } else {
+        pg_v = v;
+        pg_r = r;
+      }
+    }
+    if constexpr (kLds) wave_lds_sync();
+  }
+  // tile i's entry, region 0 (V) or 1 (records); tiles past the wave's last
+  // take its last tile's, as tile_row does
+  auto lane_tile = [&](int region, int i) -> uint32_t {
+    const int j = max(min(i, n_tiles - 1), 0);
+    if constexpr (kLds) return __builtin_amdgcn_readfirstlane(pgl[region * kWaveTiles + j]);
+    else return __builtin_amdgcn_readlane(region ? pg_r : pg_v, j);
+  };
+  // An entry outside the table or the pool reads as the pool's first page
+  // with ok = false (callers then read nothing through it).
+  auto tile_ptr = [&](uint32_t u, bool& ok) {
+    ok = u != kNoPage;
+    return p.cache + (ok ? uint64_t(u) << 8 : p.pool_offset);
   };
   auto fetch_records = [&](int i) {
     if constexpr (SW > 0) {
       const int rows = tile_rows(i);
       if constexpr (kPaged) {
         bool ok;
-        const uint64_t t = rec_tile(i, ok);
-        dma_records<SW>(p.cache + t, (rows > 0 && ok) ? uint32_t(rows * nw) * 4u : 0u, stage(i), voff16);
+        const uint8_t* t = tile_ptr(lane_tile(1, i), ok);
+        dma_records<SW>(t, (rows > 0 && ok) ? uint32_t(rows * nw) * 4u : 0u, stage(i), voff16);
       } else {
         const int64_t w0 = rec_word(i);
         const int m = int(w0 & 3);                                 // block start within its 16 bytes
@@ -864,10 +927,9 @@ __device__ void run_group(const DecodeParams& p, const SegInfo& si, const Plan& 
   const uint32_t sel2 = (cb & 1) ? 0x07060302u : 0x05040100u;      // the lane's half of a 2-bit dword
   auto vrsrc = [&](int i) {
     if constexpr (kPaged) {
-      constexpr uint32_t kTileBytes = uint32_t(kTile) * kRowBytes;
       bool ok;
-      const uint64_t t = paged_tile(p, si.table, pl.vp_a, tile_row(i) / kTile, kPageBytes / kTileBytes, kTileBytes, ok);
-      return buffer_rsrc(p.cache + t, ok ? uint32_t(tile_rows(i) * kRowBytes) : 0u);
+      const uint8_t* t = tile_ptr(lane_tile(0, i), ok);
+      return buffer_rsrc(t, ok ? uint32_t(tile_rows(i) * kRowBytes) : 0u);
     } else {
       return buffer_rsrc(vbase + int64_t(tile_row(i)) * kRowBytes, uint32_t(tile_rows(i) * kRowBytes));
     }
@@ -906,7 +968,7 @@ __device__ void run_group(const DecodeParams& p, const SegInfo& si, const Plan& 
       my = stage(i) + (kPaged ? 0 : int(rec_word(i) & 3)) + lane_rec;
     } else if constexpr (kPaged) {
       bool ok;   // (an entry outside the pool reads page 0: in memory, the segment's output is then wrong)
-      my = reinterpret_cast<const uint32_t*>(p.cache + rec_tile(i, ok)) + (min(b + lane, pl.end - 1) - b) * nw;
+      my = reinterpret_cast<const uint32_t*>(tile_ptr(lane_tile(1, i), ok)) + (min(b + lane, pl.end - 1) - b) * nw;
     } else {
       my = reinterpret_cast<const uint32_t*>(rbytes) + pl.rec0 + int64_t(min(b + lane, pl.end - 1)) * nw;
     }
@@ -1111,6 +1173,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
                                                                                                        Lens lens) {
   constexpr bool kPaged = kIsPaged<Lens>;
   __shared__ Smem<G, SW> sm;
+  __shared__ uint32_t pg_lds[kPgLdsWords<G, kPaged>];
   // Chunk-major order: every segment's first chunk, then every second chunk,
   // ...  The full 2-bit chunks come first and the short tails, fp16 and zone-C
   // chunks last, so the dispatcher's in-order fill ends on light work; and
@@ -1176,10 +1239,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   }
 
   switch (pl.kind) {
-    case 0: run_group<G, 2, SW, true, kPaged>(p, si, pl, seg, sm); break;
-    case 1: run_group<G, 4, SW, true, kPaged>(p, si, pl, seg, sm); break;
-    case 2: run_group<G, 8, SW, false, kPaged>(p, si, pl, seg, sm); break;
-    case 3: run_group<G, 16, SW, false, kPaged>(p, si, pl, seg, sm); break;
+    case 0: run_group<G, 2, SW, true, kPaged>(p, si, pl, seg, sm, pg_lds); break;
+    case 1: run_group<G, 4, SW, true, kPaged>(p, si, pl, seg, sm, pg_lds); break;
+    case 2: run_group<G, 8, SW, false, kPaged>(p, si, pl, seg, sm, pg_lds); break;
+    case 3: run_group<G, 16, SW, false, kPaged>(p, si, pl, seg, sm, pg_lds); break;
     default: run_zone_c<G, SW, kPaged>(p, si, seg, pl, c_len, append, sm); break;
   }
   __syncthreads();

@@ -132,6 +132,9 @@ constexpr int kPageBytes = RDKV_PAGE_BYTES;
 constexpr int kMaxPagedSeqs = RDKV_MAX_PAGED_SEQS;
 constexpr uint32_t kPagedMagic = 0x504B4452u;  // "RDKP"
 constexpr int kPagedTile = 64;
+// A paged cache stays below 1 TiB, so decode can hold a tile's offset in 32
+// bits as a count of 256-byte units (every tile starts on such a boundary).
+constexpr uint64_t kPagedMaxCacheBytes = uint64_t(1) << 40;
 // regions: V rows of groups 0..3, K records of groups 0..3, zone-C K, zone-C V, positions
 constexpr int kRegions = 11;
 constexpr int kRegV = 0, kRegRec = 4, kRegKC = 8, kRegVC = 9, kRegPos = 10;

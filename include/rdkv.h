@@ -365,7 +365,7 @@ typedef struct rdkv_paged_layout {
 /* Host only.  dims_max: sequence slots, layers, heads, and the bound on any
  * sequence's prefill length; budget bounds per segment; zone-C capacity;
  * n_pages >= 1.  Errors as rdkv_layout_init, RDKV_ERR_SHAPE for n_seq >
- * RDKV_MAX_PAGED_SEQS or n_pages < 1. */
+ * RDKV_MAX_PAGED_SEQS, n_pages < 1 or a cache of 1 TiB (2^40 bytes) or more. */
 rdkv_status rdkv_paged_layout_init(const rdkv_dims* dims_max, int64_t budget_v_max, int64_t budget_k_max,
                                    int32_t zone_c_capacity, int64_t n_pages, rdkv_paged_layout* out);
 /* Zero the buffer, write the header, every slot free, the table -1. */
