@@ -516,9 +516,19 @@ rdkv_status rdkv_paged_layout_init(const rdkv_dims* dims_max, int64_t budget_v_m
   P.nk_max = b.nk_max;
   P.zone_c_capacity = zone_c_capacity;
   P.rec_max = b.rec_max;
-  P.token_slots = b.token_slots;
-  P.chunk_tok2 = b.chunk_tok2;
-  P.max_chunks = b.max_chunks;
+  // Split-K granularity: the contiguous rule sizes chunks for every segment
+  // holding its whole bound, which a budget shared across segments (bounds of
+  // the group's budget) makes several times what they hold together.  The
+  // pool bounds that total: at most n_pages * kPageBytes / 32 2-bit V rows, so
+  // the chunk size is the smaller of the two rules' (equal to the contiguous
+  // layout's whenever the pool is at least what the bounds need).
+  const int64_t v_units = std::min<int64_t>(budget_v_max / 2, 8 * dims_max->n_tokens);
+  const uint64_t pool_units = uint64_t(n_pages) * kPageBytes / 32;
+  int64_t t2 = kChunkTok2Min;
+  while (t2 < b.chunk_tok2 && pool_units / uint64_t(2 * t2) >= uint64_t(kDecodeTargetChunks)) t2 *= 2;
+  P.chunk_tok2 = int32_t(t2);
+  P.token_slots = int32_t(v_units / t2 + 4);
+  P.max_chunks = int32_t(P.token_slots + cdiv(zone_c_capacity, kChunkRowsC));
   // block-table width: every region at its own worst case within the bounds
   const int64_t N = dims_max->n_tokens;
   int64_t pages = 0;

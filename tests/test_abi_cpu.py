@@ -297,9 +297,17 @@ def test_paged_layout_matches_oracle(shape):
     assert (pl.max_pages, pl.table_offset, pl.pool_offset, pl.cache_bytes) == \
         (op.max_pages, op.table_offset, op.pool_offset, op.cache_bytes)
     flat = rdkv.layout(rdkv.make_dims(S, L, Hq, Hkv, N), bv, bk, cap)
-    assert (pl.max_chunks, pl.chunk_tok2, pl.rec_max, pl.nk_max) == (flat.max_chunks, flat.chunk_tok2, flat.rec_max,
-                                                                     flat.nk_max)
-    assert pl.decode_workspace_bytes == flat.decode_workspace_bytes
+    assert (pl.rec_max, pl.nk_max) == (flat.rec_max, flat.nk_max)
+    # chunk size: the contiguous rule, capped by what the pool can hold (2-bit V rows of 32 bytes)
+    t2 = 512
+    while t2 < flat.chunk_tok2 and (n_pages * 32768 // 32) // (2 * t2) >= 512:
+        t2 *= 2
+    assert pl.chunk_tok2 == t2 <= flat.chunk_tok2
+    assert pl.token_slots == min(bv // 2, 8 * N) // t2 + 4
+    assert pl.max_chunks == pl.token_slots + -(-cap // 256)
+    assert pl.decode_workspace_bytes == S * L * Hkv * pl.max_chunks * (Hq // Hkv) * 132 * 4
+    if t2 == flat.chunk_tok2:                 # a pool that does not bind chunks like the contiguous layout
+        assert (pl.max_chunks, pl.token_slots) == (flat.max_chunks, flat.token_slots)
 
 
 def test_paged_validation(lib):
