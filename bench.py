@@ -190,12 +190,15 @@ def time_decode(rdkv, torch, lay, cache, q, kn, vn, steps, warmup, flush, grow=F
     def merge(i):
         rdkv.decode_merge(lay, cache, row(i) + 1, ws, out)
 
+    # events exist before the warmup, so the timed loop follows the
+    # synchronization with no host work in between (the part clocks down
+    # within a millisecond of idling)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     for i in range(warmup):
         step(i)
         merge(i)
         clear_caches()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
         ev[i][0].record()
@@ -275,12 +278,12 @@ def time_calls(torch, call, steps, warmup, flush):
     """Event time (ms) of call(i), i = 0..steps-1, after call(0..warmup-1),
     with the caches cleared between calls (see time_decode): mean, median."""
     fbuf = torch.ones(1 << 27, dtype=torch.int64, device="cuda") if flush else None
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for i in range(warmup):
         call(i)
         if fbuf is not None:
             fbuf.sum()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for i in range(steps):
         ev[i][0].record()
         call(i)

@@ -659,21 +659,30 @@ __device__ inline void state_init(WaveState<G>& st) {
   }
 }
 
-// Online softmax update for one tile (lane = token): the running max m (log2
-// units, wave-uniform) is raised, with the sums rescaled, only when some
-// lane's logit exceeds it.  Writes fp16 p*vs per token to LDS.
+// Online softmax update for one tile (lane = token).  The running max m (log2
+// units, wave-uniform) is a reference, not necessarily the maximum: the
+// partial (m, l, o) is exact for any m, so it is raised, with the sums
+// rescaled, only when some lane's p = 2^(t - m) would pass kLazy or its fp16
+// coefficient p*vs would overflow (and on the first tile, where m = -inf).
+// A tile in which a logit merely exceeds m (more than one in four tiles of a
+// long chunk) then costs no wave reduction.  Writes fp16 p*vs per token to LDS.
 template <int GW, int G, int SW, bool kMasked>
 __device__ inline void softmax_tile(WaveState<GW>& st, const float (&s)[GW], bool valid, float vs, float vz,
                                     Smem<G, SW>& sm, int wave, int lane) {
-  float t[GW];
-  bool up = false;
+  constexpr float kLazy = 16.f;
+  float t[GW], pr[GW], c[GW];
 #pragma unroll
   for (int g = 0; g < GW; ++g) {
     t[g] = (!kMasked || valid) ? s[g] * kLog2eOverSqrtD : -INFINITY;
-    up = up || t[g] > st.m[g];
+    pr[g] = __builtin_amdgcn_exp2f(t[g] - st.m[g]);
+    c[g] = pr[g] * vs;
   }
-  // one wave-uniform branch per tile: some lane's logit exceeds its head's
-  // running max, so every such head's max moves and its sums are rescaled
+  // one wave-uniform branch per tile, rescaling every head (a head whose
+  // logits stay below its m keeps it: alpha = 1); masked lanes of the first
+  // tile give p = NaN here, which passes no test, and 0 once m is finite
+  bool up = false;
+#pragma unroll
+  for (int g = 0; g < GW; ++g) up = up || pr[g] > kLazy || c[g] > 65504.f;
   if (__builtin_amdgcn_ballot_w64(up) != 0) {
 #pragma unroll
     for (int g = 0; g < GW; ++g) {
@@ -684,14 +693,15 @@ __device__ inline void softmax_tile(WaveState<GW>& st, const float (&s)[GW], boo
       st.z[g] *= alpha;
 #pragma unroll
       for (int e = 0; e < 8; ++e) st.acc[g][e] *= alpha;
+      pr[g] = __builtin_amdgcn_exp2f(t[g] - mnew);
+      c[g] = pr[g] * vs;
     }
   }
 #pragma unroll
   for (int g = 0; g < GW; ++g) {
-    const float pr = __builtin_amdgcn_exp2f(t[g] - st.m[g]);
-    st.l[g] += pr;
-    st.z[g] = fmaf(pr, vz, st.z[g]);
-    reinterpret_cast<uint16_t*>(&sm.coefh[wave][lane & 31][g])[lane >> 5] = __half_as_ushort(__float2half_rn(pr * vs));
+    st.l[g] += pr[g];
+    st.z[g] = fmaf(pr[g], vz, st.z[g]);
+    reinterpret_cast<uint16_t*>(&sm.coefh[wave][lane & 31][g])[lane >> 5] = __half_as_ushort(__float2half_rn(c[g]));
   }
 }
 
