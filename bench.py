@@ -466,6 +466,56 @@ def cpu_scoring_baseline(w, n_sample: int = 8192):
                        f"prefill positions, {dt:.2f} s, scaled by (N/{n})^2")
 
 
+def cpu_baseline_all_stages(name: str = "tiny-gqa4-n1k"):
+    """Every stage of the oracle, single-threaded, on the tiny one-layer
+    workload: token and channel weights and variances, the allocation, the
+    packed blob, then the workload's decode steps with appends."""
+    import oracle as O
+    from decode_attention_rdkv_amd import synth
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:
+        threadpool_limits = None
+    w = synth.WORKLOADS[name]
+    Q, K, V = synth.prefill_layer(w, 0, 0)
+    G, N = w.group, w.n_tokens
+    lay = O.Layout(1, 1, w.n_q_heads, w.n_kv_heads, 128, N, w.budget_v, w.budget_k, w.zone_c_capacity)
+    t = {}
+    ctx = threadpool_limits(1) if threadpool_limits else None
+    if ctx:
+        ctx.__enter__()
+    try:
+        t0 = time.perf_counter()
+        bts, bcs = [], []
+        for h in range(w.n_kv_heads):
+            w_tok = O.token_weights(Q[h * G:(h + 1) * G], K[h]).astype(np.float32)
+            w_chan = O.channel_weights(Q[h * G:(h + 1) * G], K[h]).astype(np.float32)
+            var_tok = O.token_variance(V[h]).astype(np.float32)
+            t1 = time.perf_counter()
+            a = O.allocate_segment(w_tok, var_tok, w_chan, K[h], w.budget_v, w.budget_k)
+            t2 = time.perf_counter()
+            t["score"] = t.get("score", 0.0) + t1 - t0
+            t["allocate"] = t.get("allocate", 0.0) + t2 - t1
+            bts.append(a["bits_tok"])
+            bcs.append(a["bits_chan"])
+            t0 = time.perf_counter()
+        blob = O.pack_cache(lay, K[None, None], V[None, None], np.stack(bts)[None, None], np.stack(bcs)[None, None])
+        t["pack"] = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        for step in range(w.decode_steps):
+            q, kn, vn = synth.decode_inputs(w, step)
+            O.decode_step(blob, lay, q, step, kn, vn)
+        t["decode"] = time.perf_counter() - t0
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    total = sum(t.values())
+    return dict(value=round(total, 3), unit="s", cores=1, kind="oracle",
+                stages_s={k: round(v, 3) for k, v in t.items()},
+                sample=f"the whole {name} workload ({w.n_kv_heads} KV head, {w.n_q_heads} query heads, {N} tokens, "
+                       f"{w.decode_steps} decode steps): scoring, allocation, packing and decode, single-threaded")
+
+
 def cpu_baseline(w, hist_tok, hist_chan, n_seg, n_c, sample_segments):
     """The oracle's decode of one step, timed on `sample_segments` segments of
     the same shape (kept-token mix and K-channel mix of the measured
@@ -511,9 +561,9 @@ def cpu_baseline(w, hist_tok, hist_chan, n_seg, n_c, sample_segments):
     else:
         value, unit = per_step_s * 1e6 / w.n_seq, "us/token"
     return dict(value=value, unit=unit, cores=1, kind="oracle",
-                sample=f"{sample_segments} of {n_seg} segments (one KV head of one layer each, {N} tokens, "
-                       f"measured bit mix, seeded K/V), oracle decode step timed single-threaded and scaled "
-                       f"by {n_seg}/{sample_segments}; host has {os.cpu_count()} cpus")
+                sample=f"{sample_segments} sampled segments (one KV head of one layer each, {N} tokens, "
+                       f"measured bit mix, seeded K/V), oracle decode step timed single-threaded; the mean per "
+                       f"segment times the step's {n_seg} segments; host has {os.cpu_count()} cpus")
 
 
 def main():
@@ -708,6 +758,9 @@ def main():
         t0 = time.time()
         result["cpu_baseline_scoring"] = cpu_scoring_baseline(w)
         log(f"cpu scoring baseline {time.time() - t0:.1f}s")
+        t0 = time.time()
+        result["cpu_baseline_tiny_all_stages"] = cpu_baseline_all_stages()
+        log(f"cpu all-stage baseline (tiny workload) {time.time() - t0:.1f}s")
     print(json.dumps(result), flush=True)
 
 
