@@ -18,6 +18,9 @@ rdkv_status check_dims(const rdkv_dims* d) {
   if (d->n_tokens < 1 || d->n_seq < 1 || d->n_layers < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1)
     return RDKV_ERR_SHAPE;
   if (d->n_q_heads % d->n_kv_heads != 0) return RDKV_ERR_SHAPE;
+  // at most kMaxSegments segments, so every size below fits 64 bits
+  const int64_t sl = int64_t(d->n_seq) * d->n_layers;   // < 2^62
+  if (sl > kMaxSegments || sl * d->n_kv_heads > kMaxSegments) return RDKV_ERR_SHAPE;
   if (d->head_dim != kHeadDim) return RDKV_ERR_UNSUPPORTED;
   const int G = d->n_q_heads / d->n_kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8) return RDKV_ERR_UNSUPPORTED;
@@ -41,11 +44,13 @@ rdkv_status check_layout(const rdkv_layout* lay) {
 
 // The layout of one generation blob of a rollover layout: the same format
 // for zone_c_capacity tokens per segment, the generation budgets, no zone C.
+// (Called on layouts that passed check_layout, whose generation layout was
+// built by layout_init; a zeroed layout if it cannot be built.)
 rdkv_layout generation_layout(const rdkv_layout& lay) {
   rdkv_dims d = lay.dims;
   d.n_tokens = lay.zone_c_capacity;
   rdkv_layout g;
-  layout_init(&d, lay.gen_budget_v, lay.gen_budget_k, 0, 0, 0, 0, &g);
+  if (layout_init(&d, lay.gen_budget_v, lay.gen_budget_k, 0, 0, 0, 0, &g) != RDKV_OK) std::memset(&g, 0, sizeof(g));
   return g;
 }
 
@@ -128,7 +133,7 @@ extern "C" {
 
 int32_t rdkv_version(void) { return (kFormatVersion << 16) | 1; }
 
-const char* rdkv_status_string(rdkv_status s) {
+const char* rdkv_status_string(int32_t s) {
   switch (s) {
     case RDKV_OK: return "ok";
     case RDKV_ERR_NULL: return "null pointer";
@@ -196,15 +201,21 @@ rdkv_status layout_init(const rdkv_dims* dims, int64_t budget_v, int64_t budget_
     L.n_generations = n_gen;
     L.gen_budget_v = gen_budget_v;
     L.gen_budget_k = gen_budget_k;
-    const rdkv_layout g = generation_layout(L);
+    rdkv_dims gd = L.dims;
+    gd.n_tokens = cap;
+    rdkv_layout g;
+    st = layout_init(&gd, gen_budget_v, gen_budget_k, 0, 0, 0, 0, &g);
+    if (st != RDKV_OK) return st;
     L.gen_offset = L.cache_bytes;
     L.gen_bytes = align_up(g.cache_bytes, kAlign);
+    if (L.gen_bytes > kMaxCacheBytes / uint64_t(n_gen)) return RDKV_ERR_SHAPE;
     L.cache_bytes = L.gen_offset + uint64_t(n_gen) * L.gen_bytes;
     L.max_chunks = int32_t(tok_chunks + int64_t(n_gen) * g.max_chunks + cdiv(cap, kChunkRowsC));
     L.zc_stats_bytes = uint64_t(L.n_seg) * G * (cap + kHeadDim) * sizeof(float);
     L.rollover_workspace_bytes = rollover_workspace_bytes(L.n_seg, cap);
   }
   L.decode_workspace_bytes = uint64_t(L.n_seg) * L.max_chunks * G * kPartialFloats * sizeof(float);
+  if (L.cache_bytes > kMaxCacheBytes || L.decode_workspace_bytes > kMaxCacheBytes) return RDKV_ERR_SHAPE;
   *out = L;
   return RDKV_OK;
 }

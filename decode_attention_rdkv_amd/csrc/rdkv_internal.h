@@ -15,6 +15,11 @@ namespace rdkv {
 
 constexpr int kHeadDim = 128;
 constexpr int64_t kMaxTokens = int64_t(1) << 19;   // prefill tokens per sequence
+constexpr int64_t kMaxSegments = int64_t(1) << 24;  // sequences x layers x KV heads of one layout
+// A layout (blob, generation blobs or decode workspace) above this many bytes
+// is refused: with the bounds on tokens, segments, zone C and generations no
+// size computation overflows before this test.
+constexpr uint64_t kMaxCacheBytes = uint64_t(1) << 50;
 constexpr uint32_t kMagic = 0x564B4452u;  // "RDKV" little-endian
 constexpr int kFormatVersion = 2;
 constexpr int kHeaderBytes = 256;

@@ -22,7 +22,9 @@
  *   been enqueued and no output has been touched.  Inputs must stay alive
  *   and unmodified until the enqueued work has finished.
  * - Only head_dim == 128 and n_q_heads / n_kv_heads in {1, 2, 4, 8} are
- *   supported (else RDKV_ERR_UNSUPPORTED).
+ *   supported (else RDKV_ERR_UNSUPPORTED).  n_tokens <= 2^19 and
+ *   n_seq * n_layers * n_kv_heads <= 2^24, and a layout whose blob or decode
+ *   workspace would pass 2^50 bytes is refused (else RDKV_ERR_SHAPE).
  * - Segment index: seg = (s * n_layers + l) * n_kv_heads + h.  Query head g
  *   belongs to KV head g / (n_q_heads / n_kv_heads).
  */
@@ -98,8 +100,10 @@ typedef struct rdkv_layout {
 /* Library version (format version in the high 16 bits, build in the low 16). */
 int32_t rdkv_version(void);
 
-/* Human-readable name of a status code (static string). */
-const char* rdkv_status_string(rdkv_status status);
+/* Human-readable name of a status code (static string); any other value,
+ * negative ones included, gives "unknown status".  The argument is a plain
+ * int32_t so that every value a caller may hold is a valid argument. */
+const char* rdkv_status_string(int32_t status);
 
 /* Fill *out for a cache of the given dimensions and budgets.  budget_v and
  * budget_k are bits per segment (the "B" of section 2.1), >= 0; zone_c_capacity
