@@ -354,10 +354,16 @@ template <int G, int SW>
 struct __align__(16) Smem {
   uint32_t qpair[kPairSlots][G];         // fp16 query pairs matching the records' code pairs
   float qsum[4][G];                      // sum of q over the 8-, 4-, 2-bit channel parts
-  uint16_t qperm[G][kHeadDim];           // query with channels in record order
-  uint16_t qnat[G][kHeadDim];            // query as given
   uint8_t perm[kHeadDim];                // record order -> channel
-  uint32_t coefh[kWaves][kTile / 2][kHeadsPerWave<G>];  // fp16 (p*scale) of tile tokens (j, j + 32)
+  // the query copies live only while the tables are built; the tiles' fp16
+  // (p*scale) coefficients of tokens (j, j + 32) take their place after it
+  union {
+    struct {
+      uint16_t qperm[G][kHeadDim];       // query with channels in record order
+      uint16_t qnat[G][kHeadDim];        // query as given
+    };
+    uint32_t coefh[kWaves][kTile / 2][kHeadsPerWave<G>];
+  };
   WaveLds<kHeadsPerWave<G>, SW> wv[kWaves];
   float part_ml[kWaves][kHeadsPerWave<G>][2];
 };
@@ -1298,6 +1304,7 @@ hipError_t launch_chunks_g(const DecodeParams& p, hipStream_t stream) {
   if (words <= 10) return launch_chunks_gs<G, 10>(p, none, stream);
   if (words <= 12) return launch_chunks_gs<G, 12>(p, none, stream);
   if (words <= 16) return launch_chunks_gs<G, 16>(p, none, stream);
+  if (words <= 20) return launch_chunks_gs<G, 20>(p, none, stream);
   if (words <= 24) return launch_chunks_gs<G, 24>(p, none, stream);
   if (words <= kMaxStagedWords) return launch_chunks_gs<G, 32>(p, none, stream);
   return launch_chunks_gs<G, 0>(p, none, stream);

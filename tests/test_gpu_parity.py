@@ -62,6 +62,11 @@ def _bits_case(name, n_seg, N, seed):
         bc[:] = 0
         bc[:, 10:30] = 8
         bc[:, 40:45] = 2
+    elif name == "k20":                      # 19-word record bound: the SW = 20 decode path
+        bc[:] = 0
+        bc[:, 0:40] = 4
+        bc[:, 40:100] = 2
+        bc[:, 100:105] = 8
     elif name == "empty_and_single":
         bt[0] = 0
         if n_seg > 1:
@@ -81,6 +86,7 @@ PACK_CASES = [
     ("odd16", 1, 1, 4, 1, 1500, 3),
     ("empty_and_single", 1, 1, 2, 2, 200, 2),
     ("mid_k", 1, 1, 8, 2, 700, 4),
+    ("k20", 1, 2, 8, 2, 600, 4),
 ]
 
 
