@@ -1,6 +1,6 @@
 """Builds librdkv.so in-tree with hipcc for gfx950.
 
-Usage: python -m decode_attention_rdkv_amd.build   (or __graft_entry__.build()).
+Usage: python -m decode_attention_rdkv_amd.build   (the repository root's build entry point calls it too).
 Each HIP translation unit is compiled to an object under _build/, in parallel,
 then linked into decode_attention_rdkv_amd/librdkv.so.
 """
