@@ -355,13 +355,10 @@ struct __align__(16) Smem {
   uint32_t qpair[kPairSlots][G];         // fp16 query pairs matching the records' code pairs
   float qsum[4][G];                      // sum of q over the 8-, 4-, 2-bit channel parts
   uint8_t perm[kHeadDim];                // record order -> channel
-  // the query copies live only while the tables are built; the tiles' fp16
-  // (p*scale) coefficients of tokens (j, j + 32) take their place after it
+  // the query copy lives only while the tables are built; the tiles' fp16
+  // (p*scale) coefficients of tokens (j, j + 32) take its place after it
   union {
-    struct {
-      uint16_t qperm[G][kHeadDim];       // query with channels in record order
-      uint16_t qnat[G][kHeadDim];        // query as given
-    };
+    uint16_t qnat[G][kHeadDim];          // query as given
     uint32_t coefh[kWaves][kTile / 2][kHeadsPerWave<G>];
   };
   WaveLds<kHeadsPerWave<G>, SW> wv[kWaves];
@@ -382,28 +379,34 @@ __device__ inline void load_qp(const Smem<G, SW>& sm, int slot, int hb, uint32_t
   }
 }
 
-// fp16 query pairs in the order the rows' code pairs come in, and the sum of
-// q over each integer part (for the zero terms).  Zone C uses natural order.
-// The global reads are one channel per thread, all in flight together; the
-// part sums are wave reductions.
+// The segment's G query rows and its channel permutation (at byte offset
+// `desc` + kDescPerm of the cache), copied to LDS as the workgroup starts:
+// these reads need nothing from the descriptor, so they overlap its reads
+// instead of following them.  Word loads (device pointers are 16-byte
+// aligned); build_query_tables reads the copies after a barrier.
 template <int G, int SW>
-__device__ void build_query_tables(const DecodeParams& p, const SegInfo& si, const Plan& pl, int64_t seg,
-                                   Smem<G, SW>& sm) {
+__device__ inline void stage_query(const DecodeParams& p, int64_t seg, uint64_t desc, Smem<G, SW>& sm) {
+  constexpr int kWords = G * kHeadDim / 2;
+  const uint32_t* q32 = reinterpret_cast<const uint32_t*>(p.q) + seg * kWords;
+  uint32_t* qn = reinterpret_cast<uint32_t*>(&sm.qnat[0][0]);
+  for (int i = threadIdx.x; i < kWords; i += kThreads) qn[i] = q32[i];
+  if (threadIdx.x < kHeadDim / 4)
+    reinterpret_cast<uint32_t*>(sm.perm)[threadIdx.x] =
+        reinterpret_cast<const uint32_t*>(p.cache + desc + kDescPerm)[threadIdx.x];
+}
+
+// fp16 query pairs in the order the rows' code pairs come in, and the sum of
+// q over each integer part (for the zero terms), from the copies stage_query
+// made.  Zone C uses natural order.  The part sums are wave reductions.
+template <int G, int SW>
+__device__ void build_query_tables(const SegInfo& si, const Plan& pl, Smem<G, SW>& sm) {
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
-  const uint8_t* perm = p.cache + si.desc + kDescPerm;
   const RecordShape rs = record_shape(si.n_chan[0], si.n_chan[1], si.n_chan[2], si.n_chan[3]);
   const int c8 = si.n_chan[0], c4 = c8 + si.n_chan[1], c2 = c4 + si.n_chan[2], c0 = c2 + si.n_chan[3];
-  const uint16_t* qh = reinterpret_cast<const uint16_t*>(p.q) + seg * G * kHeadDim;
   const bool natural = pl.kind == 4;
-  // q and the permutation are read together (no dependent global read); the
-  // permutation is applied in LDS
-  for (int i = tid; i < G * kHeadDim; i += kThreads) sm.qnat[i / kHeadDim][i % kHeadDim] = qh[i];
-  if (tid < kHeadDim) sm.perm[tid] = natural ? uint8_t(tid) : perm[tid];
-  __syncthreads();
-  for (int i = tid; i < G * kHeadDim; i += kThreads) {
-    const int g = i / kHeadDim, c = i % kHeadDim;
-    sm.qperm[g][c] = sm.qnat[g][sm.perm[c]];
-  }
+  // q_g at record position pos (a permutation entry past the head dimension,
+  // possible only in a damaged descriptor, is wrapped into it)
+  auto qat = [&](int g, int pos) -> uint16_t { return sm.qnat[g][natural ? pos : sm.perm[pos] & (kHeadDim - 1)]; };
   __syncthreads();
   for (int i = tid; i < kPairSlots * G; i += kThreads) {
     const int sl = i / G, g = i % G;
@@ -429,7 +432,7 @@ __device__ void build_query_tables(const DecodeParams& p, const SegInfo& si, con
     // query is stored divided by 2^shift (exact unless it becomes subnormal)
     auto qbits = [&](int pos) -> uint32_t {
       if (pos >= hi_end || pos >= kHeadDim) return 0u;
-      const uint16_t h = sm.qperm[g][pos];
+      const uint16_t h = qat(g, pos);
       if (shift == 0) return h;
       return __half_as_ushort(__float2half_rn(ldexpf(__half2float(__ushort_as_half(h)), -shift)));
     };
@@ -444,7 +447,7 @@ __device__ void build_query_tables(const DecodeParams& p, const SegInfo& si, con
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int c = lane + 64 * h;
-        if (c >= lo && c < hi) v += __half2float(__ushort_as_half(sm.qperm[g][c]));
+        if (c >= lo && c < hi) v += __half2float(__ushort_as_half(qat(g, c)));
       }
       v = wave_reduce<false>(v);
       if (lane == 0) sm.qsum[j][g] = v;
@@ -967,7 +970,7 @@ __device__ void run_group(const DecodeParams& p, const SegInfo& si, const Plan& 
   if constexpr (PIPE) {
     if (n_tiles > 0) load_pairs(va, 0);
   }
-  build_query_tables<G, SW>(p, si, pl, seg, sm);
+  build_query_tables<G, SW>(si, pl, sm);
   __syncthreads();
 
   WaveState<GW> st;
@@ -1051,7 +1054,7 @@ __device__ void run_zone_c(const DecodeParams& p, const SegInfo& si, int64_t seg
 
   constexpr int GW = kHeadsPerWave<G>, kNS = kStreams<G>;
   const int hb = kNS == kWaves ? 0 : (wave / kNS) * GW;           // the wave's first query head
-  build_query_tables<G, SW>(p, si, pl, seg, sm);
+  build_query_tables<G, SW>(si, pl, sm);
   __syncthreads();
   WaveState<GW> st;
   state_init(st);
@@ -1098,14 +1101,20 @@ __device__ void run_zone_c(const DecodeParams& p, const SegInfo& si, int64_t seg
 // ---------------------------------------------------------------- kernels
 
 // out[seg][g][c] = sum_k e^{m_k - M} o_k[c] / sum_k e^{m_k - M} l_k over the
-// segment's chunks, in chunk order; a segment with nothing to attend to gives
-// 0.  One 128-thread workgroup per (segment, query head), thread c owning
-// channel c; per round of up to 128 chunk slots, thread k reads slot k's
-// (m, l) once and publishes its weight in LDS, then every thread sums its
-// channel over the slots.  Every slot up to max_chunks was written by the
-// chunk kernel; slots past the segment's last chunk hold (-inf, 0, 0...), so
-// the merge needs nothing from the blob.
-constexpr int kMergeThreads = kHeadDim;
+// segment's chunks; a segment with nothing to attend to gives 0.  One
+// workgroup of Q * 128 threads per (segment, query head): thread t owns
+// channel t mod 128 and, of each round of up to 32 Q chunk slots, the slots
+// t / 128 + Q j.  A round issues all its reads (the slots' (m, l) in the
+// first waves, 32 slots of its channel per thread) before it uses any, so it
+// costs one memory round trip; Q = 4 when a segment has more than 32 chunk
+// slots (one round up to 128), else 1.  The Q partial sums are added in a
+// fixed order at the end, so the result does not depend on scheduling.
+// Every slot up to max_chunks was written by the chunk kernel; slots past the
+// segment's last chunk hold (-inf, 0, 0...), so the merge needs nothing from
+// the blob.
+constexpr int kMergeLoads = 32;
+template <int Q> constexpr int kMergeThreads = Q * kHeadDim;
+template <int Q> constexpr int kMergeRound = Q * kMergeLoads;
 
 // With kAccum (rdkv_decode_accumulate), the workgroup of (segment, head g)
 // then adds the step's final softmax probability of every zone-C row j < n_c,
@@ -1113,67 +1122,97 @@ constexpr int kMergeThreads = kHeadDim;
 // zone-C key (fp32 products of the fp16 values), to zc_stats[seg][g][j], and
 // q_g[c]^2 to zc_stats[seg][g][cap + c]; one thread per element, so no
 // atomics and a fixed order.
-template <int G, bool kAccum>
-__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParams p) {
-  __shared__ float s_w[kMergeThreads], s_lw[kMergeThreads];
-  __shared__ float s_red[kMergeThreads / 64];
+template <int G, bool kAccum, int Q>
+__global__ __launch_bounds__(kMergeThreads<Q>) void decode_merge_kernel(DecodeParams p) {
+  constexpr int kRound = kMergeRound<Q>, kRoundWaves = (kRound + 63) / 64;
+  __shared__ float s_w[kRound];
+  __shared__ float s_red[2][kRoundWaves];
+  __shared__ float s_o[Q][kHeadDim];
   const int64_t seg = blockIdx.x / G;
   const int g = int(blockIdx.x % G);
-  const int c = threadIdx.x;
+  const int t = threadIdx.x, c = t % kHeadDim, qd = t / kHeadDim;
   const int n = p.max_chunks;
   const float* part = p.partials + int64_t(seg) * n * G * kPartialFloats + g * kPartialFloats;
   const int64_t stride = int64_t(G) * kPartialFloats;
   float M = -INFINITY, L = 0.f, O = 0.f;
-  for (int k0 = 0; k0 < n; k0 += kMergeThreads) {
-    const int kn = min(kMergeThreads, n - k0);
+  for (int k0 = 0; k0 < n; k0 += kRound) {
+    const int kn = min(kRound, n - k0);
     const float* pr = part + k0 * stride;
-    const float mc = c < kn ? pr[c * stride] : -INFINITY;
-    const float lc = c < kn ? pr[c * stride + 1] : 0.f;
-    const float wm = wave_reduce<true>(mc);
-    if ((c & 63) == 0) s_red[c >> 6] = wm;
+    float mc = -INFINITY, lc = 0.f;
+    if (t < kn) {
+      mc = pr[t * stride];
+      lc = pr[t * stride + 1];
+    }
+    float o[kMergeLoads];
+#pragma unroll
+    for (int j = 0; j < kMergeLoads; ++j) {
+      const int k = qd + Q * j;   // (uniform over a wave)
+      o[j] = k < kn ? pr[k * stride + 4 + c] : 0.f;
+    }
+    // the round's largest m (the first kRoundWaves waves hold its slots)
+    if (t < 64 * kRoundWaves) {
+      const float wm = wave_reduce<true>(mc);
+      if ((t & 63) == 0) s_red[0][t >> 6] = wm;
+    }
     __syncthreads();
-    const float mb = fmaxf(M, fmaxf(s_red[0], s_red[1]));
-    const float w = mc == -INFINITY ? 0.f : exp2f(mc - mb);
-    s_w[c] = w;
-    s_lw[c] = lc * w;
+    float mb = M;
+#pragma unroll
+    for (int i = 0; i < kRoundWaves; ++i) mb = fmaxf(mb, s_red[0][i]);
+    if (t < 64 * kRoundWaves) {
+      const float w = mc == -INFINITY ? 0.f : exp2f(mc - mb);
+      if (t < kRound) s_w[t] = w;
+      const float lw = wave_reduce<false>(lc * w);
+      if ((t & 63) == 0) s_red[1][t >> 6] = lw;
+    }
     __syncthreads();
     if (mb != -INFINITY) {
       const float a = exp2f(M - mb);   // (0 while nothing was merged)
-      L *= a;
+      float lsum = 0.f;
+#pragma unroll
+      for (int i = 0; i < kRoundWaves; ++i) lsum += s_red[1][i];
+      L = fmaf(L, a, lsum);
       O *= a;
-#pragma unroll 8
-      for (int j = 0; j < kn; ++j) {
-        L += s_lw[j];
-        O = fmaf(pr[j * stride + 4 + c], s_w[j], O);
-      }
+#pragma unroll
+      for (int j = 0; j < kMergeLoads; ++j) O = fmaf(o[j], s_w[qd + Q * j], O);
       M = mb;
     }
     __syncthreads();
   }
-  p.out[(seg * G + g) * kHeadDim + c] = L > 0.f ? O / L : 0.f;
+  s_o[qd][c] = O;
+  __syncthreads();
+  if (t < kHeadDim) {
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < Q; ++i) sum += s_o[i][c];
+    p.out[(seg * G + g) * kHeadDim + c] = L > 0.f ? sum / L : 0.f;
+  }
   if constexpr (kAccum) {
     float* st = p.zc_stats + (seg * G + g) * int64_t(p.zc_cap + kHeadDim);
-    const float qc = __half2float(p.q[(seg * G + g) * kHeadDim + c]);
-    st[p.zc_cap + c] += qc * qc;
-    s_w[c] = qc;                   // free since the last barrier of the loop
+    float* s_q = s_o[0];           // free once every thread has read its sums
+    __syncthreads();
+    if (t < kHeadDim) {
+      const float qc = __half2float(p.q[(seg * G + g) * kHeadDim + c]);
+      st[p.zc_cap + c] += qc * qc;
+      s_q[c] = qc;
+    }
     __syncthreads();
     const uint8_t* d = p.cache + kHeaderBytes + uint64_t(seg) * kDescBytes;
     const uint64_t off_kc = *reinterpret_cast<const uint64_t*>(d + kDescOffKc);
     if (L > 0.f && off_kc + uint64_t(p.n_c) * kHeadDim * 2 <= p.main_bytes) {
-      for (int j = c; j < p.n_c; j += kMergeThreads) {
+      for (int j = t; j < p.n_c; j += kMergeThreads<Q>) {
         const uint4* kr = reinterpret_cast<const uint4*>(p.cache + off_kc + uint64_t(j) * kHeadDim * 2);
-        float t = 0.f;
+        float tj = 0.f;
 #pragma unroll 4
         for (int i = 0; i < kHeadDim / 8; ++i) {
           const uint4 x = kr[i];
           const uint32_t w4[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            t = fmaf(s_w[8 * i + 2 * e], half_lo(w4[e]), t);
-            t = fmaf(s_w[8 * i + 2 * e + 1], half_hi(w4[e]), t);
+            tj = fmaf(s_q[8 * i + 2 * e], half_lo(w4[e]), tj);
+            tj = fmaf(s_q[8 * i + 2 * e + 1], half_hi(w4[e]), tj);
           }
         }
-        st[j] += exp2f(t * kLog2eOverSqrtD - M) / L;
+        st[j] += exp2f(tj * kLog2eOverSqrtD - M) / L;
       }
     }
   }
@@ -1203,6 +1242,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   if constexpr (kPaged) c_len = lens.c_len[seg / p.seg_per_seq];
   // slot k: the prefill tokens' chunks, the generations' chunks, zone C
   const int gen_end = p.token_slots + p.n_gen * p.gen_slots;
+  {
+    // the descriptor this slot reads: the prefill blob's, or a generation blob's
+    uint64_t desc = kHeaderBytes + uint64_t(seg) * kDescBytes;
+    if (!kPaged && k >= p.token_slots && k < gen_end) desc += gen_blob(p, (k - p.token_slots) / p.gen_slots).base;
+    stage_query(p, seg, desc, sm);
+  }
   SegInfo si;
   Plan pl;
   if constexpr (kPaged) {
@@ -1322,14 +1367,21 @@ hipError_t launch_chunks_paged_g(const DecodeParams& p, const PagedSeqLens& lens
   return launch_chunks_gs<G, 0>(p, lens, stream);
 }
 
+template <int G, int Q>
+hipError_t launch_merge_gq(const DecodeParams& p, hipStream_t stream) {
+  if (p.zc_stats)
+    hipLaunchKernelGGL((decode_merge_kernel<G, true, Q>), dim3(unsigned(p.n_seg * G)), dim3(kMergeThreads<Q>), 0,
+                       stream, p);
+  else
+    hipLaunchKernelGGL((decode_merge_kernel<G, false, Q>), dim3(unsigned(p.n_seg * G)), dim3(kMergeThreads<Q>), 0,
+                       stream, p);
+  return hipGetLastError();
+}
+
 template <int G>
 hipError_t launch_merge_g(const DecodeParams& p, hipStream_t stream) {
   if (p.n_seg == 0) return hipSuccess;
-  if (p.zc_stats)
-    hipLaunchKernelGGL((decode_merge_kernel<G, true>), dim3(unsigned(p.n_seg * G)), dim3(kMergeThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL((decode_merge_kernel<G, false>), dim3(unsigned(p.n_seg * G)), dim3(kMergeThreads), 0, stream, p);
-  return hipGetLastError();
+  return p.max_chunks > kMergeRound<1> ? launch_merge_gq<G, 4>(p, stream) : launch_merge_gq<G, 1>(p, stream);
 }
 
 }  // namespace
