@@ -251,6 +251,34 @@ def test_decode_split_k_chunks_and_long_rows(gpu_lib):
     _decode_run(rdkv, lay, ol, cache, oblob, 3, 5)
 
 
+@pytest.mark.parametrize("n16,slots", [(1500, (1, 32)), (6000, (33, 128)), (12000, (129, 256))])
+def test_decode_merge_over_many_chunk_slots(gpu_lib, n16, slots):
+    """One segment whose fp16 group alone fills dozens to hundreds of 64-row
+    chunks: the merge's narrow form (up to 32 chunk slots), its wide form in
+    one round (33..128) and over two rounds (more than 128), each against the
+    oracle."""
+    rdkv = gpu_lib
+    N = n16 + 1000
+    r = np.random.default_rng(n16)
+    bt = np.zeros((1, N), np.uint8)
+    bt[0, r.permutation(N)[:n16]] = 16
+    bt[0, bt[0] == 0] = 2
+    bc = np.zeros((1, 128), np.uint8)
+    bc[0, :24], bc[0, 24:40] = 4, 8
+    K, V = synth.random_kv(1, N, n16 + 1)
+    bv, bk = int(bt.sum()), int(bc.sum())
+    lay = rdkv.layout(rdkv.make_dims(1, 1, 4, 1, N), bv, bk, 70)
+    assert slots[0] <= lay.max_chunks <= slots[1]
+    ol = O.Layout(1, 1, 4, 1, 128, N, bv, bk, 70)
+    shp = (1, 1, 1)
+    Ks, Vs, bts, bcs = K.reshape(shp + (N, 128)), V.reshape(shp + (N, 128)), bt.reshape(shp + (N,)), bc.reshape(shp + (128,))
+    oblob = O.pack_cache(ol, Ks, Vs, bts, bcs)
+    cache = rdkv.cache_init(lay)
+    rdkv.pack(lay, cache, dev(Ks), dev(Vs), dev(bts), dev(bcs))
+    assert np.array_equal(host(cache), oblob)
+    _decode_run(rdkv, lay, ol, cache, oblob, 3, n16)
+
+
 @pytest.mark.parametrize("G", [1, 4, 8])
 def test_zone_c_grows_to_300_rows(gpu_lib, G):
     """Zone C (fp16 rows of new tokens, RDKV summary section 2.3) appended row
