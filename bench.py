@@ -318,6 +318,17 @@ def chunk_stats(chunk_tok2, token_slots, desc):
             "per_segment_max": int(n.max()), "per_segment_mean": round(float(n.mean()), 2)}
 
 
+def record_stats(rec_max, desc):
+    """K-record words per segment (zone-A records): the layout's bound against
+    what the segments hold; decode takes records of up to 20 words through its
+    three-workgroups-per-CU ring and a longer bound's ring in a second launch."""
+    words = desc["rec"][desc["n_kept"] > 0] // 4
+    if words.size == 0:
+        return {"bound": int(rec_max // 4)}
+    return {"bound": int(rec_max // 4), "max": int(words.max()), "median": float(np.median(words)),
+            "segments_over_20": int((words > 20).sum()), "segments": int(words.size)}
+
+
 def build_paged(rdkv, torch, w, K, V, bt, bc, budget_v, budget_k, seed=0):
     """Every sequence of K, V, bt, bc ([S][L][Hkv]...) staged, given pages
     from a host free list in shuffled order (no segment's pages contiguous)
@@ -406,6 +417,7 @@ def extras(rdkv, torch, w, lay, cache, kept, q, kn, vn, ref_out, steps, warmup, 
         "contiguous_blob_bytes_per_segment_budgets": int(lay.cache_bytes),
         "resident_vs_per_segment_blob": round((pl.pool_offset + used * rdkv.PAGE_BYTES) / lay.cache_bytes, 4),
         "chunks": chunk_stats(pl.chunk_tok2, pl.token_slots, rdkv.descriptors(lay, pc)),
+        "record_words": record_stats(pl.rec_max, rdkv.descriptors(lay, pc)),
         "note": "rdkv_allocate_shared with one budget per layer (its KV heads' budgets pooled), packed on pages: "
                 "memory follows what each segment keeps instead of a slot sized for the whole layer's budget"}
     log(f"shared budget on pages: {t * 1e3:.1f} us per step, {used} pages")

@@ -186,3 +186,44 @@ def test_paged_decode_equals_contiguous_decode(rdkv):
         a = rdkv.decode(lay, flat, step, q, kn, vn)
         b = rdkv.paged_decode(pl, paged, [step] * S, q, kn, vn)
         assert torch.equal(a, b), f"step {step}"
+
+
+def test_paged_decode_mixed_record_lengths(rdkv):
+    """A paged layout whose record bound passes 20 words: a sequence with
+    5-word K records and one with 27-word records on shuffled pages of one
+    pool, decoded through the 32-word ring, against the oracle."""
+    S, L, Hkv, G, N, cap, n_pages = 2, 1, 2, 4, 1800, 40, 300
+    Hq = G * Hkv
+    bv, bk = 8000, 800
+    pl = rdkv.paged_layout(rdkv.make_dims(S, L, Hq, Hkv, N), bv, bk, cap, n_pages)
+    assert pl.rec_max // 4 > 20
+    op = O.PagedLayout(S, L, Hq, Hkv, N, bv, bk, cap, n_pages)
+    cache = rdkv.paged_cache_init(pl)
+    oblob = O.paged_empty(op)
+    pool = Pool(n_pages, 3)
+    r = np.random.default_rng(11)
+    for s, (n8, n4) in enumerate([(0, 24), (100, 0)]):
+        K, V = synth.random_kv(L * Hkv, N, 40 + s)
+        bt = r.choice(np.array([0, 2, 4, 8, 16], np.uint8), size=(L * Hkv, N), p=[0.5, 0.2, 0.15, 0.1, 0.05])
+        while int(bt.astype(np.int64).sum(axis=1).max()) > bv:
+            bt[:, r.integers(N)] = 0
+        bc = np.zeros((L * Hkv, 128), np.uint8)
+        for h in range(L * Hkv):
+            ch = r.permutation(128)
+            bc[h, ch[:n8]] = 8
+            bc[h, ch[n8:n8 + n4]] = 4
+        seq = (K.reshape(L, Hkv, N, 128), V.reshape(L, Hkv, N, 128), bt.reshape(L, Hkv, N), bc.reshape(L, Hkv, 128))
+        _add(rdkv, pl, cache, oblob, op, pool, s, (N, bv, bk), seq)
+    _same_bytes(cache, oblob, "after commits")
+    ws = rdkv.paged_decode_workspace(pl)
+    c_len = [0, 0]
+    for step in range(4):
+        q = r.standard_normal((S, L, Hq, 128)).astype(np.float16)
+        kn = r.standard_normal((S, L, Hkv, 128)).astype(np.float16)
+        vn = r.standard_normal((S, L, Hkv, 128)).astype(np.float16)
+        out = rdkv.paged_decode(pl, cache, c_len, dev(q), dev(kn), dev(vn), workspace=ws)
+        ref = O.paged_decode_step(oblob, op, q, c_len, kn, vn)
+        e = rel_err(host(out), ref)
+        assert e <= TOL, f"step {step}: rel err {e:.3g}"
+        c_len = [c + 1 for c in c_len]
+    _same_bytes(cache, oblob, "after decode steps")

@@ -279,6 +279,37 @@ def test_decode_merge_over_many_chunk_slots(gpu_lib, n16, slots):
     _decode_run(rdkv, lay, ol, cache, oblob, 3, n16)
 
 
+@pytest.mark.parametrize("G,bk", [(4, 800), (4, 1100), (8, 800), (1, 1100)])
+def test_decode_mixed_record_lengths(gpu_lib, G, bk):
+    """Segments with K records of 5, 20, 21 and 27 words in one layout whose
+    record bound passes 20 words: decoded through the ring of the bound (32
+    words at bk = 800) or with no ring (bk = 1100) while zone C grows, every
+    segment against the oracle."""
+    rdkv = gpu_lib
+    Hkv, N, cap = 4, 3000, 8
+    r = np.random.default_rng(bk + G)
+    bt = r.choice(np.array([0, 2, 4, 8, 16], np.uint8), size=(Hkv, N), p=[0.5, 0.2, 0.15, 0.1, 0.05])
+    bc = np.zeros((Hkv, 128), np.uint8)
+    for h, (n8, n4) in enumerate([(0, 24), (72, 0), (76, 0), (100, 0)]):   # 5, 20, 21, 27 words
+        ch = r.permutation(128)
+        bc[h, ch[:n8]] = 8
+        bc[h, ch[n8:n8 + n4]] = 4
+    K, V = synth.random_kv(Hkv, N, bk + G + 1)
+    bv = int(bt.astype(np.int64).sum(axis=1).max())
+    lay = rdkv.layout(rdkv.make_dims(1, 1, G * Hkv, Hkv, N), bv, bk, cap)
+    assert lay.rec_max // 4 > 20
+    ol = O.Layout(1, 1, G * Hkv, Hkv, 128, N, bv, bk, cap)
+    shp = (1, 1, Hkv)
+    Ks, Vs, bts, bcs = K.reshape(shp + (N, 128)), V.reshape(shp + (N, 128)), bt.reshape(shp + (N,)), bc.reshape(shp + (128,))
+    oblob = O.pack_cache(ol, Ks, Vs, bts, bcs)
+    cache = rdkv.cache_init(lay)
+    rdkv.pack(lay, cache, dev(Ks), dev(Vs), dev(bts), dev(bcs))
+    assert np.array_equal(host(cache), oblob)
+    assert sorted(rdkv.descriptors(lay, cache)["rec"] // 4) == [5, 20, 21, 27]
+    _decode_run(rdkv, lay, ol, cache, oblob, 4, bk)
+    assert np.array_equal(host(cache), oblob)
+
+
 @pytest.mark.parametrize("G", [1, 4, 8])
 def test_zone_c_grows_to_300_rows(gpu_lib, G):
     """Zone C (fp16 rows of new tokens, RDKV summary section 2.3) appended row
