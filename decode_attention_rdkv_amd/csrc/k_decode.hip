@@ -177,7 +177,7 @@ __device__ inline SegInfo load_segment(const DecodeParams& p, const BlobRef& b, 
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int T = chunk_tokens(b.chunk_tok2, i);
-    n_chunks += (max(s.n_tok[i], 0) + T - 1) / T;
+    n_chunks += (max(s.n_tok[i], 0) + T - 1) >> chunk_shift(b.chunk_tok2, i);
   }
   ok = ok && n_chunks <= b.token_slots;
   if (!ok) {
@@ -255,7 +255,7 @@ __device__ inline SegInfo load_segment_paged(const DecodeParams& p, int64_t seg,
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int T = chunk_tokens(p.chunk_tok2, i);
-    n_chunks += (max(s.n_tok[i], 0) + T - 1) / T;
+    n_chunks += (max(s.n_tok[i], 0) + T - 1) >> chunk_shift(p.chunk_tok2, i);
   }
   ok = ok && n_chunks <= p.token_slots;
   if (!ok) {
@@ -294,7 +294,7 @@ __device__ inline Plan plan_tokens(const SegInfo& si, int chunk_tok2, int k) {
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const int T = chunk_tokens(chunk_tok2, g);
-    const int nch = (si.n_tok[g] + T - 1) / T;
+    const int nch = (si.n_tok[g] + T - 1) >> chunk_shift(chunk_tok2, g);
     if (pl.kind < 0) {
       if (k < nch) {
         pl.kind = g;
@@ -1234,8 +1234,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   // chunks last, so the dispatcher's in-order fill ends on light work; and
   // with n_seg a multiple of 8 all chunks of a segment land on one XCD (whose
   // L2 then holds the segment's descriptor and query).
-  const int64_t seg = blockIdx.x % p.n_seg;
-  const int k = int(blockIdx.x / p.n_seg);
+  // (n_seg < 2^24: 32-bit division)
+  const uint32_t n_seg = uint32_t(p.n_seg);
+  const int64_t seg = blockIdx.x % n_seg;
+  const int k = int(blockIdx.x / n_seg);
   // this step's zone C: rows before it and whether it appends one
   int c_len = p.c_len;
   bool append = p.append != 0;

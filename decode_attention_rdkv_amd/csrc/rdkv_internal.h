@@ -57,6 +57,9 @@ constexpr int kChunkTok2Min = RDKV_CHUNK_TOK2_MIN;
 #endif
 constexpr int kChunkTok2Max = RDKV_CHUNK_TOK2_MAX;
 __host__ __device__ constexpr int chunk_tokens(int chunk_tok2, int group) { return chunk_tok2 >> group; }
+// log2 of chunk_tokens (chunk_tok2 is a power of two): chunk counts and
+// indices by shifts rather than divisions.
+__host__ __device__ inline int chunk_shift(int chunk_tok2, int group) { return __builtin_ctz(uint32_t(chunk_tok2)) - group; }
 constexpr int kChunkRowsC = 256;
 // Floats per (chunk, query head) partial: m, l, 2 pad, o[128].
 constexpr int kPartialFloats = 4 + kHeadDim;
