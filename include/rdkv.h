@@ -318,7 +318,7 @@ rdkv_status rdkv_decode_static(const rdkv_layout* layout, void* cache, size_t ca
  * (running max m, sum l, unnormalised o[128] per query head and chunk) into
  * `workspace`; arguments as rdkv_decode.
  * rdkv_decode_merge: out = sum_k e^{m_k-M} o_k / sum_k e^{m_k-M} l_k over each
- * segment's chunks, in chunk order.  The partials phase writes every chunk
+ * segment's chunks, in a fixed order.  The partials phase writes every chunk
  * slot of the workspace (slots past a segment's last chunk are marked empty),
  * so the merge needs nothing else from the blob.  zone_c_rows is the number of
  * zone-C rows the partials phase attended (its c_len, plus 1 if it appended);
