@@ -219,6 +219,28 @@ def time_decode(rdkv, torch, lay, cache, q, kn, vn, steps, warmup, flush, grow=F
                 mean_zone_c_rows=mean_rows, total_ms=float(total.sum()))
 
 
+def settle_decode(rdkv, torch, lay, cache, q, kn, vn, seconds, flush, grow=False):
+    """Untimed decode steps (the timed loop's steps, cache clearing included)
+    for about `seconds` of wall time; returns how many ran."""
+    if seconds <= 0:
+        return 0
+    ws = rdkv.decode_workspace(lay)
+    out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    fbuf = torch.ones(1 << 27, dtype=torch.int64, device="cuda") if flush else None
+    cap = max(lay.zone_c_capacity, 1)
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            row = n % cap if grow else 0
+            rdkv.decode(lay, cache, row, q, kn, vn, workspace=ws, out=out)
+            if fbuf is not None:
+                fbuf.sum()
+            n += 1
+        torch.cuda.synchronize()
+    del fbuf
+    return n
+
+
 def time_layer_graph(rdkv, torch, lay1, caches, q, kn, vn, steps, warmup, flush, ref):
     """The same decode step issued the way a model's layer loop issues it: one
     rdkv_decode (chunk + merge kernel) per layer on that layer's own blob, the
@@ -619,6 +641,9 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the paged-zone, shared-budget and rollover measurements (on by default when the "
                          "workload's fp16 K/V fits in 40 GB)")
+    ap.add_argument("--settle-s", type=float, default=0.3,
+                    help="untimed decode steps for this many seconds right before the headline's warmup "
+                         "(the part's clocks settle under sustained decode work)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run one plain 384 MiB device-to-device copy (for counter calibration)")
     args = ap.parse_args()
@@ -677,7 +702,12 @@ def main():
     st.pop("kept", None)
     torch.cuda.empty_cache()
 
-    # the headline: W warmup steps, then exactly K timed steps
+    # The headline: W warmup steps, then exactly K timed steps, after the
+    # other measurements and an untimed settling run of the same steps (the
+    # frees and host work just above can leave the part idle long enough for
+    # its clocks to drop, and they take a few hundred milliseconds of
+    # sustained decode work to come back).
+    settle = settle_decode(rdkv, torch, lay, cache, q, kn, vn, args.settle_s, not args.no_flush, grow=grow)
     tm = time_decode(rdkv, torch, lay, cache, q, kn, vn, args.steps, args.warmup, not args.no_flush, grow=grow)
     warm = None
     if not args.no_flush and lay.cache_bytes < (200 << 20):
@@ -785,6 +815,7 @@ def main():
                        "note": "per-segment budgets, and one budget shared by the layer's KV heads"}},
         "wall_s_timed_loop": round(wall, 4),
         "inputs_sha256": inputs_digest(torch, q, kn, vn, cache, lay),
+        "settle_steps_before_headline": settle,
         "right_after_setup": {"ms_per_step": round(tm0["step"], 5), "kernel_ms": round(tm0["chunk"], 5),
                               "note": "the same K steps timed right after the cache is built, before the other "
                                       "measurements; the headline is timed after them, in the clocks' steady "

@@ -75,6 +75,87 @@ __device__ double find_lambda(float cmax, int64_t budget, CostFn cost_of) {
   return __longlong_as_double(hi);
 }
 
+// The same lambda* found by radix selection instead of bisection, for
+// problems of many units.  The total bits at lambda is W(> lambda), the
+// weighted count (weights 2, 2, 4, 8) of the products p = c_u * k_j above it,
+// and lambda* is the product p* with W(> p*) <= budget < W(>= p*).  Non-negative
+// doubles order as their bit patterns, so p* is fixed one digit of its pattern
+// at a time, top down: a weighted histogram of the digit over the products
+// that match the digits fixed so far, then the digit where the count from
+// above crosses the budget.  The first digit is the whole exponent (products
+// then spread over many buckets, so the LDS atomics seldom collide), then
+// 8-bit digits of the mantissa: 8 passes over the units instead of up to 63.
+// cost0 is the total at lambda = 0 (every product of a positive cost).
+constexpr int kSelBuckets = 2048;
+constexpr int kUnitBatch = 4;   // units a thread loads together
+template <typename CostAt>
+__device__ double select_lambda(int64_t n, int64_t budget, int64_t cost0, CostAt cost_at,
+                                unsigned long long* s_hist, unsigned long long* s_state) {
+  if (cost0 <= budget) return 0.0;
+  const unsigned long long B = (unsigned long long)budget;
+  if (threadIdx.x == 0) s_state[0] = 0, s_state[1] = 0;   // weight above the prefix, prefix
+  // digits: bits 52-63 (sign and exponent), then 44-51, ..., 4-11, then 0-3
+#pragma unroll 1
+  for (int pass = 0; pass < 8; ++pass) {
+    const int width = pass == 0 ? 12 : pass == 7 ? 4 : 8;
+    const int shift = pass == 0 ? 52 : pass == 7 ? 0 : 52 - 8 * pass;
+    const int nb = 1 << width;
+    for (int i = threadIdx.x; i < nb; i += kThreads) s_hist[i] = 0;
+    __syncthreads();
+    const unsigned long long prefix = s_state[1];
+    const unsigned long long fixed = pass == 0 ? 0ull : ~0ull << (shift + width);
+    const unsigned long long dmask = (unsigned long long)(nb - 1);
+    for (int64_t t0 = threadIdx.x; t0 < n; t0 += int64_t(kThreads) * kUnitBatch) {
+      float c[kUnitBatch];
+#pragma unroll
+      for (int u = 0; u < kUnitBatch; ++u) {
+        const int64_t t = t0 + int64_t(u) * kThreads;
+        c[u] = t < n ? cost_at(t) : 0.0f;   // (a zero cost has no positive product: never counted)
+      }
+#pragma unroll
+      for (int u = 0; u < kUnitBatch; ++u) {
+        if (!(c[u] > 0.0f)) continue;
+        const double cd = double(c[u]);
+        const double pj[4] = {cd * 0.375, cd * 0.09375, cd * (15.0 / 1024.0), cd * (255.0 / 524288.0)};
+        const unsigned wj[4] = {2, 2, 4, 8};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const unsigned long long pat = __double_as_longlong(pj[j]);
+          if ((pat & fixed) == (prefix & fixed)) atomicAdd(&s_hist[(pat >> shift) & dmask], (unsigned long long)wj[j]);
+        }
+      }
+    }
+    __syncthreads();
+    // wave 0: lane L sums buckets [L C, L C + C); the lane where the weight
+    // from above crosses the budget scans its buckets top down
+    if (threadIdx.x < 64) {
+      const int L = threadIdx.x, C = nb >= 64 ? nb / 64 : 1;
+      unsigned long long sl = 0;
+      if (L * C < nb)
+        for (int i = 0; i < C; ++i) sl += s_hist[L * C + i];
+      unsigned long long incl = sl;   // weight of lanes >= L
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const unsigned long long o = __shfl_down(incl, off);
+        if (L + off < 64) incl += o;
+      }
+      const unsigned long long above = s_state[0], strictly = above + (incl - sl);
+      if (strictly <= B && above + incl > B) {   // exactly one lane (weights are non-negative)
+        unsigned long long acc = strictly;
+        int d = L * C + C - 1;
+        for (; d > L * C; --d) {
+          if (acc + s_hist[d] > B) break;
+          acc += s_hist[d];
+        }
+        s_state[0] = acc;
+        s_state[1] = prefix | ((unsigned long long)d << shift);
+      }
+    }
+    __syncthreads();
+  }
+  return __longlong_as_double(s_state[1]);
+}
+
 struct AllocVArgs {
   int64_t N;
   int32_t group;       // consecutive segments sharing the budget
@@ -89,23 +170,17 @@ struct AllocVArgs {
 // (A thread's bit count stays far below 2^31; the block total is 64-bit.)
 __global__ __launch_bounds__(kThreads) void alloc_v_kernel(AllocVArgs a) {
   __shared__ int64_t s_i[kWaves];
-  __shared__ float s_f[kWaves];
+  __shared__ unsigned long long s_hist[kSelBuckets], s_state[2];
   const int64_t n = a.N * a.group;
   const int64_t base = int64_t(blockIdx.x) * n;
   const float* w = a.w_tok + base;
   const float* v = a.var_tok + base;
-  float cmax = 0.0f;
-  for (int64_t t = threadIdx.x; t < n; t += kThreads) {
-    const float c = __fmul_rn(w[t], v[t]);
-    if (c > cmax) cmax = c;
-  }
-  cmax = block_max(cmax, s_f);
-  auto cost = [&](double lam) {
-    int k = 0;
-    for (int64_t t = threadIdx.x; t < n; t += kThreads) k += unit_bits(__fmul_rn(w[t], v[t]), lam);
-    return block_sum64(k, s_i);
-  };
-  const double lam = find_lambda(cmax, a.budget, cost);
+  int k0 = 0;   // bits at lambda = 0: 16 per unit of positive cost
+#pragma unroll 4
+  for (int64_t t = threadIdx.x; t < n; t += kThreads) k0 += __fmul_rn(w[t], v[t]) > 0.0f ? 16 : 0;
+  const int64_t cost0 = block_sum64(k0, s_i);
+  const double lam = select_lambda(n, a.budget, cost0, [&](int64_t t) { return __fmul_rn(w[t], v[t]); }, s_hist,
+                                   s_state);
   for (int64_t t = threadIdx.x; t < n; t += kThreads) a.bits_tok[base + t] = uint8_t(unit_bits(__fmul_rn(w[t], v[t]), lam));
   for (int s = threadIdx.x; s < a.group; s += kThreads) a.lambda[2 * (int64_t(blockIdx.x) * a.group + s)] = lam;
 }
