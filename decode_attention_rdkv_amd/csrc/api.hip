@@ -311,21 +311,30 @@ rdkv_status rdkv_score_from_lse(const rdkv_dims* dims, const void* Q, const void
   return hip_status(launch_score_from_lse(p, stream));
 }
 
+size_t rdkv_allocate_workspace_bytes(const rdkv_dims* dims, int32_t group) {
+  if (check_dims(dims) != RDKV_OK) return 0;
+  const int64_t n_seg = int64_t(dims->n_seq) * dims->n_layers * dims->n_kv_heads;
+  if (group < 1 || n_seg % group != 0) return 0;
+  return size_t(alloc_plan(n_seg, dims->n_tokens, group).total);
+}
+
 rdkv_status rdkv_allocate_shared(const rdkv_dims* dims, const float* w_tok, const float* var_tok,
                                  const float* w_chan, const void* K, int64_t budget_v, int64_t budget_k,
                                  int32_t group, uint8_t* bits_tok, uint8_t* bits_chan, float* var_chan,
-                                 double* lambda, hipStream_t stream) {
+                                 double* lambda, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   rdkv_status st = check_dims(dims);
   if (st != RDKV_OK) return st;
-  if (!w_tok || !var_tok || !w_chan || !K || !bits_tok || !bits_chan || !var_chan || !lambda)
-    return RDKV_ERR_NULL;
+  if (!w_tok || !var_tok || !w_chan || !K || !bits_tok || !bits_chan || !var_chan || !lambda) return RDKV_ERR_NULL;
   for (const void* p : {(const void*)w_tok, (const void*)var_tok, (const void*)w_chan, K, (const void*)bits_tok,
-                        (const void*)bits_chan, (const void*)var_chan, (const void*)lambda})
+                        (const void*)bits_chan, (const void*)var_chan, (const void*)lambda, (const void*)workspace})
     if (!aligned16(p)) return RDKV_ERR_ALIGN;
   if (budget_v < 0 || budget_k < 0) return RDKV_ERR_BUDGET;
   AllocParams p;
   p.n_seg = int64_t(dims->n_seq) * dims->n_layers * dims->n_kv_heads;
   if (group < 1 || p.n_seg % group != 0) return RDKV_ERR_SHAPE;
+  const uint64_t need = alloc_plan(p.n_seg, dims->n_tokens, group).total;
+  if (need > 0 && !workspace) return RDKV_ERR_NULL;
+  if (workspace_bytes < need) return RDKV_ERR_WORKSPACE;
   p.group = group;
   p.n_tokens = dims->n_tokens;
   p.w_tok = w_tok;
@@ -338,15 +347,16 @@ rdkv_status rdkv_allocate_shared(const rdkv_dims* dims, const float* w_tok, cons
   p.bits_chan = bits_chan;
   p.var_chan = var_chan;
   p.lambda = lambda;
+  p.workspace = static_cast<uint8_t*>(workspace);
   return hip_status(launch_allocate(p, stream));
 }
 
 rdkv_status rdkv_allocate(const rdkv_dims* dims, const float* w_tok, const float* var_tok,
                           const float* w_chan, const void* K, int64_t budget_v, int64_t budget_k,
                           uint8_t* bits_tok, uint8_t* bits_chan, float* var_chan, double* lambda,
-                          hipStream_t stream) {
+                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return rdkv_allocate_shared(dims, w_tok, var_tok, w_chan, K, budget_v, budget_k, 1, bits_tok, bits_chan, var_chan,
-                              lambda, stream);
+                              lambda, workspace, workspace_bytes, stream);
 }
 
 rdkv_status rdkv_cache_init(const rdkv_layout* layout, void* cache, size_t cache_bytes, hipStream_t stream) {

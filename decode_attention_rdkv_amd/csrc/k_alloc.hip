@@ -9,8 +9,8 @@
 // argmin of c 2^-b + lambda b with ties at the lower bitwidth.  lambda* is the
 // smallest value whose total bits fit the budget.  The total is a step
 // function of lambda that only changes at the products c_u * k_j, which are
-// exact in fp64, so a bisection over the ordered bit patterns of non-negative
-// doubles (at most 63 halvings) lands exactly on lambda*.
+// exact in fp64, so a radix selection over the ordered bit patterns of
+// non-negative doubles lands exactly on lambda*.
 //
 // A budget may be shared by a group of consecutive segments (the heads of a
 // layer, or all of a sequence): the group's units then form one problem with
@@ -24,33 +24,6 @@
 namespace rdkv {
 namespace {
 
-constexpr int kThreads = 1024;
-constexpr int kWaves = kThreads / 64;
-
-__device__ inline int64_t block_sum64(int v, int64_t* s_red) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  v = wave_sum_i(v);
-  __syncthreads();
-  if (lane == 0) s_red[wave] = v;
-  __syncthreads();
-  int64_t t = 0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) t += s_red[w];
-  return t;
-}
-
-__device__ inline float block_max(float v, float* s_red) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  v = wave_max(v);
-  __syncthreads();
-  if (lane == 0) s_red[wave] = v;
-  __syncthreads();
-  float t = s_red[0];
-#pragma unroll
-  for (int w = 1; w < kWaves; ++w) t = fmaxf(t, s_red[w]);
-  return t;
-}
-
 // Bits of one unit for a multiplier lambda: sum of the steps with c*k_j > lambda.
 __device__ inline int unit_bits(float c, double lam) {
   const double cd = double(c);
@@ -58,131 +31,214 @@ __device__ inline int unit_bits(float c, double lam) {
          8 * (cd * (255.0 / 524288.0) > lam);
 }
 
-// lambda* for the units this thread sees through `cost_of`, shared by the block.
-template <typename CostFn>
-__device__ double find_lambda(float cmax, int64_t budget, CostFn cost_of) {
-  if (cost_of(0.0) <= budget) return 0.0;
-  // invariant: cost(pattern lo) > budget >= cost(pattern hi)
-  uint64_t lo = 0;
-  uint64_t hi = __double_as_longlong(double(cmax) * 0.375);
-  while (hi - lo > 1) {
-    const uint64_t mid = lo + (hi - lo) / 2;
-    if (cost_of(__longlong_as_double(mid)) <= budget)
-      hi = mid;
-    else
-      lo = mid;
-  }
-  return __longlong_as_double(hi);
-}
-
-// The same lambda* found by radix selection instead of bisection, for
-// problems of many units.  The total bits at lambda is W(> lambda), the
+// lambda* by radix selection.  The total bits at lambda is W(> lambda), the
 // weighted count (weights 2, 2, 4, 8) of the products p = c_u * k_j above it,
-// and lambda* is the product p* with W(> p*) <= budget < W(>= p*).  Non-negative
-// doubles order as their bit patterns, so p* is fixed one digit of its pattern
-// at a time, top down: a weighted histogram of the digit over the products
-// that match the digits fixed so far, then the digit where the count from
-// above crosses the budget.  The first digit is the whole exponent (products
-// then spread over many buckets, so the LDS atomics seldom collide), then
-// 8-bit digits of the mantissa: 8 passes over the units instead of up to 63.
-// cost0 is the total at lambda = 0 (every product of a positive cost).
+// and lambda* is the product p* with W(> p*) <= budget < W(>= p*), or 0 when
+// every product fits.  Non-negative doubles order as their bit patterns, so p*
+// is fixed one digit of its pattern at a time, top down: a weighted histogram
+// of the digit over the products that match the digits fixed so far, then the
+// digit where the weight from above crosses the budget.  The first digit is
+// the exponent, then six 8-bit digits of the mantissa and a last 4-bit one:
+// 8 passes over the units.  A problem that fits one workgroup runs all passes
+// in it (alloc_one_kernel: the K channels, and short V problems); a long V
+// problem takes two launches per pass: sel_hist_kernel splits each group's
+// units over many workgroups, each adding its LDS histogram to the group's
+// histogram in the workspace (integer sums, so the order of the additions does
+// not matter), then sel_pick_kernel, one wave per group, fixes the digit and
+// clears the histogram for the next pass.
 constexpr int kSelBuckets = 2048;
-constexpr int kUnitBatch = 4;   // units a thread loads together
-template <typename CostAt>
-__device__ double select_lambda(int64_t n, int64_t budget, int64_t cost0, CostAt cost_at,
-                                unsigned long long* s_hist, unsigned long long* s_state) {
-  if (cost0 <= budget) return 0.0;
-  const unsigned long long B = (unsigned long long)budget;
-  if (threadIdx.x == 0) s_state[0] = 0, s_state[1] = 0;   // weight above the prefix, prefix
-  // digits: bits 52-63 (sign and exponent), then 44-51, ..., 4-11, then 0-3
-#pragma unroll 1
-  for (int pass = 0; pass < 8; ++pass) {
-    const int width = pass == 0 ? 12 : pass == 7 ? 4 : 8;
-    const int shift = pass == 0 ? 52 : pass == 7 ? 0 : 52 - 8 * pass;
-    const int nb = 1 << width;
-    for (int i = threadIdx.x; i < nb; i += kThreads) s_hist[i] = 0;
-    __syncthreads();
-    const unsigned long long prefix = s_state[1];
-    const unsigned long long fixed = pass == 0 ? 0ull : ~0ull << (shift + width);
-    const unsigned long long dmask = (unsigned long long)(nb - 1);
-    for (int64_t t0 = threadIdx.x; t0 < n; t0 += int64_t(kThreads) * kUnitBatch) {
-      float c[kUnitBatch];
-#pragma unroll
-      for (int u = 0; u < kUnitBatch; ++u) {
-        const int64_t t = t0 + int64_t(u) * kThreads;
-        c[u] = t < n ? cost_at(t) : 0.0f;   // (a zero cost has no positive product: never counted)
-      }
-#pragma unroll
-      for (int u = 0; u < kUnitBatch; ++u) {
-        if (!(c[u] > 0.0f)) continue;
-        const double cd = double(c[u]);
-        const double pj[4] = {cd * 0.375, cd * 0.09375, cd * (15.0 / 1024.0), cd * (255.0 / 524288.0)};
-        const unsigned wj[4] = {2, 2, 4, 8};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const unsigned long long pat = __double_as_longlong(pj[j]);
-          if ((pat & fixed) == (prefix & fixed)) atomicAdd(&s_hist[(pat >> shift) & dmask], (unsigned long long)wj[j]);
-        }
-      }
-    }
-    __syncthreads();
-    // wave 0: lane L sums buckets [L C, L C + C); the lane where the weight
-    // from above crosses the budget scans its buckets top down
-    if (threadIdx.x < 64) {
-      const int L = threadIdx.x, C = nb >= 64 ? nb / 64 : 1;
-      unsigned long long sl = 0;
-      if (L * C < nb)
-        for (int i = 0; i < C; ++i) sl += s_hist[L * C + i];
-      unsigned long long incl = sl;   // weight of lanes >= L
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const unsigned long long o = __shfl_down(incl, off);
-        if (L + off < 64) incl += o;
-      }
-      const unsigned long long above = s_state[0], strictly = above + (incl - sl);
-      if (strictly <= B && above + incl > B) {   // exactly one lane (weights are non-negative)
-        unsigned long long acc = strictly;
-        int d = L * C + C - 1;
-        for (; d > L * C; --d) {
-          if (acc + s_hist[d] > B) break;
-          acc += s_hist[d];
-        }
-        s_state[0] = acc;
-        s_state[1] = prefix | ((unsigned long long)d << shift);
-      }
-    }
-    __syncthreads();
-  }
-  return __longlong_as_double(s_state[1]);
-}
+constexpr int kSelPasses = 8;
+constexpr int kSelThreads = 256;
+constexpr int kUnitBatch = 8;   // units a thread loads together: their loads are all in flight at once
 
-struct AllocVArgs {
-  int64_t N;
-  int32_t group;       // consecutive segments sharing the budget
+// Digit `pass`: bits [shift, shift + width) of the pattern.  Bit 63 (the
+// sign) is 0 for every product, so the first digit is the 11-bit exponent.
+__host__ __device__ constexpr int sel_width(int pass) { return pass == 0 ? 11 : pass == kSelPasses - 1 ? 4 : 8; }
+__host__ __device__ constexpr int sel_shift(int pass) {
+  return pass == 0 ? 52 : pass == kSelPasses - 1 ? 0 : 52 - 8 * pass;
+}
+static_assert(sel_shift(kSelPasses - 1) == 0 && sel_shift(kSelPasses - 2) == sel_width(kSelPasses - 1) &&
+                  sel_shift(0) + sel_width(0) == 63 && sel_shift(1) + sel_width(1) == sel_shift(0),
+              "the digits tile bits 0-62 of the pattern");
+static_assert((1 << sel_width(0)) == kSelBuckets && (1 << sel_width(1)) <= kSelBuckets, "a digit's buckets fit");
+
+// A group's selection state: weight of the products above the prefix, the
+// prefix (the digits fixed so far), and a flag for "every product fits".
+enum { kStAbove = 0, kStPrefix = 1, kStDone = 2, kStWords = 4 };
+
+struct SelArgs {
+  int64_t n;                   // units per group (group * N)
+  int32_t blocks;              // workgroups per group
+  int32_t pass;
   const float* w_tok;
   const float* var_tok;
-  int64_t budget;
-  uint8_t* bits_tok;
-  double* lambda;
+  unsigned long long* hist;    // [groups][kSelBuckets]
+  unsigned long long* state;   // [groups][kStWords]
 };
 
-// One workgroup per group of segments: its group * N tokens are one problem.
-// (A thread's bit count stays far below 2^31; the block total is 64-bit.)
-__global__ __launch_bounds__(kThreads) void alloc_v_kernel(AllocVArgs a) {
-  __shared__ int64_t s_i[kWaves];
-  __shared__ unsigned long long s_hist[kSelBuckets], s_state[2];
-  const int64_t n = a.N * a.group;
-  const int64_t base = int64_t(blockIdx.x) * n;
-  const float* w = a.w_tok + base;
-  const float* v = a.var_tok + base;
-  int k0 = 0;   // bits at lambda = 0: 16 per unit of positive cost
-#pragma unroll 4
-  for (int64_t t = threadIdx.x; t < n; t += kThreads) k0 += __fmul_rn(w[t], v[t]) > 0.0f ? 16 : 0;
-  const int64_t cost0 = block_sum64(k0, s_i);
-  const double lam = select_lambda(n, a.budget, cost0, [&](int64_t t) { return __fmul_rn(w[t], v[t]); }, s_hist,
-                                   s_state);
-  for (int64_t t = threadIdx.x; t < n; t += kThreads) a.bits_tok[base + t] = uint8_t(unit_bits(__fmul_rn(w[t], v[t]), lam));
-  for (int s = threadIdx.x; s < a.group; s += kThreads) a.lambda[2 * (int64_t(blockIdx.x) * a.group + s)] = lam;
+// Units [lo, hi) of workgroup blk of a problem of n units split over `blocks`.
+__device__ inline void block_range(int64_t n, int blocks, int blk, int64_t& lo, int64_t& hi) {
+  lo = n * blk / blocks;
+  hi = n * (blk + 1) / blocks;
+}
+
+// c[u] = fl32(w * sigma) of unit t0 + u * kSelThreads (0 at or past hi: a zero
+// cost has no positive product, so it is never counted).
+__device__ inline void load_costs(const float* w, const float* v, int64_t t0, int64_t hi, float (&c)[kUnitBatch]) {
+#pragma unroll
+  for (int u = 0; u < kUnitBatch; ++u) {
+    const int64_t t = t0 + int64_t(u) * kSelThreads;
+    c[u] = t < hi ? __fmul_rn(w[t], v[t]) : 0.0f;
+  }
+}
+
+__global__ __launch_bounds__(256) void fill_u64_kernel(unsigned long long* p, int64_t n) {
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += int64_t(gridDim.x) * blockDim.x) p[i] = 0;
+}
+
+// Adds to s_hist (LDS, zero on entry for the digit's buckets) the weights of
+// the products of units [lo, hi) (this thread: lo + threadIdx.x, then every
+// kSelThreads-th) whose higher digits match `prefix`.
+__device__ void histogram_digit(const float* w, const float* v, int64_t lo, int64_t hi, int pass,
+                                unsigned long long prefix, unsigned long long* s_hist) {
+  const int width = sel_width(pass), shift = sel_shift(pass);
+  const unsigned long long fixed = pass == 0 ? 0ull : ~0ull << (shift + width);
+  const unsigned long long dmask = (1ull << width) - 1;
+  for (int64_t t0 = lo + threadIdx.x; t0 < hi; t0 += int64_t(kSelThreads) * kUnitBatch) {
+    float c[kUnitBatch];
+    load_costs(w, v, t0, hi, c);
+#pragma unroll
+    for (int u = 0; u < kUnitBatch; ++u) {
+      if (!(c[u] > 0.0f)) continue;
+      const double cd = double(c[u]);
+      const double pj[4] = {cd * 0.375, cd * 0.09375, cd * (15.0 / 1024.0), cd * (255.0 / 524288.0)};
+      const unsigned wj[4] = {2, 2, 4, 8};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const unsigned long long pat = __double_as_longlong(pj[j]);
+        if ((pat & fixed) == (prefix & fixed)) atomicAdd(&s_hist[(pat >> shift) & dmask], (unsigned long long)wj[j]);
+      }
+    }
+  }
+}
+
+// Called by one whole wave with a group's complete histogram h of digit
+// `pass` and its state st (either in LDS or in global memory): lane L sums
+// buckets [L C, L C + C); the lane where the weight from above crosses the
+// budget B scans its buckets top down and fixes the digit.  The histogram is
+// left zero for the next pass.
+__device__ void pick_digit(unsigned long long* h, unsigned long long* st, int pass, unsigned long long B) {
+  const int shift = sel_shift(pass), nb = 1 << sel_width(pass);
+  const int L = threadIdx.x & 63, C = nb >= 64 ? nb / 64 : 1;
+  const bool mine = L * C < nb;
+  unsigned long long sl = 0;
+  if (mine)
+    for (int i = 0; i < C; ++i) sl += h[L * C + i];
+  unsigned long long incl = sl;   // weight of lanes >= L
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const unsigned long long o = __shfl_down(incl, off);
+    if (L + off < 64) incl += o;
+  }
+  const unsigned long long above = st[kStAbove], prefix = st[kStPrefix];
+  const unsigned long long total = __shfl(incl, 0);
+  if (pass == 0 && total <= B) {   // every product fits: lambda* = 0 (the prefix stays 0)
+    if (L == 0) st[kStDone] = 1;
+  } else {
+    const unsigned long long strictly = above + (incl - sl);
+    if (strictly <= B && above + incl > B) {   // exactly one lane (weights are non-negative)
+      unsigned long long acc = strictly;
+      int d = L * C + C - 1;
+      for (; d > L * C; --d) {
+        if (acc + h[d] > B) break;
+        acc += h[d];
+      }
+      st[kStAbove] = acc;
+      st[kStPrefix] = prefix | ((unsigned long long)d << shift);
+    }
+  }
+  if (mine)   // (after this lane's own reads of its buckets)
+    for (int i = 0; i < C; ++i) h[L * C + i] = 0;
+}
+
+// Bits of units [lo, hi) of a group for its lambda*.
+__device__ void write_bits(const float* w, const float* v, int64_t lo, int64_t hi, double lam, uint8_t* bt) {
+  for (int64_t t0 = lo + threadIdx.x; t0 < hi; t0 += int64_t(kSelThreads) * kUnitBatch) {
+    float c[kUnitBatch];
+    load_costs(w, v, t0, hi, c);
+#pragma unroll
+    for (int u = 0; u < kUnitBatch; ++u) {
+      const int64_t t = t0 + int64_t(u) * kSelThreads;
+      if (t < hi) bt[t] = uint8_t(unit_bits(c[u], lam));
+    }
+  }
+}
+
+// A pass over many workgroups per group: each histograms its share of the
+// group's units and adds it to the group's histogram in the workspace.
+__global__ __launch_bounds__(kSelThreads) void sel_hist_kernel(SelArgs a) {
+  __shared__ unsigned long long s_hist[kSelBuckets];
+  const int64_t g = blockIdx.x / a.blocks;
+  const int blk = int(blockIdx.x % a.blocks);
+  const unsigned long long* st = a.state + g * kStWords;
+  if (st[kStDone]) return;
+  const int nb = 1 << sel_width(a.pass);
+  for (int i = threadIdx.x; i < nb; i += kSelThreads) s_hist[i] = 0;
+  __syncthreads();
+  int64_t lo, hi;
+  block_range(a.n, a.blocks, blk, lo, hi);
+  histogram_digit(a.w_tok + g * a.n, a.var_tok + g * a.n, lo, hi, a.pass, st[kStPrefix], s_hist);
+  __syncthreads();
+  unsigned long long* gh = a.hist + g * kSelBuckets;
+  for (int i = threadIdx.x; i < nb; i += kSelThreads)
+    if (s_hist[i]) atomicAdd(&gh[i], s_hist[i]);
+}
+
+// One wave per group: the digit of this pass from the group's histogram.
+__global__ __launch_bounds__(64) void sel_pick_kernel(SelArgs a, int64_t budget) {
+  const int64_t g = blockIdx.x;
+  unsigned long long* st = a.state + g * kStWords;
+  if (st[kStDone]) return;
+  pick_digit(a.hist + g * kSelBuckets, st, a.pass, (unsigned long long)budget);
+}
+
+// Bits of every V token for its group's lambda*, and lambda_V of the group's segments.
+__global__ __launch_bounds__(kSelThreads) void alloc_v_bits_kernel(SelArgs a, int32_t group, uint8_t* bits_tok,
+                                                                   double* lambda) {
+  const int64_t g = blockIdx.x / a.blocks;
+  const int blk = int(blockIdx.x % a.blocks);
+  const double lam = __longlong_as_double((long long)a.state[g * kStWords + kStPrefix]);
+  int64_t lo, hi;
+  block_range(a.n, a.blocks, blk, lo, hi);
+  write_bits(a.w_tok + g * a.n, a.var_tok + g * a.n, lo, hi, lam, bits_tok + g * a.n);
+  if (blk == 0)
+    for (int s = threadIdx.x; s < group; s += kSelThreads) lambda[2 * (g * group + s)] = lam;
+}
+
+// A whole problem of a group in one workgroup (small problems: the histogram
+// and state stay in LDS, one launch instead of 17): the V tokens, or the K
+// channels (units c = fl32(w_chan * var_chan), the same rule), whose lambda
+// goes to lambda[2 seg + lam_slot].
+__global__ __launch_bounds__(kSelThreads) void alloc_one_kernel(SelArgs a, int64_t budget, int32_t group,
+                                                                uint8_t* bits, double* lambda, int32_t lam_slot) {
+  __shared__ unsigned long long s_hist[kSelBuckets];
+  __shared__ unsigned long long s_st[kStWords];
+  const int64_t g = blockIdx.x;
+  const float* w = a.w_tok + g * a.n;
+  const float* v = a.var_tok + g * a.n;
+  for (int i = threadIdx.x; i < kSelBuckets; i += kSelThreads) s_hist[i] = 0;
+  if (threadIdx.x < kStWords) s_st[threadIdx.x] = 0;
+  __syncthreads();
+  for (int pass = 0; pass < kSelPasses; ++pass) {
+    if (s_st[kStDone]) break;   // (uniform)
+    histogram_digit(w, v, 0, a.n, pass, s_st[kStPrefix], s_hist);
+    __syncthreads();
+    if (threadIdx.x < 64) pick_digit(s_hist, s_st, pass, (unsigned long long)budget);
+    __syncthreads();
+  }
+  const double lam = __longlong_as_double((long long)s_st[kStPrefix]);
+  write_bits(w, v, 0, a.n, lam, bits + g * a.n);
+  for (int s = threadIdx.x; s < group; s += kSelThreads) lambda[2 * (g * group + s) + lam_slot] = lam;
 }
 
 // ---------------------------------------------------------------- exact variance
@@ -245,9 +301,19 @@ __device__ float round_div_to_f32(U128 M, uint64_t D, int e2) {
   return ldexpf(float(m), e);
 }
 
+// Population variance (n S2 - S1^2) / n^2 of n values X 2^-24 with sums S1 of
+// X and S2 of X^2, rounded once to fp32 (0 for n = 0).
+__device__ inline float channel_variance(int64_t S1, U128 S2, int64_t n) {
+  if (n <= 0) return 0.0f;
+  const uint64_t a1 = uint64_t(S1 < 0 ? -S1 : S1);
+  const U128 M = sub128(mul128_64(S2, uint64_t(n)), mul64(a1, a1));   // n*S2 - S1^2 >= 0
+  return round_div_to_f32(M, uint64_t(n) * uint64_t(n), -48);
+}
+
 struct AllocKArgs {
   int64_t N;
   int32_t group;       // consecutive segments sharing the budget
+  int32_t blocks;      // workgroups per segment for the sums
   const __half* K;
   const uint8_t* bits_tok;
   const float* w_chan;
@@ -255,24 +321,39 @@ struct AllocKArgs {
   uint8_t* bits_chan;
   float* var_chan;
   double* lambda;
+  int64_t* s1;         // [n_seg][blocks][128] partial sums of X
+  U128* s2;            // [n_seg][blocks][128] partial sums of X^2
+  int64_t* cnt;        // [n_seg][blocks] kept tokens
 };
 
-// One workgroup per segment: the exact variance of each K channel over the
-// segment's kept tokens.  A thread takes 8 channels of a row with one 16-byte
-// load (16 threads per row, 64 rows in flight); the integer sums are merged
-// across the rows' threads by shuffles, then across waves in LDS (exact, so
-// the order does not matter).
-__global__ __launch_bounds__(kThreads) void alloc_kvar_kernel(AllocKArgs a) {
+// Exact sums of each K channel over a segment's kept tokens, the segment's
+// tokens split over `blocks` workgroups.  A workgroup takes its tokens in
+// batches of kKeepBatch: their bit widths are read with all loads in flight
+// and the kept ones listed in LDS (list order is free: the sums are exact),
+// then a thread takes 8 channels of a listed row with one 16-byte load (16
+// threads per row, 16 rows in flight, kRowBatch rows per thread loaded
+// together).  The sums are merged across the rows' threads by shuffles, then
+// across waves in LDS, and written as the workgroup's partial sums.
+constexpr int kKThreads = 256;
+constexpr int kKWaves = kKThreads / 64;
+constexpr int kKeepPerThread = 8;
+constexpr int kKeepBatch = kKThreads * kKeepPerThread;
+constexpr int kRowBatch = 4;
+__global__ __launch_bounds__(kKThreads) void kvar_sums_kernel(AllocKArgs a) {
   constexpr int kCB = kHeadDim / 8;            // 8-channel blocks per row
-  constexpr int kRowLanes = kThreads / kCB;    // rows in flight
-  __shared__ int64_t s_i[kWaves];
-  __shared__ int64_t s_s1[kWaves][kHeadDim];
-  __shared__ U128 s_s2[kWaves][kHeadDim];
-  const int64_t seg = blockIdx.x;
+  constexpr int kRowLanes = kKThreads / kCB;   // rows in flight
+  __shared__ int64_t s_s1[kKWaves][kHeadDim];
+  __shared__ U128 s_s2[kKWaves][kHeadDim];
+  __shared__ int32_t s_list[kKeepBatch];
+  __shared__ int32_t s_count;
+  const int64_t seg = blockIdx.x / a.blocks;
+  const int blk = int(blockIdx.x % a.blocks);
   const int cb = threadIdx.x % kCB, tr = threadIdx.x / kCB;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint4* Kseg = reinterpret_cast<const uint4*>(a.K + seg * a.N * kHeadDim);
   const uint8_t* bt = a.bits_tok + seg * a.N;
+  int64_t lo, hi;
+  block_range(a.N, a.blocks, blk, lo, hi);
 
   // exact sums of X = x * 2^24 and X^2 over kept tokens, channels 8 cb + e
   int64_t s1[8];
@@ -282,10 +363,7 @@ __global__ __launch_bounds__(kThreads) void alloc_kvar_kernel(AllocKArgs a) {
     s1[e] = 0;
     s2[e] = U128{0, 0};
   }
-  int n = 0;
-  for (int64_t t = tr; t < a.N; t += kRowLanes) {
-    if (bits_group(bt[t]) < 0) continue;
-    const uint4 v = Kseg[t * kCB + cb];
+  const auto add_row = [&](const uint4 v) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -295,7 +373,34 @@ __global__ __launch_bounds__(kThreads) void alloc_kvar_kernel(AllocKArgs a) {
       const uint64_t ax = uint64_t(X < 0 ? -X : X);
       s2[e] = add128(s2[e], mul64(ax, ax));
     }
-    ++n;
+  };
+  int64_t n = 0;   // kept tokens (the same in every thread)
+  for (int64_t t0 = lo; t0 < hi; t0 += kKeepBatch) {
+    if (threadIdx.x == 0) s_count = 0;
+    __syncthreads();
+    uint8_t b[kKeepPerThread];
+#pragma unroll
+    for (int j = 0; j < kKeepPerThread; ++j) {
+      const int64_t t = t0 + threadIdx.x + int64_t(j) * kKThreads;
+      b[j] = t < hi ? bt[t] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < kKeepPerThread; ++j)
+      if (bits_group(b[j]) >= 0) s_list[atomicAdd(&s_count, 1)] = threadIdx.x + j * kKThreads;
+    __syncthreads();
+    const int cnt = s_count;
+    for (int r0 = tr; r0 < cnt; r0 += kRowLanes * kRowBatch) {
+      uint4 v[kRowBatch];
+#pragma unroll
+      for (int i = 0; i < kRowBatch; ++i) {
+        const int r = r0 + i * kRowLanes;
+        v[i] = r < cnt ? Kseg[(t0 + s_list[r]) * kCB + cb] : make_uint4(0, 0, 0, 0);   // (a zero row adds 0)
+      }
+#pragma unroll
+      for (int i = 0; i < kRowBatch; ++i) add_row(v[i]);
+    }
+    n += cnt;
+    __syncthreads();   // (s_list and s_count are rewritten by the next batch)
   }
   // the wave's 4 row lanes of each channel block: lanes cb, cb + 16, cb + 32, cb + 48
 #pragma unroll
@@ -313,60 +418,134 @@ __global__ __launch_bounds__(kThreads) void alloc_kvar_kernel(AllocKArgs a) {
       s_s2[wave][8 * cb + e] = s2[e];
     }
   }
-  n = int(block_sum64(n, s_i) / kCB);   // every kept row counted by its kCB threads
   __syncthreads();
   if (threadIdx.x < kHeadDim) {
     const int c = threadIdx.x;
     int64_t S1 = 0;
     U128 S2{0, 0};
-    for (int w = 0; w < kWaves; ++w) {
+#pragma unroll
+    for (int w = 0; w < kKWaves; ++w) {
       S1 += s_s1[w][c];
       S2 = add128(S2, s_s2[w][c]);
     }
-    float var = 0.0f;
-    if (n > 0) {
-      const uint64_t a1 = uint64_t(S1 < 0 ? -S1 : S1);
-      const U128 M = sub128(mul128_64(S2, uint64_t(n)), mul64(a1, a1));   // n*S2 - S1^2 >= 0
-      var = round_div_to_f32(M, uint64_t(n) * uint64_t(n), -48);
+    if (a.blocks == 1) {   // the whole segment: its variances directly
+      a.var_chan[seg * kHeadDim + c] = channel_variance(S1, S2, n);
+    } else {
+      const int64_t slot = seg * a.blocks + blk;
+      a.s1[slot * kHeadDim + c] = S1;
+      a.s2[slot * kHeadDim + c] = S2;
+      if (c == 0) a.cnt[slot] = n;
     }
-    a.var_chan[seg * kHeadDim + c] = var;
   }
 }
 
-// One workgroup per group of segments: the group * 128 channels are one
-// problem with unit costs fl32(w_chan * var_chan).
-__global__ __launch_bounds__(kThreads) void alloc_kbits_kernel(AllocKArgs a) {
-  __shared__ int64_t s_i[kWaves];
-  __shared__ float s_f[kWaves];
-  const int64_t n = int64_t(kHeadDim) * a.group;
-  const int64_t base = int64_t(blockIdx.x) * n;
-  auto cost_at = [&](int64_t u) { return __fmul_rn(a.w_chan[base + u], a.var_chan[base + u]); };
-  float cmax = 0.0f;
-  for (int64_t u = threadIdx.x; u < n; u += kThreads) {
-    const float cc = cost_at(u);
-    if (cc > cmax) cmax = cc;
+// var_chan of each (segment, channel): the partial sums added up (exact), and
+// the population variance n S2 - S1^2 over n^2 rounded once to fp32.
+__global__ __launch_bounds__(kHeadDim) void kvar_final_kernel(AllocKArgs a) {
+  const int64_t seg = blockIdx.x;
+  const int c = threadIdx.x;
+  constexpr int kLoads = 8;   // blocks whose partial sums are loaded together
+  int64_t S1 = 0, n = 0;
+  U128 S2{0, 0};
+  for (int b0 = 0; b0 < a.blocks; b0 += kLoads) {
+    int64_t s1[kLoads], cn[kLoads];
+    U128 s2[kLoads];
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+      const int64_t slot = seg * a.blocks + b0 + j;
+      const bool in = b0 + j < a.blocks;
+      s1[j] = in ? a.s1[slot * kHeadDim + c] : 0;
+      s2[j] = in ? a.s2[slot * kHeadDim + c] : U128{0, 0};
+      cn[j] = in ? a.cnt[slot] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+      S1 += s1[j];
+      S2 = add128(S2, s2[j]);
+      n += cn[j];
+    }
   }
-  cmax = block_max(cmax, s_f);
-  auto cost = [&](double lam) {
-    int k = 0;
-    for (int64_t u = threadIdx.x; u < n; u += kThreads) k += unit_bits(cost_at(u), lam);
-    return block_sum64(k, s_i);
-  };
-  const double lam = find_lambda(cmax, a.budget, cost);
-  for (int64_t u = threadIdx.x; u < n; u += kThreads) a.bits_chan[base + u] = uint8_t(unit_bits(cost_at(u), lam));
-  for (int s = threadIdx.x; s < a.group; s += kThreads) a.lambda[2 * (int64_t(blockIdx.x) * a.group + s) + 1] = lam;
+  a.var_chan[seg * kHeadDim + c] = channel_variance(S1, S2, n);
 }
 
 }  // namespace
 
 hipError_t launch_allocate(const AllocParams& p, hipStream_t stream) {
-  const unsigned n_groups = unsigned(p.n_seg / p.group);
-  AllocVArgs va{p.n_tokens, p.group, p.w_tok, p.var_tok, p.budget_v, p.bits_tok, p.lambda};
-  hipLaunchKernelGGL(alloc_v_kernel, dim3(n_groups), dim3(kThreads), 0, stream, va);
-  AllocKArgs ka{p.n_tokens, p.group, p.K, p.bits_tok, p.w_chan, p.budget_k, p.bits_chan, p.var_chan, p.lambda};
-  hipLaunchKernelGGL(alloc_kvar_kernel, dim3(unsigned(p.n_seg)), dim3(kThreads), 0, stream, ka);
-  hipLaunchKernelGGL(alloc_kbits_kernel, dim3(n_groups), dim3(kThreads), 0, stream, ka);
-  return hipGetLastError();
+  const int64_t n_groups = p.n_seg / p.group;
+  if (n_groups == 0) return hipSuccess;
+  const AllocPlan w = alloc_plan(p.n_seg, p.n_tokens, p.group);
+  auto* hist = reinterpret_cast<unsigned long long*>(p.workspace + w.hist);
+  auto* state = reinterpret_cast<unsigned long long*>(p.workspace + w.state);
+  // (a launch's error is kept: a later successful call would clear it)
+  hipError_t e = hipSuccess;
+  const auto check = [&]() {
+    const hipError_t l = hipGetLastError();
+    if (e == hipSuccess) e = l;
+  };
+  SelArgs sa{p.n_tokens * p.group, w.v_blocks, 0, p.w_tok, p.var_tok, hist, state};
+  if (w.v_blocks == 1) {
+    hipLaunchKernelGGL(alloc_one_kernel, dim3(unsigned(n_groups)), dim3(kSelThreads), 0, stream, sa, p.budget_v,
+                       p.group, p.bits_tok, p.lambda, 0);
+    check();
+  } else {
+    // the histograms and states start at zero (a fill kernel, so a captured graph replays it)
+    const int64_t words = (w.state + n_groups * kStWords * 8 - w.hist) / 8;
+    hipLaunchKernelGGL(fill_u64_kernel, dim3(unsigned(std::min<int64_t>(cdiv(words, 256), 1024))), dim3(256), 0,
+                       stream, hist, words);
+    check();
+    const unsigned v_grid = unsigned(n_groups * w.v_blocks);
+    for (int pass = 0; pass < kSelPasses; ++pass) {
+      sa.pass = pass;
+      hipLaunchKernelGGL(sel_hist_kernel, dim3(v_grid), dim3(kSelThreads), 0, stream, sa);
+      check();
+      hipLaunchKernelGGL(sel_pick_kernel, dim3(unsigned(n_groups)), dim3(64), 0, stream, sa, p.budget_v);
+      check();
+    }
+    hipLaunchKernelGGL(alloc_v_bits_kernel, dim3(v_grid), dim3(kSelThreads), 0, stream, sa, p.group, p.bits_tok,
+                       p.lambda);
+    check();
+  }
+  AllocKArgs ka{p.n_tokens, p.group, w.k_blocks, p.K, p.bits_tok, p.w_chan, p.budget_k, p.bits_chan, p.var_chan,
+                p.lambda, reinterpret_cast<int64_t*>(p.workspace + w.s1), reinterpret_cast<U128*>(p.workspace + w.s2),
+                reinterpret_cast<int64_t*>(p.workspace + w.cnt)};
+  hipLaunchKernelGGL(kvar_sums_kernel, dim3(unsigned(p.n_seg * w.k_blocks)), dim3(kKThreads), 0, stream, ka);
+  check();
+  if (w.k_blocks > 1) {
+    hipLaunchKernelGGL(kvar_final_kernel, dim3(unsigned(p.n_seg)), dim3(kHeadDim), 0, stream, ka);
+    check();
+  }
+  // the K channels: group * 128 units per problem, always one workgroup
+  const SelArgs sk{int64_t(kHeadDim) * p.group, 1, 0, p.w_chan, p.var_chan, nullptr, nullptr};
+  hipLaunchKernelGGL(alloc_one_kernel, dim3(unsigned(n_groups)), dim3(kSelThreads), 0, stream, sk, p.budget_k,
+                     p.group, p.bits_chan, p.lambda, 1);
+  check();
+  return e;
+}
+
+AllocPlan alloc_plan(int64_t n_seg, int64_t n_tokens, int32_t group) {
+  // workgroups per problem: enough to fill the chip (about kFill in all),
+  // none with fewer than kMinUnits V tokens or kMinTokens tokens for the sums
+  constexpr int64_t kFill = 2048, kMinUnits = 2048, kMinTokens = 2048;
+  AllocPlan w{};
+  if (n_seg <= 0 || n_tokens <= 0 || group < 1) return w;
+  const int64_t n_groups = n_seg / group, n = n_tokens * group;
+  w.v_blocks = int32_t(std::max<int64_t>(1, std::min(cdiv(kFill, n_groups), cdiv(n, kMinUnits))));
+  w.k_blocks = int32_t(std::max<int64_t>(1, std::min(cdiv(kFill, n_seg), cdiv(n_tokens, kMinTokens))));
+  uint64_t o = 0;
+  const auto take = [&](uint64_t bytes) {
+    const uint64_t at = o;
+    o += (bytes + 255) / 256 * 256;
+    return at;
+  };
+  // (one workgroup per problem keeps its histogram in LDS and its sums in registers)
+  const uint64_t vg = w.v_blocks > 1 ? uint64_t(n_groups) : 0, ks = w.k_blocks > 1 ? uint64_t(n_seg) * w.k_blocks : 0;
+  w.hist = take(vg * kSelBuckets * 8);
+  w.state = take(vg * kStWords * 8);
+  w.s1 = take(ks * kHeadDim * 8);
+  w.s2 = take(ks * kHeadDim * 16);
+  w.cnt = take(ks * 8);
+  w.total = o;
+  return w;
 }
 
 }  // namespace rdkv

@@ -108,7 +108,7 @@ __global__ __launch_bounds__(kThreads) void rollover_reset_kernel(RolloverParams
 
 // Workspace regions of a rollover, each 256-byte aligned.
 struct Workspace {
-  uint64_t kg, vg, w_tok, var_tok, w_chan, var_chan, bits_tok, bits_chan, lambda, total;
+  uint64_t kg, vg, w_tok, var_tok, w_chan, var_chan, bits_tok, bits_chan, lambda, alloc, total;
 };
 Workspace workspace_plan(int64_t n_seg, int64_t cap) {
   Workspace w;
@@ -127,6 +127,7 @@ Workspace workspace_plan(int64_t n_seg, int64_t cap) {
   w.bits_tok = take(uint64_t(n_seg) * cap);
   w.bits_chan = take(uint64_t(n_seg) * kHeadDim);
   w.lambda = take(uint64_t(n_seg) * 2 * 8);
+  w.alloc = take(alloc_plan(n_seg, cap, 1).total);
   w.total = o;
   return w;
 }
@@ -174,6 +175,7 @@ hipError_t launch_rollover(RolloverParams r, const rdkv_layout& gen_layout, int3
   ap.bits_chan = ws + w.bits_chan;
   ap.var_chan = reinterpret_cast<float*>(ws + w.var_chan);
   ap.lambda = reinterpret_cast<double*>(ws + w.lambda);
+  ap.workspace = ws + w.alloc;
   e = launch_allocate(ap, stream);
   if (e != hipSuccess) return e;
 

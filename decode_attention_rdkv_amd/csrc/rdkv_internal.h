@@ -278,8 +278,16 @@ struct AllocParams {
   uint8_t* bits_chan;
   float* var_chan;
   double* lambda;
+  uint8_t* workspace;      // alloc_plan(n_seg, n_tokens, group).total bytes, 256-byte aligned
 };
 hipError_t launch_allocate(const AllocParams& p, hipStream_t stream);
+// The allocation's workspace: per group its radix-selection histogram and
+// state, per (segment, token block) the exact K sums; byte offsets.
+struct AllocPlan {
+  int32_t v_blocks, k_blocks;   // workgroups per group (V tokens), per segment (K sums)
+  uint64_t hist, state, s1, s2, cnt, total;
+};
+AllocPlan alloc_plan(int64_t n_seg, int64_t n_tokens, int32_t group);
 
 struct ScoreParams {
   int64_t n_tokens;

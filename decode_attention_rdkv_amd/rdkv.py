@@ -68,10 +68,11 @@ SIGNATURES = {
     "rdkv_score_lse": (c_i32, [ctypes.POINTER(Dims), c_vp, c_vp, c_vp, c_vp]),
     "rdkv_score_from_lse": (c_i32, [ctypes.POINTER(Dims), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                     ctypes.c_size_t, c_vp]),
+    "rdkv_allocate_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(Dims), c_i32]),
     "rdkv_allocate": (c_i32, [ctypes.POINTER(Dims), c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp,
-                              c_vp]),
+                              c_vp, ctypes.c_size_t, c_vp]),
     "rdkv_allocate_shared": (c_i32, [ctypes.POINTER(Dims), c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i32, c_vp, c_vp,
-                                     c_vp, c_vp, c_vp]),
+                                     c_vp, c_vp, c_vp, ctypes.c_size_t, c_vp]),
     "rdkv_cache_init": (c_i32, [ctypes.POINTER(Layout), c_vp, ctypes.c_size_t, c_vp]),
     "rdkv_pack": (c_i32, [ctypes.POINTER(Layout), c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, ctypes.c_size_t, c_vp]),
     "rdkv_pack_status": (c_i32, [ctypes.POINTER(Layout), c_vp, ctypes.c_size_t, c_vp, c_vp]),
@@ -238,8 +239,20 @@ def score_from_lse(dims: Dims, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor
     return w_tok, var_tok, w_chan
 
 
-def allocate(dims: Dims, w_tok, var_tok, w_chan, K, budget_v: int, budget_k: int):
+def allocate_workspace_bytes(dims: Dims, group: int = 1) -> int:
+    return int(load().rdkv_allocate_workspace_bytes(ctypes.byref(dims), group))
+
+
+def allocate(dims: Dims, w_tok, var_tok, w_chan, K, budget_v: int, budget_k: int,
+             workspace: Optional[torch.Tensor] = None):
     """Bit allocation; returns (bits_tok u8, bits_chan u8, var_chan f32, lambda f64 [...,2])."""
+    return allocate_shared(dims, w_tok, var_tok, w_chan, K, budget_v, budget_k, 1, workspace=workspace)
+
+
+def allocate_shared(dims: Dims, w_tok, var_tok, w_chan, K, budget_v: int, budget_k: int, group: int,
+                    workspace: Optional[torch.Tensor] = None):
+    """Bit allocation with one budget per group of `group` consecutive segments
+    (rdkv_allocate for group 1)."""
     lib = load()
     S, L, Hk, N = dims.n_seq, dims.n_layers, dims.n_kv_heads, dims.n_tokens
     dev = K.device
@@ -247,32 +260,18 @@ def allocate(dims: Dims, w_tok, var_tok, w_chan, K, budget_v: int, budget_k: int
     bits_chan = torch.empty((S, L, Hk, HEAD_DIM), dtype=torch.uint8, device=dev)
     var_chan = torch.empty((S, L, Hk, HEAD_DIM), dtype=torch.float32, device=dev)
     lam = torch.empty((S, L, Hk, 2), dtype=torch.float64, device=dev)
-    _check(lib.rdkv_allocate(ctypes.byref(dims), _ptr(w_tok, torch.float32, (S, L, Hk, N), "w_tok"),
-                             _ptr(var_tok, torch.float32, (S, L, Hk, N), "var_tok"),
-                             _ptr(w_chan, torch.float32, (S, L, Hk, HEAD_DIM), "w_chan"),
-                             _ptr(K, torch.float16, (S, L, Hk, N, HEAD_DIM), "K"), budget_v, budget_k,
-                             bits_tok.data_ptr(), bits_chan.data_ptr(), var_chan.data_ptr(), lam.data_ptr(),
-                             _stream()),
-           "rdkv_allocate")
-    return bits_tok, bits_chan, var_chan, lam
-
-
-def allocate_shared(dims: Dims, w_tok, var_tok, w_chan, K, budget_v: int, budget_k: int, group: int):
-    """Bit allocation with one budget per group of `group` consecutive segments."""
-    lib = load()
-    S, L, Hk, N = dims.n_seq, dims.n_layers, dims.n_kv_heads, dims.n_tokens
-    dev = K.device
-    bits_tok = torch.empty((S, L, Hk, N), dtype=torch.uint8, device=dev)
-    bits_chan = torch.empty((S, L, Hk, HEAD_DIM), dtype=torch.uint8, device=dev)
-    var_chan = torch.empty((S, L, Hk, HEAD_DIM), dtype=torch.float32, device=dev)
-    lam = torch.empty((S, L, Hk, 2), dtype=torch.float64, device=dev)
-    _check(lib.rdkv_allocate_shared(ctypes.byref(dims), _ptr(w_tok, torch.float32, (S, L, Hk, N), "w_tok"),
-                                    _ptr(var_tok, torch.float32, (S, L, Hk, N), "var_tok"),
-                                    _ptr(w_chan, torch.float32, (S, L, Hk, HEAD_DIM), "w_chan"),
-                                    _ptr(K, torch.float16, (S, L, Hk, N, HEAD_DIM), "K"), budget_v, budget_k, group,
-                                    bits_tok.data_ptr(), bits_chan.data_ptr(), var_chan.data_ptr(), lam.data_ptr(),
-                                    _stream()),
-           "rdkv_allocate_shared")
+    if workspace is None:
+        workspace = torch.empty(max(allocate_workspace_bytes(dims, group), 16), dtype=torch.uint8, device=dev)
+    args = (ctypes.byref(dims), _ptr(w_tok, torch.float32, (S, L, Hk, N), "w_tok"),
+            _ptr(var_tok, torch.float32, (S, L, Hk, N), "var_tok"),
+            _ptr(w_chan, torch.float32, (S, L, Hk, HEAD_DIM), "w_chan"),
+            _ptr(K, torch.float16, (S, L, Hk, N, HEAD_DIM), "K"), budget_v, budget_k)
+    outs = (bits_tok.data_ptr(), bits_chan.data_ptr(), var_chan.data_ptr(), lam.data_ptr(), workspace.data_ptr(),
+            workspace.numel() * workspace.element_size(), _stream())
+    if group == 1:
+        _check(lib.rdkv_allocate(*args, *outs), "rdkv_allocate")
+    else:
+        _check(lib.rdkv_allocate_shared(*args, group, *outs), "rdkv_allocate_shared")
     return bits_tok, bits_chan, var_chan, lam
 
 

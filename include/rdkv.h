@@ -169,11 +169,19 @@ rdkv_status rdkv_score_from_lse(const rdkv_dims* dims, const void* Q, const void
  *   bits_tok  u8 [S][L][Hkv][N], bits_chan u8 [S][L][Hkv][128] (values 0,2,4,8,16)
  *   var_chan  fp32 [S][L][Hkv][128]; lambda fp64 [S][L][Hkv][2] (lambda_V, lambda_K)
  * K is the fp16 prefill K [S][L][Hkv][N][128].  Budgets are bits per segment.
- * The allocation is exact: same inputs give the same bits on every run. */
+ * workspace: device scratch of rdkv_allocate_workspace_bytes(dims, 1) bytes
+ * (group for rdkv_allocate_shared), 16-byte aligned, owned by the caller (may
+ * be NULL when that size is 0: problems small enough for one workgroup each);
+ * its contents need no initialisation and mean nothing afterwards; two calls
+ * in flight at once need two workspaces.  The allocation is exact: same inputs
+ * give the same bits on every run.  Errors: RDKV_ERR_NULL, _ALIGN (any pointer
+ * not 16-byte aligned), _BUDGET (a negative budget), _WORKSPACE (too small),
+ * _SHAPE / _UNSUPPORTED for dims; nothing is enqueued on an error. */
+size_t rdkv_allocate_workspace_bytes(const rdkv_dims* dims, int32_t group);   /* 0 for invalid dims or group */
 rdkv_status rdkv_allocate(const rdkv_dims* dims, const float* w_tok, const float* var_tok,
                           const float* w_chan, const void* K, int64_t budget_v, int64_t budget_k,
                           uint8_t* bits_tok, uint8_t* bits_chan, float* var_chan, double* lambda,
-                          hipStream_t stream);
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* The same allocation with one budget shared by each group of `group`
  * consecutive segments (section 2.1 states B as the total bit budget; segments
@@ -190,7 +198,7 @@ rdkv_status rdkv_allocate(const rdkv_dims* dims, const float* w_tok, const float
 rdkv_status rdkv_allocate_shared(const rdkv_dims* dims, const float* w_tok, const float* var_tok,
                                  const float* w_chan, const void* K, int64_t budget_v, int64_t budget_k,
                                  int32_t group, uint8_t* bits_tok, uint8_t* bits_chan, float* var_chan,
-                                 double* lambda, hipStream_t stream);
+                                 double* lambda, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------- packing
  * TriZone packing (section 2.3; quantizer of "Solusi 3").  The blob format is

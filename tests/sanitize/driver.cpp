@@ -60,14 +60,24 @@ void scoring(const rdkv_dims& d) {
   EXPECT(rdkv_score_lse(&d, D, nullptr, F(D), nullptr) == RDKV_ERR_NULL, "score_lse null K");
   EXPECT(ok_or_hip(rdkv_score_from_lse(&d, D, D, D, F(D), F(D), F(D), F(D), D, ws, nullptr)), "score_from_lse");
   EXPECT(rdkv_score_from_lse(&d, D, D, D, nullptr, F(D), F(D), F(D), D, ws, nullptr) == RDKV_ERR_NULL, "lse null");
-  EXPECT(ok_or_hip(rdkv_allocate(&d, F(D), F(D), F(D), D, 100, 50, U(D), U(D), F(D), (double*)D, nullptr)), "alloc");
-  EXPECT(rdkv_allocate(&d, F(D), F(D), F(D), D, -1, 50, U(D), U(D), F(D), (double*)D, nullptr) == RDKV_ERR_BUDGET,
+  const size_t aw = rdkv_allocate_workspace_bytes(&d, 1);
+  EXPECT(ok_or_hip(rdkv_allocate(&d, F(D), F(D), F(D), D, 100, 50, U(D), U(D), F(D), (double*)D, D, aw, nullptr)),
+         "alloc");
+  EXPECT(rdkv_allocate(&d, F(D), F(D), F(D), D, -1, 50, U(D), U(D), F(D), (double*)D, D, aw, nullptr) ==
+             RDKV_ERR_BUDGET,
          "alloc negative budget");
-  EXPECT(rdkv_allocate(&d, F(D), F(D), F(D), D, 100, 50, nullptr, U(D), F(D), (double*)D, nullptr) == RDKV_ERR_NULL,
+  EXPECT(rdkv_allocate(&d, F(D), F(D), F(D), D, 100, 50, nullptr, U(D), F(D), (double*)D, D, aw, nullptr) ==
+             RDKV_ERR_NULL,
          "alloc null out");
-  EXPECT(ok_or_hip(rdkv_allocate_shared(&d, F(D), F(D), F(D), D, 100, 50, 1, U(D), U(D), F(D), (double*)D, nullptr)),
+  if (aw > 0)
+    EXPECT(rdkv_allocate(&d, F(D), F(D), F(D), D, 100, 50, U(D), U(D), F(D), (double*)D, D, aw - 1, nullptr) ==
+               RDKV_ERR_WORKSPACE,
+           "alloc small workspace");
+  EXPECT(ok_or_hip(rdkv_allocate_shared(&d, F(D), F(D), F(D), D, 100, 50, 1, U(D), U(D), F(D), (double*)D, D, aw,
+                                        nullptr)),
          "alloc shared");
-  EXPECT(rdkv_allocate_shared(&d, F(D), F(D), F(D), D, 100, 50, 0, U(D), U(D), F(D), (double*)D, nullptr) != RDKV_OK,
+  EXPECT(rdkv_allocate_shared(&d, F(D), F(D), F(D), D, 100, 50, 0, U(D), U(D), F(D), (double*)D, D, aw, nullptr) !=
+             RDKV_OK,
          "alloc shared group 0");
 }
 
@@ -170,6 +180,7 @@ void fuzz(unsigned seed, int rounds) {
     rdkv_status s = (r() & 1) ? rdkv_layout_init(&d, pick64(), pick64(), cap, &lay)
                               : rdkv_layout_init_rollover(&d, pick64(), pick64(), cap, pick32(6), pick64(), pick64(), &lay);
     (void)rdkv_score_workspace_bytes(&d);
+    (void)rdkv_allocate_workspace_bytes(&d, pick32(700));
     if (s == RDKV_OK) {
       ++accepted;
       EXPECT(lay.cache_bytes > 0 && lay.n_seg > 0, "accepted layout with no bytes");

@@ -122,19 +122,43 @@ def test_score_halves_validation(lib):
 def test_allocate_validation(lib):
     d = _dims()
     args = [A] * 4
-    assert lib.rdkv_allocate(ctypes.byref(d), *args, -5, 8, A, A, A, A, None) == BUDGET
-    assert lib.rdkv_allocate(ctypes.byref(d), *args, 8, -5, A, A, A, A, None) == BUDGET
-    assert lib.rdkv_allocate(ctypes.byref(d), *args, 8, 8, A, None, A, A, None) == NULL
-    assert lib.rdkv_allocate(ctypes.byref(d), *args, 8, 8, A, A, A + 4, A, None) == ALIGN
+    assert lib.rdkv_allocate(ctypes.byref(d), *args, -5, 8, A, A, A, A, A, 0, None) == BUDGET
+    assert lib.rdkv_allocate(ctypes.byref(d), *args, 8, -5, A, A, A, A, A, 0, None) == BUDGET
+    assert lib.rdkv_allocate(ctypes.byref(d), *args, 8, 8, A, None, A, A, A, 0, None) == NULL
+    assert lib.rdkv_allocate(ctypes.byref(d), *args, 8, 8, A, A, A + 4, A, A, 0, None) == ALIGN
+    assert lib.rdkv_allocate(ctypes.byref(d), *args, 8, 8, A, A, A, A, A + 8, 0, None) == ALIGN
+    # a problem spread over several workgroups per segment needs the workspace
+    big = _dims(n_tokens=100000)
+    ws = lib.rdkv_allocate_workspace_bytes(ctypes.byref(big), 1)
+    assert ws > 0
+    assert lib.rdkv_allocate(ctypes.byref(big), *args, 8, 8, A, A, A, A, None, ws, None) == NULL
+    assert lib.rdkv_allocate(ctypes.byref(big), *args, 8, 8, A, A, A, A, A, ws - 1, None) == WORKSPACE
+
+
+def test_allocate_workspace_size(lib):
+    """The size query is 0 for problems of one workgroup each, grows with the
+    segments and tokens it covers, and is 0 for a group that does not divide
+    the segments."""
+    small, mid, big = _dims(n_tokens=1000), _dims(n_tokens=100000), _dims(n_tokens=100000, n_layers=4)
+    assert lib.rdkv_allocate_workspace_bytes(ctypes.byref(small), 1) == 0
+    assert 0 < lib.rdkv_allocate_workspace_bytes(ctypes.byref(mid), 1) < \
+        lib.rdkv_allocate_workspace_bytes(ctypes.byref(big), 1)
+    assert lib.rdkv_allocate_workspace_bytes(ctypes.byref(big), 4) > 0
+    for g in (0, -1, 3):
+        assert lib.rdkv_allocate_workspace_bytes(ctypes.byref(big), g) == 0, g
 
 
 def test_allocate_shared_validation(lib):
     d = _dims(n_layers=3, n_kv_heads=2)   # 6 segments
-    args = lambda g: (ctypes.byref(d), A, A, A, A, 10, 10, g, A, A, A, A, None)
+    args = lambda g: (ctypes.byref(d), A, A, A, A, 10, 10, g, A, A, A, A, A, 0, None)
     for g in (0, -1, 4, 5, 7):
         assert lib.rdkv_allocate_shared(*args(g)) == SHAPE, g
-    assert lib.rdkv_allocate_shared(ctypes.byref(d), None, A, A, A, 10, 10, 1, A, A, A, A, None) == NULL
-    assert lib.rdkv_allocate_shared(ctypes.byref(d), A, A, A, A, -1, 10, 1, A, A, A, A, None) == BUDGET
+    assert lib.rdkv_allocate_shared(ctypes.byref(d), None, A, A, A, 10, 10, 1, A, A, A, A, A, 0, None) == NULL
+    assert lib.rdkv_allocate_shared(ctypes.byref(d), A, A, A, A, -1, 10, 1, A, A, A, A, A, 0, None) == BUDGET
+    big = _dims(n_layers=3, n_kv_heads=2, n_tokens=100000)
+    ws3 = lib.rdkv_allocate_workspace_bytes(ctypes.byref(big), 3)
+    assert ws3 > 0
+    assert lib.rdkv_allocate_shared(ctypes.byref(big), A, A, A, A, 10, 10, 3, A, A, A, A, A, ws3 - 1, None) == WORKSPACE
 
 
 def test_cache_pack_decode_validation(lib):

@@ -98,15 +98,19 @@ def test_score_allocate_pack_decode_write_only_their_buffers(rdkv, G):
     # allocation, per segment and with one budget per layer
     outs = [Guarded(shp + (N,), torch.uint8), Guarded(shp + (128,), torch.uint8), Guarded(shp + (128,), torch.float32),
             Guarded(shp + (2,), torch.float64)]
+    aws = Guarded(lib.rdkv_allocate_workspace_bytes(ctypes.byref(dims), 1), torch.uint8)
     assert lib.rdkv_allocate(ctypes.byref(dims), wt.t.data_ptr(), vt.t.data_ptr(), wc.t.data_ptr(), K.data_ptr(), bv, bk,
-                             *(o.t.data_ptr() for o in outs), stream()) == 0
-    for o, what in zip(outs, ("bits_tok", "bits_chan", "var_chan", "lambda")):
+                             *(o.t.data_ptr() for o in outs), aws.t.data_ptr(), aws.n, stream()) == 0
+    for o, what in zip(outs + [aws], ("bits_tok", "bits_chan", "var_chan", "lambda", "allocation workspace")):
         o.check(what)
     shared = [Guarded(shp + (N,), torch.uint8), Guarded(shp + (128,), torch.uint8), Guarded(shp + (128,), torch.float32),
               Guarded(shp + (2,), torch.float64)]
+    aws = Guarded(lib.rdkv_allocate_workspace_bytes(ctypes.byref(dims), Hkv), torch.uint8)
     assert lib.rdkv_allocate_shared(ctypes.byref(dims), wt.t.data_ptr(), vt.t.data_ptr(), wc.t.data_ptr(), K.data_ptr(),
-                                    bv * Hkv, bk * Hkv, Hkv, *(o.t.data_ptr() for o in shared), stream()) == 0
-    for o, what in zip(shared, ("shared bits_tok", "shared bits_chan", "shared var_chan", "shared lambda")):
+                                    bv * Hkv, bk * Hkv, Hkv, *(o.t.data_ptr() for o in shared), aws.t.data_ptr(),
+                                    aws.n, stream()) == 0
+    for o, what in zip(shared + [aws], ("shared bits_tok", "shared bits_chan", "shared var_chan", "shared lambda",
+                                        "shared allocation workspace")):
         o.check(what)
     bt, bc = outs[0].t, outs[1].t
     # cache init, pack, decode (one call, two phases), with appends

@@ -384,6 +384,44 @@ def test_allocate_bit_exact(gpu_lib, N, budget_avg):
         assert int(bits_tok[s].astype(np.int64).sum()) <= bv and int(bits_chan[s].astype(np.int64).sum()) <= bk
 
 
+@pytest.mark.parametrize("group,budget_avg,ties", [(1, "0.64", False), (1, "2", True), (1, "0", False),
+                                                   (1, "17", False), (2, "0.5", True), (2, "3", False)])
+def test_allocate_many_workgroups_bit_exact(gpu_lib, group, budget_avg, ties):
+    """Segments long enough that the V selection runs over several
+    workgroups per group (histograms added in the workspace, one pick per
+    pass) and the K sums over several token blocks: bits, lambdas and
+    variances bit for bit against the oracle, with zero and saturating
+    budgets and with many equal costs (ties at the crossing)."""
+    from fractions import Fraction
+    rdkv = gpu_lib
+    S, L, Hkv, N = 1, 1, 4, 40000
+    n_seg = S * L * Hkv
+    w_tok, var_tok, w_chan = synth.random_unit_inputs(n_seg, N, seed=77)
+    if ties:   # a few distinct values: many units share each product
+        w_tok = np.float32(2.0) ** np.round(np.log2(w_tok)).clip(-20, 20).astype(np.float32)
+        var_tok = np.float32(2.0) ** np.round(np.log2(var_tok)).clip(-20, 20).astype(np.float32)
+    K, _ = synth.random_kv(n_seg, N, seed=78)
+    bv, bk = int(Fraction(budget_avg) * N) * group, int(Fraction(budget_avg) * 128) * group
+    dims = rdkv.make_dims(S, L, 4 * Hkv, Hkv, N)
+    assert rdkv.allocate_workspace_bytes(dims, group) > 0   # the many-workgroup path
+    shp = (S, L, Hkv)
+    bt, bc, vc, lam = (host(x) for x in rdkv.allocate_shared(
+        dims, dev(w_tok.reshape(shp + (N,))), dev(var_tok.reshape(shp + (N,))), dev(w_chan.reshape(shp + (128,))),
+        dev(K.reshape(shp + (N, 128))), bv, bk, group))
+    bt, bc, vc, lam = bt.reshape(n_seg, N), bc.reshape(n_seg, 128), vc.reshape(n_seg, 128), lam.reshape(n_seg, 2)
+    for g0 in range(0, n_seg, group):
+        sl = slice(g0, g0 + group)
+        ref = O.allocate_group(w_tok[sl], var_tok[sl], w_chan[sl], K[sl], bv, bk)
+        assert np.array_equal(bt[sl], ref["bits_tok"]), f"group at {g0}: V bits differ"
+        assert np.all(lam[sl, 0] == ref["lambda_v"])
+        assert np.array_equal(vc[sl].view(np.uint32), ref["var_chan"].view(np.uint32)), f"group at {g0}: var_chan"
+        assert np.array_equal(bc[sl], ref["bits_chan"]) and np.all(lam[sl, 1] == ref["lambda_k"])
+    if budget_avg == "0":
+        assert not bt.any()
+    if budget_avg == "17":
+        assert np.all(bt == 16) and np.all(lam[:, 0] == 0.0)
+
+
 @pytest.mark.parametrize("group,budget_scale", [(1, 1.0), (2, 1.0), (4, 1.0), (8, 1.0), (4, 0.0), (8, 40.0)])
 def test_allocate_shared_bit_exact(gpu_lib, group, budget_scale):
     """One budget per group of consecutive segments (2 layers x 4 KV heads:
