@@ -327,17 +327,22 @@ struct AllocKArgs {
 };
 
 // Exact sums of each K channel over a segment's kept tokens, the segment's
-// tokens split over `blocks` workgroups.  A workgroup takes its tokens in
-// batches of kKeepBatch: their bit widths are read with all loads in flight
-// and the kept ones listed in LDS (list order is free: the sums are exact),
-// then a thread takes 8 channels of a listed row with one 16-byte load (16
-// threads per row, 16 rows in flight, kRowBatch rows per thread loaded
+// tokens split over `blocks` workgroups by 64-token tiles dealt round robin
+// (tile i to workgroup i mod blocks), so a run of kept tokens (the recent
+// window, the sinks) is spread over many workgroups.  A workgroup takes its
+// tiles kTilesPerBatch at a time: their bit widths are read with all loads in
+// flight and the kept tokens listed in LDS (list order is free: the sums are
+// exact), then a thread takes 8 channels of a listed row with one 16-byte load
+// (16 threads per row, 16 rows in flight, kRowBatch rows per thread loaded
 // together).  The sums are merged across the rows' threads by shuffles, then
 // across waves in LDS, and written as the workgroup's partial sums.
 constexpr int kKThreads = 256;
 constexpr int kKWaves = kKThreads / 64;
 constexpr int kKeepPerThread = 8;
 constexpr int kKeepBatch = kKThreads * kKeepPerThread;
+constexpr int kKTile = 64;
+constexpr int kTilesPerBatch = kKeepBatch / kKTile;
+static_assert(kKTile == 64 && kTilesPerBatch == kKWaves * kKeepPerThread, "a wave reads whole tiles");
 constexpr int kRowBatch = 4;
 __global__ __launch_bounds__(kKThreads) void kvar_sums_kernel(AllocKArgs a) {
   constexpr int kCB = kHeadDim / 8;            // 8-channel blocks per row
@@ -352,8 +357,8 @@ __global__ __launch_bounds__(kKThreads) void kvar_sums_kernel(AllocKArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint4* Kseg = reinterpret_cast<const uint4*>(a.K + seg * a.N * kHeadDim);
   const uint8_t* bt = a.bits_tok + seg * a.N;
-  int64_t lo, hi;
-  block_range(a.N, a.blocks, blk, lo, hi);
+  const int64_t n_tiles = (a.N + kKTile - 1) / kKTile;
+  const int64_t my_tiles = n_tiles > blk ? (n_tiles - blk + a.blocks - 1) / a.blocks : 0;
 
   // exact sums of X = x * 2^24 and X^2 over kept tokens, channels 8 cb + e
   int64_t s1[8];
@@ -375,18 +380,23 @@ __global__ __launch_bounds__(kKThreads) void kvar_sums_kernel(AllocKArgs a) {
     }
   };
   int64_t n = 0;   // kept tokens (the same in every thread)
-  for (int64_t t0 = lo; t0 < hi; t0 += kKeepBatch) {
+  for (int64_t b0 = 0; b0 < my_tiles; b0 += kTilesPerBatch) {
     if (threadIdx.x == 0) s_count = 0;
     __syncthreads();
+    // thread: token lane of local tiles b0 + wave + kKWaves j (a wave reads a tile's 64 bytes)
     uint8_t b[kKeepPerThread];
+    int32_t tok[kKeepPerThread];
 #pragma unroll
     for (int j = 0; j < kKeepPerThread; ++j) {
-      const int64_t t = t0 + threadIdx.x + int64_t(j) * kKThreads;
-      b[j] = t < hi ? bt[t] : 0;
+      const int64_t lt = b0 + wave + kKWaves * j;
+      const int64_t t = (blk + lt * a.blocks) * kKTile + lane;
+      const bool in = lt < my_tiles && t < a.N;
+      b[j] = in ? bt[t] : 0;
+      tok[j] = int32_t(t);   // (< 2^19)
     }
 #pragma unroll
     for (int j = 0; j < kKeepPerThread; ++j)
-      if (bits_group(b[j]) >= 0) s_list[atomicAdd(&s_count, 1)] = threadIdx.x + j * kKThreads;
+      if (bits_group(b[j]) >= 0) s_list[atomicAdd(&s_count, 1)] = tok[j];
     __syncthreads();
     const int cnt = s_count;
     for (int r0 = tr; r0 < cnt; r0 += kRowLanes * kRowBatch) {
@@ -394,7 +404,7 @@ __global__ __launch_bounds__(kKThreads) void kvar_sums_kernel(AllocKArgs a) {
 #pragma unroll
       for (int i = 0; i < kRowBatch; ++i) {
         const int r = r0 + i * kRowLanes;
-        v[i] = r < cnt ? Kseg[(t0 + s_list[r]) * kCB + cb] : make_uint4(0, 0, 0, 0);   // (a zero row adds 0)
+        v[i] = r < cnt ? Kseg[int64_t(s_list[r]) * kCB + cb] : make_uint4(0, 0, 0, 0);   // (a zero row adds 0)
       }
 #pragma unroll
       for (int i = 0; i < kRowBatch; ++i) add_row(v[i]);
@@ -476,50 +486,45 @@ hipError_t launch_allocate(const AllocParams& p, hipStream_t stream) {
   const AllocPlan w = alloc_plan(p.n_seg, p.n_tokens, p.group);
   auto* hist = reinterpret_cast<unsigned long long*>(p.workspace + w.hist);
   auto* state = reinterpret_cast<unsigned long long*>(p.workspace + w.state);
-  // (a launch's error is kept: a later successful call would clear it)
-  hipError_t e = hipSuccess;
-  const auto check = [&]() {
-    const hipError_t l = hipGetLastError();
-    if (e == hipSuccess) e = l;
-  };
+  LaunchErrors le;
   SelArgs sa{p.n_tokens * p.group, w.v_blocks, 0, p.w_tok, p.var_tok, hist, state};
   if (w.v_blocks == 1) {
     hipLaunchKernelGGL(alloc_one_kernel, dim3(unsigned(n_groups)), dim3(kSelThreads), 0, stream, sa, p.budget_v,
                        p.group, p.bits_tok, p.lambda, 0);
-    check();
+    le.check();
   } else {
     // the histograms and states start at zero (a fill kernel, so a captured graph replays it)
     const int64_t words = (w.state + n_groups * kStWords * 8 - w.hist) / 8;
     hipLaunchKernelGGL(fill_u64_kernel, dim3(unsigned(std::min<int64_t>(cdiv(words, 256), 1024))), dim3(256), 0,
                        stream, hist, words);
-    check();
+    le.check();
     const unsigned v_grid = unsigned(n_groups * w.v_blocks);
     for (int pass = 0; pass < kSelPasses; ++pass) {
       sa.pass = pass;
       hipLaunchKernelGGL(sel_hist_kernel, dim3(v_grid), dim3(kSelThreads), 0, stream, sa);
-      check();
+      le.check();
       hipLaunchKernelGGL(sel_pick_kernel, dim3(unsigned(n_groups)), dim3(64), 0, stream, sa, p.budget_v);
-      check();
+      le.check();
     }
     hipLaunchKernelGGL(alloc_v_bits_kernel, dim3(v_grid), dim3(kSelThreads), 0, stream, sa, p.group, p.bits_tok,
                        p.lambda);
-    check();
+    le.check();
   }
   AllocKArgs ka{p.n_tokens, p.group, w.k_blocks, p.K, p.bits_tok, p.w_chan, p.budget_k, p.bits_chan, p.var_chan,
                 p.lambda, reinterpret_cast<int64_t*>(p.workspace + w.s1), reinterpret_cast<U128*>(p.workspace + w.s2),
                 reinterpret_cast<int64_t*>(p.workspace + w.cnt)};
   hipLaunchKernelGGL(kvar_sums_kernel, dim3(unsigned(p.n_seg * w.k_blocks)), dim3(kKThreads), 0, stream, ka);
-  check();
+  le.check();
   if (w.k_blocks > 1) {
     hipLaunchKernelGGL(kvar_final_kernel, dim3(unsigned(p.n_seg)), dim3(kHeadDim), 0, stream, ka);
-    check();
+    le.check();
   }
   // the K channels: group * 128 units per problem, always one workgroup
   const SelArgs sk{int64_t(kHeadDim) * p.group, 1, 0, p.w_chan, p.var_chan, nullptr, nullptr};
   hipLaunchKernelGGL(alloc_one_kernel, dim3(unsigned(n_groups)), dim3(kSelThreads), 0, stream, sk, p.budget_k,
                      p.group, p.bits_chan, p.lambda, 1);
-  check();
-  return e;
+  le.check();
+  return le.status();
 }
 
 AllocPlan alloc_plan(int64_t n_seg, int64_t n_tokens, int32_t group) {

@@ -667,12 +667,15 @@ __global__ __launch_bounds__(256) void paged_release_kernel(uint8_t* cache, rdkv
 }  // namespace
 
 hipError_t launch_paged_init(uint8_t* cache, const rdkv_paged_layout& pl, hipStream_t stream) {
+  LaunchErrors le;
   const uint64_t n16 = pl.cache_bytes / 16;
   const unsigned grid = unsigned(std::min<uint64_t>(cdiv(n16, 256), 8192));
   hipLaunchKernelGGL(cache_zero_kernel, dim3(grid), dim3(256), 0, stream, reinterpret_cast<uint4*>(cache), n16);
+  le.check();
   const unsigned tgrid = unsigned(std::min<uint64_t>(cdiv(uint64_t(pl.n_seg) * pl.max_pages, 256) + 1, 4096));
   hipLaunchKernelGGL(paged_header_kernel, dim3(tgrid), dim3(256), 0, stream, cache, pl);
-  return hipGetLastError();
+  le.check();
+  return le.status();
 }
 
 hipError_t launch_paged_plan(const PagedPackParams& p, hipStream_t stream) {
@@ -701,27 +704,35 @@ hipError_t launch_pack_status(const uint8_t* cache, int64_t n_seg, int32_t* out,
 }
 
 hipError_t launch_cache_init(uint8_t* cache, const rdkv_layout& lay, const rdkv_layout* gen, hipStream_t stream) {
+  LaunchErrors le;
   const uint64_t n16 = lay.cache_bytes / 16;
   const unsigned grid = unsigned(std::min<uint64_t>(cdiv(n16, 256), 8192));
   hipLaunchKernelGGL(cache_zero_kernel, dim3(grid), dim3(256), 0, stream, reinterpret_cast<uint4*>(cache), n16);
+  le.check();
   const unsigned ggrid = unsigned(cdiv(lay.n_seg, 4));
   hipLaunchKernelGGL(cache_header_kernel, dim3(ggrid), dim3(256), 0, stream, cache, lay, geom_of(lay));
+  le.check();
   // every generation blob starts as an empty blob of its own layout
-  for (int g = 0; gen && g < lay.n_generations; ++g)
+  for (int g = 0; gen && g < lay.n_generations; ++g) {
     hipLaunchKernelGGL(cache_header_kernel, dim3(ggrid), dim3(256), 0, stream, cache + lay.gen_offset + g * lay.gen_bytes,
                        *gen, geom_of(*gen));
-  return hipGetLastError();
+    le.check();
+  }
+  return le.status();
 }
 
 hipError_t launch_pack(const PackParams& p, hipStream_t stream) {
+  LaunchErrors le;
   const rdkv_layout& lay = *p.lay;
   const int64_t n_seg_in = int64_t(lay.dims.n_seq) * p.n_layers_in * lay.dims.n_kv_heads;
   IndexArgs ia{p.cache, geom_of(lay), lay.dims.n_layers, lay.dims.n_kv_heads, p.layer_begin, p.n_layers_in,
                p.bits_tok, p.bits_chan};
   hipLaunchKernelGGL(pack_index_kernel, dim3(unsigned(n_seg_in)), dim3(kIndexThreads), 0, stream, ia);
+  le.check();
   RowsArgs ra{p.cache, geom_of(lay), lay.dims.n_layers, lay.dims.n_kv_heads, p.layer_begin, p.n_layers_in, p.K, p.V};
   hipLaunchKernelGGL(pack_rows_kernel, dim3(kRowsWgPerSeg, unsigned(n_seg_in)), dim3(kRowsThreads), 0, stream, ra);
-  return hipGetLastError();
+  le.check();
+  return le.status();
 }
 
 hipError_t launch_unpack(const uint8_t* cache, uint64_t, const rdkv_layout& lay, int64_t seg, float* k_hat,

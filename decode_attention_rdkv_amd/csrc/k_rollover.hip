@@ -137,13 +137,18 @@ Workspace workspace_plan(int64_t n_seg, int64_t cap) {
 uint64_t rollover_workspace_bytes(int64_t n_seg, int64_t cap) { return workspace_plan(n_seg, cap).total; }
 
 hipError_t launch_rollover_score(const RolloverParams& r, hipStream_t stream) {
+  LaunchErrors le;
   const int64_t rows = r.n_seg * r.cap;
-  if (rows > 0)
+  if (rows > 0) {
     hipLaunchKernelGGL(rollover_rows_kernel, dim3(unsigned(cdiv(rows, kThreads / 64))), dim3(kThreads), 0, stream,
                        RowsArgs{r, nullptr, nullptr});
-  if (r.n_seg > 0)
+    le.check();
+  }
+  if (r.n_seg > 0) {
     hipLaunchKernelGGL(rollover_chan_kernel, dim3(unsigned(r.n_seg)), dim3(kHeadDim), 0, stream, r);
-  return hipGetLastError();
+    le.check();
+  }
+  return le.status();
 }
 
 hipError_t launch_rollover(RolloverParams r, const rdkv_layout& gen_layout, int32_t gen, uint8_t* ws,
@@ -155,10 +160,13 @@ hipError_t launch_rollover(RolloverParams r, const rdkv_layout& gen_layout, int3
   r.var_tok = reinterpret_cast<float*>(ws + w.var_tok);
   r.w_chan = reinterpret_cast<float*>(ws + w.w_chan);
   const int64_t rows = r.n_seg * r.cap;
+  LaunchErrors le;
   hipLaunchKernelGGL(rollover_rows_kernel, dim3(unsigned(cdiv(rows, kThreads / 64))), dim3(kThreads), 0, stream,
                      RowsArgs{r, Kg, Vg});
+  le.check();
   hipLaunchKernelGGL(rollover_chan_kernel, dim3(unsigned(r.n_seg)), dim3(kHeadDim), 0, stream, r);
-  hipError_t e = hipGetLastError();
+  le.check();
+  hipError_t e = le.status();
   if (e != hipSuccess) return e;
 
   AllocParams ap;

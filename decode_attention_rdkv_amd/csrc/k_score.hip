@@ -521,47 +521,57 @@ ScoreArgs score_args(const ScoreParams& p, float lse_scale) {
   return ScoreArgs{p.n_tokens, p.Hq, p.Hkv, p.Hq / p.Hkv, p.Q, p.K, p.lse, p.w_tok, lse_scale};
 }
 
-void launch_pass1(const ScoreParams& p, float lse_scale, hipStream_t stream) {
+void launch_pass1(const ScoreParams& p, float lse_scale, hipStream_t stream, LaunchErrors& le) {
   const unsigned nb = unsigned(cdiv(p.n_tokens, kBlockRows));
   hipLaunchKernelGGL(score_lse_kernel, dim3(nb, unsigned(p.Hq), unsigned(int64_t(p.S) * p.L)), dim3(kThreads), 0,
                      stream, score_args(p, lse_scale));
+  le.check();
 }
 
 // Pass 2 from the base-2 LSE in p.lse, then var_tok and w_chan.
-hipError_t launch_rest(const ScoreParams& p, hipStream_t stream) {
+hipError_t launch_rest(const ScoreParams& p, hipStream_t stream, LaunchErrors& le) {
   const ScoreArgs a = score_args(p, 1.0f);
   const int64_t SL = int64_t(p.S) * p.L;
   const unsigned nb = unsigned(cdiv(p.n_tokens, kBlockRows));
   hipLaunchKernelGGL(score_colsum_kernel, dim3(nb, unsigned(p.Hkv), unsigned(SL)), dim3(kThreads), 0, stream, a);
+  le.check();
   const int64_t rows = SL * p.Hkv * p.n_tokens;
   hipLaunchKernelGGL(var_tok_kernel, dim3(unsigned(cdiv(rows, kThreads / 64))), dim3(kThreads), 0, stream, p.V,
                      p.var_tok, rows);
+  le.check();
   double* part = reinterpret_cast<double*>(reinterpret_cast<uint8_t*>(p.lse) +
                                            align_up(uint64_t(SL * p.Hq * p.n_tokens) * sizeof(float), kAlign));
   const int64_t n_seg = SL * p.Hkv;
   hipLaunchKernelGGL(chan_norm_partial_kernel, dim3(kNormSplits, unsigned(n_seg)), dim3(kThreads), 0, stream, a, part);
+  le.check();
   hipLaunchKernelGGL(chan_norm_final_kernel, dim3(unsigned(n_seg)), dim3(kHeadDim), 0, stream, part, p.w_chan);
-  return hipGetLastError();
+  le.check();
+  return le.status();
 }
 
 }  // namespace
 
 hipError_t launch_score(const ScoreParams& p, hipStream_t stream) {
-  launch_pass1(p, 1.0f, stream);
-  return launch_rest(p, stream);
+  LaunchErrors le;
+  launch_pass1(p, 1.0f, stream, le);
+  return launch_rest(p, stream, le);
 }
 
 hipError_t launch_score_lse(const ScoreParams& p, hipStream_t stream) {
-  launch_pass1(p, 0.69314718055994531f, stream);
-  return hipGetLastError();
+  LaunchErrors le;
+  launch_pass1(p, 0.69314718055994531f, stream, le);
+  return le.status();
 }
 
 hipError_t launch_score_from_lse(const ScoreParams& p, hipStream_t stream) {
+  LaunchErrors le;
   const int64_t n = int64_t(p.S) * p.L * p.Hq * p.n_tokens;
-  if (n > 0)
+  if (n > 0) {
     hipLaunchKernelGGL(lse_to_base2_kernel, dim3(unsigned(cdiv(n, kThreads))), dim3(kThreads), 0, stream, p.lse_in,
                        p.lse, n);
-  return launch_rest(p, stream);
+    le.check();
+  }
+  return launch_rest(p, stream, le);
 }
 
 }  // namespace rdkv

@@ -281,6 +281,20 @@ struct AllocParams {
   uint8_t* workspace;      // alloc_plan(n_seg, n_tokens, group).total bytes, 256-byte aligned
 };
 hipError_t launch_allocate(const AllocParams& p, hipStream_t stream);
+
+// The first error of a sequence of kernel launches: hipGetLastError after each
+// launch, since a later successful call can leave success as the last status.
+class LaunchErrors {
+ public:
+  void check() {
+    const hipError_t l = hipGetLastError();
+    if (e_ == hipSuccess) e_ = l;
+  }
+  hipError_t status() const { return e_; }
+
+ private:
+  hipError_t e_ = hipSuccess;
+};
 // The allocation's workspace: per group its radix-selection histogram and
 // state, per (segment, token block) the exact K sums; byte offsets.
 struct AllocPlan {
