@@ -11,6 +11,9 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: long CPU test")
+    # a NumPy deprecation inside the oracle would become an error in a later
+    # NumPy and take every pin with it: fail on it now
+    config.addinivalue_line("filterwarnings", "error::DeprecationWarning:oracle.*")
 
 
 @pytest.fixture(scope="session")
