@@ -422,6 +422,39 @@ def test_allocate_many_workgroups_bit_exact(gpu_lib, group, budget_avg, ties):
         assert np.all(bt == 16) and np.all(lam[:, 0] == 0.0)
 
 
+def test_allocate_reuses_a_dirty_workspace(gpu_lib):
+    """One caller workspace, filled with 0xFF first, serves three allocations
+    in a row (per segment, one budget per group of 2, then a smaller
+    problem): each is bit-exact against the oracle, so nothing depends on the
+    workspace's contents before a call (the histograms and selection states
+    are cleared by a kernel of the call itself)."""
+    rdkv = gpu_lib
+    S, L, Hkv = 1, 1, 2
+    ws = None
+    for N, group, seed in ((30000, 1, 81), (30000, 2, 82), (9000, 1, 83)):
+        n_seg = S * L * Hkv
+        w_tok, var_tok, w_chan = synth.random_unit_inputs(n_seg, N, seed=seed)
+        K, _ = synth.random_kv(n_seg, N, seed=seed + 100)
+        bv, bk = int(0.8 * N) * group, 100 * group
+        dims = rdkv.make_dims(S, L, 4 * Hkv, Hkv, N)
+        if ws is None:
+            size = max(rdkv.allocate_workspace_bytes(dims, 1), rdkv.allocate_workspace_bytes(dims, 2))
+            ws = torch.full((size,), 0xFF, dtype=torch.uint8, device=DEV)
+        assert ws.numel() >= rdkv.allocate_workspace_bytes(dims, group) > 0
+        shp = (S, L, Hkv)
+        bt, bc, vc, lam = (host(x) for x in rdkv.allocate_shared(
+            dims, dev(w_tok.reshape(shp + (N,))), dev(var_tok.reshape(shp + (N,))),
+            dev(w_chan.reshape(shp + (128,))), dev(K.reshape(shp + (N, 128))), bv, bk, group, workspace=ws))
+        bt, bc, vc, lam = bt.reshape(n_seg, N), bc.reshape(n_seg, 128), vc.reshape(n_seg, 128), lam.reshape(n_seg, 2)
+        for g0 in range(0, n_seg, group):
+            sl = slice(g0, g0 + group)
+            ref = O.allocate_group(w_tok[sl], var_tok[sl], w_chan[sl], K[sl], bv, bk)
+            assert np.array_equal(bt[sl], ref["bits_tok"]), f"N={N} group={group}: V bits differ"
+            assert np.all(lam[sl, 0] == ref["lambda_v"]) and np.all(lam[sl, 1] == ref["lambda_k"])
+            assert np.array_equal(vc[sl].view(np.uint32), ref["var_chan"].view(np.uint32))
+            assert np.array_equal(bc[sl], ref["bits_chan"])
+
+
 @pytest.mark.parametrize("group,budget_scale", [(1, 1.0), (2, 1.0), (4, 1.0), (8, 1.0), (4, 0.0), (8, 40.0)])
 def test_allocate_shared_bit_exact(gpu_lib, group, budget_scale):
     """One budget per group of consecutive segments (2 layers x 4 KV heads:
