@@ -67,11 +67,11 @@ static_assert((1 << sel_width(0)) == kSelBuckets && (1 << sel_width(1)) <= kSelB
 enum { kStAbove = 0, kStPrefix = 1, kStDone = 2, kStWords = 4 };
 
 struct SelArgs {
-  int64_t n;                   // units per group (group * N)
+  int64_t n;                   // units per group (group * N tokens, or group * 128 channels)
   int32_t blocks;              // workgroups per group
   int32_t pass;
-  const float* w_tok;
-  const float* var_tok;
+  const float* w;              // unit weights [groups][n]: w_tok, or w_chan
+  const float* sigma;          // unit variances [groups][n]: var_tok, or var_chan
   unsigned long long* hist;    // [groups][kSelBuckets]
   unsigned long long* state;   // [groups][kStWords]
 };
@@ -187,7 +187,7 @@ __global__ __launch_bounds__(kSelThreads) void sel_hist_kernel(SelArgs a) {
   __syncthreads();
   int64_t lo, hi;
   block_range(a.n, a.blocks, blk, lo, hi);
-  histogram_digit(a.w_tok + g * a.n, a.var_tok + g * a.n, lo, hi, a.pass, st[kStPrefix], s_hist);
+  histogram_digit(a.w + g * a.n, a.sigma + g * a.n, lo, hi, a.pass, st[kStPrefix], s_hist);
   __syncthreads();
   unsigned long long* gh = a.hist + g * kSelBuckets;
   for (int i = threadIdx.x; i < nb; i += kSelThreads)
@@ -210,7 +210,7 @@ __global__ __launch_bounds__(kSelThreads) void alloc_v_bits_kernel(SelArgs a, in
   const double lam = __longlong_as_double((long long)a.state[g * kStWords + kStPrefix]);
   int64_t lo, hi;
   block_range(a.n, a.blocks, blk, lo, hi);
-  write_bits(a.w_tok + g * a.n, a.var_tok + g * a.n, lo, hi, lam, bits_tok + g * a.n);
+  write_bits(a.w + g * a.n, a.sigma + g * a.n, lo, hi, lam, bits_tok + g * a.n);
   if (blk == 0)
     for (int s = threadIdx.x; s < group; s += kSelThreads) lambda[2 * (g * group + s)] = lam;
 }
@@ -224,8 +224,8 @@ __global__ __launch_bounds__(kSelThreads) void alloc_one_kernel(SelArgs a, int64
   __shared__ unsigned long long s_hist[kSelBuckets];
   __shared__ unsigned long long s_st[kStWords];
   const int64_t g = blockIdx.x;
-  const float* w = a.w_tok + g * a.n;
-  const float* v = a.var_tok + g * a.n;
+  const float* w = a.w + g * a.n;
+  const float* v = a.sigma + g * a.n;
   for (int i = threadIdx.x; i < kSelBuckets; i += kSelThreads) s_hist[i] = 0;
   if (threadIdx.x < kStWords) s_st[threadIdx.x] = 0;
   __syncthreads();
