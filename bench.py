@@ -448,8 +448,17 @@ def extras(rdkv, torch, w, lay, cache, kept, q, kn, vn, ref_out, steps, warmup, 
     bvs, bks = w.budget_v * Hkv, w.budget_k * Hkv
     pl, pc, used = build_paged(rdkv, torch, w, K, V, kept["bt_shared"], kept["bc_shared"], bvs, bks, seed=2)
     ws = rdkv.paged_decode_workspace(pl)
+    shape = rdkv.paged_decode_shape(pl, pc, ws)
+    pc_shaped = pc.clone()
+    out_shaped = torch.empty_like(out)
+    t_sh, tm_sh = time_calls(torch, lambda i: rdkv.paged_decode(pl, pc_shaped, [row(i)] * S, q, kn, vn, workspace=ws,
+                                                                out=out_shaped, shape=shape), steps, warmup, flush)
     t, tm = time_calls(torch, lambda i: rdkv.paged_decode(pl, pc, [row(i)] * S, q, kn, vn, workspace=ws, out=out),
                        steps, warmup, flush)
+    shaped_diff = float(((out_shaped.double() - out.double()).abs().amax(-1) /
+                         out.double().abs().amax(-1).clamp_min(1e-30)).max())
+    shaped_cache_same = bool(torch.equal(pc, pc_shaped))
+    del pc_shaped, out_shaped
     lay_shared = rdkv.layout(rdkv.make_dims(S, w.n_layers, w.n_q_heads, Hkv, w.n_tokens), bvs, bks, cap)
     res["shared_budget_paged"] = {
         "us_per_step": round(t * 1e3, 2), "us_per_step_median": round(tm * 1e3, 2),
@@ -461,9 +470,16 @@ def extras(rdkv, torch, w, lay, cache, kept, q, kn, vn, ref_out, steps, warmup, 
         "resident_vs_per_segment_blob": round((pl.pool_offset + used * rdkv.PAGE_BYTES) / lay.cache_bytes, 4),
         "chunks": chunk_stats(pl.chunk_tok2, pl.token_slots, rdkv.descriptors(lay, pc)),
         "record_words": record_stats(pl.rec_max, rdkv.descriptors(lay, pc)),
+        "shaped": {"us_per_step": round(t_sh * 1e3, 2), "us_per_step_median": round(tm_sh * 1e3, 2),
+                   "achieved_GBs": round(algo_bytes(pc) / (t_sh * 1e-3) / 1e9, 1),
+                   "token_slots": int(shape.token_slots), "record_words": int(shape.rec_max) // 4,
+                   "max_rel_diff_vs_unshaped": shaped_diff, "cache_identical_to_unshaped": shaped_cache_same,
+                   "note": "rdkv_paged_decode_shaped with the shape rdkv_paged_decode_shape measured on the "
+                           "sequences in use: chunk slots and record ring from the segments, not the bounds"},
         "note": "rdkv_allocate_shared with one budget per layer (its KV heads' budgets pooled), packed on pages: "
                 "memory follows what each segment keeps instead of a slot sized for the whole layer's budget"}
-    log(f"shared budget on pages: {t * 1e3:.1f} us per step, {used} pages")
+    log(f"shared budget on pages: {t * 1e3:.1f} us per step ({t_sh * 1e3:.1f} with the measured shape), "
+        f"{used} pages")
     del pc, ws
     torch.cuda.empty_cache()
 

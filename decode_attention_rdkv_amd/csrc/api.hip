@@ -681,9 +681,15 @@ rdkv_status rdkv_paged_release(const rdkv_paged_layout* layout, int32_t seq, voi
   return hip_status(launch_paged_release(static_cast<uint8_t*>(cache), *layout, seq, stream));
 }
 
-rdkv_status rdkv_paged_decode(const rdkv_paged_layout* layout, void* cache, size_t cache_bytes,
-                              const int32_t* c_len, const void* q, const void* k_new, const void* v_new,
-                              float* out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// One paged decode step with the launch shape (prefill chunk slots, record
+// bound) of the layout or of a rdkv_paged_decode_shape result.
+rdkv_status paged_decode(const rdkv_paged_layout* layout, const rdkv_paged_shape* shape, void* cache,
+                         size_t cache_bytes, const int32_t* c_len, const void* q, const void* k_new, const void* v_new,
+                         float* out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   rdkv_status st = check_paged(layout);
   if (st != RDKV_OK) return st;
   if (!cache || !c_len || !q || !out || !workspace) return RDKV_ERR_NULL;
@@ -691,8 +697,19 @@ rdkv_status rdkv_paged_decode(const rdkv_paged_layout* layout, void* cache, size
   for (const void* ptr : {(const void*)cache, q, (const void*)out, (const void*)workspace})
     if (!aligned16(ptr)) return RDKV_ERR_ALIGN;
   if (k_new && (!aligned16(k_new) || !aligned16(v_new))) return RDKV_ERR_ALIGN;
-  if (cache_bytes < layout->cache_bytes || workspace_bytes < layout->decode_workspace_bytes)
-    return RDKV_ERR_WORKSPACE;
+  const int G = layout->dims.n_q_heads / layout->dims.n_kv_heads;
+  const int zc_slots = layout->max_chunks - layout->token_slots;
+  int32_t token_slots = layout->token_slots, rec_max = layout->rec_max;
+  if (shape) {
+    if (shape->reserved != 0 || shape->token_slots < 0 || shape->token_slots > layout->token_slots ||
+        shape->rec_max < 0 || shape->rec_max > layout->rec_max || shape->rec_max % 4 != 0)
+      return RDKV_ERR_SHAPE;
+    token_slots = shape->token_slots;
+    rec_max = shape->rec_max;
+  }
+  const int32_t max_chunks = token_slots + zc_slots;
+  const uint64_t ws_need = uint64_t(layout->n_seg) * max_chunks * G * kPartialFloats * sizeof(float);
+  if (cache_bytes < layout->cache_bytes || workspace_bytes < ws_need) return RDKV_ERR_WORKSPACE;
   const int append = k_new != nullptr;
   PagedSeqLens lens;
   std::memset(&lens, 0, sizeof(lens));
@@ -706,11 +723,11 @@ rdkv_status rdkv_paged_decode(const rdkv_paged_layout* layout, void* cache, size
   p.main_bytes = layout->cache_bytes;
   p.n_seg = layout->n_seg;
   p.nk_max = layout->nk_max;
-  p.max_chunks = layout->max_chunks;
-  p.token_slots = layout->token_slots;
+  p.max_chunks = max_chunks;
+  p.token_slots = token_slots;
   p.chunk_tok2 = layout->chunk_tok2;
-  p.rec_max = layout->rec_max;
-  p.group = layout->dims.n_q_heads / layout->dims.n_kv_heads;
+  p.rec_max = rec_max;
+  p.group = G;
   p.zc_cap = layout->zone_c_capacity;
   p.append = append;
   p.q = static_cast<const __half*>(q);
@@ -726,7 +743,53 @@ rdkv_status rdkv_paged_decode(const rdkv_paged_layout* layout, void* cache, size
   p.pool_offset = layout->pool_offset;
   hipError_t e = launch_decode_chunks_paged(p, lens, stream);
   if (e == hipSuccess) e = launch_decode_merge(p, stream);
+  if (e == hipSuccess && shape)
+    e = launch_paged_shape_check(p.cache, *layout, token_slots, rec_max, out, stream);
   return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+rdkv_status rdkv_paged_decode(const rdkv_paged_layout* layout, void* cache, size_t cache_bytes,
+                              const int32_t* c_len, const void* q, const void* k_new, const void* v_new,
+                              float* out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return paged_decode(layout, nullptr, cache, cache_bytes, c_len, q, k_new, v_new, out, workspace, workspace_bytes,
+                      stream);
+}
+
+rdkv_status rdkv_paged_decode_shape(const rdkv_paged_layout* layout, const void* cache, size_t cache_bytes,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                    rdkv_paged_shape* out) {
+  rdkv_status st = check_paged(layout);
+  if (st != RDKV_OK) return st;
+  if (!cache || !workspace || !out) return RDKV_ERR_NULL;
+  if (!aligned16(cache) || !aligned16(workspace)) return RDKV_ERR_ALIGN;
+  if (cache_bytes < layout->cache_bytes || workspace_bytes < 8) return RDKV_ERR_WORKSPACE;
+  int32_t* dev = static_cast<int32_t*>(workspace);
+  hipError_t e = launch_paged_shape_scan(static_cast<const uint8_t*>(cache), *layout, dev, stream);
+  int32_t host[2] = {0, 0};
+  if (e == hipSuccess) e = hipMemcpyAsync(host, dev, sizeof(host), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_status(e);
+  const int G = layout->dims.n_q_heads / layout->dims.n_kv_heads;
+  rdkv_paged_shape sh{};
+  sh.token_slots = std::min(host[0], layout->token_slots);
+  sh.rec_max = std::min((host[1] + 3) / 4 * 4, layout->rec_max);
+  sh.max_chunks = sh.token_slots + (layout->max_chunks - layout->token_slots);
+  sh.decode_workspace_bytes = uint64_t(layout->n_seg) * sh.max_chunks * G * kPartialFloats * sizeof(float);
+  *out = sh;
+  return RDKV_OK;
+}
+
+rdkv_status rdkv_paged_decode_shaped(const rdkv_paged_layout* layout, const rdkv_paged_shape* shape, void* cache,
+                                     size_t cache_bytes, const int32_t* c_len, const void* q, const void* k_new,
+                                     const void* v_new, float* out, void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream) {
+  if (!shape) return RDKV_ERR_NULL;
+  return paged_decode(layout, shape, cache, cache_bytes, c_len, q, k_new, v_new, out, workspace, workspace_bytes,
+                      stream);
 }
 
 rdkv_status rdkv_unpack(const rdkv_layout* layout, const void* cache, size_t cache_bytes, int64_t seg,

@@ -664,6 +664,71 @@ __global__ __launch_bounds__(256) void paged_release_kernel(uint8_t* cache, rdkv
   if (threadIdx.x < kDescBytes / 4) st_u32(cache + kHeaderBytes + uint64_t(seg) * kDescBytes, 4 * threadIdx.x, 0u);
 }
 
+// ---------------------------------------------------------------- decode shape (paged)
+
+// A segment in use (a committed slot: zone-C capacity of the layout) and its
+// prefill-token chunk count and K record bytes, as decode counts them; -1
+// chunks for a free or damaged slot.
+struct SegShape {
+  int chunks, rec;
+};
+__device__ inline SegShape seg_shape(const uint8_t* cache, const rdkv_paged_layout& pl, int64_t seg) {
+  const uint8_t* d = cache + kHeaderBytes + uint64_t(seg) * kDescBytes;
+  SegShape r{-1, 0};
+  if (*reinterpret_cast<const int32_t*>(d + kDescCap) != pl.zone_c_capacity) return r;
+  int chunks = 0;
+  for (int i = 0; i < 4; ++i) {
+    const int n = *reinterpret_cast<const int32_t*>(d + kDescNTok + 4 * i);
+    if (n < 0) return r;
+    chunks += (n + chunk_tokens(pl.chunk_tok2, i) - 1) >> chunk_shift(pl.chunk_tok2, i);
+  }
+  const int rec = *reinterpret_cast<const int32_t*>(d + kDescRec);
+  if (rec < 0 || rec > pl.rec_max || chunks > pl.token_slots) return r;
+  r.chunks = chunks;
+  r.rec = rec;
+  return r;
+}
+
+// The most chunks and record bytes over the segments in use (out[0], out[1],
+// zero on entry).
+__global__ __launch_bounds__(256) void paged_shape_scan_kernel(const uint8_t* cache, rdkv_paged_layout pl,
+                                                               int32_t* out) {
+  int c = 0, r = 0;
+  for (int64_t seg = int64_t(blockIdx.x) * 256 + threadIdx.x; seg < pl.n_seg; seg += int64_t(gridDim.x) * 256) {
+    const SegShape sh = seg_shape(cache, pl, seg);
+    if (sh.chunks < 0) continue;
+    c = max(c, sh.chunks);
+    r = max(r, sh.rec);
+  }
+  c = max(c, __shfl_xor(c, 32, 64));
+  r = max(r, __shfl_xor(r, 32, 64));
+  for (int x = 16; x >= 1; x >>= 1) {
+    c = max(c, __shfl_xor(c, x, 64));
+    r = max(r, __shfl_xor(r, x, 64));
+  }
+  if ((threadIdx.x & 63) == 0) {
+    atomicMax(&out[0], c);
+    atomicMax(&out[1], r);
+  }
+}
+
+__global__ __launch_bounds__(64) void zero_words_kernel(int32_t* p, int n) {
+  if (int(threadIdx.x) < n) p[threadIdx.x] = 0;
+}
+
+// After a decode with a shape: the outputs of every segment in use that the
+// shape does not cover (more chunks or longer records than it allows, so the
+// decode read it as empty) are set to NaN.
+__global__ __launch_bounds__(256) void paged_shape_check_kernel(const uint8_t* cache, rdkv_paged_layout pl,
+                                                                int32_t token_slots, int32_t rec_max, float* out) {
+  const int G = pl.dims.n_q_heads / pl.dims.n_kv_heads;
+  for (int64_t seg = blockIdx.x; seg < pl.n_seg; seg += gridDim.x) {
+    const SegShape sh = seg_shape(cache, pl, seg);
+    if (sh.chunks < 0 || (sh.chunks <= token_slots && sh.rec <= rec_max)) continue;   // (uniform)
+    for (int i = threadIdx.x; i < G * kHeadDim; i += 256) out[seg * G * kHeadDim + i] = __builtin_nanf("");
+  }
+}
+
 }  // namespace
 
 hipError_t launch_paged_init(uint8_t* cache, const rdkv_paged_layout& pl, hipStream_t stream) {
@@ -740,6 +805,25 @@ hipError_t launch_unpack(const uint8_t* cache, uint64_t, const rdkv_layout& lay,
   (void)lay;
   UnpackArgs ua{cache, seg, k_hat, v_hat};
   hipLaunchKernelGGL(unpack_kernel, dim3(64), dim3(256), 0, stream, ua);
+  return hipGetLastError();
+}
+
+hipError_t launch_paged_shape_scan(const uint8_t* cache, const rdkv_paged_layout& pl, int32_t* out,
+                                   hipStream_t stream) {
+  LaunchErrors le;
+  hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(64), 0, stream, out, 2);
+  le.check();
+  const unsigned grid = unsigned(std::min<int64_t>(cdiv(pl.n_seg, 256), 1024));
+  hipLaunchKernelGGL(paged_shape_scan_kernel, dim3(grid), dim3(256), 0, stream, cache, pl, out);
+  le.check();
+  return le.status();
+}
+
+hipError_t launch_paged_shape_check(const uint8_t* cache, const rdkv_paged_layout& pl, int32_t token_slots,
+                                    int32_t rec_max, float* out, hipStream_t stream) {
+  const unsigned grid = unsigned(std::min<int64_t>(pl.n_seg, 4096));
+  hipLaunchKernelGGL(paged_shape_check_kernel, dim3(grid), dim3(256), 0, stream, cache, pl, token_slots, rec_max,
+                     out);
   return hipGetLastError();
 }
 

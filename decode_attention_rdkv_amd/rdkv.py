@@ -52,6 +52,11 @@ class PagedLayout(ctypes.Structure):
         return self.dims.n_q_heads // self.dims.n_kv_heads
 
 
+class PagedShape(ctypes.Structure):
+    _fields_ = [("token_slots", c_i32), ("rec_max", c_i32), ("max_chunks", c_i32), ("reserved", c_i32),
+                ("decode_workspace_bytes", c_u64)]
+
+
 STATUS = ["RDKV_OK", "RDKV_ERR_NULL", "RDKV_ERR_SHAPE", "RDKV_ERR_UNSUPPORTED", "RDKV_ERR_BUDGET",
           "RDKV_ERR_ALIGN", "RDKV_ERR_WORKSPACE", "RDKV_ERR_CAPACITY", "RDKV_ERR_HIP", "RDKV_ERR_OVERFLOW"]
 RDKV_ERR_OVERFLOW = 9
@@ -100,6 +105,11 @@ SIGNATURES = {
     "rdkv_paged_release": (c_i32, [ctypes.POINTER(PagedLayout), c_i32, c_vp, ctypes.c_size_t, c_vp]),
     "rdkv_paged_decode": (c_i32, [ctypes.POINTER(PagedLayout), c_vp, ctypes.c_size_t, ctypes.POINTER(c_i32), c_vp,
                                   c_vp, c_vp, c_vp, c_vp, ctypes.c_size_t, c_vp]),
+    "rdkv_paged_decode_shape": (c_i32, [ctypes.POINTER(PagedLayout), c_vp, ctypes.c_size_t, c_vp, ctypes.c_size_t,
+                                        c_vp, ctypes.POINTER(PagedShape)]),
+    "rdkv_paged_decode_shaped": (c_i32, [ctypes.POINTER(PagedLayout), ctypes.POINTER(PagedShape), c_vp,
+                                         ctypes.c_size_t, ctypes.POINTER(c_i32), c_vp, c_vp, c_vp, c_vp, c_vp,
+                                         ctypes.c_size_t, c_vp]),
     "rdkv_unpack": (c_i32, [ctypes.POINTER(Layout), c_vp, ctypes.c_size_t, c_i64, c_vp, c_vp, c_vp]),
 }
 
@@ -513,10 +523,24 @@ def paged_decode_workspace(pl: PagedLayout, device="cuda") -> torch.Tensor:
     return torch.empty(max(int(pl.decode_workspace_bytes), 16), dtype=torch.uint8, device=device)
 
 
+def paged_decode_shape(pl: PagedLayout, cache: torch.Tensor, workspace: Optional[torch.Tensor] = None) -> PagedShape:
+    """The decode launch shape of the slots in use (synchronous: reads the device)."""
+    if workspace is None:
+        workspace = torch.empty(16, dtype=torch.uint8, device=cache.device)
+    out = PagedShape()
+    _check(load().rdkv_paged_decode_shape(ctypes.byref(pl), _ptr(cache, torch.uint8, None, "cache"), cache.numel(),
+                                          _ptr(workspace, torch.uint8, None, "workspace"), workspace.numel(),
+                                          _stream(), ctypes.byref(out)),
+           "rdkv_paged_decode_shape")
+    return out
+
+
 def paged_decode(pl: PagedLayout, cache: torch.Tensor, c_len, q, k_new=None, v_new=None,
-                 workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                 workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                 shape: Optional[PagedShape] = None) -> torch.Tensor:
     """One decode step over every sequence slot; c_len: host sequence of the
-    slots' zone-C rows before the step.  Returns out fp32 [S][L][Hq][128]."""
+    slots' zone-C rows before the step.  With `shape` (paged_decode_shape),
+    rdkv_paged_decode_shaped.  Returns out fp32 [S][L][Hq][128]."""
     d = pl.dims
     S, L, Hq, Hk = d.n_seq, d.n_layers, d.n_q_heads, d.n_kv_heads
     cl = (c_i32 * S)(*[int(x) for x in c_len])
@@ -524,13 +548,17 @@ def paged_decode(pl: PagedLayout, cache: torch.Tensor, c_len, q, k_new=None, v_n
         workspace = paged_decode_workspace(pl, q.device)
     if out is None:
         out = torch.empty((S, L, Hq, HEAD_DIM), dtype=torch.float32, device=q.device)
-    _check(load().rdkv_paged_decode(ctypes.byref(pl), _ptr(cache, torch.uint8, None, "cache"), cache.numel(), cl,
-                                    _ptr(q, torch.float16, (S, L, Hq, HEAD_DIM), "q"),
-                                    _ptr(k_new, torch.float16, (S, L, Hk, HEAD_DIM), "k_new"),
-                                    _ptr(v_new, torch.float16, (S, L, Hk, HEAD_DIM), "v_new"),
-                                    _ptr(out, torch.float32, (S, L, Hq, HEAD_DIM), "out"),
-                                    _ptr(workspace, torch.uint8, None, "workspace"), workspace.numel(), _stream()),
-           "rdkv_paged_decode")
+    args = (_ptr(cache, torch.uint8, None, "cache"), cache.numel(), cl,
+            _ptr(q, torch.float16, (S, L, Hq, HEAD_DIM), "q"),
+            _ptr(k_new, torch.float16, (S, L, Hk, HEAD_DIM), "k_new"),
+            _ptr(v_new, torch.float16, (S, L, Hk, HEAD_DIM), "v_new"),
+            _ptr(out, torch.float32, (S, L, Hq, HEAD_DIM), "out"),
+            _ptr(workspace, torch.uint8, None, "workspace"), workspace.numel(), _stream())
+    if shape is None:
+        _check(load().rdkv_paged_decode(ctypes.byref(pl), *args), "rdkv_paged_decode")
+    else:
+        _check(load().rdkv_paged_decode_shaped(ctypes.byref(pl), ctypes.byref(shape), *args),
+               "rdkv_paged_decode_shaped")
     return out
 
 

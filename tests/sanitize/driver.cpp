@@ -155,6 +155,21 @@ void paged(const rdkv_paged_layout& pl) {
          "paged decode negative length");
   EXPECT(rdkv_paged_decode(&pl, D, cb, nullptr, D, nullptr, nullptr, F(D), D, wb, nullptr) == RDKV_ERR_NULL,
          "paged decode null lengths");
+  {
+    c_len[pl.dims.n_seq - 1] = 0;
+    rdkv_paged_shape sh{};
+    EXPECT(ok_or_hip(rdkv_paged_decode_shape(&pl, D, cb, D, wb, nullptr, &sh)), "decode shape");
+    EXPECT(rdkv_paged_decode_shape(&pl, D, cb, D, 4, nullptr, &sh) == RDKV_ERR_WORKSPACE, "decode shape workspace");
+    sh = rdkv_paged_shape{pl.token_slots, pl.rec_max, pl.max_chunks, 0, 0};
+    EXPECT(ok_or_hip(rdkv_paged_decode_shaped(&pl, &sh, D, cb, c_len, D, D, D, F(D), D, wb, nullptr)),
+           "shaped decode");
+    sh.token_slots = pl.token_slots + 1;
+    EXPECT(rdkv_paged_decode_shaped(&pl, &sh, D, cb, c_len, D, D, D, F(D), D, wb, nullptr) == RDKV_ERR_SHAPE,
+           "shaped decode past the bounds");
+    sh = rdkv_paged_shape{0, 0, 0, 0, 0};
+    EXPECT(ok_or_hip(rdkv_paged_decode_shaped(&pl, &sh, D, cb, c_len, D, D, D, F(D), D, wb, nullptr)),
+           "shaped decode, no prefill chunks");
+  }
   for (size_t i = 0; i < sizeof(rdkv_paged_layout); i += 4) {
     rdkv_paged_layout bad = pl;
     reinterpret_cast<unsigned char*>(&bad)[i] ^= 0x21;
@@ -205,6 +220,9 @@ void fuzz(unsigned seed, int rounds) {
       int32_t c_len[RDKV_MAX_PAGED_SEQS];
       for (int k = 0; k < RDKV_MAX_PAGED_SEQS; ++k) c_len[k] = pick32(600);
       (void)rdkv_paged_decode(&pl, D, pl.cache_bytes, c_len, D, D, D, F(D), D, pl.decode_workspace_bytes, nullptr);
+      const rdkv_paged_shape sh{pick32(pl.token_slots + 2), pick32(pl.rec_max + 8) & ~3, 0, 0, 0};
+      (void)rdkv_paged_decode_shaped(&pl, &sh, D, pl.cache_bytes, c_len, D, D, D, F(D), D,
+                                     pl.decode_workspace_bytes, nullptr);
     }
   }
   std::printf("fuzz seed %u: %d rounds, %d layouts accepted\n", seed, rounds, accepted);

@@ -334,6 +334,38 @@ def test_paged_layout_matches_oracle(shape):
         assert (pl.max_chunks, pl.token_slots) == (flat.max_chunks, flat.token_slots)
 
 
+def test_paged_shape_validation(lib):
+    """The decode-shape entry points reject missing arguments, a workspace
+    too small for the shape, and a shape outside the layout's bounds, before
+    anything is enqueued."""
+    d = rdkv.make_dims(3, 2, 8, 2, 300)
+    pl = rdkv.paged_layout(d, 600, 256, 32, 50)
+    nb, ws = pl.cache_bytes, pl.decode_workspace_bytes
+    out = rdkv.PagedShape()
+    assert lib.rdkv_paged_decode_shape(ctypes.byref(pl), None, nb, A, 8, None, ctypes.byref(out)) == NULL
+    assert lib.rdkv_paged_decode_shape(ctypes.byref(pl), A, nb, A, 8, None, None) == NULL
+    assert lib.rdkv_paged_decode_shape(ctypes.byref(pl), A, nb, A, 4, None, ctypes.byref(out)) == WORKSPACE
+    assert lib.rdkv_paged_decode_shape(ctypes.byref(pl), A, nb - 1, A, 8, None, ctypes.byref(out)) == WORKSPACE
+    assert lib.rdkv_paged_decode_shape(ctypes.byref(pl), A + 4, nb, A, 8, None, ctypes.byref(out)) == ALIGN
+    c_len = (ctypes.c_int32 * 3)(0, 0, 0)
+
+    def shaped(sh, ws_bytes=ws):
+        return lib.rdkv_paged_decode_shaped(ctypes.byref(pl), sh, A, nb, c_len, A, None, None, A, A, ws_bytes, None)
+
+    assert shaped(None) == NULL
+    G, zc = 4, pl.max_chunks - pl.token_slots
+    for ts, rec, res, status in ((pl.token_slots + 1, 0, 0, SHAPE), (-1, 0, 0, SHAPE), (1, pl.rec_max + 4, 0, SHAPE),
+                                 (1, 6, 0, SHAPE), (1, 4, 1, SHAPE)):
+        sh = rdkv.PagedShape(ts, rec, ts + zc, res, 0)
+        assert shaped(ctypes.byref(sh)) == status, (ts, rec, res)
+    # a smaller shape needs a smaller workspace: its own size passes validation
+    # (and then fails only at the launch, on a machine without a GPU)
+    sh = rdkv.PagedShape(1, 4, 1 + zc, 0, 0)
+    need = pl.n_seg * (1 + zc) * G * 132 * 4
+    assert shaped(ctypes.byref(sh), need - 1) == WORKSPACE
+    assert shaped(ctypes.byref(sh), need) == HIP
+
+
 def test_paged_validation(lib):
     d = rdkv.make_dims(3, 2, 8, 2, 300)
     pl = rdkv.paged_layout(d, 600, 256, 32, 50)

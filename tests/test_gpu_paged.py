@@ -227,3 +227,97 @@ def test_paged_decode_mixed_record_lengths(rdkv):
         assert e <= TOL, f"step {step}: rel err {e:.3g}"
         c_len = [c + 1 for c in c_len]
     _same_bytes(cache, oblob, "after decode steps")
+
+
+def _seg_shapes(pl, cache):
+    """Per segment in use (zone-C capacity of the layout; None for a free
+    slot), from its descriptor on the host: prefill-token chunks
+    (chunk_tok2 >> g tokens of group g) and K record bytes."""
+    ints = host(cache)[256:256 + 256 * pl.n_seg].reshape(pl.n_seg, 256).view(np.int32)
+    out = []
+    for seg in range(pl.n_seg):
+        if ints[seg, 10] != pl.zone_c_capacity:
+            out.append(None)
+            continue
+        n_tok = ints[seg, 0:4]
+        out.append((sum(-(-int(n) // (pl.chunk_tok2 >> g)) for g, n in enumerate(n_tok)), int(ints[seg, 9])))
+    return out
+
+
+def _host_shape(pl, cache):
+    """The most chunks and the longest record over the segments in use."""
+    used = [x for x in _seg_shapes(pl, cache) if x is not None]
+    return max(c for c, _ in used), max(r for _, r in used)
+
+
+@pytest.mark.parametrize("G", [4, 8])
+def test_shaped_decode_follows_the_sequences_in_use(rdkv, G):
+    """A pool laid out for loose bounds (a segment may hold 16,000 V bits and
+    1,024 K bits) holding sequences that use far less: the measured shape
+    matches the descriptors, launches fewer chunk slots and a smaller record
+    ring, and decodes bit for bit like the layout's shape (appends included),
+    within 2e-3 of the oracle.  A later, larger sequence that the old shape
+    does not cover gets NaN outputs from it; a new shape covers it again.
+    The two launches merge the same chunk partials in the same order; only
+    the zone-C chunk sits at another slot, so the wave sum of the softmax
+    denominators may round differently: outputs agree within 1e-6, the caches
+    byte for byte."""
+    S, L, Hkv, N, cap, n_pages = 3, 2, 2, 3000, 24, 2000
+    Hq = G * Hkv
+    bv, bk = 16000, 1024
+    pl = rdkv.paged_layout(rdkv.make_dims(S, L, Hq, Hkv, N), bv, bk, cap, n_pages)
+    op = O.PagedLayout(S, L, Hq, Hkv, N, bv, bk, cap, n_pages)
+    cache = rdkv.paged_cache_init(pl)
+    oblob = O.paged_empty(op)
+    pool = Pool(n_pages, 5)
+    for s, seed in ((0, 201), (1, 202)):
+        _add(rdkv, pl, cache, oblob, op, pool, s, (N, 2500, 120), _sequence(L, Hkv, N, 2500, 120, seed))
+    _same_bytes(cache, oblob, "after commits")
+    shape = rdkv.paged_decode_shape(pl, cache)
+    chunks, rec = _host_shape(pl, cache)
+    assert (shape.token_slots, shape.rec_max) == (chunks, -(-rec // 4) * 4)
+    assert shape.max_chunks == chunks + pl.max_chunks - pl.token_slots
+    assert shape.token_slots < pl.token_slots and shape.rec_max < pl.rec_max
+    assert shape.decode_workspace_bytes < pl.decode_workspace_bytes
+    other = cache.clone()
+    ws = rdkv.paged_decode_workspace(pl)
+    ws_shape = torch.empty(int(shape.decode_workspace_bytes), dtype=torch.uint8, device=DEV)
+    r = np.random.default_rng(17)
+    c_len = [0, 0, 0]
+    for step in range(3):
+        q = r.standard_normal((S, L, Hq, 128)).astype(np.float16)
+        kn = r.standard_normal((S, L, Hkv, 128)).astype(np.float16)
+        vn = r.standard_normal((S, L, Hkv, 128)).astype(np.float16)
+        got = host(rdkv.paged_decode(pl, cache, c_len, dev(q), dev(kn), dev(vn), workspace=ws_shape, shape=shape))
+        want = host(rdkv.paged_decode(pl, other, c_len, dev(q), dev(kn), dev(vn), workspace=ws))
+        assert rel_err(got, want) <= 1e-6, f"step {step}: shaped and unshaped decode differ"
+        ref = O.paged_decode_step(oblob, op, q, c_len, kn, vn)
+        assert rel_err(got[:2], ref[:2]) <= TOL
+        c_len = [c + 1 if s < 2 else 0 for s, c in enumerate(c_len)]
+    assert torch.equal(cache, other)
+    # a larger sequence in slot 2, outside the old shape
+    big = _sequence(L, Hkv, N, 12000, 700, 203)
+    for c in (cache, other):
+        staging, need = rdkv.paged_stage(pl, N, 12000, 700, dev(big[0]), dev(big[1]), dev(big[2]), dev(big[3]))
+        pages = [pool.take(int(k)) for k in host(need)]
+        table = np.full((len(pages), pl.max_pages), -1, np.int32)
+        for i, pg in enumerate(pages):
+            table[i, :len(pg)] = pg
+        rdkv.paged_commit(pl, c, 2, N, 12000, 700, staging, dev(table))
+    chunks2, rec2 = _host_shape(pl, cache)
+    assert chunks2 > shape.token_slots or rec2 > shape.rec_max
+    q = r.standard_normal((S, L, Hq, 128)).astype(np.float16)
+    want = host(rdkv.paged_decode(pl, other, c_len, dev(q), workspace=ws))
+    stale = host(rdkv.paged_decode(pl, cache, c_len, dev(q), workspace=ws_shape, shape=shape))
+    assert rel_err(stale[:2], want[:2]) <= 1e-6
+    for i, sh in enumerate(_seg_shapes(pl, cache)[2 * L * Hkv:]):
+        l, h = divmod(i, Hkv)
+        rows = stale[2, l, h * G:(h + 1) * G]
+        if sh[0] > shape.token_slots or sh[1] > shape.rec_max:
+            assert np.isnan(rows).all(), f"segment {i} of slot 2 outside the shape"
+        else:
+            assert rel_err(rows, want[2, l, h * G:(h + 1) * G]) <= 1e-6
+    shape2 = rdkv.paged_decode_shape(pl, cache)
+    assert (shape2.token_slots, shape2.rec_max) == (chunks2, -(-rec2 // 4) * 4)
+    ws2 = torch.empty(int(shape2.decode_workspace_bytes), dtype=torch.uint8, device=DEV)
+    assert rel_err(host(rdkv.paged_decode(pl, cache, c_len, dev(q), workspace=ws2, shape=shape2)), want) <= 1e-6
