@@ -598,6 +598,63 @@ def cpu_baseline_all_stages(name: str = "tiny-gqa4-n1k"):
                        f"{w.decode_steps} decode steps): scoring, allocation, packing and decode, single-threaded")
 
 
+def cpu_baseline_c2_all_stages(decode_steps_sample: int = 4):
+    """Every stage of the oracle on the single 32K layer (8 KV heads, 32 query
+    heads, 32,768 tokens, 64 decode steps), single-threaded, within a bounded
+    time: the token weights of one KV head timed on the first 8,192 rows and
+    scaled by the causal score count and the 8 heads; channel weights and
+    token variances in full; the allocation of every head in full, on seeded
+    weights of the workload's shape (the scored weights would take the full
+    scoring first); the packed blob in full; decode_steps_sample decode steps
+    with appends, scaled to the workload's 64."""
+    import oracle as O
+    from decode_attention_rdkv_amd import synth
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:
+        threadpool_limits = None
+    w = synth.WORKLOADS["llama8b-layer-n32k"]
+    G, N, H = w.group, w.n_tokens, w.n_kv_heads
+    t = {}
+    score_one = cpu_scoring_baseline(w)["value"]
+    Q, K, V = synth.prefill_layer(w, 0, 0)
+    w_tok, var_tok, w_chan = synth.random_unit_inputs(H, N, seed=2)
+    lay = O.Layout(1, 1, w.n_q_heads, H, 128, N, w.budget_v, w.budget_k, w.zone_c_capacity)
+    ctx = threadpool_limits(1) if threadpool_limits else None
+    if ctx:
+        ctx.__enter__()
+    try:
+        t0 = time.perf_counter()
+        for h in range(H):
+            O.channel_weights(Q[h * G:(h + 1) * G], K[h])
+            O.token_variance(V[h])
+        t["score"] = score_one * H + time.perf_counter() - t0
+        t0 = time.perf_counter()
+        bts, bcs = [], []
+        for h in range(H):
+            a = O.allocate_segment(w_tok[h], var_tok[h], w_chan[h], K[h], w.budget_v, w.budget_k)
+            bts.append(a["bits_tok"])
+            bcs.append(a["bits_chan"])
+        t["allocate"] = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        blob = O.pack_cache(lay, K[None, None], V[None, None], np.stack(bts)[None, None], np.stack(bcs)[None, None])
+        t["pack"] = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        for step in range(decode_steps_sample):
+            q, kn, vn = synth.decode_inputs(w, step)
+            O.decode_step(blob, lay, q, step, kn, vn)
+        t["decode"] = (time.perf_counter() - t0) * w.decode_steps / decode_steps_sample
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    return dict(value=round(sum(t.values()), 1), unit="s", cores=1, kind="oracle",
+                stages_s={k: round(v, 2) for k, v in t.items()},
+                sample=f"llama8b-layer-n32k ({H} KV heads, {w.n_q_heads} query heads, {N} tokens, {w.decode_steps} "
+                       f"decode steps): token weights of one KV head on the first 8,192 rows scaled by (N/8192)^2 "
+                       f"and {H} heads; allocation (on seeded weights of the same shape) and packing in full; "
+                       f"{decode_steps_sample} decode steps scaled to {w.decode_steps}; single-threaded")
+
+
 def host_info():
     """What the host offers the oracle: cores, the cores this process may use,
     and numpy's BLAS threads (the timed oracle runs are limited to one)."""
@@ -895,6 +952,9 @@ def main():
         t0 = time.time()
         result["cpu_baseline_tiny_all_stages"] = cpu_baseline_all_stages()
         log(f"cpu all-stage baseline (tiny workload) {time.time() - t0:.1f}s")
+        t0 = time.time()
+        result["cpu_baseline_32k_layer_all_stages"] = cpu_baseline_c2_all_stages()
+        log(f"cpu all-stage baseline (32K layer, sampled) {time.time() - t0:.1f}s")
     print(json.dumps(result), flush=True)
 
 
