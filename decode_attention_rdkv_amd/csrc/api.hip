@@ -107,15 +107,15 @@ RolloverParams rollover_params(const rdkv_layout& lay, void* cache, float* zc_st
 // arguments are not checked.
 rdkv_status decode_params(const rdkv_layout* layout, void* cache, size_t cache_bytes, int32_t c_len, const void* q,
                           const void* k_new, const void* v_new, void* workspace, size_t workspace_bytes,
-                          DecodeParams* out, bool own_workspace = false) {
+                          DecodeParams* out, bool own_workspace = false, uint64_t workspace_need = ~uint64_t(0)) {
   rdkv_status st = check_layout(layout);
   if (st != RDKV_OK) return st;
   if (!cache || !q || (!workspace && !own_workspace)) return RDKV_ERR_NULL;
   if ((k_new == nullptr) != (v_new == nullptr)) return RDKV_ERR_NULL;
   if (!aligned16(cache) || !aligned16(q) || (!own_workspace && !aligned16(workspace))) return RDKV_ERR_ALIGN;
   if (k_new && (!aligned16(k_new) || !aligned16(v_new))) return RDKV_ERR_ALIGN;
-  if (cache_bytes < layout->cache_bytes || (!own_workspace && workspace_bytes < layout->decode_workspace_bytes))
-    return RDKV_ERR_WORKSPACE;
+  const uint64_t ws_need = workspace_need == ~uint64_t(0) ? layout->decode_workspace_bytes : workspace_need;
+  if (cache_bytes < layout->cache_bytes || (!own_workspace && workspace_bytes < ws_need)) return RDKV_ERR_WORKSPACE;
   const int append = k_new != nullptr;
   if (c_len < 0 || int64_t(c_len) + append > layout->zone_c_capacity) return RDKV_ERR_CAPACITY;
   DecodeParams p = base_params(layout, cache, c_len + append, c_len, append);
@@ -685,9 +685,43 @@ rdkv_status rdkv_paged_release(const rdkv_paged_layout* layout, int32_t seq, voi
 
 namespace {
 
+ShapeGeom shape_geom(const rdkv_paged_layout& pl) {
+  return ShapeGeom{pl.n_seg, pl.zone_c_capacity, pl.chunk_tok2, pl.token_slots, pl.rec_max,
+                   pl.dims.n_q_heads / pl.dims.n_kv_heads};
+}
+ShapeGeom shape_geom(const rdkv_layout& l) {   // the prefill blob's segments
+  return ShapeGeom{l.n_seg, l.zone_c_capacity, l.chunk_tok2, l.token_slots, l.rec_max,
+                   l.dims.n_q_heads / l.dims.n_kv_heads};
+}
+
+// A launch shape read back from the device: the most prefill-token chunks
+// and the longest record over the segments in use, within the bounds.
+rdkv_status measure_shape(const uint8_t* cache, const ShapeGeom& g, int32_t zc_and_gen_slots, void* workspace,
+                          hipStream_t stream, rdkv_launch_shape* out) {
+  int32_t* dev = static_cast<int32_t*>(workspace);
+  hipError_t e = launch_shape_scan(cache, g, dev, stream);
+  int32_t host[2] = {0, 0};
+  if (e == hipSuccess) e = hipMemcpyAsync(host, dev, sizeof(host), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_status(e);
+  rdkv_launch_shape sh{};
+  sh.token_slots = std::min(host[0], g.token_slots);
+  sh.rec_max = std::min((host[1] + 3) / 4 * 4, g.rec_max);
+  sh.max_chunks = sh.token_slots + zc_and_gen_slots;
+  sh.decode_workspace_bytes = uint64_t(g.n_seg) * sh.max_chunks * g.group * kPartialFloats * sizeof(float);
+  *out = sh;
+  return RDKV_OK;
+}
+
+// A caller's shape against the bounds it must stay within.
+bool shape_ok(const rdkv_launch_shape& sh, int32_t token_slots, int32_t rec_max) {
+  return sh.reserved == 0 && sh.token_slots >= 0 && sh.token_slots <= token_slots && sh.rec_max >= 0 &&
+         sh.rec_max <= rec_max && sh.rec_max % 4 == 0;
+}
+
 // One paged decode step with the launch shape (prefill chunk slots, record
 // bound) of the layout or of a rdkv_paged_decode_shape result.
-rdkv_status paged_decode(const rdkv_paged_layout* layout, const rdkv_paged_shape* shape, void* cache,
+rdkv_status paged_decode(const rdkv_paged_layout* layout, const rdkv_launch_shape* shape, void* cache,
                          size_t cache_bytes, const int32_t* c_len, const void* q, const void* k_new, const void* v_new,
                          float* out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   rdkv_status st = check_paged(layout);
@@ -701,9 +735,7 @@ rdkv_status paged_decode(const rdkv_paged_layout* layout, const rdkv_paged_shape
   const int zc_slots = layout->max_chunks - layout->token_slots;
   int32_t token_slots = layout->token_slots, rec_max = layout->rec_max;
   if (shape) {
-    if (shape->reserved != 0 || shape->token_slots < 0 || shape->token_slots > layout->token_slots ||
-        shape->rec_max < 0 || shape->rec_max > layout->rec_max || shape->rec_max % 4 != 0)
-      return RDKV_ERR_SHAPE;
+    if (!shape_ok(*shape, layout->token_slots, layout->rec_max)) return RDKV_ERR_SHAPE;
     token_slots = shape->token_slots;
     rec_max = shape->rec_max;
   }
@@ -744,7 +776,7 @@ rdkv_status paged_decode(const rdkv_paged_layout* layout, const rdkv_paged_shape
   hipError_t e = launch_decode_chunks_paged(p, lens, stream);
   if (e == hipSuccess) e = launch_decode_merge(p, stream);
   if (e == hipSuccess && shape)
-    e = launch_paged_shape_check(p.cache, *layout, token_slots, rec_max, out, stream);
+    e = launch_shape_check(p.cache, shape_geom(*layout), token_slots, rec_max, out, stream);
   return hip_status(e);
 }
 
@@ -761,29 +793,17 @@ rdkv_status rdkv_paged_decode(const rdkv_paged_layout* layout, void* cache, size
 
 rdkv_status rdkv_paged_decode_shape(const rdkv_paged_layout* layout, const void* cache, size_t cache_bytes,
                                     void* workspace, size_t workspace_bytes, hipStream_t stream,
-                                    rdkv_paged_shape* out) {
+                                    rdkv_launch_shape* out) {
   rdkv_status st = check_paged(layout);
   if (st != RDKV_OK) return st;
   if (!cache || !workspace || !out) return RDKV_ERR_NULL;
   if (!aligned16(cache) || !aligned16(workspace)) return RDKV_ERR_ALIGN;
   if (cache_bytes < layout->cache_bytes || workspace_bytes < 8) return RDKV_ERR_WORKSPACE;
-  int32_t* dev = static_cast<int32_t*>(workspace);
-  hipError_t e = launch_paged_shape_scan(static_cast<const uint8_t*>(cache), *layout, dev, stream);
-  int32_t host[2] = {0, 0};
-  if (e == hipSuccess) e = hipMemcpyAsync(host, dev, sizeof(host), hipMemcpyDeviceToHost, stream);
-  if (e == hipSuccess) e = hipStreamSynchronize(stream);
-  if (e != hipSuccess) return hip_status(e);
-  const int G = layout->dims.n_q_heads / layout->dims.n_kv_heads;
-  rdkv_paged_shape sh{};
-  sh.token_slots = std::min(host[0], layout->token_slots);
-  sh.rec_max = std::min((host[1] + 3) / 4 * 4, layout->rec_max);
-  sh.max_chunks = sh.token_slots + (layout->max_chunks - layout->token_slots);
-  sh.decode_workspace_bytes = uint64_t(layout->n_seg) * sh.max_chunks * G * kPartialFloats * sizeof(float);
-  *out = sh;
-  return RDKV_OK;
+  return measure_shape(static_cast<const uint8_t*>(cache), shape_geom(*layout),
+                       layout->max_chunks - layout->token_slots, workspace, stream, out);
 }
 
-rdkv_status rdkv_paged_decode_shaped(const rdkv_paged_layout* layout, const rdkv_paged_shape* shape, void* cache,
+rdkv_status rdkv_paged_decode_shaped(const rdkv_paged_layout* layout, const rdkv_launch_shape* shape, void* cache,
                                      size_t cache_bytes, const int32_t* c_len, const void* q, const void* k_new,
                                      const void* v_new, float* out, void* workspace, size_t workspace_bytes,
                                      hipStream_t stream) {
@@ -803,6 +823,42 @@ rdkv_status rdkv_unpack(const rdkv_layout* layout, const void* cache, size_t cac
   if (cache_bytes < layout->cache_bytes) return RDKV_ERR_WORKSPACE;
   return hip_status(launch_unpack(static_cast<const uint8_t*>(cache), layout->cache_bytes, *layout, seg,
                                   k_hat, v_hat, stream));
+}
+
+rdkv_status rdkv_decode_shape(const rdkv_layout* layout, const void* cache, size_t cache_bytes, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream, rdkv_launch_shape* out) {
+  rdkv_status st = check_layout(layout);
+  if (st != RDKV_OK) return st;
+  if (!cache || !workspace || !out) return RDKV_ERR_NULL;
+  if (!aligned16(cache) || !aligned16(workspace)) return RDKV_ERR_ALIGN;
+  if (cache_bytes < layout->cache_bytes || workspace_bytes < 8) return RDKV_ERR_WORKSPACE;
+  return measure_shape(static_cast<const uint8_t*>(cache), shape_geom(*layout),
+                       layout->max_chunks - layout->token_slots, workspace, stream, out);
+}
+
+rdkv_status rdkv_decode_shaped(const rdkv_layout* layout, const rdkv_launch_shape* shape, void* cache,
+                               size_t cache_bytes, int32_t c_len, const void* q, const void* k_new, const void* v_new,
+                               float* out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  rdkv_status st = check_layout(layout);
+  if (st != RDKV_OK) return st;
+  if (!shape || !out) return RDKV_ERR_NULL;
+  if (!shape_ok(*shape, layout->token_slots, layout->rec_max)) return RDKV_ERR_SHAPE;
+  const int G = layout->dims.n_q_heads / layout->dims.n_kv_heads;
+  const int32_t max_chunks = shape->token_slots + (layout->max_chunks - layout->token_slots);
+  const uint64_t ws_need = uint64_t(layout->n_seg) * max_chunks * G * kPartialFloats * sizeof(float);
+  DecodeParams p;
+  st = decode_params(layout, cache, cache_bytes, c_len, q, k_new, v_new, workspace, workspace_bytes, &p, false,
+                     ws_need);
+  if (st != RDKV_OK) return st;
+  if (!aligned16(out)) return RDKV_ERR_ALIGN;
+  p.out = out;
+  p.token_slots = shape->token_slots;   // the prefill blob's chunks; generations and zone C follow them
+  p.max_chunks = max_chunks;
+  p.rec_max = shape->rec_max;
+  hipError_t e = launch_decode_chunks(p, stream);
+  if (e == hipSuccess) e = launch_decode_merge(p, stream);
+  if (e == hipSuccess) e = launch_shape_check(p.cache, shape_geom(*layout), p.token_slots, p.rec_max, out, stream);
+  return hip_status(e);
 }
 
 }  // extern "C"

@@ -664,26 +664,27 @@ __global__ __launch_bounds__(256) void paged_release_kernel(uint8_t* cache, rdkv
   if (threadIdx.x < kDescBytes / 4) st_u32(cache + kHeaderBytes + uint64_t(seg) * kDescBytes, 4 * threadIdx.x, 0u);
 }
 
-// ---------------------------------------------------------------- decode shape (paged)
+// ---------------------------------------------------------------- decode launch shape
 
-// A segment in use (a committed slot: zone-C capacity of the layout) and its
-// prefill-token chunk count and K record bytes, as decode counts them; -1
-// chunks for a free or damaged slot.
+// A segment in use (zone-C capacity of the layout: a committed paged slot, or
+// any segment of a contiguous blob) and its prefill-token chunk count and K
+// record bytes, as decode counts them; -1 chunks for a free slot or one the
+// layout's own bounds already reject (decode reads it as empty either way).
 struct SegShape {
   int chunks, rec;
 };
-__device__ inline SegShape seg_shape(const uint8_t* cache, const rdkv_paged_layout& pl, int64_t seg) {
+__device__ inline SegShape seg_shape(const uint8_t* cache, const ShapeGeom& g, int64_t seg) {
   const uint8_t* d = cache + kHeaderBytes + uint64_t(seg) * kDescBytes;
   SegShape r{-1, 0};
-  if (*reinterpret_cast<const int32_t*>(d + kDescCap) != pl.zone_c_capacity) return r;
+  if (*reinterpret_cast<const int32_t*>(d + kDescCap) != g.zone_c_capacity) return r;
   int chunks = 0;
   for (int i = 0; i < 4; ++i) {
     const int n = *reinterpret_cast<const int32_t*>(d + kDescNTok + 4 * i);
     if (n < 0) return r;
-    chunks += (n + chunk_tokens(pl.chunk_tok2, i) - 1) >> chunk_shift(pl.chunk_tok2, i);
+    chunks += (n + chunk_tokens(g.chunk_tok2, i) - 1) >> chunk_shift(g.chunk_tok2, i);
   }
   const int rec = *reinterpret_cast<const int32_t*>(d + kDescRec);
-  if (rec < 0 || rec > pl.rec_max || chunks > pl.token_slots) return r;
+  if (rec < 0 || rec > g.rec_max || chunks > g.token_slots) return r;
   r.chunks = chunks;
   r.rec = rec;
   return r;
@@ -691,18 +692,15 @@ __device__ inline SegShape seg_shape(const uint8_t* cache, const rdkv_paged_layo
 
 // The most chunks and record bytes over the segments in use (out[0], out[1],
 // zero on entry).
-__global__ __launch_bounds__(256) void paged_shape_scan_kernel(const uint8_t* cache, rdkv_paged_layout pl,
-                                                               int32_t* out) {
+__global__ __launch_bounds__(256) void shape_scan_kernel(const uint8_t* cache, ShapeGeom g, int32_t* out) {
   int c = 0, r = 0;
-  for (int64_t seg = int64_t(blockIdx.x) * 256 + threadIdx.x; seg < pl.n_seg; seg += int64_t(gridDim.x) * 256) {
-    const SegShape sh = seg_shape(cache, pl, seg);
+  for (int64_t seg = int64_t(blockIdx.x) * 256 + threadIdx.x; seg < g.n_seg; seg += int64_t(gridDim.x) * 256) {
+    const SegShape sh = seg_shape(cache, g, seg);
     if (sh.chunks < 0) continue;
     c = max(c, sh.chunks);
     r = max(r, sh.rec);
   }
-  c = max(c, __shfl_xor(c, 32, 64));
-  r = max(r, __shfl_xor(r, 32, 64));
-  for (int x = 16; x >= 1; x >>= 1) {
+  for (int x = 32; x >= 1; x >>= 1) {
     c = max(c, __shfl_xor(c, x, 64));
     r = max(r, __shfl_xor(r, x, 64));
   }
@@ -719,13 +717,13 @@ __global__ __launch_bounds__(64) void zero_words_kernel(int32_t* p, int n) {
 // After a decode with a shape: the outputs of every segment in use that the
 // shape does not cover (more chunks or longer records than it allows, so the
 // decode read it as empty) are set to NaN.
-__global__ __launch_bounds__(256) void paged_shape_check_kernel(const uint8_t* cache, rdkv_paged_layout pl,
-                                                                int32_t token_slots, int32_t rec_max, float* out) {
-  const int G = pl.dims.n_q_heads / pl.dims.n_kv_heads;
-  for (int64_t seg = blockIdx.x; seg < pl.n_seg; seg += gridDim.x) {
-    const SegShape sh = seg_shape(cache, pl, seg);
+__global__ __launch_bounds__(256) void shape_check_kernel(const uint8_t* cache, ShapeGeom g, int32_t token_slots,
+                                                          int32_t rec_max, float* out) {
+  for (int64_t seg = blockIdx.x; seg < g.n_seg; seg += gridDim.x) {
+    const SegShape sh = seg_shape(cache, g, seg);
     if (sh.chunks < 0 || (sh.chunks <= token_slots && sh.rec <= rec_max)) continue;   // (uniform)
-    for (int i = threadIdx.x; i < G * kHeadDim; i += 256) out[seg * G * kHeadDim + i] = __builtin_nanf("");
+    for (int i = threadIdx.x; i < g.group * kHeadDim; i += 256)
+      out[seg * g.group * kHeadDim + i] = __builtin_nanf("");
   }
 }
 
@@ -808,22 +806,20 @@ hipError_t launch_unpack(const uint8_t* cache, uint64_t, const rdkv_layout& lay,
   return hipGetLastError();
 }
 
-hipError_t launch_paged_shape_scan(const uint8_t* cache, const rdkv_paged_layout& pl, int32_t* out,
-                                   hipStream_t stream) {
+hipError_t launch_shape_scan(const uint8_t* cache, const ShapeGeom& g, int32_t* out, hipStream_t stream) {
   LaunchErrors le;
   hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(64), 0, stream, out, 2);
   le.check();
-  const unsigned grid = unsigned(std::min<int64_t>(cdiv(pl.n_seg, 256), 1024));
-  hipLaunchKernelGGL(paged_shape_scan_kernel, dim3(grid), dim3(256), 0, stream, cache, pl, out);
+  const unsigned grid = unsigned(std::min<int64_t>(cdiv(g.n_seg, 256), 1024));
+  hipLaunchKernelGGL(shape_scan_kernel, dim3(grid), dim3(256), 0, stream, cache, g, out);
   le.check();
   return le.status();
 }
 
-hipError_t launch_paged_shape_check(const uint8_t* cache, const rdkv_paged_layout& pl, int32_t token_slots,
-                                    int32_t rec_max, float* out, hipStream_t stream) {
-  const unsigned grid = unsigned(std::min<int64_t>(pl.n_seg, 4096));
-  hipLaunchKernelGGL(paged_shape_check_kernel, dim3(grid), dim3(256), 0, stream, cache, pl, token_slots, rec_max,
-                     out);
+hipError_t launch_shape_check(const uint8_t* cache, const ShapeGeom& g, int32_t token_slots, int32_t rec_max,
+                              float* out, hipStream_t stream) {
+  const unsigned grid = unsigned(std::min<int64_t>(g.n_seg, 4096));
+  hipLaunchKernelGGL(shape_check_kernel, dim3(grid), dim3(256), 0, stream, cache, g, token_slots, rec_max, out);
   return hipGetLastError();
 }
 

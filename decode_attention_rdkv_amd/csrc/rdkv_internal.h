@@ -243,13 +243,18 @@ hipError_t launch_paged_init(uint8_t* cache, const rdkv_paged_layout& play, hipS
 hipError_t launch_paged_plan(const PagedPackParams& p, hipStream_t stream);
 hipError_t launch_paged_commit(const PagedPackParams& p, hipStream_t stream);
 hipError_t launch_paged_release(uint8_t* cache, const rdkv_paged_layout& play, int32_t seq, hipStream_t stream);
-// Decode shape of a paged cache: out[0] = the most prefill-token chunks, out[1]
-// = the longest K record (bytes) over the segments in use (device int32[2]).
-hipError_t launch_paged_shape_scan(const uint8_t* cache, const rdkv_paged_layout& pl, int32_t* out,
-                                   hipStream_t stream);
+// The decode launch shape of a cache's segments in use (a paged cache's
+// committed slots, or every segment of a contiguous blob's prefill part).
+struct ShapeGeom {
+  int64_t n_seg;
+  int32_t zone_c_capacity, chunk_tok2, token_slots, rec_max, group;
+};
+// out[0] = the most prefill-token chunks, out[1] = the longest K record
+// (bytes) over the segments in use (device int32[2]).
+hipError_t launch_shape_scan(const uint8_t* cache, const ShapeGeom& g, int32_t* out, hipStream_t stream);
 // NaN outputs for the segments in use that a shape does not cover.
-hipError_t launch_paged_shape_check(const uint8_t* cache, const rdkv_paged_layout& pl, int32_t token_slots,
-                                    int32_t rec_max, float* out, hipStream_t stream);
+hipError_t launch_shape_check(const uint8_t* cache, const ShapeGeom& g, int32_t token_slots, int32_t rec_max,
+                              float* out, hipStream_t stream);
 hipError_t launch_unpack(const uint8_t* cache, uint64_t cache_bytes, const rdkv_layout& lay, int64_t seg,
                          float* k_hat, float* v_hat, hipStream_t stream);
 

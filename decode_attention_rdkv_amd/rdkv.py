@@ -52,7 +52,7 @@ class PagedLayout(ctypes.Structure):
         return self.dims.n_q_heads // self.dims.n_kv_heads
 
 
-class PagedShape(ctypes.Structure):
+class LaunchShape(ctypes.Structure):
     _fields_ = [("token_slots", c_i32), ("rec_max", c_i32), ("max_chunks", c_i32), ("reserved", c_i32),
                 ("decode_workspace_bytes", c_u64)]
 
@@ -83,6 +83,10 @@ SIGNATURES = {
     "rdkv_pack_status": (c_i32, [ctypes.POINTER(Layout), c_vp, ctypes.c_size_t, c_vp, c_vp]),
     "rdkv_decode": (c_i32, [ctypes.POINTER(Layout), c_vp, ctypes.c_size_t, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp,
                             ctypes.c_size_t, c_vp]),
+    "rdkv_decode_shape": (c_i32, [ctypes.POINTER(Layout), c_vp, ctypes.c_size_t, c_vp, ctypes.c_size_t, c_vp,
+                                  ctypes.POINTER(LaunchShape)]),
+    "rdkv_decode_shaped": (c_i32, [ctypes.POINTER(Layout), ctypes.POINTER(LaunchShape), c_vp, ctypes.c_size_t, c_i32,
+                                   c_vp, c_vp, c_vp, c_vp, c_vp, ctypes.c_size_t, c_vp]),
     "rdkv_decode_accumulate": (c_i32, [ctypes.POINTER(Layout), c_vp, ctypes.c_size_t, c_i32, c_vp, c_vp, c_vp, c_vp,
                                        c_vp, c_vp, ctypes.c_size_t, c_vp]),
     "rdkv_rollover_score": (c_i32, [ctypes.POINTER(Layout), c_vp, ctypes.c_size_t, c_vp, c_vp, c_vp, c_vp, c_vp]),
@@ -106,8 +110,8 @@ SIGNATURES = {
     "rdkv_paged_decode": (c_i32, [ctypes.POINTER(PagedLayout), c_vp, ctypes.c_size_t, ctypes.POINTER(c_i32), c_vp,
                                   c_vp, c_vp, c_vp, c_vp, ctypes.c_size_t, c_vp]),
     "rdkv_paged_decode_shape": (c_i32, [ctypes.POINTER(PagedLayout), c_vp, ctypes.c_size_t, c_vp, ctypes.c_size_t,
-                                        c_vp, ctypes.POINTER(PagedShape)]),
-    "rdkv_paged_decode_shaped": (c_i32, [ctypes.POINTER(PagedLayout), ctypes.POINTER(PagedShape), c_vp,
+                                        c_vp, ctypes.POINTER(LaunchShape)]),
+    "rdkv_paged_decode_shaped": (c_i32, [ctypes.POINTER(PagedLayout), ctypes.POINTER(LaunchShape), c_vp,
                                          ctypes.c_size_t, ctypes.POINTER(c_i32), c_vp, c_vp, c_vp, c_vp, c_vp,
                                          ctypes.c_size_t, c_vp]),
     "rdkv_unpack": (c_i32, [ctypes.POINTER(Layout), c_vp, ctypes.c_size_t, c_i64, c_vp, c_vp, c_vp]),
@@ -329,22 +333,38 @@ def decode_workspace(lay: Layout, device="cuda") -> torch.Tensor:
     return torch.empty(max(int(lay.decode_workspace_bytes), 16), dtype=torch.uint8, device=device)
 
 
+def decode_shape(lay: Layout, cache: torch.Tensor, workspace: Optional[torch.Tensor] = None) -> "LaunchShape":
+    """The decode launch shape of the prefill blob's segments (synchronous: reads the device)."""
+    if workspace is None:
+        workspace = torch.empty(16, dtype=torch.uint8, device=cache.device)
+    out = LaunchShape()
+    _check(load().rdkv_decode_shape(ctypes.byref(lay), _ptr(cache, torch.uint8, None, "cache"), cache.numel(),
+                                    _ptr(workspace, torch.uint8, None, "workspace"), workspace.numel(), _stream(),
+                                    ctypes.byref(out)),
+           "rdkv_decode_shape")
+    return out
+
+
 def decode(lay: Layout, cache: torch.Tensor, c_len: int, q, k_new=None, v_new=None,
-           workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """One decode step; returns out fp32 [S][L][Hq][128]."""
+           workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+           shape: Optional["LaunchShape"] = None) -> torch.Tensor:
+    """One decode step (rdkv_decode_shaped with `shape`); returns out fp32 [S][L][Hq][128]."""
     d = lay.dims
     S, L, Hq, Hk = d.n_seq, d.n_layers, d.n_q_heads, d.n_kv_heads
     if workspace is None:
         workspace = decode_workspace(lay, q.device)
     if out is None:
         out = torch.empty((S, L, Hq, HEAD_DIM), dtype=torch.float32, device=q.device)
-    _check(load().rdkv_decode(ctypes.byref(lay), _ptr(cache, torch.uint8, None, "cache"), cache.numel(), c_len,
-                              _ptr(q, torch.float16, (S, L, Hq, HEAD_DIM), "q"),
-                              _ptr(k_new, torch.float16, (S, L, Hk, HEAD_DIM), "k_new"),
-                              _ptr(v_new, torch.float16, (S, L, Hk, HEAD_DIM), "v_new"),
-                              _ptr(out, torch.float32, (S, L, Hq, HEAD_DIM), "out"),
-                              _ptr(workspace, torch.uint8, None, "workspace"), workspace.numel(), _stream()),
-           "rdkv_decode")
+    args = (_ptr(cache, torch.uint8, None, "cache"), cache.numel(), c_len,
+            _ptr(q, torch.float16, (S, L, Hq, HEAD_DIM), "q"),
+            _ptr(k_new, torch.float16, (S, L, Hk, HEAD_DIM), "k_new"),
+            _ptr(v_new, torch.float16, (S, L, Hk, HEAD_DIM), "v_new"),
+            _ptr(out, torch.float32, (S, L, Hq, HEAD_DIM), "out"),
+            _ptr(workspace, torch.uint8, None, "workspace"), workspace.numel(), _stream())
+    if shape is None:
+        _check(load().rdkv_decode(ctypes.byref(lay), *args), "rdkv_decode")
+    else:
+        _check(load().rdkv_decode_shaped(ctypes.byref(lay), ctypes.byref(shape), *args), "rdkv_decode_shaped")
     return out
 
 
@@ -523,11 +543,11 @@ def paged_decode_workspace(pl: PagedLayout, device="cuda") -> torch.Tensor:
     return torch.empty(max(int(pl.decode_workspace_bytes), 16), dtype=torch.uint8, device=device)
 
 
-def paged_decode_shape(pl: PagedLayout, cache: torch.Tensor, workspace: Optional[torch.Tensor] = None) -> PagedShape:
+def paged_decode_shape(pl: PagedLayout, cache: torch.Tensor, workspace: Optional[torch.Tensor] = None) -> LaunchShape:
     """The decode launch shape of the slots in use (synchronous: reads the device)."""
     if workspace is None:
         workspace = torch.empty(16, dtype=torch.uint8, device=cache.device)
-    out = PagedShape()
+    out = LaunchShape()
     _check(load().rdkv_paged_decode_shape(ctypes.byref(pl), _ptr(cache, torch.uint8, None, "cache"), cache.numel(),
                                           _ptr(workspace, torch.uint8, None, "workspace"), workspace.numel(),
                                           _stream(), ctypes.byref(out)),
@@ -537,7 +557,7 @@ def paged_decode_shape(pl: PagedLayout, cache: torch.Tensor, workspace: Optional
 
 def paged_decode(pl: PagedLayout, cache: torch.Tensor, c_len, q, k_new=None, v_new=None,
                  workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-                 shape: Optional[PagedShape] = None) -> torch.Tensor:
+                 shape: Optional[LaunchShape] = None) -> torch.Tensor:
     """One decode step over every sequence slot; c_len: host sequence of the
     slots' zone-C rows before the step.  With `shape` (paged_decode_shape),
     rdkv_paged_decode_shaped.  Returns out fp32 [S][L][Hq][128]."""

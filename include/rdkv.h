@@ -422,37 +422,44 @@ rdkv_status rdkv_paged_decode(const rdkv_paged_layout* layout, void* cache, size
                               const int32_t* c_len, const void* q, const void* k_new, const void* v_new,
                               float* out, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Decode launch shape of the sequences in use.  rdkv_paged_decode sizes its
- * launch from the layout's bounds: chunk slots per segment for the largest
- * V budget a segment may hold, and an LDS record ring for the longest K
- * record it may have.  With one budget shared by a layer's heads
- * (rdkv_allocate_shared) those bounds are those of the whole layer's budget,
- * several times what the segments actually hold, and the launch pays for
- * empty slots and a larger ring.  rdkv_paged_decode_shape measures the
- * segments in use instead: it reads every slot's descriptor on `stream` and
- * WAITS for the result (a synchronous call, like reading pages_needed after
+/* Decode launch shape of the segments in use.  rdkv_paged_decode (and
+ * rdkv_decode) size their launch from the layout's bounds: chunk slots per
+ * segment for the largest V budget a segment may hold, and an LDS record ring
+ * for the longest K record it may have.  With one budget shared by a layer's
+ * heads (rdkv_allocate_shared) those bounds are those of the whole layer's
+ * budget, several times what the segments actually hold, and the launch pays
+ * for empty slots and a larger ring.  rdkv_paged_decode_shape (rdkv_decode_shape
+ * for a contiguous cache: its prefill blob's segments) measures the segments
+ * in use instead: it reads every segment's descriptor on `stream` and WAITS
+ * for the result (a synchronous call, like reading pages_needed after
  * rdkv_paged_stage); `workspace` is any device buffer of >= 8 bytes, e.g. the
- * decode workspace.  rdkv_paged_decode_shaped is rdkv_paged_decode with that
- * shape; its workspace needs shape->decode_workspace_bytes (<= the
- * layout's).  A shape covers the slots in use when it was made: make a new
- * one after a commit (a release leaves it valid).  A segment in use that the
- * shape does not cover (a later commit with more chunks or longer records)
- * is not decoded and takes no appended token: its outputs are set to NaN.  Errors: RDKV_ERR_SHAPE for a
- * shape outside the layout's bounds, others as rdkv_paged_decode. */
-typedef struct rdkv_paged_shape {
+ * decode workspace.  rdkv_paged_decode_shaped (rdkv_decode_shaped) is
+ * rdkv_paged_decode (rdkv_decode) launched with that shape; its workspace
+ * needs shape->decode_workspace_bytes (<= the layout's).  A shape covers the
+ * segments as they were when it was made: make a new one after a commit or a
+ * pack (a release leaves it valid).  A segment in use that the shape does not
+ * cover (more chunks or longer records than it allows) is not decoded and
+ * takes no appended token: its outputs are set to NaN.  Errors: RDKV_ERR_SHAPE
+ * for a shape outside the layout's bounds, others as the unshaped call. */
+typedef struct rdkv_launch_shape {
   int32_t token_slots;              /* prefill-token chunk slots per segment (<= layout->token_slots) */
   int32_t rec_max;                  /* bytes of the longest K record, a multiple of 4 (<= layout->rec_max) */
-  int32_t max_chunks;               /* token_slots + the zone-C chunk slots */
+  int32_t max_chunks;               /* token_slots + the other chunk slots (generations, zone C) */
   int32_t reserved;                 /* 0 */
   uint64_t decode_workspace_bytes;  /* split-K partials of a launch of this shape */
-} rdkv_paged_shape;
+} rdkv_launch_shape;
 rdkv_status rdkv_paged_decode_shape(const rdkv_paged_layout* layout, const void* cache, size_t cache_bytes,
                                     void* workspace, size_t workspace_bytes, hipStream_t stream,
-                                    rdkv_paged_shape* out);
-rdkv_status rdkv_paged_decode_shaped(const rdkv_paged_layout* layout, const rdkv_paged_shape* shape, void* cache,
+                                    rdkv_launch_shape* out);
+rdkv_status rdkv_paged_decode_shaped(const rdkv_paged_layout* layout, const rdkv_launch_shape* shape, void* cache,
                                      size_t cache_bytes, const int32_t* c_len, const void* q, const void* k_new,
                                      const void* v_new, float* out, void* workspace, size_t workspace_bytes,
                                      hipStream_t stream);
+rdkv_status rdkv_decode_shape(const rdkv_layout* layout, const void* cache, size_t cache_bytes, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream, rdkv_launch_shape* out);
+rdkv_status rdkv_decode_shaped(const rdkv_layout* layout, const rdkv_launch_shape* shape, void* cache,
+                               size_t cache_bytes, int32_t c_len, const void* q, const void* k_new, const void* v_new,
+                               float* out, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Test support: dequantized kept rows of one segment, in kept order, with the
  * fused multiply-add dequantization x_hat = fmaf(code, scale, zero).

@@ -94,6 +94,18 @@ void contiguous(const rdkv_layout& lay) {
   int32_t dropped = 0;
   EXPECT(ok_or_hip(rdkv_pack_status(&lay, D, cb, &dropped, nullptr)), "pack_status");
   EXPECT(ok_or_hip(rdkv_decode(&lay, D, cb, 0, D, D, D, F(D), D, wb, nullptr)), "decode");
+  {
+    rdkv_launch_shape sh{};
+    EXPECT(ok_or_hip(rdkv_decode_shape(&lay, D, cb, D, wb, nullptr, &sh)), "decode shape");
+    EXPECT(rdkv_decode_shape(&lay, D, cb, D, 7, nullptr, &sh) == RDKV_ERR_WORKSPACE, "decode shape workspace");
+    sh = rdkv_launch_shape{lay.token_slots, lay.rec_max, lay.max_chunks, 0, 0};
+    EXPECT(ok_or_hip(rdkv_decode_shaped(&lay, &sh, D, cb, 0, D, D, D, F(D), D, wb, nullptr)), "shaped decode");
+    sh.rec_max = lay.rec_max + 4;
+    EXPECT(rdkv_decode_shaped(&lay, &sh, D, cb, 0, D, D, D, F(D), D, wb, nullptr) == RDKV_ERR_SHAPE,
+           "shaped decode past the bounds");
+    EXPECT(rdkv_decode_shaped(&lay, nullptr, D, cb, 0, D, D, D, F(D), D, wb, nullptr) == RDKV_ERR_NULL,
+           "shaped decode without a shape");
+  }
   EXPECT(ok_or_hip(rdkv_decode(&lay, D, cb, cap, D, nullptr, nullptr, F(D), D, wb, nullptr)), "decode full zone C");
   EXPECT(rdkv_decode(&lay, D, cb, cap, D, D, D, F(D), D, wb, nullptr) == RDKV_ERR_CAPACITY, "decode over capacity");
   EXPECT(rdkv_decode(&lay, D, cb, -1, D, D, D, F(D), D, wb, nullptr) != RDKV_OK, "decode negative c_len");
@@ -157,16 +169,16 @@ void paged(const rdkv_paged_layout& pl) {
          "paged decode null lengths");
   {
     c_len[pl.dims.n_seq - 1] = 0;
-    rdkv_paged_shape sh{};
+    rdkv_launch_shape sh{};
     EXPECT(ok_or_hip(rdkv_paged_decode_shape(&pl, D, cb, D, wb, nullptr, &sh)), "decode shape");
     EXPECT(rdkv_paged_decode_shape(&pl, D, cb, D, 4, nullptr, &sh) == RDKV_ERR_WORKSPACE, "decode shape workspace");
-    sh = rdkv_paged_shape{pl.token_slots, pl.rec_max, pl.max_chunks, 0, 0};
+    sh = rdkv_launch_shape{pl.token_slots, pl.rec_max, pl.max_chunks, 0, 0};
     EXPECT(ok_or_hip(rdkv_paged_decode_shaped(&pl, &sh, D, cb, c_len, D, D, D, F(D), D, wb, nullptr)),
            "shaped decode");
     sh.token_slots = pl.token_slots + 1;
     EXPECT(rdkv_paged_decode_shaped(&pl, &sh, D, cb, c_len, D, D, D, F(D), D, wb, nullptr) == RDKV_ERR_SHAPE,
            "shaped decode past the bounds");
-    sh = rdkv_paged_shape{0, 0, 0, 0, 0};
+    sh = rdkv_launch_shape{0, 0, 0, 0, 0};
     EXPECT(ok_or_hip(rdkv_paged_decode_shaped(&pl, &sh, D, cb, c_len, D, D, D, F(D), D, wb, nullptr)),
            "shaped decode, no prefill chunks");
   }
@@ -202,6 +214,9 @@ void fuzz(unsigned seed, int rounds) {
       const int32_t c = pick32(600);
       (void)rdkv_decode(&lay, D, lay.cache_bytes, c, D, D, D, F(D), D, lay.decode_workspace_bytes, nullptr);
       (void)rdkv_decode_merge(&lay, D, lay.cache_bytes, c, F(D), D, lay.decode_workspace_bytes, nullptr);
+      const rdkv_launch_shape sh{pick32(lay.token_slots + 2), pick32(lay.rec_max + 8) & ~3, 0, 0, 0};
+      (void)rdkv_decode_shaped(&lay, &sh, D, lay.cache_bytes, c, D, D, D, F(D), D, lay.decode_workspace_bytes,
+                               nullptr);
       (void)rdkv_pack(&lay, pick32(100), pick32(100), D, D, U(D), U(D), D, lay.cache_bytes, nullptr);
       (void)rdkv_unpack(&lay, D, lay.cache_bytes, pick64(), F(D), F(D), nullptr);
       if (lay.n_generations > 0) (void)rdkv_rollover(&lay, D, lay.cache_bytes, pick32(8), F(D), D, lay.rollover_workspace_bytes, nullptr);
@@ -220,7 +235,7 @@ void fuzz(unsigned seed, int rounds) {
       int32_t c_len[RDKV_MAX_PAGED_SEQS];
       for (int k = 0; k < RDKV_MAX_PAGED_SEQS; ++k) c_len[k] = pick32(600);
       (void)rdkv_paged_decode(&pl, D, pl.cache_bytes, c_len, D, D, D, F(D), D, pl.decode_workspace_bytes, nullptr);
-      const rdkv_paged_shape sh{pick32(pl.token_slots + 2), pick32(pl.rec_max + 8) & ~3, 0, 0, 0};
+      const rdkv_launch_shape sh{pick32(pl.token_slots + 2), pick32(pl.rec_max + 8) & ~3, 0, 0, 0};
       (void)rdkv_paged_decode_shaped(&pl, &sh, D, pl.cache_bytes, c_len, D, D, D, F(D), D,
                                      pl.decode_workspace_bytes, nullptr);
     }

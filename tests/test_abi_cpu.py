@@ -341,7 +341,7 @@ def test_paged_shape_validation(lib):
     d = rdkv.make_dims(3, 2, 8, 2, 300)
     pl = rdkv.paged_layout(d, 600, 256, 32, 50)
     nb, ws = pl.cache_bytes, pl.decode_workspace_bytes
-    out = rdkv.PagedShape()
+    out = rdkv.LaunchShape()
     assert lib.rdkv_paged_decode_shape(ctypes.byref(pl), None, nb, A, 8, None, ctypes.byref(out)) == NULL
     assert lib.rdkv_paged_decode_shape(ctypes.byref(pl), A, nb, A, 8, None, None) == NULL
     assert lib.rdkv_paged_decode_shape(ctypes.byref(pl), A, nb, A, 4, None, ctypes.byref(out)) == WORKSPACE
@@ -356,12 +356,36 @@ def test_paged_shape_validation(lib):
     G, zc = 4, pl.max_chunks - pl.token_slots
     for ts, rec, res, status in ((pl.token_slots + 1, 0, 0, SHAPE), (-1, 0, 0, SHAPE), (1, pl.rec_max + 4, 0, SHAPE),
                                  (1, 6, 0, SHAPE), (1, 4, 1, SHAPE)):
-        sh = rdkv.PagedShape(ts, rec, ts + zc, res, 0)
+        sh = rdkv.LaunchShape(ts, rec, ts + zc, res, 0)
         assert shaped(ctypes.byref(sh)) == status, (ts, rec, res)
     # a smaller shape needs a smaller workspace: its own size passes validation
     # (and then fails only at the launch, on a machine without a GPU)
-    sh = rdkv.PagedShape(1, 4, 1 + zc, 0, 0)
+    sh = rdkv.LaunchShape(1, 4, 1 + zc, 0, 0)
     need = pl.n_seg * (1 + zc) * G * 132 * 4
+    assert shaped(ctypes.byref(sh), need - 1) == WORKSPACE
+    assert shaped(ctypes.byref(sh), need) == HIP
+
+
+def test_contiguous_shape_validation(lib):
+    """rdkv_decode_shape / rdkv_decode_shaped reject missing arguments, a
+    short workspace and a shape outside the layout's bounds before anything
+    is enqueued; a shape's own workspace size passes validation."""
+    lay = rdkv.layout(rdkv.make_dims(1, 2, 8, 2, 3000), 6000, 160, 16)
+    nb, ws = lay.cache_bytes, lay.decode_workspace_bytes
+    out = rdkv.LaunchShape()
+    assert lib.rdkv_decode_shape(ctypes.byref(lay), None, nb, A, 8, None, ctypes.byref(out)) == NULL
+    assert lib.rdkv_decode_shape(ctypes.byref(lay), A, nb, A, 7, None, ctypes.byref(out)) == WORKSPACE
+    assert lib.rdkv_decode_shape(ctypes.byref(lay), A, nb, A + 8, 8, None, ctypes.byref(out)) == ALIGN
+
+    def shaped(sh, ws_bytes=ws):
+        return lib.rdkv_decode_shaped(ctypes.byref(lay), sh, A, nb, 0, A, None, None, A, A, ws_bytes, None)
+
+    assert shaped(None) == NULL
+    other = lay.max_chunks - lay.token_slots
+    for ts, rec, res in ((lay.token_slots + 1, 0, 0), (1, lay.rec_max + 4, 0), (1, 2, 0), (1, 4, 3)):
+        assert shaped(ctypes.byref(rdkv.LaunchShape(ts, rec, ts + other, res, 0))) == SHAPE, (ts, rec, res)
+    sh = rdkv.LaunchShape(2, 8, 2 + other, 0, 0)
+    need = lay.n_seg * (2 + other) * 4 * 132 * 4
     assert shaped(ctypes.byref(sh), need - 1) == WORKSPACE
     assert shaped(ctypes.byref(sh), need) == HIP
 

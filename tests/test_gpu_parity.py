@@ -519,6 +519,81 @@ def test_shared_budget_cache_packs_and_decodes(gpu_lib):
     _decode_run(rdkv, lay, ol, cache, oblob, 4, 45)
 
 
+def _seg_shapes_contiguous(lay, cache):
+    """(prefill-token chunks, K record bytes) of each segment of the prefill
+    blob, from its descriptor on the host."""
+    ints = host(cache)[256:256 + 256 * lay.n_seg].reshape(lay.n_seg, 256).view(np.int32)
+    return [(sum(-(-int(n) // (lay.chunk_tok2 >> g)) for g, n in enumerate(ints[s, 0:4])), int(ints[s, 9]))
+            for s in range(lay.n_seg)]
+
+
+def test_shared_budget_cache_decodes_with_measured_shape(gpu_lib):
+    """A contiguous blob laid out for a per-layer budget (each segment's
+    bound is the layer's budget): the measured launch shape matches the
+    descriptors and stays within the bounds, the shaped decode agrees with the
+    bounds-shaped one within 1e-6 over steps with appends (caches byte-equal),
+    and after layer 1 is repacked with one head holding nearly the whole
+    budget, the old shape gives that segment NaN outputs and the others the
+    same values; a new shape covers it."""
+    rdkv = gpu_lib
+    S, L, Hq, Hkv, N, cap = 1, 2, 8, 2, 3000, 16
+    G, n_seg = Hq // Hkv, S * L * Hkv
+    w_tok, var_tok, w_chan = synth.random_unit_inputs(n_seg, N, seed=61)
+    K, V = synth.random_kv(n_seg, N, seed=62)
+    bv, bk = int(1.0 * N) * Hkv, 80 * Hkv
+    dims = rdkv.make_dims(S, L, Hq, Hkv, N)
+    shp = (S, L, Hkv)
+    Kd, Vd = dev(K.reshape(shp + (N, 128))), dev(V.reshape(shp + (N, 128)))
+
+    def allocation(wt, budget_v):
+        bt, bc, _, _ = rdkv.allocate_shared(dims, dev(wt.reshape(shp + (N,))), dev(var_tok.reshape(shp + (N,))),
+                                            dev(w_chan.reshape(shp + (128,))), Kd, budget_v, bk, Hkv)
+        return bt, bc
+
+    lay = rdkv.layout(dims, bv, bk, cap)
+    cache = rdkv.cache_init(lay)
+    rdkv.pack(lay, cache, Kd, Vd, *allocation(w_tok, bv // 4))   # a quarter of what the layout allows
+    shape = rdkv.decode_shape(lay, cache)
+    segs = _seg_shapes_contiguous(lay, cache)
+    assert (shape.token_slots, shape.rec_max) == (max(c for c, _ in segs), -(-max(r for _, r in segs) // 4) * 4)
+    assert shape.token_slots < lay.token_slots and shape.rec_max <= lay.rec_max
+    assert shape.max_chunks == shape.token_slots + lay.max_chunks - lay.token_slots
+    other = cache.clone()
+    ws = rdkv.decode_workspace(lay)
+    ws_shape = torch.empty(int(shape.decode_workspace_bytes), dtype=torch.uint8, device=DEV)
+    r = np.random.default_rng(63)
+    for c_len in range(3):
+        q = dev(r.standard_normal((S, L, Hq, 128)).astype(np.float16))
+        kn = dev(r.standard_normal((S, L, Hkv, 128)).astype(np.float16))
+        vn = dev(r.standard_normal((S, L, Hkv, 128)).astype(np.float16))
+        got = host(rdkv.decode(lay, cache, c_len, q, kn, vn, workspace=ws_shape, shape=shape))
+        want = host(rdkv.decode(lay, other, c_len, q, kn, vn, workspace=ws))
+        assert rel_err_rows(got, want) <= 1e-6, f"step {c_len}"
+    assert torch.equal(cache, other)
+    # layer 1 repacked with head 0 holding nearly the whole layer budget
+    w2 = w_tok.copy()
+    w2[2] *= np.float32(1e4)
+    bt2, bc2 = allocation(w2, bv)
+    for c in (cache, other):
+        rdkv.pack(lay, c, Kd[:, 1:2].contiguous(), Vd[:, 1:2].contiguous(), bt2[:, 1:2].contiguous(),
+                  bc2[:, 1:2].contiguous(), layer_begin=1)
+    segs2 = _seg_shapes_contiguous(lay, cache)
+    assert segs2[2][0] > shape.token_slots
+    q = dev(r.standard_normal((S, L, Hq, 128)).astype(np.float16))
+    want = host(rdkv.decode(lay, other, 0, q, workspace=ws))
+    stale = host(rdkv.decode(lay, cache, 0, q, workspace=ws_shape, shape=shape))
+    for seg, (c, rec) in enumerate(segs2):
+        l, h = divmod(seg, Hkv)
+        rows, ref = stale[0, l, h * G:(h + 1) * G], want[0, l, h * G:(h + 1) * G]
+        if c > shape.token_slots or rec > shape.rec_max:
+            assert np.isnan(rows).all(), f"segment {seg} outside the shape"
+        else:
+            assert rel_err_rows(rows, ref) <= 1e-6, f"segment {seg}"
+    shape2 = rdkv.decode_shape(lay, cache)
+    ws2 = torch.empty(int(shape2.decode_workspace_bytes), dtype=torch.uint8, device=DEV)
+    assert rel_err_rows(host(rdkv.decode(lay, cache, 0, q, workspace=ws2, shape=shape2)), want) <= 1e-6
+
+
 # ------------------------------------------------------------------ scoring
 
 def _score_case(w, seq=0, layer=0):
