@@ -170,6 +170,19 @@ def test_rollover_writes_only_its_buffers(rdkv):
     rdkv.decode(lay, cache.t, 0, q, workspace=wsd.t, out=out.t)
     out.check("output over every generation")
     assert torch.isfinite(out.t).all()
+    # the same step with the prefill blob's measured launch shape (the
+    # generations keep their own slots): only its buffers written, and the
+    # same outputs up to the merge's rounding
+    scan = Guarded(8, torch.uint8)
+    shape = rdkv.decode_shape(lay, cache.t, scan.t)
+    wss = Guarded(int(shape.decode_workspace_bytes), torch.uint8)
+    out2 = Guarded((S, L, Hq, 128), torch.float32)
+    rdkv.decode(lay, cache.t, 0, q, workspace=wss.t, out=out2.t, shape=shape)
+    for b, what in ((scan, "shape scan buffer"), (cache, "cache"), (wss, "shaped decode workspace"),
+                    (out2, "shaped output")):
+        b.check(f"{what} with the measured shape")
+    a, b = out2.t.double(), out.t.double()
+    assert float(((a - b).abs().amax(-1) / b.abs().amax(-1).clamp_min(1e-30)).max()) <= 1e-6
 
 
 def test_paged_path_writes_only_its_buffers(rdkv):
@@ -213,6 +226,19 @@ def test_paged_path_writes_only_its_buffers(rdkv):
         for b, what in ((cache, "paged cache"), (wsd, "paged decode workspace"), (out, "paged output")):
             b.check(f"{what} at step {step}")
         c_len = [c + 1 for c in c_len]
+    # the measured launch shape: its 8-byte scan buffer, then a shaped step in
+    # a workspace of exactly the shape's size
+    scan = Guarded(8, torch.uint8)
+    shape = rdkv.paged_decode_shape(pl, cache.t, scan.t)
+    scan.check("shape scan buffer")
+    cache.check("paged cache after the shape scan")
+    wss = Guarded(int(shape.decode_workspace_bytes), torch.uint8)
+    q = dev(r.standard_normal((S, L, Hq, 128)).astype(np.float16))
+    kn = dev(r.standard_normal((S, L, Hkv, 128)).astype(np.float16))
+    vn = dev(r.standard_normal((S, L, Hkv, 128)).astype(np.float16))
+    rdkv.paged_decode(pl, cache.t, c_len, q, kn, vn, workspace=wss.t, out=out.t, shape=shape)
+    for b, what in ((cache, "paged cache"), (wss, "shaped decode workspace"), (out, "paged output")):
+        b.check(f"{what} after a shaped step")
     rdkv.paged_release(pl, cache.t, 1)
     cache.check("paged cache after release")
     assert torch.isfinite(out.t).all()
