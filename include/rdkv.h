@@ -439,8 +439,11 @@ rdkv_status rdkv_paged_decode(const rdkv_paged_layout* layout, void* cache, size
  * segments as they were when it was made: make a new one after a commit or a
  * pack (a release leaves it valid).  A segment in use that the shape does not
  * cover (more chunks or longer records than it allows) is not decoded and
- * takes no appended token: its outputs are set to NaN.  Errors: RDKV_ERR_SHAPE
- * for a shape outside the layout's bounds, others as the unshaped call. */
+ * takes no appended token: its outputs are set to NaN.  The shaped calls read
+ * token_slots, rec_max and reserved from the shape; max_chunks and
+ * decode_workspace_bytes are what they derive from them, for the caller.
+ * Errors: RDKV_ERR_SHAPE for a shape outside the layout's bounds (or a
+ * nonzero reserved field), others as the unshaped call. */
 typedef struct rdkv_launch_shape {
   int32_t token_slots;              /* prefill-token chunk slots per segment (<= layout->token_slots) */
   int32_t rec_max;                  /* bytes of the longest K record, a multiple of 4 (<= layout->rec_max) */
