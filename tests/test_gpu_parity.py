@@ -527,7 +527,8 @@ def _seg_shapes_contiguous(lay, cache):
             for s in range(lay.n_seg)]
 
 
-def test_shared_budget_cache_decodes_with_measured_shape(gpu_lib):
+@pytest.mark.parametrize("G", [4, 1, 8])
+def test_shared_budget_cache_decodes_with_measured_shape(gpu_lib, G):
     """A contiguous blob laid out for a per-layer budget (each segment's
     bound is the layer's budget): the measured launch shape matches the
     descriptors and stays within the bounds, the shaped decode agrees with the
@@ -536,8 +537,8 @@ def test_shared_budget_cache_decodes_with_measured_shape(gpu_lib):
     budget, the old shape gives that segment NaN outputs and the others the
     same values; a new shape covers it."""
     rdkv = gpu_lib
-    S, L, Hq, Hkv, N, cap = 1, 2, 8, 2, 3000, 16
-    G, n_seg = Hq // Hkv, S * L * Hkv
+    S, L, Hkv, N, cap = 1, 2, 2, 3000, 16
+    Hq, n_seg = G * Hkv, S * L * Hkv
     w_tok, var_tok, w_chan = synth.random_unit_inputs(n_seg, N, seed=61)
     K, V = synth.random_kv(n_seg, N, seed=62)
     bv, bk = int(1.0 * N) * Hkv, 80 * Hkv
