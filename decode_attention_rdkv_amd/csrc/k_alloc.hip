@@ -41,11 +41,10 @@ __device__ inline int unit_bits(float c, double lam) {
 // the exponent, then six 8-bit digits of the mantissa and a last 4-bit one:
 // 8 passes over the units.  A problem that fits one workgroup runs all passes
 // in it (alloc_one_kernel: the K channels, and short V problems); a long V
-// problem takes two launches per pass: sel_hist_kernel splits each group's
-// units over many workgroups, each adding its LDS histogram to the group's
+// problem takes one launch per pass (sel_pass_kernel): its units are split
+// over many workgroups, each adding its LDS histogram to the group's
 // histogram in the workspace (integer sums, so the order of the additions does
-// not matter), then sel_pick_kernel, one wave per group, fixes the digit and
-// clears the histogram for the next pass.
+// not matter); the next launch's workgroups fix that digit from it.
 constexpr int kSelBuckets = 2048;
 constexpr int kSelPasses = 8;
 constexpr int kSelThreads = 256;
@@ -123,11 +122,13 @@ __device__ void histogram_digit(const float* w, const float* v, int64_t lo, int6
 }
 
 // Called by one whole wave with a group's complete histogram h of digit
-// `pass` and its state st (either in LDS or in global memory): lane L sums
-// buckets [L C, L C + C); the lane where the weight from above crosses the
-// budget B scans its buckets top down and fixes the digit.  The histogram is
-// left zero for the next pass.
-__device__ void pick_digit(unsigned long long* h, unsigned long long* st, int pass, unsigned long long B) {
+// `pass` and its state before that digit, st_in (LDS or global memory):
+// writes to st_out the state with the digit fixed.  Lane L sums buckets
+// [L C, L C + C); the lane where the weight from above crosses the budget B
+// scans its buckets top down.  With `clear`, each lane then zeroes its own
+// buckets for the next pass.  st_out may be st_in.
+__device__ void pick_digit(unsigned long long* h, const unsigned long long* st_in, unsigned long long* st_out,
+                           int pass, unsigned long long B, bool clear) {
   const int shift = sel_shift(pass), nb = 1 << sel_width(pass);
   const int L = threadIdx.x & 63, C = nb >= 64 ? nb / 64 : 1;
   const bool mine = L * C < nb;
@@ -140,10 +141,17 @@ __device__ void pick_digit(unsigned long long* h, unsigned long long* st, int pa
     const unsigned long long o = __shfl_down(incl, off);
     if (L + off < 64) incl += o;
   }
-  const unsigned long long above = st[kStAbove], prefix = st[kStPrefix];
+  const unsigned long long above = st_in[kStAbove], prefix = st_in[kStPrefix], done = st_in[kStDone];
   const unsigned long long total = __shfl(incl, 0);
-  if (pass == 0 && total <= B) {   // every product fits: lambda* = 0 (the prefix stays 0)
-    if (L == 0) st[kStDone] = 1;
+  if (L == 0) {
+    st_out[kStAbove] = above;
+    st_out[kStPrefix] = prefix;
+    st_out[kStDone] = done;
+  }
+  if (done) {
+    // nothing left to fix
+  } else if (pass == 0 && total <= B) {   // every product fits: lambda* = 0 (the prefix stays 0)
+    if (L == 0) st_out[kStDone] = 1;
   } else {
     const unsigned long long strictly = above + (incl - sl);
     if (strictly <= B && above + incl > B) {   // exactly one lane (weights are non-negative)
@@ -153,11 +161,11 @@ __device__ void pick_digit(unsigned long long* h, unsigned long long* st, int pa
         if (acc + h[d] > B) break;
         acc += h[d];
       }
-      st[kStAbove] = acc;
-      st[kStPrefix] = prefix | ((unsigned long long)d << shift);
+      st_out[kStAbove] = acc;
+      st_out[kStPrefix] = prefix | ((unsigned long long)d << shift);
     }
   }
-  if (mine)   // (after this lane's own reads of its buckets)
+  if (clear && mine)   // (after this lane's own reads of its buckets)
     for (int i = 0; i < C; ++i) h[L * C + i] = 0;
 }
 
@@ -174,40 +182,63 @@ __device__ void write_bits(const float* w, const float* v, int64_t lo, int64_t h
   }
 }
 
-// A pass over many workgroups per group: each histograms its share of the
-// group's units and adds it to the group's histogram in the workspace.
-__global__ __launch_bounds__(kSelThreads) void sel_hist_kernel(SelArgs a) {
+// The group's histograms and states in the workspace: three histogram
+// buffers in rotation (pass p fills buffer p mod 3, reads buffer p - 1 mod 3
+// and clears buffer p + 1 mod 3, which pass p - 1 read), and two state slots
+// (the state after digit d in slot d mod 2).
+constexpr int kHistBufs = 3, kStSlots = 2;
+
+// Pass p over many workgroups per group.  Every workgroup first fixes digit
+// p - 1 itself from the complete histogram of the previous launch (the same
+// integer arithmetic everywhere, so the same digit), and its first workgroup
+// stores that state for the next launch; then each histograms its share of
+// the group's units for digit p and adds it to the group's buffer.
+__global__ __launch_bounds__(kSelThreads) void sel_pass_kernel(SelArgs a, int64_t budget) {
   __shared__ unsigned long long s_hist[kSelBuckets];
+  __shared__ unsigned long long s_st[kStWords];
   const int64_t g = blockIdx.x / a.blocks;
   const int blk = int(blockIdx.x % a.blocks);
-  const unsigned long long* st = a.state + g * kStWords;
-  if (st[kStDone]) return;
-  const int nb = 1 << sel_width(a.pass);
+  const int p = a.pass;
+  unsigned long long* hist = a.hist + g * kHistBufs * kSelBuckets;
+  unsigned long long* state = a.state + g * kStSlots * kStWords;
+  if (p == 0) {
+    if (threadIdx.x < kStWords) s_st[threadIdx.x] = 0;
+  } else if (threadIdx.x < 64) {
+    pick_digit(hist + ((p - 1) % kHistBufs) * kSelBuckets, state + ((p - 2) & 1) * kStWords, s_st, p - 1,
+               (unsigned long long)budget, false);
+  }
+  __syncthreads();
+  if (blk == 0 && p > 0 && threadIdx.x < kStWords) state[((p - 1) & 1) * kStWords + threadIdx.x] = s_st[threadIdx.x];
+  if (s_st[kStDone]) return;   // (uniform)
+  unsigned long long* next = hist + ((p + 1) % kHistBufs) * kSelBuckets;
+  for (int i = blk * kSelThreads + threadIdx.x; i < kSelBuckets; i += a.blocks * kSelThreads) next[i] = 0;
+  const int nb = 1 << sel_width(p);
   for (int i = threadIdx.x; i < nb; i += kSelThreads) s_hist[i] = 0;
   __syncthreads();
   int64_t lo, hi;
   block_range(a.n, a.blocks, blk, lo, hi);
-  histogram_digit(a.w + g * a.n, a.sigma + g * a.n, lo, hi, a.pass, st[kStPrefix], s_hist);
+  histogram_digit(a.w + g * a.n, a.sigma + g * a.n, lo, hi, p, s_st[kStPrefix], s_hist);
   __syncthreads();
-  unsigned long long* gh = a.hist + g * kSelBuckets;
+  unsigned long long* gh = hist + (p % kHistBufs) * kSelBuckets;
   for (int i = threadIdx.x; i < nb; i += kSelThreads)
     if (s_hist[i]) atomicAdd(&gh[i], s_hist[i]);
 }
 
-// One wave per group: the digit of this pass from the group's histogram.
-__global__ __launch_bounds__(64) void sel_pick_kernel(SelArgs a, int64_t budget) {
-  const int64_t g = blockIdx.x;
-  unsigned long long* st = a.state + g * kStWords;
-  if (st[kStDone]) return;
-  pick_digit(a.hist + g * kSelBuckets, st, a.pass, (unsigned long long)budget);
-}
-
-// Bits of every V token for its group's lambda*, and lambda_V of the group's segments.
-__global__ __launch_bounds__(kSelThreads) void alloc_v_bits_kernel(SelArgs a, int32_t group, uint8_t* bits_tok,
-                                                                   double* lambda) {
+// After the last pass: every workgroup fixes the last digit (lambda*), writes
+// the bits of its share of the V tokens, and the first one lambda_V of the
+// group's segments.
+__global__ __launch_bounds__(kSelThreads) void alloc_v_bits_kernel(SelArgs a, int64_t budget, int32_t group,
+                                                                   uint8_t* bits_tok, double* lambda) {
+  __shared__ unsigned long long s_st[kStWords];
   const int64_t g = blockIdx.x / a.blocks;
   const int blk = int(blockIdx.x % a.blocks);
-  const double lam = __longlong_as_double((long long)a.state[g * kStWords + kStPrefix]);
+  constexpr int kLast = kSelPasses - 1;
+  if (threadIdx.x < 64)
+    pick_digit(a.hist + (g * kHistBufs + kLast % kHistBufs) * kSelBuckets,
+               a.state + (g * kStSlots + ((kLast - 1) & 1)) * kStWords, s_st, kLast, (unsigned long long)budget,
+               false);
+  __syncthreads();
+  const double lam = __longlong_as_double((long long)s_st[kStPrefix]);
   int64_t lo, hi;
   block_range(a.n, a.blocks, blk, lo, hi);
   write_bits(a.w + g * a.n, a.sigma + g * a.n, lo, hi, lam, bits_tok + g * a.n);
@@ -233,7 +264,7 @@ __global__ __launch_bounds__(kSelThreads) void alloc_one_kernel(SelArgs a, int64
     if (s_st[kStDone]) break;   // (uniform)
     histogram_digit(w, v, 0, a.n, pass, s_st[kStPrefix], s_hist);
     __syncthreads();
-    if (threadIdx.x < 64) pick_digit(s_hist, s_st, pass, (unsigned long long)budget);
+    if (threadIdx.x < 64) pick_digit(s_hist, s_st, s_st, pass, (unsigned long long)budget, true);
     __syncthreads();
   }
   const double lam = __longlong_as_double((long long)s_st[kStPrefix]);
@@ -494,20 +525,18 @@ hipError_t launch_allocate(const AllocParams& p, hipStream_t stream) {
     le.check();
   } else {
     // the histograms and states start at zero (a fill kernel, so a captured graph replays it)
-    const int64_t words = (w.state + n_groups * kStWords * 8 - w.hist) / 8;
+    const int64_t words = (w.state + n_groups * kStSlots * kStWords * 8 - w.hist) / 8;
     hipLaunchKernelGGL(fill_u64_kernel, dim3(unsigned(std::min<int64_t>(cdiv(words, 256), 1024))), dim3(256), 0,
                        stream, hist, words);
     le.check();
     const unsigned v_grid = unsigned(n_groups * w.v_blocks);
     for (int pass = 0; pass < kSelPasses; ++pass) {
       sa.pass = pass;
-      hipLaunchKernelGGL(sel_hist_kernel, dim3(v_grid), dim3(kSelThreads), 0, stream, sa);
-      le.check();
-      hipLaunchKernelGGL(sel_pick_kernel, dim3(unsigned(n_groups)), dim3(64), 0, stream, sa, p.budget_v);
+      hipLaunchKernelGGL(sel_pass_kernel, dim3(v_grid), dim3(kSelThreads), 0, stream, sa, p.budget_v);
       le.check();
     }
-    hipLaunchKernelGGL(alloc_v_bits_kernel, dim3(v_grid), dim3(kSelThreads), 0, stream, sa, p.group, p.bits_tok,
-                       p.lambda);
+    hipLaunchKernelGGL(alloc_v_bits_kernel, dim3(v_grid), dim3(kSelThreads), 0, stream, sa, p.budget_v, p.group,
+                       p.bits_tok, p.lambda);
     le.check();
   }
   AllocKArgs ka{p.n_tokens, p.group, w.k_blocks, p.K, p.bits_tok, p.w_chan, p.budget_k, p.bits_chan, p.var_chan,
@@ -544,8 +573,8 @@ AllocPlan alloc_plan(int64_t n_seg, int64_t n_tokens, int32_t group) {
   };
   // (one workgroup per problem keeps its histogram in LDS and its sums in registers)
   const uint64_t vg = w.v_blocks > 1 ? uint64_t(n_groups) : 0, ks = w.k_blocks > 1 ? uint64_t(n_seg) * w.k_blocks : 0;
-  w.hist = take(vg * kSelBuckets * 8);
-  w.state = take(vg * kStWords * 8);
+  w.hist = take(vg * kHistBufs * kSelBuckets * 8);
+  w.state = take(vg * kStSlots * kStWords * 8);
   w.s1 = take(ks * kHeadDim * 8);
   w.s2 = take(ks * kHeadDim * 16);
   w.cnt = take(ks * 8);
